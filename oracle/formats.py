@@ -1,0 +1,440 @@
+"""Block formats: quantize, dequantize, pack, unpack (oracle; test infrastructure only).
+
+Sources (the reader has the pages):
+
+* Handbook page "端侧推理：llama.cpp 与 GGUF、MLX、ExecuTorch", section
+  "GGUF 的量化格式" (the format list and the simplified PyTorch quantizer
+  listing) defines Q8_0, Q4_0, Q4_1 and the simplified Q4_K.
+* The low-bit README page ("我正让 LLM 能在小型老旧设备上运行"), kernel
+  before/after table: ternary weights held in 2-bit fields with one scale per
+  128 weights, 1-bit sign weights with a block scale, and Q2_K experts.
+* The Flash-MoE page: 2-bit experts.
+
+Readings where the pages are silent (each also listed with its reason in the
+design notes):
+
+R1  Scales and mins are *stored* as fp16 (the text says fp16; the listing
+    keeps fp32).  Each one is computed in fp32 exactly as the listing does,
+    rounded to fp16 (round-to-nearest-even, subnormals kept), and the codes
+    are computed against the stored value, because that is all a decoder sees.
+R2  Rounding is round-half-to-even (torch ``round``); divisions are IEEE fp32
+    divisions in the order written; clamps follow rounding.
+R3  A zero divisor gives the "zero" code: Q8_0 0, Q4_0 nibble 8, Q4_1 nibble 0,
+    K-quant scale code 1 / min code 0 / weight code 0.  Non-finite input is
+    rejected; a scale that overflows fp16 is rejected.
+R4  Byte order: nibble i of a block in byte i>>1 (low nibble when i is even);
+    2-bit field i in byte i>>2, bits 2*(i&3); bit i in byte i>>3, bit i&7.
+    K-quant meta (16 B per 256 weights): fp16 d, fp16 dmin, then a 96-bit
+    little-endian field holding eight 12-bit pairs p_j = s_j | t_j << 6 at
+    bits [12j, 12j+12).
+R5  Signed zeros in the input are canonicalised to +0 before quantization
+    (w + 0.0), so the sign of a zero scale is a function of the values only.
+R6  Q2_K (layout on no page) is the handbook's Q4_K construction with 2-bit
+    codes: 15 -> 3 and weight codes clamped to [0, 3]; 80 B per 256 weights.
+R7  tern: field f = t + 1 for t in {-1, 0, +1} (3 never emitted); bin: bit 1
+    means +1.  One fp16 scale per 128 weights for both.  The pages give no
+    ternarizer or binarizer (those models are trained so), so these two
+    "quantizers" pack given codes and scales exactly.
+
+Plane layout of one packed [N][K] matrix: the codes plane (N * K/bs blocks of
+``code_bytes``, row-major over (row, block)) followed by the meta plane
+(N * K/bs entries of ``meta_bytes``, same order).  Total = N*K*bpw/8 bytes.
+
+Parity: Q8_0, Q4_0, Q4_1, Q4_K are pinned by the page's printed error table
+(through ``page_listing``), by the bits/weight closed forms in the listing and
+by round trips of hand-built blocks.  Q2_K, tern and bin are pinned by round
+trips, closed forms and brute force only (their layouts are readings).
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+
+import numpy as np
+
+F32 = np.float32
+
+FORMATS = ("q8_0", "q4_0", "q4_1", "q4_k", "q2_k", "tern", "bin")
+
+
+class QuantInputError(ValueError):
+    """Non-finite weight given to a quantizer (reading R3)."""
+
+
+class QuantRangeError(ValueError):
+    """A computed scale or min does not fit in fp16 (reading R3)."""
+
+
+@dataclass(frozen=True)
+class Spec:
+    block: int        # weights per block (scale group of the meta plane)
+    code_bytes: int   # bytes of codes per block
+    meta_bytes: int   # bytes of meta per block
+
+    @property
+    def bpw(self) -> float:
+        return (self.code_bytes + self.meta_bytes) * 8.0 / self.block
+
+
+SPECS = {
+    "q8_0": Spec(32, 32, 2),
+    "q4_0": Spec(32, 16, 2),
+    "q4_1": Spec(32, 16, 4),
+    "q4_k": Spec(256, 128, 16),
+    "q2_k": Spec(256, 64, 16),
+    "tern": Spec(128, 32, 2),
+    "bin": Spec(128, 16, 2),
+}
+
+
+def packed_size(fmt: str, n: int, k: int) -> int:
+    s = SPECS[fmt]
+    if k % s.block:
+        raise ValueError(f"K={k} is not a multiple of the {fmt} block ({s.block})")
+    return n * (k // s.block) * (s.code_bytes + s.meta_bytes)
+
+
+def codes_plane_size(fmt: str, n: int, k: int) -> int:
+    s = SPECS[fmt]
+    return n * (k // s.block) * s.code_bytes
+
+
+# ----------------------------------------------------------------------------
+# fp16 storage (R1)
+
+def to_f16_bits(v) -> np.ndarray:
+    """fp32 -> fp16 bit pattern, round-to-nearest-even, subnormals kept.
+
+    Raises QuantRangeError when the value overflows fp16.
+    """
+    v = np.asarray(v, dtype=F32)
+    with np.errstate(over="ignore", invalid="ignore"):
+        h = v.astype(np.float16)
+    if not np.all(np.isfinite(h)):
+        raise QuantRangeError("scale or min overflows fp16")
+    return h.view(np.uint16)
+
+
+def from_f16_bits(bits) -> np.ndarray:
+    """fp16 bit pattern -> fp32 (exact)."""
+    return np.asarray(bits, dtype=np.uint16).view(np.float16).astype(F32)
+
+
+def _canonical(w: np.ndarray, block: int) -> np.ndarray:
+    w = np.asarray(w, dtype=F32)
+    if w.ndim != 2:
+        raise ValueError("weights must be a 2-D [N, K] array")
+    if w.shape[1] % block:
+        raise ValueError(f"K={w.shape[1]} is not a multiple of {block}")
+    if not np.all(np.isfinite(w)):
+        raise QuantInputError("non-finite weight")
+    return w + F32(0.0)  # R5: -0 -> +0
+
+
+def _div(a, b):
+    with np.errstate(divide="ignore", invalid="ignore"):
+        return np.divide(a, b, dtype=F32)
+
+
+# ----------------------------------------------------------------------------
+# Quantizers (one per format).  Each returns a dict of plain arrays: the
+# block representation that ``pack`` lays out and ``dequant`` decodes.
+
+def quantize_q8_0(w) -> dict:
+    """32 weights per block; d = max|b| / 127 (fp16); q = rint(b / d) in [-127, 127]."""
+    w = _canonical(w, 32)
+    n, k = w.shape
+    b = w.reshape(n, k // 32, 32)
+    a = np.abs(b).max(axis=2)
+    d16 = to_f16_bits(_div(a, F32(127)))
+    d = from_f16_bits(d16)[..., None]
+    q = np.where(d == 0, F32(0), np.clip(np.rint(_div(b, d)), -127, 127))
+    return {"d": d16, "q": q.astype(np.int8).reshape(n, k)}
+
+
+def quantize_q4_0(w) -> dict:
+    """32 weights per block; signed d = (the max-|b| element, first on ties) / -8,
+    so that element lands on code -8; codes rint(b / d) in [-8, 7], stored + 8."""
+    w = _canonical(w, 32)
+    n, k = w.shape
+    b = w.reshape(n, k // 32, 32)
+    j = np.argmax(np.abs(b), axis=2)  # first index of the maximum
+    bj = np.take_along_axis(b, j[..., None], axis=2)[..., 0]
+    d16 = to_f16_bits(_div(bj, F32(-8)))
+    d = from_f16_bits(d16)[..., None]
+    c = np.where(d == 0, F32(0), np.clip(np.rint(_div(b, d)), -8, 7))
+    return {"d": d16, "n": (c.astype(np.int16) + 8).astype(np.uint8).reshape(n, k)}
+
+
+def quantize_q4_1(w) -> dict:
+    """32 weights per block; d = (max - min) / 15 and m = min (both fp16);
+    codes rint((b - m) / d) in [0, 15]."""
+    w = _canonical(w, 32)
+    n, k = w.shape
+    b = w.reshape(n, k // 32, 32)
+    lo = b.min(axis=2)
+    hi = b.max(axis=2)
+    d16 = to_f16_bits(_div(hi - lo, F32(15)))
+    m16 = to_f16_bits(lo)
+    d = from_f16_bits(d16)[..., None]
+    m = from_f16_bits(m16)[..., None]
+    q = np.where(d == 0, F32(0), np.clip(np.rint(_div(b - m, d)), 0, 15))
+    return {"d": d16, "m": m16, "n": q.astype(np.uint8).reshape(n, k)}
+
+
+def _quantize_kquant(w, qmax: int) -> dict:
+    """Handbook's simplified K-quant with weight codes in [0, qmax].
+
+    Per 32-weight sub-block j: lo = min(min b, 0), hi = max b,
+    sc = (hi - lo) / qmax, mn = -lo.  Per 256-weight super-block: fp16
+    d = max_j sc / 63 and dmin = max_j mn / 63; 6-bit codes s_j = rint(sc / d)
+    in [1, 63] and t_j = rint(mn / dmin) in [0, 63]; restored S = s*d and
+    Mn = t*dmin (exact in fp32); weight codes rint((b + Mn) / S) in [0, qmax];
+    the weight decodes as code*S - Mn.
+    """
+    w = _canonical(w, 256)
+    n, k = w.shape
+    b = w.reshape(n, k // 256, 8, 32)
+    lo = np.minimum(b.min(axis=3), F32(0))
+    hi = b.max(axis=3)
+    sc = _div(hi - lo, F32(qmax))
+    mn = -lo
+    d16 = to_f16_bits(_div(sc.max(axis=2), F32(63)))
+    dmin16 = to_f16_bits(_div(mn.max(axis=2), F32(63)))
+    dd = from_f16_bits(d16)[..., None]
+    dm = from_f16_bits(dmin16)[..., None]
+    s = np.where(dd == 0, F32(1), np.clip(np.rint(_div(sc, dd)), 1, 63))
+    t = np.where(dm == 0, F32(0), np.clip(np.rint(_div(mn, dm)), 0, 63))
+    S = (s * dd)[..., None]
+    Mn = (t * dm)[..., None]
+    q = np.where(S == 0, F32(0), np.clip(np.rint(_div(b + Mn, S)), 0, qmax))
+    return {
+        "d": d16,
+        "dmin": dmin16,
+        "s": s.astype(np.uint8),
+        "t": t.astype(np.uint8),
+        "n": q.astype(np.uint8).reshape(n, k),
+    }
+
+
+def quantize_q4_k(w) -> dict:
+    return _quantize_kquant(w, 15)
+
+
+def quantize_q2_k(w) -> dict:
+    return _quantize_kquant(w, 3)
+
+
+def tern_from_codes(codes, scale_bits) -> dict:
+    """Ternary codes t in {-1, 0, +1} [N, K] plus fp16 scale bits [N, K/128]."""
+    codes = np.asarray(codes)
+    n, k = codes.shape
+    if k % 128:
+        raise ValueError("K must be a multiple of 128")
+    if not np.all((codes >= -1) & (codes <= 1)):
+        raise QuantInputError("ternary codes must be -1, 0 or +1")
+    sb = np.asarray(scale_bits, dtype=np.uint16).reshape(n, k // 128)
+    return {"d": sb.copy(), "f": (codes.astype(np.int16) + 1).astype(np.uint8)}
+
+
+def bin_from_codes(bits, scale_bits) -> dict:
+    """1-bit codes in {0, 1} [N, K] (1 means +1) plus fp16 scale bits [N, K/128]."""
+    bits = np.asarray(bits)
+    n, k = bits.shape
+    if k % 128:
+        raise ValueError("K must be a multiple of 128")
+    if not np.all((bits == 0) | (bits == 1)):
+        raise QuantInputError("1-bit codes must be 0 or 1")
+    sb = np.asarray(scale_bits, dtype=np.uint16).reshape(n, k // 128)
+    return {"d": sb.copy(), "b": bits.astype(np.uint8)}
+
+
+QUANTIZERS = {
+    "q8_0": quantize_q8_0,
+    "q4_0": quantize_q4_0,
+    "q4_1": quantize_q4_1,
+    "q4_k": quantize_q4_k,
+    "q2_k": quantize_q2_k,
+}
+
+
+def quantize(fmt: str, w) -> dict:
+    return QUANTIZERS[fmt](w)
+
+
+# ----------------------------------------------------------------------------
+# Dequantization: every product below is exact in fp32 (codes of <= 8 bits
+# times fp16 significands); the only rounding is the final add/subtract of
+# Q4_1's m and the K-quants' Mn.
+
+def _per_block(v, block: int, k: int):
+    """Broadcast a per-block [N, K/block] array over [N, K]."""
+    return np.repeat(v, block, axis=-1).reshape(v.shape[0], k)
+
+
+def dequant(fmt: str, blk: dict) -> np.ndarray:
+    if fmt == "q8_0":
+        q = blk["q"]
+        return q.astype(F32) * _per_block(from_f16_bits(blk["d"]), 32, q.shape[1])
+    if fmt == "q4_0":
+        nn = blk["n"]
+        c = (nn.astype(np.int16) - 8).astype(F32)
+        return c * _per_block(from_f16_bits(blk["d"]), 32, nn.shape[1])
+    if fmt == "q4_1":
+        nn = blk["n"]
+        k = nn.shape[1]
+        d = _per_block(from_f16_bits(blk["d"]), 32, k)
+        m = _per_block(from_f16_bits(blk["m"]), 32, k)
+        return nn.astype(F32) * d + m
+    if fmt in ("q4_k", "q2_k"):
+        nn = blk["n"]
+        n, k = nn.shape
+        dd = from_f16_bits(blk["d"])[..., None]
+        dm = from_f16_bits(blk["dmin"])[..., None]
+        S = (blk["s"].astype(F32) * dd).reshape(n, k // 32)
+        Mn = (blk["t"].astype(F32) * dm).reshape(n, k // 32)
+        return nn.astype(F32) * _per_block(S, 32, k) - _per_block(Mn, 32, k)
+    if fmt == "tern":
+        f = blk["f"]
+        return (f.astype(np.int16) - 1).astype(F32) * _per_block(from_f16_bits(blk["d"]), 128, f.shape[1])
+    if fmt == "bin":
+        bb = blk["b"]
+        return (2 * bb.astype(np.int16) - 1).astype(F32) * _per_block(from_f16_bits(blk["d"]), 128, bb.shape[1])
+    raise KeyError(fmt)
+
+
+# ----------------------------------------------------------------------------
+# Byte layout (R4)
+
+def _nibbles_to_bytes(v):
+    v = v.astype(np.uint8)
+    return (v[:, 0::2] | (v[:, 1::2] << 4)).astype(np.uint8)
+
+
+def _bytes_to_nibbles(by, k):
+    out = np.empty((by.shape[0], k), dtype=np.uint8)
+    out[:, 0::2] = by & 0x0F
+    out[:, 1::2] = by >> 4
+    return out
+
+
+def _crumbs_to_bytes(v):
+    v = v.astype(np.uint8)
+    return (v[:, 0::4] | (v[:, 1::4] << 2) | (v[:, 2::4] << 4) | (v[:, 3::4] << 6)).astype(np.uint8)
+
+
+def _bytes_to_crumbs(by, k):
+    out = np.empty((by.shape[0], k), dtype=np.uint8)
+    for i in range(4):
+        out[:, i::4] = (by >> (2 * i)) & 3
+    return out
+
+
+def _kquant_meta_bytes(blk) -> np.ndarray:
+    """[N, SB, 16] bytes: d, dmin (little-endian fp16), then pairs p_j = s_j | t_j<<6
+    at bits [12j, 12j+12) of a 96-bit little-endian field."""
+    d16, dm16 = blk["d"], blk["dmin"]
+    n, sb = d16.shape
+    p = blk["s"].astype(np.uint32) | (blk["t"].astype(np.uint32) << 6)  # [N, SB, 8], 12 bits each
+    out = np.empty((n, sb, 16), dtype=np.uint8)
+    out[..., 0] = d16 & 0xFF
+    out[..., 1] = d16 >> 8
+    out[..., 2] = dm16 & 0xFF
+    out[..., 3] = dm16 >> 8
+    for m in range(4):  # pairs (2m, 2m+1) fill bits [24m, 24m+24) = bytes 3m .. 3m+2
+        v = p[..., 2 * m] | (p[..., 2 * m + 1] << 12)
+        out[..., 4 + 3 * m] = v & 0xFF
+        out[..., 5 + 3 * m] = (v >> 8) & 0xFF
+        out[..., 6 + 3 * m] = (v >> 16) & 0xFF
+    return out
+
+
+def _kquant_meta_unpack(mb):
+    """Inverse of ``_kquant_meta_bytes`` for an [N, SB, 16] uint8 array."""
+    mb = mb.astype(np.uint32)
+    d16 = (mb[..., 0] | (mb[..., 1] << 8)).astype(np.uint16)
+    dm16 = (mb[..., 2] | (mb[..., 3] << 8)).astype(np.uint16)
+    n, sb = d16.shape
+    s = np.empty((n, sb, 8), dtype=np.uint8)
+    t = np.empty((n, sb, 8), dtype=np.uint8)
+    for m in range(4):
+        v = mb[..., 4 + 3 * m] | (mb[..., 5 + 3 * m] << 8) | (mb[..., 6 + 3 * m] << 16)
+        for h in range(2):
+            pj = (v >> (12 * h)) & 0xFFF
+            s[..., 2 * m + h] = pj & 0x3F
+            t[..., 2 * m + h] = pj >> 6
+    return d16, dm16, s, t
+
+
+def _u16_le(v) -> np.ndarray:
+    v = np.asarray(v, dtype=np.uint16)
+    return np.stack([(v & 0xFF).astype(np.uint8), (v >> 8).astype(np.uint8)], axis=-1)
+
+
+def _le_u16(by) -> np.ndarray:
+    by = by.astype(np.uint16)
+    return (by[..., 0] | (by[..., 1] << 8)).astype(np.uint16)
+
+
+def pack(fmt: str, blk: dict) -> np.ndarray:
+    """Block representation -> packed bytes (codes plane then meta plane)."""
+    if fmt == "q8_0":
+        codes = blk["q"].view(np.uint8)
+        meta = _u16_le(blk["d"])
+    elif fmt in ("q4_0",):
+        codes = _nibbles_to_bytes(blk["n"])
+        meta = _u16_le(blk["d"])
+    elif fmt == "q4_1":
+        codes = _nibbles_to_bytes(blk["n"])
+        meta = np.stack([_u16_le(blk["d"]), _u16_le(blk["m"])], axis=-2)
+    elif fmt == "q4_k":
+        codes = _nibbles_to_bytes(blk["n"])
+        meta = _kquant_meta_bytes(blk)
+    elif fmt == "q2_k":
+        codes = _crumbs_to_bytes(blk["n"])
+        meta = _kquant_meta_bytes(blk)
+    elif fmt == "tern":
+        codes = _crumbs_to_bytes(blk["f"])
+        meta = _u16_le(blk["d"])
+    elif fmt == "bin":
+        codes = np.packbits(blk["b"].astype(np.uint8), axis=1, bitorder="little")
+        meta = _u16_le(blk["d"])
+    else:
+        raise KeyError(fmt)
+    return np.concatenate([np.ascontiguousarray(codes).reshape(-1),
+                           np.ascontiguousarray(meta).reshape(-1)]).astype(np.uint8)
+
+
+def unpack(fmt: str, buf, n: int, k: int) -> dict:
+    """Packed bytes -> block representation (inverse of ``pack``)."""
+    buf = np.asarray(buf, dtype=np.uint8).reshape(-1)
+    spec = SPECS[fmt]
+    if buf.size != packed_size(fmt, n, k):
+        raise ValueError("buffer size does not match the format and shape")
+    nb = k // spec.block
+    cp = codes_plane_size(fmt, n, k)
+    codes = buf[:cp].reshape(n, nb * spec.code_bytes)
+    meta = buf[cp:].reshape(n, nb, spec.meta_bytes)
+    if fmt == "q8_0":
+        return {"d": _le_u16(meta), "q": codes.view(np.int8).copy()}
+    if fmt == "q4_0":
+        return {"d": _le_u16(meta), "n": _bytes_to_nibbles(codes, k)}
+    if fmt == "q4_1":
+        return {"d": _le_u16(meta[..., 0:2]), "m": _le_u16(meta[..., 2:4]), "n": _bytes_to_nibbles(codes, k)}
+    if fmt in ("q4_k", "q2_k"):
+        d16, dm16, s, t = _kquant_meta_unpack(meta)
+        nn = _bytes_to_nibbles(codes, k) if fmt == "q4_k" else _bytes_to_crumbs(codes, k)
+        return {"d": d16, "dmin": dm16, "s": s, "t": t, "n": nn}
+    if fmt == "tern":
+        return {"d": _le_u16(meta), "f": _bytes_to_crumbs(codes, k)}
+    if fmt == "bin":
+        return {"d": _le_u16(meta), "b": np.unpackbits(codes, axis=1, bitorder="little")[:, :k]}
+    raise KeyError(fmt)
+
+
+def quantize_packed(fmt: str, w) -> np.ndarray:
+    """fp32 [N, K] -> packed bytes (the quantizable formats)."""
+    return pack(fmt, quantize(fmt, w))
+
+
+def dequant_packed(fmt: str, buf, n: int, k: int) -> np.ndarray:
+    return dequant(fmt, unpack(fmt, buf, n, k))
