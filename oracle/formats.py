@@ -24,9 +24,9 @@ R3  A zero divisor gives the "zero" code: Q8_0 0, Q4_0 nibble 8, Q4_1 nibble 0,
     rejected; a scale that overflows fp16 is rejected.
 R4  Byte order: nibble i of a block in byte i>>1 (low nibble when i is even);
     2-bit field i in byte i>>2, bits 2*(i&3); bit i in byte i>>3, bit i&7.
-    K-quant meta (16 B per 256 weights): fp16 d, fp16 dmin, then a 96-bit
-    little-endian field holding eight 12-bit pairs p_j = s_j | t_j << 6 at
-    bits [12j, 12j+12).
+    K-quant meta (16 B per 256 weights): a 96-bit little-endian field holding
+    eight 12-bit pairs p_j = s_j | t_j << 6 at bits [12j, 12j+12) (bytes
+    0..11), then fp16 d (bytes 12..13) and fp16 dmin (bytes 14..15).
 R5  Signed zeros in the input are canonicalised to +0 before quantization
     (w + 0.0), so the sign of a zero scale is a function of the values only.
 R6  Q2_K (layout on no page) is the handbook's Q4_K construction with 2-bit
@@ -330,34 +330,35 @@ def _bytes_to_crumbs(by, k):
 
 
 def _kquant_meta_bytes(blk) -> np.ndarray:
-    """[N, SB, 16] bytes: d, dmin (little-endian fp16), then pairs p_j = s_j | t_j<<6
-    at bits [12j, 12j+12) of a 96-bit little-endian field."""
+    """[N, SB, 16] bytes: pairs p_j = s_j | t_j<<6 at bits [12j, 12j+12) of a
+    96-bit little-endian field (bytes 0..11), then d and dmin as little-endian
+    fp16 (bytes 12..13 and 14..15)."""
     d16, dm16 = blk["d"], blk["dmin"]
     n, sb = d16.shape
     p = blk["s"].astype(np.uint32) | (blk["t"].astype(np.uint32) << 6)  # [N, SB, 8], 12 bits each
     out = np.empty((n, sb, 16), dtype=np.uint8)
-    out[..., 0] = d16 & 0xFF
-    out[..., 1] = d16 >> 8
-    out[..., 2] = dm16 & 0xFF
-    out[..., 3] = dm16 >> 8
     for m in range(4):  # pairs (2m, 2m+1) fill bits [24m, 24m+24) = bytes 3m .. 3m+2
         v = p[..., 2 * m] | (p[..., 2 * m + 1] << 12)
-        out[..., 4 + 3 * m] = v & 0xFF
-        out[..., 5 + 3 * m] = (v >> 8) & 0xFF
-        out[..., 6 + 3 * m] = (v >> 16) & 0xFF
+        out[..., 3 * m] = v & 0xFF
+        out[..., 3 * m + 1] = (v >> 8) & 0xFF
+        out[..., 3 * m + 2] = (v >> 16) & 0xFF
+    out[..., 12] = d16 & 0xFF
+    out[..., 13] = d16 >> 8
+    out[..., 14] = dm16 & 0xFF
+    out[..., 15] = dm16 >> 8
     return out
 
 
 def _kquant_meta_unpack(mb):
     """Inverse of ``_kquant_meta_bytes`` for an [N, SB, 16] uint8 array."""
     mb = mb.astype(np.uint32)
-    d16 = (mb[..., 0] | (mb[..., 1] << 8)).astype(np.uint16)
-    dm16 = (mb[..., 2] | (mb[..., 3] << 8)).astype(np.uint16)
+    d16 = (mb[..., 12] | (mb[..., 13] << 8)).astype(np.uint16)
+    dm16 = (mb[..., 14] | (mb[..., 15] << 8)).astype(np.uint16)
     n, sb = d16.shape
     s = np.empty((n, sb, 8), dtype=np.uint8)
     t = np.empty((n, sb, 8), dtype=np.uint8)
     for m in range(4):
-        v = mb[..., 4 + 3 * m] | (mb[..., 5 + 3 * m] << 8) | (mb[..., 6 + 3 * m] << 16)
+        v = mb[..., 3 * m] | (mb[..., 3 * m + 1] << 8) | (mb[..., 3 * m + 2] << 16)
         for h in range(2):
             pj = (v >> (12 * h)) & 0xFFF
             s[..., 2 * m + h] = pj & 0x3F

@@ -215,8 +215,8 @@ def test_kquant_meta_bytes():
     blk["s"][0, 0] = np.arange(1, 9, dtype=np.uint8)
     blk["t"][0, 0] = np.arange(50, 58, dtype=np.uint8)
     meta = F.pack("q4_k", blk)[128:]
-    assert list(meta[:4]) == [0x34, 0x12, 0xCD, 0xAB]
-    field = int.from_bytes(bytes(meta[4:16]), "little")
+    assert list(meta[12:16]) == [0x34, 0x12, 0xCD, 0xAB]
+    field = int.from_bytes(bytes(meta[0:12]), "little")
     for j in range(8):
         pj = (field >> (12 * j)) & 0xFFF
         assert pj & 0x3F == j + 1 and pj >> 6 == 50 + j
