@@ -1,0 +1,256 @@
+#!/usr/bin/env python3
+"""Benchmark of the block-quantized batch-1 decode GEMV on one MI355X.
+
+Headline (the JSON line's ``value``): effective weight GB/s of the Q4_K
+batch-1 GEMV on a 14336x4096 matrix (packed bytes / wall time), cold cache:
+each step runs on the next of >= 1 GiB of distinct packed copies, so no step
+finds its weights in the 256 MB last-level cache.  One step = one GEMV call.
+
+Also reported (in ``extra``): every GEMV of the four-format comparison
+(Q8_0/Q4_0/Q4_1/Q4_K x 4096x4096/14336x4096 x batch 1/8), the low-bit
+formats, the 8B-class decode step and the MoE expert layer, each timed with
+HIP events on the launch stream.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--quick]
+
+Only one GPU is used; --gpus above 1 exits with a message.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0         # MI355X published HBM3E bandwidth
+DENSE_8B_BYTES = 3_925_868_544  # Q4_K bytes of the 8B-class step's linear weights
+COLD_BYTES = 1 << 30          # rotate over at least this many bytes of packed copies
+COUNTERS_FILE = os.path.join(ROOT, "profiles", "q4k_gemv_14336x4096_counters.txt")
+KERNEL_SOURCE = os.path.join(ROOT, "block_quantized_decode_qgemv_amd", "csrc", "gemv.hip")
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    with open(KERNEL_SOURCE, "rb") as fh:
+        return hashlib.sha256(fh.read()).hexdigest()[:16]
+
+
+def read_traffic():
+    """HBM bytes per launch from the committed counter summary, or None when the
+    kernel source changed since the counters were taken."""
+    if not os.path.exists(COUNTERS_FILE):
+        return None
+    fields = {}
+    with open(COUNTERS_FILE, encoding="utf-8") as fh:
+        for line in fh:
+            if ":" in line and not line.startswith("#"):
+                key, val = line.split(":", 1)
+                fields[key.strip()] = val.strip()
+    if fields.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None
+    try:
+        return float(fields["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+class Gemv:
+    """One GEMV configuration with rotating device copies of its packed weights."""
+
+    def __init__(self, torch, qg, fmt, n, k, b, seed, min_bytes):
+        import workloads
+
+        self.fmt, self.n, self.k, self.b = fmt, n, k, b
+        if fmt == "tern":
+            packed = qg.qpack_tern(workloads.ternary_codes(n, k, seed, 1),
+                                   workloads.scale_bits_f16((n, k // 128), seed, 2))
+        elif fmt == "bin":
+            packed = qg.qpack_bin(workloads.binary_codes(n, k, seed, 1),
+                                  workloads.scale_bits_f16((n, k // 128), seed, 2))
+        else:
+            packed = qg.qquant(fmt, workloads.student_t_weights(n, k, seed, n), n_threads=16)
+        self.bytes = packed.size
+        copies = max(1, -(-min_bytes // self.bytes))
+        src = torch.from_numpy(packed).to("cuda")
+        self.w = [src] + [src.clone() for _ in range(copies - 1)]
+        self.x = torch.from_numpy(workloads.normal((b, k), seed, 99)).to("cuda")
+        self.y = torch.empty((b, n), device="cuda")
+        self.qg = qg
+        self.i = 0
+
+    def step(self, stream):
+        self.qg.qgemv(self.fmt, self.w[self.i % len(self.w)], self.x, self.y, self.n, self.k, self.b,
+                      stream=stream)
+        self.i += 1
+
+
+def time_events(torch, fn, iters, warmup, stream):
+    """Average duration (s) of fn() from HIP event pairs around each call on `stream`."""
+    for _ in range(warmup):
+        fn()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(iters)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(iters)]
+    for i in range(iters):
+        starts[i].record(stream)
+        fn()
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    times = sorted(s.elapsed_time(e) * 1e-3 for s, e in zip(starts, ends))
+    return float(np.mean(times)), float(np.median(times))
+
+
+def cpu_baseline(seconds=12.0):
+    """The oracle (numpy dequant + float64 matvec) on a bounded sample of the
+    headline workload: whole 14336x4096 Q4_K GEMVs, repeated for ~seconds."""
+    import workloads
+    from oracle import formats as OF
+    from oracle import gemv as OG
+
+    n, k = 14336, 4096
+    w = workloads.student_t_weights(n, k, 0, n)
+    packed = OF.quantize_packed("q4_k", w)
+    x = workloads.normal((1, k), 0, 99)
+    reps = 0
+    t0 = time.perf_counter()
+    while True:
+        OG.gemv_ref(OF.dequant_packed("q4_k", packed, n, k), x)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    threads = 1
+    try:
+        from threadpoolctl import threadpool_info
+
+        threads = max([1] + [int(p.get("num_threads", 1)) for p in threadpool_info()])
+    except Exception:
+        pass
+    return {"value": packed.size * reps / el / 1e9, "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": f"{reps} full Q4_K 14336x4096 batch-1 GEMVs (dequant + float64 matvec), {el:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=2000)
+    ap.add_argument("--warmup", type=int, default=100)
+    ap.add_argument("--quick", action="store_true", help="headline only, no extra configs")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the oracle cpu_baseline leg")
+    ap.add_argument("--profile", choices=["gemv", "copy"], default=None,
+                    help="run only the headline kernel (or a 1 GiB copy) a few times, for rocprofv3")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
+              "(the GEMV is measured on one GPU's share; no collectives are built)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import block_quantized_decode_qgemv_amd as qg
+
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    qg.load()
+    stream = torch.cuda.current_stream()
+
+    if args.profile == "copy":
+        a = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        log("copied 1 GiB 3 times")
+        return
+
+    log("setup: Q4_K 14336x4096 batch 1, rotating copies")
+    head = Gemv(torch, qg, "q4_k", 14336, 4096, 1, 0, COLD_BYTES)
+    if args.profile == "gemv":
+        for _ in range(20):
+            head.step(stream)
+        torch.cuda.synchronize()
+        log("ran 20 headline GEMVs")
+        return
+
+    for _ in range(args.warmup):
+        head.step(stream)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        head.step(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    value = head.bytes * args.steps / wall / 1e9
+    log(f"headline: {value:.1f} GB/s over {args.steps} steps")
+
+    mean_s, med_s = time_events(torch, lambda: head.step(stream), min(args.steps, 1000), 10, stream)
+    achieved = head.bytes / mean_s / 1e9
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": read_traffic()}
+
+    extra = {"headline_kernel_us_mean": round(mean_s * 1e6, 3), "headline_kernel_us_median": round(med_s * 1e6, 3),
+             "tok_s_equiv": round(achieved * 1e9 / DENSE_8B_BYTES, 1)}
+    if not args.quick:
+        rows = []
+        for fmt in ("q8_0", "q4_0", "q4_1", "q4_k"):
+            for n, k in ((4096, 4096), (14336, 4096)):
+                for b in (1, 8):
+                    g = Gemv(torch, qg, fmt, n, k, b, 0, COLD_BYTES)
+                    m, md = time_events(torch, lambda: g.step(stream), 200, 20, stream)
+                    rows.append({"fmt": fmt, "N": n, "K": k, "B": b, "us": round(m * 1e6, 2),
+                                 "GBps": round(g.bytes / m / 1e9, 1)})
+                    log(f"  {fmt} {n}x{k} B={b}: {m*1e6:.2f} us, {g.bytes/m/1e9:.1f} GB/s")
+                    del g
+                    torch.cuda.empty_cache()
+        extra["four_formats"] = rows
+        rows = []
+        for fmt in ("tern", "bin", "q2_k"):
+            for n, k in ((4096, 4096), (12288, 4096), (4096, 12288)):
+                for b in (1, 4):
+                    g = Gemv(torch, qg, fmt, n, k, b, 0, COLD_BYTES)
+                    m, _ = time_events(torch, lambda: g.step(stream), 200, 20, stream)
+                    rows.append({"fmt": fmt, "N": n, "K": k, "B": b, "us": round(m * 1e6, 2),
+                                 "GBps": round(g.bytes / m / 1e9, 1),
+                                 "Gweights_s": round(n * k * b / m / 1e9, 1)})
+                    log(f"  {fmt} {n}x{k} B={b}: {m*1e6:.2f} us, {g.bytes/m/1e9:.1f} GB/s")
+                    del g
+                    torch.cuda.empty_cache()
+        extra["low_bit"] = rows
+
+    line = {
+        "metric": "Q4_K batch-1 GEMV effective weight GB/s and % of HBM peak; tok/s-equiv",
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall / args.steps * 1e3, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": "Q4_K GEMV 14336x4096, batch 1, Student-t(5)*0.02 weights, N(0,1) x, "
+                               "cold cache (rotating >= 1 GiB of packed copies)",
+                   "format": "q4_k", "N": 14336, "K": 4096, "batch": 1, "parallelism": "none"},
+        "roofline": roofline,
+        "extra": extra,
+    }
+    if not args.no_cpu:
+        log("cpu baseline (oracle)")
+        line["cpu_baseline"] = cpu_baseline()
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,276 @@
+"""Python binding for libqgemv.so, the block-quantized decode GEMV library.
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels behind the C ABI declared in ``include/qgemv.h``.  Device arguments
+are torch CUDA (HIP) tensors or raw integer device pointers; host arguments
+of the reference quantizer are numpy arrays.  ``stream=None`` means torch's
+current stream on the current device.
+
+Importing this package does not load the library; the first call does, and
+raises ``QGLibraryMissing`` if it was not built
+(``python -m block_quantized_decode_qgemv_amd.build``).  There is no
+fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+import numpy as np
+
+__all__ = [
+    "FORMATS", "QG_MOE_RENORM", "QGError", "QGLibraryMissing", "lib_path", "load",
+    "qg_packed_size", "qg_codes_plane_size", "qg_block_size", "qgemv_workspace_size",
+    "qgemv", "qgemv_q8_0", "qgemv_q4_0", "qgemv_q4_1", "qgemv_q4k", "qgemv_q2k",
+    "qgemv_tern", "qgemv_bin", "qg_dequant", "qquant", "qpack_tern", "qpack_bin",
+    "moe_expert_ffn_workspace_size", "moe_expert_ffn", "qg_strerror", "qg_last_error",
+    "qg_version", "EXPORTED_SYMBOLS",
+]
+
+FORMATS = {"q8_0": 0, "q4_0": 1, "q4_1": 2, "q4_k": 3, "q2_k": 4, "tern": 5, "bin": 6}
+QG_MOE_RENORM = 1
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_NAME = "libqgemv.so"
+_lock = threading.Lock()
+_lib = None
+
+_i32, _i64, _u32, _sz, _vp, _cp = (ctypes.c_int, ctypes.c_int64, ctypes.c_uint, ctypes.c_size_t,
+                                   ctypes.c_void_p, ctypes.c_char_p)
+_GEMV_ARGS = [_vp, _vp, _vp, _i64, _i64, _i32, _vp, _sz, _vp]
+
+# name -> (restype, argtypes); the same set include/qgemv.h declares
+_SIGNATURES = {
+    "qg_packed_size": (_sz, [_i32, _i64, _i64]),
+    "qg_codes_plane_size": (_sz, [_i32, _i64, _i64]),
+    "qg_block_size": (_i32, [_i32]),
+    "qgemv_workspace_size": (_sz, [_i32, _i64, _i64, _i32]),
+    "qgemv": (_i32, [_i32] + _GEMV_ARGS),
+    "qgemv_q8_0": (_i32, _GEMV_ARGS),
+    "qgemv_q4_0": (_i32, _GEMV_ARGS),
+    "qgemv_q4_1": (_i32, _GEMV_ARGS),
+    "qgemv_q4k": (_i32, _GEMV_ARGS),
+    "qgemv_q2k": (_i32, _GEMV_ARGS),
+    "qgemv_tern": (_i32, _GEMV_ARGS),
+    "qgemv_bin": (_i32, _GEMV_ARGS),
+    "qg_dequant": (_i32, [_i32, _vp, _vp, _i64, _i64, _vp]),
+    "qquant": (_i32, [_i32, _vp, _i64, _i64, _vp, _i32]),
+    "qpack_tern": (_i32, [_vp, _vp, _i64, _i64, _vp]),
+    "qpack_bin": (_i32, [_vp, _vp, _i64, _i64, _vp]),
+    "moe_expert_ffn_workspace_size": (_sz, [_i32, _i32, _i32, _i32, _i32]),
+    "moe_expert_ffn": (_i32, [_i32, _vp, _vp, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _i32, _u32,
+                              _vp, _vp, _sz, _vp]),
+    "qg_strerror": (_cp, [_i32]),
+    "qg_last_error": (_cp, []),
+    "qg_version": (_cp, []),
+}
+EXPORTED_SYMBOLS = tuple(_SIGNATURES)
+
+
+class QGLibraryMissing(RuntimeError):
+    """libqgemv.so has not been built; there is no fallback."""
+
+
+class QGError(RuntimeError):
+    def __init__(self, code: int, func: str, detail: str):
+        self.code = code
+        self.func = func
+        self.detail = detail
+        super().__init__(f"{func} failed with {code} ({_strerror(code)}): {detail}")
+
+
+def lib_path() -> str:
+    return os.path.join(_HERE, _LIB_NAME)
+
+
+def load():
+    """Load (once) and return the ctypes handle of libqgemv.so."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    with _lock:
+        if _lib is None:
+            path = lib_path()
+            if not os.path.exists(path):
+                raise QGLibraryMissing(f"{path} is missing; build it with "
+                                       "`python -m block_quantized_decode_qgemv_amd.build`")
+            lib = ctypes.CDLL(path)
+            for name, (res, args) in _SIGNATURES.items():
+                fn = getattr(lib, name)
+                fn.restype = res
+                fn.argtypes = args
+            _lib = lib
+    return _lib
+
+
+def _strerror(code: int) -> str:
+    try:
+        return load().qg_strerror(code).decode()
+    except Exception:  # pragma: no cover - only while reporting another error
+        return "?"
+
+
+def _check(rc: int, func: str) -> None:
+    if rc != 0:
+        raise QGError(rc, func, load().qg_last_error().decode())
+
+
+def _fmt(fmt) -> int:
+    if isinstance(fmt, str):
+        return FORMATS[fmt.lower()]
+    return int(fmt)
+
+
+def _dev(t, dtype=None, name="tensor"):
+    """Device pointer of a torch CUDA tensor (checked) or a raw int pointer."""
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    if not getattr(t, "is_cuda", False):
+        raise TypeError(f"{name} must be a device (cuda/hip) tensor or an int device pointer")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must have dtype {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(stream):
+    if stream is None:
+        import torch
+
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _torch_dtypes():
+    import torch
+
+    return torch.float32, torch.uint8
+
+
+# -------------------------------------------------------------------- sizes
+
+def qg_packed_size(fmt, n: int, k: int) -> int:
+    return load().qg_packed_size(_fmt(fmt), n, k)
+
+
+def qg_codes_plane_size(fmt, n: int, k: int) -> int:
+    return load().qg_codes_plane_size(_fmt(fmt), n, k)
+
+
+def qg_block_size(fmt) -> int:
+    return load().qg_block_size(_fmt(fmt))
+
+
+def qgemv_workspace_size(fmt, n: int, k: int, b: int = 1) -> int:
+    return load().qgemv_workspace_size(_fmt(fmt), n, k, b)
+
+
+def moe_expert_ffn_workspace_size(t: int, e: int, h: int, i: int, top_k: int) -> int:
+    return load().moe_expert_ffn_workspace_size(t, e, h, i, top_k)
+
+
+def qg_strerror(code: int) -> str:
+    return load().qg_strerror(code).decode()
+
+
+def qg_last_error() -> str:
+    return load().qg_last_error().decode()
+
+
+def qg_version() -> str:
+    return load().qg_version().decode()
+
+
+# --------------------------------------------------------------------- GEMV
+
+def qgemv(fmt, w, x, y, n: int, k: int, b: int = 1, ws=None, ws_bytes: int = 0, stream=None) -> None:
+    """y[b][n] = sum_k W[n][k] x[b][k] on the device (see qgemv in qgemv.h)."""
+    f32, u8 = _torch_dtypes()
+    rc = load().qgemv(_fmt(fmt), _dev(w, u8, "w"), _dev(x, f32, "x"), _dev(y, f32, "y"), n, k, b,
+                      _dev(ws, None, "ws"), ws_bytes, _stream(stream))
+    _check(rc, "qgemv")
+
+
+def _named(cname, fmt):
+    def fn(w, x, y, n, k, b=1, ws=None, ws_bytes=0, stream=None):
+        f32, u8 = _torch_dtypes()
+        rc = getattr(load(), cname)(_dev(w, u8, "w"), _dev(x, f32, "x"), _dev(y, f32, "y"), n, k, b,
+                                    _dev(ws, None, "ws"), ws_bytes, _stream(stream))
+        _check(rc, cname)
+
+    fn.__name__ = cname
+    fn.__doc__ = f"qgemv with the {fmt} format (see {cname} in qgemv.h)."
+    return fn
+
+
+qgemv_q8_0 = _named("qgemv_q8_0", "q8_0")
+qgemv_q4_0 = _named("qgemv_q4_0", "q4_0")
+qgemv_q4_1 = _named("qgemv_q4_1", "q4_1")
+qgemv_q4k = _named("qgemv_q4k", "q4_k")
+qgemv_q2k = _named("qgemv_q2k", "q2_k")
+qgemv_tern = _named("qgemv_tern", "tern")
+qgemv_bin = _named("qgemv_bin", "bin")
+
+
+def qg_dequant(fmt, w, out, n: int, k: int, stream=None) -> None:
+    f32, u8 = _torch_dtypes()
+    rc = load().qg_dequant(_fmt(fmt), _dev(w, u8, "w"), _dev(out, f32, "out"), n, k, _stream(stream))
+    _check(rc, "qg_dequant")
+
+
+# ---------------------------------------------------- host quantizer/packers
+
+def qquant(fmt, w_host, n_threads: int | None = None) -> np.ndarray:
+    """fp32 [N, K] host array -> packed uint8 host array (see qquant in qgemv.h)."""
+    w = np.ascontiguousarray(w_host, dtype=np.float32)
+    if w.ndim != 2:
+        raise ValueError("w_host must be 2-D [N, K]")
+    n, k = w.shape
+    size = qg_packed_size(fmt, n, k)
+    out = np.empty(max(size, 1), dtype=np.uint8)
+    threads = n_threads if n_threads is not None else min(16, os.cpu_count() or 1)
+    rc = load().qquant(_fmt(fmt), w.ctypes.data, n, k, out.ctypes.data, threads)
+    _check(rc, "qquant")
+    return out[:size]
+
+
+def qpack_tern(codes, scale_bits) -> np.ndarray:
+    t = np.ascontiguousarray(codes, dtype=np.int8)
+    s = np.ascontiguousarray(scale_bits, dtype=np.uint16)
+    n, k = t.shape
+    size = qg_packed_size("tern", n, k)
+    out = np.empty(max(size, 1), dtype=np.uint8)
+    _check(load().qpack_tern(t.ctypes.data, s.ctypes.data, n, k, out.ctypes.data), "qpack_tern")
+    return out[:size]
+
+
+def qpack_bin(bits, scale_bits) -> np.ndarray:
+    bb = np.ascontiguousarray(bits, dtype=np.uint8)
+    s = np.ascontiguousarray(scale_bits, dtype=np.uint16)
+    n, k = bb.shape
+    size = qg_packed_size("bin", n, k)
+    out = np.empty(max(size, 1), dtype=np.uint8)
+    _check(load().qpack_bin(bb.ctypes.data, s.ctypes.data, n, k, out.ctypes.data), "qpack_bin")
+    return out[:size]
+
+
+# ---------------------------------------------------------------- MoE layer
+
+def moe_expert_ffn(fmt, w_gate_up, w_down, e: int, h: int, i: int, top_k: int, x, residual,
+                   router_logits, shared_gate_logit, t: int, out, workspace, ws_bytes: int,
+                   flags: int = 0, stream=None) -> None:
+    """Routed expert layer (see moe_expert_ffn in qgemv.h)."""
+    f32, u8 = _torch_dtypes()
+    rc = load().moe_expert_ffn(_fmt(fmt), _dev(w_gate_up, u8, "w_gate_up"), _dev(w_down, u8, "w_down"),
+                               e, h, i, top_k, _dev(x, f32, "x"), _dev(residual, f32, "residual"),
+                               _dev(router_logits, f32, "router_logits"),
+                               _dev(shared_gate_logit, f32, "shared_gate_logit"), t, flags,
+                               _dev(out, f32, "out"), _dev(workspace, None, "workspace"), ws_bytes,
+                               _stream(stream))
+    _check(rc, "moe_expert_ffn")

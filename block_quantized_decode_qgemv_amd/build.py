@@ -1,0 +1,64 @@
+"""Build libqgemv.so in-tree for gfx950.
+
+    python -m block_quantized_decode_qgemv_amd.build
+
+Device code: hipcc --offload-arch=gfx950 -O3, with packed fp32 instructions
+disabled.  Host reference quantizer: g++ -O2 -ffp-contract=off (IEEE fp32 in
+the order written, no contraction).  The library lands next to this file.
+"""
+from __future__ import annotations
+
+import os
+import subprocess
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+BUILD_DIR = os.path.join(PKG, "_build")
+LIB = os.path.join(PKG, "libqgemv.so")
+
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+ARCH = "gfx950"
+
+DEVICE_SOURCES = ["gemv.hip", "moe.hip"]
+HOST_SOURCES = ["host.cpp"]
+
+HIP_FLAGS = [
+    f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall",
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-I", INCLUDE, "-I", CSRC,
+]
+HOST_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-Wall", "-ffp-contract=off", "-fno-fast-math",
+              "-I", INCLUDE, "-I", CSRC, "-I", "/opt/rocm/include"]
+
+
+def _run(cmd, verbose):
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    subprocess.run(cmd, check=True)
+
+
+def build(verbose: bool = True) -> str:
+    os.makedirs(BUILD_DIR, exist_ok=True)
+    objs = []
+    for src in DEVICE_SOURCES:
+        path = os.path.join(CSRC, src)
+        if not os.path.exists(path):
+            continue
+        obj = os.path.join(BUILD_DIR, src + ".o")
+        _run([HIPCC, *HIP_FLAGS, "-c", path, "-o", obj], verbose)
+        objs.append(obj)
+    for src in HOST_SOURCES:
+        obj = os.path.join(BUILD_DIR, src + ".o")
+        _run(["g++", *HOST_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj], verbose)
+        objs.append(obj)
+    tmp = LIB + ".tmp"
+    _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp, "-lpthread"], verbose)
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    build(verbose="-q" not in sys.argv)

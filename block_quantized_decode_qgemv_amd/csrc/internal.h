@@ -1,0 +1,29 @@
+// Internal declarations shared by the host and device translation units of
+// libqgemv.so.  Not part of the public ABI (that is include/qgemv.h).
+#pragma once
+
+#include <cstddef>
+#include <cstdint>
+
+#include "qgemv.h"
+
+namespace qg {
+
+struct FormatInfo {
+    int block;       // weights per block (one meta entry)
+    int code_bytes;  // codes per block
+    int meta_bytes;  // meta per block
+};
+
+// nullptr for an unknown format
+const FormatInfo* format_info(int fmt);
+
+// Records a thread-local message and returns `code`.
+int fail(int code, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+void clear_error();
+
+// Host-side argument checks shared by the device entry points.
+int check_matrix(int fmt, int64_t N, int64_t K);
+bool aligned(const void* p, size_t a);
+
+}  // namespace qg

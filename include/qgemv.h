@@ -1,0 +1,205 @@
+/*
+ * qgemv.h -- C ABI of the block-quantized decode GEMV library (libqgemv.so)
+ * for AMD Instinct MI355X (gfx950).
+ *
+ * What is computed.  Handbook page "端侧推理：llama.cpp 与 GGUF、MLX、
+ * ExecuTorch", section "速度上限：带宽 ÷ 权重字节数" and its self-test answers:
+ * at batch-1 decode every output is the dot product of one quantized weight
+ * row with the activation vector, y = W x, and every weight is read once per
+ * token.  Batch B stacks activation rows: Y[b][n] = sum_k W[n][k] * X[b][k].
+ * The block formats are those of the same page, section "GGUF 的量化格式"
+ * (Q8_0, Q4_0, Q4_1, Q4_K), plus Q2_K, ternary weights in 2-bit fields and
+ * 1-bit sign weights from the low-bit README page's kernel table, and the
+ * Flash-MoE page's 2-bit experts.  The MoE layer follows the Flash-MoE page,
+ * sections "模型架构", "Metal 计算着色器" and "每层流水线".
+ *
+ * Conventions for every function:
+ *   - extern "C", returns int: QG_OK (0) or a negative QG_E* code, never
+ *     throws, never aborts.  qg_last_error() then holds a thread-local
+ *     message for the failing call.
+ *   - Arguments are validated on the host before anything is launched; on
+ *     a validation error no output is touched.
+ *   - Device functions are asynchronous on `stream` (a hipStream_t; NULL is
+ *     the null stream).  A launch failure returns QG_EHIP; a fault during
+ *     execution surfaces at the caller's next synchronisation.
+ *   - All buffers are caller-owned.  The library allocates nothing, keeps no
+ *     pointer after returning, and has no global state or environment-driven
+ *     behaviour, so it is thread-safe.  Buffers must stay alive until the
+ *     stream work that uses them completes.
+ *
+ * Packed matrix layout (one [N][K] matrix, format f with block size bs):
+ *   [codes plane][meta plane], codes plane = N*(K/bs)*code_bytes bytes,
+ *   meta plane = N*(K/bs)*meta_bytes bytes, both row-major over (row, block);
+ *   total qg_packed_size() = N*K*bpw/8 exactly.
+ *     format  bs   code B  meta B  bpw    meta entry
+ *     Q8_0    32   32      2       8.5    fp16 d; codes int8
+ *     Q4_0    32   16      2       4.5    fp16 d (signed); nibble = code + 8
+ *     Q4_1    32   16      4       5.0    fp16 d, fp16 m
+ *     Q4_K    256  128     16      4.5    96-bit field of 8 pairs s_j|t_j<<6
+ *     Q2_K    256  64      16      2.5      (12 bits each, LSB first), then
+ *                                           fp16 d, fp16 dmin
+ *     TERN    128  32      2       2.125  fp16 scale; 2-bit field = t + 1
+ *     BIN     128  16      2       1.125  fp16 scale; bit 1 = +1, 0 = -1
+ *   Nibble i of a block sits in byte i>>1 (low nibble for even i); 2-bit field
+ *   i in byte i>>2 at bits 2*(i&3); bit i in byte i>>3 at bit i&7.  All
+ *   multi-byte values are little-endian.  Decoded weights:
+ *     Q8_0 q*d; Q4_0 (n-8)*d; Q4_1 n*d+m; Q4_K/Q2_K n*(s_j*d) - t_j*dmin;
+ *     TERN (f-1)*scale; BIN (2*bit-1)*scale.
+ */
+#ifndef QGEMV_H
+#define QGEMV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    QG_Q8_0 = 0,
+    QG_Q4_0 = 1,
+    QG_Q4_1 = 2,
+    QG_Q4_K = 3,
+    QG_Q2_K = 4,
+    QG_TERN = 5,
+    QG_BIN = 6
+} qg_format;
+
+enum {
+    QG_OK = 0,
+    QG_EINVAL = -1,      /* null pointer, bad enum, non-finite quantizer input */
+    QG_ESHAPE = -2,      /* N < 1, K not a positive multiple of the block, ... */
+    QG_EALIGN = -3,      /* a pointer misses its required alignment            */
+    QG_ERANGE = -4,      /* B out of range, a scale overflowing fp16, ...      */
+    QG_EHIP = -5,        /* a HIP launch or runtime call failed                */
+    QG_EUNSUPPORTED = -6 /* a valid request this build does not implement      */
+};
+
+/* Flags for moe_expert_ffn. */
+#define QG_MOE_RENORM 1u /* divide the top-K routing weights by their sum */
+
+/* Largest batch (activation rows) one GEMV call accepts. */
+#define QG_MAX_BATCH 8
+
+/* ------------------------------------------------------------------ sizes */
+
+/* Bytes of a packed [N][K] matrix (== N*K*bpw/8), or 0 if the format is
+ * unknown, N < 1 or K is not a positive multiple of the block size. */
+size_t qg_packed_size(int fmt, int64_t N, int64_t K);
+
+/* Bytes of the codes plane, i.e. the offset of the meta plane (0 if invalid). */
+size_t qg_codes_plane_size(int fmt, int64_t N, int64_t K);
+
+/* Weights per block (32, 256 or 128) or 0 for an unknown format. */
+int qg_block_size(int fmt);
+
+/* ------------------------------------------------------------------- GEMV */
+
+/* Device scratch the GEMV needs, in bytes (0 means ws may be NULL). */
+size_t qgemv_workspace_size(int fmt, int64_t N, int64_t K, int B);
+
+/* Y[b][n] = sum_k W[n][k] * X[b][k] for b < B, n < N, in fp32 with fp32
+ * accumulation (handbook page, "速度上限：带宽 ÷ 权重字节数": y = W x).
+ *   w   DEVICE, packed [N][K] matrix of format fmt, 16-byte aligned.
+ *   x   DEVICE, fp32 [B][K] row-major, 16-byte aligned.
+ *   y   DEVICE, fp32 [B][N] row-major, 4-byte aligned; overwritten.
+ *   N >= 1 (any value); K a positive multiple of the block size; 1 <= B <= 8.
+ *   ws  DEVICE scratch of >= qgemv_workspace_size() bytes, 16-byte aligned,
+ *       or NULL when that size is 0.
+ * Accuracy: |y - y_exact| <= 2e-5 * sum_k |W[n][k] X[b][k]| + 1e-7, where
+ * y_exact is the exact sum over the decoded weights.  Results are
+ * deterministic: the same inputs give the same bits on every call.
+ * Errors: QG_EINVAL (null w/x/y, unknown fmt), QG_ESHAPE, QG_ERANGE (B),
+ * QG_EALIGN, QG_EHIP. */
+int qgemv(int fmt, const void* w, const float* x, float* y, int64_t N, int64_t K, int B,
+          void* ws, size_t ws_bytes, void* stream);
+
+/* The same call with the format fixed by the name. */
+int qgemv_q8_0(const void* w, const float* x, float* y, int64_t N, int64_t K, int B,
+               void* ws, size_t ws_bytes, void* stream);
+int qgemv_q4_0(const void* w, const float* x, float* y, int64_t N, int64_t K, int B,
+               void* ws, size_t ws_bytes, void* stream);
+int qgemv_q4_1(const void* w, const float* x, float* y, int64_t N, int64_t K, int B,
+               void* ws, size_t ws_bytes, void* stream);
+int qgemv_q4k(const void* w, const float* x, float* y, int64_t N, int64_t K, int B,
+              void* ws, size_t ws_bytes, void* stream);
+int qgemv_q2k(const void* w, const float* x, float* y, int64_t N, int64_t K, int B,
+              void* ws, size_t ws_bytes, void* stream);
+int qgemv_tern(const void* w, const float* x, float* y, int64_t N, int64_t K, int B,
+               void* ws, size_t ws_bytes, void* stream);
+int qgemv_bin(const void* w, const float* x, float* y, int64_t N, int64_t K, int B,
+              void* ws, size_t ws_bytes, void* stream);
+
+/* ----------------------------------------------------------------- dequant */
+
+/* Device dequantization of a packed [N][K] matrix to fp32 out[N][K]
+ * (row-major, 4-byte aligned), with the decoded-weight formulas above.
+ * Every value is bit-exact: each product is exact in fp32 and the only
+ * rounding is Q4_1's "+m" and the K-quants' "-t*dmin".  Same pointer rules
+ * and errors as qgemv. */
+int qg_dequant(int fmt, const void* w, float* out, int64_t N, int64_t K, void* stream);
+
+/* ------------------------------------------------------ reference quantizer */
+
+/* Host quantizer: fp32 w_host[N][K] (row-major) -> packed bytes in out_host
+ * (qg_packed_size() bytes).  Q8_0, Q4_0, Q4_1 follow the handbook page's
+ * quantizer listing (section "GGUF 的量化格式"), Q4_K its simplified K-quant,
+ * Q2_K the same construction with 2-bit codes; every scale and min is stored
+ * as fp16 (round to nearest even) and the codes are computed against the
+ * stored values; rounding is half-to-even; a zero scale gives the zero code.
+ * Signed zeros in the input are treated as +0.  n_threads <= 0 means 1.
+ * Both pointers are HOST memory.  Errors: QG_EINVAL (null, non-finite input,
+ * fmt is TERN/BIN -- use qpack_tern/qpack_bin), QG_ESHAPE, QG_ERANGE (a
+ * scale or min overflows fp16; out_host is then unspecified). */
+int qquant(int fmt, const float* w_host, int64_t N, int64_t K, void* out_host, int n_threads);
+
+/* Host packers for the trained low-bit formats (the pages give no
+ * ternarizer/binarizer): t[N][K] int8 in {-1,0,1} or bits[N][K] uint8 in
+ * {0,1}, plus scale_f16[N][K/128] fp16 bit patterns -> packed bytes.
+ * Errors: QG_EINVAL (null pointer, a code out of range), QG_ESHAPE. */
+int qpack_tern(const int8_t* t, const uint16_t* scale_f16, int64_t N, int64_t K, void* out_host);
+int qpack_bin(const uint8_t* bits, const uint16_t* scale_f16, int64_t N, int64_t K, void* out_host);
+
+/* --------------------------------------------------------------- MoE layer */
+
+/* Routed expert layer for T decode tokens (Flash-MoE page, sections "模型架构",
+ * "Metal 计算着色器", "每层流水线"; the routed matmul semantics of the EPM
+ * README, section "正確性").  For each token t:
+ *   p = softmax(router_logits[t]);  e_1..e_K = the top_k largest p (ties to
+ *   the lower expert index);  w_k = p[e_k] (divided by sum_k p[e_k] when
+ *   QG_MOE_RENORM is set);  for each selected expert e and the shared expert
+ *   (index E): h = silu(W_gate,e x_t) * (W_up,e x_t), o_e = W_down,e h;
+ *   out[t] = residual[t] + sum_k w_k o_{e_k} + sigmoid(shared_gate_logit[t]) o_E.
+ *   fmt        QG_Q4_K or QG_Q2_K.
+ *   w_gate_up  DEVICE, (E+1) consecutive packed [2I][H] matrices whose row 2i
+ *              is gate row i and row 2i+1 is up row i; expert E is shared.
+ *   w_down     DEVICE, (E+1) consecutive packed [H][I] matrices.
+ *   x, residual  DEVICE fp32 [T][H] (residual may alias x); out DEVICE fp32
+ *              [T][H] (must not alias x or residual).
+ *   router_logits DEVICE fp32 [T][E]; shared_gate_logit DEVICE fp32 [T].
+ *   workspace  DEVICE scratch >= moe_expert_ffn_workspace_size() bytes,
+ *              16-byte aligned.
+ *   1 <= T <= 8, 1 <= top_k <= min(E, 8), 1 <= E <= 4096, H and I positive
+ *   multiples of 256.  Deterministic (fixed-order sums, no float atomics).
+ * Errors: QG_EINVAL, QG_ESHAPE, QG_ERANGE, QG_EALIGN, QG_EHIP. */
+size_t moe_expert_ffn_workspace_size(int T, int E, int H, int I, int top_k);
+int moe_expert_ffn(int fmt, const void* w_gate_up, const void* w_down, int E, int H, int I, int top_k,
+                   const float* x, const float* residual, const float* router_logits,
+                   const float* shared_gate_logit, int T, unsigned flags, float* out,
+                   void* workspace, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------ errors */
+
+/* Static description of an error code. */
+const char* qg_strerror(int code);
+/* Thread-local detail of the last failing call on this thread ("" if none). */
+const char* qg_last_error(void);
+/* Library version string. */
+const char* qg_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QGEMV_H */

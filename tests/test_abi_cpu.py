@@ -1,0 +1,116 @@
+"""Host-side checks of the C ABI (no GPU needed): the library loads, exports
+every function include/qgemv.h declares, validates arguments before any
+launch, and reports sizes that match the oracle's layout."""
+import os
+import re
+import subprocess
+
+import numpy as np
+import pytest
+
+import block_quantized_decode_qgemv_amd as qg
+from oracle import formats as OF
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "qgemv.h")
+
+
+def _declared():
+    text = open(HEADER, encoding="utf-8").read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*([a-z_0-9]+)\s*\(", text, flags=re.M))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = qg.load()
+    declared = _declared()
+    assert declared == set(qg.EXPORTED_SYMBOLS)
+    for name in declared:
+        assert hasattr(lib, name), name
+    out = subprocess.run(["nm", "-D", "--defined-only", qg.lib_path()], capture_output=True, text=True, check=True)
+    exported = {line.split()[-1] for line in out.stdout.splitlines() if " T " in line}
+    assert declared <= exported
+
+
+def test_version_and_strerror():
+    assert "gfx950" in qg.qg_version()
+    for code in (0, -1, -2, -3, -4, -5, -6):
+        assert qg.qg_strerror(code)
+
+
+@pytest.mark.parametrize("fmt", OF.FORMATS)
+def test_sizes_match_oracle(fmt):
+    for n, k in ((1, 256), (3, 1024), (4096, 4096), (14336, 4096), (4096, 14336)):
+        assert qg.qg_packed_size(fmt, n, k) == OF.packed_size(fmt, n, k)
+        assert qg.qg_codes_plane_size(fmt, n, k) == OF.codes_plane_size(fmt, n, k)
+    assert qg.qg_block_size(fmt) == OF.SPECS[fmt].block
+    assert qg.qg_packed_size(fmt, 0, 256) == 0
+    assert qg.qg_packed_size(fmt, 4, OF.SPECS[fmt].block + 1) == 0
+    assert qg.qg_packed_size(99, 4, 256) == 0
+
+
+# The cases below hand the library fake (aligned, non-null) device pointers
+# with arguments that must be rejected before any launch.  They are host-logic
+# tests for a machine without a GPU and are skipped where a GPU is present.
+
+def _gpu_present():
+    try:
+        import torch
+
+        return torch.cuda.is_available()
+    except Exception:
+        return False
+
+
+nogpu = pytest.mark.skipif(_gpu_present(), reason="validation-only tests use fake device pointers")
+
+P = 0x10000  # fake 16-byte aligned pointer value
+
+
+@nogpu
+@pytest.mark.parametrize("args,code", [
+    (dict(fmt=3, n=0, k=256, b=1), -2),          # N < 1
+    (dict(fmt=3, n=4, k=128, b=1), -2),          # K not a multiple of 256
+    (dict(fmt=0, n=4, k=48, b=1), -2),           # K not a multiple of 32
+    (dict(fmt=3, n=4, k=256, b=0), -4),          # B < 1
+    (dict(fmt=3, n=4, k=256, b=9), -4),          # B > 8
+    (dict(fmt=7, n=4, k=256, b=1), -1),          # unknown format
+    (dict(fmt=-1, n=4, k=256, b=1), -1),
+    (dict(fmt=3, n=4, k=256, b=1, w=0), -1),     # null w
+    (dict(fmt=3, n=4, k=256, b=1, x=0), -1),     # null x
+    (dict(fmt=3, n=4, k=256, b=1, y=0), -1),     # null y
+    (dict(fmt=3, n=4, k=256, b=1, w=P + 8), -3),  # misaligned w
+    (dict(fmt=3, n=4, k=256, b=1, x=P + 4), -3),  # misaligned x
+    (dict(fmt=3, n=4, k=256, b=1, y=P + 2), -3),  # misaligned y
+])
+def test_gemv_validation(args, code):
+    lib = qg.load()
+    rc = lib.qgemv(args["fmt"], args.get("w", P), args.get("x", P), args.get("y", P),
+                   args["n"], args["k"], args["b"], None, 0, None)
+    assert rc == code, qg.qg_last_error()
+    assert qg.qg_last_error()
+
+
+@nogpu
+def test_dequant_validation():
+    lib = qg.load()
+    assert lib.qg_dequant(3, P, P, 0, 256, None) == -2
+    assert lib.qg_dequant(3, None, P, 4, 256, None) == -1
+    assert lib.qg_dequant(3, P + 4, P, 4, 256, None) == -3
+
+
+def test_binding_rejects_host_tensors():
+    import torch
+
+    w = torch.zeros(qg.qg_packed_size("q4_k", 4, 256), dtype=torch.uint8)
+    x = torch.zeros(1, 256)
+    y = torch.zeros(1, 4)
+    with pytest.raises(TypeError):
+        qg.qgemv_q4k(w, x, y, 4, 256)
+
+
+def test_library_missing_is_loud(tmp_path, monkeypatch):
+    monkeypatch.setattr(qg, "_lib", None)
+    monkeypatch.setattr(qg, "_HERE", str(tmp_path))
+    with pytest.raises(qg.QGLibraryMissing):
+        qg.load()

@@ -1,0 +1,181 @@
+"""GPU parity of the GEMV and dequant kernels against the oracle, through the
+C ABI.  Inputs come from the seeded generators; packed weights and expected
+values come from the oracle (or, at full size, from the C++ quantizer whose
+sampled rows are first checked byte-for-byte against the oracle's)."""
+import functools
+
+import numpy as np
+import pytest
+
+import block_quantized_decode_qgemv_amd as qg
+import workloads
+from oracle import formats as OF
+from oracle import gemv as OG
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+def dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).to("cuda")
+
+
+def make_blocks(fmt, n, k, seed=0, tid=0):
+    if fmt == "tern":
+        return OF.tern_from_codes(workloads.ternary_codes(n, k, seed, tid),
+                                  workloads.scale_bits_f16((n, k // 128), seed, tid + 1))
+    if fmt == "bin":
+        return OF.bin_from_codes(workloads.binary_codes(n, k, seed, tid),
+                                 workloads.scale_bits_f16((n, k // 128), seed, tid + 1))
+    return OF.quantize(fmt, workloads.student_t_weights(n, k, seed, tid))
+
+
+def run_gemv(fmt, packed, x, n, k):
+    b = x.shape[0]
+    w_d = dev(packed)
+    x_d = dev(x)
+    y_d = torch.full((b, n), float("nan"), device="cuda")
+    qg.qgemv(fmt, w_d, x_d, y_d, n, k, b)
+    torch.cuda.synchronize()
+    return y_d.cpu().numpy()
+
+
+def assert_parity(y, w_deq, x, label):
+    ok, ratio, idx = OG.check(y, w_deq, x)
+    assert ok, f"{label}: worst |err|/tol = {ratio:.3g} at {idx}"
+
+
+SHAPES = [(1, 1), (3, 2), (67, 4), (130, 16), (9, 56)]  # (N, K in blocks of 256)
+
+
+@pytest.mark.parametrize("fmt", OF.FORMATS)
+@pytest.mark.parametrize("n,kb", SHAPES)
+def test_dequant_bit_exact(fmt, n, kb):
+    k = 256 * kb
+    blk = make_blocks(fmt, n, k, seed=1, tid=n)
+    packed = OF.pack(fmt, blk)
+    out = torch.full((n, k), float("nan"), device="cuda")
+    qg.qg_dequant(fmt, dev(packed), out, n, k)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    want = OF.dequant(fmt, blk)
+    np.testing.assert_array_equal(got.view(np.uint32), want.view(np.uint32))
+
+
+@pytest.mark.parametrize("fmt", OF.FORMATS)
+def test_dequant_subnormal_and_signed_scales(fmt):
+    """fp16 subnormal and negative scales must decode exactly (no flushing)."""
+    n, k = 4, 512
+    blk = make_blocks(fmt, n, k, seed=2)
+    blk["d"] = blk["d"].copy()
+    blk["d"][0] = 0x0001          # smallest fp16 subnormal
+    blk["d"][1] = 0x03FF          # largest fp16 subnormal
+    blk["d"][2] = blk["d"][2] | 0x8000  # negative scale
+    if "dmin" in blk:
+        blk["dmin"] = blk["dmin"].copy()
+        blk["dmin"][3] = 0x0200
+    if "m" in blk:
+        blk["m"] = blk["m"].copy()
+        blk["m"][3] = 0x8001
+    packed = OF.pack(fmt, blk)
+    out = torch.empty((n, k), device="cuda")
+    qg.qg_dequant(fmt, dev(packed), out, n, k)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(out.cpu().numpy().view(np.uint32), OF.dequant(fmt, blk).view(np.uint32))
+
+
+@pytest.mark.parametrize("fmt", OF.FORMATS)
+@pytest.mark.parametrize("b", [1, 2, 4, 8])
+@pytest.mark.parametrize("n,kb", SHAPES)
+def test_gemv_parity(fmt, b, n, kb):
+    k = 256 * kb
+    blk = make_blocks(fmt, n, k, seed=3, tid=7 * n + kb)
+    x = workloads.normal((b, k), 3, 1000 + b)
+    y = run_gemv(fmt, OF.pack(fmt, blk), x, n, k)
+    assert_parity(y, OF.dequant(fmt, blk), x, f"{fmt} B={b} N={n} K={k}")
+
+
+@pytest.mark.parametrize("fmt", ["q8_0", "q4_0", "q4_1"])
+@pytest.mark.parametrize("k", [32, 96, 160, 4064])
+def test_gemv_short_blocks(fmt, k):
+    """32-weight formats at K that is not a multiple of 256 (ragged chunk tail)."""
+    n = 37
+    blk = make_blocks(fmt, n, k, seed=4, tid=k)
+    x = workloads.normal((3, k), 4, k)
+    y = run_gemv(fmt, OF.pack(fmt, blk), x, n, k)
+    assert_parity(y, OF.dequant(fmt, blk), x, f"{fmt} K={k}")
+
+
+@pytest.mark.parametrize("fmt", OF.FORMATS)
+def test_gemv_integer_exact(fmt):
+    """Power-of-two scales and small-integer activations: every product and
+    partial sum is exact in fp32, so the result must equal the oracle exactly."""
+    g = np.random.default_rng(6)
+    n, k = 33, 1024
+    blk = make_blocks(fmt, n, k, seed=6)
+    blk["d"] = np.full_like(blk["d"], 0x3C00)      # 1.0
+    if "dmin" in blk:
+        blk["dmin"] = np.full_like(blk["dmin"], 0x3800)  # 0.5
+    if "m" in blk:
+        blk["m"] = np.full_like(blk["m"], 0xC000)  # -2.0
+    x = g.integers(-3, 4, size=(2, k)).astype(np.float32)
+    y = run_gemv(fmt, OF.pack(fmt, blk), x, n, k)
+    want = OG.gemv_ref(OF.dequant(fmt, blk), x)
+    np.testing.assert_array_equal(y.astype(np.float64), want)
+
+
+@pytest.mark.parametrize("fmt", OF.FORMATS)
+def test_gemv_deterministic(fmt):
+    n, k = 515, 4096
+    blk = make_blocks(fmt, n, k, seed=7)
+    x = workloads.normal((1, k), 7)
+    w_d, x_d = dev(OF.pack(fmt, blk)), dev(x)
+    y1 = torch.empty((1, n), device="cuda")
+    y2 = torch.empty((1, n), device="cuda")
+    qg.qgemv(fmt, w_d, x_d, y1, n, k, 1)
+    qg.qgemv(fmt, w_d, x_d, y2, n, k, 1)
+    torch.cuda.synchronize()
+    assert torch.equal(y1.view(torch.int32), y2.view(torch.int32))
+
+
+def test_single_q4k_gemv_seed0():
+    """The single Q4_K GEMV case: W 1024x1024 then x from one default_rng(0)."""
+    w, x = workloads.single_q4k_case(1024, 1024, seed=0)
+    blk = OF.quantize("q4_k", w)
+    packed = OF.pack("q4_k", blk)
+    np.testing.assert_array_equal(qg.qquant("q4_k", w), packed)
+    y = run_gemv("q4_k", packed, x, 1024, 1024)
+    assert_parity(y, OF.dequant("q4_k", blk), x, "q4_k 1024x1024 seed 0")
+
+
+@functools.lru_cache(maxsize=2)
+def full_weights(n, k):
+    return workloads.student_t_weights(n, k, seed=0, tensor_id=n)
+
+
+@pytest.mark.parametrize("n,k", [(4096, 4096), (14336, 4096)])
+@pytest.mark.parametrize("fmt", ["q8_0", "q4_0", "q4_1", "q4_k"])
+@pytest.mark.parametrize("b", [1, 8])
+def test_full_size_sampled_rows(fmt, n, k, b):
+    """Full-size GEMV (the launch the bench times); the device buffer comes from
+    the C++ quantizer, and sampled rows are re-quantized by the oracle, checked
+    byte-for-byte, and used for the expected outputs."""
+    w = full_weights(n, k)
+    packed = qg.qquant(fmt, w)
+    x = workloads.normal((b, k), 0, 50 + b)
+    y = run_gemv(fmt, packed, x, n, k)
+    rows = np.unique(np.concatenate([[0, 1, n - 1], np.random.default_rng(n + b).choice(n, 253, replace=False)]))
+    sub = OF.quantize(fmt, w[rows])
+    spec = OF.SPECS[fmt]
+    cpr = (k // spec.block) * spec.code_bytes
+    mpr = (k // spec.block) * spec.meta_bytes
+    cp = OF.codes_plane_size(fmt, n, k)
+    sub_packed = OF.pack(fmt, sub)
+    scp = OF.codes_plane_size(fmt, len(rows), k)
+    for i, r in enumerate(rows):
+        np.testing.assert_array_equal(packed[r * cpr:(r + 1) * cpr], sub_packed[i * cpr:(i + 1) * cpr])
+        np.testing.assert_array_equal(packed[cp + r * mpr:cp + (r + 1) * mpr],
+                                      sub_packed[scp + i * mpr:scp + (i + 1) * mpr])
+    assert_parity(y[:, rows], OF.dequant(fmt, sub), x, f"{fmt} {n}x{k} B={b}")
+    assert np.all(np.isfinite(y))
