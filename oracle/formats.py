@@ -35,10 +35,22 @@ R7  tern: field f = t + 1 for t in {-1, 0, +1} (3 never emitted); bin: bit 1
     means +1.  One fp16 scale per 128 weights for both.  The pages give no
     ternarizer or binarizer (those models are trained so), so these two
     "quantizers" pack given codes and scales exactly.
+R8  The pages fix block contents, not where blocks sit in memory; rows are
+    interleaved in groups of 16 (see the plane layout below).
 
-Plane layout of one packed [N][K] matrix: the codes plane (N * K/bs blocks of
-``code_bytes``, row-major over (row, block)) followed by the meta plane
-(N * K/bs entries of ``meta_bytes``, same order).  Total = N*K*bpw/8 bytes.
+Plane layout of one packed [N][K] matrix (reading R8): the codes plane
+followed by the meta plane.  Each plane starts from the row-major byte image
+of its rows (row n = its K/bs blocks' code bytes, resp. meta bytes, in block
+order) and interleaves it by groups of 16 rows: the rows of a group
+(n_g = min(16, N - 16g) of them) are cut into 16-byte units, and unit u of
+every row of the group is stored contiguously (row order), unit after unit;
+a row whose byte count is not a multiple of 16 keeps its short last unit
+(length L), and those short units follow, row after row.  So byte i of unit u
+of row r in group g sits at  group_base + u*n_g*16 + r*len(u) + i,  with
+len(u) = 16 except the short last unit.  Total = N*K*bpw/8 bytes.  This is the
+low-bit README page's repacking of rows for the dot-product lanes (kernel
+table, Q2_K row interleave), set to 16 rows: one 16-lane quarter of a gfx950
+wave reads one unit of 16 rows as 256 contiguous bytes.
 
 Parity: Q8_0, Q4_0, Q4_1, Q4_K are pinned by the page's printed error table
 (through ``page_listing``), by the bits/weight closed forms in the listing and
@@ -376,6 +388,40 @@ def _le_u16(by) -> np.ndarray:
     return (by[..., 0] | (by[..., 1] << 8)).astype(np.uint16)
 
 
+ROW_GROUP = 16
+UNIT = 16
+
+
+def interleave_rows(plane) -> np.ndarray:
+    """Row-major [N, row_bytes] plane -> the 16-row interleaved byte order."""
+    plane = np.asarray(plane, dtype=np.uint8)
+    n, rb = plane.shape
+    units, rem = divmod(rb, UNIT)
+    out = []
+    for g0 in range(0, n, ROW_GROUP):
+        rows = plane[g0:g0 + ROW_GROUP]
+        ng = rows.shape[0]
+        out.append(rows[:, :units * UNIT].reshape(ng, units, UNIT).transpose(1, 0, 2).reshape(-1))
+        out.append(rows[:, units * UNIT:].reshape(-1))
+    return np.concatenate(out) if out else np.zeros(0, np.uint8)
+
+
+def deinterleave_rows(buf, n: int, rb: int) -> np.ndarray:
+    """Inverse of ``interleave_rows``: bytes -> row-major [n, rb]."""
+    buf = np.asarray(buf, dtype=np.uint8).reshape(-1)
+    units, rem = divmod(rb, UNIT)
+    plane = np.empty((n, rb), dtype=np.uint8)
+    pos = 0
+    for g0 in range(0, n, ROW_GROUP):
+        ng = min(ROW_GROUP, n - g0)
+        full = ng * units * UNIT
+        plane[g0:g0 + ng, :units * UNIT] = buf[pos:pos + full].reshape(units, ng, UNIT).transpose(1, 0, 2).reshape(ng, -1)
+        pos += full
+        plane[g0:g0 + ng, units * UNIT:] = buf[pos:pos + ng * rem].reshape(ng, rem)
+        pos += ng * rem
+    return plane
+
+
 def pack(fmt: str, blk: dict) -> np.ndarray:
     """Block representation -> packed bytes (codes plane then meta plane)."""
     if fmt == "q8_0":
@@ -401,8 +447,10 @@ def pack(fmt: str, blk: dict) -> np.ndarray:
         meta = _u16_le(blk["d"])
     else:
         raise KeyError(fmt)
-    return np.concatenate([np.ascontiguousarray(codes).reshape(-1),
-                           np.ascontiguousarray(meta).reshape(-1)]).astype(np.uint8)
+    n = codes.shape[0]
+    codes = np.ascontiguousarray(codes).reshape(n, -1)
+    meta = np.ascontiguousarray(meta).reshape(n, -1)
+    return np.concatenate([interleave_rows(codes), interleave_rows(meta)]).astype(np.uint8)
 
 
 def unpack(fmt: str, buf, n: int, k: int) -> dict:
@@ -413,8 +461,8 @@ def unpack(fmt: str, buf, n: int, k: int) -> dict:
         raise ValueError("buffer size does not match the format and shape")
     nb = k // spec.block
     cp = codes_plane_size(fmt, n, k)
-    codes = buf[:cp].reshape(n, nb * spec.code_bytes)
-    meta = buf[cp:].reshape(n, nb, spec.meta_bytes)
+    codes = deinterleave_rows(buf[:cp], n, nb * spec.code_bytes)
+    meta = deinterleave_rows(buf[cp:], n, nb * spec.meta_bytes).reshape(n, nb, spec.meta_bytes)
     if fmt == "q8_0":
         return {"d": _le_u16(meta), "q": codes.view(np.int8).copy()}
     if fmt == "q4_0":

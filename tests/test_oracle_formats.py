@@ -208,6 +208,26 @@ def test_nibble_and_crumb_order():
     assert list(buf[:2]) == [0b0000_1001, 0b0000_0010]
 
 
+def test_row_interleave_positions():
+    """Hand-computed positions of the 16-row interleave (reading R8)."""
+    n, rb = 35, 40  # two full groups + 3 rows; 2 full units + an 8-byte short unit per row
+    plane = (np.arange(n * rb) % 251).astype(np.uint8).reshape(n, rb)
+    buf = F.interleave_rows(plane)
+    assert buf.size == n * rb
+    # group 0: unit 0 of rows 0..15, then unit 1 of rows 0..15, then short units
+    np.testing.assert_array_equal(buf[0:16], plane[0, 0:16])
+    np.testing.assert_array_equal(buf[16:32], plane[1, 0:16])
+    np.testing.assert_array_equal(buf[16 * 16:16 * 17], plane[0, 16:32])
+    np.testing.assert_array_equal(buf[32 * 16:32 * 16 + 8], plane[0, 32:40])
+    np.testing.assert_array_equal(buf[32 * 16 + 8:32 * 16 + 16], plane[1, 32:40])
+    # group 2 (rows 32..34): starts after 32 full rows
+    g2 = 32 * rb
+    np.testing.assert_array_equal(buf[g2:g2 + 16], plane[32, 0:16])
+    np.testing.assert_array_equal(buf[g2 + 16:g2 + 32], plane[33, 0:16])
+    np.testing.assert_array_equal(buf[g2 + 3 * 32:g2 + 3 * 32 + 8], plane[32, 32:40])
+    np.testing.assert_array_equal(F.deinterleave_rows(buf, n, rb), plane)
+
+
 def test_kquant_meta_bytes():
     blk = _handbuilt_kquant(15, n_rows=1, n_sb=1)
     blk["d"][:] = 0x1234
