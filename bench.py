@@ -5,13 +5,15 @@ Headline (the JSON line's ``value``): effective weight GB/s of the Q4_K
 batch-1 GEMV on a 14336x4096 matrix (packed bytes / wall time), cold cache:
 each step runs on the next of >= 1 GiB of distinct packed copies, so no step
 finds its weights in the 256 MB last-level cache.  One step = one GEMV call.
+Steps are launched from a HIP graph holding one launch per copy, replayed
+back to back, so the figure is the kernels', not the host's launch rate (the
+eagerly launched rate is reported next to it).
 
 Also reported (in ``extra``): every GEMV of the four-format comparison
-(Q8_0/Q4_0/Q4_1/Q4_K x 4096x4096/14336x4096 x batch 1/8), the low-bit
-formats, the 8B-class decode step and the MoE expert layer, each timed with
-HIP events on the launch stream.
+(Q8_0/Q4_0/Q4_1/Q4_K x 4096x4096/14336x4096 x batch 1/8) and the low-bit
+formats, each timed the same way.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--quick]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--quick] [--no-cpu]
 
 Only one GPU is used; --gpus above 1 exits with a message.
 """
@@ -29,9 +31,9 @@ import numpy as np
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-HBM_PEAK_GBS = 8000.0         # MI355X published HBM3E bandwidth
+HBM_PEAK_GBS = 8000.0           # MI355X published HBM3E bandwidth
 DENSE_8B_BYTES = 3_925_868_544  # Q4_K bytes of the 8B-class step's linear weights
-COLD_BYTES = 1 << 30          # rotate over at least this many bytes of packed copies
+COLD_BYTES = 1 << 30            # rotate over at least this many bytes of packed copies
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "q4k_gemv_14336x4096_counters.txt")
 KERNEL_SOURCE = os.path.join(ROOT, "block_quantized_decode_qgemv_amd", "csrc", "gemv.hip")
 
@@ -65,11 +67,15 @@ def read_traffic():
 
 
 class Gemv:
-    """One GEMV configuration with rotating device copies of its packed weights."""
+    """One GEMV configuration with rotating device copies of its packed weights.
 
-    def __init__(self, torch, qg, fmt, n, k, b, seed, min_bytes):
+    Launches go straight to the C ABI with precomputed device pointers; timed
+    runs replay a HIP graph holding one launch per copy."""
+
+    def __init__(self, torch, qg, fmt, n, k, b, seed, min_bytes, stream):
         import workloads
 
+        self.torch = torch
         self.fmt, self.n, self.k, self.b = fmt, n, k, b
         if fmt == "tern":
             packed = qg.qpack_tern(workloads.ternary_codes(n, k, seed, 1),
@@ -85,28 +91,48 @@ class Gemv:
         self.w = [src] + [src.clone() for _ in range(copies - 1)]
         self.x = torch.from_numpy(workloads.normal((b, k), seed, 99)).to("cuda")
         self.y = torch.empty((b, n), device="cuda")
-        self.qg = qg
+        self.lib = qg.load()
+        self.fid = qg.FORMATS[fmt]
+        self.wp = [t.data_ptr() for t in self.w]
+        self.xp, self.yp = self.x.data_ptr(), self.y.data_ptr()
+        self.stream = stream
+        self.sp = stream.cuda_stream
         self.i = 0
+        self.graph = None
 
-    def step(self, stream):
-        self.qg.qgemv(self.fmt, self.w[self.i % len(self.w)], self.x, self.y, self.n, self.k, self.b,
-                      stream=stream)
+    def step(self):
+        rc = self.lib.qgemv(self.fid, self.wp[self.i % len(self.wp)], self.xp, self.yp, self.n, self.k, self.b,
+                            None, 0, self.sp)
+        if rc:
+            raise RuntimeError(f"qgemv failed with {rc}")
         self.i += 1
 
+    def capture(self) -> int:
+        """A graph with one launch per packed copy, in rotation order."""
+        torch = self.torch
+        self.i = 0
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=self.stream):
+            for _ in range(len(self.wp)):
+                self.step()
+        self.graph = g
+        return len(self.wp)
 
-def time_events(torch, fn, iters, warmup, stream):
-    """Average duration (s) of fn() from HIP event pairs around each call on `stream`."""
-    for _ in range(warmup):
-        fn()
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(iters)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(iters)]
-    for i in range(iters):
-        starts[i].record(stream)
-        fn()
-        ends[i].record(stream)
-    torch.cuda.synchronize()
-    times = sorted(s.elapsed_time(e) * 1e-3 for s, e in zip(starts, ends))
-    return float(np.mean(times)), float(np.median(times))
+    def replay(self, reps):
+        for _ in range(reps):
+            self.graph.replay()
+
+    def timed_replay(self, reps) -> float:
+        """Average per-launch time (s) over `reps` graph replays, from HIP events
+        recorded on the launch stream."""
+        torch = self.torch
+        a = torch.cuda.Event(enable_timing=True)
+        e = torch.cuda.Event(enable_timing=True)
+        a.record(self.stream)
+        self.replay(reps)
+        e.record(self.stream)
+        e.synchronize()
+        return a.elapsed_time(e) * 1e-3 / (reps * len(self.wp))
 
 
 def cpu_baseline(seconds=12.0):
@@ -135,22 +161,22 @@ def cpu_baseline(seconds=12.0):
         threads = max([1] + [int(p.get("num_threads", 1)) for p in threadpool_info()])
     except Exception:
         pass
-    return {"value": packed.size * reps / el / 1e9, "unit": "GB/s", "cores": threads, "kind": "oracle",
-            "sample": f"{reps} full Q4_K 14336x4096 batch-1 GEMVs (dequant + float64 matvec), {el:.1f} s"}
+    return {"value": round(packed.size * reps / el / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": f"{reps} full Q4_K 14336x4096 batch-1 GEMVs (unpack + dequant + float64 matvec), {el:.1f} s"}
 
 
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=2000)
-    ap.add_argument("--warmup", type=int, default=100)
+    ap.add_argument("--steps", type=int, default=4000)
+    ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--quick", action="store_true", help="headline only, no extra configs")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle cpu_baseline leg")
     ap.add_argument("--profile", choices=["gemv", "copy"], default=None,
                     help="run only the headline kernel (or a 1 GiB copy) a few times, for rocprofv3")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
+        print(f"bench.py: this build measures one GPU; --gpus {args.gpus} is not supported "
               "(the GEMV is measured on one GPU's share; no collectives are built)", file=sys.stderr)
         sys.exit(2)
 
@@ -162,7 +188,8 @@ def main():
         print("bench.py: no GPU visible", file=sys.stderr)
         sys.exit(1)
     qg.load()
-    stream = torch.cuda.current_stream()
+    stream = torch.cuda.Stream()  # graphs are captured on a non-default stream
+    torch.cuda.set_stream(stream)
 
     if args.profile == "copy":
         a = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
@@ -174,57 +201,73 @@ def main():
         return
 
     log("setup: Q4_K 14336x4096 batch 1, rotating copies")
-    head = Gemv(torch, qg, "q4_k", 14336, 4096, 1, 0, COLD_BYTES)
+    head = Gemv(torch, qg, "q4_k", 14336, 4096, 1, 0, COLD_BYTES, stream)
     if args.profile == "gemv":
-        for _ in range(20):
-            head.step(stream)
+        for _ in range(40):
+            head.step()
         torch.cuda.synchronize()
-        log("ran 20 headline GEMVs")
+        log("ran 40 headline GEMVs")
         return
 
-    for _ in range(args.warmup):
-        head.step(stream)
+    per = head.capture()
+    reps_warm = max(1, args.warmup // per)
+    reps = max(1, args.steps // per)
+    steps = reps * per
+    head.replay(reps_warm)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for _ in range(args.steps):
-        head.step(stream)
+    head.replay(reps)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    value = head.bytes * args.steps / wall / 1e9
-    log(f"headline: {value:.1f} GB/s over {args.steps} steps")
+    value = head.bytes * steps / wall / 1e9
+    log(f"headline: {value:.1f} GB/s over {steps} steps ({reps} graph replays of {per} launches)")
 
-    mean_s, med_s = time_events(torch, lambda: head.step(stream), min(args.steps, 1000), 10, stream)
-    achieved = head.bytes / mean_s / 1e9
+    t_launch = head.timed_replay(reps)
+    achieved = head.bytes / t_launch / 1e9
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": read_traffic()}
 
-    extra = {"headline_kernel_us_mean": round(mean_s * 1e6, 3), "headline_kernel_us_median": round(med_s * 1e6, 3),
+    # eager launches (host-issued one by one), for reference
+    for _ in range(50):
+        head.step()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    for _ in range(500):
+        head.step()
+    torch.cuda.synchronize()
+    eager_us = (time.perf_counter() - t1) / 500 * 1e6
+
+    extra = {"headline_us_per_launch": round(t_launch * 1e6, 3),
+             "headline_eager_us_per_launch": round(eager_us, 3),
              "tok_s_equiv": round(achieved * 1e9 / DENSE_8B_BYTES, 1)}
     if not args.quick:
+        def measure(fmt, n, k, b):
+            g = Gemv(torch, qg, fmt, n, k, b, 0, COLD_BYTES, stream)
+            g.capture()
+            g.replay(2)
+            t = g.timed_replay(max(2, 400 // len(g.wp)))
+            nbytes = g.bytes
+            del g
+            torch.cuda.empty_cache()
+            return t, nbytes
+
         rows = []
         for fmt in ("q8_0", "q4_0", "q4_1", "q4_k"):
             for n, k in ((4096, 4096), (14336, 4096)):
                 for b in (1, 8):
-                    g = Gemv(torch, qg, fmt, n, k, b, 0, COLD_BYTES)
-                    m, md = time_events(torch, lambda: g.step(stream), 200, 20, stream)
-                    rows.append({"fmt": fmt, "N": n, "K": k, "B": b, "us": round(m * 1e6, 2),
-                                 "GBps": round(g.bytes / m / 1e9, 1)})
-                    log(f"  {fmt} {n}x{k} B={b}: {m*1e6:.2f} us, {g.bytes/m/1e9:.1f} GB/s")
-                    del g
-                    torch.cuda.empty_cache()
+                    t, nbytes = measure(fmt, n, k, b)
+                    rows.append({"fmt": fmt, "N": n, "K": k, "B": b, "us": round(t * 1e6, 2),
+                                 "GBps": round(nbytes / t / 1e9, 1)})
+                    log(f"  {fmt} {n}x{k} B={b}: {t*1e6:.2f} us, {nbytes/t/1e9:.1f} GB/s")
         extra["four_formats"] = rows
         rows = []
         for fmt in ("tern", "bin", "q2_k"):
             for n, k in ((4096, 4096), (12288, 4096), (4096, 12288)):
                 for b in (1, 4):
-                    g = Gemv(torch, qg, fmt, n, k, b, 0, COLD_BYTES)
-                    m, _ = time_events(torch, lambda: g.step(stream), 200, 20, stream)
-                    rows.append({"fmt": fmt, "N": n, "K": k, "B": b, "us": round(m * 1e6, 2),
-                                 "GBps": round(g.bytes / m / 1e9, 1),
-                                 "Gweights_s": round(n * k * b / m / 1e9, 1)})
-                    log(f"  {fmt} {n}x{k} B={b}: {m*1e6:.2f} us, {g.bytes/m/1e9:.1f} GB/s")
-                    del g
-                    torch.cuda.empty_cache()
+                    t, nbytes = measure(fmt, n, k, b)
+                    rows.append({"fmt": fmt, "N": n, "K": k, "B": b, "us": round(t * 1e6, 2),
+                                 "GBps": round(nbytes / t / 1e9, 1), "Gweights_s": round(n * k * b / t / 1e9, 1)})
+                    log(f"  {fmt} {n}x{k} B={b}: {t*1e6:.2f} us, {nbytes/t/1e9:.1f} GB/s")
         extra["low_bit"] = rows
 
     line = {
@@ -232,16 +275,16 @@ def main():
         "value": round(value, 1),
         "unit": "GB/s",
         "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": round(wall / args.steps * 1e3, 6),
+        "steps": steps,
+        "warmup": reps_warm * per,
+        "ms_per_step": round(wall / steps * 1e3, 6),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "f32",
         "data": "synthetic",
         "config": {"workload": "Q4_K GEMV 14336x4096, batch 1, Student-t(5)*0.02 weights, N(0,1) x, "
-                               "cold cache (rotating >= 1 GiB of packed copies)",
+                               "cold cache (rotating >= 1 GiB of packed copies), HIP-graph launches",
                    "format": "q4_k", "N": 14336, "K": 4096, "batch": 1, "parallelism": "none"},
         "roofline": roofline,
         "extra": extra,

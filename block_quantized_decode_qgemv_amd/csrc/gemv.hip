@@ -7,23 +7,33 @@
 // same page, plus Q2_K, ternary-in-2-bit and 1-bit from the low-bit README
 // page's kernel table.
 //
-// Kernel shape (batch 1 is HBM-bound, so nothing here is a matrix-core
+// Memory layout (see qgemv.h): rows are interleaved in groups of 16; in each
+// group, 16-byte unit u of every row is contiguous.  This is the low-bit
+// README page's row repack for dot-product lanes, sized to a gfx950
+// quarter-wave: 16 lanes own the 16 rows of a group, so one quarter-wave load
+// reads 256 contiguous bytes and every activation value read from LDS is a
+// broadcast to all 16 rows.
+//
+// Kernel shape (batch 1 is HBM-bound; nothing here is a matrix-core
 // contraction):
-//   * a workgroup is 4 waves; it stages the activation slice x[B][k0:k0+KS]
-//     in LDS once, plus per-group column sums X (the offset terms of Q4_0,
-//     Q4_1, the K-quants and the low-bit formats are applied once per group
-//     as scale * X instead of once per weight);
-//   * each wave owns 64/LPR lane groups of R rows; lane sl of a group walks
-//     the 16-byte code chunks sl, sl+LPR, ... of its rows, so one wave load
-//     instruction reads LPR*16 contiguous bytes of every row (128-bit
-//     coalesced streaming), and every x value read from LDS feeds R rows;
-//   * codes are decoded in registers (mask/shift, byte -> float convert) and
-//     multiplied in fp32; scales are decoded once per chunk and applied to
-//     the chunk's partial sum -- the Flash-MoE page's fma(nibble, scale*x,
-//     bias*x) rearrangement ("FMA 优化的反量化内核") with the bias term
+//   * one workgroup per 16-row group; its W waves hold P = 4W quarter-waves,
+//     and quarter p owns code units [p*KCS, (p+1)*KCS) of every slice of K
+//     (one slice when x fits the LDS budget);
+//   * each lane first requests its KCS code units and its meta bytes, then x
+//     is staged in LDS together with per-group column sums X (so the offset
+//     terms of Q4_0/Q4_1/K-quants/low-bit codes cost one multiply per group,
+//     not per weight);
+//   * codes are decoded in registers: nibbles, 2-bit fields and bits are
+//     masked into bytes and converted two at a time as OCP e4m3 values (a
+//     byte 0..15 is exactly n * 2^-9 there), and the 2^9 is folded into the
+//     scale; fp32 FMAs accumulate -- the Flash-MoE page's fma(nibble,
+//     scale*x, bias*x) rearrangement ("FMA 优化的反量化内核") with the bias term
 //     hoisted over the shared x as bias * sum(x);
-//   * lane partials are reduced with DPP (quad_perm, row mirrors,
-//     row_bcast15/31) in a fixed order, so results are deterministic.
+//   * K-quant scales are applied once per 256-weight super-block: the lane
+//     sums s_j * P_j and t_j * X_j over its 8 sub-blocks and multiplies by d
+//     and dmin once;
+//   * the P partial sums of each row are combined through LDS in a fixed
+//     order: results are deterministic.
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -33,36 +43,40 @@
 namespace qg {
 namespace {
 
-constexpr int kThreads = 256;            // 4 waves per workgroup
-constexpr int kWaves = kThreads / 64;
-constexpr int kLdsBudget = 64 * 1024;    // bytes of x + sums staged per workgroup
+constexpr int kLdsBudget = 64 * 1024;  // bytes of x + column sums per workgroup
+constexpr int kRowGroup = 16;          // rows per interleave group (layout constant)
 
 // ------------------------------------------------------------------ traits
-
+//
+// CPC: weights per 16-byte code unit; MBU: meta bytes per code unit; GS:
+// weights per column sum (0 = none); BLOCK, CB, MB: the format's block.
 template <int F> struct Fmt;
-// CPC: columns (weights) per 16-byte code chunk; GS: columns per staged
-// x-sum (0 = the format needs none); BLOCK / MB: weights and meta bytes per
-// meta entry.
-template <> struct Fmt<QG_Q8_0> { static constexpr int CPC = 16, GS = 0, BLOCK = 32, MB = 2, CB = 32; };
-template <> struct Fmt<QG_Q4_0> { static constexpr int CPC = 32, GS = 32, BLOCK = 32, MB = 2, CB = 16; };
-template <> struct Fmt<QG_Q4_1> { static constexpr int CPC = 32, GS = 32, BLOCK = 32, MB = 4, CB = 16; };
-template <> struct Fmt<QG_Q4_K> { static constexpr int CPC = 32, GS = 32, BLOCK = 256, MB = 16, CB = 128; };
-template <> struct Fmt<QG_Q2_K> { static constexpr int CPC = 64, GS = 32, BLOCK = 256, MB = 16, CB = 64; };
-template <> struct Fmt<QG_TERN> { static constexpr int CPC = 64, GS = 64, BLOCK = 128, MB = 2, CB = 32; };
-template <> struct Fmt<QG_BIN>  { static constexpr int CPC = 128, GS = 128, BLOCK = 128, MB = 2, CB = 16; };
+template <> struct Fmt<QG_Q8_0> { static constexpr int CPC = 16,  MBU = 1, GS = 0,   BLOCK = 32,  CB = 32,  MB = 2; };
+template <> struct Fmt<QG_Q4_0> { static constexpr int CPC = 32,  MBU = 2, GS = 32,  BLOCK = 32,  CB = 16,  MB = 2; };
+template <> struct Fmt<QG_Q4_1> { static constexpr int CPC = 32,  MBU = 4, GS = 32,  BLOCK = 32,  CB = 16,  MB = 4; };
+template <> struct Fmt<QG_Q4_K> { static constexpr int CPC = 32,  MBU = 2, GS = 32,  BLOCK = 256, CB = 128, MB = 16; };
+template <> struct Fmt<QG_Q2_K> { static constexpr int CPC = 64,  MBU = 4, GS = 32,  BLOCK = 256, CB = 64,  MB = 16; };
+template <> struct Fmt<QG_TERN> { static constexpr int CPC = 64,  MBU = 1, GS = 64,  BLOCK = 128, CB = 32,  MB = 2; };
+template <> struct Fmt<QG_BIN>  { static constexpr int CPC = 128, MBU = 2, GS = 128, BLOCK = 128, CB = 16,  MB = 2; };
 
 __device__ __forceinline__ float h2f(uint32_t bits16) {
     return (float)__builtin_bit_cast(_Float16, (uint16_t)bits16);
 }
 
-__device__ __forceinline__ float ubyte(uint32_t v, int k) { return (float)((v >> (8 * k)) & 0xFFu); }
-
-// Hide a masked code dword from the optimizer so that each byte converts
-// with one v_cvt_f32_ubyte{0..3} instead of a bit-field extract plus a
-// convert (the mask would otherwise be folded into per-byte extracts).
+// Keep a masked code dword opaque to the optimizer so each byte pair converts
+// with one v_cvt_pk_f32_fp8 (the mask would otherwise be re-folded into
+// per-byte bit-field extracts).
 __device__ __forceinline__ uint32_t opaque(uint32_t v) {
     asm volatile("" : "+v"(v));
     return v;
+}
+
+// Bytes 0..3 of v (each 0..15) as floats n * 2^-9 (OCP e4m3 encodes a byte n
+// in 0..15 exactly as n * 2^-9, subnormals included).
+__device__ __forceinline__ void fp8x4(uint32_t v, float& b0, float& b1, float& b2, float& b3) {
+    const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)v, false);
+    const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)v, true);
+    b0 = lo[0]; b1 = lo[1]; b2 = hi[0]; b3 = hi[1];
 }
 
 // ------------------------------------------------------------ DPP reduction
@@ -72,383 +86,578 @@ __device__ __forceinline__ float dpp(float v) {
     return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, ROW_MASK, 0xF, false));
 }
 
-// Sum over aligned groups of LPR lanes (LPR in 4..64).  The full sum is valid
-// in the last lane of each group.
+// Sum over aligned groups of LPR lanes (LPR in 4..64); the full sum is valid in
+// the last lane of each group.
 template <int LPR>
 __device__ __forceinline__ float group_sum(float v) {
-    v += dpp<0xB1>(v);                          // quad_perm [1,0,3,2]
-    v += dpp<0x4E>(v);                          // quad_perm [2,3,0,1]
-    if constexpr (LPR >= 8) v += dpp<0x141>(v);  // row_half_mirror
-    if constexpr (LPR >= 16) v += dpp<0x140>(v); // row_mirror
+    v += dpp<0xB1>(v);                                 // quad_perm [1,0,3,2]
+    v += dpp<0x4E>(v);                                 // quad_perm [2,3,0,1]
+    if constexpr (LPR >= 8) v += dpp<0x141>(v);        // row_half_mirror
+    if constexpr (LPR >= 16) v += dpp<0x140>(v);       // row_mirror
     if constexpr (LPR >= 32) v += dpp<0x142, 0xA>(v);  // row_bcast:15 into rows 1, 3
     if constexpr (LPR >= 64) v += dpp<0x143, 0xC>(v);  // row_bcast:31 into rows 2, 3
     return v;
 }
 
-// --------------------------------------------------- per-format chunk decode
+// -------------------------------------------------- per-format unit decode
 //
-// Chunk<F>::Meta holds what a lane needs from the meta plane for one (row,
-// chunk); load() fetches it; codes(v, w) turns code dword v into the raw code
-// values of its CPC/4 columns (column order); apply() folds the per-group
-// partial sums P (sum of code * x) and the column sums X into the row sum.
+// Unit<F>::decode(v, w) turns one code dword into the CPC/4 code values of
+// its columns, in column order, scaled by 2^-9 (the value of the e4m3 byte
+// 0x01) for the formats decoded through e4m3 (all but Q8_0).
 
-template <int F> struct Chunk;
+template <int F> struct Unit;
 
-template <> struct Chunk<QG_Q8_0> {
-    static constexpr int CPD = 4, SUBS = 1;
-    struct Meta { uint32_t d; };
-    __device__ static Meta load(const uint8_t* meta_row, int cg) {
-        return {*(const uint16_t*)(meta_row + 2 * (cg >> 1))};
-    }
-    __device__ static void codes(uint32_t v, float* w) {
+template <> struct Unit<QG_Q8_0> {
+    static constexpr int CPD = 4;
+    __device__ static void decode(uint32_t v, float* w) {
 #pragma unroll
         for (int k = 0; k < 4; ++k) w[k] = (float)(int)(int8_t)(v >> (8 * k));
     }
-    __device__ static float apply(const Meta& m, const float* P, const float*) { return h2f(m.d) * P[0]; }
 };
 
-template <> struct Chunk<QG_Q4_0> {
-    static constexpr int CPD = 8, SUBS = 1;
-    struct Meta { uint32_t d; };
-    __device__ static Meta load(const uint8_t* meta_row, int cg) { return {*(const uint16_t*)(meta_row + 2 * cg)}; }
-    __device__ static void codes(uint32_t v, float* w) {
+// nibble i of a block in byte i>>1, low nibble first: byte k of a dword holds
+// columns 2k (low) and 2k+1 (high)
+template <> struct Unit<QG_Q4_0> {
+    static constexpr int CPD = 8;
+    __device__ static void decode(uint32_t v, float* w) {
         const uint32_t lo = opaque(v & 0x0F0F0F0Fu), hi = opaque((v >> 4) & 0x0F0F0F0Fu);
-#pragma unroll
-        for (int k = 0; k < 4; ++k) { w[2 * k] = ubyte(lo, k); w[2 * k + 1] = ubyte(hi, k); }
-    }
-    // w = (n - 8) d  ->  d * (sum n x - 8 X)
-    __device__ static float apply(const Meta& m, const float* P, const float* X) {
-        return h2f(m.d) * fmaf(-8.0f, X[0], P[0]);
+        fp8x4(lo, w[0], w[2], w[4], w[6]);
+        fp8x4(hi, w[1], w[3], w[5], w[7]);
     }
 };
+template <> struct Unit<QG_Q4_1> : Unit<QG_Q4_0> {};
+template <> struct Unit<QG_Q4_K> : Unit<QG_Q4_0> {};
 
-template <> struct Chunk<QG_Q4_1> {
-    static constexpr int CPD = 8, SUBS = 1;
-    struct Meta { uint32_t dm; };
-    __device__ static Meta load(const uint8_t* meta_row, int cg) { return {*(const uint32_t*)(meta_row + 4 * cg)}; }
-    __device__ static void codes(uint32_t v, float* w) { Chunk<QG_Q4_0>::codes(v, w); }
-    // w = n d + m  ->  d * sum n x + m X
-    __device__ static float apply(const Meta& m, const float* P, const float* X) {
-        return fmaf(h2f(m.dm & 0xFFFFu), P[0], h2f(m.dm >> 16) * X[0]);
-    }
-};
-
-// K-quant meta entry (16 B per 256 weights): bytes 0..11 hold pairs
-// p_j = s_j | t_j << 6 at bits [12j, 12j+12); bytes 12..15 hold fp16 d, dmin.
-// A lane fetches the two dwords around its pair at a lane-specific offset and
-// extracts the pair with one funnel shift; it never reads past the entry.
-template <> struct Chunk<QG_Q4_K> {
-    static constexpr int CPD = 8, SUBS = 1;
-    struct Meta { uint32_t lo, hi, dd; int sh; };
-    __device__ static Meta load(const uint8_t* meta_row, int cg) {
-        const uint8_t* e = meta_row + 16 * (cg >> 3);
-        const int j = cg & 7;
-        const int w = (12 * j) >> 5;  // 0,0,0,1,1,1,2,2
-        Meta m;
-        m.lo = *(const uint32_t*)(e + 4 * w);
-        m.hi = *(const uint32_t*)(e + 4 * w + 4);
-        m.dd = *(const uint32_t*)(e + 12);
-        m.sh = 12 * j - 32 * w;
-        return m;
-    }
-    __device__ static void codes(uint32_t v, float* w) { Chunk<QG_Q4_0>::codes(v, w); }
-    // w = n s d - t dmin  ->  d * (s * sum n x) - dmin * (t * X)
-    __device__ static float apply(const Meta& m, const float* P, const float* X) {
-        const uint32_t p = __builtin_amdgcn_alignbit(m.hi, m.lo, m.sh);
-        const float s = (float)(p & 63u), t = (float)((p >> 6) & 63u);
-        return fmaf(h2f(m.dd & 0xFFFFu), s * P[0], -h2f(m.dd >> 16) * (t * X[0]));
-    }
-};
-
-// Q2_K: a 16-byte chunk is 64 weights = sub-blocks 2q and 2q+1 of its
-// super-block (q = chunk & 3); their two pairs are 24 contiguous bits.
-template <> struct Chunk<QG_Q2_K> {
-    static constexpr int CPD = 16, SUBS = 2;
-    struct Meta { uint32_t lo, hi, dd; int sh; };
-    __device__ static Meta load(const uint8_t* meta_row, int cg) {
-        const uint8_t* e = meta_row + 16 * (cg >> 2);
-        const int q = cg & 3;
-        const int w = (24 * q) >> 5;  // 0,0,1,2
-        Meta m;
-        m.lo = *(const uint32_t*)(e + 4 * w);
-        m.hi = *(const uint32_t*)(e + 4 * w + 4);
-        m.dd = *(const uint32_t*)(e + 12);
-        m.sh = 24 * q - 32 * w;
-        return m;
-    }
-    __device__ static void codes(uint32_t v, float* w) {
+// 2-bit field i in byte i>>2 at bits 2*(i&3): byte k of a dword holds columns
+// 4k..4k+3
+template <> struct Unit<QG_Q2_K> {
+    static constexpr int CPD = 16;
+    __device__ static void decode(uint32_t v, float* w) {
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
             const uint32_t f = opaque((v >> (2 * s)) & 0x03030303u);
-#pragma unroll
-            for (int k = 0; k < 4; ++k) w[4 * k + s] = ubyte(f, k);
+            fp8x4(f, w[s], w[4 + s], w[8 + s], w[12 + s]);
         }
     }
-    __device__ static float apply(const Meta& m, const float* P, const float* X) {
-        const uint32_t p = __builtin_amdgcn_alignbit(m.hi, m.lo, m.sh);
-        const float s0 = (float)(p & 63u), t0 = (float)((p >> 6) & 63u);
-        const float s1 = (float)((p >> 12) & 63u), t1 = (float)((p >> 18) & 63u);
-        const float sp = fmaf(s0, P[0], s1 * P[1]);
-        const float tx = fmaf(t0, X[0], t1 * X[1]);
-        return fmaf(h2f(m.dd & 0xFFFFu), sp, -h2f(m.dd >> 16) * tx);
-    }
 };
+template <> struct Unit<QG_TERN> : Unit<QG_Q2_K> {};
 
-// ternary: f = t + 1 in {0,1,2}; w = (f - 1) d -> d * (sum f x - X)
-template <> struct Chunk<QG_TERN> {
-    static constexpr int CPD = 16, SUBS = 1;
-    struct Meta { uint32_t d; };
-    __device__ static Meta load(const uint8_t* meta_row, int cg) { return {*(const uint16_t*)(meta_row + 2 * (cg >> 1))}; }
-    __device__ static void codes(uint32_t v, float* w) { Chunk<QG_Q2_K>::codes(v, w); }
-    __device__ static float apply(const Meta& m, const float* P, const float* X) { return h2f(m.d) * (P[0] - X[0]); }
-};
-
-// 1-bit: w = (2 beta - 1) d -> d * (2 sum_{beta=1} x - X)
-template <> struct Chunk<QG_BIN> {
-    static constexpr int CPD = 32, SUBS = 1;
-    struct Meta { uint32_t d; };
-    __device__ static Meta load(const uint8_t* meta_row, int cg) { return {*(const uint16_t*)(meta_row + 2 * cg)}; }
-    __device__ static void codes(uint32_t v, float* w) {
+// bit i in byte i>>3 at bit i&7: byte k of a dword holds columns 8k..8k+7
+template <> struct Unit<QG_BIN> {
+    static constexpr int CPD = 32;
+    __device__ static void decode(uint32_t v, float* w) {
 #pragma unroll
         for (int s = 0; s < 8; ++s) {
             const uint32_t f = opaque((v >> s) & 0x01010101u);
-#pragma unroll
-            for (int k = 0; k < 4; ++k) w[8 * k + s] = ubyte(f, k);
+            fp8x4(f, w[s], w[8 + s], w[16 + s], w[24 + s]);
         }
     }
-    __device__ static float apply(const Meta& m, const float* P, const float* X) {
-        return h2f(m.d) * fmaf(2.0f, P[0], -X[0]);
+};
+
+// Weight bytes are read exactly once per call: stream them past the caches.
+#ifndef QG_WEIGHT_NT
+#define QG_WEIGHT_NT 1
+#endif
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+template <typename V> struct NtLoad;
+template <> struct NtLoad<uint4> {
+    __device__ static uint4 ld(const uint8_t* p) {
+#if QG_WEIGHT_NT
+        const u32x4_t v = __builtin_nontemporal_load((const u32x4_t*)p);
+        return make_uint4(v.x, v.y, v.z, v.w);
+#else
+        return *(const uint4*)p;
+#endif
+    }
+};
+template <> struct NtLoad<uint2> {
+    __device__ static uint2 ld(const uint8_t* p) {
+#if QG_WEIGHT_NT
+        const u32x2_t v = __builtin_nontemporal_load((const u32x2_t*)p);
+        return make_uint2(v.x, v.y);
+#else
+        return *(const uint2*)p;
+#endif
+    }
+};
+template <> struct NtLoad<uint32_t> {
+    __device__ static uint32_t ld(const uint8_t* p) {
+#if QG_WEIGHT_NT
+        return __builtin_nontemporal_load((const uint32_t*)p);
+#else
+        return *(const uint32_t*)p;
+#endif
+    }
+};
+template <typename V>
+__device__ __forceinline__ V ld_weights(const uint8_t* p) { return NtLoad<V>::ld(p); }
+
+// --------------------------------------------------- interleaved addressing
+//
+// A row group g holds n_g = min(16, N - 16g) rows.  Its codes start at
+// 16*g*row_codes in the codes plane and its meta at 16*g*row_meta in the meta
+// plane.  Unit u of row r: base + (u*n_g + r)*16; a row's short last meta
+// unit (row_meta % 16 bytes) sits after the group's full units at
+// base + full_units*n_g*16 + r*rem.
+
+// Meta bytes [o0, o0 + NB) of row r (NB = 4, 8, 16 or 32; o0 a multiple of
+// min(NB, 16)).  Full units are read with one vector load each; a part that
+// reaches into the short last unit is read two bytes at a time and only up to
+// the row's last meta byte (bytes past it belong to no code unit in range).
+template <int NB>
+__device__ __forceinline__ void load_meta(const uint8_t* gm, int n_g, int r, int o0, int row_meta,
+                                          uint32_t (&wd)[NB / 4]) {
+    const int full = row_meta >> 4, rem = row_meta & 15;
+    constexpr int W = NB >= 16 ? 4 : NB / 4;  // dwords per part
+#pragma unroll
+    for (int h = 0; h < (NB + 15) / 16; ++h) {
+        const int o = o0 + 16 * h;
+        const int u = o >> 4, i0 = o & 15;
+        if (u < full) {
+            const uint8_t* p = gm + ((size_t)u * n_g + r) * 16 + i0;
+            if constexpr (W == 4) {
+                const uint4 v = *(const uint4*)p;
+                wd[4 * h] = v.x; wd[4 * h + 1] = v.y; wd[4 * h + 2] = v.z; wd[4 * h + 3] = v.w;
+            } else if constexpr (W == 2) {
+                const uint2 v = *(const uint2*)p;
+                wd[0] = v.x; wd[1] = v.y;
+            } else {
+                wd[0] = *(const uint32_t*)p;
+            }
+        } else {
+            const uint8_t* p = gm + (size_t)full * n_g * 16 + (size_t)r * rem;
+#pragma unroll
+            for (int k = 0; k < W; ++k) {
+                uint32_t lo = 0, hi = 0;
+                if (u == full && i0 + 4 * k < rem) lo = *(const uint16_t*)(p + i0 + 4 * k);
+                if (u == full && i0 + 4 * k + 2 < rem) hi = *(const uint16_t*)(p + i0 + 4 * k + 2);
+                wd[W * h + k] = lo | (hi << 16);
+            }
+        }
+    }
+}
+
+// ----------------------------------------------------------- scale applies
+//
+// Apply<F>::unit(wd, i, s, P, X, st, acc, ok) folds the partial sum P (sum of
+// decoded code * x over sub-group s of the lane's unit i) and the column sum X
+// of that sub-group into the row sum acc, using the lane's meta words wd.
+// i and s are compile-time after unrolling, so every meta field extraction
+// has constant positions.  K-quants keep two running sums per batch row in st
+// and apply d, dmin once per super-block.  Units with ok false lie past the
+// end of K and contribute nothing.
+
+struct KqState { float sp = 0.0f, tx = 0.0f; };
+
+// fp16 half-word h of the meta words
+__device__ __forceinline__ float meta_h(const uint32_t* wd, int h) {
+    return h2f((wd[h >> 1] >> (16 * (h & 1))) & 0xFFFFu);
+}
+
+template <int F> struct Apply;
+
+template <> struct Apply<QG_Q8_0> {
+    static constexpr int SUBS = 1;
+    // unit i belongs to block i/2; w = q d
+    __device__ static void unit(const uint32_t* wd, int i, int, float P, float, KqState&, float& acc, bool ok) {
+        const float v = fmaf(meta_h(wd, i >> 1), P, acc);
+        acc = ok ? v : acc;
+    }
+};
+
+template <> struct Apply<QG_Q4_0> {
+    static constexpr int SUBS = 1;
+    // w = (n - 8) d:  d * (512 P - 8 X)
+    __device__ static void unit(const uint32_t* wd, int i, int, float P, float X, KqState&, float& acc, bool ok) {
+        const float v = fmaf(meta_h(wd, i), fmaf(512.0f, P, -8.0f * X), acc);
+        acc = ok ? v : acc;
+    }
+};
+
+template <> struct Apply<QG_Q4_1> {
+    static constexpr int SUBS = 1;
+    // w = n d + m:  (512 d) P + m X
+    __device__ static void unit(const uint32_t* wd, int i, int, float P, float X, KqState&, float& acc, bool ok) {
+        const float v = fmaf(512.0f * meta_h(wd, 2 * i), P, fmaf(meta_h(wd, 2 * i + 1), X, acc));
+        acc = ok ? v : acc;
+    }
+};
+
+// K-quant meta entry: pairs p_j = s_j | t_j << 6 at bits [12j, 12j+12) of words
+// 0..2, fp16 d and dmin in word 3.
+__device__ __forceinline__ uint32_t kq_pair(const uint32_t* e, int j) {
+    const int bit = 12 * j, w = bit >> 5, sh = bit & 31;
+    return sh <= 20 ? (e[w] >> sh) : __builtin_amdgcn_alignbit(e[w + 1], e[w], sh);
+}
+
+// w = n s d - t dmin:  per super-block (512 d) * sum_j s_j P_j - dmin * sum_j t_j X_j
+template <int UPS>  // code units per super-block (8 for Q4_K, 4 for Q2_K)
+struct ApplyKq {
+    static constexpr int SUBS = 8 / UPS;
+    __device__ static void unit(const uint32_t* wd, int i, int s, float P, float X, KqState& st, float& acc, bool ok) {
+        const uint32_t* e = wd + 4 * (i / UPS);
+        const int j = (i % UPS) * SUBS + s;
+        const uint32_t p = kq_pair(e, j);
+        st.sp = fmaf((float)(p & 63u), P, st.sp);
+        st.tx = fmaf((float)((p >> 6) & 63u), X, st.tx);
+        if (j == 7) {
+            const float v = fmaf(512.0f * h2f(e[3] & 0xFFFFu), st.sp, fmaf(-h2f(e[3] >> 16), st.tx, acc));
+            acc = ok ? v : acc;
+            st.sp = 0.0f;
+            st.tx = 0.0f;
+        }
+    }
+};
+template <> struct Apply<QG_Q4_K> : ApplyKq<8> {};
+template <> struct Apply<QG_Q2_K> : ApplyKq<4> {};
+
+template <> struct Apply<QG_TERN> {
+    static constexpr int SUBS = 1;
+    // f = t + 1:  w = (f - 1) d  ->  d * (512 P - X); unit i is half of block i/2
+    __device__ static void unit(const uint32_t* wd, int i, int, float P, float X, KqState&, float& acc, bool ok) {
+        const float v = fmaf(meta_h(wd, i >> 1), fmaf(512.0f, P, -X), acc);
+        acc = ok ? v : acc;
+    }
+};
+
+template <> struct Apply<QG_BIN> {
+    static constexpr int SUBS = 1;
+    // w = (2 beta - 1) d  ->  d * (1024 P - X)
+    __device__ static void unit(const uint32_t* wd, int i, int, float P, float X, KqState&, float& acc, bool ok) {
+        const float v = fmaf(meta_h(wd, i), fmaf(1024.0f, P, -X), acc);
+        acc = ok ? v : acc;
     }
 };
 
 // ------------------------------------------------------------ GEMV kernel
+//
+// Template: format F, batch B, waves W, code units per lane per slice KCS.
+// Grid: one workgroup per 16-row group.  Dynamic LDS: x slice [B][SC]
+// (SC = P*KCS*CPC columns), column sums [B][SC/GS], partials [P][16][B].
 
-template <int F, int B, int R, int LPR>
-__global__ void __launch_bounds__(kThreads)
-gemv_kernel(const uint8_t* __restrict__ codes, const uint8_t* __restrict__ meta,
-            const float* __restrict__ x, float* __restrict__ y, int N, int K, int KS) {
+template <int F, int B, int W, int KCS>
+struct Gemv {
     using T = Fmt<F>;
-    using C = Chunk<F>;
-    constexpr int CPC = T::CPC, CPD = C::CPD, GS = T::GS;
-    constexpr int GPW = 64 / LPR;                 // lane groups per wave
-    constexpr int XS_PER_CHUNK = GS ? CPC / GS : 1;  // column sums per chunk
-    extern __shared__ float lds[];
-    float* xs = lds;                    // [B][KS]
-    float* xsum = lds + B * KS;         // [B][KS / GS]
+    using U = Unit<F>;
+    using A = Apply<F>;
+    static constexpr int NT = W * 64, P = 4 * W;
+    static constexpr int CPC = T::CPC, CPD = U::CPD, GS = T::GS, SUBS = A::SUBS;
+    static constexpr int SU = P * KCS;                      // code units per slice
+    static constexpr int SC = SU * CPC;                     // columns per slice
+    static constexpr int NSUM = GS ? SC / (GS ? GS : 1) : 1;  // column sums per slice row
+    static constexpr int MB = KCS * T::MBU;                 // meta bytes per lane part
+    static constexpr int DPS = 4 / SUBS;                    // code dwords per sub-group
+    static constexpr int X0 = 4;                            // x float4 per thread requested first
+    static_assert(GS == 0 || GS == CPC / SUBS, "one column sum per sub-group");
+    static_assert((4 * NT) % (GS ? GS : 4) == 0, "a staging round covers whole sum groups");
 
-    const int tid = threadIdx.x;
-    const int lane = tid & 63, wave = tid >> 6;
-    const int grp = lane / LPR, sl = lane % LPR;
-    const int row0 = ((blockIdx.x * kWaves + wave) * GPW + grp) * R;
-
-    const size_t code_row = (size_t)(K / T::BLOCK) * T::CB;
-    const size_t meta_row = (size_t)(K / T::BLOCK) * T::MB;
-    const uint8_t* crow[R];
-    const uint8_t* mrow[R];
-#pragma unroll
-    for (int r = 0; r < R; ++r) {
-        const int row = min(row0 + r, N - 1);
-        crow[r] = codes + (size_t)row * code_row;
-        mrow[r] = meta + (size_t)row * meta_row;
+    // x[b][k0 + c] for c = 4*(tid + NT*i), i = 0.. (float4 per thread)
+    __device__ static float4 ld_x(const float* __restrict__ x, int K, int k0, int cols, int b, int c) {
+        return c < cols ? *(const float4*)(x + (size_t)b * K + k0 + c) : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+    // stage one float4 of row b at column c into LDS and, when it completes a
+    // group of GS columns (a DPP sum over the GS/4 threads that hold it), the
+    // group's column sum; every thread calls this the same number of times
+    __device__ static void put_x(float* xs, float* xsum, int tid, int cols, int b, int c, float4 v) {
+        if (c < cols) *(float4*)(xs + b * SC + c) = v;
+        if constexpr (GS > 0) {
+            const float s = group_sum<GS / 4>((v.x + v.y) + (v.z + v.w));
+            if (c < cols && (tid % (GS / 4)) == GS / 4 - 1) xsum[b * NSUM + c / GS] = s;
+        }
     }
 
-    float acc[R][B];
+    // Decode this lane's KCS units and fold them into acc; units i >= nvalid
+    // lie past the end of K and contribute nothing.
+    __device__ static void compute(const uint4 (&q)[KCS], const uint32_t* wd, const float* xs, const float* xsum,
+                                   int lc0, int nvalid, float (&acc)[B]) {
+        KqState st[B];
 #pragma unroll
-    for (int r = 0; r < R; ++r)
+        for (int i = 0; i < KCS; ++i) {
+            const bool ok = i < nvalid;
+            const uint32_t dw[4] = {q[i].x, q[i].y, q[i].z, q[i].w};
+            const int xo = ok ? (lc0 + i) * CPC : 0;  // units past K read staged x harmlessly
 #pragma unroll
-        for (int b = 0; b < B; ++b) acc[r][b] = 0.0f;
-
-    for (int k0 = 0; k0 < K; k0 += KS) {
-        const int ks = min(KS, K - k0);
-        if (k0) __syncthreads();  // the previous slice is fully consumed
-        for (int i = 4 * tid; i < B * ks; i += 4 * kThreads) {
-            const int b = i / ks, c = i - b * ks;
-            *(float4*)(xs + b * KS + c) = *(const float4*)(x + (size_t)b * K + k0 + c);
-        }
-        __syncthreads();
-        if constexpr (GS > 0) {
-            for (int g = tid; g < B * (ks / GS); g += kThreads) {
-                const int b = g / (ks / GS), c = g - b * (ks / GS);
-                const float* p = xs + b * KS + c * GS;
-                float s = 0.0f;
-                for (int i = 0; i < GS; i += 4) {
-                    const float4 v = *(const float4*)(p + i);
-                    s += (v.x + v.y) + (v.z + v.w);
-                }
-                xsum[b * (KS / GS) + c] = s;
-            }
-            __syncthreads();
-        }
-
-        const int nch = ks / CPC;
-        const int c0 = k0 / CPC;
-        for (int c = sl; c < nch; c += LPR) {
-            const int cg = c0 + c;
-            uint4 q[R];
-            typename C::Meta m[R];
+            for (int s = 0; s < SUBS; ++s) {
+                float ps[B];
 #pragma unroll
-            for (int r = 0; r < R; ++r) {
-                q[r] = *(const uint4*)(crow[r] + 16 * (size_t)cg);
-                m[r] = C::load(mrow[r], cg);
-            }
-            float P[R][B][C::SUBS];
+                for (int b = 0; b < B; ++b) ps[b] = 0.0f;
 #pragma unroll
-            for (int r = 0; r < R; ++r)
-#pragma unroll
-                for (int b = 0; b < B; ++b)
-#pragma unroll
-                    for (int s = 0; s < C::SUBS; ++s) P[r][b][s] = 0.0f;
-
-#pragma unroll
-            for (int d = 0; d < 4; ++d) {
-                float xv[B][CPD];
-#pragma unroll
-                for (int b = 0; b < B; ++b)
-#pragma unroll
-                    for (int i = 0; i < CPD; i += 4) {
-                        const float4 v = *(const float4*)(xs + b * KS + c * CPC + d * CPD + i);
-                        xv[b][i] = v.x; xv[b][i + 1] = v.y; xv[b][i + 2] = v.z; xv[b][i + 3] = v.w;
-                    }
-                constexpr int DPS = 4 / C::SUBS;  // code dwords per scale group
-#pragma unroll
-                for (int r = 0; r < R; ++r) {
-                    const uint32_t v = d == 0 ? q[r].x : d == 1 ? q[r].y : d == 2 ? q[r].z : q[r].w;
+                for (int d = s * DPS; d < (s + 1) * DPS; ++d) {
                     float w[CPD];
-                    C::codes(v, w);
+                    U::decode(dw[d], w);
 #pragma unroll
                     for (int b = 0; b < B; ++b) {
-                        float p = P[r][b][d / DPS];
+                        const float* xb = xs + b * SC + xo + d * CPD;
 #pragma unroll
-                        for (int i = 0; i < CPD; ++i) p = fmaf(w[i], xv[b][i], p);
-                        P[r][b][d / DPS] = p;
+                        for (int k = 0; k < CPD; k += 4) {
+                            const float4 xx = *(const float4*)(xb + k);
+                            ps[b] = fmaf(w[k], xx.x, ps[b]);
+                            ps[b] = fmaf(w[k + 1], xx.y, ps[b]);
+                            ps[b] = fmaf(w[k + 2], xx.z, ps[b]);
+                            ps[b] = fmaf(w[k + 3], xx.w, ps[b]);
+                        }
                     }
-                }
-            }
-#pragma unroll
-            for (int b = 0; b < B; ++b) {
-                float X[XS_PER_CHUNK > 0 ? XS_PER_CHUNK : 1];
-                if constexpr (GS > 0) {
-#pragma unroll
-                    for (int s = 0; s < XS_PER_CHUNK; ++s) X[s] = xsum[b * (KS / GS) + c * XS_PER_CHUNK + s];
-                } else {
-                    X[0] = 0.0f;
+                    // wide decodes at B > 1: one code dword live at a time
+                    if constexpr (CPD * B >= 16) __builtin_amdgcn_sched_barrier(0);
                 }
 #pragma unroll
-                for (int r = 0; r < R; ++r) acc[r][b] += C::apply(m[r], P[r][b], X);
+                for (int b = 0; b < B; ++b) {
+                    const float X = GS > 0 ? xsum[b * NSUM + (ok ? (lc0 + i) * SUBS + s : 0)] : 0.0f;
+                    A::unit(wd, i, s, ps[b], X, st[b], acc[b], ok);
+                }
             }
+            // keep one unit's decode live at a time (bounds register use)
+            __builtin_amdgcn_sched_barrier(0);
         }
     }
 
+    __device__ static void run(const uint8_t* __restrict__ codes, const uint8_t* __restrict__ meta,
+                               const float* __restrict__ x, float* __restrict__ y, int N, int K) {
+        extern __shared__ float lds[];
+        float* xs = lds;                    // [B][SC]
+        float* xsum = xs + B * SC;          // [B][NSUM]
+        float* part = xsum + B * NSUM;      // [P][16][B]
+
+        const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+        const int r = lane & 15, p = wave * 4 + (lane >> 4);
+        const int g = blockIdx.x;
+        const int n_g = min(kRowGroup, N - g * kRowGroup);
+        const int rr = min(r, n_g - 1);
+        const int nb = K / T::BLOCK;
+        const int row_codes = nb * T::CB, row_meta = nb * T::MB;
+        const int nch = row_codes >> 4;
+        const bool meta_whole = (row_meta & 15) == 0;  // no short last meta unit
+        // this lane's row: unit c at gcr + c*ustride, meta unit u at gmr + u*ustride
+        const int ustride = n_g * 16;
+        const uint8_t* gcr = codes + (size_t)g * kRowGroup * row_codes + rr * 16;
+        const uint8_t* gm = meta + (size_t)g * kRowGroup * row_meta;
+        const uint8_t* gmr = gm + rr * 16;
+
+        float acc[B];
 #pragma unroll
-    for (int r = 0; r < R; ++r)
+        for (int b = 0; b < B; ++b) acc[b] = 0.0f;
+
+        for (int c_slice = 0; c_slice < nch; c_slice += SU) {
+            const int k0 = c_slice * CPC;
+            const int cols = min(SC, K - k0);
+            if (c_slice) __syncthreads();         // the previous slice's x is consumed
+
+            // (1) the first X0 float4 of x row 0 go out before the code loads,
+            // so waiting for them does not wait for the codes
+            float4 xv[X0];
 #pragma unroll
-        for (int b = 0; b < B; ++b) {
-            const float v = group_sum<LPR>(acc[r][b]);
-            if (sl == LPR - 1 && row0 + r < N) y[(size_t)b * N + row0 + r] = v;
+            for (int i = 0; i < X0; ++i) xv[i] = ld_x(x, K, k0, cols, 0, 4 * (tid + NT * i));
+
+            // (2) this lane's meta bytes and code units
+            const int c0 = c_slice + p * KCS;
+            const int nvalid = nch - c0;  // units of the part inside K (may be <= 0)
+            uint4 q[KCS];
+            uint32_t wd[MB / 4];
+            // meta first: the scale path reads it from the first unit on, and
+            // loads complete in issue order
+            const int m0 = min(c0, (nch - 1) / KCS * KCS) * T::MBU;
+            if (meta_whole) {
+                // whole 16-byte units: one vector load per unit (or half unit)
+#pragma unroll
+                for (int h = 0; h < (MB + 15) / 16; ++h) {
+                    const int o = m0 + 16 * h;
+                    const uint8_t* pm = gmr + (o >> 4) * ustride + (o & 15);
+                    if constexpr (MB >= 16) {
+                        const uint4 v = ld_weights<uint4>(pm);
+                        wd[4 * h] = v.x; wd[4 * h + 1] = v.y; wd[4 * h + 2] = v.z; wd[4 * h + 3] = v.w;
+                    } else if constexpr (MB == 8) {
+                        const uint2 v = ld_weights<uint2>(pm);
+                        wd[0] = v.x; wd[1] = v.y;
+                    } else {
+                        wd[0] = ld_weights<uint32_t>(pm);
+                    }
+                }
+            } else {
+                load_meta<MB>(gm, n_g, rr, m0, row_meta, wd);
+            }
+
+            // a unit past the end of K reads the row's last unit instead (its
+            // contribution is dropped), so every load is unconditional
+#pragma unroll
+            for (int i = 0; i < KCS; ++i) q[i] = ld_weights<uint4>(gcr + min(c0 + i, nch - 1) * ustride);
+            // (3) x to LDS with the column sums
+            const int rounds = (cols + 4 * NT - 1) / (4 * NT);  // float4 rounds per batch row
+#pragma unroll
+            for (int i = 0; i < X0; ++i)
+                if (i < rounds) put_x(xs, xsum, tid, cols, 0, 4 * (tid + NT * i), xv[i]);
+            for (int i = X0; i < rounds; ++i) {
+                const int c = 4 * (tid + NT * i);
+                put_x(xs, xsum, tid, cols, 0, c, ld_x(x, K, k0, cols, 0, c));
+            }
+#pragma unroll
+            for (int b = 1; b < B; ++b) {
+                for (int i0 = 0; i0 < rounds; i0 += X0) {
+                    float4 v[X0];
+#pragma unroll
+                    for (int i = 0; i < X0; ++i) v[i] = ld_x(x, K, k0, cols, b, 4 * (tid + NT * (i0 + i)));
+#pragma unroll
+                    for (int i = 0; i < X0; ++i)
+                        if (i0 + i < rounds) put_x(xs, xsum, tid, cols, b, 4 * (tid + NT * (i0 + i)), v[i]);
+                }
+            }
+            __syncthreads();
+
+            // (4) decode once, multiply for every batch row
+            compute(q, wd, xs, xsum, p * KCS, nvalid, acc);
         }
+
+        // (5) combine the P parts of each row in a fixed order
+#pragma unroll
+        for (int b = 0; b < B; ++b) part[(p * kRowGroup + r) * B + b] = acc[b];
+        __syncthreads();
+        for (int t = tid; t < kRowGroup * B; t += NT) {
+            const int rw = t / B, b = t - rw * B;
+            if (rw < n_g) {
+                float sum = 0.0f;
+#pragma unroll
+                for (int pp = 0; pp < P; ++pp) sum += part[(pp * kRowGroup + rw) * B + b];
+                y[(size_t)b * N + g * kRowGroup + rw] = sum;
+            }
+        }
+    }
+};
+
+template <int F, int B, int W, int KCS>
+__global__ void __launch_bounds__(W * 64)
+gemv_kernel(const uint8_t* __restrict__ codes, const uint8_t* __restrict__ meta,
+            const float* __restrict__ x, float* __restrict__ y, int N, int K) {
+    Gemv<F, B, W, KCS>::run(codes, meta, x, y, N, K);
 }
 
 // ---------------------------------------------------------- dequant kernel
-// One thread per 16-byte code chunk: decode CPC weights exactly.
+// One thread per (row, code unit): decode CPC weights exactly.
+
+__device__ __forceinline__ uint32_t meta_u16(const uint8_t* gm, int n_g, int r, int o, int row_meta) {
+    const int full = row_meta >> 4, rem = row_meta & 15;
+    const int u = o >> 4, i = o & 15;
+    const uint8_t* p = u < full ? gm + ((size_t)u * n_g + r) * 16 + i
+                                : gm + (size_t)full * n_g * 16 + (size_t)r * rem + i;
+    return *(const uint16_t*)p;
+}
 
 template <int F>
-__global__ void __launch_bounds__(kThreads)
+__global__ void __launch_bounds__(256)
 dequant_kernel(const uint8_t* __restrict__ codes, const uint8_t* __restrict__ meta,
                float* __restrict__ out, int N, int K) {
     using T = Fmt<F>;
-    using C = Chunk<F>;
-    constexpr int CPC = T::CPC, CPD = C::CPD;
-    const int nch = K / CPC;
-    const int64_t id = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+    constexpr int CPC = T::CPC, CPD = CPC / 4;
+    const int nb = K / T::BLOCK;
+    const int row_codes = nb * T::CB, row_meta = nb * T::MB;
+    const int nch = row_codes >> 4;
+    const int64_t id = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (id >= (int64_t)N * nch) return;
-    const int row = (int)(id / nch), cg = (int)(id - (int64_t)row * nch);
-    const uint8_t* crow = codes + (size_t)row * (K / T::BLOCK) * T::CB;
-    const uint8_t* mrow = meta + (size_t)row * (K / T::BLOCK) * T::MB;
-    const uint4 q = *(const uint4*)(crow + 16 * (size_t)cg);
-    float* o = out + (size_t)row * K + (size_t)cg * CPC;
+    const int row = (int)(id / nch), c = (int)(id - (int64_t)row * nch);
+    const int g = row / kRowGroup, r = row - g * kRowGroup;
+    const int n_g = min(kRowGroup, N - g * kRowGroup);
+    const uint8_t* gc = codes + (size_t)g * kRowGroup * row_codes;
+    const uint8_t* gm = meta + (size_t)g * kRowGroup * row_meta;
+    const uint4 q = *(const uint4*)(gc + ((size_t)c * n_g + r) * 16);
     const uint32_t dw[4] = {q.x, q.y, q.z, q.w};
+    float* o = out + (size_t)row * K + (size_t)c * CPC;
 #pragma unroll
     for (int d = 0; d < 4; ++d) {
         float w[CPD];
-        C::codes(dw[d], w);
-        float sc, off;  // weight = code * sc + off, exactly as the formats define it
-        if constexpr (F == QG_Q8_0 || F == QG_Q4_0 || F == QG_TERN || F == QG_BIN) {
-            const float dd = h2f(C::load(mrow, cg).d);
-            sc = dd;
-            off = 0.0f;
-            if constexpr (F == QG_Q4_0) {
+        Unit<F>::decode(dw[d], w);
+        if constexpr (F != QG_Q8_0) {
 #pragma unroll
-                for (int i = 0; i < CPD; ++i) w[i] -= 8.0f;
-            } else if constexpr (F == QG_TERN) {
-#pragma unroll
-                for (int i = 0; i < CPD; ++i) w[i] -= 1.0f;
-            } else if constexpr (F == QG_BIN) {
-#pragma unroll
-                for (int i = 0; i < CPD; ++i) w[i] = 2.0f * w[i] - 1.0f;
-            }
-        } else if constexpr (F == QG_Q4_1) {
-            const uint32_t dm = C::load(mrow, cg).dm;
-            sc = h2f(dm & 0xFFFFu);
-            off = h2f(dm >> 16);
-        } else {  // K-quants
-            const auto m = C::load(mrow, cg);
-            const uint32_t p = __builtin_amdgcn_alignbit(m.hi, m.lo, m.sh);
-            const int sub = F == QG_Q2_K ? (d >> 1) : 0;
-            const uint32_t pj = p >> (12 * sub);
-            sc = (float)(pj & 63u) * h2f(m.dd & 0xFFFFu);
-            off = -((float)((pj >> 6) & 63u) * h2f(m.dd >> 16));
+            for (int i = 0; i < CPD; ++i) w[i] *= 512.0f;  // exact: back to integer codes
         }
-        constexpr bool has_offset = F == QG_Q4_1 || F == QG_Q4_K || F == QG_Q2_K;
 #pragma unroll
         for (int i = 0; i < CPD; ++i) {
-            // the product is exact in fp32, so fma and mul-then-add round
-            // identically; formats without an offset take the bare product
-            // (adding +0 would turn a -0 product into +0)
-            o[d * CPD + i] = has_offset ? fmaf(w[i], sc, off) : w[i] * sc;
+            const int col = c * CPC + d * CPD + i;
+            const int blk = col / T::BLOCK;
+            float v;
+            if constexpr (F == QG_Q8_0) {
+                v = w[i] * h2f(meta_u16(gm, n_g, r, 2 * blk, row_meta));
+            } else if constexpr (F == QG_Q4_0) {
+                v = (w[i] - 8.0f) * h2f(meta_u16(gm, n_g, r, 2 * blk, row_meta));
+            } else if constexpr (F == QG_Q4_1) {
+                // n*d is exact, so fma and multiply-then-add round identically
+                v = fmaf(w[i], h2f(meta_u16(gm, n_g, r, 4 * blk, row_meta)),
+                         h2f(meta_u16(gm, n_g, r, 4 * blk + 2, row_meta)));
+            } else if constexpr (F == QG_Q4_K || F == QG_Q2_K) {
+                const int j = (col / 32) & 7;
+                const int bit = 12 * j;
+                const uint32_t two = meta_u16(gm, n_g, r, 16 * blk + (bit >> 3), row_meta);
+                const uint32_t pj = (two >> (bit & 7)) & 0xFFFu;
+                const float dd = h2f(meta_u16(gm, n_g, r, 16 * blk + 12, row_meta));
+                const float dm = h2f(meta_u16(gm, n_g, r, 16 * blk + 14, row_meta));
+                v = fmaf(w[i], (float)(pj & 63u) * dd, -((float)(pj >> 6) * dm));
+            } else if constexpr (F == QG_TERN) {
+                v = (w[i] - 1.0f) * h2f(meta_u16(gm, n_g, r, 2 * blk, row_meta));
+            } else {
+                v = (2.0f * w[i] - 1.0f) * h2f(meta_u16(gm, n_g, r, 2 * blk, row_meta));
+            }
+            o[d * CPD + i] = v;
         }
     }
 }
 
 // ---------------------------------------------------------------- launchers
 
-int pick_lpr(int nch) {
-    if (nch >= 64) return 64;
-    if (nch >= 32) return 32;
-    if (nch >= 16) return 16;
-    return 8;
+template <int F, int B, int W, int KCS>
+constexpr size_t gemv_lds_bytes() {
+    constexpr int P = 4 * W, SC = P * KCS * Fmt<F>::CPC, GS = Fmt<F>::GS;
+    return (size_t)B * SC * 4 + (size_t)B * (GS ? SC / (GS ? GS : 1) : 1) * 4 + (size_t)P * kRowGroup * B * 4;
 }
 
-template <int F, int B, int R, int LPR>
-hipError_t launch_gemv_lpr(const uint8_t* codes, const uint8_t* meta, const float* x, float* y,
-                           int N, int K, int KS, hipStream_t st) {
-    constexpr int rows_per_wg = kWaves * (64 / LPR) * R;
-    const int grid = (N + rows_per_wg - 1) / rows_per_wg;
-    constexpr int GS = Fmt<F>::GS;
-    const size_t lds = (size_t)B * KS * 4 + (GS ? (size_t)B * (KS / GS) * 4 : 0);
-    hipLaunchKernelGGL((gemv_kernel<F, B, R, LPR>), dim3(grid), dim3(kThreads), lds, st,
-                       codes, meta, x, y, N, K, KS);
+template <int F, int B, int W, int KCS>
+hipError_t launch_gemv_cfg(const uint8_t* codes, const uint8_t* meta, const float* x, float* y,
+                           int N, int K, hipStream_t st) {
+    static_assert(gemv_lds_bytes<F, B, W, KCS>() <= (size_t)kLdsBudget, "LDS budget");
+    const int grid = (N + kRowGroup - 1) / kRowGroup;
+    constexpr size_t lds = gemv_lds_bytes<F, B, W, KCS>();
+    hipLaunchKernelGGL((gemv_kernel<F, B, W, KCS>), dim3(grid), dim3(W * 64), lds, st, codes, meta, x, y, N, K);
     return hipGetLastError();
+}
+
+// Waves per workgroup: the fewest (from 1, 2, 4, 8) whose P = 4W parts cover K
+// in one slice, then fewer while the slice's LDS does not fit the budget.
+template <int F, int B, int KCS>
+int pick_waves(int K) {
+    const int nch = K / Fmt<F>::BLOCK * Fmt<F>::CB / 16;
+    int w = 1;
+    while (w < 8 && 4 * w * KCS < nch) w *= 2;
+    auto bytes = [](int ww) {
+        const int P = 4 * ww, SC = P * KCS * Fmt<F>::CPC, GS = Fmt<F>::GS;
+        return (size_t)B * SC * 4 + (size_t)B * (GS ? SC / (GS ? GS : 1) : 1) * 4 + (size_t)P * kRowGroup * B * 4;
+    };
+    while (w > 1 && bytes(w) > (size_t)kLdsBudget) w /= 2;
+    return w;
+}
+
+template <int F, int B, int KCS, int W>
+hipError_t launch_gemv_w(const uint8_t* codes, const uint8_t* meta, const float* x, float* y,
+                         int N, int K, hipStream_t st) {
+    if constexpr (gemv_lds_bytes<F, B, W, KCS>() <= (size_t)kLdsBudget) {
+        return launch_gemv_cfg<F, B, W, KCS>(codes, meta, x, y, N, K, st);
+    } else {
+        return hipErrorInvalidConfiguration;  // never chosen by pick_waves
+    }
+}
+
+// Code units per lane part: 256 weights for the wide-unit low-bit formats,
+// 8 units (128 or 256 weights) for the others; a K-quant part covers whole
+// super-blocks.
+template <int F> constexpr int lane_units() {
+    return F == QG_BIN ? 2 : (F == QG_Q2_K || F == QG_TERN) ? 4 : 8;
 }
 
 template <int F, int B>
 hipError_t launch_gemv_b(const uint8_t* codes, const uint8_t* meta, const float* x, float* y,
                          int N, int K, hipStream_t st) {
-    // K slice staged per pass: the whole K when x and its sums fit the LDS
-    // budget, else the largest multiple of 256 columns that does
-    constexpr int GS = Fmt<F>::GS;
-    auto bytes = [](int ks) { return (size_t)B * ks * 4 + (GS ? (size_t)B * (ks / GS) * 4 : 0); };
-    int KS = K;
-    if (bytes(KS) > (size_t)kLdsBudget) {
-        KS = 256;
-        while (bytes(KS + 256) <= (size_t)kLdsBudget) KS += 256;
-    }
-    constexpr int R = B == 1 ? 4 : (B <= 4 ? 2 : 1);
-    const int lpr = pick_lpr(KS / Fmt<F>::CPC);
-    switch (lpr) {
-        case 64: return launch_gemv_lpr<F, B, R, 64>(codes, meta, x, y, N, K, KS, st);
-        case 32: return launch_gemv_lpr<F, B, R, 32>(codes, meta, x, y, N, K, KS, st);
-        case 16: return launch_gemv_lpr<F, B, R, 16>(codes, meta, x, y, N, K, KS, st);
-        default: return launch_gemv_lpr<F, B, R, 8>(codes, meta, x, y, N, K, KS, st);
+    constexpr int KCS = lane_units<F>();
+    switch (pick_waves<F, B, KCS>(K)) {
+        case 1: return launch_gemv_w<F, B, KCS, 1>(codes, meta, x, y, N, K, st);
+        case 2: return launch_gemv_w<F, B, KCS, 2>(codes, meta, x, y, N, K, st);
+        case 4: return launch_gemv_w<F, B, KCS, 4>(codes, meta, x, y, N, K, st);
+        default: return launch_gemv_w<F, B, KCS, 8>(codes, meta, x, y, N, K, st);
     }
 }
 
@@ -483,8 +692,8 @@ hipError_t launch_gemv(int fmt, const uint8_t* codes, const uint8_t* meta, const
 template <int F>
 hipError_t launch_dequant_f(const uint8_t* codes, const uint8_t* meta, float* out, int N, int K, hipStream_t st) {
     const int64_t n = (int64_t)N * (K / Fmt<F>::CPC);
-    const int64_t grid = (n + kThreads - 1) / kThreads;
-    hipLaunchKernelGGL((dequant_kernel<F>), dim3((unsigned)grid), dim3(kThreads), 0, st, codes, meta, out, N, K);
+    const int64_t grid = (n + 255) / 256;
+    hipLaunchKernelGGL((dequant_kernel<F>), dim3((unsigned)grid), dim3(256), 0, st, codes, meta, out, N, K);
     return hipGetLastError();
 }
 
@@ -500,8 +709,7 @@ hipError_t launch_dequant(int fmt, const uint8_t* codes, const uint8_t* meta, fl
     }
 }
 
-int check_gemv_args(int fmt, const void* w, const float* x, const float* y, int64_t N, int64_t K, int B,
-                    void* ws, size_t ws_bytes) {
+int check_gemv_args(int fmt, const void* w, const float* x, const float* y, int64_t N, int64_t K, int B) {
     int rc = check_matrix(fmt, N, K);
     if (rc) return rc;
     if (!w || !x || !y) return fail(QG_EINVAL, "null w, x or y");
@@ -509,8 +717,6 @@ int check_gemv_args(int fmt, const void* w, const float* x, const float* y, int6
     if (!aligned(w, 16)) return fail(QG_EALIGN, "w must be 16-byte aligned");
     if (!aligned(x, 16)) return fail(QG_EALIGN, "x must be 16-byte aligned");
     if (!aligned(y, 4)) return fail(QG_EALIGN, "y must be 4-byte aligned");
-    (void)ws;
-    (void)ws_bytes;
     return QG_OK;
 }
 
@@ -528,8 +734,9 @@ size_t qgemv_workspace_size(int fmt, int64_t N, int64_t K, int B) {
 
 int qgemv(int fmt, const void* w, const float* x, float* y, int64_t N, int64_t K, int B,
           void* ws, size_t ws_bytes, void* stream) {
+    (void)ws; (void)ws_bytes;
     clear_error();
-    int rc = check_gemv_args(fmt, w, x, y, N, K, B, ws, ws_bytes);
+    int rc = check_gemv_args(fmt, w, x, y, N, K, B);
     if (rc) return rc;
     const uint8_t* codes = static_cast<const uint8_t*>(w);
     const uint8_t* meta = codes + qg_codes_plane_size(fmt, N, K);

@@ -12,6 +12,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <algorithm>
 #include <thread>
 #include <vector>
 
@@ -206,6 +207,17 @@ int quant_row_kquant(const float* w, int64_t K, uint8_t* codes, uint8_t* meta, i
     return QG_OK;
 }
 
+// Row-major bytes of one row group (n_g rows of rb bytes) -> the 16-row
+// interleaved order: 16-byte unit u of every row contiguous, unit after unit,
+// then each row's short last unit (rb % 16 bytes), row after row.
+void interleave_group(const uint8_t* rows, int n_g, size_t rb, uint8_t* dst) {
+    const size_t units = rb / 16, rem = rb % 16;
+    for (size_t u = 0; u < units; ++u)
+        for (int r = 0; r < n_g; ++r) std::memcpy(dst + (u * n_g + r) * 16, rows + r * rb + u * 16, 16);
+    uint8_t* tail = dst + units * n_g * 16;
+    for (int r = 0; r < n_g; ++r) std::memcpy(tail + r * rem, rows + r * rb + units * 16, rem);
+}
+
 int quant_row(int fmt, const float* w, int64_t K, uint8_t* codes, uint8_t* meta) {
     switch (fmt) {
         case QG_Q8_0: return quant_row_q8_0(w, K, codes, meta);
@@ -300,20 +312,28 @@ int qquant(int fmt, const float* w_host, int64_t N, int64_t K, void* out_host, i
     uint8_t* codes = static_cast<uint8_t*>(out_host);
     uint8_t* meta = codes + (size_t)N * row_codes;
     if (n_threads < 1) n_threads = 1;
-    if ((int64_t)n_threads > N) n_threads = (int)N;
 
+    const int64_t groups = (N + 15) / 16;
+    if ((int64_t)n_threads > groups) n_threads = (int)groups;
     std::vector<int> status(n_threads, QG_OK);
     std::vector<int64_t> bad_row(n_threads, -1);
     auto work = [&](int tid) {
         std::vector<float> row((size_t)K);
-        for (int64_t r = tid; r < N; r += n_threads) {
-            const float* src = w_host + (size_t)r * K;
-            for (int64_t k = 0; k < K; ++k) {
-                if (!std::isfinite(src[k])) { status[tid] = QG_EINVAL; bad_row[tid] = r; return; }
-                row[k] = src[k] + 0.0f;  // -0 -> +0
+        std::vector<uint8_t> gc(16 * row_codes), gm(16 * row_meta);
+        for (int64_t g = tid; g < groups; g += n_threads) {
+            const int n_g = (int)std::min<int64_t>(16, N - 16 * g);
+            for (int i = 0; i < n_g; ++i) {
+                const int64_t r = 16 * g + i;
+                const float* src = w_host + (size_t)r * K;
+                for (int64_t k = 0; k < K; ++k) {
+                    if (!std::isfinite(src[k])) { status[tid] = QG_EINVAL; bad_row[tid] = r; return; }
+                    row[k] = src[k] + 0.0f;  // -0 -> +0
+                }
+                const int s = quant_row(fmt, row.data(), K, gc.data() + i * row_codes, gm.data() + i * row_meta);
+                if (s != QG_OK) { status[tid] = s; bad_row[tid] = r; return; }
             }
-            const int s = quant_row(fmt, row.data(), K, codes + (size_t)r * row_codes, meta + (size_t)r * row_meta);
-            if (s != QG_OK) { status[tid] = s; bad_row[tid] = r; return; }
+            interleave_group(gc.data(), n_g, row_codes, codes + (size_t)(16 * g) * row_codes);
+            interleave_group(gm.data(), n_g, row_meta, meta + (size_t)(16 * g) * row_meta);
         }
     };
     if (n_threads == 1) {
@@ -336,19 +356,28 @@ int qpack_tern(const int8_t* t, const uint16_t* scale_f16, int64_t N, int64_t K,
     int rc = check_matrix(QG_TERN, N, K);
     if (rc) return rc;
     if (!t || !scale_f16 || !out_host) return fail(QG_EINVAL, "null pointer");
+    const size_t row_codes = (size_t)K / 4, row_meta = (size_t)(K / 128) * 2;
     uint8_t* codes = static_cast<uint8_t*>(out_host);
-    uint8_t* meta = codes + (size_t)N * (size_t)(K / 4);
-    for (int64_t r = 0; r < N; ++r) {
-        for (int64_t k = 0; k < K; k += 4) {
-            uint8_t byte = 0;
-            for (int i = 0; i < 4; ++i) {
-                const int v = t[(size_t)r * K + k + i];
-                if (v < -1 || v > 1) return fail(QG_EINVAL, "ternary code %d at (%lld, %lld)", v, (long long)r, (long long)(k + i));
-                byte |= (uint8_t)((v + 1) << (2 * i));
+    uint8_t* meta = codes + (size_t)N * row_codes;
+    std::vector<uint8_t> gc(16 * row_codes), gm(16 * row_meta);
+    for (int64_t g = 0; g < (N + 15) / 16; ++g) {
+        const int n_g = (int)std::min<int64_t>(16, N - 16 * g);
+        for (int i = 0; i < n_g; ++i) {
+            const int64_t r = 16 * g + i;
+            for (int64_t k = 0; k < K; k += 4) {
+                uint8_t byte = 0;
+                for (int j = 0; j < 4; ++j) {
+                    const int v = t[(size_t)r * K + k + j];
+                    if (v < -1 || v > 1)
+                        return fail(QG_EINVAL, "ternary code %d at (%lld, %lld)", v, (long long)r, (long long)(k + j));
+                    byte |= (uint8_t)((v + 1) << (2 * j));
+                }
+                gc[i * row_codes + k / 4] = byte;
             }
-            codes[(size_t)r * (K / 4) + k / 4] = byte;
+            for (int64_t b = 0; b < K / 128; ++b) put_u16(gm.data() + i * row_meta + 2 * b, scale_f16[(size_t)r * (K / 128) + b]);
         }
-        for (int64_t b = 0; b < K / 128; ++b) put_u16(meta + ((size_t)r * (K / 128) + b) * 2, scale_f16[(size_t)r * (K / 128) + b]);
+        interleave_group(gc.data(), n_g, row_codes, codes + (size_t)(16 * g) * row_codes);
+        interleave_group(gm.data(), n_g, row_meta, meta + (size_t)(16 * g) * row_meta);
     }
     return QG_OK;
 }
@@ -358,19 +387,28 @@ int qpack_bin(const uint8_t* bits, const uint16_t* scale_f16, int64_t N, int64_t
     int rc = check_matrix(QG_BIN, N, K);
     if (rc) return rc;
     if (!bits || !scale_f16 || !out_host) return fail(QG_EINVAL, "null pointer");
+    const size_t row_codes = (size_t)K / 8, row_meta = (size_t)(K / 128) * 2;
     uint8_t* codes = static_cast<uint8_t*>(out_host);
-    uint8_t* meta = codes + (size_t)N * (size_t)(K / 8);
-    for (int64_t r = 0; r < N; ++r) {
-        for (int64_t k = 0; k < K; k += 8) {
-            uint8_t byte = 0;
-            for (int i = 0; i < 8; ++i) {
-                const unsigned v = bits[(size_t)r * K + k + i];
-                if (v > 1) return fail(QG_EINVAL, "1-bit code %u at (%lld, %lld)", v, (long long)r, (long long)(k + i));
-                byte |= (uint8_t)(v << i);
+    uint8_t* meta = codes + (size_t)N * row_codes;
+    std::vector<uint8_t> gc(16 * row_codes), gm(16 * row_meta);
+    for (int64_t g = 0; g < (N + 15) / 16; ++g) {
+        const int n_g = (int)std::min<int64_t>(16, N - 16 * g);
+        for (int i = 0; i < n_g; ++i) {
+            const int64_t r = 16 * g + i;
+            for (int64_t k = 0; k < K; k += 8) {
+                uint8_t byte = 0;
+                for (int j = 0; j < 8; ++j) {
+                    const unsigned v = bits[(size_t)r * K + k + j];
+                    if (v > 1)
+                        return fail(QG_EINVAL, "1-bit code %u at (%lld, %lld)", v, (long long)r, (long long)(k + j));
+                    byte |= (uint8_t)(v << j);
+                }
+                gc[i * row_codes + k / 8] = byte;
             }
-            codes[(size_t)r * (K / 8) + k / 8] = byte;
+            for (int64_t b = 0; b < K / 128; ++b) put_u16(gm.data() + i * row_meta + 2 * b, scale_f16[(size_t)r * (K / 128) + b]);
         }
-        for (int64_t b = 0; b < K / 128; ++b) put_u16(meta + ((size_t)r * (K / 128) + b) * 2, scale_f16[(size_t)r * (K / 128) + b]);
+        interleave_group(gc.data(), n_g, row_codes, codes + (size_t)(16 * g) * row_codes);
+        interleave_group(gm.data(), n_g, row_meta, meta + (size_t)(16 * g) * row_meta);
     }
     return QG_OK;
 }

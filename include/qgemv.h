@@ -29,8 +29,15 @@
  *
  * Packed matrix layout (one [N][K] matrix, format f with block size bs):
  *   [codes plane][meta plane], codes plane = N*(K/bs)*code_bytes bytes,
- *   meta plane = N*(K/bs)*meta_bytes bytes, both row-major over (row, block);
- *   total qg_packed_size() = N*K*bpw/8 exactly.
+ *   meta plane = N*(K/bs)*meta_bytes bytes; total qg_packed_size() =
+ *   N*K*bpw/8 exactly.  Each plane is the row-major image of its rows (row n:
+ *   its blocks' code bytes, resp. meta bytes, in block order) interleaved by
+ *   groups of 16 rows (the low-bit README page's row repack for dot-product
+ *   lanes): group g holds rows 16g .. 16g+n_g-1 (n_g = min(16, N-16g)) and
+ *   starts at byte 16*g*row_bytes; within it, 16-byte unit u of row r sits at
+ *   (u*n_g + r)*16, and when row_bytes is not a multiple of 16 the rows' short
+ *   last units (L = row_bytes % 16 bytes) follow the full units at
+ *   full_units*n_g*16 + r*L.
  *     format  bs   code B  meta B  bpw    meta entry
  *     Q8_0    32   32      2       8.5    fp16 d; codes int8
  *     Q4_0    32   16      2       4.5    fp16 d (signed); nibble = code + 8

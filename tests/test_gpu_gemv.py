@@ -171,11 +171,11 @@ def test_full_size_sampled_rows(fmt, n, k, b):
     cpr = (k // spec.block) * spec.code_bytes
     mpr = (k // spec.block) * spec.meta_bytes
     cp = OF.codes_plane_size(fmt, n, k)
+    codes_rows = OF.deinterleave_rows(packed[:cp], n, cpr)
+    meta_rows = OF.deinterleave_rows(packed[cp:], n, mpr)
     sub_packed = OF.pack(fmt, sub)
     scp = OF.codes_plane_size(fmt, len(rows), k)
-    for i, r in enumerate(rows):
-        np.testing.assert_array_equal(packed[r * cpr:(r + 1) * cpr], sub_packed[i * cpr:(i + 1) * cpr])
-        np.testing.assert_array_equal(packed[cp + r * mpr:cp + (r + 1) * mpr],
-                                      sub_packed[scp + i * mpr:scp + (i + 1) * mpr])
+    np.testing.assert_array_equal(codes_rows[rows], OF.deinterleave_rows(sub_packed[:scp], len(rows), cpr))
+    np.testing.assert_array_equal(meta_rows[rows], OF.deinterleave_rows(sub_packed[scp:], len(rows), mpr))
     assert_parity(y[:, rows], OF.dequant(fmt, sub), x, f"{fmt} {n}x{k} B={b}")
     assert np.all(np.isfinite(y))
