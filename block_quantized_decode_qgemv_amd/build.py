@@ -11,6 +11,7 @@ from __future__ import annotations
 import os
 import subprocess
 import sys
+from concurrent.futures import ThreadPoolExecutor
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
@@ -42,20 +43,19 @@ def _run(cmd, verbose):
 
 def build(verbose: bool = True) -> str:
     os.makedirs(BUILD_DIR, exist_ok=True)
-    objs = []
+    jobs = []  # (command, object); the sources compile concurrently
     for src in DEVICE_SOURCES:
-        path = os.path.join(CSRC, src)
-        if not os.path.exists(path):
-            continue
         obj = os.path.join(BUILD_DIR, src + ".o")
-        _run([HIPCC, *HIP_FLAGS, "-c", path, "-o", obj], verbose)
-        objs.append(obj)
+        jobs.append(([HIPCC, *HIP_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj], obj))
     for src in HOST_SOURCES:
         obj = os.path.join(BUILD_DIR, src + ".o")
-        _run(["g++", *HOST_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj], verbose)
-        objs.append(obj)
+        jobs.append((["g++", *HOST_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj], obj))
+    with ThreadPoolExecutor(max_workers=min(len(jobs), 8)) as pool:
+        for f in [pool.submit(_run, cmd, verbose) for cmd, _ in jobs]:
+            f.result()
     tmp = LIB + ".tmp"
-    _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp, "-lpthread"], verbose)
+    _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *[o for _, o in jobs], "-o", tmp, "-lpthread"],
+         verbose)
     os.replace(tmp, LIB)
     return LIB
 

@@ -1,0 +1,540 @@
+// Row-group GEMV core shared by the dense GEMV (gemv.hip) and the MoE expert
+// kernels (moe.hip): format traits, code decoders, interleaved addressing and
+// the Gemv<F, B, W, KCS> device routine that computes one 16-row group.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "internal.h"
+
+namespace qg {
+namespace core {
+
+constexpr int kLdsBudget = 64 * 1024;  // bytes of x + column sums per workgroup
+constexpr int kRowGroup = 16;          // rows per interleave group (layout constant)
+
+// ------------------------------------------------------------------ traits
+//
+// CPC: weights per 16-byte code unit; MBU: meta bytes per code unit; GS:
+// weights per column sum (0 = none); BLOCK, CB, MB: the format's block.
+template <int F> struct Fmt;
+template <> struct Fmt<QG_Q8_0> { static constexpr int CPC = 16,  MBU = 1, GS = 0,   BLOCK = 32,  CB = 32,  MB = 2; };
+template <> struct Fmt<QG_Q4_0> { static constexpr int CPC = 32,  MBU = 2, GS = 32,  BLOCK = 32,  CB = 16,  MB = 2; };
+template <> struct Fmt<QG_Q4_1> { static constexpr int CPC = 32,  MBU = 4, GS = 32,  BLOCK = 32,  CB = 16,  MB = 4; };
+template <> struct Fmt<QG_Q4_K> { static constexpr int CPC = 32,  MBU = 2, GS = 32,  BLOCK = 256, CB = 128, MB = 16; };
+template <> struct Fmt<QG_Q2_K> { static constexpr int CPC = 64,  MBU = 4, GS = 32,  BLOCK = 256, CB = 64,  MB = 16; };
+template <> struct Fmt<QG_TERN> { static constexpr int CPC = 64,  MBU = 1, GS = 64,  BLOCK = 128, CB = 32,  MB = 2; };
+template <> struct Fmt<QG_BIN>  { static constexpr int CPC = 128, MBU = 2, GS = 128, BLOCK = 128, CB = 16,  MB = 2; };
+
+__device__ __forceinline__ float h2f(uint32_t bits16) {
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)bits16);
+}
+
+// Keep a masked code dword opaque to the optimizer so each byte pair converts
+// with one v_cvt_pk_f32_fp8 (the mask would otherwise be re-folded into
+// per-byte bit-field extracts).
+__device__ __forceinline__ uint32_t opaque(uint32_t v) {
+    asm volatile("" : "+v"(v));
+    return v;
+}
+
+// Bytes 0..3 of v (each 0..15) as floats n * 2^-9 (OCP e4m3 encodes a byte n
+// in 0..15 exactly as n * 2^-9, subnormals included).
+__device__ __forceinline__ void fp8x4(uint32_t v, float& b0, float& b1, float& b2, float& b3) {
+    const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)v, false);
+    const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)v, true);
+    b0 = lo[0]; b1 = lo[1]; b2 = hi[0]; b3 = hi[1];
+}
+
+// ------------------------------------------------------------ DPP reduction
+
+template <int CTRL, int ROW_MASK = 0xF>
+__device__ __forceinline__ float dpp(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, ROW_MASK, 0xF, false));
+}
+
+// Sum over aligned groups of LPR lanes (LPR in 4..64); the full sum is valid in
+// the last lane of each group.
+template <int LPR>
+__device__ __forceinline__ float group_sum(float v) {
+    v += dpp<0xB1>(v);                                 // quad_perm [1,0,3,2]
+    v += dpp<0x4E>(v);                                 // quad_perm [2,3,0,1]
+    if constexpr (LPR >= 8) v += dpp<0x141>(v);        // row_half_mirror
+    if constexpr (LPR >= 16) v += dpp<0x140>(v);       // row_mirror
+    if constexpr (LPR >= 32) v += dpp<0x142, 0xA>(v);  // row_bcast:15 into rows 1, 3
+    if constexpr (LPR >= 64) v += dpp<0x143, 0xC>(v);  // row_bcast:31 into rows 2, 3
+    return v;
+}
+
+// -------------------------------------------------- per-format unit decode
+//
+// Unit<F>::decode(v, w) turns one code dword into the CPC/4 code values of
+// its columns, in column order, scaled by 2^-9 (the value of the e4m3 byte
+// 0x01) for the formats decoded through e4m3 (all but Q8_0).
+
+template <int F> struct Unit;
+
+template <> struct Unit<QG_Q8_0> {
+    static constexpr int CPD = 4;
+    __device__ static void decode(uint32_t v, float* w) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) w[k] = (float)(int)(int8_t)(v >> (8 * k));
+    }
+};
+
+// nibble i of a block in byte i>>1, low nibble first: byte k of a dword holds
+// columns 2k (low) and 2k+1 (high)
+template <> struct Unit<QG_Q4_0> {
+    static constexpr int CPD = 8;
+    __device__ static void decode(uint32_t v, float* w) {
+        const uint32_t lo = opaque(v & 0x0F0F0F0Fu), hi = opaque((v >> 4) & 0x0F0F0F0Fu);
+        fp8x4(lo, w[0], w[2], w[4], w[6]);
+        fp8x4(hi, w[1], w[3], w[5], w[7]);
+    }
+};
+template <> struct Unit<QG_Q4_1> : Unit<QG_Q4_0> {};
+template <> struct Unit<QG_Q4_K> : Unit<QG_Q4_0> {};
+
+// 2-bit field i in byte i>>2 at bits 2*(i&3): byte k of a dword holds columns
+// 4k..4k+3
+template <> struct Unit<QG_Q2_K> {
+    static constexpr int CPD = 16;
+    __device__ static void decode(uint32_t v, float* w) {
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            const uint32_t f = opaque((v >> (2 * s)) & 0x03030303u);
+            fp8x4(f, w[s], w[4 + s], w[8 + s], w[12 + s]);
+        }
+    }
+};
+template <> struct Unit<QG_TERN> : Unit<QG_Q2_K> {};
+
+// bit i in byte i>>3 at bit i&7: byte k of a dword holds columns 8k..8k+7
+template <> struct Unit<QG_BIN> {
+    static constexpr int CPD = 32;
+    __device__ static void decode(uint32_t v, float* w) {
+#pragma unroll
+        for (int s = 0; s < 8; ++s) {
+            const uint32_t f = opaque((v >> s) & 0x01010101u);
+            fp8x4(f, w[s], w[8 + s], w[16 + s], w[24 + s]);
+        }
+    }
+};
+
+// Weight bytes are read exactly once per call: stream them past the caches.
+#ifndef QG_WEIGHT_NT
+#define QG_WEIGHT_NT 1
+#endif
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+template <typename V> struct NtLoad;
+template <> struct NtLoad<uint4> {
+    __device__ static uint4 ld(const uint8_t* p) {
+#if QG_WEIGHT_NT
+        const u32x4_t v = __builtin_nontemporal_load((const u32x4_t*)p);
+        return make_uint4(v.x, v.y, v.z, v.w);
+#else
+        return *(const uint4*)p;
+#endif
+    }
+};
+template <> struct NtLoad<uint2> {
+    __device__ static uint2 ld(const uint8_t* p) {
+#if QG_WEIGHT_NT
+        const u32x2_t v = __builtin_nontemporal_load((const u32x2_t*)p);
+        return make_uint2(v.x, v.y);
+#else
+        return *(const uint2*)p;
+#endif
+    }
+};
+template <> struct NtLoad<uint32_t> {
+    __device__ static uint32_t ld(const uint8_t* p) {
+#if QG_WEIGHT_NT
+        return __builtin_nontemporal_load((const uint32_t*)p);
+#else
+        return *(const uint32_t*)p;
+#endif
+    }
+};
+template <typename V>
+__device__ __forceinline__ V ld_weights(const uint8_t* p) { return NtLoad<V>::ld(p); }
+
+// --------------------------------------------------- interleaved addressing
+//
+// A row group g holds n_g = min(16, N - 16g) rows.  Its codes start at
+// 16*g*row_codes in the codes plane and its meta at 16*g*row_meta in the meta
+// plane.  Unit u of row r: base + (u*n_g + r)*16; a row's short last meta
+// unit (row_meta % 16 bytes) sits after the group's full units at
+// base + full_units*n_g*16 + r*rem.
+
+// Meta bytes [o0, o0 + NB) of row r (NB = 4, 8, 16 or 32; o0 a multiple of
+// min(NB, 16)).  Full units are read with one vector load each; a part that
+// reaches into the short last unit is read two bytes at a time and only up to
+// the row's last meta byte (bytes past it belong to no code unit in range).
+template <int NB>
+__device__ __forceinline__ void load_meta(const uint8_t* gm, int n_g, int r, int o0, int row_meta,
+                                          uint32_t (&wd)[NB / 4]) {
+    const int full = row_meta >> 4, rem = row_meta & 15;
+    constexpr int W = NB >= 16 ? 4 : NB / 4;  // dwords per part
+#pragma unroll
+    for (int h = 0; h < (NB + 15) / 16; ++h) {
+        const int o = o0 + 16 * h;
+        const int u = o >> 4, i0 = o & 15;
+        if (u < full) {
+            const uint8_t* p = gm + ((size_t)u * n_g + r) * 16 + i0;
+            if constexpr (W == 4) {
+                const uint4 v = *(const uint4*)p;
+                wd[4 * h] = v.x; wd[4 * h + 1] = v.y; wd[4 * h + 2] = v.z; wd[4 * h + 3] = v.w;
+            } else if constexpr (W == 2) {
+                const uint2 v = *(const uint2*)p;
+                wd[0] = v.x; wd[1] = v.y;
+            } else {
+                wd[0] = *(const uint32_t*)p;
+            }
+        } else {
+            const uint8_t* p = gm + (size_t)full * n_g * 16 + (size_t)r * rem;
+#pragma unroll
+            for (int k = 0; k < W; ++k) {
+                uint32_t lo = 0, hi = 0;
+                if (u == full && i0 + 4 * k < rem) lo = *(const uint16_t*)(p + i0 + 4 * k);
+                if (u == full && i0 + 4 * k + 2 < rem) hi = *(const uint16_t*)(p + i0 + 4 * k + 2);
+                wd[W * h + k] = lo | (hi << 16);
+            }
+        }
+    }
+}
+
+// ----------------------------------------------------------- scale applies
+//
+// Apply<F>::unit(wd, i, s, P, X, st, acc, ok) folds the partial sum P (sum of
+// decoded code * x over sub-group s of the lane's unit i) and the column sum X
+// of that sub-group into the row sum acc, using the lane's meta words wd.
+// i and s are compile-time after unrolling, so every meta field extraction
+// has constant positions.  K-quants keep two running sums per batch row in st
+// and apply d, dmin once per super-block.  Units with ok false lie past the
+// end of K and contribute nothing.
+
+struct KqState { float sp = 0.0f, tx = 0.0f; };
+
+// fp16 half-word h of the meta words
+__device__ __forceinline__ float meta_h(const uint32_t* wd, int h) {
+    return h2f((wd[h >> 1] >> (16 * (h & 1))) & 0xFFFFu);
+}
+
+template <int F> struct Apply;
+
+template <> struct Apply<QG_Q8_0> {
+    static constexpr int SUBS = 1;
+    // unit i belongs to block i/2; w = q d
+    __device__ static void unit(const uint32_t* wd, int i, int, float P, float, KqState&, float& acc, bool ok) {
+        const float v = fmaf(meta_h(wd, i >> 1), P, acc);
+        acc = ok ? v : acc;
+    }
+};
+
+template <> struct Apply<QG_Q4_0> {
+    static constexpr int SUBS = 1;
+    // w = (n - 8) d:  d * (512 P - 8 X)
+    __device__ static void unit(const uint32_t* wd, int i, int, float P, float X, KqState&, float& acc, bool ok) {
+        const float v = fmaf(meta_h(wd, i), fmaf(512.0f, P, -8.0f * X), acc);
+        acc = ok ? v : acc;
+    }
+};
+
+template <> struct Apply<QG_Q4_1> {
+    static constexpr int SUBS = 1;
+    // w = n d + m:  (512 d) P + m X
+    __device__ static void unit(const uint32_t* wd, int i, int, float P, float X, KqState&, float& acc, bool ok) {
+        const float v = fmaf(512.0f * meta_h(wd, 2 * i), P, fmaf(meta_h(wd, 2 * i + 1), X, acc));
+        acc = ok ? v : acc;
+    }
+};
+
+// K-quant meta entry: pairs p_j = s_j | t_j << 6 at bits [12j, 12j+12) of words
+// 0..2, fp16 d and dmin in word 3.
+__device__ __forceinline__ uint32_t kq_pair(const uint32_t* e, int j) {
+    const int bit = 12 * j, w = bit >> 5, sh = bit & 31;
+    return sh <= 20 ? (e[w] >> sh) : __builtin_amdgcn_alignbit(e[w + 1], e[w], sh);
+}
+
+// w = n s d - t dmin:  per super-block (512 d) * sum_j s_j P_j - dmin * sum_j t_j X_j
+template <int UPS>  // code units per super-block (8 for Q4_K, 4 for Q2_K)
+struct ApplyKq {
+    static constexpr int SUBS = 8 / UPS;
+    __device__ static void unit(const uint32_t* wd, int i, int s, float P, float X, KqState& st, float& acc, bool ok) {
+        const uint32_t* e = wd + 4 * (i / UPS);
+        const int j = (i % UPS) * SUBS + s;
+        const uint32_t p = kq_pair(e, j);
+        st.sp = fmaf((float)(p & 63u), P, st.sp);
+        st.tx = fmaf((float)((p >> 6) & 63u), X, st.tx);
+        if (j == 7) {
+            const float v = fmaf(512.0f * h2f(e[3] & 0xFFFFu), st.sp, fmaf(-h2f(e[3] >> 16), st.tx, acc));
+            acc = ok ? v : acc;
+            st.sp = 0.0f;
+            st.tx = 0.0f;
+        }
+    }
+};
+template <> struct Apply<QG_Q4_K> : ApplyKq<8> {};
+template <> struct Apply<QG_Q2_K> : ApplyKq<4> {};
+
+template <> struct Apply<QG_TERN> {
+    static constexpr int SUBS = 1;
+    // f = t + 1:  w = (f - 1) d  ->  d * (512 P - X); unit i is half of block i/2
+    __device__ static void unit(const uint32_t* wd, int i, int, float P, float X, KqState&, float& acc, bool ok) {
+        const float v = fmaf(meta_h(wd, i >> 1), fmaf(512.0f, P, -X), acc);
+        acc = ok ? v : acc;
+    }
+};
+
+template <> struct Apply<QG_BIN> {
+    static constexpr int SUBS = 1;
+    // w = (2 beta - 1) d  ->  d * (1024 P - X)
+    __device__ static void unit(const uint32_t* wd, int i, int, float P, float X, KqState&, float& acc, bool ok) {
+        const float v = fmaf(meta_h(wd, i), fmaf(1024.0f, P, -X), acc);
+        acc = ok ? v : acc;
+    }
+};
+
+// ------------------------------------------------------------ GEMV kernel
+//
+// Template: format F, batch B, waves W, code units per lane per slice KCS.
+// Grid: one workgroup per 16-row group.  Dynamic LDS: x slice [B][SC]
+// (SC = P*KCS*CPC columns), column sums [B][SC/GS], partials [P][16][B].
+
+template <int F, int B, int W, int KCS>
+struct Gemv {
+    using T = Fmt<F>;
+    using U = Unit<F>;
+    using A = Apply<F>;
+    static constexpr int NT = W * 64, P = 4 * W;
+    static constexpr int CPC = T::CPC, CPD = U::CPD, GS = T::GS, SUBS = A::SUBS;
+    static constexpr int SU = P * KCS;                      // code units per slice
+    static constexpr int SC = SU * CPC;                     // columns per slice
+    static constexpr int NSUM = GS ? SC / (GS ? GS : 1) : 1;  // column sums per slice row
+    static constexpr int MB = KCS * T::MBU;                 // meta bytes per lane part
+    static constexpr int DPS = 4 / SUBS;                    // code dwords per sub-group
+    static constexpr int X0 = 4;                            // x float4 per thread requested first
+    static_assert(GS == 0 || GS == CPC / SUBS, "one column sum per sub-group");
+    static_assert((4 * NT) % (GS ? GS : 4) == 0, "a staging round covers whole sum groups");
+
+    // xr[k0 + c] of an activation row xr, c = 4*(tid + NT*i) (float4 per thread)
+    __device__ static float4 ld_x(const float* __restrict__ xr, int k0, int cols, int c) {
+        return c < cols ? *(const float4*)(xr + k0 + c) : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+    // stage one float4 of row b at column c into LDS and, when it completes a
+    // group of GS columns (a DPP sum over the GS/4 threads that hold it), the
+    // group's column sum; every thread calls this the same number of times
+    __device__ static void put_x(float* xs, float* xsum, int tid, int cols, int b, int c, float4 v) {
+        if (c < cols) *(float4*)(xs + b * SC + c) = v;
+        if constexpr (GS > 0) {
+            const float s = group_sum<GS / 4>((v.x + v.y) + (v.z + v.w));
+            if (c < cols && (tid % (GS / 4)) == GS / 4 - 1) xsum[b * NSUM + c / GS] = s;
+        }
+    }
+
+    // Decode this lane's KCS units and fold them into acc; units i >= nvalid
+    // lie past the end of K and contribute nothing.
+    __device__ static void compute(const uint4 (&q)[KCS], const uint32_t* wd, const float* xs, const float* xsum,
+                                   int lc0, int nvalid, float (&acc)[B]) {
+        KqState st[B];
+#pragma unroll
+        for (int i = 0; i < KCS; ++i) {
+            const bool ok = i < nvalid;
+            const uint32_t dw[4] = {q[i].x, q[i].y, q[i].z, q[i].w};
+            const int xo = ok ? (lc0 + i) * CPC : 0;  // units past K read staged x harmlessly
+#pragma unroll
+            for (int s = 0; s < SUBS; ++s) {
+                float ps[B];
+#pragma unroll
+                for (int b = 0; b < B; ++b) ps[b] = 0.0f;
+#pragma unroll
+                for (int d = s * DPS; d < (s + 1) * DPS; ++d) {
+                    float w[CPD];
+                    U::decode(dw[d], w);
+#pragma unroll
+                    for (int b = 0; b < B; ++b) {
+                        const float* xb = xs + b * SC + xo + d * CPD;
+#pragma unroll
+                        for (int k = 0; k < CPD; k += 4) {
+                            const float4 xx = *(const float4*)(xb + k);
+                            ps[b] = fmaf(w[k], xx.x, ps[b]);
+                            ps[b] = fmaf(w[k + 1], xx.y, ps[b]);
+                            ps[b] = fmaf(w[k + 2], xx.z, ps[b]);
+                            ps[b] = fmaf(w[k + 3], xx.w, ps[b]);
+                        }
+                    }
+                    // wide decodes at B > 1: one code dword live at a time
+                    if constexpr (CPD * B >= 16) __builtin_amdgcn_sched_barrier(0);
+                }
+#pragma unroll
+                for (int b = 0; b < B; ++b) {
+                    const float X = GS > 0 ? xsum[b * NSUM + (ok ? (lc0 + i) * SUBS + s : 0)] : 0.0f;
+                    A::unit(wd, i, s, ps[b], X, st[b], acc[b], ok);
+                }
+            }
+            // keep one unit's decode live at a time (bounds register use)
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+
+    // One 16-row group g of a packed [N][K] matrix against nb <= B activation
+    // rows; xrow(b) gives row b (K floats, 16-byte aligned).  After the parts
+    // are combined, every thread calls epi(sums, n_g) with sums[rw * B + b]
+    // the row sums in LDS (rows rw < n_g, batch rows b < nb valid).
+    template <class XRow, class Epi>
+    __device__ static void run(const uint8_t* __restrict__ codes, const uint8_t* __restrict__ meta,
+                               int N, int K, int g, XRow xrow, int nb, Epi epi) {
+        extern __shared__ float lds[];
+        float* xs = lds;                    // [B][SC]
+        float* xsum = xs + B * SC;          // [B][NSUM]
+        float* part = xsum + B * NSUM;      // [P][16][B]; reused for the sums
+
+        const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+        const int r = lane & 15, p = wave * 4 + (lane >> 4);
+        const int n_g = min(kRowGroup, N - g * kRowGroup);
+        const int rr = min(r, n_g - 1);
+        const int nb_blocks = K / T::BLOCK;
+        const int row_codes = nb_blocks * T::CB, row_meta = nb_blocks * T::MB;
+        const int nch = row_codes >> 4;
+        const bool meta_whole = (row_meta & 15) == 0;  // no short last meta unit
+        // this lane's row: unit c at gcr + c*ustride, meta unit u at gmr + u*ustride
+        const int ustride = n_g * 16;
+        const uint8_t* gcr = codes + (size_t)g * kRowGroup * row_codes + rr * 16;
+        const uint8_t* gm = meta + (size_t)g * kRowGroup * row_meta;
+        const uint8_t* gmr = gm + rr * 16;
+        const float* x0 = xrow(0);
+
+        float acc[B];
+#pragma unroll
+        for (int b = 0; b < B; ++b) acc[b] = 0.0f;
+
+        for (int c_slice = 0; c_slice < nch; c_slice += SU) {
+            const int k0 = c_slice * CPC;
+            const int cols = min(SC, K - k0);
+            if (c_slice) __syncthreads();  // the previous slice's x is consumed
+
+            // (1) the first X0 float4 of x row 0 go out before the code loads,
+            // so waiting for them does not wait for the codes
+            float4 xv[X0];
+#pragma unroll
+            for (int i = 0; i < X0; ++i) xv[i] = ld_x(x0, k0, cols, 4 * (tid + NT * i));
+
+            // (2) this lane's meta bytes and code units
+            const int c0 = c_slice + p * KCS;
+            const int nvalid = nch - c0;  // units of the part inside K (may be <= 0)
+            uint4 q[KCS];
+            uint32_t wd[MB / 4];
+            // meta first: the scale path reads it from the first unit on, and
+            // loads complete in issue order
+            const int m0 = min(c0, (nch - 1) / KCS * KCS) * T::MBU;
+            if (meta_whole) {
+                // whole 16-byte units: one vector load per unit (or half unit)
+#pragma unroll
+                for (int h = 0; h < (MB + 15) / 16; ++h) {
+                    const int o = m0 + 16 * h;
+                    const uint8_t* pm = gmr + (o >> 4) * ustride + (o & 15);
+                    if constexpr (MB >= 16) {
+                        const uint4 v = ld_weights<uint4>(pm);
+                        wd[4 * h] = v.x; wd[4 * h + 1] = v.y; wd[4 * h + 2] = v.z; wd[4 * h + 3] = v.w;
+                    } else if constexpr (MB == 8) {
+                        const uint2 v = ld_weights<uint2>(pm);
+                        wd[0] = v.x; wd[1] = v.y;
+                    } else {
+                        wd[0] = ld_weights<uint32_t>(pm);
+                    }
+                }
+            } else {
+                load_meta<MB>(gm, n_g, rr, m0, row_meta, wd);
+            }
+            // a unit past the end of K reads the row's last unit instead (its
+            // contribution is dropped), so every load is unconditional
+#pragma unroll
+            for (int i = 0; i < KCS; ++i) q[i] = ld_weights<uint4>(gcr + min(c0 + i, nch - 1) * ustride);
+
+            // (3) x to LDS with the column sums
+            const int rounds = (cols + 4 * NT - 1) / (4 * NT);  // float4 rounds per batch row
+#pragma unroll
+            for (int i = 0; i < X0; ++i)
+                if (i < rounds) put_x(xs, xsum, tid, cols, 0, 4 * (tid + NT * i), xv[i]);
+            for (int i = X0; i < rounds; ++i) {
+                const int c = 4 * (tid + NT * i);
+                put_x(xs, xsum, tid, cols, 0, c, ld_x(x0, k0, cols, c));
+            }
+#pragma unroll
+            for (int b = 1; b < B; ++b) {
+                if (b < nb) {
+                    const float* xb = xrow(b);
+                    for (int i0 = 0; i0 < rounds; i0 += X0) {
+                        float4 v[X0];
+#pragma unroll
+                        for (int i = 0; i < X0; ++i) v[i] = ld_x(xb, k0, cols, 4 * (tid + NT * (i0 + i)));
+#pragma unroll
+                        for (int i = 0; i < X0; ++i)
+                            if (i0 + i < rounds) put_x(xs, xsum, tid, cols, b, 4 * (tid + NT * (i0 + i)), v[i]);
+                    }
+                }
+            }
+            __syncthreads();
+
+            // (4) decode once, multiply for every batch row
+            compute(q, wd, xs, xsum, p * KCS, nvalid, acc);
+        }
+
+        // (5) combine the P parts of each row in a fixed order
+#pragma unroll
+        for (int b = 0; b < B; ++b) part[(p * kRowGroup + r) * B + b] = acc[b];
+        __syncthreads();
+        constexpr int PER = (kRowGroup * B + NT - 1) / NT;  // sums per thread
+        float sum[PER];
+#pragma unroll
+        for (int j = 0; j < PER; ++j) {
+            const int t = tid + NT * j;
+            sum[j] = 0.0f;
+            if (t < kRowGroup * B) {
+#pragma unroll
+                for (int pp = 0; pp < P; ++pp) sum[j] += part[(pp * kRowGroup + t / B) * B + t % B];
+            }
+        }
+        __syncthreads();
+#pragma unroll
+        for (int j = 0; j < PER; ++j)
+            if (tid + NT * j < kRowGroup * B) part[tid + NT * j] = sum[j];  // sums[rw * B + b]
+        __syncthreads();
+        epi(part, n_g);
+    }
+};
+
+template <int F, int B, int W, int KCS>
+constexpr size_t gemv_lds_bytes() {
+    constexpr int P = 4 * W, SC = P * KCS * Fmt<F>::CPC, GS = Fmt<F>::GS;
+    return (size_t)B * SC * 4 + (size_t)B * (GS ? SC / (GS ? GS : 1) : 1) * 4 + (size_t)P * kRowGroup * B * 4;
+}
+
+// Code units per lane part: 256 weights for the wide-unit low-bit formats,
+// 8 units (128 or 256 weights) for the others; a K-quant part covers whole
+// super-blocks.
+template <int F> constexpr int lane_units() {
+    return F == QG_BIN ? 2 : (F == QG_Q2_K || F == QG_TERN) ? 4 : 8;
+}
+
+// Waves per workgroup: the fewest (from 1, 2, 4, 8) whose P = 4W parts cover K
+// in one slice, then fewer while the slice's LDS does not fit the budget.
+template <int F, int B, int KCS>
+int pick_waves(int K) {
+    const int nch = K / Fmt<F>::BLOCK * Fmt<F>::CB / 16;
+    int w = 1;
+    while (w < 8 && 4 * w * KCS < nch) w *= 2;
+    auto bytes = [](int ww) {
+        const int P = 4 * ww, SC = P * KCS * Fmt<F>::CPC, GS = Fmt<F>::GS;
+        return (size_t)B * SC * 4 + (size_t)B * (GS ? SC / (GS ? GS : 1) : 1) * 4 + (size_t)P * kRowGroup * B * 4;
+    };
+    while (w > 1 && bytes(w) > (size_t)kLdsBudget) w /= 2;
+    return w;
+}
+
+}  // namespace core
+}  // namespace qg

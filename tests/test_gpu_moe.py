@@ -1,0 +1,271 @@
+"""GPU parity of the routed MoE expert layer (moe_expert_ffn) against the
+oracle's moe_ref, through the C ABI.
+
+Experts are oracle-quantized Student-t(5)*0.02 matrices; x, residual, router
+and shared-gate logits are N(0,1).  Small layers use fully independent
+experts; the full layer (512 experts + 1 shared, hidden 4096, intermediate
+1024) writes real experts only into the slots the oracle's router selects and
+fills every other slot with 0xFF bytes (fp16 NaN scales), so a kernel that
+reads a wrong expert produces NaN."""
+import numpy as np
+import pytest
+
+import block_quantized_decode_qgemv_amd as qg
+import workloads
+from oracle import formats as OF
+from oracle import moe as OM
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+KFORMATS = ["q4_k", "q2_k"]
+
+
+def dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).to("cuda")
+
+
+class Expert:
+    """One expert: packed gate/up (2I x H, rows interleaved) and down (H x I)
+    bytes, and the dequantized fp32 gate, up and down matrices."""
+
+    def __init__(self, fmt, wg, wu, wd):
+        gu = OF.quantize(fmt, OM.interleave_gate_up(wg, wu))
+        dn = OF.quantize(fmt, wd)
+        self.gu_packed = OF.pack(fmt, gu)
+        self.dn_packed = OF.pack(fmt, dn)
+        gu_deq = OF.dequant(fmt, gu)
+        self.gate, self.up = gu_deq[0::2], gu_deq[1::2]
+        self.down = OF.dequant(fmt, dn)
+
+
+def random_expert(fmt, h, i, seed, e):
+    return Expert(fmt, workloads.student_t_weights(i, h, seed, 3 * e),
+                  workloads.student_t_weights(i, h, seed, 3 * e + 1),
+                  workloads.student_t_weights(h, i, seed, 3 * e + 2))
+
+
+class Layer:
+    """Sequence-like views of the experts for moe_ref (index E = shared)."""
+
+    def __init__(self, experts):
+        self.experts = experts
+
+    def view(self, attr):
+        ex = self.experts
+
+        class _V:
+            def __len__(self):
+                return len(ex)
+
+            def __getitem__(self, j):
+                return getattr(ex[j], attr)
+
+        return _V()
+
+
+def inputs(t, e, h, seed):
+    x = workloads.normal((t, h), seed, 9001)
+    residual = workloads.normal((t, h), seed, 9002)
+    logits = workloads.normal((t, e), seed, 9003)
+    s = workloads.normal((t,), seed, 9004)
+    return x, residual, logits, s
+
+
+def run_moe(fmt, gu_d, dn_d, e, h, i, top_k, x, residual, logits, s, flags=0, alias_residual=False):
+    t = x.shape[0]
+    x_d = dev(x)
+    r_d = x_d if alias_residual else dev(residual)
+    out = torch.full((t, h), float("nan"), device="cuda")
+    ws_bytes = qg.moe_expert_ffn_workspace_size(t, e, h, i, top_k)
+    assert ws_bytes > 0
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
+    qg.moe_expert_ffn(fmt, gu_d, dn_d, e, h, i, top_k, x_d, r_d, dev(logits), dev(s), t, out, ws, ws_bytes,
+                      flags=flags)
+    torch.cuda.synchronize()
+    return out.cpu().numpy()
+
+
+def check(out, layer, x, residual, logits, s, top_k, renorm, label):
+    if top_k < logits.shape[1]:
+        assert np.all(OM.route_margin(logits, top_k) > 1e-6), f"{label}: near-tied route; change the seed"
+    wg, wu, wd = layer.view("gate"), layer.view("up"), layer.view("down")
+    ref = OM.moe_ref(wg, wu, wd, x, residual, logits, s, top_k, renorm)
+    tol = OM.out_tolerance(wg, wu, wd, x, residual, ref)
+    err = np.abs(out.astype(np.float64) - ref["out"])
+    worst = np.unravel_index(np.argmax(err / tol), err.shape)
+    assert np.all(err <= tol), f"{label}: |err|/tol = {err[worst] / tol[worst]:.3g} at {worst}"
+    return ref
+
+
+def small_layer(fmt, e, h, i, seed):
+    experts = [random_expert(fmt, h, i, seed, j) for j in range(e + 1)]
+    gu = np.concatenate([ex.gu_packed for ex in experts])
+    dn = np.concatenate([ex.dn_packed for ex in experts])
+    assert gu.size == (e + 1) * qg.qg_packed_size(fmt, 2 * i, h)
+    assert dn.size == (e + 1) * qg.qg_packed_size(fmt, h, i)
+    return Layer(experts), dev(gu), dev(dn)
+
+
+@pytest.mark.parametrize("fmt", KFORMATS)
+@pytest.mark.parametrize("t", [1, 2, 3, 8])
+@pytest.mark.parametrize("renorm", [False, True])
+def test_moe_small(fmt, t, renorm):
+    e, h, i, top_k = 16, 512, 256, 4
+    layer, gu, dn = small_layer(fmt, e, h, i, seed=11)
+    x, residual, logits, s = inputs(t, e, h, seed=100 + t)
+    flags = qg.QG_MOE_RENORM if renorm else 0
+    out = run_moe(fmt, gu, dn, e, h, i, top_k, x, residual, logits, s, flags)
+    check(out, layer, x, residual, logits, s, top_k, renorm, f"{fmt} T={t} renorm={renorm}")
+
+
+@pytest.mark.parametrize("fmt", KFORMATS)
+@pytest.mark.parametrize("e,top_k,t", [(4, 4, 5), (9, 1, 8), (12, 8, 7), (1, 1, 3)])
+def test_moe_topk_edges(fmt, e, top_k, t):
+    """Every expert selected (top_k = E), a single pick, the widest top_k, and a
+    single-expert layer; odd T leaves a one-token shared-expert item."""
+    h, i = 256, 512
+    layer, gu, dn = small_layer(fmt, e, h, i, seed=12)
+    x, residual, logits, s = inputs(t, e, h, seed=200 + e)
+    if e == 1:
+        logits = np.zeros_like(logits)  # one expert: p = 1 whatever the logit
+    out = run_moe(fmt, gu, dn, e, h, i, top_k, x, residual, logits, s)
+    check(out, layer, x, residual, logits, s, top_k, False, f"{fmt} E={e} top_k={top_k} T={t}")
+
+
+@pytest.mark.parametrize("fmt", KFORMATS)
+def test_moe_shared_routes(fmt):
+    """All 8 tokens route to the same 4 experts, in different orders, so every
+    expert item carries two tokens; a -inf shared logit turns the shared
+    expert off for one token and +inf fully on for another; residual aliases x."""
+    e, h, i, top_k, t = 10, 512, 256, 4, 8
+    layer, gu, dn = small_layer(fmt, e, h, i, seed=13)
+    x, _, logits, s = inputs(t, e, h, seed=300)
+    logits = logits.copy()
+    favourites = [7, 2, 9, 4]
+    for tok in range(t):
+        for rank, ex in enumerate(np.roll(favourites, tok)):
+            logits[tok, ex] = 6.0 - 0.5 * rank
+    s = s.copy()
+    s[1], s[6] = -np.inf, np.inf
+    out = run_moe(fmt, gu, dn, e, h, i, top_k, x, x, logits, s, alias_residual=True)
+    ref = check(out, layer, x, x, logits, s, top_k, False, f"{fmt} shared routes")
+    assert all(set(ref["ids"][tok]) == set(favourites) for tok in range(t))
+
+
+def test_moe_dominant_logit_matches_single_expert():
+    """One dominant logit per token: the routed part reduces to that expert's
+    forward with weight ~1, checked against expert_forward directly."""
+    fmt, e, h, i, top_k, t = "q4_k", 8, 256, 256, 1, 2
+    layer, gu, dn = small_layer(fmt, e, h, i, seed=14)
+    x, residual, logits, _ = inputs(t, e, h, seed=400)
+    logits = logits.copy()
+    logits[0, 5] = logits[1, 3] = 60.0
+    s = np.full((t,), -np.inf, np.float32)  # no shared expert
+    out = run_moe(fmt, gu, dn, e, h, i, top_k, x, residual, logits, s)
+    check(out, layer, x, residual, logits, s, top_k, False, "dominant")
+    for tok, ex in [(0, 5), (1, 3)]:
+        ee = layer.experts[ex]
+        _, _, _, o = OM.expert_forward(ee.gate, ee.up, ee.down, x[tok:tok + 1])
+        np.testing.assert_allclose(out[tok], residual[tok] + o[0], rtol=1e-4, atol=1e-4)
+
+
+def test_moe_deterministic():
+    fmt, e, h, i, top_k, t = "q2_k", 16, 512, 256, 4, 8
+    layer, gu, dn = small_layer(fmt, e, h, i, seed=15)
+    x, residual, logits, s = inputs(t, e, h, seed=500)
+    a = run_moe(fmt, gu, dn, e, h, i, top_k, x, residual, logits, s)
+    b = run_moe(fmt, gu, dn, e, h, i, top_k, x, residual, logits, s)
+    np.testing.assert_array_equal(a.view(np.uint32), b.view(np.uint32))
+
+
+# ------------------------------------------------------------- full layer
+
+FULL_E, FULL_H, FULL_I, FULL_K = 512, 4096, 1024, 4
+
+
+class PooledExperts:
+    """Experts of the full layer, made on demand: each is a seeded row
+    permutation of one Student-t(5)*0.02 pool matrix per role (i.i.d. rows, so
+    each expert still has the workload's weight distribution), quantized by
+    permuting the pool's quantized rows (quantization is row by row)."""
+
+    def __init__(self, fmt, seed):
+        self.fmt = fmt
+        h, i = FULL_H, FULL_I
+        gu_pool = OM.interleave_gate_up(workloads.student_t_weights(i, h, seed, 0),
+                                        workloads.student_t_weights(i, h, seed, 1))
+        self.gu_blk = OF.quantize(fmt, gu_pool)
+        self.dn_blk = OF.quantize(fmt, workloads.student_t_weights(h, i, seed, 2))
+        self.seed = seed
+        self.cache = {}
+
+    def __getitem__(self, e):
+        if e not in self.cache:
+            g = workloads.rng_for(self.seed, 1000 + e)
+            # permute gate/up pairs together so rows 2i, 2i+1 stay one pair
+            pairs = g.permutation(FULL_I)
+            gu_rows = np.stack([2 * pairs, 2 * pairs + 1], axis=1).reshape(-1)
+            dn_rows = g.permutation(FULL_H)
+            gu = {k: v[gu_rows] for k, v in self.gu_blk.items()}
+            dn = {k: v[dn_rows] for k, v in self.dn_blk.items()}
+            ex = Expert.__new__(Expert)
+            ex.gu_packed = OF.pack(self.fmt, gu)
+            ex.dn_packed = OF.pack(self.fmt, dn)
+            gu_deq = OF.dequant(self.fmt, gu)
+            ex.gate, ex.up = gu_deq[0::2], gu_deq[1::2]
+            ex.down = OF.dequant(self.fmt, dn)
+            self.cache[e] = ex
+        return self.cache[e]
+
+    def __len__(self):
+        return FULL_E + 1
+
+
+@pytest.mark.parametrize("fmt", KFORMATS)
+@pytest.mark.parametrize("t", [1, 8])
+def test_moe_full_layer(fmt, t):
+    e, h, i, top_k = FULL_E, FULL_H, FULL_I, FULL_K
+    x, residual, logits, s = inputs(t, e, h, seed=600 + t)
+    ids, _, _ = OM.route(logits, top_k)
+    used = sorted(set(ids.reshape(-1).tolist()) | {e})
+    pool = PooledExperts(fmt, seed=21)
+    gu_sz, dn_sz = qg.qg_packed_size(fmt, 2 * i, h), qg.qg_packed_size(fmt, h, i)
+    gu = torch.full(((e + 1) * gu_sz,), 0xFF, dtype=torch.uint8, device="cuda")
+    dn = torch.full(((e + 1) * dn_sz,), 0xFF, dtype=torch.uint8, device="cuda")
+    for ex in used:
+        gu[ex * gu_sz:(ex + 1) * gu_sz].copy_(dev(pool[ex].gu_packed))
+        dn[ex * dn_sz:(ex + 1) * dn_sz].copy_(dev(pool[ex].dn_packed))
+    out = run_moe(fmt, gu, dn, e, h, i, top_k, x, residual, logits, s)
+    assert np.all(np.isfinite(out)), "a kernel read an unselected expert"
+    check(out, Layer(pool), x, residual, logits, s, top_k, False, f"{fmt} full T={t}")
+
+
+def test_moe_graph_replay():
+    """The four launches captured in a graph replay bit-equal to eager, with
+    eager work in between that overwrites the workspace."""
+    fmt, e, h, i, top_k, t = "q4_k", 16, 512, 256, 4, 8
+    _, gu, dn = small_layer(fmt, e, h, i, seed=16)
+    x, residual, logits, s = inputs(t, e, h, seed=700)
+    x_d, r_d, l_d, s_d = dev(x), dev(residual), dev(logits), dev(s)
+    ws_bytes = qg.moe_expert_ffn_workspace_size(t, e, h, i, top_k)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
+    eager = torch.empty((t, h), device="cuda")
+    qg.moe_expert_ffn(fmt, gu, dn, e, h, i, top_k, x_d, r_d, l_d, s_d, t, eager, ws, ws_bytes)
+    torch.cuda.synchronize()
+    out = torch.empty((t, h), device="cuda")
+    stream = torch.cuda.Stream()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(stream):
+        with torch.cuda.graph(graph, stream=stream):
+            qg.moe_expert_ffn(fmt, gu, dn, e, h, i, top_k, x_d, r_d, l_d, s_d, t, out, ws, ws_bytes,
+                              stream=stream)
+    torch.cuda.synchronize()
+    for _ in range(4):
+        out.fill_(float("nan"))
+        ws.fill_(0xAB)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int32), eager.view(torch.int32))
