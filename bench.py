@@ -35,15 +35,17 @@ HBM_PEAK_GBS = 8000.0           # MI355X published HBM3E bandwidth
 DENSE_8B_BYTES = 3_925_868_544  # Q4_K bytes of the 8B-class step's linear weights
 COLD_BYTES = 1 << 30            # rotate over at least this many bytes of packed copies
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "q4k_gemv_14336x4096_counters.txt")
-KERNEL_SOURCE = os.path.join(ROOT, "block_quantized_decode_qgemv_amd", "csrc", "gemv.hip")
+CSRC = os.path.join(ROOT, "block_quantized_decode_qgemv_amd", "csrc")
+KERNEL_SOURCES = {"kernel_source_sha256_16": os.path.join(CSRC, "gemv.hip"),
+                  "kernel_core_sha256_16": os.path.join(CSRC, "gemv_core.h")}
 
 
 def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
-def kernel_source_hash() -> str:
-    with open(KERNEL_SOURCE, "rb") as fh:
+def source_hash(path) -> str:
+    with open(path, "rb") as fh:
         return hashlib.sha256(fh.read()).hexdigest()[:16]
 
 
@@ -58,7 +60,7 @@ def read_traffic():
             if ":" in line and not line.startswith("#"):
                 key, val = line.split(":", 1)
                 fields[key.strip()] = val.strip()
-    if fields.get("kernel_source_sha256_16") != kernel_source_hash():
+    if any(fields.get(key) != source_hash(path) for key, path in KERNEL_SOURCES.items()):
         return None
     try:
         return float(fields["hbm_bytes_per_launch"])
@@ -224,8 +226,12 @@ def main():
 
     t_launch = head.timed_replay(reps)
     achieved = head.bytes / t_launch / 1e9
+    # traffic: counter-measured HBM bytes per launch over the same launch time,
+    # in the unit of `achieved` (so traffic / achieved = measured / algorithmic bytes)
+    hbm_bytes = read_traffic()
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": read_traffic()}
+                "frac": round(achieved / HBM_PEAK_GBS, 4),
+                "traffic": None if hbm_bytes is None else round(hbm_bytes / t_launch / 1e9, 1)}
 
     # eager launches (host-issued one by one), for reference
     for _ in range(50):
@@ -239,7 +245,9 @@ def main():
 
     extra = {"headline_us_per_launch": round(t_launch * 1e6, 3),
              "headline_eager_us_per_launch": round(eager_us, 3),
-             "tok_s_equiv": round(achieved * 1e9 / DENSE_8B_BYTES, 1)}
+             "tok_s_equiv": round(achieved * 1e9 / DENSE_8B_BYTES, 1),
+             "headline_algorithmic_bytes": head.bytes,
+             "headline_hbm_bytes_counted": hbm_bytes}
     if not args.quick:
         def measure(fmt, n, k, b):
             g = Gemv(torch, qg, fmt, n, k, b, 0, COLD_BYTES, stream)
