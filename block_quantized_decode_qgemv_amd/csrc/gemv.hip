@@ -59,6 +59,19 @@ gemv_kernel(const uint8_t* __restrict__ codes, const uint8_t* __restrict__ meta,
         });
 }
 
+template <int F, int B, int W, int KCS>
+__global__ void __launch_bounds__(W * 64)
+gemv_dpp_kernel(const uint8_t* __restrict__ codes, const uint8_t* __restrict__ meta,
+                const float* __restrict__ x, float* __restrict__ y, int N, int K) {
+    const int g = blockIdx.x;
+    GemvDpp<F, B, W, KCS>::run(
+        codes, meta, N, K, g, [&](int b) { return x + (size_t)b * K; }, B,
+        [&](const float* sums, int n_g) {
+            for (int t = threadIdx.x; t < kRowGroup * B; t += W * 64)
+                if (t / B < n_g) y[(size_t)(t % B) * N + g * kRowGroup + t / B] = sums[t];
+        });
+}
+
 // ---------------------------------------------------------- dequant kernel
 // One thread per (row, code unit): decode CPC weights exactly.
 
@@ -150,9 +163,28 @@ hipError_t launch_gemv_w(const uint8_t* codes, const uint8_t* meta, const float*
     }
 }
 
+template <int F, int B, int W>
+hipError_t launch_gemv_dpp_w(const uint8_t* codes, const uint8_t* meta, const float* x, float* y,
+                             int N, int K, hipStream_t st) {
+    constexpr int KCS = dpp_lane_units<F>();
+    const int grid = (N + kRowGroup - 1) / kRowGroup;
+    hipLaunchKernelGGL((gemv_dpp_kernel<F, B, W, KCS>), dim3(grid), dim3(W * 64), 0, st, codes, meta, x, y, N, K);
+    return hipGetLastError();
+}
+
 template <int F, int B>
 hipError_t launch_gemv_b(const uint8_t* codes, const uint8_t* meta, const float* x, float* y,
                          int N, int K, hipStream_t st) {
+    if constexpr (B <= dpp_max_batch<F>()) {
+        // x in registers, read across lanes by DPP (no LDS staging)
+        switch (pick_waves_dpp<F, dpp_lane_units<F>()>(K)) {
+            case 1: return launch_gemv_dpp_w<F, B, 1>(codes, meta, x, y, N, K, st);
+            case 2: return launch_gemv_dpp_w<F, B, 2>(codes, meta, x, y, N, K, st);
+            case 4: return launch_gemv_dpp_w<F, B, 4>(codes, meta, x, y, N, K, st);
+            case 8: return launch_gemv_dpp_w<F, B, 8>(codes, meta, x, y, N, K, st);
+            default: return launch_gemv_dpp_w<F, B, 16>(codes, meta, x, y, N, K, st);
+        }
+    }
     constexpr int KCS = lane_units<F>();
     switch (pick_waves<F, B, KCS>(K)) {
         case 1: return launch_gemv_w<F, B, KCS, 1>(codes, meta, x, y, N, K, st);

@@ -6,6 +6,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
+#include <utility>
 
 #include "internal.h"
 
@@ -533,6 +534,283 @@ int pick_waves(int K) {
         return (size_t)B * SC * 4 + (size_t)B * (GS ? SC / (GS ? GS : 1) : 1) * 4 + (size_t)P * kRowGroup * B * 4;
     };
     while (w > 1 && bytes(w) > (size_t)kLdsBudget) w /= 2;
+    return w;
+}
+
+
+// --------------------------------------------------- register-x GEMV (DPP)
+//
+// Same grid and epilogue contract as Gemv, without LDS for x.  The 16 lanes
+// of a DPP row are the 16 rows of the group working on one part of KCS code
+// units (NXC = KCS*CPC columns from column k0); lane r keeps x columns
+// k0 + 64m + 4r .. +3 (m < NXC/64) of every batch row in registers, and each
+// multiply-add reads its x operand from the lane holding it (row_newbcast).
+// x is thus read once per wave from the cache and never staged; column sums
+// are DPP sums over the lanes of a sum group.  Part sums are combined with
+// lane shuffles inside a wave and through a small LDS array across waves, in
+// a fixed order.
+
+template <int... Is, class Fn>
+__device__ __forceinline__ void static_for_impl(std::integer_sequence<int, Is...>, Fn&& fn) {
+    (fn(std::integral_constant<int, Is>{}), ...);
+}
+template <int N, class Fn>
+__device__ __forceinline__ void static_for(Fn&& fn) {
+    static_for_impl(std::make_integer_sequence<int, N>{}, fn);
+}
+
+// a[k % 4] += w[k] * (component k of lane L's xa), k = 0..3.
+//
+// Hazard rule: a DPP instruction reads all its VGPR operands (the broadcast x,
+// the weight and the accumulator) early, so none of them may have been
+// written by a VALU instruction in the two instructions before it.  The
+// compiler cannot see into inline asm, so (1) every block starts with
+// s_nop 1, covering whatever the compiler placed just before it, and (2)
+// consecutive multiply-adds rotate over four accumulators, so an accumulator
+// is read three instructions after its last write.  The x operands are only
+// read, and the blocks' results are never DPP sources elsewhere.
+template <int L>
+__device__ __forceinline__ void fma4_bcast(float (&a)[4], const float4& xa, const float* w) {
+    asm("s_nop 1\n\t"
+        "v_fmac_f32_dpp %0, %4, %8 row_newbcast:%c12 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %1, %5, %9 row_newbcast:%c12 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %2, %6, %10 row_newbcast:%c12 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %3, %7, %11 row_newbcast:%c12 row_mask:0xf bank_mask:0xf"
+        : "+v"(a[0]), "+v"(a[1]), "+v"(a[2]), "+v"(a[3])
+        : "v"(xa.x), "v"(xa.y), "v"(xa.z), "v"(xa.w), "v"(w[0]), "v"(w[1]), "v"(w[2]), "v"(w[3]), "n"(L));
+}
+// the same for w[0..3] against lane L and w[4..7] against lane L + 1
+template <int L>
+__device__ __forceinline__ void fma8_bcast(float (&a)[4], const float4& xa, const float* w) {
+    asm("s_nop 1\n\t"
+        "v_fmac_f32_dpp %0, %4, %8 row_newbcast:%c16 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %1, %5, %9 row_newbcast:%c16 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %2, %6, %10 row_newbcast:%c16 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %3, %7, %11 row_newbcast:%c16 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %0, %4, %12 row_newbcast:%c17 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %1, %5, %13 row_newbcast:%c17 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %2, %6, %14 row_newbcast:%c17 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %3, %7, %15 row_newbcast:%c17 row_mask:0xf bank_mask:0xf"
+        : "+v"(a[0]), "+v"(a[1]), "+v"(a[2]), "+v"(a[3])
+        : "v"(xa.x), "v"(xa.y), "v"(xa.z), "v"(xa.w), "v"(w[0]), "v"(w[1]), "v"(w[2]), "v"(w[3]),
+          "v"(w[4]), "v"(w[5]), "v"(w[6]), "v"(w[7]), "n"(L), "n"(L + 1));
+}
+
+// lane L's value of v in every lane of its DPP row
+template <int L>
+__device__ __forceinline__ float row_bcast(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x150 + L, 0xF, 0xF, true));
+}
+
+// a[t % 4] += w[t] * x[column CB + t] over the CPD columns from part column CB
+template <int CB, int CPD, int NX4>
+__device__ __forceinline__ void fma_cols(float (&a)[4], const float4 (&xv)[NX4], const float* w) {
+    if constexpr (CPD == 4) {
+        fma4_bcast<(CB % 64) / 4>(a, xv[CB / 64], w);
+    } else {
+        static_for<CPD / 8>([&](auto G) {
+            constexpr int c = CB + 8 * decltype(G)::value;
+            fma8_bcast<(c % 64) / 4>(a, xv[c / 64], w + 8 * decltype(G)::value);
+        });
+    }
+}
+
+template <int F> constexpr bool is_kquant() { return F == QG_Q4_K || F == QG_Q2_K; }
+
+// Code units per lane part in the register-x kernel: NXC = 64 columns for
+// Q8_0 and 128 or 256 for the others; a K-quant part stays inside one
+// super-block.
+template <int F> constexpr int dpp_lane_units() {
+    return F == QG_BIN ? 2 : 4;
+}
+// Largest batch for the register-x kernel: x registers per lane B*NXC/16 <= 32.
+template <int F> constexpr int dpp_max_batch() {
+    return 32 / (dpp_lane_units<F>() * Fmt<F>::CPC / 16);
+}
+
+template <int F, int B, int W, int KCS>
+struct GemvDpp {
+    using T = Fmt<F>;
+    using U = Unit<F>;
+    using A = Apply<F>;
+    static constexpr int NT = W * 64, P = 4 * W;
+    static constexpr int CPC = T::CPC, CPD = U::CPD, GS = T::GS, SUBS = A::SUBS;
+    static constexpr int SU = P * KCS;            // code units per slice
+    static constexpr int NXC = KCS * CPC;         // x columns per part
+    static constexpr int NX4 = NXC / 64;          // x float4 per lane per batch row
+    static constexpr int MB = KCS * T::MBU;       // meta bytes per lane part
+    static constexpr int DPS = 4 / SUBS;          // code dwords per sub-group
+    static constexpr int UPS = is_kquant<F>() ? T::BLOCK / CPC : 1;  // units per super-block
+    static_assert(NXC % 64 == 0, "a part covers whole 64-column spans");
+    static_assert(!is_kquant<F>() || UPS % KCS == 0, "a K-quant part stays in one super-block");
+    static_assert(B * NX4 * 4 <= 32, "x registers per lane");
+
+    // column sum of the GS columns from part column CS of one batch row;
+    // gs[m] holds the DPP sums of span m
+    template <int CS>
+    __device__ static float col_sum(const float (&gs)[NX4]) {
+        if constexpr (GS == 32) return row_bcast<(CS % 64) / 4>(gs[CS / 64]);
+        else if constexpr (GS == 64) return gs[CS / 64];
+        else return gs[CS / 64] + gs[CS / 64 + 1];  // GS == 128
+    }
+
+    template <class XRow, class Epi>
+    __device__ static void run(const uint8_t* __restrict__ codes, const uint8_t* __restrict__ meta,
+                               int N, int K, int g, XRow xrow, int nb, Epi epi) {
+        __shared__ float red[W][kRowGroup * B];
+        __shared__ float sums[kRowGroup * B];
+        const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+        const int r = lane & 15, p = wave * 4 + (lane >> 4);
+        const int n_g = min(kRowGroup, N - g * kRowGroup);
+        const int rr = min(r, n_g - 1);
+        const int nb_blocks = K / T::BLOCK;
+        const int row_codes = nb_blocks * T::CB, row_meta = nb_blocks * T::MB;
+        const int nch = row_codes >> 4;
+        const bool meta_whole = (row_meta & 15) == 0;
+        const int ustride = n_g * 16;
+        const uint8_t* gcr = codes + (size_t)g * kRowGroup * row_codes + rr * 16;
+        const uint8_t* gm = meta + (size_t)g * kRowGroup * row_meta;
+        const uint8_t* gmr = gm + rr * 16;
+
+        float acc[B];
+#pragma unroll
+        for (int b = 0; b < B; ++b) acc[b] = 0.0f;
+
+        for (int c_slice = 0; c_slice < nch; c_slice += SU) {
+            const int c0 = c_slice + p * KCS;  // first code unit of this lane's part
+            const int k0 = c0 * CPC;           // its first column
+            const int nvalid = nch - c0;
+
+            // (1) x of the part, four columns per lane per span
+            float4 xv[B][NX4];
+#pragma unroll
+            for (int b = 0; b < B; ++b) {
+                if (b < nb) {
+                    const float* xb = xrow(b);
+#pragma unroll
+                    for (int m = 0; m < NX4; ++m) {
+                        const int c = k0 + 64 * m + 4 * r;
+                        xv[b][m] = c < K ? *(const float4*)(xb + c) : make_float4(0.f, 0.f, 0.f, 0.f);
+                    }
+                }
+            }
+            // (2) meta, then the code units (clamped into the row; units past
+            // its end are dropped by the scale step)
+            uint32_t wd[is_kquant<F>() ? 4 : (MB + 3) / 4];
+            if constexpr (is_kquant<F>()) {
+                const int sbi = min(c0, nch - 1) / UPS, uo = min(c0, nch - 1) % UPS;
+                const uint4 v = ld_weights<uint4>(gmr + (size_t)sbi * ustride);
+                // pairs of the part's first unit moved to the bottom of the field
+                const unsigned __int128 f =
+                    ((unsigned __int128)v.z << 64 | (unsigned __int128)v.y << 32 | v.x) >> (12 * SUBS * uo);
+                wd[0] = (uint32_t)f; wd[1] = (uint32_t)(f >> 32); wd[2] = (uint32_t)(f >> 64); wd[3] = v.w;
+            } else {
+                const int m0 = min(c0, (nch - 1) / KCS * KCS) * T::MBU;
+                if (meta_whole) {
+                    const uint8_t* pm = gmr + (m0 >> 4) * ustride + (m0 & 15);
+                    if constexpr (MB >= 16) {
+                        const uint4 v = ld_weights<uint4>(pm);
+                        wd[0] = v.x; wd[1] = v.y; wd[2] = v.z; wd[3] = v.w;
+                    } else if constexpr (MB == 8) {
+                        const uint2 v = ld_weights<uint2>(pm);
+                        wd[0] = v.x; wd[1] = v.y;
+                    } else {
+                        wd[0] = ld_weights<uint32_t>(pm);
+                    }
+                } else {
+                    load_meta<MB>(gm, n_g, rr, m0, row_meta, wd);
+                }
+            }
+            uint4 q[KCS];
+#pragma unroll
+            for (int i = 0; i < KCS; ++i) q[i] = ld_weights<uint4>(gcr + min(c0 + i, nch - 1) * ustride);
+
+            // (3) column-sum spans of every batch row
+            float gs[B][NX4];
+            if constexpr (GS > 0) {
+#pragma unroll
+                for (int b = 0; b < B; ++b)
+#pragma unroll
+                    for (int m = 0; m < NX4; ++m) {
+                        const float s = (xv[b][m].x + xv[b][m].y) + (xv[b][m].z + xv[b][m].w);
+                        gs[b][m] = GS == 32 ? group_sum<8>(s) : group_sum<16>(s);
+                    }
+            }
+
+            // (4) decode each unit once, multiply-add it for every batch row
+            KqState st[B];
+            static_for<KCS>([&](auto I) {
+                constexpr int i = decltype(I)::value;
+                const bool ok = i < nvalid;
+                const uint32_t dw[4] = {q[i].x, q[i].y, q[i].z, q[i].w};
+                static_for<SUBS>([&](auto S) {
+                    constexpr int s = decltype(S)::value;
+                    float pa[B][4];
+#pragma unroll
+                    for (int b = 0; b < B; ++b) pa[b][0] = pa[b][1] = pa[b][2] = pa[b][3] = 0.0f;
+                    static_for<DPS>([&](auto D) {
+                        constexpr int d = s * DPS + decltype(D)::value;
+                        float w[CPD];
+                        U::decode(dw[d], w);
+#pragma unroll
+                        for (int b = 0; b < B; ++b) fma_cols<i * CPC + d * CPD, CPD, NX4>(pa[b], xv[b], w);
+                    });
+                    float ps[B];
+#pragma unroll
+                    for (int b = 0; b < B; ++b) ps[b] = (pa[b][0] + pa[b][1]) + (pa[b][2] + pa[b][3]);
+#pragma unroll
+                    for (int b = 0; b < B; ++b) {
+                        float X = 0.0f;
+                        if constexpr (GS > 0) X = col_sum<i * CPC + s * (CPC / SUBS)>(gs[b]);
+                        if constexpr (is_kquant<F>()) {
+                            const uint32_t pr = kq_pair(wd, i * SUBS + s);
+                            st[b].sp = fmaf((float)(pr & 63u), ps[b], st[b].sp);
+                            st[b].tx = fmaf((float)((pr >> 6) & 63u), X, st[b].tx);
+                        } else {
+                            A::unit(wd, i, s, ps[b], X, st[b], acc[b], ok);
+                        }
+                    }
+                });
+                __builtin_amdgcn_sched_barrier(0);
+            });
+            if constexpr (is_kquant<F>()) {
+                // a K-quant part lies in one super-block: valid as a whole or not at all
+                const float d = 512.0f * h2f(wd[3] & 0xFFFFu), dmin = h2f(wd[3] >> 16);
+#pragma unroll
+                for (int b = 0; b < B; ++b) {
+                    const float v = fmaf(d, st[b].sp, fmaf(-dmin, st[b].tx, acc[b]));
+                    acc[b] = nvalid > 0 ? v : acc[b];
+                }
+            }
+        }
+
+        // (5) combine the parts: lanes r, r+16, r+32, r+48 of a wave, then waves
+#pragma unroll
+        for (int b = 0; b < B; ++b) {
+            float v = acc[b];
+            v += __shfl_xor(v, 16);
+            v += __shfl_xor(v, 32);
+            if (lane < 16) red[wave][r * B + b] = v;
+        }
+        __syncthreads();
+        for (int t = tid; t < kRowGroup * B; t += NT) {
+            float v = 0.0f;
+#pragma unroll
+            for (int w = 0; w < W; ++w) v += red[w][t];
+            sums[t] = v;
+        }
+        __syncthreads();
+        epi(sums, n_g);
+    }
+};
+
+// Waves per workgroup of the register-x kernel: the fewest (1..16, powers of
+// two) whose 4W parts cover the row in one slice, else 16 and several slices.
+template <int F, int KCS>
+int pick_waves_dpp(int K) {
+    const int nch = K / Fmt<F>::BLOCK * Fmt<F>::CB / 16;
+    int w = 1;
+    while (w < 16 && 4 * w * KCS < nch) w *= 2;
     return w;
 }
 

@@ -96,6 +96,20 @@ def test_gemv_parity(fmt, b, n, kb):
     assert_parity(y, OF.dequant(fmt, blk), x, f"{fmt} B={b} N={n} K={k}")
 
 
+@pytest.mark.parametrize("fmt", OF.FORMATS)
+@pytest.mark.parametrize("b", [1, 2])
+def test_gemv_widest_workgroup(fmt, b):
+    """K = 16384 gives the register-x kernel its widest workgroup (16 waves,
+    one per SIMD slot at low occupancy, where back-to-back issue of a wave's
+    instructions is most likely), with several slices for the narrow-unit
+    formats; 33 rows leave a one-row last group."""
+    n, k = 33, 16384
+    blk = make_blocks(fmt, n, k, seed=8, tid=b)
+    x = workloads.normal((b, k), 8, 100 + b)
+    y = run_gemv(fmt, OF.pack(fmt, blk), x, n, k)
+    assert_parity(y, OF.dequant(fmt, blk), x, f"{fmt} B={b} N={n} K={k}")
+
+
 @pytest.mark.parametrize("fmt", ["q8_0", "q4_0", "q4_1"])
 @pytest.mark.parametrize("k", [32, 96, 160, 4064])
 def test_gemv_short_blocks(fmt, k):
