@@ -384,8 +384,8 @@ struct Gemv {
 
     // One 16-row group g of a packed [N][K] matrix against nb <= B activation
     // rows; xrow(b) gives row b (K floats, 16-byte aligned).  After the parts
-    // are combined, every thread calls epi(sums, n_g) with sums[rw * B + b]
-    // the row sums in LDS (rows rw < n_g, batch rows b < nb valid).
+    // are combined, every thread calls epi(sum, n_g), where sum(t) returns the
+    // row sum for t = rw * B + b (rows rw < n_g, batch rows b < nb valid).
     template <class XRow, class Epi>
     __device__ static void run(const uint8_t* __restrict__ codes, const uint8_t* __restrict__ meta,
                                int N, int K, int g, XRow xrow, int nb, Epi epi) {
@@ -505,7 +505,7 @@ struct Gemv {
         for (int j = 0; j < PER; ++j)
             if (tid + NT * j < kRowGroup * B) part[tid + NT * j] = sum[j];  // sums[rw * B + b]
         __syncthreads();
-        epi(part, n_g);
+        epi([&](int t) { return part[t]; }, n_g);
     }
 };
 
@@ -658,7 +658,6 @@ struct GemvDpp {
     __device__ static void run(const uint8_t* __restrict__ codes, const uint8_t* __restrict__ meta,
                                int N, int K, int g, XRow xrow, int nb, Epi epi) {
         __shared__ float red[W][kRowGroup * B];
-        __shared__ float sums[kRowGroup * B];
         const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
         const int r = lane & 15, p = wave * 4 + (lane >> 4);
         const int n_g = min(kRowGroup, N - g * kRowGroup);
@@ -689,8 +688,10 @@ struct GemvDpp {
                     const float* xb = xrow(b);
 #pragma unroll
                     for (int m = 0; m < NX4; ++m) {
-                        const int c = k0 + 64 * m + 4 * r;
-                        xv[b][m] = c < K ? *(const float4*)(xb + c) : make_float4(0.f, 0.f, 0.f, 0.f);
+                        // columns past K read the row's last float4 instead: they
+                        // only meet code units whose contributions are dropped
+                        const int c = min(k0 + 64 * m + 4 * r, K - 4);
+                        xv[b][m] = *(const float4*)(xb + c);
                     }
                 }
             }
@@ -793,14 +794,14 @@ struct GemvDpp {
             if (lane < 16) red[wave][r * B + b] = v;
         }
         __syncthreads();
-        for (int t = tid; t < kRowGroup * B; t += NT) {
-            float v = 0.0f;
+        epi(
+            [&](int t) {
+                float v = 0.0f;
 #pragma unroll
-            for (int w = 0; w < W; ++w) v += red[w][t];
-            sums[t] = v;
-        }
-        __syncthreads();
-        epi(sums, n_g);
+                for (int w = 0; w < W; ++w) v += red[w][t];
+                return v;
+            },
+            n_g);
     }
 };
 

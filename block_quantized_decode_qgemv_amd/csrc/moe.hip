@@ -233,15 +233,15 @@ moe_gate_up_kernel(const uint8_t* __restrict__ wgu, size_t expert_bytes, size_t 
     float* hj = h + (size_t)j * 2 * I;
     auto xrow = [&](int b) { return x + (size_t)it.tok[b] * H; };
     auto epi = [&](int B) {
-        return [=](const float* sums, int) {
+        return [=](auto sums, int) {
             for (int t = threadIdx.x; t < 8 * B; t += W * 64) {
                 const int i = t / B, b = t % B;
-                if (b < it.count) hj[(size_t)b * I + 8 * g + i] = silu(sums[(2 * i) * B + b]) * sums[(2 * i + 1) * B + b];
+                if (b < it.count) hj[(size_t)b * I + 8 * g + i] = silu(sums((2 * i) * B + b)) * sums((2 * i + 1) * B + b);
             }
         };
     };
-    if (it.count == 1) Gemv<F, 1, W, KCS>::run(codes, meta, 2 * I, H, g, xrow, 1, epi(1));
-    else Gemv<F, 2, W, KCS>::run(codes, meta, 2 * I, H, g, xrow, 2, epi(2));
+    if (it.count == 1) GemvDpp<F, 1, W, KCS>::run(codes, meta, 2 * I, H, g, xrow, 1, epi(1));
+    else GemvDpp<F, 2, W, KCS>::run(codes, meta, 2 * I, H, g, xrow, 2, epi(2));
 }
 
 // down: partial[tok][kslot][row] = weight * (W_down h)[row]
@@ -258,19 +258,19 @@ moe_down_kernel(const uint8_t* __restrict__ wdn, size_t expert_bytes, size_t cod
     const float* hj = h + (size_t)j * 2 * I;
     auto xrow = [&](int b) { return hj + (size_t)b * I; };
     auto epi = [&](int B) {
-        return [=](const float* sums, int n_g) {
+        return [=](auto sums, int n_g) {
             for (int t = threadIdx.x; t < kRowGroup * B; t += W * 64) {
                 const int rw = t / B, b = t % B;
                 // selects, not it.tok[b]: a runtime index would put the item in scratch
                 const int tok = b ? it.tok[1] : it.tok[0], ks = b ? it.kslot[1] : it.kslot[0];
                 const float wt = b ? it.wt[1] : it.wt[0];
                 if (b < it.count && rw < n_g)
-                    partial[((size_t)tok * (top_k + 1) + ks) * H + kRowGroup * g + rw] = wt * sums[t];
+                    partial[((size_t)tok * (top_k + 1) + ks) * H + kRowGroup * g + rw] = wt * sums(t);
             }
         };
     };
-    if (it.count == 1) Gemv<F, 1, W, KCS>::run(codes, meta, H, I, g, xrow, 1, epi(1));
-    else Gemv<F, 2, W, KCS>::run(codes, meta, H, I, g, xrow, 2, epi(2));
+    if (it.count == 1) GemvDpp<F, 1, W, KCS>::run(codes, meta, H, I, g, xrow, 1, epi(1));
+    else GemvDpp<F, 2, W, KCS>::run(codes, meta, H, I, g, xrow, 2, epi(2));
 }
 
 // out = residual + sum_k partial[k] (k = 0 .. top_k, the last being the
@@ -291,36 +291,28 @@ moe_combine_kernel(const float* __restrict__ residual, const float* __restrict__
 template <int F, int W, int KCS>
 hipError_t launch_gate_up_w(const uint8_t* wgu, int H, int I, const float* x, const int* items, float* h,
                             int max_items, hipStream_t st) {
-    constexpr size_t lds = gemv_lds_bytes<F, 2, W, KCS>();
-    if constexpr (lds <= (size_t)kLdsBudget) {
-        const size_t eb = qg_packed_size(F, 2 * (int64_t)I, H), cb = qg_codes_plane_size(F, 2 * (int64_t)I, H);
-        hipLaunchKernelGGL((moe_gate_up_kernel<F, W, KCS>), dim3(2 * I / kRowGroup, max_items), dim3(W * 64), lds, st,
-                           wgu, eb, cb, H, I, x, items, h);
-        return hipGetLastError();
-    } else {
-        return hipErrorInvalidConfiguration;
-    }
+    const size_t eb = qg_packed_size(F, 2 * (int64_t)I, H), cb = qg_codes_plane_size(F, 2 * (int64_t)I, H);
+    hipLaunchKernelGGL((moe_gate_up_kernel<F, W, KCS>), dim3(2 * I / kRowGroup, max_items), dim3(W * 64), 0, st,
+                       wgu, eb, cb, H, I, x, items, h);
+    return hipGetLastError();
 }
 
 template <int F, int W, int KCS>
 hipError_t launch_down_w(const uint8_t* wdn, int H, int I, int top_k, const int* items, const float* h,
                          float* partial, int max_items, hipStream_t st) {
-    constexpr size_t lds = gemv_lds_bytes<F, 2, W, KCS>();
-    if constexpr (lds <= (size_t)kLdsBudget) {
-        const size_t eb = qg_packed_size(F, H, I), cb = qg_codes_plane_size(F, H, I);
-        hipLaunchKernelGGL((moe_down_kernel<F, W, KCS>), dim3(H / kRowGroup, max_items), dim3(W * 64), lds, st,
-                           wdn, eb, cb, H, I, top_k, items, h, partial);
-        return hipGetLastError();
-    } else {
-        return hipErrorInvalidConfiguration;
-    }
+    const size_t eb = qg_packed_size(F, H, I), cb = qg_codes_plane_size(F, H, I);
+    hipLaunchKernelGGL((moe_down_kernel<F, W, KCS>), dim3(H / kRowGroup, max_items), dim3(W * 64), 0, st,
+                       wdn, eb, cb, H, I, top_k, items, h, partial);
+    return hipGetLastError();
 }
 
 template <int F>
 hipError_t launch_moe(const uint8_t* wgu, const uint8_t* wdn, int E, int H, int I, int top_k, const float* x,
                       const float* residual, const float* logits, const float* slogit, int T, unsigned flags,
                       float* out, uint8_t* ws, hipStream_t st) {
-    constexpr int KCS = lane_units<F>();
+    // register-x GEMVs (items carry at most 2 tokens)
+    constexpr int KCS = dpp_lane_units<F>();
+    static_assert(dpp_max_batch<F>() >= 2, "two tokens per item");
     const MoeLayout L(T, H, I, top_k);
     int* items = reinterpret_cast<int*>(ws + L.items);
     float* h = reinterpret_cast<float*>(ws + L.h);
@@ -328,18 +320,20 @@ hipError_t launch_moe(const uint8_t* wgu, const uint8_t* wdn, int E, int H, int 
     hipLaunchKernelGGL(moe_route_kernel, dim3(1), dim3(512), 0, st, logits, slogit, T, E, top_k, flags, items);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    switch (pick_waves<F, 2, KCS>(H)) {
+    switch (pick_waves_dpp<F, KCS>(H)) {
         case 1: e = launch_gate_up_w<F, 1, KCS>(wgu, H, I, x, items, h, L.max_items, st); break;
         case 2: e = launch_gate_up_w<F, 2, KCS>(wgu, H, I, x, items, h, L.max_items, st); break;
         case 4: e = launch_gate_up_w<F, 4, KCS>(wgu, H, I, x, items, h, L.max_items, st); break;
-        default: e = launch_gate_up_w<F, 8, KCS>(wgu, H, I, x, items, h, L.max_items, st); break;
+        case 8: e = launch_gate_up_w<F, 8, KCS>(wgu, H, I, x, items, h, L.max_items, st); break;
+        default: e = launch_gate_up_w<F, 16, KCS>(wgu, H, I, x, items, h, L.max_items, st); break;
     }
     if (e != hipSuccess) return e;
-    switch (pick_waves<F, 2, KCS>(I)) {
+    switch (pick_waves_dpp<F, KCS>(I)) {
         case 1: e = launch_down_w<F, 1, KCS>(wdn, H, I, top_k, items, h, partial, L.max_items, st); break;
         case 2: e = launch_down_w<F, 2, KCS>(wdn, H, I, top_k, items, h, partial, L.max_items, st); break;
         case 4: e = launch_down_w<F, 4, KCS>(wdn, H, I, top_k, items, h, partial, L.max_items, st); break;
-        default: e = launch_down_w<F, 8, KCS>(wdn, H, I, top_k, items, h, partial, L.max_items, st); break;
+        case 8: e = launch_down_w<F, 8, KCS>(wdn, H, I, top_k, items, h, partial, L.max_items, st); break;
+        default: e = launch_down_w<F, 16, KCS>(wdn, H, I, top_k, items, h, partial, L.max_items, st); break;
     }
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(moe_combine_kernel, dim3((T * H + 255) / 256), dim3(256), 0, st, residual, partial, out, T, H,
