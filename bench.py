@@ -137,6 +137,152 @@ class Gemv:
         return a.elapsed_time(e) * 1e-3 / (reps * len(self.wp))
 
 
+def graph_time(torch, stream, launches, reps):
+    """Capture `launches` (a list of zero-argument callables issuing work on
+    `stream`) into one HIP graph; return (seconds per replay, graph)."""
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        for fn in launches:
+            fn()
+    for _ in range(2):
+        g.replay()
+    torch.cuda.synchronize()
+    a = torch.cuda.Event(enable_timing=True)
+    e = torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for _ in range(reps):
+        g.replay()
+    e.record(stream)
+    e.synchronize()
+    return a.elapsed_time(e) * 1e-3 / reps, g
+
+
+def read_probe(torch, qg, stream, head):
+    """Streaming-read rate of the library's probe kernel: over the headline's
+    rotating copies (same size, same cold cache) and over one 4 GiB buffer."""
+    lib = qg.load()
+    sink = torch.zeros(4, dtype=torch.int32, device="cuda")
+    sp = stream.cuda_stream
+
+    def probe(ptr, nbytes):
+        return lambda: lib.qg_hbm_read_probe(ptr, nbytes, sink.data_ptr(), sp)
+
+    t, _ = graph_time(torch, stream, [probe(p, head.bytes) for p in head.wp], 20)
+    same = head.bytes * len(head.wp) / t / 1e9
+    big = torch.empty(4 << 30, dtype=torch.uint8, device="cuda")
+    t_big, _ = graph_time(torch, stream, [probe(big.data_ptr(), big.numel())], 10)
+    out = {"same_size_GBps": round(same, 1), "bytes_same_size": head.bytes,
+           "large_4GiB_GBps": round(big.numel() / t_big / 1e9, 1)}
+    del big
+    torch.cuda.empty_cache()
+    return out
+
+
+DENSE_LAYER = (("q", 4096, 4096), ("k", 1024, 4096), ("v", 1024, 4096), ("o", 4096, 4096),
+               ("gate", 14336, 4096), ("up", 14336, 4096), ("down", 4096, 14336))
+DENSE_LAYERS = 32
+
+
+def dense_step(torch, qg, stream):
+    """The 8B-class decode step: 32 layers x 7 Q4_K GEMVs at batch 1, one HIP
+    graph.  One layer's weights are drawn and quantized; the 32 layers are
+    distinct device copies of it (3.9 GB, far beyond the 256 MB cache, so the
+    content repeat does not help the reads).  Also timed with q/k/v and
+    gate/up each fused into one matrix (128 launches instead of 224)."""
+    import workloads
+
+    lib = qg.load()
+    fid = qg.FORMATS["q4_k"]
+    sp = stream.cuda_stream
+    host = {}
+    for j, (name, n, k) in enumerate(DENSE_LAYER):
+        host[name] = workloads.student_t_weights_device(n, k, 0, 700 + j).cpu().numpy()
+    packed = {name: qg.qquant("q4_k", w, n_threads=16) for name, w in host.items()}
+    fused = {"qkv": qg.qquant("q4_k", np.concatenate([host["q"], host["k"], host["v"]]), n_threads=16),
+             "gateup": qg.qquant("q4_k", np.concatenate([host["gate"], host["up"]]), n_threads=16)}
+    del host
+    total = sum(p.size for p in packed.values()) * DENSE_LAYERS
+    xs = {4096: workloads.normal_device((1, 4096), 0, 801), 14336: workloads.normal_device((1, 14336), 0, 802)}
+    ys = {n: torch.empty((1, n), device="cuda") for n in (1024, 4096, 6144, 14336, 28672)}
+
+    def gemv(w, n, k):
+        wp, xp, yp = w.data_ptr(), xs[k].data_ptr(), ys[n].data_ptr()
+        return lambda: lib.qgemv(fid, wp, xp, yp, n, k, 1, None, 0, sp)
+
+    dev = [{name: torch.from_numpy(packed[name]).to("cuda") for name, _, _ in DENSE_LAYER} for _ in range(DENSE_LAYERS)]
+    launches = [gemv(layer[name], n, k) for layer in dev for name, n, k in DENSE_LAYER]
+    t, _ = graph_time(torch, stream, launches, 20)
+    del dev, launches
+    torch.cuda.empty_cache()
+    dev = [{name: torch.from_numpy(p).to("cuda") for name, p in fused.items()} |
+           {name: torch.from_numpy(packed[name]).to("cuda") for name in ("o", "down")} for _ in range(DENSE_LAYERS)]
+    launches = []
+    for layer in dev:
+        launches += [gemv(layer["qkv"], 6144, 4096), gemv(layer["o"], 4096, 4096),
+                     gemv(layer["gateup"], 28672, 4096), gemv(layer["down"], 4096, 14336)]
+    t_fused, _ = graph_time(torch, stream, launches, 20)
+    del dev, launches
+    torch.cuda.empty_cache()
+    return {"layers": DENSE_LAYERS, "bytes": total,
+            "launches": DENSE_LAYERS * len(DENSE_LAYER), "step_us": round(t * 1e6, 1),
+            "tok_s": round(1.0 / t, 1), "GBps": round(total / t / 1e9, 1),
+            "fused_launches": DENSE_LAYERS * 4, "fused_step_us": round(t_fused * 1e6, 1),
+            "fused_tok_s": round(1.0 / t_fused, 1), "fused_GBps": round(total / t_fused / 1e9, 1)}
+
+
+MOE_E, MOE_H, MOE_I, MOE_TOPK, MOE_POOL, MOE_SETS = 512, 4096, 1024, 4, 8, 32
+
+
+def moe_layer(torch, qg, stream, fmt, t_tokens):
+    """The MoE layer (512 experts + 1 shared, hidden 4096, intermediate 1024,
+    top-4) at T tokens, every expert resident.  Experts are distinct device
+    copies of a pool of MOE_POOL drawn experts (the pool repeats every
+    MOE_POOL slots; 2-3.6 GB in all, beyond the cache).  MOE_SETS router and
+    shared-gate logit sets are drawn; one graph replays a call per set, so
+    every call routes anew.  Bytes per call: the distinct experts it touches
+    (plus the shared one), gate/up and down."""
+    import workloads
+
+    lib = qg.load()
+    e_, h_, i_, k_ = MOE_E, MOE_H, MOE_I, MOE_TOPK
+    gu_sz, dn_sz = qg.qg_packed_size(fmt, 2 * i_, h_), qg.qg_packed_size(fmt, h_, i_)
+    gu = torch.empty((e_ + 1) * gu_sz, dtype=torch.uint8, device="cuda")
+    dn = torch.empty((e_ + 1) * dn_sz, dtype=torch.uint8, device="cuda")
+    pool = []
+    for j in range(MOE_POOL):
+        wg = workloads.student_t_weights_device(2 * i_, h_, 1, 3 * j).cpu().numpy()
+        wd = workloads.student_t_weights_device(h_, i_, 1, 3 * j + 2).cpu().numpy()
+        pool.append((torch.from_numpy(qg.qquant(fmt, wg, n_threads=16)).to("cuda"),
+                     torch.from_numpy(qg.qquant(fmt, wd, n_threads=16)).to("cuda")))
+    for e in range(e_ + 1):
+        gu[e * gu_sz:(e + 1) * gu_sz].copy_(pool[e % MOE_POOL][0])
+        dn[e * dn_sz:(e + 1) * dn_sz].copy_(pool[e % MOE_POOL][1])
+    del pool
+    x = workloads.normal_device((t_tokens, h_), 2, 1)
+    res = workloads.normal_device((t_tokens, h_), 2, 2)
+    logits = [workloads.normal_device((t_tokens, e_), 2, 100 + r) for r in range(MOE_SETS)]
+    slog = [workloads.normal_device((t_tokens,), 2, 200 + r) for r in range(MOE_SETS)]
+    out = torch.empty((t_tokens, h_), device="cuda")
+    ws_bytes = qg.moe_expert_ffn_workspace_size(t_tokens, e_, h_, i_, k_)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
+    fid, sp = qg.FORMATS[fmt], stream.cuda_stream
+
+    def call(r):
+        args = (fid, gu.data_ptr(), dn.data_ptr(), e_, h_, i_, k_, x.data_ptr(), res.data_ptr(),
+                logits[r].data_ptr(), slog[r].data_ptr(), t_tokens, 0, out.data_ptr(), ws.data_ptr(), ws_bytes, sp)
+        return lambda: lib.moe_expert_ffn(*args)
+
+    t, _ = graph_time(torch, stream, [call(r) for r in range(MOE_SETS)], 10)
+    t /= MOE_SETS
+    touched = np.mean([len(set(np.argsort(-lg.cpu().numpy(), axis=1, kind="stable")[:, :k_].ravel().tolist())) + 1
+                       for lg in logits])
+    nbytes = touched * (gu_sz + dn_sz)
+    del gu, dn, ws
+    torch.cuda.empty_cache()
+    return {"fmt": fmt, "T": t_tokens, "us": round(t * 1e6, 2), "experts_touched": round(float(touched), 2),
+            "bytes": int(nbytes), "GBps": round(float(nbytes) / t / 1e9, 1)}
+
+
 def cpu_baseline(seconds=12.0):
     """The oracle (numpy dequant + float64 matvec) on a bounded sample of the
     headline workload: whole 14336x4096 Q4_K GEMVs, repeated for ~seconds."""
@@ -174,7 +320,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--quick", action="store_true", help="headline only, no extra configs")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle cpu_baseline leg")
-    ap.add_argument("--profile", choices=["gemv", "copy"], default=None,
+    ap.add_argument("--profile", choices=["gemv", "copy", "probe"], default=None,
                     help="run only the headline kernel (or a 1 GiB copy) a few times, for rocprofv3")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -209,6 +355,13 @@ def main():
             head.step()
         torch.cuda.synchronize()
         log("ran 40 headline GEMVs")
+        return
+    if args.profile == "probe":
+        sink = torch.zeros(4, dtype=torch.int32, device="cuda")
+        for p in head.wp:
+            qg.qg_hbm_read_probe(p, head.bytes, sink, stream)
+        torch.cuda.synchronize()
+        log(f"ran {len(head.wp)} read probes")
         return
 
     per = head.capture()
@@ -277,6 +430,18 @@ def main():
                                  "GBps": round(nbytes / t / 1e9, 1), "Gweights_s": round(n * k * b / t / 1e9, 1)})
                     log(f"  {fmt} {n}x{k} B={b}: {t*1e6:.2f} us, {nbytes/t/1e9:.1f} GB/s")
         extra["low_bit"] = rows
+        log("8B decode step (32 layers x 7 Q4_K GEMVs)")
+        extra["dense_8b_step"] = dense_step(torch, qg, stream)
+        log(f"  {extra['dense_8b_step']}")
+        rows = []
+        for fmt in ("q4_k", "q2_k"):
+            for t_tokens in (1, 8):
+                rows.append(moe_layer(torch, qg, stream, fmt, t_tokens))
+                log(f"  moe {rows[-1]}")
+        extra["moe_layer"] = rows
+    extra["hbm_read_probe"] = read_probe(torch, qg, stream, head)
+    extra["headline_frac_of_read_probe"] = round(achieved / extra["hbm_read_probe"]["same_size_GBps"], 4)
+    log(f"  read probe {extra['hbm_read_probe']}")
 
     line = {
         "metric": "Q4_K batch-1 GEMV effective weight GB/s and % of HBM peak; tok/s-equiv",

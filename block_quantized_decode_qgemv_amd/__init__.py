@@ -61,6 +61,7 @@ _SIGNATURES = {
     "moe_expert_ffn_workspace_size": (_sz, [_i32, _i32, _i32, _i32, _i32]),
     "moe_expert_ffn": (_i32, [_i32, _vp, _vp, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _i32, _u32,
                               _vp, _vp, _sz, _vp]),
+    "qg_hbm_read_probe": (_i32, [_vp, _sz, _vp, _vp]),
     "qg_strerror": (_cp, [_i32]),
     "qg_last_error": (_cp, []),
     "qg_version": (_cp, []),
@@ -173,6 +174,12 @@ def qgemv_workspace_size(fmt, n: int, k: int, b: int = 1) -> int:
 
 def moe_expert_ffn_workspace_size(t: int, e: int, h: int, i: int, top_k: int) -> int:
     return load().moe_expert_ffn_workspace_size(t, e, h, i, top_k)
+
+
+def qg_hbm_read_probe(buf, nbytes: int, sink, stream=None) -> None:
+    """Stream-read nbytes of a device buffer (see qg_hbm_read_probe in qgemv.h)."""
+    rc = load().qg_hbm_read_probe(_dev(buf, None, "buf"), nbytes, _dev(sink, None, "sink"), _stream(stream))
+    _check(rc, "qg_hbm_read_probe")
 
 
 def qg_strerror(code: int) -> str:

@@ -196,6 +196,18 @@ int moe_expert_ffn(int fmt, const void* w_gate_up, const void* w_down, int E, in
                    const float* shared_gate_logit, int T, unsigned flags, float* out,
                    void* workspace, size_t ws_bytes, void* stream);
 
+/* ------------------------------------------------------------ measurement */
+
+/* Streaming-read probe: reads `bytes` bytes of DEVICE memory at `buf` with
+ * 128-bit non-temporal loads, the access pattern of the GEMV weight stream,
+ * and touches *sink (DEVICE, 4 bytes) only when a data-dependent value that
+ * never occurs is met, so the loads cannot be dropped.  It exists to measure
+ * the HBM read rate that the GEMV is compared with (the handbook page's
+ * decode bound, section "速度上限：带宽 ÷ 权重字节数", divides the weight bytes
+ * by that rate).  buf 16-byte aligned, bytes a positive multiple of 16;
+ * otherwise QG_EALIGN / QG_ESHAPE.  Asynchronous on `stream`. */
+int qg_hbm_read_probe(const void* buf, size_t bytes, unsigned* sink, void* stream);
+
 /* ------------------------------------------------------------------ errors */
 
 /* Static description of an error code. */

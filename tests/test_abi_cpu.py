@@ -99,6 +99,15 @@ def test_dequant_validation():
     assert lib.qg_dequant(3, P + 4, P, 4, 256, None) == -3
 
 
+@nogpu
+def test_read_probe_validation():
+    lib = qg.load()
+    assert lib.qg_hbm_read_probe(None, 16, P, None) == -1
+    assert lib.qg_hbm_read_probe(P, 0, P, None) == -2
+    assert lib.qg_hbm_read_probe(P, 24, P, None) == -2
+    assert lib.qg_hbm_read_probe(P + 4, 32, P, None) == -3
+
+
 def test_binding_rejects_host_tensors():
     import torch
 

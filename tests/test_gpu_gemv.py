@@ -193,3 +193,10 @@ def test_full_size_sampled_rows(fmt, n, k, b):
     np.testing.assert_array_equal(meta_rows[rows], OF.deinterleave_rows(sub_packed[scp:], len(rows), mpr))
     assert_parity(y[:, rows], OF.dequant(fmt, sub), x, f"{fmt} {n}x{k} B={b}")
     assert np.all(np.isfinite(y))
+
+
+@pytest.mark.parametrize("n,k", [(1024, 4096), (4096, 14336)])
+def test_decode_step_shapes_sampled_rows(n, k):
+    """The 8B step's k/v and down shapes (Q4_K, batch 1) at full size, sampled
+    rows against the oracle as in the full-size test."""
+    test_full_size_sampled_rows("q4_k", n, k, 1)

@@ -19,6 +19,11 @@ Recipes (shapes and distributions follow the pages' workloads):
 Every generator takes an explicit integer seed and a tensor id, and builds its
 stream as ``numpy.random.default_rng(SeedSequence([seed, tensor_id]))``, so a
 tensor is reproducible on its own without drawing all tensors before it.
+
+The ``*_device`` generators draw the same distributions with torch's device
+generator (seeded from seed and tensor id), for the bench's multi-gigabyte
+inputs: numpy needs about 120 ns per Student-t sample on the host.  Student-t
+is drawn as Z / sqrt(V / 5) with Z ~ N(0, 1) and V = 2 Gamma(5/2) ~ chi^2(5).
 """
 from __future__ import annotations
 
@@ -32,6 +37,8 @@ __all__ = [
     "binary_codes",
     "scale_bits_f16",
     "single_q4k_case",
+    "student_t_weights_device",
+    "normal_device",
 ]
 
 STUDENT_T_DOF = 5.0
@@ -85,3 +92,30 @@ def single_q4k_case(n: int = 1024, k: int = 1024, seed: int = 0):
     w = (g.standard_t(STUDENT_T_DOF, size=(n, k)) * STUDENT_T_SCALE).astype(np.float32)
     x = g.standard_normal(size=(1, k)).astype(np.float32)
     return w, x
+
+
+def _device_generator(seed: int, tensor_id: int, device):
+    import torch
+
+    g = torch.Generator(device=device)
+    g.manual_seed((int(seed) * 1_000_003 + int(tensor_id)) % (1 << 62))
+    return g
+
+
+def student_t_weights_device(n: int, k: int, seed: int = 0, tensor_id: int = 0, device="cuda"):
+    """float32 [n, k] torch tensor on ``device``, Student-t(5) * 0.02."""
+    import torch
+
+    g = _device_generator(seed, tensor_id, device)
+    z = torch.randn((n, k), generator=g, device=device, dtype=torch.float32)
+    v = torch._standard_gamma(torch.full((n, k), STUDENT_T_DOF / 2, device=device, dtype=torch.float32),
+                              generator=g) * 2.0
+    return z * torch.rsqrt(v / STUDENT_T_DOF) * STUDENT_T_SCALE
+
+
+def normal_device(shape, seed: int = 0, tensor_id: int = 0, device="cuda"):
+    """float32 N(0, 1) torch tensor on ``device``."""
+    import torch
+
+    return torch.randn(shape, generator=_device_generator(seed, tensor_id, device), device=device,
+                       dtype=torch.float32)
