@@ -320,7 +320,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--quick", action="store_true", help="headline only, no extra configs")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle cpu_baseline leg")
-    ap.add_argument("--profile", choices=["gemv", "copy", "probe"], default=None,
+    ap.add_argument("--profile", choices=["gemv", "copy", "probe", "moe", "step"], default=None,
                     help="run only the headline kernel (or a 1 GiB copy) a few times, for rocprofv3")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -346,6 +346,15 @@ def main():
             b.copy_(a)
         torch.cuda.synchronize()
         log("copied 1 GiB 3 times")
+        return
+
+    if args.profile == "moe":
+        for fmt in ("q4_k", "q2_k"):
+            for t_tokens in (1, 8):
+                log(f"moe {moe_layer(torch, qg, stream, fmt, t_tokens)}")
+        return
+    if args.profile == "step":
+        log(f"step {dense_step(torch, qg, stream)}")
         return
 
     log("setup: Q4_K 14336x4096 batch 1, rotating copies")

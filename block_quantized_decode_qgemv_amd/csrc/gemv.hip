@@ -53,8 +53,8 @@ gemv_kernel(const uint8_t* __restrict__ codes, const uint8_t* __restrict__ meta,
     const int g = blockIdx.x;
     Gemv<F, B, W, KCS>::run(
         codes, meta, N, K, g, [&](int b) { return x + (size_t)b * K; }, B,
-        [&](auto sums, int n_g) {
-            for (int t = threadIdx.x; t < kRowGroup * B; t += W * 64)
+        [&](auto sums, int n_g, int tid) {
+            for (int t = tid; t < kRowGroup * B; t += W * 64)
                 if (t / B < n_g) y[(size_t)(t % B) * N + g * kRowGroup + t / B] = sums(t);
         });
 }
@@ -66,8 +66,8 @@ gemv_dpp_kernel(const uint8_t* __restrict__ codes, const uint8_t* __restrict__ m
     const int g = blockIdx.x;
     GemvDpp<F, B, W, KCS>::run(
         codes, meta, N, K, g, [&](int b) { return x + (size_t)b * K; }, B,
-        [&](auto sums, int n_g) {
-            for (int t = threadIdx.x; t < kRowGroup * B; t += W * 64)
+        [&](auto sums, int n_g, int tid) {
+            for (int t = tid; t < kRowGroup * B; t += W * 64)
                 if (t / B < n_g) y[(size_t)(t % B) * N + g * kRowGroup + t / B] = sums(t);
         });
 }

@@ -384,8 +384,9 @@ struct Gemv {
 
     // One 16-row group g of a packed [N][K] matrix against nb <= B activation
     // rows; xrow(b) gives row b (K floats, 16-byte aligned).  After the parts
-    // are combined, every thread calls epi(sum, n_g), where sum(t) returns the
-    // row sum for t = rw * B + b (rows rw < n_g, batch rows b < nb valid).
+    // are combined, every thread calls epi(sum, n_g, tid), where sum(t) returns
+    // the row sum for t = rw * B + b (rows rw < n_g, batch rows b < nb valid)
+    // and tid is the thread's index in the workgroup.
     template <class XRow, class Epi>
     __device__ static void run(const uint8_t* __restrict__ codes, const uint8_t* __restrict__ meta,
                                int N, int K, int g, XRow xrow, int nb, Epi epi) {
@@ -505,7 +506,7 @@ struct Gemv {
         for (int j = 0; j < PER; ++j)
             if (tid + NT * j < kRowGroup * B) part[tid + NT * j] = sum[j];  // sums[rw * B + b]
         __syncthreads();
-        epi([&](int t) { return part[t]; }, n_g);
+        epi([&](int t) { return part[t]; }, n_g, tid);
     }
 };
 
@@ -657,8 +658,17 @@ struct GemvDpp {
     template <class XRow, class Epi>
     __device__ static void run(const uint8_t* __restrict__ codes, const uint8_t* __restrict__ meta,
                                int N, int K, int g, XRow xrow, int nb, Epi epi) {
-        __shared__ float red[W][kRowGroup * B];
-        const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+        __shared__ float red[W * kRowGroup * B];
+        run_group(codes, meta, N, K, g, xrow, nb, epi, 0, red);
+    }
+
+    // The same on waves [wave0, wave0 + W) of a larger workgroup, with the
+    // cross-wave partials in red (W * 16 * B floats of LDS).  Every wave of the
+    // workgroup must call it (it synchronizes the whole workgroup once).
+    template <class XRow, class Epi>
+    __device__ static void run_group(const uint8_t* __restrict__ codes, const uint8_t* __restrict__ meta,
+                                     int N, int K, int g, XRow xrow, int nb, Epi epi, int wave0, float* red) {
+        const int tid = threadIdx.x - 64 * wave0, lane = tid & 63, wave = tid >> 6;
         const int r = lane & 15, p = wave * 4 + (lane >> 4);
         const int n_g = min(kRowGroup, N - g * kRowGroup);
         const int rr = min(r, n_g - 1);
@@ -791,17 +801,17 @@ struct GemvDpp {
             float v = acc[b];
             v += __shfl_xor(v, 16);
             v += __shfl_xor(v, 32);
-            if (lane < 16) red[wave][r * B + b] = v;
+            if (lane < 16) red[(wave * kRowGroup + r) * B + b] = v;
         }
         __syncthreads();
         epi(
             [&](int t) {
                 float v = 0.0f;
 #pragma unroll
-                for (int w = 0; w < W; ++w) v += red[w][t];
+                for (int w = 0; w < W; ++w) v += red[w * kRowGroup * B + t];
                 return v;
             },
-            n_g);
+            n_g, tid);
     }
 };
 

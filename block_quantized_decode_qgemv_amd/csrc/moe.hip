@@ -15,11 +15,12 @@
 //      gate and up rows are interleaved (row 2i = gate i, row 2i+1 = up i), so
 //      each 16-row group holds 8 (gate, up) pairs and the epilogue writes
 //      h = silu(gate) * up directly (fused SwiGLU);
-//   3. down: one grouped GEMV of each item's h rows; the epilogue scales by
-//      the token's routing weight (sigmoid gate for the shared expert) and
-//      writes a per-(token, slot) partial output;
-//   4. combine: out = residual + sum of the K routed partials + the shared
-//      partial, in that fixed order (deterministic; no float atomics).
+//   3. down + combine: one workgroup per (16 output rows, token) runs the
+//      down projection of each of the token's K + 1 slots in its own wave
+//      group, scales it by the slot's routing weight (sigmoid gate for the
+//      shared expert), and writes out = residual + the K routed sums + the
+//      shared sum, in that fixed order (deterministic; no float atomics and
+//      no partial results leaving the workgroup).
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -39,160 +40,189 @@ constexpr int kItemInts = 8;  // expert, count, tok[2], kslot[2], wt[2] (as floa
 // Workspace layout, byte offsets (each region 256-byte aligned).
 struct MoeLayout {
     int max_items;
-    size_t items, h, partial, total;
+    size_t items, hsel, h, total;
     MoeLayout(int T, int H, int I, int top_k) {
+        (void)H;
         max_items = T * top_k + (T + 1) / 2;
         auto up = [](size_t v) { return (v + 255) / 256 * 256; };
         items = 0;
-        h = up(items + (size_t)(1 + max_items) * kItemInts * 4);
-        partial = up(h + (size_t)max_items * 2 * I * 4);
-        total = up(partial + (size_t)T * (top_k + 1) * H * 4);
+        hsel = up(items + (size_t)(1 + max_items) * kItemInts * 4);  // [T][top_k + 1]: 2 * item + b
+        h = up(hsel + (size_t)T * (top_k + 1) * 4);
+        total = up(h + (size_t)max_items * 2 * I * 4);
     }
 };
-
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m));
-    return v;
-}
-
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m);
-    return v;
-}
 
 // ------------------------------------------------------------------ route
 // items[0] = number of items; item j at items + 8*(1+j):
 //   {expert, count, tok0, tok1, kslot0, kslot1, wt0 bits, wt1 bits}
 
+// In-row DPP steps (quad_perm [1,0,3,2], [2,3,0,1], row_half_mirror,
+// row_mirror) leave each 16-lane row's result in all its lanes; the four row
+// results are then read into scalars and combined.
+template <int CTRL>
+__device__ __forceinline__ int dpp_i(int v) { return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, false); }
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+    return __builtin_bit_cast(float, dpp_i<CTRL>(__builtin_bit_cast(int, v)));
+}
+
+__device__ __forceinline__ float rl(float v, int lane) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), lane));
+}
+
+__device__ __forceinline__ float wave_max_dpp(float v) {
+    v = fmaxf(v, dpp_f<0xB1>(v));
+    v = fmaxf(v, dpp_f<0x4E>(v));
+    v = fmaxf(v, dpp_f<0x141>(v));
+    v = fmaxf(v, dpp_f<0x140>(v));
+    return fmaxf(fmaxf(rl(v, 0), rl(v, 16)), fmaxf(rl(v, 32), rl(v, 48)));
+}
+
+__device__ __forceinline__ float wave_sum_dpp(float v) {
+    v += dpp_f<0xB1>(v);
+    v += dpp_f<0x4E>(v);
+    v += dpp_f<0x141>(v);
+    v += dpp_f<0x140>(v);
+    return (rl(v, 0) + rl(v, 16)) + (rl(v, 32) + rl(v, 48));
+}
+
+constexpr int kNone = 0x7fffffff;  // "no candidate": loses to every key
+
+// (value, index) keys in a total order: larger value first, then the lower
+// index; kNone loses to everything
+__device__ __forceinline__ void key_max(float& bv, int& bi, float ov, int oi) {
+    if (oi != kNone && (bi == kNone || ov > bv || (ov == bv && oi < bi))) { bv = ov; bi = oi; }
+}
+
+template <int CTRL>
+__device__ __forceinline__ void key_step(float& bv, int& bi) {
+    key_max(bv, bi, dpp_f<CTRL>(bv), dpp_i<CTRL>(bi));
+}
+
+template <int MPL>  // experts per lane: E <= 64 * MPL
 __global__ void __launch_bounds__(512)
 moe_route_kernel(const float* __restrict__ logits, const float* __restrict__ shared_logit, int T, int E,
-                 int top_k, unsigned flags, int* __restrict__ items) {
+                 int top_k, unsigned flags, int* __restrict__ items, int* __restrict__ hsel) {
     __shared__ int sel_e[kMaxT * kMaxTopK];
     __shared__ float sel_w[kMaxT * kMaxTopK];
     __shared__ float sig[kMaxT];
-    __shared__ int sub_base[kMaxT * kMaxTopK];
-    __shared__ int n_routed;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
 
+    // (1) one wave per token: softmax statistics, then top_k rounds of a wave
+    // argmax; lane owns experts lane + 64 m (values in registers) and marks
+    // picked ones in a bit mask
     if (wave < T) {
         const float* l = logits + (size_t)wave * E;
-        float m = -INFINITY;
-        for (int i = lane; i < E; i += 64) m = fmaxf(m, l[i]);
-        m = wave_max(m);
+        const float sl = shared_logit[wave];  // requested with the router logits
+        float v[MPL];
+#pragma unroll
+        for (int m = 0; m < MPL; ++m) {
+            const int i = lane + 64 * m;
+            const float x = i < E ? l[i] : -INFINITY;
+            v[m] = __builtin_isnan(x) ? -INFINITY : x;  // NaN counts as -inf
+        }
+        float mx = -INFINITY;
+#pragma unroll
+        for (int m = 0; m < MPL; ++m) mx = fmaxf(mx, v[m]);
+        mx = wave_max_dpp(mx);
         float s = 0.0f;
-        for (int i = lane; i < E; i += 64) s += expf(l[i] - m);
-        s = wave_sum(s);
-        int chosen[kMaxTopK];
-        float wsum = 0.0f;
+#pragma unroll
+        for (int m = 0; m < MPL; ++m)
+            if (lane + 64 * m < E) s += expf(v[m] - mx);
+        s = wave_sum_dpp(s);
+        uint64_t taken = 0;
+        int my_e = 0;
+        float my_p = 0.0f, wsum = 0.0f;
         for (int k = 0; k < top_k; ++k) {
-            // (value, index) keys in a total order: larger value first, then
-            // the lower index; NaN counts as -inf and "no candidate" (index
-            // kNone) loses to everything, so the pick is always a valid expert
-            constexpr int kNone = 0x7fffffff;
             float best = -INFINITY;
             int bi = kNone;
-            for (int i = lane; i < E; i += 64) {
-                bool taken = false;
-                for (int j = 0; j < k; ++j) taken |= chosen[j] == i;
-                const float v = __builtin_isnan(l[i]) ? -INFINITY : l[i];
-                if (!taken && (bi == kNone || v > best || (v == best && i < bi))) { best = v; bi = i; }
-            }
 #pragma unroll
-            for (int msk = 32; msk >= 1; msk >>= 1) {
-                const float ov = __shfl_xor(best, msk);
-                const int oi = __shfl_xor(bi, msk);
-                if (oi != kNone && (bi == kNone || ov > best || (ov == best && oi < bi))) { best = ov; bi = oi; }
+            for (int m = 0; m < MPL; ++m) {
+                const int i = lane + 64 * m;
+                const bool free = i < E && !((taken >> m) & 1u);
+                if (free && (bi == kNone || v[m] > best)) { best = v[m]; bi = i; }  // i rises: ties keep the lower
             }
-            chosen[k] = bi;
-            const float p = expf(best - m) / s;
+            key_step<0xB1>(best, bi);
+            key_step<0x4E>(best, bi);
+            key_step<0x141>(best, bi);
+            key_step<0x140>(best, bi);
+            float wv = rl(best, 0);
+            int wi = __builtin_amdgcn_readlane(bi, 0);
+#pragma unroll
+            for (int row = 1; row < 4; ++row) key_max(wv, wi, rl(best, 16 * row), __builtin_amdgcn_readlane(bi, 16 * row));
+            if (lane == (wi & 63)) taken |= 1ull << (wi >> 6);
+            const float p = expf(wv - mx) / s;
             wsum += p;
-            if (lane == 0) {
-                sel_e[wave * top_k + k] = bi;
-                sel_w[wave * top_k + k] = p;
-            }
+            if (lane == k) { my_e = wi; my_p = p; }
         }
-        if (lane == 0) {
-            if (flags & QG_MOE_RENORM)
-                for (int k = 0; k < top_k; ++k) sel_w[wave * top_k + k] /= wsum;
-            sig[wave] = 1.0f / (1.0f + expf(-shared_logit[wave]));
+        if (lane < top_k) {
+            sel_e[wave * top_k + lane] = my_e;
+            sel_w[wave * top_k + lane] = (flags & QG_MOE_RENORM) ? my_p / wsum : my_p;
         }
+        if (lane == 0) sig[wave] = 1.0f / (1.0f + expf(-sl));
     }
     __syncthreads();
 
-    // group the pairs q = t*top_k + k by expert, in order of first appearance
-    const int P = T * top_k;
-    int e = 0, pos = 0, cnt = 0;
-    bool leader = false;
-    if (tid < P) {
-        e = sel_e[tid];
-        leader = true;
-        for (int q = 0; q < P; ++q) {
-            const bool same = sel_e[q] == e;
+    // (2) wave 0 groups the pairs q = t*top_k + k (lane q) by expert, in order of
+    // first appearance, into items of at most two tokens
+    if (wave == 0) {
+        const int P = T * top_k;  // <= 64
+        const bool act = lane < P;
+        const int e = act ? sel_e[lane] : -1 - lane;  // inactive lanes match nothing
+        int cnt = 0, pos = 0, lead = lane;
+        for (int r = 0; r < P; ++r) {
+            const int er = __builtin_amdgcn_readlane(e, r);
+            const bool same = er == e;
             cnt += same;
-            if (q < tid && same) { leader = false; ++pos; }
-        }
-    }
-    __syncthreads();
-    if (tid < P && leader) {
-        // items of the experts that appear first before this one
-        int base = 0;
-        for (int q = 0; q < tid; ++q) {
-            const int eq = sel_e[q];
-            bool first = true;
-            int c = 0;
-            for (int r = 0; r < P; ++r) {
-                c += sel_e[r] == eq;
-                first &= !(r < q && sel_e[r] == eq);
+            if (same && r < lane) {
+                ++pos;
+                lead = min(lead, r);
             }
-            if (first) base += (c + 1) / 2;
         }
-        sub_base[tid] = base;
-    }
-    if (tid == 0) {
-        int total = 0;
-        for (int q = 0; q < P; ++q) {
-            bool first = true;
-            int c = 0;
-            for (int r = 0; r < P; ++r) {
-                c += sel_e[r] == sel_e[q];
-                first &= !(r < q && sel_e[r] == sel_e[q]);
+        const int nit = (act && pos == 0) ? (cnt + 1) / 2 : 0;  // items of this expert, at its first pair
+        int base = 0, n_routed = 0;  // items of experts first seen before the lead pair; all items
+        for (int r = 0; r < P; ++r) {
+            const int nr = __builtin_amdgcn_readlane(nit, r);
+            n_routed += nr;
+            if (r < lead) base += nr;
+        }
+        if (act) {
+            const int item = base + pos / 2, slot = pos % 2;
+            int* it = items + kItemInts * (1 + item);
+            const int tok = lane / top_k, ks = lane % top_k;
+            const int wbits = __float_as_int(sel_w[lane]);
+            hsel[tok * (top_k + 1) + ks] = 2 * item + slot;
+            if (slot == 0) {
+                const int c = min(2, cnt - pos);
+                it[0] = e;
+                it[1] = c;
+                it[2] = tok;
+                it[4] = ks;
+                it[6] = wbits;
+                if (c == 1) { it[3] = tok; it[5] = ks; it[7] = 0; }  // unused second slot
+            } else {
+                it[3] = tok;
+                it[5] = ks;
+                it[7] = wbits;
             }
-            if (first) total += (c + 1) / 2;
         }
-        n_routed = total;
-    }
-    __syncthreads();
-    if (tid < P) {
-        int lead = tid;
-        for (int q = 0; q < tid; ++q)
-            if (sel_e[q] == e) { lead = q; break; }
-        const int item = sub_base[lead] + pos / 2, slot = pos % 2;
-        int* it = items + kItemInts * (1 + item);
-        if (slot == 0) {
-            it[0] = e;
-            it[1] = min(2, cnt - pos);
+        // the shared expert (index E): tokens (2j, 2j+1), weight sigmoid(s_t)
+        if (lane < (T + 1) / 2) {
+            const int j = lane;
+            int* it = items + kItemInts * (1 + n_routed + j);
+            const int c = min(2, T - 2 * j);
+            it[0] = E;
+            it[1] = c;
+            it[2] = 2 * j;
+            it[3] = c > 1 ? 2 * j + 1 : 2 * j;
+            it[4] = top_k;
+            it[5] = top_k;
+            it[6] = __float_as_int(sig[2 * j]);
+            it[7] = __float_as_int(c > 1 ? sig[2 * j + 1] : 0.0f);
         }
-        it[2 + slot] = tid / top_k;
-        it[4 + slot] = tid % top_k;
-        it[6 + slot] = __float_as_int(sel_w[tid]);
+        if (lane < T) hsel[lane * (top_k + 1) + top_k] = 2 * (n_routed + lane / 2) + (lane & 1);
+        if (lane == 0) items[0] = n_routed + (T + 1) / 2;
     }
-    // the shared expert (index E): tokens (2j, 2j+1), weight sigmoid(s_t)
-    if (tid < (T + 1) / 2) {
-        const int j = tid;
-        int* it = items + kItemInts * (1 + n_routed + j);
-        const int c = min(2, T - 2 * j);
-        it[0] = E;
-        it[1] = c;
-        it[2] = 2 * j;
-        it[3] = c > 1 ? 2 * j + 1 : 2 * j;
-        it[4] = top_k;
-        it[5] = top_k;
-        it[6] = __float_as_int(sig[2 * j]);
-        it[7] = __float_as_int(c > 1 ? sig[2 * j + 1] : 0.0f);
-    }
-    if (tid == 0) items[0] = n_routed + (T + 1) / 2;
 }
 
 // ------------------------------------------------------- grouped GEMVs
@@ -233,8 +263,8 @@ moe_gate_up_kernel(const uint8_t* __restrict__ wgu, size_t expert_bytes, size_t 
     float* hj = h + (size_t)j * 2 * I;
     auto xrow = [&](int b) { return x + (size_t)it.tok[b] * H; };
     auto epi = [&](int B) {
-        return [=](auto sums, int) {
-            for (int t = threadIdx.x; t < 8 * B; t += W * 64) {
+        return [=](auto sums, int, int tid) {
+            for (int t = tid; t < 8 * B; t += W * 64) {
                 const int i = t / B, b = t % B;
                 if (b < it.count) hj[(size_t)b * I + 8 * g + i] = silu(sums((2 * i) * B + b)) * sums((2 * i + 1) * B + b);
             }
@@ -244,46 +274,40 @@ moe_gate_up_kernel(const uint8_t* __restrict__ wgu, size_t expert_bytes, size_t 
     else GemvDpp<F, 2, W, KCS>::run(codes, meta, 2 * I, H, g, xrow, 2, epi(2));
 }
 
-// down: partial[tok][kslot][row] = weight * (W_down h)[row]
-template <int F, int W, int KCS>
-__global__ void __launch_bounds__(W * 64)
+// down + combine: one workgroup per (16-row group g, token t).  Its waves form
+// top_k + 1 groups of WD waves; group s runs the down projection of the
+// token's slot s (the K routed experts, then the shared one) on its h row and
+// scales it by the slot's weight; then out = residual + the slot sums in slot
+// order.  A token pair sharing an item reads that expert's down rows twice,
+// but no partial leaves the workgroup.
+template <int F, int WD, int KCS>
+__global__ void __launch_bounds__(1024)
 moe_down_kernel(const uint8_t* __restrict__ wdn, size_t expert_bytes, size_t codes_bytes, int H, int I,
-                int top_k, const int* __restrict__ items, const float* __restrict__ h, float* __restrict__ partial) {
-    const int j = blockIdx.y;
-    if (j >= items[0]) return;
-    const Item it = read_item(items, j);
-    const uint8_t* codes = wdn + (size_t)it.expert * expert_bytes;
+                int top_k, const int* __restrict__ items, const int* __restrict__ hsel,
+                const float* __restrict__ h, const float* __restrict__ residual, float* __restrict__ out) {
+    __shared__ float red[kMaxTopK + 1][WD * kRowGroup];
+    __shared__ float slot_sum[kMaxTopK + 1][kRowGroup];
+    const int g = blockIdx.x, t = blockIdx.y;
+    const int s = threadIdx.x / (64 * WD);  // slot group, uniform per wave
+    const int hs = hsel[t * (top_k + 1) + s];
+    const int* it = items + kItemInts * (1 + (hs >> 1));
+    const float wt = __int_as_float(it[6 + (hs & 1)]);
+    const uint8_t* codes = wdn + (size_t)it[0] * expert_bytes;
     const uint8_t* meta = codes + codes_bytes;
-    const int g = blockIdx.x;
-    const float* hj = h + (size_t)j * 2 * I;
-    auto xrow = [&](int b) { return hj + (size_t)b * I; };
-    auto epi = [&](int B) {
-        return [=](auto sums, int n_g) {
-            for (int t = threadIdx.x; t < kRowGroup * B; t += W * 64) {
-                const int rw = t / B, b = t % B;
-                // selects, not it.tok[b]: a runtime index would put the item in scratch
-                const int tok = b ? it.tok[1] : it.tok[0], ks = b ? it.kslot[1] : it.kslot[0];
-                const float wt = b ? it.wt[1] : it.wt[0];
-                if (b < it.count && rw < n_g)
-                    partial[((size_t)tok * (top_k + 1) + ks) * H + kRowGroup * g + rw] = wt * sums(t);
-            }
-        };
-    };
-    if (it.count == 1) GemvDpp<F, 1, W, KCS>::run(codes, meta, H, I, g, xrow, 1, epi(1));
-    else GemvDpp<F, 2, W, KCS>::run(codes, meta, H, I, g, xrow, 2, epi(2));
-}
-
-// out = residual + sum_k partial[k] (k = 0 .. top_k, the last being the
-// shared expert), in that order
-__global__ void __launch_bounds__(256)
-moe_combine_kernel(const float* __restrict__ residual, const float* __restrict__ partial, float* __restrict__ out,
-                   int T, int H, int top_k) {
-    const int idx = blockIdx.x * 256 + threadIdx.x;
-    if (idx >= T * H) return;
-    const int t = idx / H, c = idx - t * H;
-    float v = residual[idx];
-    for (int k = 0; k <= top_k; ++k) v += partial[((size_t)t * (top_k + 1) + k) * H + c];
-    out[idx] = v;
+    const float* xr = h + (size_t)hs * I;
+    GemvDpp<F, 1, WD, KCS>::run_group(
+        codes, meta, H, I, g, [&](int) { return xr; }, 1,
+        [&](auto sum, int, int tid) {
+            if (tid < kRowGroup) slot_sum[s][tid] = wt * sum(tid);
+        },
+        s * WD, &red[s][0]);
+    __syncthreads();
+    if (threadIdx.x < kRowGroup) {
+        const size_t o = (size_t)t * H + (size_t)kRowGroup * g + threadIdx.x;
+        float v = residual[o];
+        for (int k = 0; k <= top_k; ++k) v += slot_sum[k][threadIdx.x];
+        out[o] = v;
+    }
 }
 
 // ------------------------------------------------------------- launchers
@@ -297,12 +321,20 @@ hipError_t launch_gate_up_w(const uint8_t* wgu, int H, int I, const float* x, co
     return hipGetLastError();
 }
 
-template <int F, int W, int KCS>
-hipError_t launch_down_w(const uint8_t* wdn, int H, int I, int top_k, const int* items, const float* h,
-                         float* partial, int max_items, hipStream_t st) {
+template <int F, int WD, int KCS>
+hipError_t launch_down_w(const uint8_t* wdn, int H, int I, int top_k, int T, const int* items, const int* hsel,
+                         const float* h, const float* residual, float* out, hipStream_t st) {
     const size_t eb = qg_packed_size(F, H, I), cb = qg_codes_plane_size(F, H, I);
-    hipLaunchKernelGGL((moe_down_kernel<F, W, KCS>), dim3(H / kRowGroup, max_items), dim3(W * 64), 0, st,
-                       wdn, eb, cb, H, I, top_k, items, h, partial);
+    hipLaunchKernelGGL((moe_down_kernel<F, WD, KCS>), dim3(H / kRowGroup, T), dim3((top_k + 1) * WD * 64), 0, st,
+                       wdn, eb, cb, H, I, top_k, items, hsel, h, residual, out);
+    return hipGetLastError();
+}
+
+template <int MPL>
+hipError_t launch_route(const float* logits, const float* slogit, int T, int E, int top_k, unsigned flags,
+                        int* items, int* hsel, hipStream_t st) {
+    hipLaunchKernelGGL(moe_route_kernel<MPL>, dim3(1), dim3(512), 0, st, logits, slogit, T, E, top_k, flags, items,
+                       hsel);
     return hipGetLastError();
 }
 
@@ -315,10 +347,16 @@ hipError_t launch_moe(const uint8_t* wgu, const uint8_t* wdn, int E, int H, int 
     static_assert(dpp_max_batch<F>() >= 2, "two tokens per item");
     const MoeLayout L(T, H, I, top_k);
     int* items = reinterpret_cast<int*>(ws + L.items);
+    int* hsel = reinterpret_cast<int*>(ws + L.hsel);
     float* h = reinterpret_cast<float*>(ws + L.h);
-    float* partial = reinterpret_cast<float*>(ws + L.partial);
-    hipLaunchKernelGGL(moe_route_kernel, dim3(1), dim3(512), 0, st, logits, slogit, T, E, top_k, flags, items);
-    hipError_t e = hipGetLastError();
+    hipError_t e;
+    if (E <= 64) e = launch_route<1>(logits, slogit, T, E, top_k, flags, items, hsel, st);
+    else if (E <= 128) e = launch_route<2>(logits, slogit, T, E, top_k, flags, items, hsel, st);
+    else if (E <= 256) e = launch_route<4>(logits, slogit, T, E, top_k, flags, items, hsel, st);
+    else if (E <= 512) e = launch_route<8>(logits, slogit, T, E, top_k, flags, items, hsel, st);
+    else if (E <= 1024) e = launch_route<16>(logits, slogit, T, E, top_k, flags, items, hsel, st);
+    else if (E <= 2048) e = launch_route<32>(logits, slogit, T, E, top_k, flags, items, hsel, st);
+    else e = launch_route<64>(logits, slogit, T, E, top_k, flags, items, hsel, st);
     if (e != hipSuccess) return e;
     switch (pick_waves_dpp<F, KCS>(H)) {
         case 1: e = launch_gate_up_w<F, 1, KCS>(wgu, H, I, x, items, h, L.max_items, st); break;
@@ -328,17 +366,15 @@ hipError_t launch_moe(const uint8_t* wgu, const uint8_t* wdn, int E, int H, int 
         default: e = launch_gate_up_w<F, 16, KCS>(wgu, H, I, x, items, h, L.max_items, st); break;
     }
     if (e != hipSuccess) return e;
-    switch (pick_waves_dpp<F, KCS>(I)) {
-        case 1: e = launch_down_w<F, 1, KCS>(wdn, H, I, top_k, items, h, partial, L.max_items, st); break;
-        case 2: e = launch_down_w<F, 2, KCS>(wdn, H, I, top_k, items, h, partial, L.max_items, st); break;
-        case 4: e = launch_down_w<F, 4, KCS>(wdn, H, I, top_k, items, h, partial, L.max_items, st); break;
-        case 8: e = launch_down_w<F, 8, KCS>(wdn, H, I, top_k, items, h, partial, L.max_items, st); break;
-        default: e = launch_down_w<F, 16, KCS>(wdn, H, I, top_k, items, h, partial, L.max_items, st); break;
+    // down waves per slot: what the row needs, within 16 waves for top_k + 1 slots
+    int wd = pick_waves_dpp<F, KCS>(I);
+    while (wd > 1 && (top_k + 1) * wd > 16) wd /= 2;
+    switch (wd) {
+        case 1: return launch_down_w<F, 1, KCS>(wdn, H, I, top_k, T, items, hsel, h, residual, out, st);
+        case 2: return launch_down_w<F, 2, KCS>(wdn, H, I, top_k, T, items, hsel, h, residual, out, st);
+        case 4: return launch_down_w<F, 4, KCS>(wdn, H, I, top_k, T, items, hsel, h, residual, out, st);
+        default: return launch_down_w<F, 8, KCS>(wdn, H, I, top_k, T, items, hsel, h, residual, out, st);
     }
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(moe_combine_kernel, dim3((T * H + 255) / 256), dim3(256), 0, st, residual, partial, out, T, H,
-                       top_k);
-    return hipGetLastError();
 }
 
 }  // namespace

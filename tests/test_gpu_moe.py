@@ -171,6 +171,37 @@ def test_moe_dominant_logit_matches_single_expert():
         np.testing.assert_allclose(out[tok], residual[tok] + o[0], rtol=1e-4, atol=1e-4)
 
 
+@pytest.mark.parametrize("e", [100, 1000, 4096])
+def test_moe_many_experts(e):
+    """Router sizes past 512 (more experts per lane in the route kernel, up to
+    the 4096 limit); only the selected experts hold weights, every other slot
+    is 0xFF (NaN scales)."""
+    fmt, h, i, top_k, t = "q4_k", 256, 256, 8, 5
+    x, residual, logits, s = inputs(t, e, h, seed=900 + e)
+    ids, _, _ = OM.route(logits, top_k)
+    used = sorted(set(ids.reshape(-1).tolist()) | {e})
+    gu_sz, dn_sz = qg.qg_packed_size(fmt, 2 * i, h), qg.qg_packed_size(fmt, h, i)
+    gu = torch.full(((e + 1) * gu_sz,), 0xFF, dtype=torch.uint8, device="cuda")
+    dn = torch.full(((e + 1) * dn_sz,), 0xFF, dtype=torch.uint8, device="cuda")
+    experts = {}
+    for ex in used:
+        experts[ex] = random_expert(fmt, h, i, 17, ex)
+        gu[ex * gu_sz:(ex + 1) * gu_sz].copy_(dev(experts[ex].gu_packed))
+        dn[ex * dn_sz:(ex + 1) * dn_sz].copy_(dev(experts[ex].dn_packed))
+
+    class Sparse:
+        def __len__(self):
+            return e + 1
+
+        def __getitem__(self, j):
+            # the oracle reads slot 0 for the intermediate width only
+            return experts[j] if j in experts else experts[e]
+
+    out = run_moe(fmt, gu, dn, e, h, i, top_k, x, residual, logits, s)
+    assert np.all(np.isfinite(out)), "a kernel read an unselected expert"
+    check(out, Layer(Sparse()), x, residual, logits, s, top_k, False, f"E={e}")
+
+
 def test_moe_deterministic():
     fmt, e, h, i, top_k, t = "q2_k", 16, 512, 256, 4, 8
     layer, gu, dn = small_layer(fmt, e, h, i, seed=15)
