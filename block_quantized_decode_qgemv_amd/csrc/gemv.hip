@@ -177,12 +177,15 @@ hipError_t launch_gemv_b(const uint8_t* codes, const uint8_t* meta, const float*
                          int N, int K, hipStream_t st) {
     if constexpr (B <= dpp_max_batch<F>()) {
         // x in registers, read across lanes by DPP (no LDS staging)
-        switch (pick_waves_dpp<F, dpp_lane_units<F>()>(K)) {
+        constexpr int MW = dpp_max_waves<F, B>();
+        switch (pick_waves_dpp<F, dpp_lane_units<F>()>(K, MW)) {
             case 1: return launch_gemv_dpp_w<F, B, 1>(codes, meta, x, y, N, K, st);
             case 2: return launch_gemv_dpp_w<F, B, 2>(codes, meta, x, y, N, K, st);
             case 4: return launch_gemv_dpp_w<F, B, 4>(codes, meta, x, y, N, K, st);
             case 8: return launch_gemv_dpp_w<F, B, 8>(codes, meta, x, y, N, K, st);
-            default: return launch_gemv_dpp_w<F, B, 16>(codes, meta, x, y, N, K, st);
+            default:
+                if constexpr (MW == 16) return launch_gemv_dpp_w<F, B, 16>(codes, meta, x, y, N, K, st);
+                return hipErrorInvalidConfiguration;  // never chosen
         }
     }
     constexpr int KCS = lane_units<F>();

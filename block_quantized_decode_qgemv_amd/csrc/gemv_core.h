@@ -624,9 +624,9 @@ template <int F> constexpr bool is_kquant() { return F == QG_Q4_K || F == QG_Q2_
 template <int F> constexpr int dpp_lane_units() {
     return F == QG_BIN ? 2 : 4;
 }
-// Largest batch for the register-x kernel: x registers per lane B*NXC/16 <= 32.
+// Largest batch for the register-x kernel: x registers per lane B*NXC/16 <= 64.
 template <int F> constexpr int dpp_max_batch() {
-    return 32 / (dpp_lane_units<F>() * Fmt<F>::CPC / 16);
+    return 64 / (dpp_lane_units<F>() * Fmt<F>::CPC / 16);
 }
 
 template <int F, int B, int W, int KCS>
@@ -644,7 +644,7 @@ struct GemvDpp {
     static constexpr int UPS = is_kquant<F>() ? T::BLOCK / CPC : 1;  // units per super-block
     static_assert(NXC % 64 == 0, "a part covers whole 64-column spans");
     static_assert(!is_kquant<F>() || UPS % KCS == 0, "a K-quant part stays in one super-block");
-    static_assert(B * NX4 * 4 <= 32, "x registers per lane");
+    static_assert(B * NX4 * 4 <= 64, "x registers per lane");
 
     // column sum of the GS columns from part column CS of one batch row;
     // gs[m] holds the DPP sums of span m
@@ -815,13 +815,22 @@ struct GemvDpp {
     }
 };
 
-// Waves per workgroup of the register-x kernel: the fewest (1..16, powers of
-// two) whose 4W parts cover the row in one slice, else 16 and several slices.
+// Most waves per workgroup of the register-x kernel at batch B: 16, or 8 when
+// more than 40 x registers per lane would leave too few VGPRs under the
+// 128-per-wave limit of a 1024-thread workgroup.
+template <int F, int B>
+constexpr int dpp_max_waves() {
+    return B * (dpp_lane_units<F>() * Fmt<F>::CPC / 16) > 40 ? 8 : 16;
+}
+
+// Waves per workgroup of the register-x kernel: the fewest (powers of two up
+// to max_w) whose 4W parts cover the row in one slice, else max_w and several
+// slices.
 template <int F, int KCS>
-int pick_waves_dpp(int K) {
+int pick_waves_dpp(int K, int max_w = 16) {
     const int nch = K / Fmt<F>::BLOCK * Fmt<F>::CB / 16;
     int w = 1;
-    while (w < 16 && 4 * w * KCS < nch) w *= 2;
+    while (w < max_w && 4 * w * KCS < nch) w *= 2;
     return w;
 }
 
