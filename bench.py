@@ -89,8 +89,14 @@ class Gemv:
             packed = qg.qquant(fmt, workloads.student_t_weights(n, k, seed, n), n_threads=16)
         self.bytes = packed.size
         copies = max(1, -(-min_bytes // self.bytes))
+        # the copies are slices of one allocation, 256-byte aligned
+        stride = -(-self.bytes // 256) * 256
+        self.pool = torch.empty(stride * copies, dtype=torch.uint8, device="cuda")
         src = torch.from_numpy(packed).to("cuda")
-        self.w = [src] + [src.clone() for _ in range(copies - 1)]
+        self.w = [self.pool[i * stride:i * stride + self.bytes] for i in range(copies)]
+        for t in self.w:
+            t.copy_(src)
+        del src
         self.x = torch.from_numpy(workloads.normal((b, k), seed, 99)).to("cuda")
         self.y = torch.empty((b, n), device="cuda")
         self.lib = qg.load()

@@ -245,11 +245,15 @@ hipError_t launch_dequant(int fmt, const uint8_t* codes, const uint8_t* meta, fl
     }
 }
 
+constexpr int64_t kMaxGemvK = (int64_t)1 << 26;
+
 int check_gemv_args(int fmt, const void* w, const float* x, const float* y, int64_t N, int64_t K, int B) {
     int rc = check_matrix(fmt, N, K);
     if (rc) return rc;
     if (!w || !x || !y) return fail(QG_EINVAL, "null w, x or y");
     if (B < 1 || B > QG_MAX_BATCH) return fail(QG_ERANGE, "B=%d must be in [1, %d]", B, QG_MAX_BATCH);
+    // offsets inside a 16-row group are 32-bit
+    if (K > kMaxGemvK) return fail(QG_ESHAPE, "K=%lld exceeds the GEMV limit %lld", (long long)K, (long long)kMaxGemvK);
     if (!aligned(w, 16)) return fail(QG_EALIGN, "w must be 16-byte aligned");
     if (!aligned(x, 16)) return fail(QG_EALIGN, "x must be 16-byte aligned");
     if (!aligned(y, 4)) return fail(QG_EALIGN, "y must be 4-byte aligned");

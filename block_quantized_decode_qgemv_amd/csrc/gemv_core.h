@@ -580,6 +580,35 @@ __device__ __forceinline__ void fma4_bcast(float (&a)[4], const float4& xa, cons
         : "+v"(a[0]), "+v"(a[1]), "+v"(a[2]), "+v"(a[3])
         : "v"(xa.x), "v"(xa.y), "v"(xa.z), "v"(xa.w), "v"(w[0]), "v"(w[1]), "v"(w[2]), "v"(w[3]), "n"(L));
 }
+// a[k] = w[k] * (component k of lane L's xa): the first block of a sum, so
+// the accumulators need no zeroing (outputs written before the inputs are
+// all read, hence early-clobber)
+template <int L>
+__device__ __forceinline__ void mul4_bcast(float (&a)[4], const float4& xa, const float* w) {
+    asm("s_nop 1\n\t"
+        "v_mul_f32_dpp %0, %4, %8 row_newbcast:%c12 row_mask:0xf bank_mask:0xf\n\t"
+        "v_mul_f32_dpp %1, %5, %9 row_newbcast:%c12 row_mask:0xf bank_mask:0xf\n\t"
+        "v_mul_f32_dpp %2, %6, %10 row_newbcast:%c12 row_mask:0xf bank_mask:0xf\n\t"
+        "v_mul_f32_dpp %3, %7, %11 row_newbcast:%c12 row_mask:0xf bank_mask:0xf"
+        : "=&v"(a[0]), "=&v"(a[1]), "=&v"(a[2]), "=&v"(a[3])
+        : "v"(xa.x), "v"(xa.y), "v"(xa.z), "v"(xa.w), "v"(w[0]), "v"(w[1]), "v"(w[2]), "v"(w[3]), "n"(L));
+}
+template <int L>
+__device__ __forceinline__ void mul8_bcast(float (&a)[4], const float4& xa, const float* w) {
+    asm("s_nop 1\n\t"
+        "v_mul_f32_dpp %0, %4, %8 row_newbcast:%c16 row_mask:0xf bank_mask:0xf\n\t"
+        "v_mul_f32_dpp %1, %5, %9 row_newbcast:%c16 row_mask:0xf bank_mask:0xf\n\t"
+        "v_mul_f32_dpp %2, %6, %10 row_newbcast:%c16 row_mask:0xf bank_mask:0xf\n\t"
+        "v_mul_f32_dpp %3, %7, %11 row_newbcast:%c16 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %0, %4, %12 row_newbcast:%c17 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %1, %5, %13 row_newbcast:%c17 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %2, %6, %14 row_newbcast:%c17 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %3, %7, %15 row_newbcast:%c17 row_mask:0xf bank_mask:0xf"
+        : "=&v"(a[0]), "=&v"(a[1]), "=&v"(a[2]), "=&v"(a[3])
+        : "v"(xa.x), "v"(xa.y), "v"(xa.z), "v"(xa.w), "v"(w[0]), "v"(w[1]), "v"(w[2]), "v"(w[3]),
+          "v"(w[4]), "v"(w[5]), "v"(w[6]), "v"(w[7]), "n"(L), "n"(L + 1));
+}
+
 // the same for w[0..3] against lane L and w[4..7] against lane L + 1
 template <int L>
 __device__ __forceinline__ void fma8_bcast(float (&a)[4], const float4& xa, const float* w) {
@@ -604,14 +633,17 @@ __device__ __forceinline__ float row_bcast(float v) {
 }
 
 // a[t % 4] += w[t] * x[column CB + t] over the CPD columns from part column CB
-template <int CB, int CPD, int NX4>
+// (FIRST: the accumulators start with these products)
+template <int CB, int CPD, int NX4, bool FIRST>
 __device__ __forceinline__ void fma_cols(float (&a)[4], const float4 (&xv)[NX4], const float* w) {
     if constexpr (CPD == 4) {
-        fma4_bcast<(CB % 64) / 4>(a, xv[CB / 64], w);
+        if constexpr (FIRST) mul4_bcast<(CB % 64) / 4>(a, xv[CB / 64], w);
+        else fma4_bcast<(CB % 64) / 4>(a, xv[CB / 64], w);
     } else {
         static_for<CPD / 8>([&](auto G) {
             constexpr int c = CB + 8 * decltype(G)::value;
-            fma8_bcast<(c % 64) / 4>(a, xv[c / 64], w + 8 * decltype(G)::value);
+            if constexpr (FIRST && decltype(G)::value == 0) mul8_bcast<(c % 64) / 4>(a, xv[c / 64], w);
+            else fma8_bcast<(c % 64) / 4>(a, xv[c / 64], w + 8 * decltype(G)::value);
         });
     }
 }
@@ -709,8 +741,8 @@ struct GemvDpp {
             // its end are dropped by the scale step)
             uint32_t wd[is_kquant<F>() ? 4 : (MB + 3) / 4];
             if constexpr (is_kquant<F>()) {
-                const int sbi = min(c0, nch - 1) / UPS, uo = min(c0, nch - 1) % UPS;
-                const uint4 v = ld_weights<uint4>(gmr + (size_t)sbi * ustride);
+                const int sbi = c0 / UPS, uo = c0 % UPS;
+                const uint4 v = ld_weights<uint4>(gmr + min(sbi, nb_blocks - 1) * ustride);
                 // pairs of the part's first unit moved to the bottom of the field
                 const unsigned __int128 f =
                     ((unsigned __int128)v.z << 64 | (unsigned __int128)v.y << 32 | v.x) >> (12 * SUBS * uo);
@@ -756,15 +788,14 @@ struct GemvDpp {
                 const uint32_t dw[4] = {q[i].x, q[i].y, q[i].z, q[i].w};
                 static_for<SUBS>([&](auto S) {
                     constexpr int s = decltype(S)::value;
-                    float pa[B][4];
-#pragma unroll
-                    for (int b = 0; b < B; ++b) pa[b][0] = pa[b][1] = pa[b][2] = pa[b][3] = 0.0f;
+                    float pa[B][4];  // started by the first dword's multiplies
                     static_for<DPS>([&](auto D) {
                         constexpr int d = s * DPS + decltype(D)::value;
                         float w[CPD];
                         U::decode(dw[d], w);
 #pragma unroll
-                        for (int b = 0; b < B; ++b) fma_cols<i * CPC + d * CPD, CPD, NX4>(pa[b], xv[b], w);
+                        for (int b = 0; b < B; ++b)
+                            fma_cols<i * CPC + d * CPD, CPD, NX4, decltype(D)::value == 0>(pa[b], xv[b], w);
                     });
                     float ps[B];
 #pragma unroll

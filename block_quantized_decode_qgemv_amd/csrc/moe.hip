@@ -385,7 +385,8 @@ using namespace qg;
 extern "C" {
 
 size_t moe_expert_ffn_workspace_size(int T, int E, int H, int I, int top_k) {
-    if (T < 1 || T > kMaxT || E < 1 || E > kMaxE || H < 256 || I < 256 || H % 256 || I % 256 || top_k < 1 ||
+    if (T < 1 || T > kMaxT || E < 1 || E > kMaxE || H < 256 || I < 256 || H % 256 || I % 256 ||
+        H > (1 << 26) || I > (1 << 26) || top_k < 1 ||
         top_k > kMaxTopK || top_k > E)
         return 0;
     return MoeLayout(T, H, I, top_k).total;
@@ -403,8 +404,8 @@ int moe_expert_ffn(int fmt, const void* w_gate_up, const void* w_down, int E, in
     if (E < 1 || E > kMaxE) return fail(QG_ERANGE, "E=%d must be in [1, %d]", E, kMaxE);
     if (top_k < 1 || top_k > kMaxTopK || top_k > E)
         return fail(QG_ERANGE, "top_k=%d must be in [1, min(E, %d)]", top_k, kMaxTopK);
-    if (H < 256 || H % 256 || I < 256 || I % 256)
-        return fail(QG_ESHAPE, "H=%d and I=%d must be positive multiples of 256", H, I);
+    if (H < 256 || H % 256 || I < 256 || I % 256 || H > (1 << 26) || I > (1 << 26))
+        return fail(QG_ESHAPE, "H=%d and I=%d must be multiples of 256 in [256, 2^26]", H, I);
     if (flags & ~QG_MOE_RENORM) return fail(QG_EINVAL, "unknown flags 0x%x", flags);
     if (!aligned(w_gate_up, 16) || !aligned(w_down, 16) || !aligned(x, 16) || !aligned(workspace, 16))
         return fail(QG_EALIGN, "weights, x and workspace must be 16-byte aligned");

@@ -111,7 +111,9 @@ size_t qgemv_workspace_size(int fmt, int64_t N, int64_t K, int B);
  *   w   DEVICE, packed [N][K] matrix of format fmt, 16-byte aligned.
  *   x   DEVICE, fp32 [B][K] row-major, 16-byte aligned.
  *   y   DEVICE, fp32 [B][N] row-major, 4-byte aligned; overwritten.
- *   N >= 1 (any value); K a positive multiple of the block size; 1 <= B <= 8.
+ *   N >= 1 (any value); K a positive multiple of the block size, at most
+ *   2^26 (offsets inside a 16-row group are 32-bit);
+ *   1 <= B <= 8.
  *   ws  DEVICE scratch of >= qgemv_workspace_size() bytes, 16-byte aligned,
  *       or NULL when that size is 0.
  * Accuracy: |y - y_exact| <= 2e-5 * sum_k |W[n][k] X[b][k]| + 1e-7, where
@@ -187,8 +189,9 @@ int qpack_bin(const uint8_t* bits, const uint16_t* scale_f16, int64_t N, int64_t
  *   router_logits DEVICE fp32 [T][E]; shared_gate_logit DEVICE fp32 [T].
  *   workspace  DEVICE scratch >= moe_expert_ffn_workspace_size() bytes,
  *              16-byte aligned.
- *   1 <= T <= 8, 1 <= top_k <= min(E, 8), 1 <= E <= 4096, H and I positive
- *   multiples of 256.  Deterministic (fixed-order sums, no float atomics).
+ *   1 <= T <= 8, 1 <= top_k <= min(E, 8), 1 <= E <= 4096, H and I
+ *   multiples of 256 in [256, 2^26].  Deterministic (fixed-order sums, no
+ *   float atomics).
  * Errors: QG_EINVAL, QG_ESHAPE, QG_ERANGE, QG_EALIGN, QG_EHIP. */
 size_t moe_expert_ffn_workspace_size(int T, int E, int H, int I, int top_k);
 int moe_expert_ffn(int fmt, const void* w_gate_up, const void* w_down, int E, int H, int I, int top_k,

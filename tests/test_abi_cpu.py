@@ -79,6 +79,7 @@ P = 0x10000  # fake 16-byte aligned pointer value
     (dict(fmt=3, n=4, k=256, b=1, w=0), -1),     # null w
     (dict(fmt=3, n=4, k=256, b=1, x=0), -1),     # null x
     (dict(fmt=3, n=4, k=256, b=1, y=0), -1),     # null y
+    (dict(fmt=3, n=4, k=1 << 27, b=1), -2),      # K beyond the GEMV limit
     (dict(fmt=3, n=4, k=256, b=1, w=P + 8), -3),  # misaligned w
     (dict(fmt=3, n=4, k=256, b=1, x=P + 4), -3),  # misaligned x
     (dict(fmt=3, n=4, k=256, b=1, y=P + 2), -3),  # misaligned y
