@@ -709,9 +709,10 @@ struct GemvDpp {
         const int nch = row_codes >> 4;
         const bool meta_whole = (row_meta & 15) == 0;
         const int ustride = n_g * 16;
-        const uint8_t* gcr = codes + (size_t)g * kRowGroup * row_codes + rr * 16;
+        // uniform group bases plus unsigned 32-bit lane offsets (scalar-base loads)
+        const uint8_t* gc = codes + (size_t)g * kRowGroup * row_codes;
         const uint8_t* gm = meta + (size_t)g * kRowGroup * row_meta;
-        const uint8_t* gmr = gm + rr * 16;
+        const uint32_t ro = (uint32_t)rr * 16;
 
         float acc[B];
 #pragma unroll
@@ -732,8 +733,8 @@ struct GemvDpp {
                     for (int m = 0; m < NX4; ++m) {
                         // columns past K read the row's last float4 instead: they
                         // only meet code units whose contributions are dropped
-                        const int c = min(k0 + 64 * m + 4 * r, K - 4);
-                        xv[b][m] = *(const float4*)(xb + c);
+                        const uint32_t c = (uint32_t)min(k0 + 64 * m + 4 * r, K - 4);
+                        xv[b][m] = *(const float4*)((const uint8_t*)xb + c * 4u);
                     }
                 }
             }
@@ -742,7 +743,7 @@ struct GemvDpp {
             uint32_t wd[is_kquant<F>() ? 4 : (MB + 3) / 4];
             if constexpr (is_kquant<F>()) {
                 const int sbi = c0 / UPS, uo = c0 % UPS;
-                const uint4 v = ld_weights<uint4>(gmr + min(sbi, nb_blocks - 1) * ustride);
+                const uint4 v = ld_weights<uint4>(gm + ((uint32_t)min(sbi, nb_blocks - 1) * ustride + ro));
                 // pairs of the part's first unit moved to the bottom of the field
                 const unsigned __int128 f =
                     ((unsigned __int128)v.z << 64 | (unsigned __int128)v.y << 32 | v.x) >> (12 * SUBS * uo);
@@ -750,7 +751,7 @@ struct GemvDpp {
             } else {
                 const int m0 = min(c0, (nch - 1) / KCS * KCS) * T::MBU;
                 if (meta_whole) {
-                    const uint8_t* pm = gmr + (m0 >> 4) * ustride + (m0 & 15);
+                    const uint8_t* pm = gm + ((uint32_t)(m0 >> 4) * ustride + ro + (m0 & 15));
                     if constexpr (MB >= 16) {
                         const uint4 v = ld_weights<uint4>(pm);
                         wd[0] = v.x; wd[1] = v.y; wd[2] = v.z; wd[3] = v.w;
@@ -766,7 +767,7 @@ struct GemvDpp {
             }
             uint4 q[KCS];
 #pragma unroll
-            for (int i = 0; i < KCS; ++i) q[i] = ld_weights<uint4>(gcr + min(c0 + i, nch - 1) * ustride);
+            for (int i = 0; i < KCS; ++i) q[i] = ld_weights<uint4>(gc + ((uint32_t)min(c0 + i, nch - 1) * ustride + ro));
 
             // (3) column-sum spans of every batch row
             float gs[B][NX4];
