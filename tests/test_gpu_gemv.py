@@ -97,15 +97,28 @@ def test_gemv_parity(fmt, b, n, kb):
 
 
 @pytest.mark.parametrize("fmt", OF.FORMATS)
-@pytest.mark.parametrize("b", [1, 2])
+@pytest.mark.parametrize("b", [1, 2, 4, 8])
 def test_gemv_widest_workgroup(fmt, b):
     """K = 16384 gives the register-x kernel its widest workgroup (16 waves,
     one per SIMD slot at low occupancy, where back-to-back issue of a wave's
-    instructions is most likely), with several slices for the narrow-unit
-    formats; 33 rows leave a one-row last group."""
+    instructions is most likely) at small batches, and 8 waves with several
+    K slices at the larger ones (and the LDS kernel for low-bit batch 8);
+    33 rows leave a one-row last group."""
     n, k = 33, 16384
     blk = make_blocks(fmt, n, k, seed=8, tid=b)
     x = workloads.normal((b, k), 8, 100 + b)
+    y = run_gemv(fmt, OF.pack(fmt, blk), x, n, k)
+    assert_parity(y, OF.dequant(fmt, blk), x, f"{fmt} B={b} N={n} K={k}")
+
+
+@pytest.mark.parametrize("fmt", OF.FORMATS)
+@pytest.mark.parametrize("b", [3, 5, 6, 7])
+def test_gemv_odd_batches(fmt, b):
+    """Every batch size has its own kernel instance (register-x up to 8 for Q8_0
+    and Q4_x, up to 4 for the low-bit formats, LDS beyond)."""
+    n, k = 45, 2048
+    blk = make_blocks(fmt, n, k, seed=9, tid=b)
+    x = workloads.normal((b, k), 9, 300 + b)
     y = run_gemv(fmt, OF.pack(fmt, blk), x, n, k)
     assert_parity(y, OF.dequant(fmt, blk), x, f"{fmt} B={b} N={n} K={k}")
 
