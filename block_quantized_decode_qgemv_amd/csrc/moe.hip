@@ -86,12 +86,15 @@ __device__ __forceinline__ float wave_sum_dpp(float v) {
     return (rl(v, 0) + rl(v, 16)) + (rl(v, 32) + rl(v, 48));
 }
 
-constexpr int kNone = 0x7fffffff;  // "no candidate": loses to every key
-
 // (value, index) keys in a total order: larger value first, then the lower
-// index; kNone loses to everything
+// index.  The start key (-inf, kNoIndex) loses to every expert, -inf logits
+// included, so a round's pick is always a valid expert.
+constexpr int kNoIndex = 0x7fffffff;
+
 __device__ __forceinline__ void key_max(float& bv, int& bi, float ov, int oi) {
-    if (oi != kNone && (bi == kNone || ov > bv || (ov == bv && oi < bi))) { bv = ov; bi = oi; }
+    const bool take = (ov > bv) | ((ov == bv) & (oi < bi));  // no short circuit: selects, not branches
+    bv = take ? ov : bv;
+    bi = take ? oi : bi;
 }
 
 template <int CTRL>
@@ -135,12 +138,12 @@ moe_route_kernel(const float* __restrict__ logits, const float* __restrict__ sha
         float my_p = 0.0f, wsum = 0.0f;
         for (int k = 0; k < top_k; ++k) {
             float best = -INFINITY;
-            int bi = kNone;
+            int bi = kNoIndex;
 #pragma unroll
             for (int m = 0; m < MPL; ++m) {
                 const int i = lane + 64 * m;
                 const bool free = i < E && !((taken >> m) & 1u);
-                if (free && (bi == kNone || v[m] > best)) { best = v[m]; bi = i; }  // i rises: ties keep the lower
+                key_max(best, bi, free ? v[m] : -INFINITY, free ? i : kNoIndex);
             }
             key_step<0xB1>(best, bi);
             key_step<0x4E>(best, bi);
