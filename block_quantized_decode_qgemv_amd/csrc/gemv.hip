@@ -9,31 +9,27 @@
 //
 // Memory layout (see qgemv.h): rows are interleaved in groups of 16; in each
 // group, 16-byte unit u of every row is contiguous.  This is the low-bit
-// README page's row repack for dot-product lanes, sized to a gfx950
-// quarter-wave: 16 lanes own the 16 rows of a group, so one quarter-wave load
-// reads 256 contiguous bytes and every activation value read from LDS is a
-// broadcast to all 16 rows.
+// README page's row repack for dot-product lanes, sized to a gfx950 DPP row:
+// 16 lanes own the 16 rows of a group, so one quarter-wave load reads 256
+// contiguous bytes and the 16 lanes that share x columns can exchange x.
 //
-// Kernel shape (batch 1 is HBM-bound; nothing here is a matrix-core
-// contraction):
-//   * one workgroup per 16-row group; its W waves hold P = 4W quarter-waves,
-//     and quarter p owns code units [p*KCS, (p+1)*KCS) of every slice of K
-//     (one slice when x fits the LDS budget);
-//   * each lane first requests its KCS code units and its meta bytes, then x
-//     is staged in LDS together with per-group column sums X (so the offset
-//     terms of Q4_0/Q4_1/K-quants/low-bit codes cost one multiply per group,
-//     not per weight);
-//   * codes are decoded in registers: nibbles, 2-bit fields and bits are
-//     masked into bytes and converted two at a time as OCP e4m3 values (a
-//     byte 0..15 is exactly n * 2^-9 there), and the 2^9 is folded into the
-//     scale; fp32 FMAs accumulate -- the Flash-MoE page's fma(nibble,
-//     scale*x, bias*x) rearrangement ("FMA 优化的反量化内核") with the bias term
-//     hoisted over the shared x as bias * sum(x);
-//   * K-quant scales are applied once per 256-weight super-block: the lane
-//     sums s_j * P_j and t_j * X_j over its 8 sub-blocks and multiplies by d
-//     and dmin once;
-//   * the P partial sums of each row are combined through LDS in a fixed
-//     order: results are deterministic.
+// Kernels (batch <= 8 is not a matrix-core contraction; everything is fp32
+// VALU work):
+//   * gemv_dpp_kernel (GemvDpp, gemv_core.h) -- batches up to 64 x floats per
+//     lane (Q8_0/Q4_x <= 8, Q2_K/tern/bin <= 4): one workgroup per 16-row
+//     group, W waves of four 16-lane parts; each part's x columns live in the
+//     lanes' registers and every multiply-add reads its x operand from the
+//     owning lane with a DPP broadcast, so x never goes through LDS;
+//   * gemv_kernel (Gemv) -- the larger low-bit batches: the same grid with x
+//     and its column sums staged in LDS per K slice;
+//   * both decode codes in registers (masks put one code per byte and
+//     v_cvt_pk_f32_fp8 turns two bytes into exact floats n * 2^-9, the 2^9
+//     folded into the scale) and accumulate in fp32: the Flash-MoE page's
+//     fma(nibble, scale*x, bias*x) rearrangement ("FMA 优化的反量化内核") with
+//     the bias term hoisted over the shared x as bias * sum(x); K-quant scales
+//     are applied once per super-block;
+//   * the parts of a row are combined in a fixed order, so results repeat
+//     bit for bit.
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
