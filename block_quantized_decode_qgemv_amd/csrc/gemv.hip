@@ -13,16 +13,15 @@
 // 16 lanes own the 16 rows of a group, so one quarter-wave load reads 256
 // contiguous bytes and the 16 lanes that share x columns can exchange x.
 //
-// Kernels (batch <= 8 is not a matrix-core contraction; everything is fp32
-// VALU work):
-//   * gemv_dpp_kernel (GemvDpp, gemv_core.h) -- batches up to 64 x floats per
-//     lane (Q8_0/Q4_x <= 8, Q2_K/tern/bin <= 4): one workgroup per 16-row
-//     group, W waves of four 16-lane parts; each part's x columns live in the
-//     lanes' registers and every multiply-add reads its x operand from the
-//     owning lane with a DPP broadcast, so x never goes through LDS;
-//   * gemv_kernel (Gemv) -- the larger low-bit batches: the same grid with x
-//     and its column sums staged in LDS per K slice;
-//   * both decode codes in registers (masks put one code per byte and
+// Kernel (batch <= 8 is not a matrix-core contraction; everything is fp32
+// VALU work): gemv_dpp_kernel (GemvDpp, gemv_core.h), one workgroup per
+// 16-row group, W waves of four 16-lane parts of KCS code units each.  Each
+// part's x columns live in the lanes' registers and every multiply-add reads
+// its x operand from the owning lane with a DPP broadcast, so x never goes
+// through LDS.  Fewer units per part at the larger batches keep x within 32
+// registers per lane; the waves per workgroup follow the row length and how
+// many workgroups a compute unit holds at that register count.
+//   * codes are decoded in registers (masks put one code per byte and
 //     v_cvt_pk_f32_fp8 turns two bytes into exact floats n * 2^-9, the 2^9
 //     folded into the scale) and accumulate in fp32: the Flash-MoE page's
 //     fma(nibble, scale*x, bias*x) rearrangement ("FMA 优化的反量化内核") with
@@ -32,6 +31,7 @@
 //     bit for bit.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cstdint>
 
 #include "gemv_core.h"
@@ -41,19 +41,6 @@ namespace qg {
 namespace {
 
 using namespace core;
-
-template <int F, int B, int W, int KCS>
-__global__ void __launch_bounds__(W * 64)
-gemv_kernel(const uint8_t* __restrict__ codes, const uint8_t* __restrict__ meta,
-            const float* __restrict__ x, float* __restrict__ y, int N, int K) {
-    const int g = blockIdx.x;
-    Gemv<F, B, W, KCS>::run(
-        codes, meta, N, K, g, [&](int b) { return x + (size_t)b * K; }, B,
-        [&](auto sums, int n_g, int tid) {
-            for (int t = tid; t < kRowGroup * B; t += W * 64)
-                if (t / B < n_g) y[(size_t)(t % B) * N + g * kRowGroup + t / B] = sums(t);
-        });
-}
 
 template <int F, int B, int W, int KCS>
 __global__ void __launch_bounds__(W * 64)
@@ -139,57 +126,92 @@ dequant_kernel(const uint8_t* __restrict__ codes, const uint8_t* __restrict__ me
 
 // ---------------------------------------------------------------- launchers
 
-template <int F, int B, int W, int KCS>
-hipError_t launch_gemv_cfg(const uint8_t* codes, const uint8_t* meta, const float* x, float* y,
-                           int N, int K, hipStream_t st) {
-    static_assert(gemv_lds_bytes<F, B, W, KCS>() <= (size_t)kLdsBudget, "LDS budget");
-    const int grid = (N + kRowGroup - 1) / kRowGroup;
-    constexpr size_t lds = gemv_lds_bytes<F, B, W, KCS>();
-    hipLaunchKernelGGL((gemv_kernel<F, B, W, KCS>), dim3(grid), dim3(W * 64), lds, st, codes, meta, x, y, N, K);
-    return hipGetLastError();
+}  // namespace
+
+int device_cus() {
+    constexpr int kMaxDevices = 64;
+    static std::atomic<int> cache[kMaxDevices];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+        (void)hipGetLastError();
+        return 256;
+    }
+    int c = cache[dev].load(std::memory_order_relaxed);
+    if (c == 0) {
+        if (hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || c <= 0) {
+            (void)hipGetLastError();
+            c = 256;
+        }
+        cache[dev].store(c, std::memory_order_relaxed);
+    }
+    return c;
 }
 
-template <int F, int B, int KCS, int W>
-hipError_t launch_gemv_w(const uint8_t* codes, const uint8_t* meta, const float* x, float* y,
-                         int N, int K, hipStream_t st) {
-    if constexpr (gemv_lds_bytes<F, B, W, KCS>() <= (size_t)kLdsBudget) {
-        return launch_gemv_cfg<F, B, W, KCS>(codes, meta, x, y, N, K, st);
-    } else {
-        return hipErrorInvalidConfiguration;  // never chosen by pick_waves
-    }
-}
+namespace {
 
 template <int F, int B, int W>
 hipError_t launch_gemv_dpp_w(const uint8_t* codes, const uint8_t* meta, const float* x, float* y,
                              int N, int K, hipStream_t st) {
-    constexpr int KCS = dpp_lane_units<F>();
+    constexpr int KCS = dpp_lane_units<F, B>();
     const int grid = (N + kRowGroup - 1) / kRowGroup;
     hipLaunchKernelGGL((gemv_dpp_kernel<F, B, W, KCS>), dim3(grid), dim3(W * 64), 0, st, codes, meta, x, y, N, K);
     return hipGetLastError();
 }
 
+// Workgroups of gemv_dpp_kernel<F, B, W> that one compute unit holds at once
+// (registers decide it); queried once per kernel.
+template <int F, int B, int W>
+int dpp_resident() {
+    static const int n = [] {
+        int b = 0;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&b, gemv_dpp_kernel<F, B, W, dpp_lane_units<F, B>()>,
+                                                         W * 64, 0) != hipSuccess) {
+            (void)hipGetLastError();
+            b = 1;
+        }
+        return b < 1 ? 1 : b;
+    }();
+    return n;
+}
+
+// Waves per workgroup: start from the fewest that cover a row in one slice
+// (pick_waves_dpp), then halve while too few workgroups fit on a compute unit:
+// one when the grid has at most one workgroup per compute unit, else two, so
+// that a workgroup's reduction and tail overlap another's streaming.
+template <int F, int B>
+int choose_waves_dpp(int N, int K) {
+    constexpr int MW = dpp_max_waves<F, B>();
+    const int groups = (N + kRowGroup - 1) / kRowGroup;
+    const int need = groups > device_cus() ? 2 : 1;
+    int w = pick_waves_dpp<F, dpp_lane_units<F, B>()>(K, MW);
+    for (; w > 1; w /= 2) {
+        int res = 1;
+        switch (w) {
+            case 2: res = dpp_resident<F, B, 2>(); break;
+            case 4: res = dpp_resident<F, B, 4>(); break;
+            case 8: res = dpp_resident<F, B, 8>(); break;
+            default:
+                if constexpr (MW == 16) res = dpp_resident<F, B, 16>();
+                break;
+        }
+        if (res >= need) break;
+    }
+    return w;
+}
+
 template <int F, int B>
 hipError_t launch_gemv_b(const uint8_t* codes, const uint8_t* meta, const float* x, float* y,
                          int N, int K, hipStream_t st) {
-    if constexpr (B <= dpp_max_batch<F>()) {
-        // x in registers, read across lanes by DPP (no LDS staging)
-        constexpr int MW = dpp_max_waves<F, B>();
-        switch (pick_waves_dpp<F, dpp_lane_units<F>()>(K, MW)) {
-            case 1: return launch_gemv_dpp_w<F, B, 1>(codes, meta, x, y, N, K, st);
-            case 2: return launch_gemv_dpp_w<F, B, 2>(codes, meta, x, y, N, K, st);
-            case 4: return launch_gemv_dpp_w<F, B, 4>(codes, meta, x, y, N, K, st);
-            case 8: return launch_gemv_dpp_w<F, B, 8>(codes, meta, x, y, N, K, st);
-            default:
-                if constexpr (MW == 16) return launch_gemv_dpp_w<F, B, 16>(codes, meta, x, y, N, K, st);
-                return hipErrorInvalidConfiguration;  // never chosen
-        }
-    }
-    constexpr int KCS = lane_units<F>();
-    switch (pick_waves<F, B, KCS>(K)) {
-        case 1: return launch_gemv_w<F, B, KCS, 1>(codes, meta, x, y, N, K, st);
-        case 2: return launch_gemv_w<F, B, KCS, 2>(codes, meta, x, y, N, K, st);
-        case 4: return launch_gemv_w<F, B, KCS, 4>(codes, meta, x, y, N, K, st);
-        default: return launch_gemv_w<F, B, KCS, 8>(codes, meta, x, y, N, K, st);
+    static_assert(B <= dpp_max_batch<F>(), "every batch runs the register-x kernel");
+    constexpr int MW = dpp_max_waves<F, B>();
+    switch (choose_waves_dpp<F, B>(N, K)) {
+        case 1: return launch_gemv_dpp_w<F, B, 1>(codes, meta, x, y, N, K, st);
+        case 2: return launch_gemv_dpp_w<F, B, 2>(codes, meta, x, y, N, K, st);
+        case 4: return launch_gemv_dpp_w<F, B, 4>(codes, meta, x, y, N, K, st);
+        case 8: return launch_gemv_dpp_w<F, B, 8>(codes, meta, x, y, N, K, st);
+        default:
+            if constexpr (MW == 16) return launch_gemv_dpp_w<F, B, 16>(codes, meta, x, y, N, K, st);
+            return hipErrorInvalidConfiguration;  // never chosen
     }
 }
 

@@ -1,6 +1,6 @@
 // Row-group GEMV core shared by the dense GEMV (gemv.hip) and the MoE expert
 // kernels (moe.hip): format traits, code decoders, interleaved addressing and
-// the Gemv<F, B, W, KCS> device routine that computes one 16-row group.
+// the GemvDpp<F, B, W, KCS> device routine that computes one 16-row group.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -13,7 +13,6 @@
 namespace qg {
 namespace core {
 
-constexpr int kLdsBudget = 64 * 1024;  // bytes of x + column sums per workgroup
 constexpr int kRowGroup = 16;          // rows per interleave group (layout constant)
 
 // ------------------------------------------------------------------ traits
@@ -177,9 +176,9 @@ __device__ __forceinline__ V ld_weights(const uint8_t* p) { return NtLoad<V>::ld
 // the row's last meta byte (bytes past it belong to no code unit in range).
 template <int NB>
 __device__ __forceinline__ void load_meta(const uint8_t* gm, int n_g, int r, int o0, int row_meta,
-                                          uint32_t (&wd)[NB / 4]) {
+                                          uint32_t (&wd)[(NB + 3) / 4]) {
     const int full = row_meta >> 4, rem = row_meta & 15;
-    constexpr int W = NB >= 16 ? 4 : NB / 4;  // dwords per part
+    constexpr int W = NB >= 16 ? 4 : (NB + 3) / 4;  // dwords per part
 #pragma unroll
     for (int h = 0; h < (NB + 15) / 16; ++h) {
         const int o = o0 + 16 * h;
@@ -192,8 +191,10 @@ __device__ __forceinline__ void load_meta(const uint8_t* gm, int n_g, int r, int
             } else if constexpr (W == 2) {
                 const uint2 v = *(const uint2*)p;
                 wd[0] = v.x; wd[1] = v.y;
-            } else {
+            } else if constexpr (NB == 4) {
                 wd[0] = *(const uint32_t*)p;
+            } else {
+                wd[0] = *(const uint16_t*)p;  // NB == 2
             }
         } else {
             const uint8_t* p = gm + (size_t)full * n_g * 16 + (size_t)r * rem;
@@ -201,7 +202,7 @@ __device__ __forceinline__ void load_meta(const uint8_t* gm, int n_g, int r, int
             for (int k = 0; k < W; ++k) {
                 uint32_t lo = 0, hi = 0;
                 if (u == full && i0 + 4 * k < rem) lo = *(const uint16_t*)(p + i0 + 4 * k);
-                if (u == full && i0 + 4 * k + 2 < rem) hi = *(const uint16_t*)(p + i0 + 4 * k + 2);
+                if (NB > 2 && u == full && i0 + 4 * k + 2 < rem) hi = *(const uint16_t*)(p + i0 + 4 * k + 2);
                 wd[W * h + k] = lo | (hi << 16);
             }
         }
@@ -300,249 +301,11 @@ template <> struct Apply<QG_BIN> {
     }
 };
 
-// ------------------------------------------------------------ GEMV kernel
-//
-// Template: format F, batch B, waves W, code units per lane per slice KCS.
-// Grid: one workgroup per 16-row group.  Dynamic LDS: x slice [B][SC]
-// (SC = P*KCS*CPC columns), column sums [B][SC/GS], partials [P][16][B].
-
-template <int F, int B, int W, int KCS>
-struct Gemv {
-    using T = Fmt<F>;
-    using U = Unit<F>;
-    using A = Apply<F>;
-    static constexpr int NT = W * 64, P = 4 * W;
-    static constexpr int CPC = T::CPC, CPD = U::CPD, GS = T::GS, SUBS = A::SUBS;
-    static constexpr int SU = P * KCS;                      // code units per slice
-    static constexpr int SC = SU * CPC;                     // columns per slice
-    static constexpr int NSUM = GS ? SC / (GS ? GS : 1) : 1;  // column sums per slice row
-    static constexpr int MB = KCS * T::MBU;                 // meta bytes per lane part
-    static constexpr int DPS = 4 / SUBS;                    // code dwords per sub-group
-    static constexpr int X0 = 4;                            // x float4 per thread requested first
-    static_assert(GS == 0 || GS == CPC / SUBS, "one column sum per sub-group");
-    static_assert((4 * NT) % (GS ? GS : 4) == 0, "a staging round covers whole sum groups");
-
-    // xr[k0 + c] of an activation row xr, c = 4*(tid + NT*i) (float4 per thread)
-    __device__ static float4 ld_x(const float* __restrict__ xr, int k0, int cols, int c) {
-        return c < cols ? *(const float4*)(xr + k0 + c) : make_float4(0.f, 0.f, 0.f, 0.f);
-    }
-    // stage one float4 of row b at column c into LDS and, when it completes a
-    // group of GS columns (a DPP sum over the GS/4 threads that hold it), the
-    // group's column sum; every thread calls this the same number of times
-    __device__ static void put_x(float* xs, float* xsum, int tid, int cols, int b, int c, float4 v) {
-        if (c < cols) *(float4*)(xs + b * SC + c) = v;
-        if constexpr (GS > 0) {
-            const float s = group_sum<GS / 4>((v.x + v.y) + (v.z + v.w));
-            if (c < cols && (tid % (GS / 4)) == GS / 4 - 1) xsum[b * NSUM + c / GS] = s;
-        }
-    }
-
-    // Decode this lane's KCS units and fold them into acc; units i >= nvalid
-    // lie past the end of K and contribute nothing.
-    __device__ static void compute(const uint4 (&q)[KCS], const uint32_t* wd, const float* xs, const float* xsum,
-                                   int lc0, int nvalid, float (&acc)[B]) {
-        KqState st[B];
-#pragma unroll
-        for (int i = 0; i < KCS; ++i) {
-            const bool ok = i < nvalid;
-            const uint32_t dw[4] = {q[i].x, q[i].y, q[i].z, q[i].w};
-            const int xo = ok ? (lc0 + i) * CPC : 0;  // units past K read staged x harmlessly
-#pragma unroll
-            for (int s = 0; s < SUBS; ++s) {
-                float ps[B];
-#pragma unroll
-                for (int b = 0; b < B; ++b) ps[b] = 0.0f;
-#pragma unroll
-                for (int d = s * DPS; d < (s + 1) * DPS; ++d) {
-                    float w[CPD];
-                    U::decode(dw[d], w);
-#pragma unroll
-                    for (int b = 0; b < B; ++b) {
-                        const float* xb = xs + b * SC + xo + d * CPD;
-#pragma unroll
-                        for (int k = 0; k < CPD; k += 4) {
-                            const float4 xx = *(const float4*)(xb + k);
-                            ps[b] = fmaf(w[k], xx.x, ps[b]);
-                            ps[b] = fmaf(w[k + 1], xx.y, ps[b]);
-                            ps[b] = fmaf(w[k + 2], xx.z, ps[b]);
-                            ps[b] = fmaf(w[k + 3], xx.w, ps[b]);
-                        }
-                    }
-                    // wide decodes at B > 1: one code dword live at a time
-                    if constexpr (CPD * B >= 16) __builtin_amdgcn_sched_barrier(0);
-                }
-#pragma unroll
-                for (int b = 0; b < B; ++b) {
-                    const float X = GS > 0 ? xsum[b * NSUM + (ok ? (lc0 + i) * SUBS + s : 0)] : 0.0f;
-                    A::unit(wd, i, s, ps[b], X, st[b], acc[b], ok);
-                }
-            }
-            // keep one unit's decode live at a time (bounds register use)
-            __builtin_amdgcn_sched_barrier(0);
-        }
-    }
-
-    // One 16-row group g of a packed [N][K] matrix against nb <= B activation
-    // rows; xrow(b) gives row b (K floats, 16-byte aligned).  After the parts
-    // are combined, every thread calls epi(sum, n_g, tid), where sum(t) returns
-    // the row sum for t = rw * B + b (rows rw < n_g, batch rows b < nb valid)
-    // and tid is the thread's index in the workgroup.
-    template <class XRow, class Epi>
-    __device__ static void run(const uint8_t* __restrict__ codes, const uint8_t* __restrict__ meta,
-                               int N, int K, int g, XRow xrow, int nb, Epi epi) {
-        extern __shared__ float lds[];
-        float* xs = lds;                    // [B][SC]
-        float* xsum = xs + B * SC;          // [B][NSUM]
-        float* part = xsum + B * NSUM;      // [P][16][B]; reused for the sums
-
-        const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-        const int r = lane & 15, p = wave * 4 + (lane >> 4);
-        const int n_g = min(kRowGroup, N - g * kRowGroup);
-        const int rr = min(r, n_g - 1);
-        const int nb_blocks = K / T::BLOCK;
-        const int row_codes = nb_blocks * T::CB, row_meta = nb_blocks * T::MB;
-        const int nch = row_codes >> 4;
-        const bool meta_whole = (row_meta & 15) == 0;  // no short last meta unit
-        // this lane's row: unit c at gcr + c*ustride, meta unit u at gmr + u*ustride
-        const int ustride = n_g * 16;
-        const uint8_t* gcr = codes + (size_t)g * kRowGroup * row_codes + rr * 16;
-        const uint8_t* gm = meta + (size_t)g * kRowGroup * row_meta;
-        const uint8_t* gmr = gm + rr * 16;
-        const float* x0 = xrow(0);
-
-        float acc[B];
-#pragma unroll
-        for (int b = 0; b < B; ++b) acc[b] = 0.0f;
-
-        for (int c_slice = 0; c_slice < nch; c_slice += SU) {
-            const int k0 = c_slice * CPC;
-            const int cols = min(SC, K - k0);
-            if (c_slice) __syncthreads();  // the previous slice's x is consumed
-
-            // (1) the first X0 float4 of x row 0 go out before the code loads,
-            // so waiting for them does not wait for the codes
-            float4 xv[X0];
-#pragma unroll
-            for (int i = 0; i < X0; ++i) xv[i] = ld_x(x0, k0, cols, 4 * (tid + NT * i));
-
-            // (2) this lane's meta bytes and code units
-            const int c0 = c_slice + p * KCS;
-            const int nvalid = nch - c0;  // units of the part inside K (may be <= 0)
-            uint4 q[KCS];
-            uint32_t wd[MB / 4];
-            // meta first: the scale path reads it from the first unit on, and
-            // loads complete in issue order
-            const int m0 = min(c0, (nch - 1) / KCS * KCS) * T::MBU;
-            if (meta_whole) {
-                // whole 16-byte units: one vector load per unit (or half unit)
-#pragma unroll
-                for (int h = 0; h < (MB + 15) / 16; ++h) {
-                    const int o = m0 + 16 * h;
-                    const uint8_t* pm = gmr + (o >> 4) * ustride + (o & 15);
-                    if constexpr (MB >= 16) {
-                        const uint4 v = ld_weights<uint4>(pm);
-                        wd[4 * h] = v.x; wd[4 * h + 1] = v.y; wd[4 * h + 2] = v.z; wd[4 * h + 3] = v.w;
-                    } else if constexpr (MB == 8) {
-                        const uint2 v = ld_weights<uint2>(pm);
-                        wd[0] = v.x; wd[1] = v.y;
-                    } else {
-                        wd[0] = ld_weights<uint32_t>(pm);
-                    }
-                }
-            } else {
-                load_meta<MB>(gm, n_g, rr, m0, row_meta, wd);
-            }
-            // a unit past the end of K reads the row's last unit instead (its
-            // contribution is dropped), so every load is unconditional
-#pragma unroll
-            for (int i = 0; i < KCS; ++i) q[i] = ld_weights<uint4>(gcr + min(c0 + i, nch - 1) * ustride);
-
-            // (3) x to LDS with the column sums
-            const int rounds = (cols + 4 * NT - 1) / (4 * NT);  // float4 rounds per batch row
-#pragma unroll
-            for (int i = 0; i < X0; ++i)
-                if (i < rounds) put_x(xs, xsum, tid, cols, 0, 4 * (tid + NT * i), xv[i]);
-            for (int i = X0; i < rounds; ++i) {
-                const int c = 4 * (tid + NT * i);
-                put_x(xs, xsum, tid, cols, 0, c, ld_x(x0, k0, cols, c));
-            }
-#pragma unroll
-            for (int b = 1; b < B; ++b) {
-                if (b < nb) {
-                    const float* xb = xrow(b);
-                    for (int i0 = 0; i0 < rounds; i0 += X0) {
-                        float4 v[X0];
-#pragma unroll
-                        for (int i = 0; i < X0; ++i) v[i] = ld_x(xb, k0, cols, 4 * (tid + NT * (i0 + i)));
-#pragma unroll
-                        for (int i = 0; i < X0; ++i)
-                            if (i0 + i < rounds) put_x(xs, xsum, tid, cols, b, 4 * (tid + NT * (i0 + i)), v[i]);
-                    }
-                }
-            }
-            __syncthreads();
-
-            // (4) decode once, multiply for every batch row
-            compute(q, wd, xs, xsum, p * KCS, nvalid, acc);
-        }
-
-        // (5) combine the P parts of each row in a fixed order
-#pragma unroll
-        for (int b = 0; b < B; ++b) part[(p * kRowGroup + r) * B + b] = acc[b];
-        __syncthreads();
-        constexpr int PER = (kRowGroup * B + NT - 1) / NT;  // sums per thread
-        float sum[PER];
-#pragma unroll
-        for (int j = 0; j < PER; ++j) {
-            const int t = tid + NT * j;
-            sum[j] = 0.0f;
-            if (t < kRowGroup * B) {
-#pragma unroll
-                for (int pp = 0; pp < P; ++pp) sum[j] += part[(pp * kRowGroup + t / B) * B + t % B];
-            }
-        }
-        __syncthreads();
-#pragma unroll
-        for (int j = 0; j < PER; ++j)
-            if (tid + NT * j < kRowGroup * B) part[tid + NT * j] = sum[j];  // sums[rw * B + b]
-        __syncthreads();
-        epi([&](int t) { return part[t]; }, n_g, tid);
-    }
-};
-
-template <int F, int B, int W, int KCS>
-constexpr size_t gemv_lds_bytes() {
-    constexpr int P = 4 * W, SC = P * KCS * Fmt<F>::CPC, GS = Fmt<F>::GS;
-    return (size_t)B * SC * 4 + (size_t)B * (GS ? SC / (GS ? GS : 1) : 1) * 4 + (size_t)P * kRowGroup * B * 4;
-}
-
-// Code units per lane part: 256 weights for the wide-unit low-bit formats,
-// 8 units (128 or 256 weights) for the others; a K-quant part covers whole
-// super-blocks.
-template <int F> constexpr int lane_units() {
-    return F == QG_BIN ? 2 : (F == QG_Q2_K || F == QG_TERN) ? 4 : 8;
-}
-
-// Waves per workgroup: the fewest (from 1, 2, 4, 8) whose P = 4W parts cover K
-// in one slice, then fewer while the slice's LDS does not fit the budget.
-template <int F, int B, int KCS>
-int pick_waves(int K) {
-    const int nch = K / Fmt<F>::BLOCK * Fmt<F>::CB / 16;
-    int w = 1;
-    while (w < 8 && 4 * w * KCS < nch) w *= 2;
-    auto bytes = [](int ww) {
-        const int P = 4 * ww, SC = P * KCS * Fmt<F>::CPC, GS = Fmt<F>::GS;
-        return (size_t)B * SC * 4 + (size_t)B * (GS ? SC / (GS ? GS : 1) : 1) * 4 + (size_t)P * kRowGroup * B * 4;
-    };
-    while (w > 1 && bytes(w) > (size_t)kLdsBudget) w /= 2;
-    return w;
-}
-
-
 // --------------------------------------------------- register-x GEMV (DPP)
 //
-// Same grid and epilogue contract as Gemv, without LDS for x.  The 16 lanes
-// of a DPP row are the 16 rows of the group working on one part of KCS code
+// Template: format F, batch B, waves W, code units per lane part KCS.  Grid:
+// one workgroup per 16-row group; the epilogue functor receives the group's
+// 16*B sums (row-major by row, then batch).  The 16 lanes of a DPP row are the 16 rows of the group working on one part of KCS code
 // units (NXC = KCS*CPC columns from column k0); lane r keeps x columns
 // k0 + 64m + 4r .. +3 (m < NXC/64) of every batch row in registers, and each
 // multiply-add reads its x operand from the lane holding it (row_newbcast).
@@ -650,15 +413,35 @@ __device__ __forceinline__ void fma_cols(float (&a)[4], const float4 (&xv)[NX4],
 
 template <int F> constexpr bool is_kquant() { return F == QG_Q4_K || F == QG_Q2_K; }
 
-// Code units per lane part in the register-x kernel: NXC = 64 columns for
-// Q8_0 and 128 or 256 for the others; a K-quant part stays inside one
-// super-block.
-template <int F> constexpr int dpp_lane_units() {
-    return F == QG_BIN ? 2 : 4;
+// Code units per lane part in the register-x kernel at batch B: the largest
+// of 4 (2 for bin), 2, 1 whose part (KCS*CPC columns) still covers whole 64-column spans
+// and whole blocks (inside one super-block for K-quants) and keeps the x
+// registers per lane
+// (B * KCS * CPC / 16) within 32; else the smallest such part.  Fewer x
+// registers leave room for more waves per SIMD at the larger batches.
+template <int F> constexpr bool dpp_units_ok(int kcs) {
+    using T = Fmt<F>;
+    return (kcs * T::CPC) % 64 == 0 &&
+           (is_kquant<F>() ? (T::BLOCK / T::CPC) % kcs == 0      // inside one super-block
+                           : (kcs * T::CPC) % T::BLOCK == 0) &&  // whole blocks (aligned meta)
+           kcs * T::MBU >= 2;                                    // at least one fp16 of meta
 }
-// Largest batch for the register-x kernel: x registers per lane B*NXC/16 <= 64.
+template <int F, int B> constexpr int dpp_lane_units() {
+    int best = 0;
+    // 1-bit parts of 4 units (512 weights per lane) decode into too many
+    // registers even at batch 1
+    for (int kcs = F == QG_BIN ? 2 : 4; kcs >= 1; kcs /= 2) {
+        if (!dpp_units_ok<F>(kcs)) continue;
+        if (B * kcs * Fmt<F>::CPC / 16 <= 32) return kcs;
+        best = kcs;
+    }
+    return best;
+}
+// Largest batch for the register-x kernel: x registers per lane <= 64 with the
+// narrowest part.
 template <int F> constexpr int dpp_max_batch() {
-    return 64 / (dpp_lane_units<F>() * Fmt<F>::CPC / 16);
+    constexpr int nx = dpp_lane_units<F, 64>() * Fmt<F>::CPC / 16;  // x floats per batch row
+    return 64 / nx < 8 ? 64 / nx : 8;
 }
 
 template <int F, int B, int W, int KCS>
@@ -758,8 +541,10 @@ struct GemvDpp {
                     } else if constexpr (MB == 8) {
                         const uint2 v = ld_weights<uint2>(pm);
                         wd[0] = v.x; wd[1] = v.y;
-                    } else {
+                    } else if constexpr (MB == 4) {
                         wd[0] = ld_weights<uint32_t>(pm);
+                    } else {
+                        wd[0] = *(const uint16_t*)pm;  // MB == 2
                     }
                 } else {
                     load_meta<MB>(gm, n_g, rr, m0, row_meta, wd);
@@ -852,7 +637,7 @@ struct GemvDpp {
 // 128-per-wave limit of a 1024-thread workgroup.
 template <int F, int B>
 constexpr int dpp_max_waves() {
-    return B * (dpp_lane_units<F>() * Fmt<F>::CPC / 16) > 40 ? 8 : 16;
+    return B * (dpp_lane_units<F, B>() * Fmt<F>::CPC / 16) > 40 ? 8 : 16;
 }
 
 // Waves per workgroup of the register-x kernel: the fewest (powers of two up

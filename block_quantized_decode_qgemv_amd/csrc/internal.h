@@ -26,4 +26,7 @@ void clear_error();
 int check_matrix(int fmt, int64_t N, int64_t K);
 bool aligned(const void* p, size_t a);
 
+// Compute units of the current device (cached per device; 256 if the query fails).
+int device_cus();
+
 }  // namespace qg

@@ -346,7 +346,7 @@ hipError_t launch_moe(const uint8_t* wgu, const uint8_t* wdn, int E, int H, int 
                       const float* residual, const float* logits, const float* slogit, int T, unsigned flags,
                       float* out, uint8_t* ws, hipStream_t st) {
     // register-x GEMVs (items carry at most 2 tokens)
-    constexpr int KCS = dpp_lane_units<F>();
+    constexpr int KCS = dpp_lane_units<F, 2>();
     static_assert(dpp_max_batch<F>() >= 2, "two tokens per item");
     const MoeLayout L(T, H, I, top_k);
     int* items = reinterpret_cast<int*>(ws + L.items);
