@@ -102,8 +102,7 @@ def test_gemv_widest_workgroup(fmt, b):
     """K = 16384 gives the register-x kernel its widest workgroup (16 waves,
     one per SIMD slot at low occupancy, where back-to-back issue of a wave's
     instructions is most likely) at small batches, and 8 waves with several
-    K slices at the larger ones (and the LDS kernel for low-bit batch 8);
-    33 rows leave a one-row last group."""
+    K slices at the larger ones; 33 rows leave a one-row last group."""
     n, k = 33, 16384
     blk = make_blocks(fmt, n, k, seed=8, tid=b)
     x = workloads.normal((b, k), 8, 100 + b)
@@ -114,8 +113,8 @@ def test_gemv_widest_workgroup(fmt, b):
 @pytest.mark.parametrize("fmt", OF.FORMATS)
 @pytest.mark.parametrize("b", [3, 5, 6, 7])
 def test_gemv_odd_batches(fmt, b):
-    """Every batch size has its own kernel instance (register-x up to 8 for Q8_0
-    and Q4_x, up to 4 for the low-bit formats, LDS beyond)."""
+    """Every batch size has its own kernel instance (with fewer code units per
+    lane part as the batch grows)."""
     n, k = 45, 2048
     blk = make_blocks(fmt, n, k, seed=9, tid=b)
     x = workloads.normal((b, k), 9, 300 + b)
@@ -176,9 +175,37 @@ def test_single_q4k_gemv_seed0():
     assert_parity(y, OF.dequant("q4_k", blk), x, "q4_k 1024x1024 seed 0")
 
 
-@functools.lru_cache(maxsize=2)
+@functools.lru_cache(maxsize=4)
 def full_weights(n, k):
     return workloads.student_t_weights(n, k, seed=0, tensor_id=n)
+
+
+@functools.lru_cache(maxsize=4)
+def full_low_bit_codes(fmt, n, k):
+    gen = workloads.ternary_codes if fmt == "tern" else workloads.binary_codes
+    return gen(n, k, 11, n), workloads.scale_bits_f16((n, k // 128), 11, n + 1)
+
+
+def sampled_rows(n, salt):
+    return np.unique(np.concatenate([[0, 1, n - 1], np.random.default_rng(salt).choice(n, 253, replace=False)]))
+
+
+def check_sampled_rows(fmt, packed, sub, rows, n, k, x, y):
+    """Rows `rows` of the full device buffer `packed` must equal, byte for byte,
+    the oracle's packing of the blocks `sub` of those rows; their outputs are
+    checked against the oracle."""
+    spec = OF.SPECS[fmt]
+    cpr = (k // spec.block) * spec.code_bytes
+    mpr = (k // spec.block) * spec.meta_bytes
+    cp = OF.codes_plane_size(fmt, n, k)
+    codes_rows = OF.deinterleave_rows(packed[:cp], n, cpr)
+    meta_rows = OF.deinterleave_rows(packed[cp:], n, mpr)
+    sub_packed = OF.pack(fmt, sub)
+    scp = OF.codes_plane_size(fmt, len(rows), k)
+    np.testing.assert_array_equal(codes_rows[rows], OF.deinterleave_rows(sub_packed[:scp], len(rows), cpr))
+    np.testing.assert_array_equal(meta_rows[rows], OF.deinterleave_rows(sub_packed[scp:], len(rows), mpr))
+    assert_parity(y[:, rows], OF.dequant(fmt, sub), x, f"{fmt} {n}x{k} B={x.shape[0]}")
+    assert np.all(np.isfinite(y))
 
 
 @pytest.mark.parametrize("n,k", [(4096, 4096), (14336, 4096)])
@@ -192,20 +219,34 @@ def test_full_size_sampled_rows(fmt, n, k, b):
     packed = qg.qquant(fmt, w)
     x = workloads.normal((b, k), 0, 50 + b)
     y = run_gemv(fmt, packed, x, n, k)
-    rows = np.unique(np.concatenate([[0, 1, n - 1], np.random.default_rng(n + b).choice(n, 253, replace=False)]))
-    sub = OF.quantize(fmt, w[rows])
-    spec = OF.SPECS[fmt]
-    cpr = (k // spec.block) * spec.code_bytes
-    mpr = (k // spec.block) * spec.meta_bytes
-    cp = OF.codes_plane_size(fmt, n, k)
-    codes_rows = OF.deinterleave_rows(packed[:cp], n, cpr)
-    meta_rows = OF.deinterleave_rows(packed[cp:], n, mpr)
-    sub_packed = OF.pack(fmt, sub)
-    scp = OF.codes_plane_size(fmt, len(rows), k)
-    np.testing.assert_array_equal(codes_rows[rows], OF.deinterleave_rows(sub_packed[:scp], len(rows), cpr))
-    np.testing.assert_array_equal(meta_rows[rows], OF.deinterleave_rows(sub_packed[scp:], len(rows), mpr))
-    assert_parity(y[:, rows], OF.dequant(fmt, sub), x, f"{fmt} {n}x{k} B={b}")
-    assert np.all(np.isfinite(y))
+    rows = sampled_rows(n, n + b)
+    check_sampled_rows(fmt, packed, OF.quantize(fmt, w[rows]), rows, n, k, x, y)
+
+
+@pytest.mark.parametrize("n,k", [(12288, 4096), (4096, 12288)])
+@pytest.mark.parametrize("fmt", ["q2_k", "tern", "bin"])
+@pytest.mark.parametrize("b", [1, 4, 8])
+def test_full_size_low_bit_sampled_rows(fmt, n, k, b):
+    """The low-bit formats at the bench's full sizes: Q2_K from the C++
+    quantizer, tern and bin from the C++ packers over seeded codes; sampled
+    rows as in the full-size test.  At batch 8 on 12288 rows the launcher
+    halves the waves per workgroup for occupancy."""
+    x = workloads.normal((b, k), 0, 60 + b)
+    rows = sampled_rows(n, n + 7 * b)
+    if fmt == "q2_k":
+        w = full_weights(n, k)
+        packed = qg.qquant(fmt, w)
+        sub = OF.quantize(fmt, w[rows])
+    else:
+        codes, scales = full_low_bit_codes(fmt, n, k)
+        if fmt == "tern":
+            packed = qg.qpack_tern(codes, scales)
+            sub = OF.tern_from_codes(codes[rows], scales[rows])
+        else:
+            packed = qg.qpack_bin(codes, scales)
+            sub = OF.bin_from_codes(codes[rows], scales[rows])
+    y = run_gemv(fmt, packed, x, n, k)
+    check_sampled_rows(fmt, packed, sub, rows, n, k, x, y)
 
 
 @pytest.mark.parametrize("n,k", [(1024, 4096), (4096, 14336)])
