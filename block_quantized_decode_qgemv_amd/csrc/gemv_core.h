@@ -6,6 +6,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
+#include <type_traits>
 #include <utility>
 
 #include "internal.h"
@@ -501,123 +502,141 @@ struct GemvDpp {
 #pragma unroll
         for (int b = 0; b < B; ++b) acc[b] = 0.0f;
 
-        for (int c_slice = 0; c_slice < nch; c_slice += SU) {
-            const int c0 = c_slice + p * KCS;  // first code unit of this lane's part
-            const int k0 = c0 * CPC;           // its first column
-            const int nvalid = nch - c0;
+        // FULL: a whole 16-row group and whole slices, so no address needs a
+        // clamp and every part is valid (constant strides).  Only the larger
+        // batches take this second copy of the loop: at batch 1 and 2 it
+        // measured slower than the clamped loop alone.
+        auto slices = [&](auto full_tag) {
+            constexpr bool FULL = decltype(full_tag)::value;
+            const uint32_t ust = FULL ? kRowGroup * 16 : (uint32_t)ustride;
+            const uint32_t rof = FULL ? (uint32_t)r * 16 : ro;
+            for (int c_slice = 0; c_slice < nch; c_slice += SU) {
+                const int c0 = c_slice + p * KCS;  // first code unit of this lane's part
+                const int k0 = c0 * CPC;           // its first column
+                const int nvalid = FULL ? KCS : nch - c0;
 
-            // (1) x of the part, four columns per lane per span
-            float4 xv[B][NX4];
-#pragma unroll
-            for (int b = 0; b < B; ++b) {
-                if (b < nb) {
-                    const float* xb = xrow(b);
-#pragma unroll
-                    for (int m = 0; m < NX4; ++m) {
-                        // columns past K read the row's last float4 instead: they
-                        // only meet code units whose contributions are dropped
-                        const uint32_t c = (uint32_t)min(k0 + 64 * m + 4 * r, K - 4);
-                        xv[b][m] = *(const float4*)((const uint8_t*)xb + c * 4u);
-                    }
-                }
-            }
-            // (2) meta, then the code units (clamped into the row; units past
-            // its end are dropped by the scale step)
-            uint32_t wd[is_kquant<F>() ? 4 : (MB + 3) / 4];
-            if constexpr (is_kquant<F>()) {
-                const int sbi = c0 / UPS, uo = c0 % UPS;
-                const uint4 v = ld_weights<uint4>(gm + ((uint32_t)min(sbi, nb_blocks - 1) * ustride + ro));
-                // pairs of the part's first unit moved to the bottom of the field
-                const unsigned __int128 f =
-                    ((unsigned __int128)v.z << 64 | (unsigned __int128)v.y << 32 | v.x) >> (12 * SUBS * uo);
-                wd[0] = (uint32_t)f; wd[1] = (uint32_t)(f >> 32); wd[2] = (uint32_t)(f >> 64); wd[3] = v.w;
-            } else {
-                const int m0 = min(c0, (nch - 1) / KCS * KCS) * T::MBU;
-                if (meta_whole) {
-                    const uint8_t* pm = gm + ((uint32_t)(m0 >> 4) * ustride + ro + (m0 & 15));
-                    if constexpr (MB >= 16) {
-                        const uint4 v = ld_weights<uint4>(pm);
-                        wd[0] = v.x; wd[1] = v.y; wd[2] = v.z; wd[3] = v.w;
-                    } else if constexpr (MB == 8) {
-                        const uint2 v = ld_weights<uint2>(pm);
-                        wd[0] = v.x; wd[1] = v.y;
-                    } else if constexpr (MB == 4) {
-                        wd[0] = ld_weights<uint32_t>(pm);
-                    } else {
-                        wd[0] = *(const uint16_t*)pm;  // MB == 2
-                    }
-                } else {
-                    load_meta<MB>(gm, n_g, rr, m0, row_meta, wd);
-                }
-            }
-            uint4 q[KCS];
-#pragma unroll
-            for (int i = 0; i < KCS; ++i) q[i] = ld_weights<uint4>(gc + ((uint32_t)min(c0 + i, nch - 1) * ustride + ro));
-
-            // (3) column-sum spans of every batch row
-            float gs[B][NX4];
-            if constexpr (GS > 0) {
-#pragma unroll
-                for (int b = 0; b < B; ++b)
-#pragma unroll
-                    for (int m = 0; m < NX4; ++m) {
-                        const float s = (xv[b][m].x + xv[b][m].y) + (xv[b][m].z + xv[b][m].w);
-                        gs[b][m] = GS == 32 ? group_sum<8>(s) : group_sum<16>(s);
-                    }
-            }
-
-            // (4) decode each unit once, multiply-add it for every batch row
-            KqState st[B];
-            static_for<KCS>([&](auto I) {
-                constexpr int i = decltype(I)::value;
-                const bool ok = i < nvalid;
-                const uint32_t dw[4] = {q[i].x, q[i].y, q[i].z, q[i].w};
-                static_for<SUBS>([&](auto S) {
-                    constexpr int s = decltype(S)::value;
-                    float pa[B][4];  // started by the first dword's multiplies
-                    static_for<DPS>([&](auto D) {
-                        constexpr int d = s * DPS + decltype(D)::value;
-                        float w[CPD];
-                        U::decode(dw[d], w);
-#pragma unroll
-                        for (int b = 0; b < B; ++b)
-                            fma_cols<i * CPC + d * CPD, CPD, NX4, decltype(D)::value == 0>(pa[b], xv[b], w);
-                    });
-                    float ps[B];
-#pragma unroll
-                    for (int b = 0; b < B; ++b) ps[b] = (pa[b][0] + pa[b][1]) + (pa[b][2] + pa[b][3]);
-#pragma unroll
-                    for (int b = 0; b < B; ++b) {
-                        float X = 0.0f;
-                        if constexpr (GS > 0) X = col_sum<i * CPC + s * (CPC / SUBS)>(gs[b]);
-                        if constexpr (is_kquant<F>()) {
-                            const uint32_t pr = kq_pair(wd, i * SUBS + s);
-                            st[b].sp = fmaf((float)(pr & 63u), ps[b], st[b].sp);
-                            st[b].tx = fmaf((float)((pr >> 6) & 63u), X, st[b].tx);
-                        } else {
-                            A::unit(wd, i, s, ps[b], X, st[b], acc[b], ok);
+                // (1) x of the part, four columns per lane per span
+                float4 xv[B][NX4];
+    #pragma unroll
+                for (int b = 0; b < B; ++b) {
+                    if (b < nb) {
+                        const float* xb = xrow(b);
+    #pragma unroll
+                        for (int m = 0; m < NX4; ++m) {
+                            // columns past K read the row's last float4 instead: they
+                            // only meet code units whose contributions are dropped
+                            const uint32_t c = (uint32_t)(FULL ? k0 + 64 * m + 4 * r : min(k0 + 64 * m + 4 * r, K - 4));
+                            xv[b][m] = *(const float4*)((const uint8_t*)xb + c * 4u);
                         }
                     }
+                }
+                // (2) meta, then the code units (clamped into the row; units past
+                // its end are dropped by the scale step)
+                uint32_t wd[is_kquant<F>() ? 4 : (MB + 3) / 4];
+                if constexpr (is_kquant<F>()) {
+                    const int sbi = c0 / UPS, uo = c0 % UPS;
+                    const uint4 v = ld_weights<uint4>(gm + ((uint32_t)(FULL ? sbi : min(sbi, nb_blocks - 1)) * ust + rof));
+                    // pairs of the part's first unit moved to the bottom of the field
+                    const unsigned __int128 f =
+                        ((unsigned __int128)v.z << 64 | (unsigned __int128)v.y << 32 | v.x) >> (12 * SUBS * uo);
+                    wd[0] = (uint32_t)f; wd[1] = (uint32_t)(f >> 32); wd[2] = (uint32_t)(f >> 64); wd[3] = v.w;
+                } else {
+                    const int m0 = (FULL ? c0 : min(c0, (nch - 1) / KCS * KCS)) * T::MBU;
+                    if (meta_whole) {
+                        const uint8_t* pm = gm + ((uint32_t)(m0 >> 4) * ust + rof + (m0 & 15));
+                        if constexpr (MB >= 16) {
+                            const uint4 v = ld_weights<uint4>(pm);
+                            wd[0] = v.x; wd[1] = v.y; wd[2] = v.z; wd[3] = v.w;
+                        } else if constexpr (MB == 8) {
+                            const uint2 v = ld_weights<uint2>(pm);
+                            wd[0] = v.x; wd[1] = v.y;
+                        } else if constexpr (MB == 4) {
+                            wd[0] = ld_weights<uint32_t>(pm);
+                        } else {
+                            wd[0] = *(const uint16_t*)pm;  // MB == 2
+                        }
+                    } else {
+                        load_meta<MB>(gm, n_g, rr, m0, row_meta, wd);
+                    }
+                }
+                uint4 q[KCS];
+    #pragma unroll
+                for (int i = 0; i < KCS; ++i) q[i] = ld_weights<uint4>(gc + ((uint32_t)(FULL ? c0 + i : min(c0 + i, nch - 1)) * ust + rof));
+
+                // (3) column-sum spans of every batch row
+                float gs[B][NX4];
+                if constexpr (GS > 0) {
+    #pragma unroll
+                    for (int b = 0; b < B; ++b)
+    #pragma unroll
+                        for (int m = 0; m < NX4; ++m) {
+                            const float s = (xv[b][m].x + xv[b][m].y) + (xv[b][m].z + xv[b][m].w);
+                            gs[b][m] = GS == 32 ? group_sum<8>(s) : group_sum<16>(s);
+                        }
+                }
+
+                // (4) decode each unit once, multiply-add it for every batch row
+                KqState st[B];
+                static_for<KCS>([&](auto I) {
+                    constexpr int i = decltype(I)::value;
+                    const bool ok = i < nvalid;
+                    const uint32_t dw[4] = {q[i].x, q[i].y, q[i].z, q[i].w};
+                    static_for<SUBS>([&](auto S) {
+                        constexpr int s = decltype(S)::value;
+                        float pa[B][4];  // started by the first dword's multiplies
+                        static_for<DPS>([&](auto D) {
+                            constexpr int d = s * DPS + decltype(D)::value;
+                            float w[CPD];
+                            U::decode(dw[d], w);
+    #pragma unroll
+                            for (int b = 0; b < B; ++b)
+                                fma_cols<i * CPC + d * CPD, CPD, NX4, decltype(D)::value == 0>(pa[b], xv[b], w);
+                        });
+                        float ps[B];
+    #pragma unroll
+                        for (int b = 0; b < B; ++b) ps[b] = (pa[b][0] + pa[b][1]) + (pa[b][2] + pa[b][3]);
+    #pragma unroll
+                        for (int b = 0; b < B; ++b) {
+                            float X = 0.0f;
+                            if constexpr (GS > 0) X = col_sum<i * CPC + s * (CPC / SUBS)>(gs[b]);
+                            if constexpr (is_kquant<F>()) {
+                                const uint32_t pr = kq_pair(wd, i * SUBS + s);
+                                st[b].sp = fmaf((float)(pr & 63u), ps[b], st[b].sp);
+                                st[b].tx = fmaf((float)((pr >> 6) & 63u), X, st[b].tx);
+                            } else {
+                                A::unit(wd, i, s, ps[b], X, st[b], acc[b], ok);
+                            }
+                        }
+                    });
+                    __builtin_amdgcn_sched_barrier(0);
                 });
-                __builtin_amdgcn_sched_barrier(0);
-            });
-            if constexpr (is_kquant<F>()) {
-                // a K-quant part lies in one super-block: valid as a whole or not at all
-                const float d = 512.0f * h2f(wd[3] & 0xFFFFu), dmin = h2f(wd[3] >> 16);
-#pragma unroll
-                for (int b = 0; b < B; ++b) {
-                    const float v = fmaf(d, st[b].sp, fmaf(-dmin, st[b].tx, acc[b]));
-                    acc[b] = nvalid > 0 ? v : acc[b];
+                if constexpr (is_kquant<F>()) {
+                    // a K-quant part lies in one super-block: valid as a whole or not at all
+                    const float d = 512.0f * h2f(wd[3] & 0xFFFFu), dmin = h2f(wd[3] >> 16);
+    #pragma unroll
+                    for (int b = 0; b < B; ++b) {
+                        const float v = fmaf(d, st[b].sp, fmaf(-dmin, st[b].tx, acc[b]));
+                        acc[b] = nvalid > 0 ? v : acc[b];
+                    }
                 }
             }
+        };
+        if constexpr (B > 2) {
+            if (n_g == kRowGroup && nch % SU == 0) slices(std::true_type{});
+            else slices(std::false_type{});
+        } else {
+            slices(std::false_type{});
         }
 
         // (5) combine the parts: lanes r, r+16, r+32, r+48 of a wave, then waves
 #pragma unroll
         for (int b = 0; b < B; ++b) {
-            float v = acc[b];
-            v += __shfl_xor(v, 16);
-            v += __shfl_xor(v, 32);
+            // (lanes l and l ^ 32, then l and l ^ 16: VALU lane swaps, no LDS)
+            const auto h = __builtin_amdgcn_permlane32_swap(__float_as_uint(acc[b]), __float_as_uint(acc[b]),
+                                                            false, false);
+            const float v2 = __uint_as_float(h[0]) + __uint_as_float(h[1]);
+            const auto q2 = __builtin_amdgcn_permlane16_swap(__float_as_uint(v2), __float_as_uint(v2), false, false);
+            const float v = __uint_as_float(q2[0]) + __uint_as_float(q2[1]);
             if (lane < 16) red[(wave * kRowGroup + r) * B + b] = v;
         }
         __syncthreads();
