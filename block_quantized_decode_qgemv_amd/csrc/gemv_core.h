@@ -53,7 +53,8 @@ __device__ __forceinline__ void fp8x4(uint32_t v, float& b0, float& b1, float& b
 
 template <int CTRL, int ROW_MASK = 0xF>
 __device__ __forceinline__ float dpp(float v) {
-    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, ROW_MASK, 0xF, false));
+    return __builtin_bit_cast(float,
+                              __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, ROW_MASK, 0xF, false));
 }
 
 // Sum over aligned groups of LPR lanes (LPR in 4..64); the full sum is valid in
@@ -306,14 +307,14 @@ template <> struct Apply<QG_BIN> {
 //
 // Template: format F, batch B, waves W, code units per lane part KCS.  Grid:
 // one workgroup per 16-row group; the epilogue functor receives the group's
-// 16*B sums (row-major by row, then batch).  The 16 lanes of a DPP row are the 16 rows of the group working on one part of KCS code
-// units (NXC = KCS*CPC columns from column k0); lane r keeps x columns
-// k0 + 64m + 4r .. +3 (m < NXC/64) of every batch row in registers, and each
-// multiply-add reads its x operand from the lane holding it (row_newbcast).
-// x is thus read once per wave from the cache and never staged; column sums
-// are DPP sums over the lanes of a sum group.  Part sums are combined with
-// lane shuffles inside a wave and through a small LDS array across waves, in
-// a fixed order.
+// 16*B sums (row-major by row, then batch).  The 16 lanes of a DPP row are
+// the 16 rows of the group working on one part of KCS code units (NXC =
+// KCS*CPC columns from column k0); lane r keeps x columns k0 + 64m + 4r .. +3
+// (m < NXC/64) of every batch row in registers, and each multiply-add reads
+// its x operand from the lane holding it (row_newbcast).  x is thus read once
+// per wave from the cache and never staged; column sums are DPP sums over the
+// lanes of a sum group.  Part sums are combined with lane swaps inside a wave
+// and through a small LDS array across waves, in a fixed order.
 
 template <int... Is, class Fn>
 __device__ __forceinline__ void static_for_impl(std::integer_sequence<int, Is...>, Fn&& fn) {
@@ -415,11 +416,11 @@ __device__ __forceinline__ void fma_cols(float (&a)[4], const float4 (&xv)[NX4],
 template <int F> constexpr bool is_kquant() { return F == QG_Q4_K || F == QG_Q2_K; }
 
 // Code units per lane part in the register-x kernel at batch B: the largest
-// of 4 (2 for bin), 2, 1 whose part (KCS*CPC columns) still covers whole 64-column spans
-// and whole blocks (inside one super-block for K-quants) and keeps the x
-// registers per lane
-// (B * KCS * CPC / 16) within 32; else the smallest such part.  Fewer x
-// registers leave room for more waves per SIMD at the larger batches.
+// of 4 (2 for bin), 2, 1 whose part (KCS*CPC columns) covers whole 64-column
+// spans and whole blocks (inside one super-block for K-quants) and keeps the
+// x registers per lane (B * KCS * CPC / 16) within 32; else the smallest such
+// part.  Fewer x registers leave room for more waves per SIMD at the larger
+// batches.
 template <int F> constexpr bool dpp_units_ok(int kcs) {
     using T = Fmt<F>;
     return (kcs * T::CPC) % 64 == 0 &&
@@ -517,11 +518,11 @@ struct GemvDpp {
 
                 // (1) x of the part, four columns per lane per span
                 float4 xv[B][NX4];
-    #pragma unroll
+#pragma unroll
                 for (int b = 0; b < B; ++b) {
                     if (b < nb) {
                         const float* xb = xrow(b);
-    #pragma unroll
+#pragma unroll
                         for (int m = 0; m < NX4; ++m) {
                             // columns past K read the row's last float4 instead: they
                             // only meet code units whose contributions are dropped
@@ -535,7 +536,8 @@ struct GemvDpp {
                 uint32_t wd[is_kquant<F>() ? 4 : (MB + 3) / 4];
                 if constexpr (is_kquant<F>()) {
                     const int sbi = c0 / UPS, uo = c0 % UPS;
-                    const uint4 v = ld_weights<uint4>(gm + ((uint32_t)(FULL ? sbi : min(sbi, nb_blocks - 1)) * ust + rof));
+                    const uint32_t u = (uint32_t)(FULL ? sbi : min(sbi, nb_blocks - 1));
+                    const uint4 v = ld_weights<uint4>(gm + (u * ust + rof));
                     // pairs of the part's first unit moved to the bottom of the field
                     const unsigned __int128 f =
                         ((unsigned __int128)v.z << 64 | (unsigned __int128)v.y << 32 | v.x) >> (12 * SUBS * uo);
@@ -560,15 +562,18 @@ struct GemvDpp {
                     }
                 }
                 uint4 q[KCS];
-    #pragma unroll
-                for (int i = 0; i < KCS; ++i) q[i] = ld_weights<uint4>(gc + ((uint32_t)(FULL ? c0 + i : min(c0 + i, nch - 1)) * ust + rof));
+#pragma unroll
+                for (int i = 0; i < KCS; ++i) {
+                    const uint32_t u = (uint32_t)(FULL ? c0 + i : min(c0 + i, nch - 1));
+                    q[i] = ld_weights<uint4>(gc + (u * ust + rof));
+                }
 
                 // (3) column-sum spans of every batch row
                 float gs[B][NX4];
                 if constexpr (GS > 0) {
-    #pragma unroll
+#pragma unroll
                     for (int b = 0; b < B; ++b)
-    #pragma unroll
+#pragma unroll
                         for (int m = 0; m < NX4; ++m) {
                             const float s = (xv[b][m].x + xv[b][m].y) + (xv[b][m].z + xv[b][m].w);
                             gs[b][m] = GS == 32 ? group_sum<8>(s) : group_sum<16>(s);
@@ -588,14 +593,14 @@ struct GemvDpp {
                             constexpr int d = s * DPS + decltype(D)::value;
                             float w[CPD];
                             U::decode(dw[d], w);
-    #pragma unroll
+#pragma unroll
                             for (int b = 0; b < B; ++b)
                                 fma_cols<i * CPC + d * CPD, CPD, NX4, decltype(D)::value == 0>(pa[b], xv[b], w);
                         });
                         float ps[B];
-    #pragma unroll
+#pragma unroll
                         for (int b = 0; b < B; ++b) ps[b] = (pa[b][0] + pa[b][1]) + (pa[b][2] + pa[b][3]);
-    #pragma unroll
+#pragma unroll
                         for (int b = 0; b < B; ++b) {
                             float X = 0.0f;
                             if constexpr (GS > 0) X = col_sum<i * CPC + s * (CPC / SUBS)>(gs[b]);
@@ -613,7 +618,7 @@ struct GemvDpp {
                 if constexpr (is_kquant<F>()) {
                     // a K-quant part lies in one super-block: valid as a whole or not at all
                     const float d = 512.0f * h2f(wd[3] & 0xFFFFu), dmin = h2f(wd[3] >> 16);
-    #pragma unroll
+#pragma unroll
                     for (int b = 0; b < B; ++b) {
                         const float v = fmaf(d, st[b].sp, fmaf(-dmin, st[b].tx, acc[b]));
                         acc[b] = nvalid > 0 ? v : acc[b];
