@@ -413,6 +413,94 @@ __device__ __forceinline__ void fma_cols(float (&a)[4], const float4 (&xv)[NX4],
     }
 }
 
+// Component C of v.
+template <int C>
+__device__ __forceinline__ float comp(const float4& v) {
+    if constexpr (C == 0) return v.x;
+    else if constexpr (C == 1) return v.y;
+    else if constexpr (C == 2) return v.z;
+    else return v.w;
+}
+
+// a[j] += w * (lane L's xj), j < NB (NB <= 4): one weight column against NB
+// batch rows (FIRST: a[j] = the product).  Interleaving batch rows spaces the
+// writes of one accumulator NB instructions apart, so with three or more
+// batch rows a single accumulator per row meets the DPP rule (see fma4_bcast)
+// without rotation; the block starts with s_nop 1 for whatever precedes it.
+template <int L, int NB, bool FIRST>
+__device__ __forceinline__ void fma_batch_bcast(float* a, float x0, float x1, float x2, float x3, float w) {
+    if constexpr (FIRST) {
+        if constexpr (NB == 1) {
+            asm("s_nop 1\n\tv_mul_f32_dpp %0, %1, %2 row_newbcast:%c3 row_mask:0xf bank_mask:0xf"
+                : "=&v"(a[0]) : "v"(x0), "v"(w), "n"(L));
+        } else if constexpr (NB == 2) {
+            asm("s_nop 1\n\t"
+                "v_mul_f32_dpp %0, %2, %4 row_newbcast:%c5 row_mask:0xf bank_mask:0xf\n\t"
+                "v_mul_f32_dpp %1, %3, %4 row_newbcast:%c5 row_mask:0xf bank_mask:0xf"
+                : "=&v"(a[0]), "=&v"(a[1]) : "v"(x0), "v"(x1), "v"(w), "n"(L));
+        } else if constexpr (NB == 3) {
+            asm("s_nop 1\n\t"
+                "v_mul_f32_dpp %0, %3, %6 row_newbcast:%c7 row_mask:0xf bank_mask:0xf\n\t"
+                "v_mul_f32_dpp %1, %4, %6 row_newbcast:%c7 row_mask:0xf bank_mask:0xf\n\t"
+                "v_mul_f32_dpp %2, %5, %6 row_newbcast:%c7 row_mask:0xf bank_mask:0xf"
+                : "=&v"(a[0]), "=&v"(a[1]), "=&v"(a[2]) : "v"(x0), "v"(x1), "v"(x2), "v"(w), "n"(L));
+        } else {
+            asm("s_nop 1\n\t"
+                "v_mul_f32_dpp %0, %4, %8 row_newbcast:%c9 row_mask:0xf bank_mask:0xf\n\t"
+                "v_mul_f32_dpp %1, %5, %8 row_newbcast:%c9 row_mask:0xf bank_mask:0xf\n\t"
+                "v_mul_f32_dpp %2, %6, %8 row_newbcast:%c9 row_mask:0xf bank_mask:0xf\n\t"
+                "v_mul_f32_dpp %3, %7, %8 row_newbcast:%c9 row_mask:0xf bank_mask:0xf"
+                : "=&v"(a[0]), "=&v"(a[1]), "=&v"(a[2]), "=&v"(a[3])
+                : "v"(x0), "v"(x1), "v"(x2), "v"(x3), "v"(w), "n"(L));
+        }
+    } else {
+        if constexpr (NB == 1) {
+            asm("s_nop 1\n\tv_fmac_f32_dpp %0, %1, %2 row_newbcast:%c3 row_mask:0xf bank_mask:0xf"
+                : "+v"(a[0]) : "v"(x0), "v"(w), "n"(L));
+        } else if constexpr (NB == 2) {
+            asm("s_nop 1\n\t"
+                "v_fmac_f32_dpp %0, %2, %4 row_newbcast:%c5 row_mask:0xf bank_mask:0xf\n\t"
+                "v_fmac_f32_dpp %1, %3, %4 row_newbcast:%c5 row_mask:0xf bank_mask:0xf"
+                : "+v"(a[0]), "+v"(a[1]) : "v"(x0), "v"(x1), "v"(w), "n"(L));
+        } else if constexpr (NB == 3) {
+            asm("s_nop 1\n\t"
+                "v_fmac_f32_dpp %0, %3, %6 row_newbcast:%c7 row_mask:0xf bank_mask:0xf\n\t"
+                "v_fmac_f32_dpp %1, %4, %6 row_newbcast:%c7 row_mask:0xf bank_mask:0xf\n\t"
+                "v_fmac_f32_dpp %2, %5, %6 row_newbcast:%c7 row_mask:0xf bank_mask:0xf"
+                : "+v"(a[0]), "+v"(a[1]), "+v"(a[2]) : "v"(x0), "v"(x1), "v"(x2), "v"(w), "n"(L));
+        } else {
+            asm("s_nop 1\n\t"
+                "v_fmac_f32_dpp %0, %4, %8 row_newbcast:%c9 row_mask:0xf bank_mask:0xf\n\t"
+                "v_fmac_f32_dpp %1, %5, %8 row_newbcast:%c9 row_mask:0xf bank_mask:0xf\n\t"
+                "v_fmac_f32_dpp %2, %6, %8 row_newbcast:%c9 row_mask:0xf bank_mask:0xf\n\t"
+                "v_fmac_f32_dpp %3, %7, %8 row_newbcast:%c9 row_mask:0xf bank_mask:0xf"
+                : "+v"(a[0]), "+v"(a[1]), "+v"(a[2]), "+v"(a[3])
+                : "v"(x0), "v"(x1), "v"(x2), "v"(x3), "v"(w), "n"(L));
+        }
+    }
+}
+
+// ps[b] (+)= sum over the CPD columns from part column CB of w[t] * x_b, for
+// all B >= 3 batch rows: column by column, batch rows interleaved in blocks
+// of four.
+template <int CB, int CPD, int NX4, int B, bool FIRST>
+__device__ __forceinline__ void fma_cols_batched(float (&ps)[B], const float4 (&xv)[B][NX4], const float* w) {
+    static_assert(B >= 3, "hazard spacing needs three or more batch rows");
+    static_for<CPD>([&](auto T) {
+        constexpr int t = decltype(T)::value, c = CB + t;
+        constexpr int L = (c % 64) / 4, C = c % 4, M = c / 64;
+        constexpr bool first = FIRST && t == 0;
+        static_for<(B + 3) / 4>([&](auto Q) {
+            constexpr int b0 = 4 * decltype(Q)::value, nb = B - b0 < 4 ? B - b0 : 4;
+            const float x0 = comp<C>(xv[b0][M]);
+            const float x1 = nb > 1 ? comp<C>(xv[b0 + (nb > 1)][M]) : 0.0f;
+            const float x2 = nb > 2 ? comp<C>(xv[b0 + 2 * (nb > 2)][M]) : 0.0f;
+            const float x3 = nb > 3 ? comp<C>(xv[b0 + 3 * (nb > 3)][M]) : 0.0f;
+            fma_batch_bcast<L, nb, first>(&ps[b0], x0, x1, x2, x3, w[t]);
+        });
+    });
+}
+
 template <int F> constexpr bool is_kquant() { return F == QG_Q4_K || F == QG_Q2_K; }
 
 // Code units per lane part in the register-x kernel at batch B: the largest
@@ -588,18 +676,28 @@ struct GemvDpp {
                     const uint32_t dw[4] = {q[i].x, q[i].y, q[i].z, q[i].w};
                     static_for<SUBS>([&](auto S) {
                         constexpr int s = decltype(S)::value;
-                        float pa[B][4];  // started by the first dword's multiplies
-                        static_for<DPS>([&](auto D) {
-                            constexpr int d = s * DPS + decltype(D)::value;
-                            float w[CPD];
-                            U::decode(dw[d], w);
-#pragma unroll
-                            for (int b = 0; b < B; ++b)
-                                fma_cols<i * CPC + d * CPD, CPD, NX4, decltype(D)::value == 0>(pa[b], xv[b], w);
-                        });
                         float ps[B];
+                        if constexpr (B >= 3) {
+                            // one accumulator per batch row, batch rows interleaved
+                            static_for<DPS>([&](auto D) {
+                                constexpr int d = s * DPS + decltype(D)::value;
+                                float w[CPD];
+                                U::decode(dw[d], w);
+                                fma_cols_batched<i * CPC + d * CPD, CPD, NX4, B, decltype(D)::value == 0>(ps, xv, w);
+                            });
+                        } else {
+                            float pa[B][4];  // started by the first dword's multiplies
+                            static_for<DPS>([&](auto D) {
+                                constexpr int d = s * DPS + decltype(D)::value;
+                                float w[CPD];
+                                U::decode(dw[d], w);
 #pragma unroll
-                        for (int b = 0; b < B; ++b) ps[b] = (pa[b][0] + pa[b][1]) + (pa[b][2] + pa[b][3]);
+                                for (int b = 0; b < B; ++b)
+                                    fma_cols<i * CPC + d * CPD, CPD, NX4, decltype(D)::value == 0>(pa[b], xv[b], w);
+                            });
+#pragma unroll
+                            for (int b = 0; b < B; ++b) ps[b] = (pa[b][0] + pa[b][1]) + (pa[b][2] + pa[b][3]);
+                        }
 #pragma unroll
                         for (int b = 0; b < B; ++b) {
                             float X = 0.0f;
