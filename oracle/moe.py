@@ -39,7 +39,10 @@ from . import gemv as _gemv
 
 
 def softmax64(logits) -> np.ndarray:
+    """Softmax over the last axis in float64, max-subtracted.  A NaN logit
+    counts as -inf (the pages do not say; this is the stated reading)."""
     z = np.asarray(logits, np.float32).astype(np.float64)
+    z = np.where(np.isnan(z), -np.inf, z)
     z = z - z.max(axis=-1, keepdims=True)
     e = np.exp(z)
     return e / e.sum(axis=-1, keepdims=True)

@@ -38,6 +38,24 @@ def test_route_ties_prefer_lower_index():
     assert list(ids[0]) == [2, 5, 6, 0]
 
 
+def test_route_nan_counts_as_minus_inf_and_signed_zeros_tie():
+    """NaN logits route like -inf (the stated reading); -0 and +0 are equal
+    logits, so the lower index wins between them; -inf experts still fill the
+    top-K after every finite one, lower index first, with weight 0."""
+    logits = np.array([[np.nan, -1.0, np.nan, 2.0, -1.0, 0.5],
+                       [-0.0, -1.0, 0.0, -0.0, -2.0, -3.0],
+                       [-np.inf, 0.3, -np.inf, 0.3, -np.inf, -np.inf]], np.float32)
+    ids, w, _ = M.route(logits, 4)
+    assert list(ids[0]) == [3, 5, 1, 4]
+    assert list(ids[1]) == [0, 2, 3, 1]
+    assert list(ids[2]) == [1, 3, 0, 2]
+    assert w[2, 2] == 0.0 and w[2, 3] == 0.0
+    nan_free = np.where(np.isnan(logits), -np.inf, logits)
+    ids2, w2, _ = M.route(nan_free, 4)
+    np.testing.assert_array_equal(ids, ids2)
+    np.testing.assert_array_equal(w, w2)
+
+
 def test_identical_experts_closed_form():
     e, h, i, t = 6, 256, 256, 3
     wg, wu, wd = _experts(e, h, i, identical=True)
