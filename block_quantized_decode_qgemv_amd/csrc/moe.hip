@@ -86,20 +86,42 @@ __device__ __forceinline__ float wave_sum_dpp(float v) {
     return (rl(v, 0) + rl(v, 16)) + (rl(v, 32) + rl(v, 48));
 }
 
-// (value, index) keys in a total order: larger value first, then the lower
-// index.  The start key (-inf, kNoIndex) loses to every expert, -inf logits
-// included, so a round's pick is always a valid expert.
-constexpr int kNoIndex = 0x7fffffff;
+// (value, index) keys in a total order as one 64-bit integer: an
+// order-preserving image of the logit's bits above the complemented index, so
+// a larger value wins and, between equal values, the lower index (-0 is first
+// turned into +0, which compares equal to it).  Key 0 is below every expert,
+// -inf logits included, so a round's pick is always a valid expert.
+__device__ __forceinline__ uint64_t logit_key(float v, int i) {
+    const uint32_t b = __float_as_uint(v + 0.0f);
+    const uint32_t ord = (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+    return ((uint64_t)ord << 32) | (uint32_t)~i;
+}
+__device__ __forceinline__ float key_value(uint64_t k) {
+    const uint32_t ord = (uint32_t)(k >> 32);
+    return __uint_as_float((ord & 0x80000000u) ? (ord & 0x7FFFFFFFu) : ~ord);
+}
+__device__ __forceinline__ int key_index(uint64_t k) { return (int)~(uint32_t)k; }
 
-__device__ __forceinline__ void key_max(float& bv, int& bi, float ov, int oi) {
-    const bool take = (ov > bv) | ((ov == bv) & (oi < bi));  // no short circuit: selects, not branches
-    bv = take ? ov : bv;
-    bi = take ? oi : bi;
+__device__ __forceinline__ uint64_t key_max(uint64_t a, uint64_t b) { return a > b ? a : b; }
+
+template <int CTRL, int ROW_MASK = 0xF>
+__device__ __forceinline__ uint64_t dpp_key(uint64_t k) {
+    const int lo = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)k, CTRL, ROW_MASK, 0xF, false);
+    const int hi = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)(k >> 32), CTRL, ROW_MASK, 0xF, false);
+    return ((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo;
 }
 
-template <int CTRL>
-__device__ __forceinline__ void key_step(float& bv, int& bi) {
-    key_max(bv, bi, dpp_f<CTRL>(bv), dpp_i<CTRL>(bi));
+// the wave's largest key, in every lane
+__device__ __forceinline__ uint64_t wave_key_max(uint64_t k) {
+    k = key_max(k, dpp_key<0xB1>(k));        // quad_perm [1,0,3,2]
+    k = key_max(k, dpp_key<0x4E>(k));        // quad_perm [2,3,0,1]
+    k = key_max(k, dpp_key<0x141>(k));       // row_half_mirror
+    k = key_max(k, dpp_key<0x140>(k));       // row_mirror: every lane of a row holds its max
+    k = key_max(k, dpp_key<0x142, 0xA>(k));  // row_bcast:15 into rows 1, 3
+    k = key_max(k, dpp_key<0x143, 0xC>(k));  // row_bcast:31 into rows 2, 3: lane 63 holds the max
+    const uint32_t lo = __builtin_amdgcn_readlane((int)(uint32_t)k, 63);
+    const uint32_t hi = __builtin_amdgcn_readlane((int)(uint32_t)(k >> 32), 63);
+    return ((uint64_t)hi << 32) | lo;
 }
 
 template <int MPL>  // experts per lane: E <= 64 * MPL
@@ -109,6 +131,7 @@ moe_route_kernel(const float* __restrict__ logits, const float* __restrict__ sha
     __shared__ int sel_e[kMaxT * kMaxTopK];
     __shared__ float sel_w[kMaxT * kMaxTopK];
     __shared__ float sig[kMaxT];
+    __shared__ uint64_t expert_pairs[kMaxE];  // only the chosen experts' entries are touched
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
 
     // (1) one wave per token: softmax statistics, then top_k rounds of a wave
@@ -133,31 +156,26 @@ moe_route_kernel(const float* __restrict__ logits, const float* __restrict__ sha
         for (int m = 0; m < MPL; ++m)
             if (lane + 64 * m < E) s += expf(v[m] - mx);
         s = wave_sum_dpp(s);
-        uint64_t taken = 0;
+        uint64_t key[MPL];
+#pragma unroll
+        for (int m = 0; m < MPL; ++m) key[m] = lane + 64 * m < E ? logit_key(v[m], lane + 64 * m) : 0;
         int my_e = 0;
-        float my_p = 0.0f, wsum = 0.0f;
+        float my_v = -INFINITY;  // round k's winning logit, kept by lane k
         for (int k = 0; k < top_k; ++k) {
-            float best = -INFINITY;
-            int bi = kNoIndex;
+            uint64_t best = key[0];
 #pragma unroll
-            for (int m = 0; m < MPL; ++m) {
-                const int i = lane + 64 * m;
-                const bool free = i < E && !((taken >> m) & 1u);
-                key_max(best, bi, free ? v[m] : -INFINITY, free ? i : kNoIndex);
-            }
-            key_step<0xB1>(best, bi);
-            key_step<0x4E>(best, bi);
-            key_step<0x141>(best, bi);
-            key_step<0x140>(best, bi);
-            float wv = rl(best, 0);
-            int wi = __builtin_amdgcn_readlane(bi, 0);
+            for (int m = 1; m < MPL; ++m) best = key_max(best, key[m]);
+            const uint64_t win = wave_key_max(best);
 #pragma unroll
-            for (int row = 1; row < 4; ++row) key_max(wv, wi, rl(best, 16 * row), __builtin_amdgcn_readlane(bi, 16 * row));
-            if (lane == (wi & 63)) taken |= 1ull << (wi >> 6);
-            const float p = expf(wv - mx) / s;
-            wsum += p;
-            if (lane == k) { my_e = wi; my_p = p; }
+            for (int m = 0; m < MPL; ++m) key[m] = key[m] == win ? 0 : key[m];  // taken
+            if (lane == k) { my_e = key_index(win); my_v = key_value(win); }
         }
+        // the weights, off the rounds' dependency chain: lane k turns its logit
+        // into a probability; the renormalising sum adds them in round order
+        const float my_p = expf(my_v - mx) / s;
+        float wsum = 0.0f;
+        if (flags & QG_MOE_RENORM)
+            for (int k = 0; k < top_k; ++k) wsum += rl(my_p, k);
         if (lane < top_k) {
             sel_e[wave * top_k + lane] = my_e;
             sel_w[wave * top_k + lane] = (flags & QG_MOE_RENORM) ? my_p / wsum : my_p;
@@ -171,24 +189,30 @@ moe_route_kernel(const float* __restrict__ logits, const float* __restrict__ sha
     if (wave == 0) {
         const int P = T * top_k;  // <= 64
         const bool act = lane < P;
-        const int e = act ? sel_e[lane] : -1 - lane;  // inactive lanes match nothing
-        int cnt = 0, pos = 0, lead = lane;
-        for (int r = 0; r < P; ++r) {
-            const int er = __builtin_amdgcn_readlane(e, r);
-            const bool same = er == e;
-            cnt += same;
-            if (same && r < lane) {
-                ++pos;
-                lead = min(lead, r);
-            }
-        }
+        const int e = act ? sel_e[lane] : 0;
+        // the set of pairs that chose each expert, as a lane mask in LDS: cleared,
+        // then or-ed by every pair (LDS operations of one wave run in order)
+        if (act) expert_pairs[e] = 0;
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        if (act) __hip_atomic_fetch_or(&expert_pairs[e], 1ull << lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        const uint64_t same = act ? expert_pairs[e] : 0;
+        const int cnt = __popcll(same);                                  // pairs of this expert
+        const int pos = __popcll(same & ((1ull << lane) - 1));          // earlier pairs of it
+        const int lead = act ? __builtin_ctzll(same) : lane;             // its first pair
         const int nit = (act && pos == 0) ? (cnt + 1) / 2 : 0;  // items of this expert, at its first pair
-        int base = 0, n_routed = 0;  // items of experts first seen before the lead pair; all items
-        for (int r = 0; r < P; ++r) {
-            const int nr = __builtin_amdgcn_readlane(nit, r);
-            n_routed += nr;
-            if (r < lead) base += nr;
+        // items of experts first seen before the lead pair (exclusive scan over
+        // lanes), and all items
+        int incl = nit;
+#pragma unroll
+        for (int d = 1; d < 64; d *= 2) {
+            const int v = __shfl_up(incl, d);
+            incl += lane >= d ? v : 0;
         }
+        const int base = __shfl(incl - nit, lead);
+        const int n_routed = __shfl(incl, 63);
         if (act) {
             const int item = base + pos / 2, slot = pos % 2;
             int* it = items + kItemInts * (1 + item);

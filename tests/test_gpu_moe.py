@@ -154,6 +154,33 @@ def test_moe_shared_routes(fmt):
     assert all(set(ref["ids"][tok]) == set(favourites) for tok in range(t))
 
 
+@pytest.mark.parametrize("fmt", KFORMATS)
+def test_moe_route_ties_nan_inf_zero(fmt):
+    """Exact ties (lower expert index first), NaN logits (counted as -inf),
+    -inf logits and signed zeros: the routed output equals the oracle's, whose
+    stable sort settles ties the same way."""
+    e, h, i, top_k, t = 16, 256, 256, 4, 6
+    layer, gu_d, dn_d = small_layer(fmt, e, h, i, 31)
+    x, residual, logits, s = inputs(t, e, h, 31)
+    logits[0, :] = 0.5                                            # all tied
+    logits[1, :] = -1.0
+    logits[1, [2, 9, 11]] = 1.0                                   # three tied leaders
+    logits[1, [0, 5]] = np.nan
+    logits[2, :] = -1.0
+    logits[2, [3, 9]] = -0.0
+    logits[2, [7]] = 0.0                                          # signed zeros tie
+    logits[3, :] = -np.inf
+    logits[3, [4, 12]] = 0.25                                     # two finite, rest -inf
+    logits[4, :] = np.nan
+    logits[4, [1, 6, 8, 15]] = [0.1, 0.1, -0.3, 0.1]             # NaN elsewhere
+    out = run_moe(fmt, gu_d, dn_d, e, h, i, top_k, x, residual, logits, s)
+    wg, wu, wd = layer.view("gate"), layer.view("up"), layer.view("down")
+    ref = OM.moe_ref(wg, wu, wd, x, residual, logits, s, top_k)
+    tol = OM.out_tolerance(wg, wu, wd, x, residual, ref)
+    err = np.abs(out.astype(np.float64) - ref["out"])
+    assert np.all(err <= tol), f"|err|/tol = {np.max(err / tol):.3g}"
+
+
 def test_moe_dominant_logit_matches_single_expert():
     """One dominant logit per token: the routed part reduces to that expert's
     forward with weight ~1, checked against expert_forward directly."""
