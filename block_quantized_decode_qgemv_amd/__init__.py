@@ -21,7 +21,7 @@ import numpy as np
 
 __all__ = [
     "FORMATS", "QG_MOE_RENORM", "QGError", "QGLibraryMissing", "lib_path", "load",
-    "qg_packed_size", "qg_codes_plane_size", "qg_block_size", "qgemv_workspace_size",
+    "qg_packed_size", "qg_codes_plane_size", "qg_codes_plane_offset", "qg_block_size", "qgemv_workspace_size",
     "qgemv", "qgemv_q8_0", "qgemv_q4_0", "qgemv_q4_1", "qgemv_q4k", "qgemv_q2k",
     "qgemv_tern", "qgemv_bin", "qg_dequant", "qquant", "qpack_tern", "qpack_bin",
     "moe_expert_ffn_workspace_size", "moe_expert_ffn", "qg_strerror", "qg_last_error",
@@ -44,6 +44,7 @@ _GEMV_ARGS = [_vp, _vp, _vp, _i64, _i64, _i32, _vp, _sz, _vp]
 _SIGNATURES = {
     "qg_packed_size": (_sz, [_i32, _i64, _i64]),
     "qg_codes_plane_size": (_sz, [_i32, _i64, _i64]),
+    "qg_codes_plane_offset": (_sz, [_i32, _i64, _i64]),
     "qg_block_size": (_i32, [_i32]),
     "qgemv_workspace_size": (_sz, [_i32, _i64, _i64, _i32]),
     "qgemv": (_i32, [_i32] + _GEMV_ARGS),
@@ -162,6 +163,11 @@ def qg_packed_size(fmt, n: int, k: int) -> int:
 
 def qg_codes_plane_size(fmt, n: int, k: int) -> int:
     return load().qg_codes_plane_size(_fmt(fmt), n, k)
+
+
+def qg_codes_plane_offset(fmt, n: int, k: int) -> int:
+    """Where the codes plane ends and the meta plane begins (see qgemv.h)."""
+    return load().qg_codes_plane_offset(_fmt(fmt), n, k)
 
 
 def qg_block_size(fmt) -> int:

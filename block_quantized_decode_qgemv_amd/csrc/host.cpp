@@ -277,6 +277,8 @@ size_t qg_codes_plane_size(int fmt, int64_t N, int64_t K) {
     return (size_t)N * (size_t)(K / fi->block) * (size_t)fi->code_bytes;
 }
 
+size_t qg_codes_plane_offset(int fmt, int64_t N, int64_t K) { return qg_codes_plane_size(fmt, N, K); }
+
 int qg_block_size(int fmt) {
     const FormatInfo* fi = format_info(fmt);
     return fi ? fi->block : 0;

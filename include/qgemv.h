@@ -98,6 +98,11 @@ size_t qg_packed_size(int fmt, int64_t N, int64_t K);
 /* Bytes of the codes plane, i.e. the offset of the meta plane (0 if invalid). */
 size_t qg_codes_plane_size(int fmt, int64_t N, int64_t K);
 
+/* The same value, named for the layout [codes plane][meta plane]: the byte
+ * offset at which the codes plane ends and the meta plane begins (the codes
+ * plane itself starts at offset 0).  0 if invalid. */
+size_t qg_codes_plane_offset(int fmt, int64_t N, int64_t K);
+
 /* Weights per block (32, 256 or 128) or 0 for an unknown format. */
 int qg_block_size(int fmt);
 

@@ -43,6 +43,7 @@ def test_sizes_match_oracle(fmt):
     for n, k in ((1, 256), (3, 1024), (4096, 4096), (14336, 4096), (4096, 14336)):
         assert qg.qg_packed_size(fmt, n, k) == OF.packed_size(fmt, n, k)
         assert qg.qg_codes_plane_size(fmt, n, k) == OF.codes_plane_size(fmt, n, k)
+        assert qg.qg_codes_plane_offset(fmt, n, k) == OF.codes_plane_size(fmt, n, k)
     assert qg.qg_block_size(fmt) == OF.SPECS[fmt].block
     assert qg.qg_packed_size(fmt, 0, 256) == 0
     assert qg.qg_packed_size(fmt, 4, OF.SPECS[fmt].block + 1) == 0
