@@ -16,6 +16,8 @@ define, in numpy:
 * ``gemv``      -- y = W x in float64 and the acceptance bound.
 * ``moe``       -- the routed expert layer (softmax top-K, SwiGLU, gated
                    combine + residual) and its propagated error bound.
+* ``norm``      -- RMS normalisation (two passes) feeding the GEMV, and
+                   its bound.
 * ``decode_bound`` -- the handbook page's decode speed bound
                    (bandwidth x efficiency / weight bytes).
 
