@@ -10,8 +10,8 @@ back to back, so the figure is the kernels', not the host's launch rate (the
 eagerly launched rate is reported next to it).
 
 Also reported (in ``extra``): every GEMV of the four-format comparison
-(Q8_0/Q4_0/Q4_1/Q4_K x 4096x4096/14336x4096 x batch 1/8) and the low-bit
-formats, each timed the same way.
+(Q8_0/Q4_0/Q4_1/Q4_K x 4096x4096/14336x4096 x batch 1/8), the low-bit
+formats and the RMS-normalising Q4_K GEMV, each timed the same way.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--quick] [--no-cpu]
 
@@ -37,7 +37,8 @@ COLD_BYTES = 1 << 30            # rotate over at least this many bytes of packed
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "q4k_gemv_14336x4096_counters.txt")
 CSRC = os.path.join(ROOT, "block_quantized_decode_qgemv_amd", "csrc")
 KERNEL_SOURCES = {"kernel_source_sha256_16": os.path.join(CSRC, "gemv.hip"),
-                  "kernel_core_sha256_16": os.path.join(CSRC, "gemv_core.h")}
+                  "kernel_core_sha256_16": os.path.join(CSRC, "gemv_core.h"),
+                  "kernel_dispatch_sha256_16": os.path.join(CSRC, "gemv_dispatch.h")}
 
 
 def log(msg):
@@ -74,7 +75,7 @@ class Gemv:
     Launches go straight to the C ABI with precomputed device pointers; timed
     runs replay a HIP graph holding one launch per copy."""
 
-    def __init__(self, torch, qg, fmt, n, k, b, seed, min_bytes, stream):
+    def __init__(self, torch, qg, fmt, n, k, b, seed, min_bytes, stream, rmsnorm=False):
         import workloads
 
         self.torch = torch
@@ -103,14 +104,23 @@ class Gemv:
         self.fid = qg.FORMATS[fmt]
         self.wp = [t.data_ptr() for t in self.w]
         self.xp, self.yp = self.x.data_ptr(), self.y.data_ptr()
+        # rmsnorm: the same GEMV fed by RMS norm of x (gain gamma, eps 1e-5)
+        self.rmsnorm = rmsnorm
+        if rmsnorm:
+            self.gamma = torch.from_numpy(1.0 + 0.25 * workloads.normal((k,), seed, 98)).float().to("cuda")
+            self.gp = self.gamma.data_ptr()
         self.stream = stream
         self.sp = stream.cuda_stream
         self.i = 0
         self.graph = None
 
     def step(self):
-        rc = self.lib.qgemv(self.fid, self.wp[self.i % len(self.wp)], self.xp, self.yp, self.n, self.k, self.b,
-                            None, 0, self.sp)
+        w = self.wp[self.i % len(self.wp)]
+        if self.rmsnorm:
+            rc = self.lib.qgemv_rmsnorm(self.fid, w, self.xp, self.gp, 1e-5, self.yp, self.n, self.k, self.b,
+                                        self.sp)
+        else:
+            rc = self.lib.qgemv(self.fid, w, self.xp, self.yp, self.n, self.k, self.b, None, 0, self.sp)
         if rc:
             raise RuntimeError(f"qgemv failed with {rc}")
         self.i += 1
@@ -417,8 +427,8 @@ def main():
              "headline_algorithmic_bytes": head.bytes,
              "headline_hbm_bytes_counted": hbm_bytes}
     if not args.quick:
-        def measure(fmt, n, k, b):
-            g = Gemv(torch, qg, fmt, n, k, b, 0, COLD_BYTES, stream)
+        def measure(fmt, n, k, b, rmsnorm=False):
+            g = Gemv(torch, qg, fmt, n, k, b, 0, COLD_BYTES, stream, rmsnorm)
             g.capture()
             g.replay(2)
             t = g.timed_replay(max(2, 400 // len(g.wp)))
@@ -445,6 +455,14 @@ def main():
                                  "GBps": round(nbytes / t / 1e9, 1), "Gweights_s": round(n * k * b / t / 1e9, 1)})
                     log(f"  {fmt} {n}x{k} B={b}: {t*1e6:.2f} us, {nbytes/t/1e9:.1f} GB/s")
         extra["low_bit"] = rows
+        rows = []
+        for n, k in ((14336, 4096), (4096, 4096)):
+            for b in (1, 8):
+                t, nbytes = measure("q4_k", n, k, b, rmsnorm=True)
+                rows.append({"fmt": "q4_k", "N": n, "K": k, "B": b, "us": round(t * 1e6, 2),
+                             "GBps": round(nbytes / t / 1e9, 1)})
+                log(f"  rmsnorm + q4_k {n}x{k} B={b}: {t*1e6:.2f} us, {nbytes/t/1e9:.1f} GB/s")
+        extra["rmsnorm_gemv"] = rows
         log("8B decode step (32 layers x 7 Q4_K GEMVs)")
         extra["dense_8b_step"] = dense_step(torch, qg, stream)
         log(f"  {extra['dense_8b_step']}")

@@ -23,7 +23,7 @@ __all__ = [
     "FORMATS", "QG_MOE_RENORM", "QGError", "QGLibraryMissing", "lib_path", "load",
     "qg_packed_size", "qg_codes_plane_size", "qg_codes_plane_offset", "qg_block_size", "qgemv_workspace_size",
     "qgemv", "qgemv_q8_0", "qgemv_q4_0", "qgemv_q4_1", "qgemv_q4k", "qgemv_q2k",
-    "qgemv_tern", "qgemv_bin", "qg_dequant", "qquant", "qpack_tern", "qpack_bin",
+    "qgemv_tern", "qgemv_bin", "qgemv_rmsnorm", "qg_dequant", "qquant", "qpack_tern", "qpack_bin",
     "moe_expert_ffn_workspace_size", "moe_expert_ffn", "qg_strerror", "qg_last_error",
     "qg_version", "EXPORTED_SYMBOLS",
 ]
@@ -55,6 +55,7 @@ _SIGNATURES = {
     "qgemv_q2k": (_i32, _GEMV_ARGS),
     "qgemv_tern": (_i32, _GEMV_ARGS),
     "qgemv_bin": (_i32, _GEMV_ARGS),
+    "qgemv_rmsnorm": (_i32, [_i32, _vp, _vp, _vp, ctypes.c_float, _vp, _i64, _i64, _i32, _vp]),
     "qg_dequant": (_i32, [_i32, _vp, _vp, _i64, _i64, _vp]),
     "qquant": (_i32, [_i32, _vp, _i64, _i64, _vp, _i32]),
     "qpack_tern": (_i32, [_vp, _vp, _i64, _i64, _vp]),
@@ -229,6 +230,14 @@ qgemv_q4k = _named("qgemv_q4k", "q4_k")
 qgemv_q2k = _named("qgemv_q2k", "q2_k")
 qgemv_tern = _named("qgemv_tern", "tern")
 qgemv_bin = _named("qgemv_bin", "bin")
+
+
+def qgemv_rmsnorm(fmt, w, x, gamma, eps: float, y, n: int, k: int, b: int = 1, stream=None) -> None:
+    """y[b] = W rmsnorm(x[b]; gamma, eps) on the device (see qgemv_rmsnorm in qgemv.h)."""
+    f32, u8 = _torch_dtypes()
+    rc = load().qgemv_rmsnorm(_fmt(fmt), _dev(w, u8, "w"), _dev(x, f32, "x"), _dev(gamma, f32, "gamma"),
+                              float(eps), _dev(y, f32, "y"), n, k, b, _stream(stream))
+    _check(rc, "qgemv_rmsnorm")
 
 
 def qg_dequant(fmt, w, out, n: int, k: int, stream=None) -> None:

@@ -35,6 +35,7 @@
 #include <cstdint>
 
 #include "gemv_core.h"
+#include "gemv_dispatch.h"
 #include "internal.h"
 
 namespace qg {
@@ -149,99 +150,16 @@ int device_cus() {
 
 namespace {
 
-template <int F, int B, int W>
-hipError_t launch_gemv_dpp_w(const uint8_t* codes, const uint8_t* meta, const float* x, float* y,
-                             int N, int K, hipStream_t st) {
-    constexpr int KCS = dpp_lane_units<F, B>();
-    const int grid = (N + kRowGroup - 1) / kRowGroup;
-    hipLaunchKernelGGL((gemv_dpp_kernel<F, B, W, KCS>), dim3(grid), dim3(W * 64), 0, st, codes, meta, x, y, N, K);
-    return hipGetLastError();
-}
-
-// Workgroups of gemv_dpp_kernel<F, B, W> that one compute unit holds at once
-// (registers decide it); queried once per kernel.
-template <int F, int B, int W>
-int dpp_resident() {
-    static const int n = [] {
-        int b = 0;
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&b, gemv_dpp_kernel<F, B, W, dpp_lane_units<F, B>()>,
-                                                         W * 64, 0) != hipSuccess) {
-            (void)hipGetLastError();
-            b = 1;
-        }
-        return b < 1 ? 1 : b;
-    }();
-    return n;
-}
-
-// Waves per workgroup: start from the fewest that cover a row in one slice
-// (pick_waves_dpp), then halve while too few workgroups fit on a compute unit:
-// one when the grid has at most one workgroup per compute unit, else two, so
-// that a workgroup's reduction and tail overlap another's streaming.
-template <int F, int B>
-int choose_waves_dpp(int N, int K) {
-    constexpr int MW = dpp_max_waves<F, B>();
-    const int groups = (N + kRowGroup - 1) / kRowGroup;
-    const int need = groups > device_cus() ? 2 : 1;
-    int w = pick_waves_dpp<F, dpp_lane_units<F, B>()>(K, MW);
-    for (; w > 1; w /= 2) {
-        int res = 1;
-        switch (w) {
-            case 2: res = dpp_resident<F, B, 2>(); break;
-            case 4: res = dpp_resident<F, B, 4>(); break;
-            case 8: res = dpp_resident<F, B, 8>(); break;
-            default:
-                if constexpr (MW == 16) res = dpp_resident<F, B, 16>();
-                break;
-        }
-        if (res >= need) break;
+// The plain GEMV as a kernel set for the shared dispatch.
+template <int F, int B, int W, int KCS>
+struct PlainGemv {
+    static hipError_t launch(dim3 grid, dim3 block, hipStream_t st, const uint8_t* codes, const uint8_t* meta,
+                             const float* x, float* y, int N, int K) {
+        hipLaunchKernelGGL((gemv_dpp_kernel<F, B, W, KCS>), grid, block, 0, st, codes, meta, x, y, N, K);
+        return hipGetLastError();
     }
-    return w;
-}
-
-template <int F, int B>
-hipError_t launch_gemv_b(const uint8_t* codes, const uint8_t* meta, const float* x, float* y,
-                         int N, int K, hipStream_t st) {
-    static_assert(B <= dpp_max_batch<F>(), "every batch runs the register-x kernel");
-    constexpr int MW = dpp_max_waves<F, B>();
-    switch (choose_waves_dpp<F, B>(N, K)) {
-        case 1: return launch_gemv_dpp_w<F, B, 1>(codes, meta, x, y, N, K, st);
-        case 2: return launch_gemv_dpp_w<F, B, 2>(codes, meta, x, y, N, K, st);
-        case 4: return launch_gemv_dpp_w<F, B, 4>(codes, meta, x, y, N, K, st);
-        case 8: return launch_gemv_dpp_w<F, B, 8>(codes, meta, x, y, N, K, st);
-        default:
-            if constexpr (MW == 16) return launch_gemv_dpp_w<F, B, 16>(codes, meta, x, y, N, K, st);
-            return hipErrorInvalidConfiguration;  // never chosen
-    }
-}
-
-template <int F>
-hipError_t launch_gemv_f(const uint8_t* codes, const uint8_t* meta, const float* x, float* y,
-                         int N, int K, int B, hipStream_t st) {
-    switch (B) {
-        case 1: return launch_gemv_b<F, 1>(codes, meta, x, y, N, K, st);
-        case 2: return launch_gemv_b<F, 2>(codes, meta, x, y, N, K, st);
-        case 3: return launch_gemv_b<F, 3>(codes, meta, x, y, N, K, st);
-        case 4: return launch_gemv_b<F, 4>(codes, meta, x, y, N, K, st);
-        case 5: return launch_gemv_b<F, 5>(codes, meta, x, y, N, K, st);
-        case 6: return launch_gemv_b<F, 6>(codes, meta, x, y, N, K, st);
-        case 7: return launch_gemv_b<F, 7>(codes, meta, x, y, N, K, st);
-        default: return launch_gemv_b<F, 8>(codes, meta, x, y, N, K, st);
-    }
-}
-
-hipError_t launch_gemv(int fmt, const uint8_t* codes, const uint8_t* meta, const float* x, float* y,
-                       int N, int K, int B, hipStream_t st) {
-    switch (fmt) {
-        case QG_Q8_0: return launch_gemv_f<QG_Q8_0>(codes, meta, x, y, N, K, B, st);
-        case QG_Q4_0: return launch_gemv_f<QG_Q4_0>(codes, meta, x, y, N, K, B, st);
-        case QG_Q4_1: return launch_gemv_f<QG_Q4_1>(codes, meta, x, y, N, K, B, st);
-        case QG_Q4_K: return launch_gemv_f<QG_Q4_K>(codes, meta, x, y, N, K, B, st);
-        case QG_Q2_K: return launch_gemv_f<QG_Q2_K>(codes, meta, x, y, N, K, B, st);
-        case QG_TERN: return launch_gemv_f<QG_TERN>(codes, meta, x, y, N, K, B, st);
-        default: return launch_gemv_f<QG_BIN>(codes, meta, x, y, N, K, B, st);
-    }
-}
+    static int resident() { return resident_blocks(gemv_dpp_kernel<F, B, W, KCS>, W * 64); }
+};
 
 template <int F>
 hipError_t launch_dequant_f(const uint8_t* codes, const uint8_t* meta, float* out, int N, int K, hipStream_t st) {
@@ -265,6 +183,8 @@ hipError_t launch_dequant(int fmt, const uint8_t* codes, const uint8_t* meta, fl
 
 constexpr int64_t kMaxGemvK = (int64_t)1 << 26;
 
+}  // namespace
+
 int check_gemv_args(int fmt, const void* w, const float* x, const float* y, int64_t N, int64_t K, int B) {
     int rc = check_matrix(fmt, N, K);
     if (rc) return rc;
@@ -278,7 +198,6 @@ int check_gemv_args(int fmt, const void* w, const float* x, const float* y, int6
     return QG_OK;
 }
 
-}  // namespace
 }  // namespace qg
 
 using namespace qg;
@@ -298,7 +217,8 @@ int qgemv(int fmt, const void* w, const float* x, float* y, int64_t N, int64_t K
     if (rc) return rc;
     const uint8_t* codes = static_cast<const uint8_t*>(w);
     const uint8_t* meta = codes + qg_codes_plane_size(fmt, N, K);
-    hipError_t e = launch_gemv(fmt, codes, meta, x, y, (int)N, (int)K, B, static_cast<hipStream_t>(stream));
+    hipError_t e = core::launch_dpp<PlainGemv>(fmt, (int)N, (int)K, B, static_cast<hipStream_t>(stream), codes, meta, x, y,
+                                         (int)N, (int)K);
     if (e != hipSuccess) return fail(QG_EHIP, "GEMV launch failed: %s", hipGetErrorString(e));
     return QG_OK;
 }

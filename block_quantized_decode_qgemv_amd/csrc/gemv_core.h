@@ -567,12 +567,29 @@ struct GemvDpp {
         run_group(codes, meta, N, K, g, xrow, nb, epi, 0, red);
     }
 
+    // The same with the activation rows RMS-normalised on the way in:
+    // x_k -> x_k * gamma_k / sqrt(mean_k x_k^2 + eps), per batch row.  The
+    // waves that load x also sum its squares (every column once), gamma is
+    // applied to x in registers, and the 1/rms of each batch row scales the
+    // finished row sums, so the normalised x is never stored.
+    template <class XRow, class Epi>
+    __device__ static void run_rmsnorm(const uint8_t* __restrict__ codes, const uint8_t* __restrict__ meta,
+                                       int N, int K, int g, XRow xrow, int nb, const float* __restrict__ gamma,
+                                       float eps, Epi epi) {
+        __shared__ float red[W * kRowGroup * B];
+        __shared__ float red_ss[W * B];
+        run_group<true>(codes, meta, N, K, g, xrow, nb, epi, 0, red, gamma, eps, red_ss);
+    }
+
     // The same on waves [wave0, wave0 + W) of a larger workgroup, with the
     // cross-wave partials in red (W * 16 * B floats of LDS).  Every wave of the
     // workgroup must call it (it synchronizes the whole workgroup once).
-    template <class XRow, class Epi>
+    // NORM: see run_rmsnorm; red_ss holds W * B floats.
+    template <bool NORM = false, class XRow, class Epi>
     __device__ static void run_group(const uint8_t* __restrict__ codes, const uint8_t* __restrict__ meta,
-                                     int N, int K, int g, XRow xrow, int nb, Epi epi, int wave0, float* red) {
+                                     int N, int K, int g, XRow xrow, int nb, Epi epi, int wave0, float* red,
+                                     const float* __restrict__ gamma = nullptr, float eps = 0.0f,
+                                     float* red_ss = nullptr) {
         const int tid = threadIdx.x - 64 * wave0, lane = tid & 63, wave = tid >> 6;
         const int r = lane & 15, p = wave * 4 + (lane >> 4);
         const int n_g = min(kRowGroup, N - g * kRowGroup);
@@ -587,9 +604,9 @@ struct GemvDpp {
         const uint8_t* gm = meta + (size_t)g * kRowGroup * row_meta;
         const uint32_t ro = (uint32_t)rr * 16;
 
-        float acc[B];
+        float acc[B], ss[B];  // row sums; sums of x^2 (NORM)
 #pragma unroll
-        for (int b = 0; b < B; ++b) acc[b] = 0.0f;
+        for (int b = 0; b < B; ++b) acc[b] = ss[b] = 0.0f;
 
         // FULL: a whole 16-row group and whole slices, so no address needs a
         // clamp and every part is valid (constant strides).  Only the larger
@@ -616,6 +633,14 @@ struct GemvDpp {
                             // only meet code units whose contributions are dropped
                             const uint32_t c = (uint32_t)(FULL ? k0 + 64 * m + 4 * r : min(k0 + 64 * m + 4 * r, K - 4));
                             xv[b][m] = *(const float4*)((const uint8_t*)xb + c * 4u);
+                            if constexpr (NORM) {
+                                const float4 v = xv[b][m];
+                                // each column once: the lanes of a part tile it, parts are disjoint
+                                if (FULL || k0 + 64 * m + 4 * r < K)
+                                    ss[b] += (v.x * v.x + v.y * v.y) + (v.z * v.z + v.w * v.w);
+                                const float4 gm4 = *(const float4*)((const uint8_t*)gamma + c * 4u);
+                                xv[b][m] = make_float4(v.x * gm4.x, v.y * gm4.y, v.z * gm4.z, v.w * gm4.w);
+                            }
                         }
                     }
                 }
@@ -742,12 +767,33 @@ struct GemvDpp {
             const float v = __uint_as_float(q2[0]) + __uint_as_float(q2[1]);
             if (lane < 16) red[(wave * kRowGroup + r) * B + b] = v;
         }
+        if constexpr (NORM) {
+            // the wave's sum of squares per batch row: the four rows of lanes,
+            // then the 16 lanes of a row (valid in its last lane)
+#pragma unroll
+            for (int b = 0; b < B; ++b) {
+                const auto h = __builtin_amdgcn_permlane32_swap(__float_as_uint(ss[b]), __float_as_uint(ss[b]),
+                                                                false, false);
+                const float v2 = __uint_as_float(h[0]) + __uint_as_float(h[1]);
+                const auto q2 = __builtin_amdgcn_permlane16_swap(__float_as_uint(v2), __float_as_uint(v2), false,
+                                                                 false);
+                const float v = group_sum<16>(__uint_as_float(q2[0]) + __uint_as_float(q2[1]));
+                if (lane == 15) red_ss[wave * B + b] = v;
+            }
+        }
         __syncthreads();
         epi(
             [&](int t) {
                 float v = 0.0f;
 #pragma unroll
                 for (int w = 0; w < W; ++w) v += red[w * kRowGroup * B + t];
+                if constexpr (NORM) {
+                    const int b = t % B;
+                    float q = 0.0f;
+#pragma unroll
+                    for (int w = 0; w < W; ++w) q += red_ss[w * B + b];
+                    v = v / sqrtf(q / (float)K + eps);
+                }
                 return v;
             },
             n_g, tid);

@@ -1,0 +1,71 @@
+// GEMV on RMS-normalised activations: Y[b] = W * rmsnorm(X[b]), with
+// rmsnorm(x)_k = x_k * gamma_k / sqrt(mean_k x_k^2 + eps).
+//
+// The Flash-MoE page runs RMS normalisation on the GPU in two passes (a
+// sum-of-squares reduction, then its application; section "Metal 计算着色器")
+// and keeps the combine + norm on the GPU so that it feeds the next layer's
+// projection directly (section "延迟 GPU 专家计算").  Here both passes fold
+// into the projection that consumes the normalised vector: the waves that
+// load x for the register-x GEMV also sum its squares, gamma multiplies x in
+// registers, and each batch row's 1/rms scales its finished row sums
+// (GemvDpp::run_rmsnorm in gemv_core.h).  The normalised vector is never
+// written, and the call costs one launch like the plain GEMV.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+
+#include "gemv_core.h"
+#include "gemv_dispatch.h"
+#include "internal.h"
+
+namespace qg {
+namespace {
+
+using namespace core;
+
+template <int F, int B, int W, int KCS>
+__global__ void __launch_bounds__(W * 64)
+gemv_rmsnorm_kernel(const uint8_t* __restrict__ codes, const uint8_t* __restrict__ meta,
+                    const float* __restrict__ x, const float* __restrict__ gamma, float eps,
+                    float* __restrict__ y, int N, int K) {
+    const int g = blockIdx.x;
+    GemvDpp<F, B, W, KCS>::run_rmsnorm(
+        codes, meta, N, K, g, [&](int b) { return x + (size_t)b * K; }, B, gamma, eps,
+        [&](auto sums, int n_g, int tid) {
+            for (int t = tid; t < kRowGroup * B; t += W * 64)
+                if (t / B < n_g) y[(size_t)(t % B) * N + g * kRowGroup + t / B] = sums(t);
+        });
+}
+
+template <int F, int B, int W, int KCS>
+struct RmsNormGemv {
+    static hipError_t launch(dim3 grid, dim3 block, hipStream_t st, const uint8_t* codes, const uint8_t* meta,
+                             const float* x, const float* gamma, float eps, float* y, int N, int K) {
+        hipLaunchKernelGGL((gemv_rmsnorm_kernel<F, B, W, KCS>), grid, block, 0, st, codes, meta, x, gamma, eps, y,
+                           N, K);
+        return hipGetLastError();
+    }
+    static int resident() { return resident_blocks(gemv_rmsnorm_kernel<F, B, W, KCS>, W * 64); }
+};
+
+}  // namespace
+}  // namespace qg
+
+using namespace qg;
+
+extern "C" int qgemv_rmsnorm(int fmt, const void* w, const float* x, const float* gamma, float eps, float* y,
+                             int64_t N, int64_t K, int B, void* stream) {
+    clear_error();
+    int rc = check_gemv_args(fmt, w, x, y, N, K, B);
+    if (rc) return rc;
+    if (!gamma) return fail(QG_EINVAL, "null gamma");
+    if (!aligned(gamma, 16)) return fail(QG_EALIGN, "gamma must be 16-byte aligned");
+    if (!(eps >= 0.0f) || !std::isfinite(eps)) return fail(QG_ERANGE, "eps=%g must be finite and >= 0", (double)eps);
+    const uint8_t* codes = static_cast<const uint8_t*>(w);
+    const uint8_t* meta = codes + qg_codes_plane_size(fmt, N, K);
+    hipError_t e = core::launch_dpp<RmsNormGemv>(fmt, (int)N, (int)K, B, static_cast<hipStream_t>(stream), codes,
+                                                 meta, x, gamma, eps, y, (int)N, (int)K);
+    if (e != hipSuccess) return fail(QG_EHIP, "GEMV launch failed: %s", hipGetErrorString(e));
+    return QG_OK;
+}

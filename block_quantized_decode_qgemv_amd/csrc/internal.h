@@ -29,4 +29,8 @@ bool aligned(const void* p, size_t a);
 // Compute units of the current device (cached per device; 256 if the query fails).
 int device_cus();
 
+// Host checks of a GEMV call (format, shape, batch, pointers, alignment);
+// QG_OK or the error code with the detail recorded.
+int check_gemv_args(int fmt, const void* w, const float* x, const float* y, int64_t N, int64_t K, int B);
+
 }  // namespace qg

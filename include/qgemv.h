@@ -145,6 +145,27 @@ int qgemv_tern(const void* w, const float* x, float* y, int64_t N, int64_t K, in
 int qgemv_bin(const void* w, const float* x, float* y, int64_t N, int64_t K, int B,
               void* ws, size_t ws_bytes, void* stream);
 
+/* ------------------------------------------------- GEMV on normalised x */
+
+/* Y[b][n] = sum_k W[n][k] * xhat[b][k] with the RMS normalisation
+ *   xhat[b][k] = X[b][k] * gamma[k] / sqrt(mean_k X[b][k]^2 + eps)
+ * of each activation row folded into the GEMV (Flash-MoE page: RMS
+ * normalisation in two passes, sum of squares then application, section
+ * "Metal 计算着色器"; the norm feeding the next projection on the GPU, section
+ * "延迟 GPU 专家计算").  The sum of squares is taken while x is loaded, gamma
+ * scales x in registers and 1/rms scales each row sum, so no normalised copy
+ * of x is written.
+ *   gamma  DEVICE, fp32 [K], 16-byte aligned.
+ *   eps    finite, >= 0 (a zero row with eps = 0 gives non-finite y, as the
+ *          definition does).
+ *   w, x, y, N, K, B, stream: as for qgemv.
+ * Accuracy: |error| <= 3e-5 * sum_k |W[n][k] xhat[b][k]| + 1e-7: the qgemv
+ * bound on xhat plus the fp32 sum of squares, square root and gamma product.
+ * Deterministic.  Errors: as qgemv, plus QG_EINVAL (null gamma), QG_EALIGN
+ * (gamma), QG_ERANGE (eps). */
+int qgemv_rmsnorm(int fmt, const void* w, const float* x, const float* gamma, float eps, float* y,
+                  int64_t N, int64_t K, int B, void* stream);
+
 /* ----------------------------------------------------------------- dequant */
 
 /* Device dequantization of a packed [N][K] matrix to fp32 out[N][K]

@@ -94,6 +94,26 @@ def test_gemv_validation(args, code):
 
 
 @nogpu
+def test_gemv_rmsnorm_validation():
+    import ctypes
+
+    lib = qg.load()
+
+    def call(fmt=3, w=P, x=P, gamma=P, eps=1e-6, y=P, n=4, k=256, b=1):
+        return lib.qgemv_rmsnorm(fmt, w, x, gamma, ctypes.c_float(eps), y, n, k, b, None)
+
+    assert call(gamma=None) == -1
+    assert call(gamma=P + 4) == -3
+    assert call(eps=-1e-6) == -4
+    assert call(eps=float("nan")) == -4
+    assert call(eps=float("inf")) == -4
+    assert call(k=128) == -2            # the plain GEMV's checks come first
+    assert call(b=9) == -4
+    assert call(x=None) == -1
+    assert qg.qg_last_error()
+
+
+@nogpu
 def test_dequant_validation():
     lib = qg.load()
     assert lib.qg_dequant(3, P, P, 0, 256, None) == -2

@@ -194,6 +194,13 @@ def check_sampled_rows(fmt, packed, sub, rows, n, k, x, y):
     """Rows `rows` of the full device buffer `packed` must equal, byte for byte,
     the oracle's packing of the blocks `sub` of those rows; their outputs are
     checked against the oracle."""
+    check_sampled_bytes(fmt, packed, sub, rows, n, k)
+    assert_parity(y[:, rows], OF.dequant(fmt, sub), x, f"{fmt} {n}x{k} B={x.shape[0]}")
+    assert np.all(np.isfinite(y))
+
+
+def check_sampled_bytes(fmt, packed, sub, rows, n, k):
+    """Rows `rows` of the full buffer `packed` equal the oracle's packing of `sub`."""
     spec = OF.SPECS[fmt]
     cpr = (k // spec.block) * spec.code_bytes
     mpr = (k // spec.block) * spec.meta_bytes
@@ -204,8 +211,6 @@ def check_sampled_rows(fmt, packed, sub, rows, n, k, x, y):
     scp = OF.codes_plane_size(fmt, len(rows), k)
     np.testing.assert_array_equal(codes_rows[rows], OF.deinterleave_rows(sub_packed[:scp], len(rows), cpr))
     np.testing.assert_array_equal(meta_rows[rows], OF.deinterleave_rows(sub_packed[scp:], len(rows), mpr))
-    assert_parity(y[:, rows], OF.dequant(fmt, sub), x, f"{fmt} {n}x{k} B={x.shape[0]}")
-    assert np.all(np.isfinite(y))
 
 
 @pytest.mark.parametrize("n,k", [(4096, 4096), (14336, 4096)])

@@ -1,0 +1,130 @@
+"""GPU parity of the RMS-normalising GEMV (qgemv_rmsnorm) against the oracle,
+through the C ABI: every format, batches 1..8, ragged row groups, K tails of
+the 32-weight formats, the widest workgroup, the eps edge cases, and the
+decode layer's full projection shapes on sampled rows."""
+import numpy as np
+import pytest
+
+import block_quantized_decode_qgemv_amd as qg
+import workloads
+from oracle import formats as OF
+from oracle import norm as ON
+
+from .test_gpu_gemv import check_sampled_bytes, dev, full_weights, make_blocks, sampled_rows
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+def residual_stream(b, k, seed, tid):
+    """Activations entering a norm: a residual stream well away from unit RMS."""
+    return (workloads.normal((b, k), seed, tid) * np.float32(6.0)).astype(np.float32)
+
+
+def gain(k, seed, tid):
+    return (1.0 + 0.25 * workloads.normal((1, k), seed, tid)[0]).astype(np.float32)
+
+
+def run_norm(fmt, packed, x, gamma, eps, n, k):
+    b = x.shape[0]
+    y_d = torch.full((b, n), float("nan"), device="cuda")
+    qg.qgemv_rmsnorm(fmt, dev(packed), dev(x), dev(gamma), eps, y_d, n, k, b)
+    torch.cuda.synchronize()
+    return y_d.cpu().numpy()
+
+
+def assert_norm_parity(y, w_deq, x, gamma, eps, label):
+    ok, ratio, idx = ON.check(y, w_deq, x, gamma, eps)
+    assert ok, f"{label}: worst |err|/tol = {ratio:.3g} at {idx}"
+
+
+SHAPES = [(1, 1), (67, 4), (130, 16), (9, 56)]  # (N, K in blocks of 256)
+
+
+@pytest.mark.parametrize("fmt", OF.FORMATS)
+@pytest.mark.parametrize("b", [1, 2, 3, 8])
+@pytest.mark.parametrize("n,kb", SHAPES)
+def test_rmsnorm_gemv_parity(fmt, b, n, kb):
+    k = 256 * kb
+    blk = make_blocks(fmt, n, k, seed=21, tid=5 * n + kb)
+    x, g = residual_stream(b, k, 21, 400 + b), gain(k, 21, 500 + kb)
+    y = run_norm(fmt, OF.pack(fmt, blk), x, g, 1e-6, n, k)
+    assert_norm_parity(y, OF.dequant(fmt, blk), x, g, 1e-6, f"{fmt} B={b} N={n} K={k}")
+
+
+@pytest.mark.parametrize("fmt", OF.FORMATS)
+@pytest.mark.parametrize("b", [1, 5, 8])
+def test_rmsnorm_gemv_widest_workgroup(fmt, b):
+    """K = 16384: the widest workgroup and, at larger batches, several K
+    slices whose sums of squares are combined across waves."""
+    n, k = 33, 16384
+    blk = make_blocks(fmt, n, k, seed=22, tid=b)
+    x, g = residual_stream(b, k, 22, b), gain(k, 22, 99)
+    y = run_norm(fmt, OF.pack(fmt, blk), x, g, 1e-5, n, k)
+    assert_norm_parity(y, OF.dequant(fmt, blk), x, g, 1e-5, f"{fmt} B={b} N={n} K={k}")
+
+
+@pytest.mark.parametrize("fmt", ["q8_0", "q4_0", "q4_1"])
+@pytest.mark.parametrize("k", [32, 160, 4064])
+def test_rmsnorm_gemv_short_blocks(fmt, k):
+    """32-weight formats at K off the 256 grid: the sum of squares must cover
+    the ragged tail once, like the dot products."""
+    n = 37
+    blk = make_blocks(fmt, n, k, seed=23, tid=k)
+    x, g = residual_stream(3, k, 23, k), gain(k, 23, k + 1)
+    y = run_norm(fmt, OF.pack(fmt, blk), x, g, 1e-6, n, k)
+    assert_norm_parity(y, OF.dequant(fmt, blk), x, g, 1e-6, f"{fmt} N={n} K={k}")
+
+
+@pytest.mark.parametrize("fmt", ["q4_k", "q8_0"])
+def test_rmsnorm_gemv_eps_cases(fmt):
+    """eps = 0 on nonzero rows; a zero row with eps > 0 gives exactly zero;
+    a tiny-RMS row where eps dominates; a zero row with eps = 0 is 0/0."""
+    n, k = 20, 1024
+    blk = make_blocks(fmt, n, k, seed=24)
+    packed, w_deq = OF.pack(fmt, blk), OF.dequant(fmt, blk)
+    g = gain(k, 24, 1)
+    x = residual_stream(3, k, 24, 2)
+    x[1] = 0.0
+    x[2] *= np.float32(1e-4)
+    y = run_norm(fmt, packed, x, g, 0.5, n, k)
+    assert_norm_parity(y, w_deq, x, g, 0.5, f"{fmt} eps=0.5")
+    assert np.all(y[1] == 0.0)
+    y0 = run_norm(fmt, packed, x[[0, 2]], g, 0.0, n, k)
+    assert_norm_parity(y0, w_deq, x[[0, 2]], g, 0.0, f"{fmt} eps=0")
+    yz = run_norm(fmt, packed, x[[1]], g, 0.0, n, k)
+    assert np.all(np.isnan(yz))
+
+
+def test_rmsnorm_gemv_deterministic():
+    n, k = 300, 4096
+    blk = make_blocks("q4_k", n, k, seed=25)
+    packed = dev(OF.pack("q4_k", blk))
+    x, g = dev(residual_stream(2, k, 25, 1)), dev(gain(k, 25, 2))
+    ys = []
+    for _ in range(3):
+        y = torch.empty((2, n), device="cuda")
+        qg.qgemv_rmsnorm("q4_k", packed, x, g, 1e-6, y, n, k, 2)
+        ys.append(y)
+    torch.cuda.synchronize()
+    assert all(torch.equal(ys[0], t) for t in ys[1:])
+
+
+@pytest.mark.parametrize("n,k", [(14336, 4096), (4096, 4096), (1024, 4096)])
+@pytest.mark.parametrize("fmt", ["q4_k", "q8_0"])
+@pytest.mark.parametrize("b", [1, 8])
+def test_rmsnorm_gemv_full_size_sampled_rows(fmt, n, k, b):
+    """The projections a decode layer feeds from its norms (gate/up, q/o,
+    k/v), at full size with the C++ quantizer's buffer; sampled rows are
+    re-quantized by the oracle, checked byte for byte, and checked against
+    the oracle's normalised GEMV."""
+    w = full_weights(n, k)
+    packed = qg.qquant(fmt, w)
+    x, g = residual_stream(b, k, 26, b), gain(k, 26, 0)
+    y = run_norm(fmt, packed, x, g, 1e-5, n, k)
+    rows = sampled_rows(n, 3 * n + b)
+    sub = OF.quantize(fmt, w[rows])
+    check_sampled_bytes(fmt, packed, sub, rows, n, k)
+    assert_norm_parity(y[:, rows], OF.dequant(fmt, sub), x, g, 1e-5, f"{fmt} {n}x{k} B={b}")
+    assert np.all(np.isfinite(y))
