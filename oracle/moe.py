@@ -80,10 +80,25 @@ def sigmoid(z):
         return 1.0 / (1.0 + np.exp(-z))
 
 
+def _rows(x) -> np.ndarray:
+    """Activation rows as float64 [B, H]: fp32 inputs widened exactly, float64
+    inputs (an activation the oracle itself computed, such as a normalised x)
+    taken as they are, without rounding to fp32."""
+    a = np.atleast_2d(np.asarray(x))
+    if a.dtype != np.float64:
+        a = a.astype(np.float32)
+    return a.astype(np.float64)
+
+
+def _gemv64(w, x) -> np.ndarray:
+    """W x over the rows of x, exact products, float64 sums."""
+    return _rows(x) @ np.asarray(w, np.float32).astype(np.float64).T
+
+
 def expert_forward(wg, wu, wd, x):
     """One expert on activation rows x [B, H]: returns (g, u, h, o), float64."""
-    g = _gemv.gemv_ref(wg, x)
-    u = _gemv.gemv_ref(wu, x)
+    g = _gemv64(wg, x)
+    u = _gemv64(wu, x)
     h = silu(g) * u
     o = np.asarray(h, np.float64) @ np.asarray(wd, np.float32).astype(np.float64).T
     return g, u, h, o
@@ -93,7 +108,7 @@ def moe_ref(w_gate, w_up, w_down, x, residual, logits, shared_logit, top_k: int,
     """Full layer.  w_gate/w_up: [E+1] of [I, H]; w_down: [E+1] of [H, I]
     (expert E is the shared one); x, residual: [T, H]; logits: [T, E];
     shared_logit: [T].  Returns a dict with out [T, H] and the intermediates."""
-    x = np.atleast_2d(np.asarray(x, np.float32))
+    x = _rows(x)
     t = x.shape[0]
     e = len(w_gate) - 1
     ids, w, _ = route(logits, top_k, renorm)
@@ -120,12 +135,14 @@ COMBINE_REL = 2e-6   # fp32 softmax over E terms, sigmoid, and the 6-term combin
 ACT_REL = 1e-6       # fp32 silu(g) * u beyond the propagated GEMV errors
 
 
-def h_tolerance(wg, wu, x):
-    """Bound on |h_gpu - h_ref| for one expert and activation rows x."""
-    g = _gemv.gemv_ref(wg, x)
-    u = _gemv.gemv_ref(wu, x)
-    dg = _gemv.tolerance(wg, x)
-    du = _gemv.tolerance(wu, x)
+def h_tolerance(wg, wu, x, rel: float = _gemv.REL_TOL):
+    """Bound on |h_gpu - h_ref| for one expert and activation rows x, the
+    gate/up GEMVs within rel * sum |w x| + ABS_TOL."""
+    g = _gemv64(wg, x)
+    u = _gemv64(wu, x)
+    ax = np.abs(_rows(x))
+    dg = rel * (ax @ np.abs(np.asarray(wg, np.float32).astype(np.float64)).T) + _gemv.ABS_TOL
+    du = rel * (ax @ np.abs(np.asarray(wu, np.float32).astype(np.float64)).T) + _gemv.ABS_TOL
     s = sigmoid(g)
     dsilu = s * (1.0 + g * (1.0 - s))
     h = silu(g) * u
@@ -140,8 +157,9 @@ def o_tolerance(wd, h, dh):
     return _gemv.REL_TOL * (np.abs(h) @ wd64.T) + dh @ wd64.T + _gemv.ABS_TOL
 
 
-def out_tolerance(w_gate, w_up, w_down, x, residual, ref) -> np.ndarray:
-    x = np.atleast_2d(np.asarray(x, np.float32))
+def out_tolerance(w_gate, w_up, w_down, x, residual, ref, rel: float = _gemv.REL_TOL) -> np.ndarray:
+    """Bound on |out_gpu - out_ref|; rel is the gate/up GEMV bound's relative part."""
+    x = _rows(x)
     t = x.shape[0]
     top_k = ref["ids"].shape[1]
     e = len(w_gate) - 1
@@ -152,7 +170,7 @@ def out_tolerance(w_gate, w_up, w_down, x, residual, ref) -> np.ndarray:
         acc = np.zeros(x.shape[1])
         mag = np.abs(np.asarray(residual, np.float32)[i].astype(np.float64))
         for k, ex in enumerate(slots):
-            dh = h_tolerance(w_gate[ex], w_up[ex], x[i:i + 1])
+            dh = h_tolerance(w_gate[ex], w_up[ex], x[i:i + 1], rel)
             do = o_tolerance(w_down[ex], ref["h"][i, k][None], dh)[0]
             acc += coef[k] * do
             mag += coef[k] * np.abs(ref["o"][i, k])

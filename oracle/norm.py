@@ -27,6 +27,11 @@ rest covers the fp32 sum of squares (a sum of K positive terms, whose
 relative error is at most its longest sequential chain times the unit
 roundoff, halved by the square root) and the fp32 square root and products.
 
+The MoE layer fed through the same norm (every expert sees xhat; the
+residual is the caller's, the un-normalised x in a pre-norm block) is the
+moe oracle applied to the float64 xhat, with the gate/up GEMV bound widened
+to this module's.
+
 Parity: pinned by hand-computed vectors, closed forms (constant x gives the
 row sums of W; a zero vector gives zero with eps > 0), the invariants of the
 definition (scale invariance with eps = 0; unit mean square of xhat with
@@ -36,6 +41,8 @@ separately pinned GEMV oracle.
 from __future__ import annotations
 
 import numpy as np
+
+from . import moe as _moe
 
 REL_TOL = 3e-5
 ABS_TOL = 1e-7
@@ -74,3 +81,14 @@ def check(y, w_deq, x, gamma, eps: float):
     idx = np.unravel_index(int(np.argmax(ratio)), ratio.shape)
     return bool(np.all(err <= tol)), float(ratio[idx]), idx
 
+
+
+def moe_rmsnorm_ref(w_gate, w_up, w_down, x, gamma, eps: float, residual, logits, shared_logit, top_k: int,
+                    renorm: bool = False):
+    """The routed expert layer on rmsnorm(x) (see oracle.moe.moe_ref)."""
+    return _moe.moe_ref(w_gate, w_up, w_down, rmsnorm_ref(x, gamma, eps), residual, logits, shared_logit,
+                        top_k, renorm)
+
+
+def moe_rmsnorm_tolerance(w_gate, w_up, w_down, x, gamma, eps: float, residual, ref) -> np.ndarray:
+    return _moe.out_tolerance(w_gate, w_up, w_down, rmsnorm_ref(x, gamma, eps), residual, ref, rel=REL_TOL)

@@ -153,3 +153,52 @@ def test_planted_mistake_fails_a_pin(mutant):
     with np.errstate(all="ignore"):  # centring a constant row divides 0 by 0
         failed = [p.__name__ for p in PINS if not p(mutant)]
     assert failed, f"{mutant.__name__} passes every pin"
+
+
+# ------------------------------------------------------- norm-fed MoE layer
+
+def _moe_case(t=3, e=6, h=64, i=32, seed=40):
+    from oracle import moe as OM
+
+    rng = np.random.default_rng(seed)
+    wg = [rng.standard_normal((i, h)).astype(F32) * F32(0.1) for _ in range(e + 1)]
+    wu = [rng.standard_normal((i, h)).astype(F32) * F32(0.1) for _ in range(e + 1)]
+    wd = [rng.standard_normal((h, i)).astype(F32) * F32(0.1) for _ in range(e + 1)]
+    x = rng.standard_normal((t, h)).astype(F32) * F32(3)
+    res = rng.standard_normal((t, h)).astype(F32)
+    logits = rng.standard_normal((t, e)).astype(F32)
+    s = rng.standard_normal(t).astype(F32)
+    return OM, wg, wu, wd, x, res, logits, s
+
+
+def test_moe_norm_reduces_to_moe_on_unit_rms_rows():
+    """x of +-1 entries has RMS 1: with gamma = 1 and eps = 0 the norm is the
+    identity and the layer equals the (separately pinned) MoE oracle."""
+    OM, wg, wu, wd, x, res, logits, s = _moe_case()
+    x = np.sign(x).astype(F32)
+    got = ON.moe_rmsnorm_ref(wg, wu, wd, x, np.ones(x.shape[1], F32), 0.0, res, logits, s, 2)["out"]
+    want = OM.moe_ref(wg, wu, wd, x, res, logits, s, 2)["out"]
+    assert _close(got, want, 1e-12)
+
+
+def test_moe_norm_scale_invariant_and_exact_xhat():
+    """Scaling x by 8 (eps = 0) leaves every expert input and so the layer
+    unchanged; and the experts see the float64 xhat unrounded (the result
+    differs from feeding them xhat rounded to fp32)."""
+    OM, wg, wu, wd, x, res, logits, s = _moe_case(seed=41)
+    g = (1 + 0.25 * np.random.default_rng(1).standard_normal(x.shape[1])).astype(F32)
+    a = ON.moe_rmsnorm_ref(wg, wu, wd, x, g, 0.0, res, logits, s, 3)["out"]
+    b = ON.moe_rmsnorm_ref(wg, wu, wd, x * F32(8), g, 0.0, res, logits, s, 3)["out"]
+    assert _close(a, b, 1e-12)
+    xh = ON.rmsnorm_ref(x, g, 0.0)
+    assert _close(a, OM.moe_ref(wg, wu, wd, xh, res, logits, s, 3)["out"], 0.0)
+    assert not np.array_equal(a, OM.moe_ref(wg, wu, wd, xh.astype(F32), res, logits, s, 3)["out"])
+
+
+def test_moe_norm_tolerance_widens_gate_up_bound():
+    OM, wg, wu, wd, x, res, logits, s = _moe_case(seed=42)
+    g = np.ones(x.shape[1], F32)
+    ref = ON.moe_rmsnorm_ref(wg, wu, wd, x, g, 1e-6, res, logits, s, 2)
+    wide = ON.moe_rmsnorm_tolerance(wg, wu, wd, x, g, 1e-6, res, ref)
+    narrow = OM.out_tolerance(wg, wu, wd, ON.rmsnorm_ref(x, g, 1e-6), res, ref)
+    assert np.all(wide > narrow) and np.all(np.isfinite(wide))
