@@ -237,26 +237,46 @@ def dense_step(torch, qg, stream):
         launches += [gemv(layer["qkv"], 6144, 4096), gemv(layer["o"], 4096, 4096),
                      gemv(layer["gateup"], 28672, 4096), gemv(layer["down"], 4096, 14336)]
     t_fused, _ = graph_time(torch, stream, launches, 20)
-    del dev, launches
+    # the same with each layer's two RMS norms folded into the projections
+    # they feed (attention norm -> q/k/v, FFN norm -> gate/up)
+    gammas = [workloads.normal_device((2, 4096), 0, 900 + j) * 0.25 + 1.0 for j in range(DENSE_LAYERS)]
+
+    def gemv_norm(w, n, k, gamma):
+        wp, xp, yp, gp = w.data_ptr(), xs[k].data_ptr(), ys[n].data_ptr(), gamma.data_ptr()
+        return lambda: lib.qgemv_rmsnorm(fid, wp, xp, gp, 1e-5, yp, n, k, 1, sp)
+
+    launches = []
+    for layer, gm in zip(dev, gammas):
+        launches += [gemv_norm(layer["qkv"], 6144, 4096, gm[0]), gemv(layer["o"], 4096, 4096),
+                     gemv_norm(layer["gateup"], 28672, 4096, gm[1]), gemv(layer["down"], 4096, 14336)]
+    t_norm, _ = graph_time(torch, stream, launches, 20)
+    del dev, launches, gammas
     torch.cuda.empty_cache()
     return {"layers": DENSE_LAYERS, "bytes": total,
             "launches": DENSE_LAYERS * len(DENSE_LAYER), "step_us": round(t * 1e6, 1),
             "tok_s": round(1.0 / t, 1), "GBps": round(total / t / 1e9, 1),
             "fused_launches": DENSE_LAYERS * 4, "fused_step_us": round(t_fused * 1e6, 1),
-            "fused_tok_s": round(1.0 / t_fused, 1), "fused_GBps": round(total / t_fused / 1e9, 1)}
+            "fused_tok_s": round(1.0 / t_fused, 1), "fused_GBps": round(total / t_fused / 1e9, 1),
+            "fused_with_norms_step_us": round(t_norm * 1e6, 1), "fused_with_norms_tok_s": round(1.0 / t_norm, 1)}
 
 
 MOE_E, MOE_H, MOE_I, MOE_TOPK, MOE_POOL, MOE_SETS = 512, 4096, 1024, 4, 8, 32
 
 
-def moe_layer(torch, qg, stream, fmt, t_tokens):
+def moe_layer(torch, qg, stream, fmt, t_tokens, norm=False):
     """The MoE layer (512 experts + 1 shared, hidden 4096, intermediate 1024,
     top-4) at T tokens, every expert resident.  Experts are distinct device
     copies of a pool of MOE_POOL drawn experts (the pool repeats every
     MOE_POOL slots; 2-3.6 GB in all, beyond the cache).  MOE_SETS router and
     shared-gate logit sets are drawn; one graph replays a call per set, so
     every call routes anew.  Bytes per call: the distinct experts it touches
-    (plus the shared one), gate/up and down."""
+    (plus the shared one), gate/up and down.
+
+    norm=True times the layer as a pre-norm block step instead: the router
+    projection (Q8_0 [E][H]) fed by the RMS norm of the block input, then the
+    expert layer on the normalised input with the block input as residual;
+    MOE_SETS input sets, so every call routes anew.  Its bytes add the
+    router's."""
     import workloads
 
     lib = qg.load()
@@ -288,14 +308,41 @@ def moe_layer(torch, qg, stream, fmt, t_tokens):
                 logits[r].data_ptr(), slog[r].data_ptr(), t_tokens, 0, out.data_ptr(), ws.data_ptr(), ws_bytes, sp)
         return lambda: lib.moe_expert_ffn(*args)
 
-    t, _ = graph_time(torch, stream, [call(r) for r in range(MOE_SETS)], 10)
+    router_bytes = 0
+    if norm:
+        q8 = qg.FORMATS["q8_0"]
+        router = torch.from_numpy(qg.qquant("q8_0", workloads.student_t_weights_device(e_, h_, 1, 77).cpu().numpy(),
+                                            n_threads=16)).to("cuda")
+        router_bytes = router.numel()
+        gamma = workloads.normal_device((h_,), 2, 78) * 0.25 + 1.0
+        xs = [workloads.normal_device((t_tokens, h_), 2, 300 + r) * 6.0 for r in range(MOE_SETS)]
+
+        def call_norm(r):
+            def fn():
+                rc = lib.qgemv_rmsnorm(q8, router.data_ptr(), xs[r].data_ptr(), gamma.data_ptr(), 1e-6,
+                                       logits[r].data_ptr(), e_, h_, t_tokens, sp)
+                rc = rc or lib.moe_expert_ffn_rmsnorm(fid, gu.data_ptr(), dn.data_ptr(), e_, h_, i_, k_,
+                                                      xs[r].data_ptr(), gamma.data_ptr(), 1e-6, xs[r].data_ptr(),
+                                                      logits[r].data_ptr(), slog[r].data_ptr(), t_tokens, 0,
+                                                      out.data_ptr(), ws.data_ptr(), ws_bytes, sp)
+                if rc:
+                    raise RuntimeError(f"MoE block step failed with {rc}")
+            return fn
+
+        for r in range(MOE_SETS):
+            call_norm(r)()  # the logits the step's routes come from
+        torch.cuda.synchronize()
+        t, _ = graph_time(torch, stream, [call_norm(r) for r in range(MOE_SETS)], 10)
+    else:
+        t, _ = graph_time(torch, stream, [call(r) for r in range(MOE_SETS)], 10)
     t /= MOE_SETS
     touched = np.mean([len(set(np.argsort(-lg.cpu().numpy(), axis=1, kind="stable")[:, :k_].ravel().tolist())) + 1
                        for lg in logits])
-    nbytes = touched * (gu_sz + dn_sz)
+    nbytes = touched * (gu_sz + dn_sz) + router_bytes
     del gu, dn, ws
     torch.cuda.empty_cache()
-    return {"fmt": fmt, "T": t_tokens, "us": round(t * 1e6, 2), "experts_touched": round(float(touched), 2),
+    return {"fmt": fmt, "T": t_tokens, "norm_block": norm, "us": round(t * 1e6, 2),
+            "experts_touched": round(float(touched), 2),
             "bytes": int(nbytes), "GBps": round(float(nbytes) / t / 1e9, 1)}
 
 
@@ -471,6 +518,9 @@ def main():
             for t_tokens in (1, 8):
                 rows.append(moe_layer(torch, qg, stream, fmt, t_tokens))
                 log(f"  moe {rows[-1]}")
+        for t_tokens in (1, 8):
+            rows.append(moe_layer(torch, qg, stream, "q4_k", t_tokens, norm=True))
+            log(f"  moe {rows[-1]}")
         extra["moe_layer"] = rows
     extra["hbm_read_probe"] = read_probe(torch, qg, stream, head)
     extra["headline_frac_of_read_probe"] = round(achieved / extra["hbm_read_probe"]["same_size_GBps"], 4)

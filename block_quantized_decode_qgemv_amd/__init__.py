@@ -24,7 +24,7 @@ __all__ = [
     "qg_packed_size", "qg_codes_plane_size", "qg_codes_plane_offset", "qg_block_size", "qgemv_workspace_size",
     "qgemv", "qgemv_q8_0", "qgemv_q4_0", "qgemv_q4_1", "qgemv_q4k", "qgemv_q2k",
     "qgemv_tern", "qgemv_bin", "qgemv_rmsnorm", "qg_dequant", "qquant", "qpack_tern", "qpack_bin",
-    "moe_expert_ffn_workspace_size", "moe_expert_ffn", "qg_strerror", "qg_last_error",
+    "moe_expert_ffn_workspace_size", "moe_expert_ffn", "moe_expert_ffn_rmsnorm", "qg_strerror", "qg_last_error",
     "qg_version", "EXPORTED_SYMBOLS",
 ]
 
@@ -63,6 +63,8 @@ _SIGNATURES = {
     "moe_expert_ffn_workspace_size": (_sz, [_i32, _i32, _i32, _i32, _i32]),
     "moe_expert_ffn": (_i32, [_i32, _vp, _vp, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _i32, _u32,
                               _vp, _vp, _sz, _vp]),
+    "moe_expert_ffn_rmsnorm": (_i32, [_i32, _vp, _vp, _i32, _i32, _i32, _i32, _vp, _vp, ctypes.c_float, _vp, _vp,
+                                      _vp, _i32, _u32, _vp, _vp, _sz, _vp]),
     "qg_hbm_read_probe": (_i32, [_vp, _sz, _vp, _vp]),
     "qg_strerror": (_cp, [_i32]),
     "qg_last_error": (_cp, []),
@@ -296,3 +298,17 @@ def moe_expert_ffn(fmt, w_gate_up, w_down, e: int, h: int, i: int, top_k: int, x
                                _dev(out, f32, "out"), _dev(workspace, None, "workspace"), ws_bytes,
                                _stream(stream))
     _check(rc, "moe_expert_ffn")
+
+
+def moe_expert_ffn_rmsnorm(fmt, w_gate_up, w_down, e: int, h: int, i: int, top_k: int, x, gamma, eps: float,
+                           residual, router_logits, shared_gate_logit, t: int, out, workspace, ws_bytes: int,
+                           flags: int = 0, stream=None) -> None:
+    """Routed expert layer on RMS-normalised x (see moe_expert_ffn_rmsnorm in qgemv.h)."""
+    f32, u8 = _torch_dtypes()
+    rc = load().moe_expert_ffn_rmsnorm(_fmt(fmt), _dev(w_gate_up, u8, "w_gate_up"), _dev(w_down, u8, "w_down"),
+                                       e, h, i, top_k, _dev(x, f32, "x"), _dev(gamma, f32, "gamma"), float(eps),
+                                       _dev(residual, f32, "residual"), _dev(router_logits, f32, "router_logits"),
+                                       _dev(shared_gate_logit, f32, "shared_gate_logit"), t, flags,
+                                       _dev(out, f32, "out"), _dev(workspace, None, "workspace"), ws_bytes,
+                                       _stream(stream))
+    _check(rc, "moe_expert_ffn_rmsnorm")

@@ -623,6 +623,14 @@ struct GemvDpp {
 
                 // (1) x of the part, four columns per lane per span
                 float4 xv[B][NX4];
+                float4 gv[NORM ? NX4 : 1];  // gamma of the same columns (NORM)
+                if constexpr (NORM) {
+#pragma unroll
+                    for (int m = 0; m < NX4; ++m) {
+                        const uint32_t c = (uint32_t)(FULL ? k0 + 64 * m + 4 * r : min(k0 + 64 * m + 4 * r, K - 4));
+                        gv[m] = *(const float4*)((const uint8_t*)gamma + c * 4u);
+                    }
+                }
 #pragma unroll
                 for (int b = 0; b < B; ++b) {
                     if (b < nb) {
@@ -633,14 +641,21 @@ struct GemvDpp {
                             // only meet code units whose contributions are dropped
                             const uint32_t c = (uint32_t)(FULL ? k0 + 64 * m + 4 * r : min(k0 + 64 * m + 4 * r, K - 4));
                             xv[b][m] = *(const float4*)((const uint8_t*)xb + c * 4u);
-                            if constexpr (NORM) {
-                                const float4 v = xv[b][m];
-                                // each column once: the lanes of a part tile it, parts are disjoint
-                                if (FULL || k0 + 64 * m + 4 * r < K)
-                                    ss[b] += (v.x * v.x + v.y * v.y) + (v.z * v.z + v.w * v.w);
-                                const float4 gm4 = *(const float4*)((const uint8_t*)gamma + c * 4u);
-                                xv[b][m] = make_float4(v.x * gm4.x, v.y * gm4.y, v.z * gm4.z, v.w * gm4.w);
-                            }
+                        }
+                    }
+                }
+                if constexpr (NORM) {
+#pragma unroll
+                    for (int b = 0; b < B; ++b) {
+                        if (b >= nb) continue;
+#pragma unroll
+                        for (int m = 0; m < NX4; ++m) {
+                            const float4 v = xv[b][m], g4 = gv[m];
+                            // each column once: the lanes of a part tile it, parts are
+                            // disjoint, and clamped columns past K are not added
+                            const float sq = fmaf(v.w, v.w, fmaf(v.z, v.z, fmaf(v.y, v.y, fmaf(v.x, v.x, ss[b]))));
+                            if (FULL || k0 + 64 * m + 4 * r < K) ss[b] = sq;
+                            xv[b][m] = make_float4(v.x * g4.x, v.y * g4.y, v.z * g4.z, v.w * g4.w);
                         }
                     }
                 }
@@ -792,7 +807,9 @@ struct GemvDpp {
                     float q = 0.0f;
 #pragma unroll
                     for (int w = 0; w < W; ++w) q += red_ss[w * B + b];
-                    v = v / sqrtf(q / (float)K + eps);
+                    // hardware reciprocal and reciprocal square root (about
+                    // 1 ulp each), well inside the bound's fp32 allowance
+                    v *= __builtin_amdgcn_rsqf(fmaf(q, __builtin_amdgcn_rcpf((float)K), eps));
                 }
                 return v;
             },

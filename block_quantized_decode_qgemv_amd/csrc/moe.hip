@@ -276,11 +276,14 @@ __device__ __forceinline__ Item read_item(const int* items, int j) {
 __device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }
 
 // gate/up rows interleaved: group g holds gate rows 8g..8g+7 (rows 2i) and up
-// rows (rows 2i+1); h[item][b][8g + i] = silu(gate) * up
-template <int F, int W, int KCS>
+// rows (rows 2i+1); h[item][b][8g + i] = silu(gate) * up.  NORM: the token
+// rows are RMS-normalised on the way in (gain gamma, eps), as in the
+// normalising GEMV.
+template <int F, int W, int KCS, bool NORM>
 __global__ void __launch_bounds__(W * 64)
 moe_gate_up_kernel(const uint8_t* __restrict__ wgu, size_t expert_bytes, size_t codes_bytes, int H, int I,
-                   const float* __restrict__ x, const int* __restrict__ items, float* __restrict__ h) {
+                   const float* __restrict__ x, const float* __restrict__ gamma, float eps,
+                   const int* __restrict__ items, float* __restrict__ h) {
     const int j = blockIdx.y;
     if (j >= items[0]) return;  // uniform: unused item slot
     const Item it = read_item(items, j);
@@ -297,8 +300,13 @@ moe_gate_up_kernel(const uint8_t* __restrict__ wgu, size_t expert_bytes, size_t 
             }
         };
     };
-    if (it.count == 1) GemvDpp<F, 1, W, KCS>::run(codes, meta, 2 * I, H, g, xrow, 1, epi(1));
-    else GemvDpp<F, 2, W, KCS>::run(codes, meta, 2 * I, H, g, xrow, 2, epi(2));
+    if constexpr (NORM) {
+        if (it.count == 1) GemvDpp<F, 1, W, KCS>::run_rmsnorm(codes, meta, 2 * I, H, g, xrow, 1, gamma, eps, epi(1));
+        else GemvDpp<F, 2, W, KCS>::run_rmsnorm(codes, meta, 2 * I, H, g, xrow, 2, gamma, eps, epi(2));
+    } else {
+        if (it.count == 1) GemvDpp<F, 1, W, KCS>::run(codes, meta, 2 * I, H, g, xrow, 1, epi(1));
+        else GemvDpp<F, 2, W, KCS>::run(codes, meta, 2 * I, H, g, xrow, 2, epi(2));
+    }
 }
 
 // down + combine: one workgroup per (16-row group g, token t).  Its waves form
@@ -339,12 +347,12 @@ moe_down_kernel(const uint8_t* __restrict__ wdn, size_t expert_bytes, size_t cod
 
 // ------------------------------------------------------------- launchers
 
-template <int F, int W, int KCS>
-hipError_t launch_gate_up_w(const uint8_t* wgu, int H, int I, const float* x, const int* items, float* h,
-                            int max_items, hipStream_t st) {
+template <int F, int W, int KCS, bool NORM>
+hipError_t launch_gate_up_w(const uint8_t* wgu, int H, int I, const float* x, const float* gamma, float eps,
+                            const int* items, float* h, int max_items, hipStream_t st) {
     const size_t eb = qg_packed_size(F, 2 * (int64_t)I, H), cb = qg_codes_plane_size(F, 2 * (int64_t)I, H);
-    hipLaunchKernelGGL((moe_gate_up_kernel<F, W, KCS>), dim3(2 * I / kRowGroup, max_items), dim3(W * 64), 0, st,
-                       wgu, eb, cb, H, I, x, items, h);
+    hipLaunchKernelGGL((moe_gate_up_kernel<F, W, KCS, NORM>), dim3(2 * I / kRowGroup, max_items), dim3(W * 64), 0,
+                       st, wgu, eb, cb, H, I, x, gamma, eps, items, h);
     return hipGetLastError();
 }
 
@@ -365,10 +373,10 @@ hipError_t launch_route(const float* logits, const float* slogit, int T, int E, 
     return hipGetLastError();
 }
 
-template <int F>
+template <int F, bool NORM>
 hipError_t launch_moe(const uint8_t* wgu, const uint8_t* wdn, int E, int H, int I, int top_k, const float* x,
-                      const float* residual, const float* logits, const float* slogit, int T, unsigned flags,
-                      float* out, uint8_t* ws, hipStream_t st) {
+                      const float* gamma, float eps, const float* residual, const float* logits,
+                      const float* slogit, int T, unsigned flags, float* out, uint8_t* ws, hipStream_t st) {
     // register-x GEMVs (items carry at most 2 tokens)
     constexpr int KCS = dpp_lane_units<F, 2>();
     static_assert(dpp_max_batch<F>() >= 2, "two tokens per item");
@@ -386,11 +394,11 @@ hipError_t launch_moe(const uint8_t* wgu, const uint8_t* wdn, int E, int H, int 
     else e = launch_route<64>(logits, slogit, T, E, top_k, flags, items, hsel, st);
     if (e != hipSuccess) return e;
     switch (pick_waves_dpp<F, KCS>(H)) {
-        case 1: e = launch_gate_up_w<F, 1, KCS>(wgu, H, I, x, items, h, L.max_items, st); break;
-        case 2: e = launch_gate_up_w<F, 2, KCS>(wgu, H, I, x, items, h, L.max_items, st); break;
-        case 4: e = launch_gate_up_w<F, 4, KCS>(wgu, H, I, x, items, h, L.max_items, st); break;
-        case 8: e = launch_gate_up_w<F, 8, KCS>(wgu, H, I, x, items, h, L.max_items, st); break;
-        default: e = launch_gate_up_w<F, 16, KCS>(wgu, H, I, x, items, h, L.max_items, st); break;
+        case 1: e = launch_gate_up_w<F, 1, KCS, NORM>(wgu, H, I, x, gamma, eps, items, h, L.max_items, st); break;
+        case 2: e = launch_gate_up_w<F, 2, KCS, NORM>(wgu, H, I, x, gamma, eps, items, h, L.max_items, st); break;
+        case 4: e = launch_gate_up_w<F, 4, KCS, NORM>(wgu, H, I, x, gamma, eps, items, h, L.max_items, st); break;
+        case 8: e = launch_gate_up_w<F, 8, KCS, NORM>(wgu, H, I, x, gamma, eps, items, h, L.max_items, st); break;
+        default: e = launch_gate_up_w<F, 16, KCS, NORM>(wgu, H, I, x, gamma, eps, items, h, L.max_items, st); break;
     }
     if (e != hipSuccess) return e;
     // down waves per slot: what the row needs, within 16 waves for top_k + 1 slots
@@ -419,11 +427,15 @@ size_t moe_expert_ffn_workspace_size(int T, int E, int H, int I, int top_k) {
     return MoeLayout(T, H, I, top_k).total;
 }
 
-int moe_expert_ffn(int fmt, const void* w_gate_up, const void* w_down, int E, int H, int I, int top_k,
+}  // extern "C"
+
+namespace {
+
+// Host validation shared by both MoE entry points (QG_OK or the error set).
+int check_moe_args(int fmt, const void* w_gate_up, const void* w_down, int E, int H, int I, int top_k,
                    const float* x, const float* residual, const float* router_logits,
-                   const float* shared_gate_logit, int T, unsigned flags, float* out,
-                   void* workspace, size_t ws_bytes, void* stream) {
-    clear_error();
+                   const float* shared_gate_logit, int T, unsigned flags, float* out, void* workspace,
+                   size_t ws_bytes) {
     if (fmt != QG_Q4_K && fmt != QG_Q2_K) return fail(QG_EINVAL, "moe_expert_ffn takes Q4_K or Q2_K experts");
     if (!w_gate_up || !w_down || !x || !residual || !router_logits || !shared_gate_logit || !out || !workspace)
         return fail(QG_EINVAL, "null pointer");
@@ -442,15 +454,55 @@ int moe_expert_ffn(int fmt, const void* w_gate_up, const void* w_down, int E, in
     if (ws_bytes < need) return fail(QG_ERANGE, "workspace of %zu bytes is below the %zu needed", ws_bytes, need);
     if ((const void*)out == (const void*)x || (const void*)out == (const void*)residual)
         return fail(QG_EINVAL, "out must not alias x or residual");
+    return QG_OK;
+}
+
+template <bool NORM>
+int moe_call(int fmt, const void* w_gate_up, const void* w_down, int E, int H, int I, int top_k, const float* x,
+             const float* gamma, float eps, const float* residual, const float* router_logits,
+             const float* shared_gate_logit, int T, unsigned flags, float* out, void* workspace, void* stream) {
     const uint8_t* wgu = static_cast<const uint8_t*>(w_gate_up);
     const uint8_t* wdn = static_cast<const uint8_t*>(w_down);
     hipStream_t st = static_cast<hipStream_t>(stream);
     uint8_t* ws = static_cast<uint8_t*>(workspace);
     hipError_t e = fmt == QG_Q4_K
-        ? launch_moe<QG_Q4_K>(wgu, wdn, E, H, I, top_k, x, residual, router_logits, shared_gate_logit, T, flags, out, ws, st)
-        : launch_moe<QG_Q2_K>(wgu, wdn, E, H, I, top_k, x, residual, router_logits, shared_gate_logit, T, flags, out, ws, st);
+        ? launch_moe<QG_Q4_K, NORM>(wgu, wdn, E, H, I, top_k, x, gamma, eps, residual, router_logits,
+                                    shared_gate_logit, T, flags, out, ws, st)
+        : launch_moe<QG_Q2_K, NORM>(wgu, wdn, E, H, I, top_k, x, gamma, eps, residual, router_logits,
+                                    shared_gate_logit, T, flags, out, ws, st);
     if (e != hipSuccess) return fail(QG_EHIP, "MoE launch failed: %s", hipGetErrorString(e));
     return QG_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int moe_expert_ffn(int fmt, const void* w_gate_up, const void* w_down, int E, int H, int I, int top_k,
+                   const float* x, const float* residual, const float* router_logits,
+                   const float* shared_gate_logit, int T, unsigned flags, float* out,
+                   void* workspace, size_t ws_bytes, void* stream) {
+    clear_error();
+    const int rc = check_moe_args(fmt, w_gate_up, w_down, E, H, I, top_k, x, residual, router_logits,
+                                  shared_gate_logit, T, flags, out, workspace, ws_bytes);
+    if (rc) return rc;
+    return moe_call<false>(fmt, w_gate_up, w_down, E, H, I, top_k, x, nullptr, 0.0f, residual, router_logits,
+                           shared_gate_logit, T, flags, out, workspace, stream);
+}
+
+int moe_expert_ffn_rmsnorm(int fmt, const void* w_gate_up, const void* w_down, int E, int H, int I, int top_k,
+                           const float* x, const float* gamma, float eps, const float* residual,
+                           const float* router_logits, const float* shared_gate_logit, int T, unsigned flags,
+                           float* out, void* workspace, size_t ws_bytes, void* stream) {
+    clear_error();
+    const int rc = check_moe_args(fmt, w_gate_up, w_down, E, H, I, top_k, x, residual, router_logits,
+                                  shared_gate_logit, T, flags, out, workspace, ws_bytes);
+    if (rc) return rc;
+    if (!gamma) return fail(QG_EINVAL, "null gamma");
+    if (!aligned(gamma, 16)) return fail(QG_EALIGN, "gamma must be 16-byte aligned");
+    if (!(eps >= 0.0f) || !std::isfinite(eps)) return fail(QG_ERANGE, "eps=%g must be finite and >= 0", (double)eps);
+    return moe_call<true>(fmt, w_gate_up, w_down, E, H, I, top_k, x, gamma, eps, residual, router_logits,
+                          shared_gate_logit, T, flags, out, workspace, stream);
 }
 
 }  // extern "C"

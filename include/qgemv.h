@@ -225,6 +225,25 @@ int moe_expert_ffn(int fmt, const void* w_gate_up, const void* w_down, int E, in
                    const float* shared_gate_logit, int T, unsigned flags, float* out,
                    void* workspace, size_t ws_bytes, void* stream);
 
+/* The same layer fed through an RMS norm: every expert (routed and shared)
+ * sees xhat[t][k] = x[t][k] * gamma[k] / sqrt(mean_k x[t][k]^2 + eps)
+ * instead of x, the norm folded into the gate/up GEMVs as in qgemv_rmsnorm
+ * (Flash-MoE page: the RMS norm's two passes, section "Metal 计算着色器";
+ * the norm in the layer's GPU pipeline ahead of routing and the experts,
+ * section "每层流水线").  In a pre-norm block residual is the un-normalised
+ * x itself (it may alias x); router_logits are the router projection of
+ * xhat, e.g. from qgemv_rmsnorm with the same gamma and eps.
+ *   gamma  DEVICE fp32 [H], 16-byte aligned; eps finite, >= 0.
+ *   Every other argument as for moe_expert_ffn (same workspace size).
+ * Accuracy: the moe_expert_ffn bound with the gate/up GEMV bound widened to
+ * 3e-5 * sum_k |W[n][k] xhat[t][k]| + 1e-7 (the qgemv_rmsnorm bound).
+ * Errors: as moe_expert_ffn, plus QG_EINVAL (null gamma), QG_EALIGN (gamma),
+ * QG_ERANGE (eps). */
+int moe_expert_ffn_rmsnorm(int fmt, const void* w_gate_up, const void* w_down, int E, int H, int I, int top_k,
+                           const float* x, const float* gamma, float eps, const float* residual,
+                           const float* router_logits, const float* shared_gate_logit, int T, unsigned flags,
+                           float* out, void* workspace, size_t ws_bytes, void* stream);
+
 /* ------------------------------------------------------------ measurement */
 
 /* Streaming-read probe: reads `bytes` bytes of DEVICE memory at `buf` with

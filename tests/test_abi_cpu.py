@@ -114,6 +114,27 @@ def test_gemv_rmsnorm_validation():
 
 
 @nogpu
+def test_moe_rmsnorm_validation():
+    import ctypes
+
+    lib = qg.load()
+    ws = qg.moe_expert_ffn_workspace_size(2, 16, 512, 256, 4)
+
+    def call(fmt=3, gamma=P, eps=1e-6, x=P, t=2, ws_bytes=ws):
+        return lib.moe_expert_ffn_rmsnorm(fmt, P, P, 16, 512, 256, 4, x, gamma, ctypes.c_float(eps), P + 64,
+                                          P + 128, P + 192, t, 0, P + 256, P + 512, ws_bytes, None)
+
+    assert call(gamma=None) == -1
+    assert call(gamma=P + 4) == -3
+    assert call(eps=-1.0) == -4
+    assert call(eps=float("nan")) == -4
+    assert call(fmt=0) == -1            # the plain layer's checks come first
+    assert call(t=9) == -4
+    assert call(ws_bytes=ws - 16) == -4
+    assert qg.qg_last_error()
+
+
+@nogpu
 def test_dequant_validation():
     lib = qg.load()
     assert lib.qg_dequant(3, P, P, 0, 256, None) == -2

@@ -14,6 +14,7 @@ import block_quantized_decode_qgemv_amd as qg
 import workloads
 from oracle import formats as OF
 from oracle import moe as OM
+from oracle import norm as ON
 
 pytestmark = pytest.mark.gpu
 
@@ -298,6 +299,88 @@ def test_moe_full_layer(fmt, t):
     out = run_moe(fmt, gu, dn, e, h, i, top_k, x, residual, logits, s)
     assert np.all(np.isfinite(out)), "a kernel read an unselected expert"
     check(out, Layer(pool), x, residual, logits, s, top_k, False, f"{fmt} full T={t}")
+
+
+# ------------------------------------------------- RMS-norm-fed expert layer
+
+def norm_inputs(t, e, h, seed):
+    """A pre-norm block's input (a residual stream, N(0,1)*6), the norm's gain
+    1 + 0.25*N(0,1), and the routing inputs."""
+    x, residual, logits, s = inputs(t, e, h, seed)
+    gamma = (1.0 + 0.25 * workloads.normal((1, h), seed, 9005)[0]).astype(np.float32)
+    return (x * np.float32(6.0)).astype(np.float32), gamma, residual, logits, s
+
+
+def run_moe_norm(fmt, gu_d, dn_d, e, h, i, top_k, x, gamma, eps, residual, logits, s, flags=0,
+                 alias_residual=False):
+    t = x.shape[0]
+    x_d = dev(x)
+    r_d = x_d if alias_residual else dev(residual)
+    out = torch.full((t, h), float("nan"), device="cuda")
+    ws_bytes = qg.moe_expert_ffn_workspace_size(t, e, h, i, top_k)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
+    qg.moe_expert_ffn_rmsnorm(fmt, gu_d, dn_d, e, h, i, top_k, x_d, dev(gamma), eps, r_d, dev(logits), dev(s), t,
+                              out, ws, ws_bytes, flags=flags)
+    torch.cuda.synchronize()
+    return out.cpu().numpy()
+
+
+def check_norm(out, layer, x, gamma, eps, residual, logits, s, top_k, renorm, label):
+    if top_k < logits.shape[1]:
+        assert np.all(OM.route_margin(logits, top_k) > 1e-6), f"{label}: near-tied route; change the seed"
+    wg, wu, wd = layer.view("gate"), layer.view("up"), layer.view("down")
+    ref = ON.moe_rmsnorm_ref(wg, wu, wd, x, gamma, eps, residual, logits, s, top_k, renorm)
+    tol = ON.moe_rmsnorm_tolerance(wg, wu, wd, x, gamma, eps, residual, ref)
+    err = np.abs(out.astype(np.float64) - ref["out"])
+    worst = np.unravel_index(np.argmax(err / tol), err.shape)
+    assert np.all(err <= tol), f"{label}: |err|/tol = {err[worst] / tol[worst]:.3g} at {worst}"
+    return ref
+
+
+@pytest.mark.parametrize("fmt", KFORMATS)
+@pytest.mark.parametrize("t", [1, 3, 8])
+def test_moe_rmsnorm_small(fmt, t):
+    e, h, i, top_k = 16, 512, 256, 4
+    layer, gu, dn = small_layer(fmt, e, h, i, seed=11)
+    x, gamma, residual, logits, s = norm_inputs(t, e, h, seed=150 + t)
+    out = run_moe_norm(fmt, gu, dn, e, h, i, top_k, x, gamma, 1e-6, residual, logits, s)
+    check_norm(out, layer, x, gamma, 1e-6, residual, logits, s, top_k, False, f"{fmt} norm T={t}")
+
+
+@pytest.mark.parametrize("fmt", KFORMATS)
+def test_moe_rmsnorm_pre_norm_block(fmt):
+    """out = x + MoE(rmsnorm(x)): residual aliases x; all 8 tokens share four
+    experts (two-token items), renormalised weights, eps = 1e-5."""
+    e, h, i, top_k, t = 10, 512, 256, 4, 8
+    layer, gu, dn = small_layer(fmt, e, h, i, seed=13)
+    x, gamma, _, logits, s = norm_inputs(t, e, h, seed=350)
+    logits = logits.copy()
+    favourites = [7, 2, 9, 4]
+    for tok in range(t):
+        for rank, ex in enumerate(np.roll(favourites, tok)):
+            logits[tok, ex] = 6.0 - 0.5 * rank
+    out = run_moe_norm(fmt, gu, dn, e, h, i, top_k, x, gamma, 1e-5, x, logits, s, flags=qg.QG_MOE_RENORM,
+                       alias_residual=True)
+    check_norm(out, layer, x, gamma, 1e-5, x, logits, s, top_k, True, f"{fmt} pre-norm block")
+
+
+@pytest.mark.parametrize("fmt", KFORMATS)
+@pytest.mark.parametrize("t", [1, 8])
+def test_moe_rmsnorm_full_layer(fmt, t):
+    e, h, i, top_k = FULL_E, FULL_H, FULL_I, FULL_K
+    x, gamma, residual, logits, s = norm_inputs(t, e, h, seed=650 + t)
+    ids, _, _ = OM.route(logits, top_k)
+    used = sorted(set(ids.reshape(-1).tolist()) | {e})
+    pool = PooledExperts(fmt, seed=21)
+    gu_sz, dn_sz = qg.qg_packed_size(fmt, 2 * i, h), qg.qg_packed_size(fmt, h, i)
+    gu = torch.full(((e + 1) * gu_sz,), 0xFF, dtype=torch.uint8, device="cuda")
+    dn = torch.full(((e + 1) * dn_sz,), 0xFF, dtype=torch.uint8, device="cuda")
+    for ex in used:
+        gu[ex * gu_sz:(ex + 1) * gu_sz].copy_(dev(pool[ex].gu_packed))
+        dn[ex * dn_sz:(ex + 1) * dn_sz].copy_(dev(pool[ex].dn_packed))
+    out = run_moe_norm(fmt, gu, dn, e, h, i, top_k, x, gamma, 1e-6, residual, logits, s)
+    assert np.all(np.isfinite(out)), "a kernel read an unselected expert"
+    check_norm(out, Layer(pool), x, gamma, 1e-6, residual, logits, s, top_k, False, f"{fmt} norm full T={t}")
 
 
 def test_moe_graph_replay():
