@@ -23,7 +23,8 @@ __all__ = [
     "FORMATS", "QG_MOE_RENORM", "QGError", "QGLibraryMissing", "lib_path", "load",
     "qg_packed_size", "qg_codes_plane_size", "qg_codes_plane_offset", "qg_block_size", "qgemv_workspace_size",
     "qgemv", "qgemv_q8_0", "qgemv_q4_0", "qgemv_q4_1", "qgemv_q4k", "qgemv_q2k",
-    "qgemv_tern", "qgemv_bin", "qgemv_rmsnorm", "qg_dequant", "qquant", "qpack_tern", "qpack_bin",
+    "qgemv_tern", "qgemv_bin", "qgemv_rmsnorm", "qg_dequant", "qquant", "qquant_device", "qrequant_workspace_size", "qrequant",
+    "qpack_tern", "qpack_bin",
     "moe_expert_ffn_workspace_size", "moe_expert_ffn", "moe_expert_ffn_rmsnorm", "qg_strerror", "qg_last_error",
     "qg_version", "EXPORTED_SYMBOLS",
 ]
@@ -58,6 +59,9 @@ _SIGNATURES = {
     "qgemv_rmsnorm": (_i32, [_i32, _vp, _vp, _vp, ctypes.c_float, _vp, _i64, _i64, _i32, _vp]),
     "qg_dequant": (_i32, [_i32, _vp, _vp, _i64, _i64, _vp]),
     "qquant": (_i32, [_i32, _vp, _i64, _i64, _vp, _i32]),
+    "qquant_device": (_i32, [_i32, _vp, _i64, _i64, _vp, _vp, _vp]),
+    "qrequant_workspace_size": (_sz, [_i64, _i64]),
+    "qrequant": (_i32, [_i32, _vp, _i32, _vp, _i64, _i64, _vp, _sz, _vp, _vp]),
     "qpack_tern": (_i32, [_vp, _vp, _i64, _i64, _vp]),
     "qpack_bin": (_i32, [_vp, _vp, _i64, _i64, _vp]),
     "moe_expert_ffn_workspace_size": (_sz, [_i32, _i32, _i32, _i32, _i32]),
@@ -240,6 +244,27 @@ def qgemv_rmsnorm(fmt, w, x, gamma, eps: float, y, n: int, k: int, b: int = 1, s
     rc = load().qgemv_rmsnorm(_fmt(fmt), _dev(w, u8, "w"), _dev(x, f32, "x"), _dev(gamma, f32, "gamma"),
                               float(eps), _dev(y, f32, "y"), n, k, b, _stream(stream))
     _check(rc, "qgemv_rmsnorm")
+
+
+def qquant_device(fmt, w, out, n: int, k: int, status, stream=None) -> None:
+    """Quantize fp32 device weights into packed device bytes (see qquant_device
+    in qgemv.h); `status` (a device int32) reports device-side failures."""
+    f32, u8 = _torch_dtypes()
+    rc = load().qquant_device(_fmt(fmt), _dev(w, f32, "w"), n, k, _dev(out, u8, "out"), _dev(status, None, "status"),
+                              _stream(stream))
+    _check(rc, "qquant_device")
+
+
+def qrequant_workspace_size(n: int, k: int) -> int:
+    return load().qrequant_workspace_size(n, k)
+
+
+def qrequant(src_fmt, src, dst_fmt, dst, n: int, k: int, workspace, ws_bytes: int, status, stream=None) -> None:
+    """Decode src and quantize it to dst_fmt on the device (see qrequant in qgemv.h)."""
+    _, u8 = _torch_dtypes()
+    rc = load().qrequant(_fmt(src_fmt), _dev(src, u8, "src"), _fmt(dst_fmt), _dev(dst, u8, "dst"), n, k,
+                         _dev(workspace, None, "workspace"), ws_bytes, _dev(status, None, "status"), _stream(stream))
+    _check(rc, "qrequant")
 
 
 def qg_dequant(fmt, w, out, n: int, k: int, stream=None) -> None:

@@ -189,6 +189,37 @@ int qg_dequant(int fmt, const void* w, float* out, int64_t N, int64_t K, void* s
  * scale or min overflows fp16; out_host is then unspecified). */
 int qquant(int fmt, const float* w_host, int64_t N, int64_t K, void* out_host, int n_threads);
 
+/* Device quantizer: the same quantizers as qquant (byte-identical output),
+ * run on weights already in device memory.
+ *   w       DEVICE fp32 [N][K] row-major, 4-byte aligned.
+ *   out     DEVICE, qg_packed_size(fmt, N, K) bytes, 16-byte aligned.
+ *   status  DEVICE int, 4-byte aligned: set to QG_OK by the call, then to a
+ *           negative code if a block fails on the device -- QG_EINVAL (a
+ *           non-finite weight) or QG_ERANGE (a scale or min overflows fp16);
+ *           with several failures it holds the smallest code.  The blocks
+ *           that fail leave their bytes of out unspecified.
+ * fmt Q8_0, Q4_0, Q4_1, Q4_K or Q2_K (TERN and BIN: QG_EUNSUPPORTED; the
+ * pages give no ternarizer or binarizer).  Asynchronous on `stream`; read
+ * status after synchronising.  Host errors: QG_EINVAL, QG_ESHAPE, QG_EALIGN,
+ * QG_EUNSUPPORTED, QG_EHIP. */
+int qquant_device(int fmt, const float* w, int64_t N, int64_t K, void* out, int* status, void* stream);
+
+/* Device re-quantizer: decode a packed src matrix (any format) and quantize
+ * it to dst_fmt, as qg_dequant followed by qquant_device -- e.g. 4-bit
+ * experts re-quantized to 2 bits, which the Flash-MoE page does offline
+ * (sections "性能表现" and "项目结构": its 2-bit experts come from the
+ * 4-bit ones).
+ *   src        DEVICE packed [N][K] of src_fmt, 16-byte aligned.
+ *   dst        DEVICE packed [N][K] of dst_fmt, 16-byte aligned.
+ *   workspace  DEVICE scratch of >= qrequant_workspace_size(N, K) bytes
+ *              (the decoded fp32 matrix), 16-byte aligned.
+ *   status     as for qquant_device.
+ * src, dst and workspace must not overlap (QG_EINVAL).  Errors: as
+ * qg_dequant and qquant_device, plus QG_ERANGE (workspace too small). */
+size_t qrequant_workspace_size(int64_t N, int64_t K);
+int qrequant(int src_fmt, const void* src, int dst_fmt, void* dst, int64_t N, int64_t K, void* workspace,
+             size_t ws_bytes, int* status, void* stream);
+
 /* Host packers for the trained low-bit formats (the pages give no
  * ternarizer/binarizer): t[N][K] int8 in {-1,0,1} or bits[N][K] uint8 in
  * {0,1}, plus scale_f16[N][K/128] fp16 bit patterns -> packed bytes.

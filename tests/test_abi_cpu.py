@@ -135,6 +135,26 @@ def test_moe_rmsnorm_validation():
 
 
 @nogpu
+def test_device_quantizer_validation():
+    lib = qg.load()
+    assert lib.qquant_device(5, P, 4, 256, P, P, None) == -6          # tern: no quantizer
+    assert lib.qquant_device(6, P, 4, 256, P, P, None) == -6          # bin
+    assert lib.qquant_device(3, P, 4, 128, P, P, None) == -2          # K off the block grid
+    assert lib.qquant_device(3, None, 4, 256, P, P, None) == -1
+    assert lib.qquant_device(3, P, 4, 256, P, None, None) == -1       # null status
+    assert lib.qquant_device(3, P, 4, 256, P + 8, P, None) == -3      # misaligned out
+    ws = qg.qrequant_workspace_size(4, 256)
+    assert ws == 4 * 256 * 4
+    big = 1 << 24
+    assert lib.qrequant(3, P, 4, P + big, 4, 256, P + 2 * big, ws - 4, P + 3 * big, None) == -4
+    assert lib.qrequant(3, P, 4, P + 16, 4, 256, P + 2 * big, ws, P + 3 * big, None) == -1   # src/dst overlap
+    assert lib.qrequant(3, P, 4, P + big, 4, 256, P + big + 16, ws, P + 3 * big, None) == -1  # ws/dst overlap
+    assert lib.qrequant(3, P, 5, P + big, 4, 256, P + 2 * big, ws, P + 3 * big, None) == -6  # dst tern
+    assert lib.qrequant(9, P, 4, P + big, 4, 256, P + 2 * big, ws, P + 3 * big, None) == -1  # unknown src
+    assert qg.qg_last_error()
+
+
+@nogpu
 def test_dequant_validation():
     lib = qg.load()
     assert lib.qg_dequant(3, P, P, 0, 256, None) == -2
