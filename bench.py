@@ -383,8 +383,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--quick", action="store_true", help="headline only, no extra configs")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle cpu_baseline leg")
-    ap.add_argument("--profile", choices=["gemv", "copy", "probe", "moe", "step"], default=None,
-                    help="run only the headline kernel (or a 1 GiB copy) a few times, for rocprofv3")
+    ap.add_argument("--profile", choices=["gemv", "copy", "probe", "moe", "step", "norm"], default=None,
+                    help="run only one part (the headline kernel, a 1 GiB copy, the read probe, the MoE layer, "
+                         "the 8B step, or the RMS-norm GEMVs and MoE block step) for rocprofv3")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build measures one GPU; --gpus {args.gpus} is not supported "
@@ -415,6 +416,20 @@ def main():
         for fmt in ("q4_k", "q2_k"):
             for t_tokens in (1, 8):
                 log(f"moe {moe_layer(torch, qg, stream, fmt, t_tokens)}")
+        return
+    if args.profile == "norm":
+        for n, k in ((14336, 4096), (4096, 4096)):
+            for b in (1, 8):
+                for norm in (False, True):
+                    g = Gemv(torch, qg, "q4_k", n, k, b, 0, COLD_BYTES, stream, norm)
+                    g.capture()
+                    g.replay(2)
+                    t = g.timed_replay(max(2, 400 // len(g.wp)))
+                    log(f"q4_k {n}x{k} B={b} rmsnorm={norm}: {t * 1e6:.2f} us")
+                    del g
+                    torch.cuda.empty_cache()
+        for t_tokens in (1, 8):
+            log(f"moe block {moe_layer(torch, qg, stream, 'q4_k', t_tokens, norm=True)}")
         return
     if args.profile == "step":
         log(f"step {dense_step(torch, qg, stream)}")
