@@ -24,8 +24,16 @@ namespace {
 
 using namespace core;
 
+// Minimum waves per SIMD to compile for.  Q4_K at batch 8 needs 130 VGPRs
+// with the norm's registers, which leaves room for one 8-wave workgroup per
+// compute unit; capped at 128 (no spill) it keeps two, like the plain kernel.
+template <int F, int B>
+constexpr int norm_waves_per_eu() {
+    return F == QG_Q4_K && B == 8 ? 4 : 1;
+}
+
 template <int F, int B, int W, int KCS>
-__global__ void __launch_bounds__(W * 64)
+__global__ void __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(norm_waves_per_eu<F, B>())))
 gemv_rmsnorm_kernel(const uint8_t* __restrict__ codes, const uint8_t* __restrict__ meta,
                     const float* __restrict__ x, const float* __restrict__ gamma, float eps,
                     float* __restrict__ y, int N, int K) {
