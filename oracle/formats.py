@@ -37,6 +37,17 @@ R7  tern: field f = t + 1 for t in {-1, 0, +1} (3 never emitted); bin: bit 1
     "quantizers" pack given codes and scales exactly.
 R8  The pages fix block contents, not where blocks sit in memory; rows are
     interleaved in groups of 16 (see the plane layout below).
+R9  bin8 is the low-bit page's 1-bit format whose block scales are 8-bit
+    codes of an affine map held per row (kernel table, the Q1_0 bit-plane
+    row, which prints the size saving): the 1-bit codes of ``bin`` and, per
+    128-weight block, one byte c_j, with the block scale
+    d_j = fp32(base + fp32(step * c_j)) from a per-row fp32 pair
+    (base, step).  From given fp16 block scales d (as ``bin`` takes them):
+    base = min_j d_j, step = (max_j d_j - base) / 255 in fp32, and
+    c_j = clamp(round_half_even((d_j - base) / step), 0, 255) (all 0 when
+    step = 0).  The (base, step) pairs form a third plane after the meta
+    plane, which is zero-padded to a multiple of 16 bytes: N rows of two
+    little-endian fp32, row-major, not interleaved.
 
 Plane layout of one packed [N][K] matrix (reading R8): the codes plane
 followed by the meta plane.  Each plane starts from the row-major byte image
@@ -52,7 +63,9 @@ low-bit README page's repacking of rows for the dot-product lanes (kernel
 table, Q2_K row interleave), set to 16 rows: one 16-lane quarter of a gfx950
 wave reads one unit of 16 rows as 256 contiguous bytes.
 
-Parity: Q8_0, Q4_0, Q4_1, Q4_K are pinned by the page's printed error table
+Parity: bin8 is pinned by the page's printed size saving (5.6 %), by exact
+round trips of affine-representable scales and by the rounding bound of the
+scale codes.  Q8_0, Q4_0, Q4_1, Q4_K are pinned by the page's printed error table
 (through ``page_listing``), by the bits/weight closed forms in the listing and
 by round trips of hand-built blocks.  Q2_K, tern and bin are pinned by round
 trips, closed forms and brute force only (their layouts are readings).
@@ -65,7 +78,7 @@ import numpy as np
 
 F32 = np.float32
 
-FORMATS = ("q8_0", "q4_0", "q4_1", "q4_k", "q2_k", "tern", "bin")
+FORMATS = ("q8_0", "q4_0", "q4_1", "q4_k", "q2_k", "tern", "bin", "bin8")
 
 
 class QuantInputError(ValueError):
@@ -95,14 +108,25 @@ SPECS = {
     "q2_k": Spec(256, 64, 16),
     "tern": Spec(128, 32, 2),
     "bin": Spec(128, 16, 2),
+    "bin8": Spec(128, 16, 1),
 }
+
+# bytes per row of the per-row plane after the meta plane (R9)
+ROW_BYTES = {"bin8": 8}
 
 
 def packed_size(fmt: str, n: int, k: int) -> int:
     s = SPECS[fmt]
     if k % s.block:
         raise ValueError(f"K={k} is not a multiple of the {fmt} block ({s.block})")
-    return n * (k // s.block) * (s.code_bytes + s.meta_bytes)
+    return n * (k // s.block) * s.code_bytes + _meta_span(fmt, n, k) + n * ROW_BYTES.get(fmt, 0)
+
+
+def _meta_span(fmt: str, n: int, k: int) -> int:
+    """Bytes of the meta plane, padded to 16 when a per-row plane follows (R9)."""
+    s = SPECS[fmt]
+    mp = n * (k // s.block) * s.meta_bytes
+    return -(-mp // 16) * 16 if fmt in ROW_BYTES else mp
 
 
 def codes_plane_size(fmt: str, n: int, k: int) -> int:
@@ -260,6 +284,31 @@ def bin_from_codes(bits, scale_bits) -> dict:
     return {"d": sb.copy(), "b": bits.astype(np.uint8)}
 
 
+def bin8_from_codes(bits, scale_bits) -> dict:
+    """1-bit codes [N, K] plus fp16 block scales [N, K/128] -> bin8 (R9): the
+    scales re-coded as 8-bit codes of a per-row affine map."""
+    bits = np.asarray(bits)
+    n, k = bits.shape
+    if k % 128:
+        raise ValueError("K must be a multiple of 128")
+    if not np.all((bits == 0) | (bits == 1)):
+        raise QuantInputError("1-bit codes must be 0 or 1")
+    d = from_f16_bits(np.asarray(scale_bits, dtype=np.uint16).reshape(n, k // 128))
+    if not np.all(np.isfinite(d)):
+        raise QuantInputError("block scales must be finite")
+    base = d.min(axis=1)
+    step = ((d.max(axis=1) - base) / F32(255)).astype(F32)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        c = np.where(step[:, None] == 0, F32(0), np.clip(np.rint((d - base[:, None]) / step[:, None]), 0, 255))
+    return {"b": bits.astype(np.uint8), "c": c.astype(np.uint8), "base": base.astype(F32), "step": step}
+
+
+def bin8_scales(blk) -> np.ndarray:
+    """fp32 [N, K/128] block scales of a bin8 block set: base + step * c."""
+    prod = (blk["step"][:, None] * blk["c"].astype(F32)).astype(F32)
+    return (blk["base"][:, None] + prod).astype(F32)
+
+
 QUANTIZERS = {
     "q8_0": quantize_q8_0,
     "q4_0": quantize_q4_0,
@@ -311,6 +360,9 @@ def dequant(fmt: str, blk: dict) -> np.ndarray:
     if fmt == "bin":
         bb = blk["b"]
         return (2 * bb.astype(np.int16) - 1).astype(F32) * _per_block(from_f16_bits(blk["d"]), 128, bb.shape[1])
+    if fmt == "bin8":
+        bb = blk["b"]
+        return (2 * bb.astype(np.int16) - 1).astype(F32) * _per_block(bin8_scales(blk), 128, bb.shape[1])
     raise KeyError(fmt)
 
 
@@ -445,12 +497,20 @@ def pack(fmt: str, blk: dict) -> np.ndarray:
     elif fmt == "bin":
         codes = np.packbits(blk["b"].astype(np.uint8), axis=1, bitorder="little")
         meta = _u16_le(blk["d"])
+    elif fmt == "bin8":
+        codes = np.packbits(blk["b"].astype(np.uint8), axis=1, bitorder="little")
+        meta = blk["c"].astype(np.uint8)
     else:
         raise KeyError(fmt)
     n = codes.shape[0]
     codes = np.ascontiguousarray(codes).reshape(n, -1)
     meta = np.ascontiguousarray(meta).reshape(n, -1)
-    return np.concatenate([interleave_rows(codes), interleave_rows(meta)]).astype(np.uint8)
+    parts = [interleave_rows(codes), interleave_rows(meta)]
+    if fmt == "bin8":  # zero pad to 16, then the per-row (base, step) plane, little-endian fp32
+        parts.append(np.zeros(-parts[1].size % 16, np.uint8))
+        pairs = np.stack([blk["base"], blk["step"]], axis=1).astype("<f4")
+        parts.append(pairs.view(np.uint8).reshape(-1))
+    return np.concatenate(parts).astype(np.uint8)
 
 
 def unpack(fmt: str, buf, n: int, k: int) -> dict:
@@ -462,7 +522,8 @@ def unpack(fmt: str, buf, n: int, k: int) -> dict:
     nb = k // spec.block
     cp = codes_plane_size(fmt, n, k)
     codes = deinterleave_rows(buf[:cp], n, nb * spec.code_bytes)
-    meta = deinterleave_rows(buf[cp:], n, nb * spec.meta_bytes).reshape(n, nb, spec.meta_bytes)
+    mp = n * nb * spec.meta_bytes
+    meta = deinterleave_rows(buf[cp:cp + mp], n, nb * spec.meta_bytes).reshape(n, nb, spec.meta_bytes)
     if fmt == "q8_0":
         return {"d": _le_u16(meta), "q": codes.view(np.int8).copy()}
     if fmt == "q4_0":
@@ -477,6 +538,10 @@ def unpack(fmt: str, buf, n: int, k: int) -> dict:
         return {"d": _le_u16(meta), "f": _bytes_to_crumbs(codes, k)}
     if fmt == "bin":
         return {"d": _le_u16(meta), "b": np.unpackbits(codes, axis=1, bitorder="little")[:, :k]}
+    if fmt == "bin8":
+        pairs = buf[cp + _meta_span(fmt, n, k):].copy().view("<f4").reshape(n, 2).astype(F32)
+        return {"b": np.unpackbits(codes, axis=1, bitorder="little")[:, :k], "c": meta[..., 0].copy(),
+                "base": pairs[:, 0].copy(), "step": pairs[:, 1].copy()}
     raise KeyError(fmt)
 
 

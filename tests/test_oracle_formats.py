@@ -15,6 +15,8 @@ import workloads
 from oracle import formats as F
 from oracle import page_listing as PL
 
+F32 = np.float32
+
 PAGE_NAMES = {"Q8_0": "q8_0", "Q4_0": "q4_0", "Q4_1": "q4_1", "Q4_K": "q4_k"}
 
 
@@ -64,7 +66,8 @@ def test_bpw_closed_forms(golden):
     assert F.SPECS["bin"].bpw == 1 + 16 / 128 == 1.125
     for fmt, spec in F.SPECS.items():
         for n, k in ((1, 256), (7, 512), (4096, 4096), (14336, 4096)):
-            assert F.packed_size(fmt, n, k) * 8 == n * k * spec.bpw
+            pad = -(n * k // spec.block * spec.meta_bytes) % 16 if fmt in F.ROW_BYTES else 0
+            assert F.packed_size(fmt, n, k) * 8 == n * k * spec.bpw + 8 * (n * F.ROW_BYTES.get(fmt, 0) + pad)
             assert F.codes_plane_size(fmt, n, k) % 16 == 0
 
 
@@ -188,6 +191,64 @@ def test_roundtrip_tern_bin():
     w = F.dequant("bin", blk)
     np.testing.assert_array_equal(w > 0, bits == 1)
     np.testing.assert_array_equal(np.abs(w), np.repeat(F.from_f16_bits(sc), 128, axis=1))
+
+
+def test_bin8_size_saving_matches_page(golden):
+    """The block part of bin8 (1 bit + one byte per 128 weights) against bin's
+    1 bit + fp16 per 128: the saving the page prints (5.6 %); the per-row
+    (base, step) pair adds 64 / K bits per weight on top."""
+    printed = float(golden("lowbit_q1_affine_saving.txt")[0][1])
+    assert F.SPECS["bin8"].bpw == 1 + 8 / 128 == 1.0625
+    assert round(100 * (1 - F.SPECS["bin8"].bpw / F.SPECS["bin"].bpw), 1) == printed
+    assert F.packed_size("bin8", 3, 4096) == F.packed_size("bin", 3, 4096) - 3 * 32 + 3 * 8  # 96 B meta: no pad
+    assert F.packed_size("bin8", 3, 384) == 3 * 48 + 16 + 3 * 8  # 9 B of meta padded to 16
+
+
+def test_bin8_affine_representable_scales_are_exact():
+    """Block scales 0.5 + c/256 with c covering 0..255: base = 0.5 and
+    step = 1/256 come out exactly, the codes are c, and the decode equals
+    bin's decode of the same fp16 scales."""
+    n, k = 3, 256 * 128
+    c = np.stack([np.arange(256), np.arange(255, -1, -1), (np.arange(256) * 7) % 256]).astype(np.uint8)
+    c[2, 0], c[2, 1] = 0, 255
+    d16 = F.to_f16_bits((0.5 + c.astype(np.float64) / 256).astype(F32))
+    bits = workloads.binary_codes(n, k, seed=3)
+    blk = F.bin8_from_codes(bits, d16)
+    assert np.all(blk["base"] == F32(0.5)) and np.all(blk["step"] == F32(1 / 256))
+    np.testing.assert_array_equal(blk["c"], c)
+    np.testing.assert_array_equal(F.dequant("bin8", blk), F.dequant("bin", F.bin_from_codes(bits, d16)))
+
+
+def test_bin8_scale_code_rounding_bound_and_constant_rows():
+    """Any fp16 scales: each decoded scale is within half a step (plus the two
+    fp32 roundings) of the given one; a row of equal scales has step 0, codes
+    0 and decodes exactly."""
+    n, k = 6, 128 * 40
+    sc = workloads.scale_bits_f16((n, k // 128), seed=4)
+    sc[5] = sc[5, 0]
+    blk = F.bin8_from_codes(workloads.binary_codes(n, k, seed=4), sc)
+    d = F.from_f16_bits(sc).astype(np.float64)
+    got = F.bin8_scales(blk).astype(np.float64)
+    bound = blk["step"].astype(np.float64)[:, None] / 2 + 2 * np.abs(d) * 2.0 ** -24
+    assert np.all(np.abs(got - d) <= bound)
+    assert blk["step"][5] == 0 and np.all(blk["c"][5] == 0) and np.all(got[5] == d[5])
+    # the extreme blocks of every row decode to their own scales up to rounding
+    for r in range(n):
+        assert got[r].min() == d[r].min()
+
+
+def test_roundtrip_bin8_and_plane_order():
+    bits = workloads.binary_codes(19, 384, seed=5)
+    sc = workloads.scale_bits_f16((19, 3), seed=5, tensor_id=1)
+    blk = F.bin8_from_codes(bits, sc)
+    buf = F.pack("bin8", blk)
+    assert buf.size == F.packed_size("bin8", 19, 384)
+    _same(F.unpack("bin8", buf, 19, 384), blk)
+    # 19 * 48 B of codes, 57 B of meta padded to 64, then row r's (base, step) at 8 r
+    assert np.all(buf[19 * 48 + 57:19 * 48 + 64] == 0)
+    tail = buf[19 * 48 + 64:].view("<f4").reshape(19, 2)
+    np.testing.assert_array_equal(tail[:, 0], blk["base"])
+    np.testing.assert_array_equal(tail[:, 1], blk["step"])
 
 
 # ----------------------------------------------------------------------------
