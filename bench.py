@@ -83,9 +83,9 @@ class Gemv:
         if fmt == "tern":
             packed = qg.qpack_tern(workloads.ternary_codes(n, k, seed, 1),
                                    workloads.scale_bits_f16((n, k // 128), seed, 2))
-        elif fmt == "bin":
-            packed = qg.qpack_bin(workloads.binary_codes(n, k, seed, 1),
-                                  workloads.scale_bits_f16((n, k // 128), seed, 2))
+        elif fmt in ("bin", "bin8"):
+            pack = qg.qpack_bin if fmt == "bin" else qg.qpack_bin8
+            packed = pack(workloads.binary_codes(n, k, seed, 1), workloads.scale_bits_f16((n, k // 128), seed, 2))
         else:
             packed = qg.qquant(fmt, workloads.student_t_weights(n, k, seed, n), n_threads=16)
         self.bytes = packed.size
@@ -509,7 +509,7 @@ def main():
                     log(f"  {fmt} {n}x{k} B={b}: {t*1e6:.2f} us, {nbytes/t/1e9:.1f} GB/s")
         extra["four_formats"] = rows
         rows = []
-        for fmt in ("tern", "bin", "q2_k"):
+        for fmt in ("tern", "bin", "bin8", "q2_k"):
             for n, k in ((4096, 4096), (12288, 4096), (4096, 12288)):
                 for b in (1, 4):
                     t, nbytes = measure(fmt, n, k, b)

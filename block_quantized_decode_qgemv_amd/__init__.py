@@ -24,12 +24,12 @@ __all__ = [
     "qg_packed_size", "qg_codes_plane_size", "qg_codes_plane_offset", "qg_block_size", "qgemv_workspace_size",
     "qgemv", "qgemv_q8_0", "qgemv_q4_0", "qgemv_q4_1", "qgemv_q4k", "qgemv_q2k",
     "qgemv_tern", "qgemv_bin", "qgemv_rmsnorm", "qg_dequant", "qquant", "qquant_device", "qrequant_workspace_size", "qrequant",
-    "qpack_tern", "qpack_bin",
+    "qpack_tern", "qpack_bin", "qpack_bin8",
     "moe_expert_ffn_workspace_size", "moe_expert_ffn", "moe_expert_ffn_rmsnorm", "qg_strerror", "qg_last_error",
     "qg_version", "EXPORTED_SYMBOLS",
 ]
 
-FORMATS = {"q8_0": 0, "q4_0": 1, "q4_1": 2, "q4_k": 3, "q2_k": 4, "tern": 5, "bin": 6}
+FORMATS = {"q8_0": 0, "q4_0": 1, "q4_1": 2, "q4_k": 3, "q2_k": 4, "tern": 5, "bin": 6, "bin8": 7}
 QG_MOE_RENORM = 1
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -64,6 +64,7 @@ _SIGNATURES = {
     "qrequant": (_i32, [_i32, _vp, _i32, _vp, _i64, _i64, _vp, _sz, _vp, _vp]),
     "qpack_tern": (_i32, [_vp, _vp, _i64, _i64, _vp]),
     "qpack_bin": (_i32, [_vp, _vp, _i64, _i64, _vp]),
+    "qpack_bin8": (_i32, [_vp, _vp, _i64, _i64, _vp]),
     "moe_expert_ffn_workspace_size": (_sz, [_i32, _i32, _i32, _i32, _i32]),
     "moe_expert_ffn": (_i32, [_i32, _vp, _vp, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _i32, _u32,
                               _vp, _vp, _sz, _vp]),
@@ -306,6 +307,17 @@ def qpack_bin(bits, scale_bits) -> np.ndarray:
     size = qg_packed_size("bin", n, k)
     out = np.empty(max(size, 1), dtype=np.uint8)
     _check(load().qpack_bin(bb.ctypes.data, s.ctypes.data, n, k, out.ctypes.data), "qpack_bin")
+    return out[:size]
+
+
+def qpack_bin8(bits, scale_bits) -> np.ndarray:
+    """1-bit codes and fp16 block scales -> packed bin8 bytes (see qpack_bin8 in qgemv.h)."""
+    bb = np.ascontiguousarray(bits, dtype=np.uint8)
+    s = np.ascontiguousarray(scale_bits, dtype=np.uint16)
+    n, k = bb.shape
+    size = qg_packed_size("bin8", n, k)
+    out = np.empty(max(size, 1), dtype=np.uint8)
+    _check(load().qpack_bin8(bb.ctypes.data, s.ctypes.data, n, k, out.ctypes.data), "qpack_bin8")
     return out[:size]
 
 

@@ -85,6 +85,16 @@ dequant_kernel(const uint8_t* __restrict__ codes, const uint8_t* __restrict__ me
     const uint8_t* gm = meta + (size_t)g * kRowGroup * row_meta;
     const uint4 q = *(const uint4*)(gc + ((size_t)c * n_g + r) * 16);
     const uint32_t dw[4] = {q.x, q.y, q.z, q.w};
+    float d8 = 0.0f;  // bin8: this unit's block scale, base + step * c
+    if constexpr (F == QG_BIN8) {
+        const int full = row_meta >> 4, rem = row_meta & 15;
+        const int u = c >> 4, i = c & 15;
+        const uint8_t* pm = u < full ? gm + ((size_t)u * n_g + r) * 16 + i
+                                     : gm + (size_t)full * n_g * 16 + (size_t)r * rem + i;
+        const size_t span = ((size_t)N * row_meta + 15) / 16 * 16;
+        const float2 ab = *(const float2*)(meta + span + (size_t)row * 8);
+        d8 = bin8_scale(ab.x, ab.y, *pm);
+    }
     float* o = out + (size_t)row * K + (size_t)c * CPC;
 #pragma unroll
     for (int d = 0; d < 4; ++d) {
@@ -117,6 +127,8 @@ dequant_kernel(const uint8_t* __restrict__ codes, const uint8_t* __restrict__ me
                 v = fmaf(w[i], (float)(pj & 63u) * dd, -((float)(pj >> 6) * dm));
             } else if constexpr (F == QG_TERN) {
                 v = (w[i] - 1.0f) * h2f(meta_u16(gm, n_g, r, 2 * blk, row_meta));
+            } else if constexpr (F == QG_BIN8) {
+                v = (2.0f * w[i] - 1.0f) * d8;
             } else {
                 v = (2.0f * w[i] - 1.0f) * h2f(meta_u16(gm, n_g, r, 2 * blk, row_meta));
             }
@@ -177,6 +189,7 @@ hipError_t launch_dequant(int fmt, const uint8_t* codes, const uint8_t* meta, fl
         case QG_Q4_K: return launch_dequant_f<QG_Q4_K>(codes, meta, out, N, K, st);
         case QG_Q2_K: return launch_dequant_f<QG_Q2_K>(codes, meta, out, N, K, st);
         case QG_TERN: return launch_dequant_f<QG_TERN>(codes, meta, out, N, K, st);
+        case QG_BIN8: return launch_dequant_f<QG_BIN8>(codes, meta, out, N, K, st);
         default: return launch_dequant_f<QG_BIN>(codes, meta, out, N, K, st);
     }
 }
@@ -195,6 +208,9 @@ int check_gemv_args(int fmt, const void* w, const float* x, const float* y, int6
     if (!aligned(w, 16)) return fail(QG_EALIGN, "w must be 16-byte aligned");
     if (!aligned(x, 16)) return fail(QG_EALIGN, "x must be 16-byte aligned");
     if (!aligned(y, 4)) return fail(QG_EALIGN, "y must be 4-byte aligned");
+    // every workgroup reads all of x and writes its own rows of y: no overlap
+    const size_t yb = (size_t)B * N * 4, xb = (size_t)B * K * 4, wb = qg_packed_size(fmt, N, K);
+    if (overlap(y, yb, x, xb) || overlap(y, yb, w, wb)) return fail(QG_EINVAL, "y must not overlap x or w");
     return QG_OK;
 }
 

@@ -28,6 +28,7 @@ template <> struct Fmt<QG_Q4_K> { static constexpr int CPC = 32,  MBU = 2, GS = 
 template <> struct Fmt<QG_Q2_K> { static constexpr int CPC = 64,  MBU = 4, GS = 32,  BLOCK = 256, CB = 64,  MB = 16; };
 template <> struct Fmt<QG_TERN> { static constexpr int CPC = 64,  MBU = 1, GS = 64,  BLOCK = 128, CB = 32,  MB = 2; };
 template <> struct Fmt<QG_BIN>  { static constexpr int CPC = 128, MBU = 2, GS = 128, BLOCK = 128, CB = 16,  MB = 2; };
+template <> struct Fmt<QG_BIN8> { static constexpr int CPC = 128, MBU = 1, GS = 128, BLOCK = 128, CB = 16,  MB = 1; };
 
 __device__ __forceinline__ float h2f(uint32_t bits16) {
     return (float)__builtin_bit_cast(_Float16, (uint16_t)bits16);
@@ -125,6 +126,8 @@ template <> struct Unit<QG_BIN> {
     }
 };
 
+template <> struct Unit<QG_BIN8> : Unit<QG_BIN> {};
+
 // Weight bytes are read exactly once per call: stream them past the caches.
 #ifndef QG_WEIGHT_NT
 #define QG_WEIGHT_NT 1
@@ -195,15 +198,19 @@ __device__ __forceinline__ void load_meta(const uint8_t* gm, int n_g, int r, int
                 wd[0] = v.x; wd[1] = v.y;
             } else if constexpr (NB == 4) {
                 wd[0] = *(const uint32_t*)p;
+            } else if constexpr (NB == 2) {
+                wd[0] = *(const uint16_t*)p;
             } else {
-                wd[0] = *(const uint16_t*)p;  // NB == 2
+                wd[0] = *p;  // NB == 1
             }
         } else {
             const uint8_t* p = gm + (size_t)full * n_g * 16 + (size_t)r * rem;
 #pragma unroll
             for (int k = 0; k < W; ++k) {
                 uint32_t lo = 0, hi = 0;
-                if (u == full && i0 + 4 * k < rem) lo = *(const uint16_t*)(p + i0 + 4 * k);
+                if constexpr (NB == 1) {
+                    if (u == full && i0 < rem) lo = p[i0];
+                } else if (u == full && i0 + 4 * k < rem) lo = *(const uint16_t*)(p + i0 + 4 * k);
                 if (NB > 2 && u == full && i0 + 4 * k + 2 < rem) hi = *(const uint16_t*)(p + i0 + 4 * k + 2);
                 wd[W * h + k] = lo | (hi << 16);
             }
@@ -299,6 +306,24 @@ template <> struct Apply<QG_BIN> {
     // w = (2 beta - 1) d  ->  d * (1024 P - X)
     __device__ static void unit(const uint32_t* wd, int i, int, float P, float X, KqState&, float& acc, bool ok) {
         const float v = fmaf(meta_h(wd, i), fmaf(1024.0f, P, -X), acc);
+        acc = ok ? v : acc;
+    }
+};
+
+// bin8 block scale fp32(base + fp32(step * c)): two roundings, never fused
+__device__ __forceinline__ float bin8_scale(float base, float step, uint32_t c) {
+#pragma clang fp contract(off)
+    const float prod = step * (float)c;
+    return base + prod;
+}
+
+// bin8: the block scale is base + step * c for the unit's meta byte c; the
+// lane's row (base, step) ride in wd[1], wd[2]
+template <> struct Apply<QG_BIN8> {
+    static constexpr int SUBS = 1;
+    __device__ static void unit(const uint32_t* wd, int i, int, float P, float X, KqState&, float& acc, bool ok) {
+        const float d = bin8_scale(__uint_as_float(wd[1]), __uint_as_float(wd[2]), (wd[0] >> (8 * i)) & 0xFFu);
+        const float v = fmaf(d, fmaf(1024.0f, P, -X), acc);
         acc = ok ? v : acc;
     }
 };
@@ -580,13 +605,13 @@ template <int F> constexpr bool dpp_units_ok(int kcs) {
     return (kcs * T::CPC) % 64 == 0 &&
            (is_kquant<F>() ? (T::BLOCK / T::CPC) % kcs == 0      // inside one super-block
                            : (kcs * T::CPC) % T::BLOCK == 0) &&  // whole blocks (aligned meta)
-           kcs * T::MBU >= 2;                                    // at least one fp16 of meta
+           (kcs * T::MBU >= 2 || T::MB == 1);                    // at least one fp16 of meta, or whole 1-byte entries
 }
 template <int F, int B> constexpr int dpp_lane_units() {
     int best = 0;
     // 1-bit parts of 4 units (512 weights per lane) decode into too many
     // registers even at batch 1
-    for (int kcs = F == QG_BIN ? 2 : 4; kcs >= 1; kcs /= 2) {
+    for (int kcs = (F == QG_BIN || F == QG_BIN8) ? 2 : 4; kcs >= 1; kcs /= 2) {
         if (!dpp_units_ok<F>(kcs)) continue;
         if (B * kcs * Fmt<F>::CPC / 16 <= 32) return kcs;
         best = kcs;
@@ -673,6 +698,15 @@ struct GemvDpp {
         const uint8_t* gm = meta + (size_t)g * kRowGroup * row_meta;
         const uint32_t ro = (uint32_t)rr * 16;
 
+        // bin8: the meta byte of the part plus the row's (base, step), from
+        // the per-row plane after the 16-byte-padded meta plane
+        uint32_t wx[3] = {0u, 0u, 0u};
+        if constexpr (F == QG_BIN8) {
+            const size_t span = ((size_t)N * row_meta + 15) / 16 * 16;
+            const float2 ab = *(const float2*)(meta + span + ((size_t)g * kRowGroup + rr) * 8);
+            wx[1] = __float_as_uint(ab.x);
+            wx[2] = __float_as_uint(ab.y);
+        }
         float acc[B], ss[B];  // row sums; sums of x^2 (NORM)
 #pragma unroll
         for (int b = 0; b < B; ++b) acc[b] = ss[b] = 0.0f;
@@ -751,12 +785,15 @@ struct GemvDpp {
                             wd[0] = v.x; wd[1] = v.y;
                         } else if constexpr (MB == 4) {
                             wd[0] = ld_weights<uint32_t>(pm);
+                        } else if constexpr (MB == 2) {
+                            wd[0] = *(const uint16_t*)pm;
                         } else {
-                            wd[0] = *(const uint16_t*)pm;  // MB == 2
+                            wd[0] = *pm;  // MB == 1
                         }
                     } else {
                         load_meta<MB>(gm, n_g, rr, m0, row_meta, wd);
                     }
+                    if constexpr (F == QG_BIN8) wx[0] = wd[0];
                 }
                 uint4 q[KCS];
 #pragma unroll
@@ -816,7 +853,8 @@ struct GemvDpp {
                                 st[b].sp = fmaf((float)(pr & 63u), ps[b], st[b].sp);
                                 st[b].tx = fmaf((float)((pr >> 6) & 63u), X, st[b].tx);
                             } else {
-                                A::unit(wd, i, s, ps[b], X, st[b], acc[b], ok);
+                                if constexpr (F == QG_BIN8) A::unit(wx, i, s, ps[b], X, st[b], acc[b], ok);
+                                else A::unit(wd, i, s, ps[b], X, st[b], acc[b], ok);
                             }
                         }
                     });

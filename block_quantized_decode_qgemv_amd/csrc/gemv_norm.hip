@@ -70,6 +70,7 @@ extern "C" int qgemv_rmsnorm(int fmt, const void* w, const float* x, const float
     if (!gamma) return fail(QG_EINVAL, "null gamma");
     if (!aligned(gamma, 16)) return fail(QG_EALIGN, "gamma must be 16-byte aligned");
     if (!(eps >= 0.0f) || !std::isfinite(eps)) return fail(QG_ERANGE, "eps=%g must be finite and >= 0", (double)eps);
+    if (overlap(y, (size_t)B * N * 4, gamma, (size_t)K * 4)) return fail(QG_EINVAL, "y must not overlap gamma");
     const uint8_t* codes = static_cast<const uint8_t*>(w);
     const uint8_t* meta = codes + qg_codes_plane_size(fmt, N, K);
     hipError_t e = core::launch_dpp<RmsNormGemv>(fmt, (int)N, (int)K, B, static_cast<hipStream_t>(stream), codes,

@@ -30,6 +30,7 @@ const FormatInfo kFormats[] = {
     {256, 64, 16},  // Q2_K
     {128, 32, 2},   // TERN
     {128, 16, 2},   // BIN
+    {128, 16, 1},   // BIN8 (plus the per-row plane, see qg_packed_size)
 };
 
 thread_local char g_last_error[512] = "";
@@ -232,7 +233,7 @@ int quant_row(int fmt, const float* w, int64_t K, uint8_t* codes, uint8_t* meta)
 }  // namespace
 
 const FormatInfo* format_info(int fmt) {
-    if (fmt < QG_Q8_0 || fmt > QG_BIN) return nullptr;
+    if (fmt < QG_Q8_0 || fmt > QG_BIN8) return nullptr;
     return &kFormats[fmt];
 }
 
@@ -247,6 +248,11 @@ int fail(int code, const char* fmt, ...) {
 void clear_error() { g_last_error[0] = '\0'; }
 
 bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+bool overlap(const void* a, size_t na, const void* b, size_t nb) {
+    const uintptr_t pa = (uintptr_t)a, pb = (uintptr_t)b;
+    return na > 0 && nb > 0 && pa < pb + nb && pb < pa + na;
+}
 
 int check_matrix(int fmt, int64_t N, int64_t K) {
     const FormatInfo* fi = format_info(fmt);
@@ -268,7 +274,10 @@ extern "C" {
 size_t qg_packed_size(int fmt, int64_t N, int64_t K) {
     const FormatInfo* fi = format_info(fmt);
     if (!fi || N < 1 || K < fi->block || K % fi->block) return 0;
-    return (size_t)N * (size_t)(K / fi->block) * (size_t)(fi->code_bytes + fi->meta_bytes);
+    const size_t meta = (size_t)N * (size_t)(K / fi->block) * (size_t)fi->meta_bytes;
+    if (fmt == QG_BIN8)  // meta padded to 16, then (base, step) per row
+        return qg_codes_plane_size(fmt, N, K) + (meta + 15) / 16 * 16 + (size_t)N * 8;
+    return qg_codes_plane_size(fmt, N, K) + meta;
 }
 
 size_t qg_codes_plane_size(int fmt, int64_t N, int64_t K) {
@@ -303,8 +312,8 @@ const char* qg_version(void) { return "qgemv 0.1 (gfx950)"; }
 
 int qquant(int fmt, const float* w_host, int64_t N, int64_t K, void* out_host, int n_threads) {
     clear_error();
-    if (fmt == QG_TERN || fmt == QG_BIN)
-        return fail(QG_EINVAL, "format %d packs given codes: use qpack_tern / qpack_bin", fmt);
+    if (fmt == QG_TERN || fmt == QG_BIN || fmt == QG_BIN8)
+        return fail(QG_EINVAL, "format %d packs given codes: use qpack_tern / qpack_bin / qpack_bin8", fmt);
     int rc = check_matrix(fmt, N, K);
     if (rc) return rc;
     if (!w_host || !out_host) return fail(QG_EINVAL, "null pointer");
@@ -408,6 +417,55 @@ int qpack_bin(const uint8_t* bits, const uint16_t* scale_f16, int64_t N, int64_t
                 gc[i * row_codes + k / 8] = byte;
             }
             for (int64_t b = 0; b < K / 128; ++b) put_u16(gm.data() + i * row_meta + 2 * b, scale_f16[(size_t)r * (K / 128) + b]);
+        }
+        interleave_group(gc.data(), n_g, row_codes, codes + (size_t)(16 * g) * row_codes);
+        interleave_group(gm.data(), n_g, row_meta, meta + (size_t)(16 * g) * row_meta);
+    }
+    return QG_OK;
+}
+
+int qpack_bin8(const uint8_t* bits, const uint16_t* scale_f16, int64_t N, int64_t K, void* out_host) {
+    clear_error();
+    int rc = check_matrix(QG_BIN8, N, K);
+    if (rc) return rc;
+    if (!bits || !scale_f16 || !out_host) return fail(QG_EINVAL, "null pointer");
+    const int64_t nb = K / 128;
+    const size_t row_codes = (size_t)K / 8, row_meta = (size_t)nb;
+    uint8_t* codes = static_cast<uint8_t*>(out_host);
+    uint8_t* meta = codes + (size_t)N * row_codes;
+    const size_t meta_span = ((size_t)N * row_meta + 15) / 16 * 16;
+    uint8_t* pairs = meta + meta_span;
+    std::memset(meta + (size_t)N * row_meta, 0, meta_span - (size_t)N * row_meta);
+    std::vector<uint8_t> gc(16 * row_codes), gm(16 * row_meta);
+    std::vector<float> d((size_t)nb);
+    for (int64_t g = 0; g < (N + 15) / 16; ++g) {
+        const int n_g = (int)std::min<int64_t>(16, N - 16 * g);
+        for (int i = 0; i < n_g; ++i) {
+            const int64_t r = 16 * g + i;
+            for (int64_t k = 0; k < K; k += 8) {
+                uint8_t byte = 0;
+                for (int j = 0; j < 8; ++j) {
+                    const unsigned v = bits[(size_t)r * K + k + j];
+                    if (v > 1)
+                        return fail(QG_EINVAL, "1-bit code %u at (%lld, %lld)", v, (long long)r, (long long)(k + j));
+                    byte |= (uint8_t)(v << j);
+                }
+                gc[i * row_codes + k / 8] = byte;
+            }
+            // the row's block scales as 8-bit codes of base + step * c
+            float lo = 0.0f, hi = 0.0f;
+            for (int64_t b = 0; b < nb; ++b) {
+                d[b] = f16_to_f32(scale_f16[(size_t)r * nb + b]);
+                if (!std::isfinite(d[b])) return fail(QG_EINVAL, "non-finite scale in row %lld", (long long)r);
+                if (b == 0 || d[b] < lo) lo = d[b];
+                if (b == 0 || d[b] > hi) hi = d[b];
+            }
+            const float step = (hi - lo) / 255.0f;
+            for (int64_t b = 0; b < nb; ++b)
+                gm[i * row_meta + b] =
+                    step == 0.0f ? 0 : (uint8_t)clampf(std::nearbyint((d[b] - lo) / step), 0.0f, 255.0f);
+            std::memcpy(pairs + (size_t)r * 8, &lo, 4);
+            std::memcpy(pairs + (size_t)r * 8 + 4, &step, 4);
         }
         interleave_group(gc.data(), n_g, row_codes, codes + (size_t)(16 * g) * row_codes);
         interleave_group(gm.data(), n_g, row_meta, meta + (size_t)(16 * g) * row_meta);

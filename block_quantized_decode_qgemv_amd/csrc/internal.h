@@ -25,6 +25,8 @@ void clear_error();
 // Host-side argument checks shared by the device entry points.
 int check_matrix(int fmt, int64_t N, int64_t K);
 bool aligned(const void* p, size_t a);
+// Whether the byte ranges [a, a + na) and [b, b + nb) share a byte.
+bool overlap(const void* a, size_t na, const void* b, size_t nb);
 
 // Compute units of the current device (cached per device; 256 if the query fails).
 int device_cus();

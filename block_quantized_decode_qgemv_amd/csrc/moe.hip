@@ -452,8 +452,13 @@ int check_moe_args(int fmt, const void* w_gate_up, const void* w_down, int E, in
         return fail(QG_EALIGN, "residual, logits and out must be 4-byte aligned");
     const size_t need = MoeLayout(T, H, I, top_k).total;
     if (ws_bytes < need) return fail(QG_ERANGE, "workspace of %zu bytes is below the %zu needed", ws_bytes, need);
-    if ((const void*)out == (const void*)x || (const void*)out == (const void*)residual)
-        return fail(QG_EINVAL, "out must not alias x or residual");
+    const size_t act = (size_t)T * H * 4;
+    if (overlap(out, act, x, act) || overlap(out, act, residual, act))
+        return fail(QG_EINVAL, "out must not overlap x or residual");
+    if (overlap(workspace, need, x, act) || overlap(workspace, need, residual, act) ||
+        overlap(workspace, need, out, act) || overlap(workspace, need, router_logits, (size_t)T * E * 4) ||
+        overlap(workspace, need, shared_gate_logit, (size_t)T * 4))
+        return fail(QG_EINVAL, "workspace must not overlap the inputs or out");
     return QG_OK;
 }
 
@@ -501,6 +506,9 @@ int moe_expert_ffn_rmsnorm(int fmt, const void* w_gate_up, const void* w_down, i
     if (!gamma) return fail(QG_EINVAL, "null gamma");
     if (!aligned(gamma, 16)) return fail(QG_EALIGN, "gamma must be 16-byte aligned");
     if (!(eps >= 0.0f) || !std::isfinite(eps)) return fail(QG_ERANGE, "eps=%g must be finite and >= 0", (double)eps);
+    if (overlap(gamma, (size_t)H * 4, out, (size_t)T * H * 4) ||
+        overlap(gamma, (size_t)H * 4, workspace, MoeLayout(T, H, I, top_k).total))
+        return fail(QG_EINVAL, "gamma must not overlap out or the workspace");
     return moe_call<true>(fmt, w_gate_up, w_down, E, H, I, top_k, x, gamma, eps, residual, router_logits,
                           shared_gate_logit, T, flags, out, workspace, stream);
 }

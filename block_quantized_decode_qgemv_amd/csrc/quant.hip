@@ -250,7 +250,7 @@ hipError_t launch_quant(int fmt, const float* w, int64_t N, int64_t K, uint8_t* 
 }
 
 int check_quant(int fmt, int64_t N, int64_t K, const void* out, const int* status) {
-    if (fmt == QG_TERN || fmt == QG_BIN)
+    if (fmt == QG_TERN || fmt == QG_BIN || fmt == QG_BIN8)
         return fail(QG_EUNSUPPORTED, "format %d has no quantizer (it packs given codes)", fmt);
     int rc = check_matrix(fmt, N, K);
     if (rc) return rc;
@@ -273,6 +273,9 @@ int qquant_device(int fmt, const float* w, int64_t N, int64_t K, void* out, int*
     if (rc) return rc;
     if (!w) return fail(QG_EINVAL, "null w");
     if (!aligned(w, 4)) return fail(QG_EALIGN, "w must be 4-byte aligned");
+    const size_t ob = qg_packed_size(fmt, N, K), wb = (size_t)N * (size_t)K * 4;
+    if (overlap(out, ob, w, wb) || overlap(status, 4, w, wb) || overlap(status, 4, out, ob))
+        return fail(QG_EINVAL, "w, out and status must not overlap");
     hipError_t e = launch_quant(fmt, w, N, K, static_cast<uint8_t*>(out), status, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return fail(QG_EHIP, "quantizer launch failed: %s", hipGetErrorString(e));
     return QG_OK;
@@ -298,9 +301,9 @@ int qrequant(int src_fmt, const void* src, int dst_fmt, void* dst, int64_t N, in
     const uint8_t* d = static_cast<const uint8_t*>(dst);
     const size_t src_bytes = qg_packed_size(src_fmt, N, K), dst_bytes = qg_packed_size(dst_fmt, N, K);
     const uint8_t* t = static_cast<const uint8_t*>(workspace);
-    if ((s < d + dst_bytes && d < s + src_bytes) || (t < d + dst_bytes && d < t + need) ||
-        (t < s + src_bytes && s < t + need))
-        return fail(QG_EINVAL, "src, dst and workspace must not overlap");
+    if (overlap(s, src_bytes, d, dst_bytes) || overlap(t, need, d, dst_bytes) || overlap(t, need, s, src_bytes) ||
+        overlap(status, 4, d, dst_bytes) || overlap(status, 4, t, need))
+        return fail(QG_EINVAL, "src, dst, workspace and status must not overlap");
     float* tmp = static_cast<float*>(workspace);
     rc = qg_dequant(src_fmt, src, tmp, N, K, stream);
     if (rc) return rc;

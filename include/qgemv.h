@@ -70,7 +70,8 @@ typedef enum {
     QG_Q4_K = 3,
     QG_Q2_K = 4,
     QG_TERN = 5,
-    QG_BIN = 6
+    QG_BIN = 6,
+    QG_BIN8 = 7
 } qg_format;
 
 enum {
@@ -115,7 +116,8 @@ size_t qgemv_workspace_size(int fmt, int64_t N, int64_t K, int B);
  * accumulation (handbook page, "速度上限：带宽 ÷ 权重字节数": y = W x).
  *   w   DEVICE, packed [N][K] matrix of format fmt, 16-byte aligned.
  *   x   DEVICE, fp32 [B][K] row-major, 16-byte aligned.
- *   y   DEVICE, fp32 [B][N] row-major, 4-byte aligned; overwritten.
+ *   y   DEVICE, fp32 [B][N] row-major, 4-byte aligned; overwritten; must not
+ *       overlap x or w (QG_EINVAL).
  *   N >= 1 (any value); K a positive multiple of the block size, at most
  *   2^26 (offsets inside a 16-row group are 32-bit);
  *   1 <= B <= 8.
@@ -155,7 +157,7 @@ int qgemv_bin(const void* w, const float* x, float* y, int64_t N, int64_t K, int
  * "延迟 GPU 专家计算").  The sum of squares is taken while x is loaded, gamma
  * scales x in registers and 1/rms scales each row sum, so no normalised copy
  * of x is written.
- *   gamma  DEVICE, fp32 [K], 16-byte aligned.
+ *   gamma  DEVICE, fp32 [K], 16-byte aligned, not overlapping y.
  *   eps    finite, >= 0 (a zero row with eps = 0 gives non-finite y, as the
  *          definition does).
  *   w, x, y, N, K, B, stream: as for qgemv.
@@ -185,7 +187,7 @@ int qg_dequant(int fmt, const void* w, float* out, int64_t N, int64_t K, void* s
  * stored values; rounding is half-to-even; a zero scale gives the zero code.
  * Signed zeros in the input are treated as +0.  n_threads <= 0 means 1.
  * Both pointers are HOST memory.  Errors: QG_EINVAL (null, non-finite input,
- * fmt is TERN/BIN -- use qpack_tern/qpack_bin), QG_ESHAPE, QG_ERANGE (a
+ * fmt is TERN/BIN/BIN8 -- use qpack_tern/qpack_bin/qpack_bin8), QG_ESHAPE, QG_ERANGE (a
  * scale or min overflows fp16; out_host is then unspecified). */
 int qquant(int fmt, const float* w_host, int64_t N, int64_t K, void* out_host, int n_threads);
 
@@ -198,6 +200,7 @@ int qquant(int fmt, const float* w_host, int64_t N, int64_t K, void* out_host, i
  *           non-finite weight) or QG_ERANGE (a scale or min overflows fp16);
  *           with several failures it holds the smallest code.  The blocks
  *           that fail leave their bytes of out unspecified.
+ * w, out and status must not overlap (QG_EINVAL).
  * fmt Q8_0, Q4_0, Q4_1, Q4_K or Q2_K (TERN and BIN: QG_EUNSUPPORTED; the
  * pages give no ternarizer or binarizer).  Asynchronous on `stream`; read
  * status after synchronising.  Host errors: QG_EINVAL, QG_ESHAPE, QG_EALIGN,
@@ -214,7 +217,7 @@ int qquant_device(int fmt, const float* w, int64_t N, int64_t K, void* out, int*
  *   workspace  DEVICE scratch of >= qrequant_workspace_size(N, K) bytes
  *              (the decoded fp32 matrix), 16-byte aligned.
  *   status     as for qquant_device.
- * src, dst and workspace must not overlap (QG_EINVAL).  Errors: as
+ * src, dst, workspace and status must not overlap (QG_EINVAL).  Errors: as
  * qg_dequant and qquant_device, plus QG_ERANGE (workspace too small). */
 size_t qrequant_workspace_size(int64_t N, int64_t K);
 int qrequant(int src_fmt, const void* src, int dst_fmt, void* dst, int64_t N, int64_t K, void* workspace,
@@ -226,6 +229,19 @@ int qrequant(int src_fmt, const void* src, int dst_fmt, void* dst, int64_t N, in
  * Errors: QG_EINVAL (null pointer, a code out of range), QG_ESHAPE. */
 int qpack_tern(const int8_t* t, const uint16_t* scale_f16, int64_t N, int64_t K, void* out_host);
 int qpack_bin(const uint8_t* bits, const uint16_t* scale_f16, int64_t N, int64_t K, void* out_host);
+
+/* Host packer for QG_BIN8, the 1-bit format whose block scales are 8-bit
+ * codes of a per-row affine map (low-bit README page, kernel table, the
+ * Q1_0 bit-plane row).  Takes the same bits and fp16 block scales as
+ * qpack_bin and re-codes each row's scales d_j as
+ *   base = min_j d_j, step = (max_j d_j - base) / 255      (fp32),
+ *   c_j  = clamp(round_half_even((d_j - base) / step), 0, 255), 0 if step = 0,
+ * decoded as d_j' = fp32(base + fp32(step * c_j)).  Layout: the codes plane
+ * (as QG_BIN), the meta plane (one byte c_j per 128-weight block, rows
+ * interleaved by 16 as usual) zero-padded to a multiple of 16 bytes, then N
+ * rows of (base, step) as two little-endian fp32, row-major.
+ * Errors: as qpack_bin, plus QG_EINVAL for a non-finite scale. */
+int qpack_bin8(const uint8_t* bits, const uint16_t* scale_f16, int64_t N, int64_t K, void* out_host);
 
 /* --------------------------------------------------------------- MoE layer */
 
@@ -242,10 +258,10 @@ int qpack_bin(const uint8_t* bits, const uint16_t* scale_f16, int64_t N, int64_t
  *              is gate row i and row 2i+1 is up row i; expert E is shared.
  *   w_down     DEVICE, (E+1) consecutive packed [H][I] matrices.
  *   x, residual  DEVICE fp32 [T][H] (residual may alias x); out DEVICE fp32
- *              [T][H] (must not alias x or residual).
+ *              [T][H] (must not overlap x or residual).
  *   router_logits DEVICE fp32 [T][E]; shared_gate_logit DEVICE fp32 [T].
  *   workspace  DEVICE scratch >= moe_expert_ffn_workspace_size() bytes,
- *              16-byte aligned.
+ *              16-byte aligned, overlapping no input and not out.
  *   1 <= T <= 8, 1 <= top_k <= min(E, 8), 1 <= E <= 4096, H and I
  *   multiples of 256 in [256, 2^26].  Deterministic (fixed-order sums, no
  *   float atomics).
@@ -264,7 +280,8 @@ int moe_expert_ffn(int fmt, const void* w_gate_up, const void* w_down, int E, in
  * section "每层流水线").  In a pre-norm block residual is the un-normalised
  * x itself (it may alias x); router_logits are the router projection of
  * xhat, e.g. from qgemv_rmsnorm with the same gamma and eps.
- *   gamma  DEVICE fp32 [H], 16-byte aligned; eps finite, >= 0.
+ *   gamma  DEVICE fp32 [H], 16-byte aligned, overlapping neither out nor
+ *          the workspace; eps finite, >= 0.
  *   Every other argument as for moe_expert_ffn (same workspace size).
  * Accuracy: the moe_expert_ffn bound with the gate/up GEMV bound widened to
  * 3e-5 * sum_k |W[n][k] xhat[t][k]| + 1e-7 (the qgemv_rmsnorm bound).

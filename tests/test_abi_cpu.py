@@ -84,6 +84,8 @@ P = 0x10000  # fake 16-byte aligned pointer value
     (dict(fmt=3, n=4, k=256, b=1, w=P + 8), -3),  # misaligned w
     (dict(fmt=3, n=4, k=256, b=1, x=P + 4), -3),  # misaligned x
     (dict(fmt=3, n=4, k=256, b=1, y=P + 2), -3),  # misaligned y
+    (dict(fmt=3, n=4, k=256, b=2, x=P + 1024, y=P + 1024 + 2040), -1),  # y overlaps the end of x
+    (dict(fmt=3, n=4, k=256, b=1, w=P + 4096, y=P + 4096 + 560), -1),   # y overlaps the end of w (576 B)
 ])
 def test_gemv_validation(args, code):
     lib = qg.load()
@@ -99,7 +101,9 @@ def test_gemv_rmsnorm_validation():
 
     lib = qg.load()
 
-    def call(fmt=3, w=P, x=P, gamma=P, eps=1e-6, y=P, n=4, k=256, b=1):
+    big = 1 << 24  # distinct, non-overlapping fake buffers
+
+    def call(fmt=3, w=P, x=P + big, gamma=P + 2 * big, eps=1e-6, y=P + 3 * big, n=4, k=256, b=1):
         return lib.qgemv_rmsnorm(fmt, w, x, gamma, ctypes.c_float(eps), y, n, k, b, None)
 
     assert call(gamma=None) == -1
@@ -110,6 +114,7 @@ def test_gemv_rmsnorm_validation():
     assert call(k=128) == -2            # the plain GEMV's checks come first
     assert call(b=9) == -4
     assert call(x=None) == -1
+    assert call(y=P + 2 * big + 1008) == -1   # y overlaps the end of gamma (1 KiB)
     assert qg.qg_last_error()
 
 
@@ -120,9 +125,12 @@ def test_moe_rmsnorm_validation():
     lib = qg.load()
     ws = qg.moe_expert_ffn_workspace_size(2, 16, 512, 256, 4)
 
-    def call(fmt=3, gamma=P, eps=1e-6, x=P, t=2, ws_bytes=ws):
-        return lib.moe_expert_ffn_rmsnorm(fmt, P, P, 16, 512, 256, 4, x, gamma, ctypes.c_float(eps), P + 64,
-                                          P + 128, P + 192, t, 0, P + 256, P + 512, ws_bytes, None)
+    big = 1 << 24  # distinct, non-overlapping fake buffers
+    wsp = P + 7 * big
+
+    def call(fmt=3, gamma=P + 6 * big, eps=1e-6, x=P + big, t=2, ws_bytes=ws):
+        return lib.moe_expert_ffn_rmsnorm(fmt, P, P, 16, 512, 256, 4, x, gamma, ctypes.c_float(eps), P + 2 * big,
+                                          P + 3 * big, P + 4 * big, t, 0, P + 5 * big, wsp, ws_bytes, None)
 
     assert call(gamma=None) == -1
     assert call(gamma=P + 4) == -3
@@ -131,6 +139,8 @@ def test_moe_rmsnorm_validation():
     assert call(fmt=0) == -1            # the plain layer's checks come first
     assert call(t=9) == -4
     assert call(ws_bytes=ws - 16) == -4
+    assert call(gamma=wsp + 512) == -1   # gamma inside the workspace
+    assert call(x=P + 5 * big - 64) == -1  # x overlaps out
     assert qg.qg_last_error()
 
 
@@ -151,6 +161,9 @@ def test_device_quantizer_validation():
     assert lib.qrequant(3, P, 4, P + big, 4, 256, P + big + 16, ws, P + 3 * big, None) == -1  # ws/dst overlap
     assert lib.qrequant(3, P, 5, P + big, 4, 256, P + 2 * big, ws, P + 3 * big, None) == -6  # dst tern
     assert lib.qrequant(9, P, 4, P + big, 4, 256, P + 2 * big, ws, P + 3 * big, None) == -1  # unknown src
+    assert lib.qrequant(3, P, 4, P + big, 4, 256, P + 2 * big, ws, P + big + 4, None) == -1  # status in dst
+    assert lib.qquant_device(3, P, 4, 256, P + 1024, P + 8192, None) == -1          # out overlaps w (4 KiB)
+    assert lib.qquant_device(3, P, 4, 256, P + 8192, P + 8192 + 16, None) == -1     # status in out
     assert qg.qg_last_error()
 
 

@@ -28,6 +28,9 @@ def make_blocks(fmt, n, k, seed=0, tid=0):
     if fmt == "bin":
         return OF.bin_from_codes(workloads.binary_codes(n, k, seed, tid),
                                  workloads.scale_bits_f16((n, k // 128), seed, tid + 1))
+    if fmt == "bin8":
+        return OF.bin8_from_codes(workloads.binary_codes(n, k, seed, tid),
+                                  workloads.scale_bits_f16((n, k // 128), seed, tid + 1))
     return OF.quantize(fmt, workloads.student_t_weights(n, k, seed, tid))
 
 
@@ -65,9 +68,18 @@ def test_dequant_bit_exact(fmt, n, kb):
 
 @pytest.mark.parametrize("fmt", OF.FORMATS)
 def test_dequant_subnormal_and_signed_scales(fmt):
-    """fp16 subnormal and negative scales must decode exactly (no flushing)."""
+    """fp16 subnormal and negative scales must decode exactly (no flushing);
+    bin8: fp32 subnormal, negative and zero-step per-row (base, step) pairs."""
     n, k = 4, 512
     blk = make_blocks(fmt, n, k, seed=2)
+    if fmt == "bin8":
+        blk["base"] = np.array([1e-40, -0.75, 3.0, 0.0], np.float32)
+        blk["step"] = np.array([1e-41, 2.0 ** -10, 0.0, -1e-3], np.float32)
+        out = torch.empty((n, k), device="cuda")
+        qg.qg_dequant(fmt, dev(OF.pack(fmt, blk)), out, n, k)
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(out.cpu().numpy().view(np.uint32), OF.dequant(fmt, blk).view(np.uint32))
+        return
     blk["d"] = blk["d"].copy()
     blk["d"][0] = 0x0001          # smallest fp16 subnormal
     blk["d"][1] = 0x03FF          # largest fp16 subnormal
@@ -140,7 +152,11 @@ def test_gemv_integer_exact(fmt):
     g = np.random.default_rng(6)
     n, k = 33, 1024
     blk = make_blocks(fmt, n, k, seed=6)
-    blk["d"] = np.full_like(blk["d"], 0x3C00)      # 1.0
+    if fmt == "bin8":  # scales 0.5 + c/256 for the random codes c: exact in fp32
+        blk["base"] = np.full(n, 0.5, np.float32)
+        blk["step"] = np.full(n, 1 / 256, np.float32)
+    else:
+        blk["d"] = np.full_like(blk["d"], 0x3C00)      # 1.0
     if "dmin" in blk:
         blk["dmin"] = np.full_like(blk["dmin"], 0x3800)  # 0.5
     if "m" in blk:
@@ -206,11 +222,12 @@ def check_sampled_bytes(fmt, packed, sub, rows, n, k):
     mpr = (k // spec.block) * spec.meta_bytes
     cp = OF.codes_plane_size(fmt, n, k)
     codes_rows = OF.deinterleave_rows(packed[:cp], n, cpr)
-    meta_rows = OF.deinterleave_rows(packed[cp:], n, mpr)
+    meta_rows = OF.deinterleave_rows(packed[cp:cp + n * mpr], n, mpr)
     sub_packed = OF.pack(fmt, sub)
     scp = OF.codes_plane_size(fmt, len(rows), k)
     np.testing.assert_array_equal(codes_rows[rows], OF.deinterleave_rows(sub_packed[:scp], len(rows), cpr))
-    np.testing.assert_array_equal(meta_rows[rows], OF.deinterleave_rows(sub_packed[scp:], len(rows), mpr))
+    np.testing.assert_array_equal(meta_rows[rows],
+                                  OF.deinterleave_rows(sub_packed[scp:scp + len(rows) * mpr], len(rows), mpr))
 
 
 @pytest.mark.parametrize("n,k", [(4096, 4096), (14336, 4096)])
@@ -229,7 +246,7 @@ def test_full_size_sampled_rows(fmt, n, k, b):
 
 
 @pytest.mark.parametrize("n,k", [(12288, 4096), (4096, 12288)])
-@pytest.mark.parametrize("fmt", ["q2_k", "tern", "bin"])
+@pytest.mark.parametrize("fmt", ["q2_k", "tern", "bin", "bin8"])
 @pytest.mark.parametrize("b", [1, 4, 8])
 def test_full_size_low_bit_sampled_rows(fmt, n, k, b):
     """The low-bit formats at the bench's full sizes: Q2_K from the C++
@@ -247,10 +264,17 @@ def test_full_size_low_bit_sampled_rows(fmt, n, k, b):
         if fmt == "tern":
             packed = qg.qpack_tern(codes, scales)
             sub = OF.tern_from_codes(codes[rows], scales[rows])
-        else:
+        elif fmt == "bin":
             packed = qg.qpack_bin(codes, scales)
             sub = OF.bin_from_codes(codes[rows], scales[rows])
+        else:
+            packed = qg.qpack_bin8(codes, scales)
+            sub = OF.bin8_from_codes(codes[rows], scales[rows])
     y = run_gemv(fmt, packed, x, n, k)
+    if fmt == "bin8":  # the per-row plane after the meta plane, row by row
+        tail = packed[-8 * n:].view("<f4").reshape(n, 2)
+        np.testing.assert_array_equal(tail[rows, 0], sub["base"])
+        np.testing.assert_array_equal(tail[rows, 1], sub["step"])
     check_sampled_rows(fmt, packed, sub, rows, n, k, x, y)
 
 

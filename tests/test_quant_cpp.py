@@ -53,6 +53,17 @@ def test_tern_bin_packers_identical():
     np.testing.assert_array_equal(qg.qpack_bin(bits, sc), OF.pack("bin", OF.bin_from_codes(bits, sc)))
 
 
+@pytest.mark.parametrize("n,k", [(9, 384), (17, 128), (40, 2048), (3, 128 * 300)])
+def test_bin8_packer_identical(n, k):
+    """The C++ bin8 packer (per-row affine re-coding of the fp16 scales)
+    against the oracle's, byte for byte: ragged groups, meta rows with and
+    without a short unit, a one-block row (step 0) and long rows."""
+    bits = workloads.binary_codes(n, k, seed=k)
+    sc = workloads.scale_bits_f16((n, k // 128), seed=k, tensor_id=1)
+    sc[0] = sc[0, 0]  # a row of equal scales
+    np.testing.assert_array_equal(qg.qpack_bin8(bits, sc), OF.pack("bin8", OF.bin8_from_codes(bits, sc)))
+
+
 def test_quantizer_errors():
     w = np.ones((2, 256), np.float32)
     w[1, 3] = np.inf
@@ -73,4 +84,10 @@ def test_quantizer_errors():
     assert e.value.code == -1
     with pytest.raises(qg.QGError) as e:
         qg.qpack_bin(np.full((1, 128), 3, np.uint8), np.zeros((1, 1), np.uint16))
+    assert e.value.code == -1
+    with pytest.raises(qg.QGError) as e:
+        qg.qpack_bin8(np.zeros((1, 256), np.uint8), np.array([[0x3C00, 0x7E00]], np.uint16))  # NaN scale
+    assert e.value.code == -1
+    with pytest.raises(qg.QGError) as e:
+        qg.qquant("bin8", np.zeros((1, 128), np.float32))
     assert e.value.code == -1
