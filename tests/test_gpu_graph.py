@@ -66,3 +66,52 @@ def test_graph_capture_before_any_eager_call():
         g.replay()
         torch.cuda.synchronize()
         assert torch.equal(y.view(torch.int32), y_eager.view(torch.int32)), rep
+
+
+def test_graph_norm_gemv_and_requant_replays():
+    """A captured decode-layer fragment: the norm-fed GEMV (bin8 and Q4_K, two
+    batch sizes) and a device re-quantization with its status word; every
+    replay equals the eager results bit for bit, with eager work that
+    overwrites the outputs, the workspace and the status in between."""
+    n, k = 300, 2048
+    g8 = np.random.default_rng(5)
+    bits = workloads.binary_codes(n, k, 5, 1)
+    sc = workloads.scale_bits_f16((n, k // 128), 5, 2)
+    w8 = torch.from_numpy(OF.pack("bin8", OF.bin8_from_codes(bits, sc))).cuda()
+    blk = OF.quantize("q4_k", workloads.student_t_weights(n, k, 5, 3))
+    wk = torch.from_numpy(OF.pack("q4_k", blk)).cuda()
+    x = torch.from_numpy((workloads.normal((3, k), 5, 4) * 6).astype(np.float32)).cuda()
+    gamma = torch.from_numpy((1 + 0.25 * g8.standard_normal(k)).astype(np.float32)).cuda()
+    ya, yb = torch.empty((1, n), device="cuda"), torch.empty((3, n), device="cuda")
+    q2 = torch.empty(qg.qg_packed_size("q2_k", n, k), dtype=torch.uint8, device="cuda")
+    ws_bytes = qg.qrequant_workspace_size(n, k)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
+    status = torch.empty(1, dtype=torch.int32, device="cuda")
+
+    def fragment(stream=None):
+        qg.qgemv_rmsnorm("bin8", w8, x[:1], gamma, 1e-5, ya, n, k, 1, stream=stream)
+        qg.qgemv_rmsnorm("q4_k", wk, x, gamma, 1e-5, yb, n, k, 3, stream=stream)
+        qg.qrequant("q4_k", wk, "q2_k", q2, n, k, ws, ws_bytes, status, stream=stream)
+
+    fragment()
+    torch.cuda.synchronize()
+    eager = [ya.clone(), yb.clone(), q2.clone()]
+    assert int(status.item()) == 0
+    np.testing.assert_array_equal(eager[2].cpu().numpy(),
+                                  OF.pack("q2_k", OF.quantize("q2_k", OF.dequant("q4_k", blk))))
+    stream = torch.cuda.Stream()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        fragment(stream)
+    for rep in range(4):
+        ya.fill_(float("nan"))
+        yb.fill_(float("nan"))
+        q2.fill_(0x5A)
+        ws.fill_(0xAB)
+        status.fill_(-99)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert int(status.item()) == 0, rep
+        for got, want in zip((ya, yb, q2), eager):
+            assert torch.equal(got, want), rep
