@@ -9,7 +9,8 @@
  * token.  Batch B stacks activation rows: Y[b][n] = sum_k W[n][k] * X[b][k].
  * The block formats are those of the same page, section "GGUF 的量化格式"
  * (Q8_0, Q4_0, Q4_1, Q4_K), plus Q2_K, ternary weights in 2-bit fields and
- * 1-bit sign weights from the low-bit README page's kernel table, and the
+ * 1-bit sign weights (with fp16 block scales, or 8-bit per-row affine ones)
+ * from the low-bit README page's kernel table, and the
  * Flash-MoE page's 2-bit experts.  The MoE layer follows the Flash-MoE page,
  * sections "模型架构", "Metal 计算着色器" and "每层流水线".
  *
@@ -30,7 +31,7 @@
  * Packed matrix layout (one [N][K] matrix, format f with block size bs):
  *   [codes plane][meta plane], codes plane = N*(K/bs)*code_bytes bytes,
  *   meta plane = N*(K/bs)*meta_bytes bytes; total qg_packed_size() =
- *   N*K*bpw/8 exactly.  Each plane is the row-major image of its rows (row n:
+ *   N*K*bpw/8 exactly (BIN8: plus its per-row plane below).  Each plane is the row-major image of its rows (row n:
  *   its blocks' code bytes, resp. meta bytes, in block order) interleaved by
  *   groups of 16 rows (the low-bit README page's row repack for dot-product
  *   lanes): group g holds rows 16g .. 16g+n_g-1 (n_g = min(16, N-16g)) and
@@ -47,11 +48,15 @@
  *                                           fp16 d, fp16 dmin
  *     TERN    128  32      2       2.125  fp16 scale; 2-bit field = t + 1
  *     BIN     128  16      2       1.125  fp16 scale; bit 1 = +1, 0 = -1
+ *     BIN8    128  16      1       1.0625 scale code c; bits as BIN
+ *   BIN8 adds a third plane: the meta plane is zero-padded to a multiple of
+ *   16 bytes and followed by N rows of (base, step), two little-endian fp32;
+ *   the block scale is fp32(base + fp32(step * c)) (see qpack_bin8).
  *   Nibble i of a block sits in byte i>>1 (low nibble for even i); 2-bit field
  *   i in byte i>>2 at bits 2*(i&3); bit i in byte i>>3 at bit i&7.  All
  *   multi-byte values are little-endian.  Decoded weights:
  *     Q8_0 q*d; Q4_0 (n-8)*d; Q4_1 n*d+m; Q4_K/Q2_K n*(s_j*d) - t_j*dmin;
- *     TERN (f-1)*scale; BIN (2*bit-1)*scale.
+ *     TERN (f-1)*scale; BIN, BIN8 (2*bit-1)*scale.
  */
 #ifndef QGEMV_H
 #define QGEMV_H
