@@ -145,6 +145,20 @@ def test_gemv_short_blocks(fmt, k):
     assert_parity(y, OF.dequant(fmt, blk), x, f"{fmt} K={k}")
 
 
+@pytest.mark.parametrize("fmt", ["tern", "bin", "bin8"])
+@pytest.mark.parametrize("k", [128, 384, 1152, 2176, 4224])
+@pytest.mark.parametrize("b", [1, 3, 8])
+def test_gemv_odd_unit_counts(fmt, k, b):
+    """128-weight formats at K = 128 * odd: an odd number of blocks per row, so
+    parts of two units end half outside the row and meta rows end in a short
+    unit (bin8: one byte per block)."""
+    n = 37
+    blk = make_blocks(fmt, n, k, seed=12, tid=k + b)
+    x = workloads.normal((b, k), 12, k + b)
+    y = run_gemv(fmt, OF.pack(fmt, blk), x, n, k)
+    assert_parity(y, OF.dequant(fmt, blk), x, f"{fmt} B={b} K={k}")
+
+
 @pytest.mark.parametrize("fmt", OF.FORMATS)
 def test_gemv_integer_exact(fmt):
     """Power-of-two scales and small-integer activations: every product and
