@@ -358,9 +358,13 @@ def cpu_baseline(seconds=12.0):
     packed = OF.quantize_packed("q4_k", w)
     x = workloads.normal((1, k), 0, 99)
     reps = 0
+    t_deq = 0.0
     t0 = time.perf_counter()
     while True:
-        OG.gemv_ref(OF.dequant_packed("q4_k", packed, n, k), x)
+        t1 = time.perf_counter()
+        w_deq = OF.dequant_packed("q4_k", packed, n, k)
+        t_deq += time.perf_counter() - t1
+        OG.gemv_ref(w_deq, x)
         reps += 1
         el = time.perf_counter() - t0
         if el >= seconds:
@@ -373,7 +377,8 @@ def cpu_baseline(seconds=12.0):
     except Exception:
         pass
     return {"value": round(packed.size * reps / el / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
-            "sample": f"{reps} full Q4_K 14336x4096 batch-1 GEMVs (unpack + dequant + float64 matvec), {el:.1f} s"}
+            "sample": f"{reps} full Q4_K 14336x4096 batch-1 GEMVs (unpack + dequant + float64 matvec), {el:.1f} s; "
+                      f"unpack + dequant {100 * t_deq / el:.0f} % of it"}
 
 
 def main():
