@@ -23,7 +23,7 @@ __all__ = [
     "FORMATS", "QG_MOE_RENORM", "QGError", "QGLibraryMissing", "lib_path", "load",
     "qg_packed_size", "qg_codes_plane_size", "qg_codes_plane_offset", "qg_block_size", "qgemv_workspace_size",
     "qgemv", "qgemv_q8_0", "qgemv_q4_0", "qgemv_q4_1", "qgemv_q4k", "qgemv_q2k",
-    "qgemv_tern", "qgemv_bin", "qgemv_rmsnorm", "qg_dequant", "qquant", "qquant_device", "qrequant_workspace_size", "qrequant",
+    "qgemv_tern", "qgemv_bin", "qgemv_bin8", "qgemv_rmsnorm", "qg_dequant", "qquant", "qquant_device", "qrequant_workspace_size", "qrequant",
     "qpack_tern", "qpack_bin", "qpack_bin8",
     "moe_expert_ffn_workspace_size", "moe_expert_ffn", "moe_expert_ffn_rmsnorm", "qg_strerror", "qg_last_error",
     "qg_version", "EXPORTED_SYMBOLS",
@@ -56,6 +56,7 @@ _SIGNATURES = {
     "qgemv_q2k": (_i32, _GEMV_ARGS),
     "qgemv_tern": (_i32, _GEMV_ARGS),
     "qgemv_bin": (_i32, _GEMV_ARGS),
+    "qgemv_bin8": (_i32, _GEMV_ARGS),
     "qgemv_rmsnorm": (_i32, [_i32, _vp, _vp, _vp, ctypes.c_float, _vp, _i64, _i64, _i32, _vp]),
     "qg_dequant": (_i32, [_i32, _vp, _vp, _i64, _i64, _vp]),
     "qquant": (_i32, [_i32, _vp, _i64, _i64, _vp, _i32]),
@@ -237,6 +238,7 @@ qgemv_q4k = _named("qgemv_q4k", "q4_k")
 qgemv_q2k = _named("qgemv_q2k", "q2_k")
 qgemv_tern = _named("qgemv_tern", "tern")
 qgemv_bin = _named("qgemv_bin", "bin")
+qgemv_bin8 = _named("qgemv_bin8", "bin8")
 
 
 def qgemv_rmsnorm(fmt, w, x, gamma, eps: float, y, n: int, k: int, b: int = 1, stream=None) -> None:

@@ -251,6 +251,7 @@ QG_GEMV_ALIAS(qgemv_q4k, QG_Q4_K)
 QG_GEMV_ALIAS(qgemv_q2k, QG_Q2_K)
 QG_GEMV_ALIAS(qgemv_tern, QG_TERN)
 QG_GEMV_ALIAS(qgemv_bin, QG_BIN)
+QG_GEMV_ALIAS(qgemv_bin8, QG_BIN8)
 #undef QG_GEMV_ALIAS
 
 int qg_dequant(int fmt, const void* w, float* out, int64_t N, int64_t K, void* stream) {

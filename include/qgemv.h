@@ -151,6 +151,8 @@ int qgemv_tern(const void* w, const float* x, float* y, int64_t N, int64_t K, in
                void* ws, size_t ws_bytes, void* stream);
 int qgemv_bin(const void* w, const float* x, float* y, int64_t N, int64_t K, int B,
               void* ws, size_t ws_bytes, void* stream);
+int qgemv_bin8(const void* w, const float* x, float* y, int64_t N, int64_t K, int B,
+               void* ws, size_t ws_bytes, void* stream);
 
 /* ------------------------------------------------- GEMV on normalised x */
 

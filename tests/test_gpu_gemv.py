@@ -297,3 +297,21 @@ def test_decode_step_shapes_sampled_rows(n, k):
     """The 8B step's k/v and down shapes (Q4_K, batch 1) at full size, sampled
     rows against the oracle as in the full-size test."""
     test_full_size_sampled_rows("q4_k", n, k, 1)
+
+
+ALIASES = {"q8_0": "qgemv_q8_0", "q4_0": "qgemv_q4_0", "q4_1": "qgemv_q4_1", "q4_k": "qgemv_q4k",
+           "q2_k": "qgemv_q2k", "tern": "qgemv_tern", "bin": "qgemv_bin", "bin8": "qgemv_bin8"}
+
+
+@pytest.mark.parametrize("fmt", OF.FORMATS)
+def test_per_format_entry_points_match_qgemv(fmt):
+    """Each per-format entry point is qgemv with its format: same bits."""
+    n, k, b = 70, 1024, 3
+    blk = make_blocks(fmt, n, k, seed=13)
+    w_d, x_d = dev(OF.pack(fmt, blk)), dev(workloads.normal((b, k), 13, 1))
+    y1 = torch.empty((b, n), device="cuda")
+    y2 = torch.empty((b, n), device="cuda")
+    qg.qgemv(fmt, w_d, x_d, y1, n, k, b)
+    getattr(qg, ALIASES[fmt])(w_d, x_d, y2, n, k, b)
+    torch.cuda.synchronize()
+    assert torch.equal(y1.view(torch.int32), y2.view(torch.int32))
