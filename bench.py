@@ -393,7 +393,7 @@ def main():
                          "the 8B step, or the RMS-norm GEMVs and MoE block step) for rocprofv3")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py: this build measures one GPU; --gpus {args.gpus} is not supported "
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "
               "(the GEMV is measured on one GPU's share; no collectives are built)", file=sys.stderr)
         sys.exit(2)
 

@@ -86,7 +86,7 @@ enum {
     QG_EALIGN = -3,      /* a pointer misses its required alignment            */
     QG_ERANGE = -4,      /* B out of range, a scale overflowing fp16, ...      */
     QG_EHIP = -5,        /* a HIP launch or runtime call failed                */
-    QG_EUNSUPPORTED = -6 /* a valid request this build does not implement      */
+    QG_EUNSUPPORTED = -6 /* a valid request the library does not implement     */
 };
 
 /* Flags for moe_expert_ffn. */
