@@ -369,3 +369,39 @@ def test_q4k_matches_scalar_loop():
                 assert list(blk["s"][r, sb]) == s
                 assert list(blk["t"][r, sb]) == t
                 assert list(blk["n"][r, sb * 256:(sb + 1) * 256]) == n
+
+
+# planted mistakes in copies of the bin8 re-coding (R9), each caught by a pin above
+
+def _bin8_mutant(kind):
+    def recode(bits, scale_bits):
+        n, k = np.asarray(bits).shape
+        d = F.from_f16_bits(np.asarray(scale_bits, np.uint16).reshape(n, k // 128))
+        base = d.min(axis=1)
+        div = F32(256) if kind == "divisor" else F32(255)
+        step = ((d.max(axis=1) - base) / div).astype(F32)
+        q = (d - base[:, None]) / np.where(step == 0, F32(1), step)[:, None]
+        q = np.floor(q) if kind == "floor" else np.rint(q)
+        c = np.where(step[:, None] == 0, 0, np.clip(q, 0, 255)).astype(np.uint8)
+        if kind == "max_base":
+            base = d.max(axis=1)
+        return {"b": np.asarray(bits, np.uint8), "c": c, "base": base.astype(F32), "step": step}
+    return recode
+
+
+@pytest.mark.parametrize("kind", ["divisor", "floor", "max_base"])
+def test_bin8_planted_mistakes_fail(kind):
+    mutant = _bin8_mutant(kind)
+    n, k = 3, 256 * 128
+    c = np.stack([np.arange(256), np.arange(255, -1, -1), (np.arange(256) * 7) % 256]).astype(np.uint8)
+    d16 = F.to_f16_bits((0.5 + c.astype(np.float64) / 256).astype(F32))
+    bits = workloads.binary_codes(n, k, seed=3)
+    blk = mutant(bits, d16)
+    exact = np.array_equal(F.dequant("bin8", blk), F.dequant("bin", F.bin_from_codes(bits, d16)))
+    # the rounding-bound pin on random scales
+    sc = workloads.scale_bits_f16((6, 40), seed=4)
+    b2 = mutant(workloads.binary_codes(6, 40 * 128, seed=4), sc)
+    d = F.from_f16_bits(sc).astype(np.float64)
+    bound = b2["step"].astype(np.float64)[:, None] / 2 + 2 * np.abs(d) * 2.0 ** -24
+    within = bool(np.all(np.abs(F.bin8_scales(b2).astype(np.float64) - d) <= bound))
+    assert not (exact and within), f"{kind} passes both pins"
