@@ -104,11 +104,12 @@ class Gemv:
         self.fid = qg.FORMATS[fmt]
         self.wp = [t.data_ptr() for t in self.w]
         self.xp, self.yp = self.x.data_ptr(), self.y.data_ptr()
-        # rmsnorm: the same GEMV fed by RMS norm of x (gain gamma, eps 1e-5)
+        # rmsnorm: the same GEMV fed by RMS norm of x (gain gamma, eps 1e-5);
+        # "unit": unit gain, the gain folded into the weights (no gamma read)
         self.rmsnorm = rmsnorm
         if rmsnorm:
             self.gamma = torch.from_numpy(1.0 + 0.25 * workloads.normal((k,), seed, 98)).float().to("cuda")
-            self.gp = self.gamma.data_ptr()
+            self.gp = None if rmsnorm == "unit" else self.gamma.data_ptr()
         self.stream = stream
         self.sp = stream.cuda_stream
         self.i = 0
@@ -242,7 +243,8 @@ def dense_step(torch, qg, stream):
     gammas = [workloads.normal_device((2, 4096), 0, 900 + j) * 0.25 + 1.0 for j in range(DENSE_LAYERS)]
 
     def gemv_norm(w, n, k, gamma):
-        wp, xp, yp, gp = w.data_ptr(), xs[k].data_ptr(), ys[n].data_ptr(), gamma.data_ptr()
+        wp, xp, yp = w.data_ptr(), xs[k].data_ptr(), ys[n].data_ptr()
+        gp = None if gamma is None else gamma.data_ptr()
         return lambda: lib.qgemv_rmsnorm(fid, wp, xp, gp, 1e-5, yp, n, k, 1, sp)
 
     launches = []
@@ -250,6 +252,12 @@ def dense_step(torch, qg, stream):
         launches += [gemv_norm(layer["qkv"], 6144, 4096, gm[0]), gemv(layer["o"], 4096, 4096),
                      gemv_norm(layer["gateup"], 28672, 4096, gm[1]), gemv(layer["down"], 4096, 14336)]
     t_norm, _ = graph_time(torch, stream, launches, 20)
+    # the gains folded into q/k/v and gate/up (same bytes), unit-gain norms at run time
+    launches = []
+    for layer in dev:
+        launches += [gemv_norm(layer["qkv"], 6144, 4096, None), gemv(layer["o"], 4096, 4096),
+                     gemv_norm(layer["gateup"], 28672, 4096, None), gemv(layer["down"], 4096, 14336)]
+    t_fold, _ = graph_time(torch, stream, launches, 20)
     del dev, launches, gammas
     torch.cuda.empty_cache()
     return {"layers": DENSE_LAYERS, "bytes": total,
@@ -257,7 +265,9 @@ def dense_step(torch, qg, stream):
             "tok_s": round(1.0 / t, 1), "GBps": round(total / t / 1e9, 1),
             "fused_launches": DENSE_LAYERS * 4, "fused_step_us": round(t_fused * 1e6, 1),
             "fused_tok_s": round(1.0 / t_fused, 1), "fused_GBps": round(total / t_fused / 1e9, 1),
-            "fused_with_norms_step_us": round(t_norm * 1e6, 1), "fused_with_norms_tok_s": round(1.0 / t_norm, 1)}
+            "fused_with_norms_step_us": round(t_norm * 1e6, 1), "fused_with_norms_tok_s": round(1.0 / t_norm, 1),
+            "fused_with_folded_norms_step_us": round(t_fold * 1e6, 1),
+            "fused_with_folded_norms_tok_s": round(1.0 / t_fold, 1)}
 
 
 MOE_E, MOE_H, MOE_I, MOE_TOPK, MOE_POOL, MOE_SETS = 512, 4096, 1024, 4, 8, 32
@@ -425,7 +435,7 @@ def main():
     if args.profile == "norm":
         for n, k in ((14336, 4096), (4096, 4096)):
             for b in (1, 8):
-                for norm in (False, True):
+                for norm in (False, True, "unit"):
                     g = Gemv(torch, qg, "q4_k", n, k, b, 0, COLD_BYTES, stream, norm)
                     g.capture()
                     g.replay(2)
@@ -523,12 +533,14 @@ def main():
                     log(f"  {fmt} {n}x{k} B={b}: {t*1e6:.2f} us, {nbytes/t/1e9:.1f} GB/s")
         extra["low_bit"] = rows
         rows = []
-        for n, k in ((14336, 4096), (4096, 4096)):
-            for b in (1, 8):
-                t, nbytes = measure("q4_k", n, k, b, rmsnorm=True)
-                rows.append({"fmt": "q4_k", "N": n, "K": k, "B": b, "us": round(t * 1e6, 2),
-                             "GBps": round(nbytes / t / 1e9, 1)})
-                log(f"  rmsnorm + q4_k {n}x{k} B={b}: {t*1e6:.2f} us, {nbytes/t/1e9:.1f} GB/s")
+        for gain in (True, "unit"):
+            for n, k in ((14336, 4096), (4096, 4096)):
+                for b in (1, 8):
+                    t, nbytes = measure("q4_k", n, k, b, rmsnorm=gain)
+                    rows.append({"fmt": "q4_k", "N": n, "K": k, "B": b, "gain": "folded" if gain == "unit" else "vector",
+                                 "us": round(t * 1e6, 2), "GBps": round(nbytes / t / 1e9, 1)})
+                    log(f"  rmsnorm ({rows[-1]['gain']} gain) + q4_k {n}x{k} B={b}: {t*1e6:.2f} us, "
+                        f"{nbytes/t/1e9:.1f} GB/s")
         extra["rmsnorm_gemv"] = rows
         log("8B decode step (32 layers x 7 Q4_K GEMVs)")
         extra["dense_8b_step"] = dense_step(torch, qg, stream)

@@ -242,7 +242,8 @@ qgemv_bin8 = _named("qgemv_bin8", "bin8")
 
 
 def qgemv_rmsnorm(fmt, w, x, gamma, eps: float, y, n: int, k: int, b: int = 1, stream=None) -> None:
-    """y[b] = W rmsnorm(x[b]; gamma, eps) on the device (see qgemv_rmsnorm in qgemv.h)."""
+    """y[b] = W rmsnorm(x[b]; gamma, eps) on the device (see qgemv_rmsnorm in qgemv.h);
+    gamma=None means unit gain (gamma folded into the weights)."""
     f32, u8 = _torch_dtypes()
     rc = load().qgemv_rmsnorm(_fmt(fmt), _dev(w, u8, "w"), _dev(x, f32, "x"), _dev(gamma, f32, "gamma"),
                               float(eps), _dev(y, f32, "y"), n, k, b, _stream(stream))

@@ -665,21 +665,22 @@ struct GemvDpp {
     // x_k -> x_k * gamma_k / sqrt(mean_k x_k^2 + eps), per batch row.  The
     // waves that load x also sum its squares (every column once), gamma is
     // applied to x in registers, and the 1/rms of each batch row scales the
-    // finished row sums, so the normalised x is never stored.
-    template <class XRow, class Epi>
+    // finished row sums, so the normalised x is never stored.  GAMMA false:
+    // unit gain (gamma folded into W by the caller), no gamma loads.
+    template <bool GAMMA = true, class XRow, class Epi>
     __device__ static void run_rmsnorm(const uint8_t* __restrict__ codes, const uint8_t* __restrict__ meta,
                                        int N, int K, int g, XRow xrow, int nb, const float* __restrict__ gamma,
                                        float eps, Epi epi) {
         __shared__ float red[W * kRowGroup * B];
         __shared__ float red_ss[W * B];
-        run_group<true>(codes, meta, N, K, g, xrow, nb, epi, 0, red, gamma, eps, red_ss);
+        run_group<true, GAMMA>(codes, meta, N, K, g, xrow, nb, epi, 0, red, gamma, eps, red_ss);
     }
 
     // The same on waves [wave0, wave0 + W) of a larger workgroup, with the
     // cross-wave partials in red (W * 16 * B floats of LDS).  Every wave of the
     // workgroup must call it (it synchronizes the whole workgroup once).
-    // NORM: see run_rmsnorm; red_ss holds W * B floats.
-    template <bool NORM = false, class XRow, class Epi>
+    // NORM, GAMMA: see run_rmsnorm; red_ss holds W * B floats.
+    template <bool NORM = false, bool GAMMA = true, class XRow, class Epi>
     __device__ static void run_group(const uint8_t* __restrict__ codes, const uint8_t* __restrict__ meta,
                                      int N, int K, int g, XRow xrow, int nb, Epi epi, int wave0, float* red,
                                      const float* __restrict__ gamma = nullptr, float eps = 0.0f,
@@ -727,8 +728,8 @@ struct GemvDpp {
 
                 // (1) x of the part, four columns per lane per span
                 float4 xv[B][NX4];
-                float4 gv[NORM ? NX4 : 1];  // gamma of the same columns (NORM)
-                if constexpr (NORM) {
+                float4 gv[NORM && GAMMA ? NX4 : 1];  // gamma of the same columns
+                if constexpr (NORM && GAMMA) {
 #pragma unroll
                     for (int m = 0; m < NX4; ++m) {
                         const uint32_t c = (uint32_t)(FULL ? k0 + 64 * m + 4 * r : min(k0 + 64 * m + 4 * r, K - 4));
@@ -754,12 +755,15 @@ struct GemvDpp {
                         if (b >= nb) continue;
 #pragma unroll
                         for (int m = 0; m < NX4; ++m) {
-                            const float4 v = xv[b][m], g4 = gv[m];
+                            const float4 v = xv[b][m];
                             // each column once: the lanes of a part tile it, parts are
                             // disjoint, and clamped columns past K are not added
                             const float sq = fmaf(v.w, v.w, fmaf(v.z, v.z, fmaf(v.y, v.y, fmaf(v.x, v.x, ss[b]))));
                             if (FULL || k0 + 64 * m + 4 * r < K) ss[b] = sq;
-                            xv[b][m] = make_float4(v.x * g4.x, v.y * g4.y, v.z * g4.z, v.w * g4.w);
+                            if constexpr (GAMMA) {
+                                const float4 g4 = gv[m];
+                                xv[b][m] = make_float4(v.x * g4.x, v.y * g4.y, v.z * g4.z, v.w * g4.w);
+                            }
                         }
                     }
                 }

@@ -32,13 +32,13 @@ constexpr int norm_waves_per_eu() {
     return F == QG_Q4_K && B == 8 ? 4 : 1;
 }
 
-template <int F, int B, int W, int KCS>
+template <int F, int B, int W, int KCS, bool GAMMA>
 __global__ void __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(norm_waves_per_eu<F, B>())))
 gemv_rmsnorm_kernel(const uint8_t* __restrict__ codes, const uint8_t* __restrict__ meta,
                     const float* __restrict__ x, const float* __restrict__ gamma, float eps,
                     float* __restrict__ y, int N, int K) {
     const int g = blockIdx.x;
-    GemvDpp<F, B, W, KCS>::run_rmsnorm(
+    GemvDpp<F, B, W, KCS>::template run_rmsnorm<GAMMA>(
         codes, meta, N, K, g, [&](int b) { return x + (size_t)b * K; }, B, gamma, eps,
         [&](auto sums, int n_g, int tid) {
             for (int t = tid; t < kRowGroup * B; t += W * 64)
@@ -46,16 +46,19 @@ gemv_rmsnorm_kernel(const uint8_t* __restrict__ codes, const uint8_t* __restrict
         });
 }
 
-template <int F, int B, int W, int KCS>
-struct RmsNormGemv {
+template <int F, int B, int W, int KCS, bool GAMMA>
+struct RmsNormGemvG {
     static hipError_t launch(dim3 grid, dim3 block, hipStream_t st, const uint8_t* codes, const uint8_t* meta,
                              const float* x, const float* gamma, float eps, float* y, int N, int K) {
-        hipLaunchKernelGGL((gemv_rmsnorm_kernel<F, B, W, KCS>), grid, block, 0, st, codes, meta, x, gamma, eps, y,
-                           N, K);
+        hipLaunchKernelGGL((gemv_rmsnorm_kernel<F, B, W, KCS, GAMMA>), grid, block, 0, st, codes, meta, x, gamma,
+                           eps, y, N, K);
         return hipGetLastError();
     }
-    static int resident() { return resident_blocks(gemv_rmsnorm_kernel<F, B, W, KCS>, W * 64); }
+    static int resident() { return resident_blocks(gemv_rmsnorm_kernel<F, B, W, KCS, GAMMA>, W * 64); }
 };
+// with a gain vector, and with unit gain (gamma folded into W)
+template <int F, int B, int W, int KCS> struct RmsNormGemv : RmsNormGemvG<F, B, W, KCS, true> {};
+template <int F, int B, int W, int KCS> struct RmsNormUnitGemv : RmsNormGemvG<F, B, W, KCS, false> {};
 
 }  // namespace
 }  // namespace qg
@@ -67,14 +70,17 @@ extern "C" int qgemv_rmsnorm(int fmt, const void* w, const float* x, const float
     clear_error();
     int rc = check_gemv_args(fmt, w, x, y, N, K, B);
     if (rc) return rc;
-    if (!gamma) return fail(QG_EINVAL, "null gamma");
-    if (!aligned(gamma, 16)) return fail(QG_EALIGN, "gamma must be 16-byte aligned");
+    if (gamma && !aligned(gamma, 16)) return fail(QG_EALIGN, "gamma must be 16-byte aligned");
     if (!(eps >= 0.0f) || !std::isfinite(eps)) return fail(QG_ERANGE, "eps=%g must be finite and >= 0", (double)eps);
-    if (overlap(y, (size_t)B * N * 4, gamma, (size_t)K * 4)) return fail(QG_EINVAL, "y must not overlap gamma");
+    if (gamma && overlap(y, (size_t)B * N * 4, gamma, (size_t)K * 4))
+        return fail(QG_EINVAL, "y must not overlap gamma");
     const uint8_t* codes = static_cast<const uint8_t*>(w);
     const uint8_t* meta = codes + qg_codes_plane_size(fmt, N, K);
-    hipError_t e = core::launch_dpp<RmsNormGemv>(fmt, (int)N, (int)K, B, static_cast<hipStream_t>(stream), codes,
-                                                 meta, x, gamma, eps, y, (int)N, (int)K);
+    const hipStream_t st = static_cast<hipStream_t>(stream);
+    hipError_t e = gamma ? core::launch_dpp<RmsNormGemv>(fmt, (int)N, (int)K, B, st, codes, meta, x, gamma, eps, y,
+                                                         (int)N, (int)K)
+                         : core::launch_dpp<RmsNormUnitGemv>(fmt, (int)N, (int)K, B, st, codes, meta, x, gamma, eps,
+                                                             y, (int)N, (int)K);
     if (e != hipSuccess) return fail(QG_EHIP, "GEMV launch failed: %s", hipGetErrorString(e));
     return QG_OK;
 }

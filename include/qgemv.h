@@ -164,14 +164,16 @@ int qgemv_bin8(const void* w, const float* x, float* y, int64_t N, int64_t K, in
  * "延迟 GPU 专家计算").  The sum of squares is taken while x is loaded, gamma
  * scales x in registers and 1/rms scales each row sum, so no normalised copy
  * of x is written.
- *   gamma  DEVICE, fp32 [K], 16-byte aligned, not overlapping y.
+ *   gamma  DEVICE, fp32 [K], 16-byte aligned, not overlapping y; or NULL
+ *          for unit gain, when the caller has folded gamma into the weights
+ *          (quantizing W * diag(gamma) instead of W): then no gamma is read.
  *   eps    finite, >= 0 (a zero row with eps = 0 gives non-finite y, as the
  *          definition does).
  *   w, x, y, N, K, B, stream: as for qgemv.
  * Accuracy: |error| <= 3e-5 * sum_k |W[n][k] xhat[b][k]| + 1e-7: the qgemv
  * bound on xhat plus the fp32 sum of squares, square root and gamma product.
- * Deterministic.  Errors: as qgemv, plus QG_EINVAL (null gamma), QG_EALIGN
- * (gamma), QG_ERANGE (eps). */
+ * Deterministic.  Errors: as qgemv, plus QG_EALIGN (gamma), QG_EINVAL
+ * (gamma overlaps y), QG_ERANGE (eps). */
 int qgemv_rmsnorm(int fmt, const void* w, const float* x, const float* gamma, float eps, float* y,
                   int64_t N, int64_t K, int B, void* stream);
 

@@ -106,8 +106,8 @@ def test_gemv_rmsnorm_validation():
     def call(fmt=3, w=P, x=P + big, gamma=P + 2 * big, eps=1e-6, y=P + 3 * big, n=4, k=256, b=1):
         return lib.qgemv_rmsnorm(fmt, w, x, gamma, ctypes.c_float(eps), y, n, k, b, None)
 
-    assert call(gamma=None) == -1
     assert call(gamma=P + 4) == -3
+    assert call(gamma=None, eps=-1e-6) == -4   # unit gain: the other checks still apply
     assert call(eps=-1e-6) == -4
     assert call(eps=float("nan")) == -4
     assert call(eps=float("inf")) == -4

@@ -29,7 +29,7 @@ def gain(k, seed, tid):
 def run_norm(fmt, packed, x, gamma, eps, n, k):
     b = x.shape[0]
     y_d = torch.full((b, n), float("nan"), device="cuda")
-    qg.qgemv_rmsnorm(fmt, dev(packed), dev(x), dev(gamma), eps, y_d, n, k, b)
+    qg.qgemv_rmsnorm(fmt, dev(packed), dev(x), None if gamma is None else dev(gamma), eps, y_d, n, k, b)
     torch.cuda.synchronize()
     return y_d.cpu().numpy()
 
@@ -95,6 +95,36 @@ def test_rmsnorm_gemv_eps_cases(fmt):
     assert_norm_parity(y0, w_deq, x[[0, 2]], g, 0.0, f"{fmt} eps=0")
     yz = run_norm(fmt, packed, x[[1]], g, 0.0, n, k)
     assert np.all(np.isnan(yz))
+
+
+@pytest.mark.parametrize("fmt", OF.FORMATS)
+@pytest.mark.parametrize("b", [1, 3, 8])
+@pytest.mark.parametrize("n,kb", [(67, 4), (9, 56)])
+def test_rmsnorm_gemv_unit_gain(fmt, b, n, kb):
+    """gamma = NULL (the gain folded into W by the caller): the oracle with a
+    gain of ones."""
+    k = 256 * kb
+    blk = make_blocks(fmt, n, k, seed=27, tid=n + kb)
+    x = residual_stream(b, k, 27, b)
+    y = run_norm(fmt, OF.pack(fmt, blk), x, None, 1e-5, n, k)
+    assert_norm_parity(y, OF.dequant(fmt, blk), x, np.ones(k, np.float32), 1e-5, f"{fmt} unit gain B={b}")
+
+
+@pytest.mark.parametrize("n,k", [(14336, 4096), (1024, 4096)])
+@pytest.mark.parametrize("b", [1, 8])
+def test_rmsnorm_gemv_folded_gain_full_size(n, k, b):
+    """Full size with the gain folded into the weights before quantization
+    (W * diag(gamma), C++ quantizer) and gamma = NULL at run time; sampled
+    rows against the oracle's unit-gain normalised GEMV of the same bytes."""
+    g = gain(k, 28, 0)
+    wf = (full_weights(n, k) * g[None, :]).astype(np.float32)
+    packed = qg.qquant("q4_k", wf)
+    x = residual_stream(b, k, 28, b)
+    y = run_norm("q4_k", packed, x, None, 1e-5, n, k)
+    rows = sampled_rows(n, 5 * n + b)
+    sub = OF.quantize("q4_k", wf[rows])
+    check_sampled_bytes("q4_k", packed, sub, rows, n, k)
+    assert_norm_parity(y[:, rows], OF.dequant("q4_k", sub), x, np.ones(k, np.float32), 1e-5, f"folded {n}x{k} B={b}")
 
 
 def test_rmsnorm_gemv_deterministic():

@@ -88,6 +88,17 @@ def test_oracle_meets_pin(pin):
     assert pin(ON.gemv_rmsnorm_ref)
 
 
+def test_gain_folds_into_the_weights():
+    """W rmsnorm(x; gamma) == (W diag(gamma)) rmsnorm(x; 1): the reading that
+    gamma scales columns, which is what lets a caller fold it into W."""
+    rng = np.random.default_rng(9)
+    w, x = _w(5, 64, 11), rng.standard_normal((2, 64)).astype(F32)
+    g = (2.0 ** rng.integers(-2, 3, 64)).astype(F32)  # exact column scaling of W
+    a = ON.gemv_rmsnorm_ref(w, x, g, 1e-3)
+    b = ON.gemv_rmsnorm_ref((w * g[None, :]).astype(F32), x, np.ones(64, F32), 1e-3)
+    assert _close(a, b, 1e-12)
+
+
 def test_rms_pass_alone():
     assert _close(ON.rms([[3, 4, 0, 0]], 0.0), [2.5])
     assert _close(ON.rms([[2, 2, 2, 2]], 5.0), [3.0])
