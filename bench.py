@@ -327,12 +327,14 @@ def moe_layer(torch, qg, stream, fmt, t_tokens, norm=False):
         gamma = workloads.normal_device((h_,), 2, 78) * 0.25 + 1.0
         xs = [workloads.normal_device((t_tokens, h_), 2, 300 + r) * 6.0 for r in range(MOE_SETS)]
 
+        gp = None if norm == "unit" else gamma.data_ptr()  # "unit": gains folded into the weights
+
         def call_norm(r):
             def fn():
-                rc = lib.qgemv_rmsnorm(q8, router.data_ptr(), xs[r].data_ptr(), gamma.data_ptr(), 1e-6,
+                rc = lib.qgemv_rmsnorm(q8, router.data_ptr(), xs[r].data_ptr(), gp, 1e-6,
                                        logits[r].data_ptr(), e_, h_, t_tokens, sp)
                 rc = rc or lib.moe_expert_ffn_rmsnorm(fid, gu.data_ptr(), dn.data_ptr(), e_, h_, i_, k_,
-                                                      xs[r].data_ptr(), gamma.data_ptr(), 1e-6, xs[r].data_ptr(),
+                                                      xs[r].data_ptr(), gp, 1e-6, xs[r].data_ptr(),
                                                       logits[r].data_ptr(), slog[r].data_ptr(), t_tokens, 0,
                                                       out.data_ptr(), ws.data_ptr(), ws_bytes, sp)
                 if rc:
@@ -351,7 +353,8 @@ def moe_layer(torch, qg, stream, fmt, t_tokens, norm=False):
     nbytes = touched * (gu_sz + dn_sz) + router_bytes
     del gu, dn, ws
     torch.cuda.empty_cache()
-    return {"fmt": fmt, "T": t_tokens, "norm_block": norm, "us": round(t * 1e6, 2),
+    return {"fmt": fmt, "T": t_tokens, "norm_block": {False: False, True: "gain vector", "unit": "gain folded"}[norm],
+            "us": round(t * 1e6, 2),
             "experts_touched": round(float(touched), 2),
             "bytes": int(nbytes), "GBps": round(float(nbytes) / t / 1e9, 1)}
 
@@ -550,9 +553,10 @@ def main():
             for t_tokens in (1, 8):
                 rows.append(moe_layer(torch, qg, stream, fmt, t_tokens))
                 log(f"  moe {rows[-1]}")
-        for t_tokens in (1, 8):
-            rows.append(moe_layer(torch, qg, stream, "q4_k", t_tokens, norm=True))
-            log(f"  moe {rows[-1]}")
+        for norm in (True, "unit"):
+            for t_tokens in (1, 8):
+                rows.append(moe_layer(torch, qg, stream, "q4_k", t_tokens, norm=norm))
+                log(f"  moe {rows[-1]}")
         extra["moe_layer"] = rows
     extra["hbm_read_probe"] = read_probe(torch, qg, stream, head)
     extra["headline_frac_of_read_probe"] = round(achieved / extra["hbm_read_probe"]["same_size_GBps"], 4)

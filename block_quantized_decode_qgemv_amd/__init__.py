@@ -343,7 +343,8 @@ def moe_expert_ffn(fmt, w_gate_up, w_down, e: int, h: int, i: int, top_k: int, x
 def moe_expert_ffn_rmsnorm(fmt, w_gate_up, w_down, e: int, h: int, i: int, top_k: int, x, gamma, eps: float,
                            residual, router_logits, shared_gate_logit, t: int, out, workspace, ws_bytes: int,
                            flags: int = 0, stream=None) -> None:
-    """Routed expert layer on RMS-normalised x (see moe_expert_ffn_rmsnorm in qgemv.h)."""
+    """Routed expert layer on RMS-normalised x (see moe_expert_ffn_rmsnorm in qgemv.h);
+    gamma=None means unit gain (the gain folded into the gate/up weights)."""
     f32, u8 = _torch_dtypes()
     rc = load().moe_expert_ffn_rmsnorm(_fmt(fmt), _dev(w_gate_up, u8, "w_gate_up"), _dev(w_down, u8, "w_down"),
                                        e, h, i, top_k, _dev(x, f32, "x"), _dev(gamma, f32, "gamma"), float(eps),

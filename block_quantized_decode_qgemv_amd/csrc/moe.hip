@@ -276,10 +276,10 @@ __device__ __forceinline__ Item read_item(const int* items, int j) {
 __device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }
 
 // gate/up rows interleaved: group g holds gate rows 8g..8g+7 (rows 2i) and up
-// rows (rows 2i+1); h[item][b][8g + i] = silu(gate) * up.  NORM: the token
+// rows (rows 2i+1); h[item][b][8g + i] = silu(gate) * up.  NORM 1 or 2: the token
 // rows are RMS-normalised on the way in (gain gamma, eps), as in the
 // normalising GEMV.
-template <int F, int W, int KCS, bool NORM>
+template <int F, int W, int KCS, int NORM>
 __global__ void __launch_bounds__(W * 64)
 moe_gate_up_kernel(const uint8_t* __restrict__ wgu, size_t expert_bytes, size_t codes_bytes, int H, int I,
                    const float* __restrict__ x, const float* __restrict__ gamma, float eps,
@@ -300,9 +300,11 @@ moe_gate_up_kernel(const uint8_t* __restrict__ wgu, size_t expert_bytes, size_t 
             }
         };
     };
-    if constexpr (NORM) {
-        if (it.count == 1) GemvDpp<F, 1, W, KCS>::run_rmsnorm(codes, meta, 2 * I, H, g, xrow, 1, gamma, eps, epi(1));
-        else GemvDpp<F, 2, W, KCS>::run_rmsnorm(codes, meta, 2 * I, H, g, xrow, 2, gamma, eps, epi(2));
+    if constexpr (NORM != 0) {
+        if (it.count == 1)
+            GemvDpp<F, 1, W, KCS>::template run_rmsnorm<NORM == 1>(codes, meta, 2 * I, H, g, xrow, 1, gamma, eps, epi(1));
+        else
+            GemvDpp<F, 2, W, KCS>::template run_rmsnorm<NORM == 1>(codes, meta, 2 * I, H, g, xrow, 2, gamma, eps, epi(2));
     } else {
         if (it.count == 1) GemvDpp<F, 1, W, KCS>::run(codes, meta, 2 * I, H, g, xrow, 1, epi(1));
         else GemvDpp<F, 2, W, KCS>::run(codes, meta, 2 * I, H, g, xrow, 2, epi(2));
@@ -347,7 +349,7 @@ moe_down_kernel(const uint8_t* __restrict__ wdn, size_t expert_bytes, size_t cod
 
 // ------------------------------------------------------------- launchers
 
-template <int F, int W, int KCS, bool NORM>
+template <int F, int W, int KCS, int NORM>
 hipError_t launch_gate_up_w(const uint8_t* wgu, int H, int I, const float* x, const float* gamma, float eps,
                             const int* items, float* h, int max_items, hipStream_t st) {
     const size_t eb = qg_packed_size(F, 2 * (int64_t)I, H), cb = qg_codes_plane_size(F, 2 * (int64_t)I, H);
@@ -373,7 +375,7 @@ hipError_t launch_route(const float* logits, const float* slogit, int T, int E, 
     return hipGetLastError();
 }
 
-template <int F, bool NORM>
+template <int F, int NORM>
 hipError_t launch_moe(const uint8_t* wgu, const uint8_t* wdn, int E, int H, int I, int top_k, const float* x,
                       const float* gamma, float eps, const float* residual, const float* logits,
                       const float* slogit, int T, unsigned flags, float* out, uint8_t* ws, hipStream_t st) {
@@ -462,7 +464,8 @@ int check_moe_args(int fmt, const void* w_gate_up, const void* w_down, int E, in
     return QG_OK;
 }
 
-template <bool NORM>
+// NORM: 0 plain, 1 RMS norm with a gain vector, 2 RMS norm with unit gain
+template <int NORM>
 int moe_call(int fmt, const void* w_gate_up, const void* w_down, int E, int H, int I, int top_k, const float* x,
              const float* gamma, float eps, const float* residual, const float* router_logits,
              const float* shared_gate_logit, int T, unsigned flags, float* out, void* workspace, void* stream) {
@@ -491,7 +494,7 @@ int moe_expert_ffn(int fmt, const void* w_gate_up, const void* w_down, int E, in
     const int rc = check_moe_args(fmt, w_gate_up, w_down, E, H, I, top_k, x, residual, router_logits,
                                   shared_gate_logit, T, flags, out, workspace, ws_bytes);
     if (rc) return rc;
-    return moe_call<false>(fmt, w_gate_up, w_down, E, H, I, top_k, x, nullptr, 0.0f, residual, router_logits,
+    return moe_call<0>(fmt, w_gate_up, w_down, E, H, I, top_k, x, nullptr, 0.0f, residual, router_logits,
                            shared_gate_logit, T, flags, out, workspace, stream);
 }
 
@@ -503,14 +506,16 @@ int moe_expert_ffn_rmsnorm(int fmt, const void* w_gate_up, const void* w_down, i
     const int rc = check_moe_args(fmt, w_gate_up, w_down, E, H, I, top_k, x, residual, router_logits,
                                   shared_gate_logit, T, flags, out, workspace, ws_bytes);
     if (rc) return rc;
-    if (!gamma) return fail(QG_EINVAL, "null gamma");
-    if (!aligned(gamma, 16)) return fail(QG_EALIGN, "gamma must be 16-byte aligned");
+    if (gamma && !aligned(gamma, 16)) return fail(QG_EALIGN, "gamma must be 16-byte aligned");
     if (!(eps >= 0.0f) || !std::isfinite(eps)) return fail(QG_ERANGE, "eps=%g must be finite and >= 0", (double)eps);
-    if (overlap(gamma, (size_t)H * 4, out, (size_t)T * H * 4) ||
-        overlap(gamma, (size_t)H * 4, workspace, MoeLayout(T, H, I, top_k).total))
+    if (gamma && (overlap(gamma, (size_t)H * 4, out, (size_t)T * H * 4) ||
+                  overlap(gamma, (size_t)H * 4, workspace, MoeLayout(T, H, I, top_k).total)))
         return fail(QG_EINVAL, "gamma must not overlap out or the workspace");
-    return moe_call<true>(fmt, w_gate_up, w_down, E, H, I, top_k, x, gamma, eps, residual, router_logits,
-                          shared_gate_logit, T, flags, out, workspace, stream);
+    if (!gamma)  // unit gain: the gain folded into the gate/up weights
+        return moe_call<2>(fmt, w_gate_up, w_down, E, H, I, top_k, x, gamma, eps, residual, router_logits,
+                           shared_gate_logit, T, flags, out, workspace, stream);
+    return moe_call<1>(fmt, w_gate_up, w_down, E, H, I, top_k, x, gamma, eps, residual, router_logits,
+                       shared_gate_logit, T, flags, out, workspace, stream);
 }
 
 }  // extern "C"

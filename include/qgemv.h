@@ -290,12 +290,13 @@ int moe_expert_ffn(int fmt, const void* w_gate_up, const void* w_down, int E, in
  * x itself (it may alias x); router_logits are the router projection of
  * xhat, e.g. from qgemv_rmsnorm with the same gamma and eps.
  *   gamma  DEVICE fp32 [H], 16-byte aligned, overlapping neither out nor
- *          the workspace; eps finite, >= 0.
+ *          the workspace; or NULL for unit gain (the gain folded into every
+ *          expert's gate/up weights); eps finite, >= 0.
  *   Every other argument as for moe_expert_ffn (same workspace size).
  * Accuracy: the moe_expert_ffn bound with the gate/up GEMV bound widened to
  * 3e-5 * sum_k |W[n][k] xhat[t][k]| + 1e-7 (the qgemv_rmsnorm bound).
- * Errors: as moe_expert_ffn, plus QG_EINVAL (null gamma), QG_EALIGN (gamma),
- * QG_ERANGE (eps). */
+ * Errors: as moe_expert_ffn, plus QG_EALIGN (gamma), QG_EINVAL (gamma
+ * overlaps out or the workspace), QG_ERANGE (eps). */
 int moe_expert_ffn_rmsnorm(int fmt, const void* w_gate_up, const void* w_down, int E, int H, int I, int top_k,
                            const float* x, const float* gamma, float eps, const float* residual,
                            const float* router_logits, const float* shared_gate_logit, int T, unsigned flags,

@@ -132,8 +132,8 @@ def test_moe_rmsnorm_validation():
         return lib.moe_expert_ffn_rmsnorm(fmt, P, P, 16, 512, 256, 4, x, gamma, ctypes.c_float(eps), P + 2 * big,
                                           P + 3 * big, P + 4 * big, t, 0, P + 5 * big, wsp, ws_bytes, None)
 
-    assert call(gamma=None) == -1
     assert call(gamma=P + 4) == -3
+    assert call(gamma=None, eps=-1.0) == -4   # unit gain: the other checks still apply
     assert call(eps=-1.0) == -4
     assert call(eps=float("nan")) == -4
     assert call(fmt=0) == -1            # the plain layer's checks come first

@@ -319,8 +319,8 @@ def run_moe_norm(fmt, gu_d, dn_d, e, h, i, top_k, x, gamma, eps, residual, logit
     out = torch.full((t, h), float("nan"), device="cuda")
     ws_bytes = qg.moe_expert_ffn_workspace_size(t, e, h, i, top_k)
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
-    qg.moe_expert_ffn_rmsnorm(fmt, gu_d, dn_d, e, h, i, top_k, x_d, dev(gamma), eps, r_d, dev(logits), dev(s), t,
-                              out, ws, ws_bytes, flags=flags)
+    qg.moe_expert_ffn_rmsnorm(fmt, gu_d, dn_d, e, h, i, top_k, x_d, None if gamma is None else dev(gamma), eps, r_d,
+                              dev(logits), dev(s), t, out, ws, ws_bytes, flags=flags)
     torch.cuda.synchronize()
     return out.cpu().numpy()
 
@@ -345,6 +345,18 @@ def test_moe_rmsnorm_small(fmt, t):
     x, gamma, residual, logits, s = norm_inputs(t, e, h, seed=150 + t)
     out = run_moe_norm(fmt, gu, dn, e, h, i, top_k, x, gamma, 1e-6, residual, logits, s)
     check_norm(out, layer, x, gamma, 1e-6, residual, logits, s, top_k, False, f"{fmt} norm T={t}")
+
+
+@pytest.mark.parametrize("fmt", KFORMATS)
+@pytest.mark.parametrize("t", [1, 8])
+def test_moe_rmsnorm_unit_gain(fmt, t):
+    """gamma = NULL (the gain folded into the experts' gate/up weights): the
+    oracle with a gain of ones."""
+    e, h, i, top_k = 16, 512, 256, 4
+    layer, gu, dn = small_layer(fmt, e, h, i, seed=11)
+    x, _, residual, logits, s = norm_inputs(t, e, h, seed=170 + t)
+    out = run_moe_norm(fmt, gu, dn, e, h, i, top_k, x, None, 1e-6, residual, logits, s)
+    check_norm(out, layer, x, np.ones(h, np.float32), 1e-6, residual, logits, s, top_k, False, f"{fmt} unit T={t}")
 
 
 @pytest.mark.parametrize("fmt", KFORMATS)
