@@ -23,7 +23,7 @@ LIB = os.path.join(PKG, "libqgemv.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
-DEVICE_SOURCES = ["gemv.hip", "gemv_norm.hip", "moe.hip", "quant.hip", "probe.hip"]
+DEVICE_SOURCES = ["gemv.hip", "gemv_norm.hip", "gemv_norm_unit.hip", "moe.hip", "quant.hip", "probe.hip"]
 HOST_SOURCES = ["host.cpp"]
 
 HIP_FLAGS = [
