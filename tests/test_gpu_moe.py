@@ -338,7 +338,7 @@ def check_norm(out, layer, x, gamma, eps, residual, logits, s, top_k, renorm, la
 
 
 @pytest.mark.parametrize("fmt", KFORMATS)
-@pytest.mark.parametrize("t", [1, 3, 8])
+@pytest.mark.parametrize("t", [1, 2, 3, 5, 7, 8])
 def test_moe_rmsnorm_small(fmt, t):
     e, h, i, top_k = 16, 512, 256, 4
     layer, gu, dn = small_layer(fmt, e, h, i, seed=11)

@@ -53,6 +53,17 @@ def test_rmsnorm_gemv_parity(fmt, b, n, kb):
     assert_norm_parity(y, OF.dequant(fmt, blk), x, g, 1e-6, f"{fmt} B={b} N={n} K={k}")
 
 
+@pytest.mark.parametrize("fmt", ["q4_k", "q4_1", "q2_k", "bin8"])
+@pytest.mark.parametrize("b", [4, 5, 6, 7])
+def test_rmsnorm_gemv_mid_batches(fmt, b):
+    """Batches 4 to 7 (four-row blocks, one wide block, the unclamped loop)."""
+    n, k = 45, 2048
+    blk = make_blocks(fmt, n, k, seed=29, tid=b)
+    x, g = residual_stream(b, k, 29, b), gain(k, 29, 1)
+    y = run_norm(fmt, OF.pack(fmt, blk), x, g, 1e-6, n, k)
+    assert_norm_parity(y, OF.dequant(fmt, blk), x, g, 1e-6, f"{fmt} B={b}")
+
+
 @pytest.mark.parametrize("fmt", OF.FORMATS)
 @pytest.mark.parametrize("b", [1, 5, 8])
 def test_rmsnorm_gemv_widest_workgroup(fmt, b):

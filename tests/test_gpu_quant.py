@@ -122,3 +122,13 @@ def test_requant_full_expert_q4k_to_q2k():
     assert int(status.item()) == 0
     deq = OF.dequant_packed("q4_k", q4, n, k)
     np.testing.assert_array_equal(out.cpu().numpy(), OF.pack("q2_k", OF.quantize("q2_k", deq)))
+
+
+@pytest.mark.parametrize("fmt,n,k", [("q4_k", 14336, 4096), ("q8_0", 4096, 4096), ("q2_k", 4096, 14336)])
+def test_quant_device_full_size_matches_host_quantizer(fmt, n, k):
+    """The device quantizer on a full projection matrix equals the C++ host
+    quantizer byte for byte (the host quantizer is pinned to the oracle)."""
+    w = workloads.student_t_weights(n, k, 36, n)
+    got, status = run_quant(fmt, w)
+    assert status == 0
+    np.testing.assert_array_equal(got, qg.qquant(fmt, w, n_threads=16))
