@@ -315,3 +315,24 @@ def test_per_format_entry_points_match_qgemv(fmt):
     getattr(qg, ALIASES[fmt])(w_d, x_d, y2, n, k, b)
     torch.cuda.synchronize()
     assert torch.equal(y1.view(torch.int32), y2.view(torch.int32))
+
+
+@pytest.mark.parametrize("fmt,n,k,b", [("q4_k", 57344, 4096, 1), ("q8_0", 64, 65536, 2), ("q4_k", 48, 131072, 3),
+                                       ("bin8", 40, 65536, 8)])
+def test_large_shapes(fmt, n, k, b):
+    """Far beyond the bench's shapes: 57344 rows (3584 row groups, several
+    rounds of workgroups per compute unit) and K up to 131072 (many K slices
+    per workgroup); sampled rows (all rows when few) against the oracle."""
+    x = workloads.normal((b, k), 37, n + k)
+    if fmt == "bin8":
+        bits, sc = workloads.binary_codes(n, k, 37, 1), workloads.scale_bits_f16((n, k // 128), 37, 2)
+        packed = qg.qpack_bin8(bits, sc)
+        rows = np.arange(n)
+        sub = OF.bin8_from_codes(bits, sc)
+    else:
+        w = workloads.student_t_weights(n, k, 37, n)
+        packed = qg.qquant(fmt, w, n_threads=16)
+        rows = sampled_rows(n, n + k) if n > 256 else np.arange(n)
+        sub = OF.quantize(fmt, w[rows])
+    y = run_gemv(fmt, packed, x, n, k)
+    check_sampled_rows(fmt, packed, sub, rows, n, k, x, y)
