@@ -230,6 +230,66 @@ def test_moe_many_experts(e):
     check(out, Layer(Sparse()), x, residual, logits, s, top_k, False, f"E={e}")
 
 
+def tie_logits(e, t=6):
+    """Router logits with exact ties at large E: all equal; equal leaders
+    that share a route-kernel lane (experts 5, 69, 133, ... are lane 5's) next
+    to another lane's; signed zeros; -inf and NaN fill-ins; one random row
+    whose three leaders tie."""
+    lg = workloads.normal((t, e), 41, e).copy()
+    lg[0, :] = 0.5
+    lg[1, :] = -1.0
+    lg[1, [5, 69, 133, 197, 261, 4, 68]] = 2.0
+    lg[1, [0, 64]] = np.nan
+    lg[2, :] = -1.0
+    lg[2, [300, 7, 450]] = -0.0
+    lg[2, [193]] = 0.0
+    lg[3, :] = -np.inf
+    lg[3, [511, 256]] = 0.25
+    lg[4, :] = np.nan
+    lg[4, [1, 6, 8, 15]] = [0.1, 0.1, -0.3, 0.1]
+    lg[5, [10, 500, e - 1]] = 9.0
+    return lg.astype(np.float32)
+
+
+@pytest.mark.parametrize("e", [512, 4096])
+def test_moe_route_ties_many_experts(e):
+    """Ties settled by the lower expert index where each lane of the route
+    kernel holds 8 or 64 experts; only the oracle's picks hold weights (every
+    other slot is 0xFF, NaN scales), so a different pick shows as NaN."""
+    fmt, h, i, top_k = "q4_k", 256, 256, 8
+    lg = tie_logits(e)
+    t = lg.shape[0]
+    ids, _, _ = OM.route(lg, top_k)
+    assert ids[1].tolist() == [4, 5, 68, 69, 133, 197, 261, 1]
+    assert OM.route_margin(lg[5:6], top_k)[0] > 1e-6
+    x, residual, _, s = inputs(t, e, h, seed=42)
+    used = sorted(set(ids.reshape(-1).tolist()) | {e})
+    gu_sz, dn_sz = qg.qg_packed_size(fmt, 2 * i, h), qg.qg_packed_size(fmt, h, i)
+    gu = torch.full(((e + 1) * gu_sz,), 0xFF, dtype=torch.uint8, device="cuda")
+    dn = torch.full(((e + 1) * dn_sz,), 0xFF, dtype=torch.uint8, device="cuda")
+    experts = {}
+    for ex in used:
+        experts[ex] = random_expert(fmt, h, i, 43, ex)
+        gu[ex * gu_sz:(ex + 1) * gu_sz].copy_(dev(experts[ex].gu_packed))
+        dn[ex * dn_sz:(ex + 1) * dn_sz].copy_(dev(experts[ex].dn_packed))
+
+    class Sparse:
+        def __len__(self):
+            return e + 1
+
+        def __getitem__(self, j):
+            return experts[j] if j in experts else experts[e]
+
+    out = run_moe(fmt, gu, dn, e, h, i, top_k, x, residual, lg, s)
+    assert np.all(np.isfinite(out)), "a tie went to an expert the oracle did not pick"
+    layer = Layer(Sparse())
+    wg, wu, wd = layer.view("gate"), layer.view("up"), layer.view("down")
+    ref = OM.moe_ref(wg, wu, wd, x, residual, lg, s, top_k)
+    tol = OM.out_tolerance(wg, wu, wd, x, residual, ref)
+    err = np.abs(out.astype(np.float64) - ref["out"])
+    assert np.all(err <= tol), f"E={e}: |err|/tol = {np.max(err / tol):.3g}"
+
+
 def test_moe_deterministic():
     fmt, e, h, i, top_k, t = "q2_k", 16, 512, 256, 4, 8
     layer, gu, dn = small_layer(fmt, e, h, i, seed=15)
