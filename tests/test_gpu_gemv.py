@@ -336,3 +336,39 @@ def test_large_shapes(fmt, n, k, b):
         sub = OF.quantize(fmt, w[rows])
     y = run_gemv(fmt, packed, x, n, k)
     check_sampled_rows(fmt, packed, sub, rows, n, k, x, y)
+
+
+@pytest.mark.parametrize("fmt,reps,k,b", [("q8_0", 5120, 16384, 2), ("q4_k", 10240, 16384, 1)])
+def test_over_4gib_matrix(fmt, reps, k, b):
+    """A matrix of 5.7-6 GB, so both planes and the meta plane's start lie
+    past 2^32 bytes: a 64-row matrix from the C++ quantizer tiled `reps`
+    times on the device.  Each plane stores row groups in order, so tiling
+    each plane gives the matrix whose row r is row r mod 64 (checked on the
+    host at 4 copies against the quantizer of the tiled weights); every
+    output row is checked against the oracle's GEMV of the 64 rows."""
+    n0 = 64
+    w0 = workloads.student_t_weights(n0, k, 38, k)
+    small = qg.qquant(fmt, w0)
+    cb0 = qg.qg_codes_plane_size(fmt, n0, k)
+    np.testing.assert_array_equal(
+        np.concatenate([np.tile(small[:cb0], 4), np.tile(small[cb0:], 4)]),
+        qg.qquant(fmt, np.tile(w0, (4, 1))))
+    n = n0 * reps
+    cb, total = qg.qg_codes_plane_size(fmt, n, k), qg.qg_packed_size(fmt, n, k)
+    assert cb == reps * cb0 and total == reps * small.size and total > (1 << 32) + cb0
+    big = torch.empty(total, dtype=torch.uint8, device="cuda")
+    small_d = dev(small)
+    big[:cb].view(reps, cb0).copy_(small_d[:cb0].expand(reps, cb0))
+    big[cb:].view(reps, -1).copy_(small_d[cb0:].expand(reps, small.size - cb0))
+    x = workloads.normal((b, k), 38, 1)
+    y_d = torch.full((b, n), float("nan"), device="cuda")
+    qg.qgemv(fmt, big, dev(x), y_d, n, k, b)
+    torch.cuda.synchronize()
+    y = y_d.cpu().numpy().reshape(b, reps, n0).astype(np.float64)
+    del big
+    torch.cuda.empty_cache()
+    w_deq = OF.dequant_packed(fmt, small, n0, k)
+    err = np.abs(y - OG.gemv_ref(w_deq, x)[:, None, :])
+    tol = OG.tolerance(w_deq, x)[:, None, :]
+    worst = np.unravel_index(int(np.argmax(err / tol)), err.shape)
+    assert np.all(err <= tol), f"{fmt}: |err|/tol = {err[worst] / tol[worst]:.3g} at (b, copy, row) {worst}"
