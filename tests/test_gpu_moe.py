@@ -361,6 +361,40 @@ def test_moe_full_layer(fmt, t):
     check(out, Layer(pool), x, residual, logits, s, top_k, False, f"{fmt} full T={t}")
 
 
+
+def test_moe_experts_past_4gib():
+    """1024 experts at the full layer's sizes (gate/up array 4.8 GB): the
+    router is steered to experts 1000-1023, whose gate/up rows lie past 2^32
+    bytes, like the shared expert's (index 1024); unselected slots hold 0xFF
+    (NaN scales)."""
+    fmt, e, h, i, top_k, t = "q4_k", 1024, FULL_H, FULL_I, FULL_K, 2
+    x, residual, logits, s = inputs(t, e, h, seed=650)
+    logits = logits.copy()
+    logits[:, 1000:] += 10.0
+    ids, _, _ = OM.route(logits, top_k)
+    assert ids.min() >= 1000
+    pool = PooledExperts(fmt, seed=22)
+    gu_sz, dn_sz = qg.qg_packed_size(fmt, 2 * i, h), qg.qg_packed_size(fmt, h, i)
+    assert 1000 * gu_sz > (1 << 32)
+    gu = torch.full(((e + 1) * gu_sz,), 0xFF, dtype=torch.uint8, device="cuda")
+    dn = torch.full(((e + 1) * dn_sz,), 0xFF, dtype=torch.uint8, device="cuda")
+    for ex in sorted(set(ids.reshape(-1).tolist()) | {e}):
+        gu[ex * gu_sz:(ex + 1) * gu_sz].copy_(dev(pool[ex].gu_packed))
+        dn[ex * dn_sz:(ex + 1) * dn_sz].copy_(dev(pool[ex].dn_packed))
+
+    class Wide:
+        def __len__(self):
+            return e + 1
+
+        def __getitem__(self, j):
+            return pool[j]
+
+    out = run_moe(fmt, gu, dn, e, h, i, top_k, x, residual, logits, s)
+    del gu, dn
+    torch.cuda.empty_cache()
+    assert np.all(np.isfinite(out)), "a kernel read an unselected expert"
+    check(out, Layer(Wide()), x, residual, logits, s, top_k, False, "experts past 4 GiB")
+
 # ------------------------------------------------- RMS-norm-fed expert layer
 
 def norm_inputs(t, e, h, seed):
