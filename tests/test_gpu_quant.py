@@ -132,3 +132,29 @@ def test_quant_device_full_size_matches_host_quantizer(fmt, n, k):
     got, status = run_quant(fmt, w)
     assert status == 0
     np.testing.assert_array_equal(got, qg.qquant(fmt, w, n_threads=16))
+
+
+@pytest.mark.parametrize("fmt,reps,k", [("q8_0", 5120, 16384), ("q4_k", 10240, 16384)])
+def test_quant_device_over_4gib_output(fmt, reps, k):
+    """A 21-43 GB fp32 matrix (a 64-row matrix tiled on the device) quantized
+    on the device into a 5.7-6 GB buffer whose planes run past 2^32 bytes.  Each
+    plane stores row groups in order, so the expected buffer is each plane of
+    the oracle's packing of the 64 rows repeated `reps` times; every byte is
+    compared on the device."""
+    n0 = 64
+    w0 = workloads.student_t_weights(n0, k, 39, k)
+    small = OF.pack(fmt, OF.quantize(fmt, w0))
+    cb0 = OF.codes_plane_size(fmt, n0, k)
+    n = n0 * reps
+    cb, total = qg.qg_codes_plane_size(fmt, n, k), qg.qg_packed_size(fmt, n, k)
+    assert cb == reps * cb0 and total == reps * small.size and total > (1 << 32)
+    w = dev(w0).repeat(reps, 1)
+    out = torch.full((total,), 0xA5, dtype=torch.uint8, device="cuda")
+    status = torch.full((1,), 12345, dtype=torch.int32, device="cuda")
+    qg.qquant_device(fmt, w, out, n, k, status)
+    torch.cuda.synchronize()
+    del w
+    assert int(status.item()) == 0
+    small_d = dev(small)
+    assert torch.equal(out[:cb].view(reps, cb0), small_d[:cb0].expand(reps, cb0))
+    assert torch.equal(out[cb:].view(reps, -1), small_d[cb0:].expand(reps, small.size - cb0))
