@@ -260,8 +260,9 @@ int check_matrix(int fmt, int64_t N, int64_t K) {
     if (N < 1) return fail(QG_ESHAPE, "N=%lld must be >= 1", (long long)N);
     if (K < fi->block || K % fi->block)
         return fail(QG_ESHAPE, "K=%lld is not a positive multiple of the block size %d", (long long)K, fi->block);
-    if (N > (int64_t)1 << 31 || K > (int64_t)1 << 30)
-        return fail(QG_ESHAPE, "N=%lld, K=%lld exceed the supported range", (long long)N, (long long)K);
+    if (N >= (int64_t)1 << 31 || K > (int64_t)1 << 30)  // kernels take N and K as int
+        return fail(QG_ESHAPE, "N=%lld, K=%lld exceed the supported range (N < 2^31, K <= 2^30)", (long long)N,
+                    (long long)K);
     return QG_OK;
 }
 

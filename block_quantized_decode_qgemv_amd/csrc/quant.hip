@@ -282,7 +282,7 @@ int qquant_device(int fmt, const float* w, int64_t N, int64_t K, void* out, int*
 }
 
 size_t qrequant_workspace_size(int64_t N, int64_t K) {
-    if (N < 1 || K < 1 || N > (int64_t)1 << 31 || K > (int64_t)1 << 30) return 0;
+    if (N < 1 || K < 1 || N >= (int64_t)1 << 31 || K > (int64_t)1 << 30) return 0;
     return (size_t)N * (size_t)K * sizeof(float);
 }
 

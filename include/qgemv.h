@@ -123,7 +123,7 @@ size_t qgemv_workspace_size(int fmt, int64_t N, int64_t K, int B);
  *   x   DEVICE, fp32 [B][K] row-major, 16-byte aligned.
  *   y   DEVICE, fp32 [B][N] row-major, 4-byte aligned; overwritten; must not
  *       overlap x or w (QG_EINVAL).
- *   N >= 1 (any value); K a positive multiple of the block size, at most
+ *   1 <= N < 2^31; K a positive multiple of the block size, at most
  *   2^26 (offsets inside a 16-row group are 32-bit);
  *   1 <= B <= 8.
  *   ws  DEVICE scratch of >= qgemv_workspace_size() bytes, 16-byte aligned,

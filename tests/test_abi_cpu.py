@@ -75,7 +75,8 @@ P = 0x10000  # fake 16-byte aligned pointer value
     (dict(fmt=0, n=4, k=48, b=1), -2),           # K not a multiple of 32
     (dict(fmt=3, n=4, k=256, b=0), -4),          # B < 1
     (dict(fmt=3, n=4, k=256, b=9), -4),          # B > 8
-    (dict(fmt=7, n=4, k=256, b=1), -1),          # unknown format
+    (dict(fmt=8, n=4, k=256, b=1), -1),          # unknown format
+    (dict(fmt=3, n=1 << 31, k=256, b=1), -2),    # N beyond int
     (dict(fmt=-1, n=4, k=256, b=1), -1),
     (dict(fmt=3, n=4, k=256, b=1, w=0), -1),     # null w
     (dict(fmt=3, n=4, k=256, b=1, x=0), -1),     # null x
@@ -155,6 +156,7 @@ def test_device_quantizer_validation():
     assert lib.qquant_device(3, P, 4, 256, P + 8, P, None) == -3      # misaligned out
     ws = qg.qrequant_workspace_size(4, 256)
     assert ws == 4 * 256 * 4
+    assert qg.qrequant_workspace_size((1 << 31) - 1, 256) > 0 and qg.qrequant_workspace_size(1 << 31, 256) == 0
     big = 1 << 24
     assert lib.qrequant(3, P, 4, P + big, 4, 256, P + 2 * big, ws - 4, P + 3 * big, None) == -4
     assert lib.qrequant(3, P, 4, P + 16, 4, 256, P + 2 * big, ws, P + 3 * big, None) == -1   # src/dst overlap
