@@ -372,3 +372,38 @@ def test_over_4gib_matrix(fmt, reps, k, b):
     tol = OG.tolerance(w_deq, x)[:, None, :]
     worst = np.unravel_index(int(np.argmax(err / tol)), err.shape)
     assert np.all(err <= tol), f"{fmt}: |err|/tol = {err[worst] / tol[worst]:.3g} at (b, copy, row) {worst}"
+
+
+@pytest.mark.parametrize("fmt", ["q8_0", "q4_k"])
+def test_max_k_one_row_group(fmt):
+    """K = 2^26, the GEMV limit, on one 16-row group (in-group offsets up to
+    2^30 bytes, 32-bit by design): a 16 x 4096 matrix repeated 2^14 times
+    along K.  For one row group each plane is the row's units in order, so
+    repeating the planes repeats the columns (checked on the host at 3
+    copies); with x repeated the same way the exact result is 2^14 times the
+    small one, and the accuracy bound scales the same way."""
+    rows, k0, reps, b = 16, 4096, 1 << 14, 2
+    k = k0 * reps
+    w0 = workloads.student_t_weights(rows, k0, 40, 1)
+    small = qg.qquant(fmt, w0)
+    cb0 = qg.qg_codes_plane_size(fmt, rows, k0)
+    np.testing.assert_array_equal(np.concatenate([np.tile(small[:cb0], 3), np.tile(small[cb0:], 3)]),
+                                  qg.qquant(fmt, np.tile(w0, (1, 3))))
+    cb, total = qg.qg_codes_plane_size(fmt, rows, k), qg.qg_packed_size(fmt, rows, k)
+    assert cb == reps * cb0 and total == reps * small.size
+    big = torch.empty(total, dtype=torch.uint8, device="cuda")
+    small_d = dev(small)
+    big[:cb].view(reps, cb0).copy_(small_d[:cb0].expand(reps, cb0))
+    big[cb:].view(reps, -1).copy_(small_d[cb0:].expand(reps, small.size - cb0))
+    x0 = workloads.normal((b, k0), 40, 2)
+    x = dev(x0).repeat(1, reps)
+    y_d = torch.full((b, rows), float("nan"), device="cuda")
+    qg.qgemv(fmt, big, x, y_d, rows, k, b)
+    torch.cuda.synchronize()
+    y = y_d.cpu().numpy().astype(np.float64)
+    del big, x
+    torch.cuda.empty_cache()
+    w_deq = OF.dequant_packed(fmt, small, rows, k0)
+    err = np.abs(y - reps * OG.gemv_ref(w_deq, x0))
+    tol = reps * OG.tolerance(w_deq, x0)
+    assert np.all(err <= tol), f"{fmt}: worst |err|/tol = {np.max(err / tol):.3g}"
