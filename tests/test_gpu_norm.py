@@ -169,3 +169,39 @@ def test_rmsnorm_gemv_full_size_sampled_rows(fmt, n, k, b):
     check_sampled_bytes(fmt, packed, sub, rows, n, k)
     assert_norm_parity(y[:, rows], OF.dequant(fmt, sub), x, g, 1e-5, f"{fmt} {n}x{k} B={b}")
     assert np.all(np.isfinite(y))
+
+
+@pytest.mark.parametrize("fmt,with_gain", [("q4_k", True), ("q8_0", False)])
+def test_rmsnorm_gemv_max_k(fmt, with_gain):
+    """K = 2^26, the GEMV limit, on one 16-row group: a 16 x 4096 matrix,
+    x and gamma repeated 2^14 times along K (the planes of one row group
+    repeat with the columns).  The RMS of the repeated row equals the small
+    row's, so the exact result is 2^14 times the small normalised GEMV; the
+    tolerance's relative part scales the same way."""
+    rows, k0, reps, b, eps = 16, 4096, 1 << 14, 2, 1e-5
+    k = k0 * reps
+    w0 = workloads.student_t_weights(rows, k0, 41, 1)
+    small = qg.qquant(fmt, w0)
+    cb0 = qg.qg_codes_plane_size(fmt, rows, k0)
+    np.testing.assert_array_equal(np.concatenate([np.tile(small[:cb0], 2), np.tile(small[cb0:], 2)]),
+                                  qg.qquant(fmt, np.tile(w0, (1, 2))))
+    cb, total = qg.qg_codes_plane_size(fmt, rows, k), qg.qg_packed_size(fmt, rows, k)
+    assert cb == reps * cb0 and total == reps * small.size
+    big = torch.empty(total, dtype=torch.uint8, device="cuda")
+    small_d = dev(small)
+    big[:cb].view(reps, cb0).copy_(small_d[:cb0].expand(reps, cb0))
+    big[cb:].view(reps, -1).copy_(small_d[cb0:].expand(reps, small.size - cb0))
+    x0 = residual_stream(b, k0, 41, 2)
+    g0 = gain(k0, 41, 3) if with_gain else np.ones(k0, np.float32)
+    x = dev(x0).repeat(1, reps)
+    g = dev(g0).repeat(reps) if with_gain else None
+    y_d = torch.full((b, rows), float("nan"), device="cuda")
+    qg.qgemv_rmsnorm(fmt, big, x, g, eps, y_d, rows, k, b)
+    torch.cuda.synchronize()
+    y = y_d.cpu().numpy().astype(np.float64)
+    del big, x, g
+    torch.cuda.empty_cache()
+    w_deq = OF.dequant_packed(fmt, small, rows, k0)
+    err = np.abs(y - reps * ON.gemv_rmsnorm_ref(w_deq, x0, g0, eps))
+    tol = reps * ON.tolerance(w_deq, x0, g0, eps)
+    assert np.all(err <= tol), f"{fmt}: worst |err|/tol = {np.max(err / tol):.3g}"
