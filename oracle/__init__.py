@@ -11,8 +11,9 @@ define, in numpy:
 * ``formats``   -- the block formats (Q8_0, Q4_0, Q4_1, Q4_K on the handbook
                    page; Q2_K, ternary-in-2-bit and 1-bit from the low-bit
                    pages), their quantizers, dequantizers and the byte layout.
-* ``page_listing`` -- the handbook page's fp32 quantizer listing, restated,
-                   used only to pin the page's printed error table.
+* ``page_sample`` -- the handbook page's weight sample (the torch draw its
+                   error table is printed for); the table is reproduced by
+                   the quantizers' page-literal mode (fp32 scales).
 * ``gemv``      -- y = W x in float64 and the acceptance bound.
 * ``moe``       -- the routed expert layer (softmax top-K, SwiGLU, gated
                    combine + residual) and its propagated error bound.

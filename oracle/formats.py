@@ -63,10 +63,17 @@ low-bit README page's repacking of rows for the dot-product lanes (kernel
 table, Q2_K row interleave), set to 16 rows: one 16-lane quarter of a gfx950
 wave reads one unit of 16 rows as 256 contiguous bytes.
 
+Page-literal mode.  The listing keeps every scale and min in fp32; the
+quantizers take ``literal=True`` to do the same (no fp16 storage: the block
+dict then holds fp32 scale values instead of fp16 bit patterns, which
+``dequant`` accepts and ``pack`` refuses).  It exists only so the page's
+printed error table can pin the quantizer arithmetic this module shares with
+the listing; everything else uses fp16 storage (R1).
+
 Parity: bin8 is pinned by the page's printed size saving (5.6 %), by exact
 round trips of affine-representable scales and by the rounding bound of the
-scale codes.  Q8_0, Q4_0, Q4_1, Q4_K are pinned by the page's printed error table
-(through ``page_listing``), by the bits/weight closed forms in the listing and
+scale codes.  Q8_0, Q4_0, Q4_1, Q4_K are pinned by the page's printed error
+table (page-literal mode), by the bits/weight closed forms in the listing and
 by round trips of hand-built blocks.  Q2_K, tern and bin are pinned by round
 trips, closed forms and brute force only (their layouts are readings).
 """
@@ -155,6 +162,23 @@ def from_f16_bits(bits) -> np.ndarray:
     return np.asarray(bits, dtype=np.uint16).view(np.float16).astype(F32)
 
 
+def _store(v, literal: bool) -> np.ndarray:
+    """A computed scale or min as stored: its fp16 bit pattern (R1), or in the
+    page-literal mode the fp32 value itself."""
+    return np.asarray(v, dtype=F32).copy() if literal else to_f16_bits(v)
+
+
+def scale_values(stored) -> np.ndarray:
+    """fp32 values of stored scales or mins: fp16 bit patterns widened exactly,
+    page-literal fp32 values as they are."""
+    stored = np.asarray(stored)
+    if stored.dtype == np.uint16:
+        return from_f16_bits(stored)
+    if stored.dtype != F32:
+        raise TypeError(f"stored scales must be fp16 bit patterns or fp32 values, got {stored.dtype}")
+    return stored
+
+
 def _canonical(w: np.ndarray, block: int) -> np.ndarray:
     w = np.asarray(w, dtype=F32)
     if w.ndim != 2:
@@ -175,19 +199,19 @@ def _div(a, b):
 # Quantizers (one per format).  Each returns a dict of plain arrays: the
 # block representation that ``pack`` lays out and ``dequant`` decodes.
 
-def quantize_q8_0(w) -> dict:
+def quantize_q8_0(w, literal: bool = False) -> dict:
     """32 weights per block; d = max|b| / 127 (fp16); q = rint(b / d) in [-127, 127]."""
     w = _canonical(w, 32)
     n, k = w.shape
     b = w.reshape(n, k // 32, 32)
     a = np.abs(b).max(axis=2)
-    d16 = to_f16_bits(_div(a, F32(127)))
-    d = from_f16_bits(d16)[..., None]
+    d_st = _store(_div(a, F32(127)), literal)
+    d = scale_values(d_st)[..., None]
     q = np.where(d == 0, F32(0), np.clip(np.rint(_div(b, d)), -127, 127))
-    return {"d": d16, "q": q.astype(np.int8).reshape(n, k)}
+    return {"d": d_st, "q": q.astype(np.int8).reshape(n, k)}
 
 
-def quantize_q4_0(w) -> dict:
+def quantize_q4_0(w, literal: bool = False) -> dict:
     """32 weights per block; signed d = (the max-|b| element, first on ties) / -8,
     so that element lands on code -8; codes rint(b / d) in [-8, 7], stored + 8."""
     w = _canonical(w, 32)
@@ -195,13 +219,13 @@ def quantize_q4_0(w) -> dict:
     b = w.reshape(n, k // 32, 32)
     j = np.argmax(np.abs(b), axis=2)  # first index of the maximum
     bj = np.take_along_axis(b, j[..., None], axis=2)[..., 0]
-    d16 = to_f16_bits(_div(bj, F32(-8)))
-    d = from_f16_bits(d16)[..., None]
+    d_st = _store(_div(bj, F32(-8)), literal)
+    d = scale_values(d_st)[..., None]
     c = np.where(d == 0, F32(0), np.clip(np.rint(_div(b, d)), -8, 7))
-    return {"d": d16, "n": (c.astype(np.int16) + 8).astype(np.uint8).reshape(n, k)}
+    return {"d": d_st, "n": (c.astype(np.int16) + 8).astype(np.uint8).reshape(n, k)}
 
 
-def quantize_q4_1(w) -> dict:
+def quantize_q4_1(w, literal: bool = False) -> dict:
     """32 weights per block; d = (max - min) / 15 and m = min (both fp16);
     codes rint((b - m) / d) in [0, 15]."""
     w = _canonical(w, 32)
@@ -209,15 +233,15 @@ def quantize_q4_1(w) -> dict:
     b = w.reshape(n, k // 32, 32)
     lo = b.min(axis=2)
     hi = b.max(axis=2)
-    d16 = to_f16_bits(_div(hi - lo, F32(15)))
-    m16 = to_f16_bits(lo)
-    d = from_f16_bits(d16)[..., None]
-    m = from_f16_bits(m16)[..., None]
+    d_st = _store(_div(hi - lo, F32(15)), literal)
+    m_st = _store(lo, literal)
+    d = scale_values(d_st)[..., None]
+    m = scale_values(m_st)[..., None]
     q = np.where(d == 0, F32(0), np.clip(np.rint(_div(b - m, d)), 0, 15))
-    return {"d": d16, "m": m16, "n": q.astype(np.uint8).reshape(n, k)}
+    return {"d": d_st, "m": m_st, "n": q.astype(np.uint8).reshape(n, k)}
 
 
-def _quantize_kquant(w, qmax: int) -> dict:
+def _quantize_kquant(w, qmax: int, literal: bool = False) -> dict:
     """Handbook's simplified K-quant with weight codes in [0, qmax].
 
     Per 32-weight sub-block j: lo = min(min b, 0), hi = max b,
@@ -234,30 +258,30 @@ def _quantize_kquant(w, qmax: int) -> dict:
     hi = b.max(axis=3)
     sc = _div(hi - lo, F32(qmax))
     mn = -lo
-    d16 = to_f16_bits(_div(sc.max(axis=2), F32(63)))
-    dmin16 = to_f16_bits(_div(mn.max(axis=2), F32(63)))
-    dd = from_f16_bits(d16)[..., None]
-    dm = from_f16_bits(dmin16)[..., None]
+    d_st = _store(_div(sc.max(axis=2), F32(63)), literal)
+    dmin_st = _store(_div(mn.max(axis=2), F32(63)), literal)
+    dd = scale_values(d_st)[..., None]
+    dm = scale_values(dmin_st)[..., None]
     s = np.where(dd == 0, F32(1), np.clip(np.rint(_div(sc, dd)), 1, 63))
     t = np.where(dm == 0, F32(0), np.clip(np.rint(_div(mn, dm)), 0, 63))
     S = (s * dd)[..., None]
     Mn = (t * dm)[..., None]
     q = np.where(S == 0, F32(0), np.clip(np.rint(_div(b + Mn, S)), 0, qmax))
     return {
-        "d": d16,
-        "dmin": dmin16,
+        "d": d_st,
+        "dmin": dmin_st,
         "s": s.astype(np.uint8),
         "t": t.astype(np.uint8),
         "n": q.astype(np.uint8).reshape(n, k),
     }
 
 
-def quantize_q4_k(w) -> dict:
-    return _quantize_kquant(w, 15)
+def quantize_q4_k(w, literal: bool = False) -> dict:
+    return _quantize_kquant(w, 15, literal)
 
 
-def quantize_q2_k(w) -> dict:
-    return _quantize_kquant(w, 3)
+def quantize_q2_k(w, literal: bool = False) -> dict:
+    return _quantize_kquant(w, 3, literal)
 
 
 def tern_from_codes(codes, scale_bits) -> dict:
@@ -318,8 +342,16 @@ QUANTIZERS = {
 }
 
 
-def quantize(fmt: str, w) -> dict:
-    return QUANTIZERS[fmt](w)
+def quantize(fmt: str, w, literal: bool = False) -> dict:
+    """fp32 [N, K] -> block representation; literal=True keeps the scales in
+    fp32 as the page's listing does (see the module docstring)."""
+    return QUANTIZERS[fmt](w, literal)
+
+
+def relative_error(deq, w) -> float:
+    """The page's accuracy figure ||deq - w|| / ||w||, evaluated in float64."""
+    w64 = np.asarray(w, np.float64)
+    return float(np.linalg.norm(np.asarray(deq, np.float64) - w64) / np.linalg.norm(w64))
 
 
 # ----------------------------------------------------------------------------
@@ -335,31 +367,31 @@ def _per_block(v, block: int, k: int):
 def dequant(fmt: str, blk: dict) -> np.ndarray:
     if fmt == "q8_0":
         q = blk["q"]
-        return q.astype(F32) * _per_block(from_f16_bits(blk["d"]), 32, q.shape[1])
+        return q.astype(F32) * _per_block(scale_values(blk["d"]), 32, q.shape[1])
     if fmt == "q4_0":
         nn = blk["n"]
         c = (nn.astype(np.int16) - 8).astype(F32)
-        return c * _per_block(from_f16_bits(blk["d"]), 32, nn.shape[1])
+        return c * _per_block(scale_values(blk["d"]), 32, nn.shape[1])
     if fmt == "q4_1":
         nn = blk["n"]
         k = nn.shape[1]
-        d = _per_block(from_f16_bits(blk["d"]), 32, k)
-        m = _per_block(from_f16_bits(blk["m"]), 32, k)
+        d = _per_block(scale_values(blk["d"]), 32, k)
+        m = _per_block(scale_values(blk["m"]), 32, k)
         return nn.astype(F32) * d + m
     if fmt in ("q4_k", "q2_k"):
         nn = blk["n"]
         n, k = nn.shape
-        dd = from_f16_bits(blk["d"])[..., None]
-        dm = from_f16_bits(blk["dmin"])[..., None]
+        dd = scale_values(blk["d"])[..., None]
+        dm = scale_values(blk["dmin"])[..., None]
         S = (blk["s"].astype(F32) * dd).reshape(n, k // 32)
         Mn = (blk["t"].astype(F32) * dm).reshape(n, k // 32)
         return nn.astype(F32) * _per_block(S, 32, k) - _per_block(Mn, 32, k)
     if fmt == "tern":
         f = blk["f"]
-        return (f.astype(np.int16) - 1).astype(F32) * _per_block(from_f16_bits(blk["d"]), 128, f.shape[1])
+        return (f.astype(np.int16) - 1).astype(F32) * _per_block(scale_values(blk["d"]), 128, f.shape[1])
     if fmt == "bin":
         bb = blk["b"]
-        return (2 * bb.astype(np.int16) - 1).astype(F32) * _per_block(from_f16_bits(blk["d"]), 128, bb.shape[1])
+        return (2 * bb.astype(np.int16) - 1).astype(F32) * _per_block(scale_values(blk["d"]), 128, bb.shape[1])
     if fmt == "bin8":
         bb = blk["b"]
         return (2 * bb.astype(np.int16) - 1).astype(F32) * _per_block(bin8_scales(blk), 128, bb.shape[1])
@@ -475,7 +507,11 @@ def deinterleave_rows(buf, n: int, rb: int) -> np.ndarray:
 
 
 def pack(fmt: str, blk: dict) -> np.ndarray:
-    """Block representation -> packed bytes (codes plane then meta plane)."""
+    """Block representation -> packed bytes (codes plane then meta plane).
+    Page-literal blocks (fp32 scales) have no byte layout and are refused."""
+    for key in ("d", "m", "dmin"):
+        if key in blk and fmt != "bin8" and np.asarray(blk[key]).dtype != np.uint16:
+            raise TypeError(f"{fmt}: '{key}' must be fp16 bit patterns to be packed (page-literal blocks do not pack)")
     if fmt == "q8_0":
         codes = blk["q"].view(np.uint8)
         meta = _u16_le(blk["d"])

@@ -5,6 +5,7 @@ import pytest
 import workloads
 from oracle import formats as F
 from oracle import moe as M
+from tests import oracle_pins as P
 
 
 def _experts(e, h, i, seed=0, identical=False):
@@ -109,3 +110,22 @@ def test_interleave_gate_up():
     il = M.interleave_gate_up(a, b)
     np.testing.assert_array_equal(il[0::2], a)
     np.testing.assert_array_equal(il[1::2], b)
+
+
+# ----------------------------------------------------------------------------
+# independent pins (tests/oracle_pins.py): brute force with math.fsum
+
+
+def test_expert_forward_against_fsum():
+    """expert_forward against a brute-force expert (H != I and square)."""
+    P.expert_forward_fsum(M)
+
+
+def test_route_against_fsum():
+    P.route_pin(M)
+
+
+def test_moe_ref_against_fsum():
+    """The whole layer -- route, experts, gated combine and residual -- by
+    brute force on tiny experts."""
+    P.moe_combine_fsum(M)

@@ -1,92 +1,147 @@
-"""Plant plausible mistakes in (copies of) the oracle's arithmetic, on the CPU,
-and check that the pins catch each one.  Nothing here touches the GPU path."""
+"""Planted mistakes in the oracle's own source, each rejected by a pin.
+
+Every case below edits the source of ``oracle.formats`` or ``oracle.moe``
+(tests/mutate.py builds the edited module; the oracle on disk is untouched)
+and runs the pin named next to it from tests/oracle_pins.py, which must fail
+on the mutant.  The same pins pass on the oracle itself (test_oracle_formats,
+test_oracle_moe).  CPU only.
+"""
 import numpy as np
 import pytest
 
-from oracle import page_listing as PL
-
-F32 = np.float32
+from oracle import formats as OF
+from oracle import moe as OM
+from oracle import page_sample
+from tests import oracle_pins as P
+from tests.mutate import mutant
 
 
 @pytest.fixture(scope="module")
 def page_w():
-    return PL.page_weights()
+    return page_sample.page_weights()
 
 
-def _printed(golden):
-    return {r[0]: float(r[2]) for r in golden("handbook_error_table.txt")}
+@pytest.fixture(scope="module")
+def printed():
+    from tests.conftest import read_golden
+
+    return {r[0]: float(r[2]) for r in read_golden("handbook_error_table.txt")}
 
 
-def _q4_0_unsigned(w):
-    b = np.asarray(w, F32).reshape(-1, 32)
-    d = PL._div(np.abs(b).max(axis=1, keepdims=True), F32(8))   # mistake: |max| / 8
-    return (np.clip(np.rint(PL._div(b, d)), -8, 7) * d).reshape(-1), 4.5
+KQ_5BIT = [
+    ("_div(sc.max(axis=2), F32(63))", "_div(sc.max(axis=2), F32(31))"),
+    ("_div(mn.max(axis=2), F32(63))", "_div(mn.max(axis=2), F32(31))"),
+    ("np.clip(np.rint(_div(sc, dd)), 1, 63)", "np.clip(np.rint(_div(sc, dd)), 1, 31)"),
+    ("np.clip(np.rint(_div(mn, dm)), 0, 63)", "np.clip(np.rint(_div(mn, dm)), 0, 31)"),
+]
+
+# (name, edits, pin) -- pin is called with the mutant module and must fail
+FORMAT_MUTANTS = [
+    ("q8_0 divides by 128", [("_div(a, F32(127))", "_div(a, F32(128))")], "table"),
+    ("q4_0 scale divided by +8", [("_div(bj, F32(-8))", "_div(bj, F32(8))")], "table"),
+    ("q4_0 unsigned scale |max| / 8", [("_div(bj, F32(-8))", "_div(np.abs(bj), F32(8))")], "table"),
+    ("q4_0 tie takes the last index",
+     [("j = np.argmax(np.abs(b), axis=2)", "j = b.shape[2] - 1 - np.argmax(np.abs(b)[..., ::-1], axis=2)")],
+     "q4_0_tie"),
+    ("q4_1 sixteen levels", [("_div(hi - lo, F32(15))", "_div(hi - lo, F32(16))")], "table"),
+    ("q4_1 offset from the max", [("m_st = _store(lo, literal)", "m_st = _store(hi, literal)")], "table"),
+    ("k-quant 5-bit scale codes", KQ_5BIT, "table"),
+    ("k-quant codes floored", [("np.clip(np.rint(_div(b + Mn, S)), 0, qmax)",
+                                "np.clip(np.floor(_div(b + Mn, S)), 0, qmax)")], "table"),
+    ("k-quant minimum not clamped to <= 0", [("lo = np.minimum(b.min(axis=3), F32(0))", "lo = b.min(axis=3)")],
+     "kquant_roundtrip"),
+    ("codes against the unrounded scale (R1)",
+     [("d = scale_values(d_st)[..., None]\n    q = np.where(d == 0, F32(0), np.clip(np.rint(_div(b, d)), -127, 127))",
+       "d = _div(a, F32(127))[..., None]\n    q = np.where(d == 0, F32(0), np.clip(np.rint(_div(b, d)), -127, 127))")],
+     "q8_0_r1"),
+    ("q4_1 decode subtracts m", [("return nn.astype(F32) * d + m", "return nn.astype(F32) * d - m")], "q4_1_roundtrip"),
+    ("nibbles high first", [("(v[:, 0::2] | (v[:, 1::2] << 4))", "((v[:, 0::2] << 4) | v[:, 1::2])")], "bytes"),
+    ("k-quant pair holds t low, s high",
+     [('p = blk["s"].astype(np.uint32) | (blk["t"].astype(np.uint32) << 6)',
+       'p = blk["t"].astype(np.uint32) | (blk["s"].astype(np.uint32) << 6)')], "kquant_meta"),
+    ("rows not interleaved", [(".reshape(ng, units, UNIT).transpose(1, 0, 2).reshape(-1)",
+                               ".reshape(ng, units, UNIT).reshape(-1)")], "interleave"),
+    ("bin bit 1 means -1",
+     [('return (2 * bb.astype(np.int16) - 1).astype(F32) * _per_block(scale_values(blk["d"]), 128, bb.shape[1])',
+       'return (1 - 2 * bb.astype(np.int16)).astype(F32) * _per_block(scale_values(blk["d"]), 128, bb.shape[1])')],
+     "tern_bin"),
+    ("tern field offset 2", [("(f.astype(np.int16) - 1)", "(f.astype(np.int16) - 2)")], "tern_bin"),
+    ("bin8 step over 256", [("/ F32(255)).astype(F32)", "/ F32(256)).astype(F32)")], "bin8"),
+    ("bin8 codes floored", [("np.clip(np.rint((d - base[:, None]) / step[:, None]), 0, 255)",
+                             "np.clip(np.floor((d - base[:, None]) / step[:, None]), 0, 255)")], "bin8"),
+    ("bin8 base from the max", [("base = d.min(axis=1)", "base = d.max(axis=1)")], "bin8"),
+]
+
+MOE_MUTANTS = [
+    ("SwiGLU on the up projection", [("    u = _gemv64(wu, x)\n    h = silu(g) * u\n",
+                                      "    u = _gemv64(wu, x)\n    h = g * silu(u)\n")], "expert"),
+    ("down projection transposed",
+     [("o = np.asarray(h, np.float64) @ np.asarray(wd, np.float32).astype(np.float64).T",
+       "o = np.asarray(h, np.float64) @ np.asarray(wd, np.float32).astype(np.float64)")], "expert"),
+    ("silu replaced by sigmoid", [("return z / (1.0 + np.exp(-z))", "return 1.0 / (1.0 + np.exp(-z))")], "expert"),
+    ("top-K always renormalised", [("    if renorm:\n        w = w / w.sum", "    if True:\n        w = w / w.sum")],
+     "route"),
+    ("ties to the higher index", [('order = np.argsort(-p[i], kind="stable")',
+                                   'order = len(p[i]) - 1 - np.argsort(-p[i][::-1], kind="stable")')], "route"),
+    ("softmax not normalised", [("return e / e.sum(axis=-1, keepdims=True)", "return e")], "route"),
+    ("shared expert ungated", [("out[i] += sig[i] * o_all[i, top_k]", "out[i] += o_all[i, top_k]")], "combine"),
+    ("residual dropped", [('out = np.asarray(residual, np.float32).astype(np.float64).copy()',
+                           'out = np.zeros_like(np.asarray(residual, np.float32), dtype=np.float64)')], "combine"),
+]
 
 
-def _q4_0_sign_flip(w):
-    b = np.asarray(w, F32).reshape(-1, 32)
-    j = np.argmax(np.abs(b), axis=1)[:, None]
-    d = PL._div(np.take_along_axis(b, j, axis=1), F32(8))        # mistake: / +8
-    return (np.clip(np.rint(PL._div(b, d)), -8, 7) * d).reshape(-1), 4.5
+def _run_format_pin(kind, mod, page_w, printed):
+    if kind == "table":
+        P.error_table_literal(mod, page_w, printed)
+    elif kind == "q4_0_tie":
+        P.q4_0_tie_takes_first_index(mod)
+    elif kind == "kquant_roundtrip":
+        P.roundtrip_kquant(mod, "q4_k", 15)
+    elif kind == "q8_0_r1":
+        P.q8_0_codes_against_stored_scale(mod)
+    elif kind == "q4_1_roundtrip":
+        P.roundtrip_q4_1(mod)
+    elif kind == "bytes":
+        P.byte_order(mod)
+    elif kind == "kquant_meta":
+        P.kquant_meta_bytes(mod)
+    elif kind == "interleave":
+        P.row_interleave(mod)
+    elif kind == "tern_bin":
+        P.roundtrip_tern_bin(mod)
+    elif kind == "bin8":
+        P.bin8_affine_exact(mod)
+        P.bin8_rounding_bound(mod)
+    else:
+        raise KeyError(kind)
 
 
-def _q4_1_sixteen(w):
-    b = np.asarray(w, F32).reshape(-1, 32)
-    lo, hi = b.min(axis=1, keepdims=True), b.max(axis=1, keepdims=True)
-    d = PL._div(hi - lo, F32(16))                                # mistake: 16 levels
-    return (np.clip(np.rint(PL._div(b - lo, d)), 0, 15) * d + lo).reshape(-1), 5.0
+def _run_moe_pin(kind, mod):
+    {"expert": P.expert_forward_fsum, "route": P.route_pin, "combine": P.moe_combine_fsum}[kind](mod)
 
 
-def _q4_k_no_min_clamp(w):
-    b = np.asarray(w, F32).reshape(-1, 8, 32)
-    lo = b.min(axis=2, keepdims=True)                            # mistake: no clamp(max=0)
-    hi = b.max(axis=2, keepdims=True)
-    sc, mn = PL._div(hi - lo, F32(15)), -lo
-    dsc = PL._div(sc.max(axis=1, keepdims=True), F32(63))
-    dmn = PL._div(np.abs(mn).max(axis=1, keepdims=True), F32(63))
-    sc_q = np.clip(np.rint(PL._div(sc, dsc)), 1, 63) * dsc
-    mn_q = np.clip(np.rint(PL._div(mn, dmn)), 0, 63) * dmn
-    q = np.clip(np.rint(PL._div(b + mn_q, sc_q)), 0, 15)
-    return (q * sc_q - mn_q).reshape(-1), 4.5
+@pytest.mark.parametrize("name,edits,pin", FORMAT_MUTANTS, ids=[m[0] for m in FORMAT_MUTANTS])
+def test_format_mutant_rejected(page_w, printed, name, edits, pin):
+    _run_format_pin(pin, OF, page_w, printed)  # the pin holds on the oracle itself
+    mod = mutant(OF, edits)
+    with pytest.raises((AssertionError, ValueError, IndexError)):
+        _run_format_pin(pin, mod, page_w, printed)
 
 
-def _q4_k_scale_bits_5(w):
-    b = np.asarray(w, F32).reshape(-1, 8, 32)
-    lo = np.minimum(b.min(axis=2, keepdims=True), F32(0))
-    hi = b.max(axis=2, keepdims=True)
-    sc, mn = PL._div(hi - lo, F32(15)), -lo
-    dsc = PL._div(sc.max(axis=1, keepdims=True), F32(31))        # mistake: 5-bit scale codes
-    dmn = PL._div(mn.max(axis=1, keepdims=True), F32(31))
-    sc_q = np.clip(np.rint(PL._div(sc, dsc)), 1, 31) * dsc
-    mn_q = np.clip(np.rint(PL._div(mn, dmn)), 0, 31) * dmn
-    q = np.clip(np.rint(PL._div(b + mn_q, sc_q)), 0, 15)
-    return (q * sc_q - mn_q).reshape(-1), 4.5
+@pytest.mark.parametrize("name,edits,pin", MOE_MUTANTS, ids=[m[0] for m in MOE_MUTANTS])
+def test_moe_mutant_rejected(name, edits, pin):
+    _run_moe_pin(pin, OM)
+    mod = mutant(OM, edits)
+    with pytest.raises((AssertionError, ValueError)):
+        _run_moe_pin(pin, mod)
 
 
-def _q8_0_128(w):
-    b = np.asarray(w, F32).reshape(-1, 32)
-    d = PL._div(np.abs(b).max(axis=1, keepdims=True), F32(128))   # mistake: / 128
-    return (np.clip(np.rint(PL._div(b, d)), -127, 127) * d).reshape(-1), 8.5
-
-
-@pytest.mark.parametrize("name,fn", [
-    ("Q4_0", _q4_0_unsigned), ("Q4_0", _q4_0_sign_flip), ("Q4_1", _q4_1_sixteen),
-    ("Q4_K", _q4_k_scale_bits_5), ("Q8_0", _q8_0_128),
-])
-def test_planted_mistake_breaks_error_table(page_w, golden, name, fn):
-    deq, _ = fn(page_w)
-    assert round(PL.relative_error(deq, page_w), 4) != _printed(golden)[name]
-
-
-def test_planted_missing_min_clamp_breaks_handbuilt_roundtrip():
-    """Student-t blocks always have a negative minimum, so the table cannot see
-    a missing min clamp; the hand-built all-positive sub-block does."""
-    from oracle import formats as F
-    from tests.test_oracle_formats import _handbuilt_kquant
-
-    blk = _handbuilt_kquant(15)
-    w = F.dequant("q4_k", blk)
-    deq, _ = _q4_k_no_min_clamp(w.reshape(-1))
-    assert not np.array_equal(deq.reshape(w.shape), w)
-    deq_ok, _ = PL.q4_k(w.reshape(-1))
-    np.testing.assert_array_equal(deq_ok.reshape(w.shape), w)
+def test_transposed_down_on_square_expert_fails_on_values():
+    """On the square expert the transposed down projection runs and must fail
+    on the values, not on a shape error."""
+    mod = mutant(OM, [("o = np.asarray(h, np.float64) @ np.asarray(wd, np.float32).astype(np.float64).T",
+                       "o = np.asarray(h, np.float64) @ np.asarray(wd, np.float32).astype(np.float64)")])
+    wg, wu, wd, x = P._tiny_expert(128, 128, 12)
+    _, _, _, o = mod.expert_forward(wg, wu, wd, x)
+    eo = P.expert_fsum(wg, wu, wd, x[0])[3]
+    assert not np.allclose(o[0], eo, rtol=1e-6)
