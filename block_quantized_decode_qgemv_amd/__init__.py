@@ -133,8 +133,12 @@ def _fmt(fmt) -> int:
     return int(fmt)
 
 
-def _dev(t, dtype=None, name="tensor"):
-    """Device pointer of a torch CUDA tensor (checked) or a raw int pointer."""
+def _dev(t, dtype=None, name="tensor", nbytes=None):
+    """Device pointer of a torch CUDA tensor (checked) or a raw int pointer.
+
+    For a tensor, `nbytes` is the size the call reads or writes through it: a
+    smaller tensor raises ValueError here, before anything is launched.  A raw
+    int pointer is passed through unchecked (the caller vouches for it)."""
     if t is None:
         return None
     if isinstance(t, int):
@@ -145,7 +149,21 @@ def _dev(t, dtype=None, name="tensor"):
         raise TypeError(f"{name} must have dtype {dtype}, got {t.dtype}")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
+    if nbytes is not None:
+        have = t.numel() * t.element_size()
+        if have < nbytes:
+            raise ValueError(f"{name} holds {have} bytes; the call needs {nbytes}")
     return t.data_ptr()
+
+
+def _packed_bytes(fmt, n, k) -> int:
+    """Bytes of a packed [n][k] matrix, or 0 for arguments the library rejects
+    (it then reports the error itself)."""
+    return qg_packed_size(fmt, n, k) if n > 0 and k > 0 else 0
+
+
+def _ws(ws, ws_bytes, name="ws"):
+    return _dev(ws, None, name, ws_bytes if ws_bytes > 0 else None)
 
 
 def _stream(stream):
@@ -193,7 +211,8 @@ def moe_expert_ffn_workspace_size(t: int, e: int, h: int, i: int, top_k: int) ->
 
 def qg_hbm_read_probe(buf, nbytes: int, sink, stream=None) -> None:
     """Stream-read nbytes of a device buffer (see qg_hbm_read_probe in qgemv.h)."""
-    rc = load().qg_hbm_read_probe(_dev(buf, None, "buf"), nbytes, _dev(sink, None, "sink"), _stream(stream))
+    rc = load().qg_hbm_read_probe(_dev(buf, None, "buf", nbytes), nbytes, _dev(sink, None, "sink", 4),
+                                  _stream(stream))
     _check(rc, "qg_hbm_read_probe")
 
 
@@ -214,16 +233,19 @@ def qg_version() -> str:
 def qgemv(fmt, w, x, y, n: int, k: int, b: int = 1, ws=None, ws_bytes: int = 0, stream=None) -> None:
     """y[b][n] = sum_k W[n][k] x[b][k] on the device (see qgemv in qgemv.h)."""
     f32, u8 = _torch_dtypes()
-    rc = load().qgemv(_fmt(fmt), _dev(w, u8, "w"), _dev(x, f32, "x"), _dev(y, f32, "y"), n, k, b,
-                      _dev(ws, None, "ws"), ws_bytes, _stream(stream))
+    f, bb = _fmt(fmt), max(b, 0)
+    rc = load().qgemv(f, _dev(w, u8, "w", _packed_bytes(f, n, k)), _dev(x, f32, "x", 4 * bb * k),
+                      _dev(y, f32, "y", 4 * bb * n), n, k, b, _ws(ws, ws_bytes), ws_bytes, _stream(stream))
     _check(rc, "qgemv")
 
 
 def _named(cname, fmt):
     def fn(w, x, y, n, k, b=1, ws=None, ws_bytes=0, stream=None):
         f32, u8 = _torch_dtypes()
-        rc = getattr(load(), cname)(_dev(w, u8, "w"), _dev(x, f32, "x"), _dev(y, f32, "y"), n, k, b,
-                                    _dev(ws, None, "ws"), ws_bytes, _stream(stream))
+        bb = max(b, 0)
+        rc = getattr(load(), cname)(_dev(w, u8, "w", _packed_bytes(fmt, n, k)), _dev(x, f32, "x", 4 * bb * k),
+                                    _dev(y, f32, "y", 4 * bb * n), n, k, b, _ws(ws, ws_bytes), ws_bytes,
+                                    _stream(stream))
         _check(rc, cname)
 
     fn.__name__ = cname
@@ -245,8 +267,10 @@ def qgemv_rmsnorm(fmt, w, x, gamma, eps: float, y, n: int, k: int, b: int = 1, s
     """y[b] = W rmsnorm(x[b]; gamma, eps) on the device (see qgemv_rmsnorm in qgemv.h);
     gamma=None means unit gain (gamma folded into the weights)."""
     f32, u8 = _torch_dtypes()
-    rc = load().qgemv_rmsnorm(_fmt(fmt), _dev(w, u8, "w"), _dev(x, f32, "x"), _dev(gamma, f32, "gamma"),
-                              float(eps), _dev(y, f32, "y"), n, k, b, _stream(stream))
+    f, bb = _fmt(fmt), max(b, 0)
+    rc = load().qgemv_rmsnorm(f, _dev(w, u8, "w", _packed_bytes(f, n, k)), _dev(x, f32, "x", 4 * bb * k),
+                              _dev(gamma, f32, "gamma", 4 * max(k, 0)), float(eps), _dev(y, f32, "y", 4 * bb * n),
+                              n, k, b, _stream(stream))
     _check(rc, "qgemv_rmsnorm")
 
 
@@ -254,7 +278,9 @@ def qquant_device(fmt, w, out, n: int, k: int, status, stream=None) -> None:
     """Quantize fp32 device weights into packed device bytes (see qquant_device
     in qgemv.h); `status` (a device int32) reports device-side failures."""
     f32, u8 = _torch_dtypes()
-    rc = load().qquant_device(_fmt(fmt), _dev(w, f32, "w"), n, k, _dev(out, u8, "out"), _dev(status, None, "status"),
+    f = _fmt(fmt)
+    rc = load().qquant_device(f, _dev(w, f32, "w", 4 * max(n, 0) * max(k, 0)), n, k,
+                              _dev(out, u8, "out", _packed_bytes(f, n, k)), _dev(status, None, "status", 4),
                               _stream(stream))
     _check(rc, "qquant_device")
 
@@ -266,14 +292,18 @@ def qrequant_workspace_size(n: int, k: int) -> int:
 def qrequant(src_fmt, src, dst_fmt, dst, n: int, k: int, workspace, ws_bytes: int, status, stream=None) -> None:
     """Decode src and quantize it to dst_fmt on the device (see qrequant in qgemv.h)."""
     _, u8 = _torch_dtypes()
-    rc = load().qrequant(_fmt(src_fmt), _dev(src, u8, "src"), _fmt(dst_fmt), _dev(dst, u8, "dst"), n, k,
-                         _dev(workspace, None, "workspace"), ws_bytes, _dev(status, None, "status"), _stream(stream))
+    sf, df = _fmt(src_fmt), _fmt(dst_fmt)
+    rc = load().qrequant(sf, _dev(src, u8, "src", _packed_bytes(sf, n, k)), df,
+                         _dev(dst, u8, "dst", _packed_bytes(df, n, k)), n, k, _ws(workspace, ws_bytes, "workspace"),
+                         ws_bytes, _dev(status, None, "status", 4), _stream(stream))
     _check(rc, "qrequant")
 
 
 def qg_dequant(fmt, w, out, n: int, k: int, stream=None) -> None:
     f32, u8 = _torch_dtypes()
-    rc = load().qg_dequant(_fmt(fmt), _dev(w, u8, "w"), _dev(out, f32, "out"), n, k, _stream(stream))
+    f = _fmt(fmt)
+    rc = load().qg_dequant(f, _dev(w, u8, "w", _packed_bytes(f, n, k)), _dev(out, f32, "out", 4 * max(n, 0) * max(k, 0)),
+                           n, k, _stream(stream))
     _check(rc, "qg_dequant")
 
 
@@ -293,10 +323,23 @@ def qquant(fmt, w_host, n_threads: int | None = None) -> np.ndarray:
     return out[:size]
 
 
-def qpack_tern(codes, scale_bits) -> np.ndarray:
-    t = np.ascontiguousarray(codes, dtype=np.int8)
+def _codes_and_scales(codes, scale_bits, dtype, name):
+    """2-D [N, K] codes and fp16 scale bits of shape [N, K/128], checked so the
+    host packer never reads past either array."""
+    c = np.ascontiguousarray(codes, dtype=dtype)
     s = np.ascontiguousarray(scale_bits, dtype=np.uint16)
-    n, k = t.shape
+    if c.ndim != 2:
+        raise ValueError(f"{name}: codes must be 2-D [N, K], got shape {c.shape}")
+    n, k = c.shape
+    if k % 128:
+        raise ValueError(f"{name}: K={k} must be a multiple of 128")
+    if s.shape != (n, k // 128):
+        raise ValueError(f"{name}: scale_bits must have shape {(n, k // 128)}, got {s.shape}")
+    return c, s, n, k
+
+
+def qpack_tern(codes, scale_bits) -> np.ndarray:
+    t, s, n, k = _codes_and_scales(codes, scale_bits, np.int8, "qpack_tern")
     size = qg_packed_size("tern", n, k)
     out = np.empty(max(size, 1), dtype=np.uint8)
     _check(load().qpack_tern(t.ctypes.data, s.ctypes.data, n, k, out.ctypes.data), "qpack_tern")
@@ -304,9 +347,7 @@ def qpack_tern(codes, scale_bits) -> np.ndarray:
 
 
 def qpack_bin(bits, scale_bits) -> np.ndarray:
-    bb = np.ascontiguousarray(bits, dtype=np.uint8)
-    s = np.ascontiguousarray(scale_bits, dtype=np.uint16)
-    n, k = bb.shape
+    bb, s, n, k = _codes_and_scales(bits, scale_bits, np.uint8, "qpack_bin")
     size = qg_packed_size("bin", n, k)
     out = np.empty(max(size, 1), dtype=np.uint8)
     _check(load().qpack_bin(bb.ctypes.data, s.ctypes.data, n, k, out.ctypes.data), "qpack_bin")
@@ -315,9 +356,7 @@ def qpack_bin(bits, scale_bits) -> np.ndarray:
 
 def qpack_bin8(bits, scale_bits) -> np.ndarray:
     """1-bit codes and fp16 block scales -> packed bin8 bytes (see qpack_bin8 in qgemv.h)."""
-    bb = np.ascontiguousarray(bits, dtype=np.uint8)
-    s = np.ascontiguousarray(scale_bits, dtype=np.uint16)
-    n, k = bb.shape
+    bb, s, n, k = _codes_and_scales(bits, scale_bits, np.uint8, "qpack_bin8")
     size = qg_packed_size("bin8", n, k)
     out = np.empty(max(size, 1), dtype=np.uint8)
     _check(load().qpack_bin8(bb.ctypes.data, s.ctypes.data, n, k, out.ctypes.data), "qpack_bin8")
@@ -326,16 +365,26 @@ def qpack_bin8(bits, scale_bits) -> np.ndarray:
 
 # ---------------------------------------------------------------- MoE layer
 
+def _moe_sizes(fmt, e, h, i, t):
+    """Bytes each MoE argument spans: (gate/up, down, activations, logits, shared logits)."""
+    f = _fmt(fmt)
+    ok = e > 0 and h > 0 and i > 0 and t > 0
+    gu = (e + 1) * _packed_bytes(f, 2 * i, h) if ok else 0
+    dn = (e + 1) * _packed_bytes(f, h, i) if ok else 0
+    return f, gu, dn, 4 * max(t, 0) * max(h, 0), 4 * max(t, 0) * max(e, 0), 4 * max(t, 0)
+
+
 def moe_expert_ffn(fmt, w_gate_up, w_down, e: int, h: int, i: int, top_k: int, x, residual,
                    router_logits, shared_gate_logit, t: int, out, workspace, ws_bytes: int,
                    flags: int = 0, stream=None) -> None:
     """Routed expert layer (see moe_expert_ffn in qgemv.h)."""
     f32, u8 = _torch_dtypes()
-    rc = load().moe_expert_ffn(_fmt(fmt), _dev(w_gate_up, u8, "w_gate_up"), _dev(w_down, u8, "w_down"),
-                               e, h, i, top_k, _dev(x, f32, "x"), _dev(residual, f32, "residual"),
-                               _dev(router_logits, f32, "router_logits"),
-                               _dev(shared_gate_logit, f32, "shared_gate_logit"), t, flags,
-                               _dev(out, f32, "out"), _dev(workspace, None, "workspace"), ws_bytes,
+    f, gu, dn, act, lg, sl = _moe_sizes(fmt, e, h, i, t)
+    rc = load().moe_expert_ffn(f, _dev(w_gate_up, u8, "w_gate_up", gu), _dev(w_down, u8, "w_down", dn),
+                               e, h, i, top_k, _dev(x, f32, "x", act), _dev(residual, f32, "residual", act),
+                               _dev(router_logits, f32, "router_logits", lg),
+                               _dev(shared_gate_logit, f32, "shared_gate_logit", sl), t, flags,
+                               _dev(out, f32, "out", act), _ws(workspace, ws_bytes, "workspace"), ws_bytes,
                                _stream(stream))
     _check(rc, "moe_expert_ffn")
 
@@ -346,10 +395,12 @@ def moe_expert_ffn_rmsnorm(fmt, w_gate_up, w_down, e: int, h: int, i: int, top_k
     """Routed expert layer on RMS-normalised x (see moe_expert_ffn_rmsnorm in qgemv.h);
     gamma=None means unit gain (the gain folded into the gate/up weights)."""
     f32, u8 = _torch_dtypes()
-    rc = load().moe_expert_ffn_rmsnorm(_fmt(fmt), _dev(w_gate_up, u8, "w_gate_up"), _dev(w_down, u8, "w_down"),
-                                       e, h, i, top_k, _dev(x, f32, "x"), _dev(gamma, f32, "gamma"), float(eps),
-                                       _dev(residual, f32, "residual"), _dev(router_logits, f32, "router_logits"),
-                                       _dev(shared_gate_logit, f32, "shared_gate_logit"), t, flags,
-                                       _dev(out, f32, "out"), _dev(workspace, None, "workspace"), ws_bytes,
+    f, gu, dn, act, lg, sl = _moe_sizes(fmt, e, h, i, t)
+    rc = load().moe_expert_ffn_rmsnorm(f, _dev(w_gate_up, u8, "w_gate_up", gu), _dev(w_down, u8, "w_down", dn),
+                                       e, h, i, top_k, _dev(x, f32, "x", act), _dev(gamma, f32, "gamma", 4 * max(h, 0)),
+                                       float(eps), _dev(residual, f32, "residual", act),
+                                       _dev(router_logits, f32, "router_logits", lg),
+                                       _dev(shared_gate_logit, f32, "shared_gate_logit", sl), t, flags,
+                                       _dev(out, f32, "out", act), _ws(workspace, ws_bytes, "workspace"), ws_bytes,
                                        _stream(stream))
     _check(rc, "moe_expert_ffn_rmsnorm")

@@ -201,3 +201,125 @@ def test_library_missing_is_loud(tmp_path, monkeypatch):
     monkeypatch.setattr(qg, "_HERE", str(tmp_path))
     with pytest.raises(qg.QGLibraryMissing):
         qg.load()
+
+
+# The binding compares every tensor's byte size with what the call reads or
+# writes through it, before anything reaches the library.  A stand-in for a
+# device tensor (it only answers the questions the binding asks) lets the
+# checks run without a GPU.
+
+class _FakeDev:
+    is_cuda = True
+
+    def __init__(self, nbytes, dtype):
+        import torch
+
+        self.dtype = dtype
+        self._esize = torch.empty(0, dtype=dtype).element_size()
+        self._numel = nbytes // self._esize
+
+    def is_contiguous(self):
+        return True
+
+    def numel(self):
+        return self._numel
+
+    def element_size(self):
+        return self._esize
+
+    def data_ptr(self):
+        # a fake aligned address: every call below fails its size check
+        # before the library is entered, so it is never dereferenced
+        return P
+
+
+def _f32(nbytes):
+    import torch
+
+    return _FakeDev(nbytes, torch.float32)
+
+
+def _u8(nbytes):
+    import torch
+
+    return _FakeDev(nbytes, torch.uint8)
+
+
+@pytest.mark.parametrize("short", ["w", "x", "y", "ws"])
+def test_binding_rejects_undersized_gemv_tensors(short):
+    n, k, b = 40, 512, 3
+    size = {"w": qg.qg_packed_size("q4_k", n, k), "x": 4 * b * k, "y": 4 * b * n, "ws": 256}
+    args = {name: (_u8 if name in ("w", "ws") else _f32)(nb - (4 if name == short else 0)) for name, nb in size.items()}
+    with pytest.raises(ValueError, match=short):
+        qg.qgemv("q4_k", args["w"], args["x"], args["y"], n, k, b, ws=args["ws"], ws_bytes=256)
+    if short != "ws":
+        with pytest.raises(ValueError, match=short):
+            qg.qgemv_q4k(args["w"], args["x"], args["y"], n, k, b)
+
+
+@pytest.mark.parametrize("short", ["w", "x", "gamma", "y"])
+def test_binding_rejects_undersized_rmsnorm_tensors(short):
+    n, k, b = 16, 256, 2
+    size = {"w": qg.qg_packed_size("q8_0", n, k), "x": 4 * b * k, "gamma": 4 * k, "y": 4 * b * n}
+    a = {name: (_u8 if name == "w" else _f32)(nb - (4 if name == short else 0)) for name, nb in size.items()}
+    with pytest.raises(ValueError, match=short):
+        qg.qgemv_rmsnorm("q8_0", a["w"], a["x"], a["gamma"], 1e-6, a["y"], n, k, b)
+
+
+def test_binding_rejects_undersized_dequant_quant_probe():
+    n, k = 32, 256
+    with pytest.raises(ValueError, match="out"):
+        qg.qg_dequant("q4_0", _u8(qg.qg_packed_size("q4_0", n, k)), _f32(4 * n * k - 4), n, k)
+    with pytest.raises(ValueError, match="w"):
+        qg.qg_dequant("q4_0", _u8(qg.qg_packed_size("q4_0", n, k) - 1), _f32(4 * n * k), n, k)
+    with pytest.raises(ValueError, match="out"):
+        qg.qquant_device("q4_k", _f32(4 * n * k), _u8(qg.qg_packed_size("q4_k", n, k) - 16), n, k, _u8(4))
+    with pytest.raises(ValueError, match="status"):
+        qg.qquant_device("q4_k", _f32(4 * n * k), _u8(qg.qg_packed_size("q4_k", n, k)), n, k, _u8(2))
+    ws = qg.qrequant_workspace_size(n, k)
+    with pytest.raises(ValueError, match="dst"):
+        qg.qrequant("q4_k", _u8(qg.qg_packed_size("q4_k", n, k)), "q2_k", _u8(qg.qg_packed_size("q2_k", n, k) - 1),
+                    n, k, _u8(ws), ws, _u8(4))
+    with pytest.raises(ValueError, match="workspace"):
+        qg.qrequant("q4_k", _u8(qg.qg_packed_size("q4_k", n, k)), "q2_k", _u8(qg.qg_packed_size("q2_k", n, k)),
+                    n, k, _u8(ws - 4), ws, _u8(4))
+    with pytest.raises(ValueError, match="buf"):
+        qg.qg_hbm_read_probe(_u8(1024), 2048, _u8(4))
+
+
+@pytest.mark.parametrize("short", ["w_gate_up", "w_down", "x", "residual", "router_logits", "shared_gate_logit",
+                                   "out", "workspace", "gamma"])
+def test_binding_rejects_undersized_moe_tensors(short):
+    t, e, h, i, top_k = 2, 6, 256, 256, 2
+    ws = qg.moe_expert_ffn_workspace_size(t, e, h, i, top_k)
+    size = {"w_gate_up": (e + 1) * qg.qg_packed_size("q4_k", 2 * i, h),
+            "w_down": (e + 1) * qg.qg_packed_size("q4_k", h, i),
+            "x": 4 * t * h, "residual": 4 * t * h, "router_logits": 4 * t * e, "shared_gate_logit": 4 * t,
+            "out": 4 * t * h, "workspace": ws, "gamma": 4 * h}
+    a = {name: (_u8 if name in ("w_gate_up", "w_down", "workspace") else _f32)(nb - (4 if name == short else 0))
+         for name, nb in size.items()}
+    with pytest.raises(ValueError, match=short):
+        qg.moe_expert_ffn_rmsnorm("q4_k", a["w_gate_up"], a["w_down"], e, h, i, top_k, a["x"], a["gamma"], 1e-6,
+                                  a["residual"], a["router_logits"], a["shared_gate_logit"], t, a["out"],
+                                  a["workspace"], ws)
+    if short != "gamma":
+        with pytest.raises(ValueError, match=short):
+            qg.moe_expert_ffn("q4_k", a["w_gate_up"], a["w_down"], e, h, i, top_k, a["x"], a["residual"],
+                              a["router_logits"], a["shared_gate_logit"], t, a["out"], a["workspace"], ws)
+
+
+@pytest.mark.parametrize("packer,codes", [("qpack_tern", np.zeros((3, 256), np.int8)),
+                                          ("qpack_bin", np.zeros((3, 256), np.uint8)),
+                                          ("qpack_bin8", np.zeros((3, 256), np.uint8))])
+def test_packers_check_scale_shape(packer, codes):
+    fn = getattr(qg, packer)
+    good = np.full((3, 2), 0x3C00, np.uint16)
+    assert fn(codes, good).size == qg.qg_packed_size(packer[len("qpack_"):], 3, 256)
+    for bad in (np.full((3, 1), 0x3C00, np.uint16), np.full((2, 2), 0x3C00, np.uint16),
+                np.full((6,), 0x3C00, np.uint16)):
+        with pytest.raises(ValueError, match="scale_bits"):
+            fn(codes, bad)
+    with pytest.raises(ValueError, match="2-D"):
+        fn(codes.reshape(-1), good)
+    with pytest.raises(ValueError, match="multiple of 128"):
+        fn(np.zeros((3, 200), codes.dtype), good)
