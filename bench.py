@@ -2,27 +2,38 @@
 """Benchmark of the block-quantized batch-1 decode GEMV on one MI355X.
 
 Headline (the JSON line's ``value``): effective weight GB/s of the Q4_K
-batch-1 GEMV on a 14336x4096 matrix (packed bytes / wall time), cold cache:
-each step runs on the next of >= 1 GiB of distinct packed copies, so no step
-finds its weights in the 256 MB last-level cache.  One step = one GEMV call.
-Steps are launched from a HIP graph holding one launch per copy, replayed
-back to back, so the figure is the kernels', not the host's launch rate (the
-eagerly launched rate is reported next to it).
+batch-1 GEMV on a 14336x4096 matrix, cold cache.  The packed matrix exists as
+>= 1 GiB of distinct device copies (33 of 33 MB), so no launch finds its
+weights in the 256 MB last-level cache.  One *step* is one replay of a HIP
+graph that holds one GEMV launch per copy, i.e. one pass of the headline
+GEMV over every copy.  ``--warmup W`` replays are untimed; then exactly
+``--steps K`` replays are timed, each bracketed by HIP events on the launch
+stream.  ``ms_per_step`` is the median replay time, ``value`` the packed bytes
+of one step over that median, and ``roofline.achieved`` the same median per
+launch; p10 and p90 of the per-launch time come from the same samples.
 
-Also reported (in ``extra``): every GEMV of the four-format comparison
-(Q8_0/Q4_0/Q4_1/Q4_K x 4096x4096/14336x4096 x batch 1/8), the low-bit
-formats and the RMS-normalising Q4_K GEMV, each timed the same way.
+Also reported: the measured HBM read peak (a 4 GiB streaming read) and the
+headline's fraction of it, a same-size read, every GEMV of the four-format
+comparison (Q8_0/Q4_0/Q4_1/Q4_K x 4096x4096/14336x4096 x batch 1/8), the
+low-bit formats (tern/bin/bin8/Q2_K, batch 1/4) with their fraction of the
+VALU peak where VALU counters were taken, the row-starved shapes of the 8B
+step, the RMS-normalising GEMVs, the 8B decode step and the MoE layer.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--quick] [--no-cpu]
+    python bench.py --profile {gemv,copy,probe4g,valu,moe,step,norm}   # one part, for rocprofv3
+    python bench.py --summarize KIND CSV...                              # rocprofv3 CSVs -> profiles/
 
 Only one GPU is used; --gpus above 1 exits with a message.
 """
 from __future__ import annotations
 
 import argparse
+import csv
 import hashlib
 import json
 import os
+import platform
+import subprocess
 import sys
 import time
 
@@ -32,13 +43,28 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0           # MI355X published HBM3E bandwidth
+# non-packed fp32 VALU lane operations per second: 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz
+VALU_PEAK_LANE_OPS = 256 * 4 * 16 * 2.4e9
 DENSE_8B_BYTES = 3_925_868_544  # Q4_K bytes of the 8B-class step's linear weights
 COLD_BYTES = 1 << 30            # rotate over at least this many bytes of packed copies
-COUNTERS_FILE = os.path.join(ROOT, "profiles", "q4k_gemv_14336x4096_counters.txt")
+PROFILES = os.path.join(ROOT, "profiles")
+COUNTERS_FILE = os.path.join(PROFILES, "q4k_gemv_14336x4096_counters.txt")
+VALU_FILE = os.path.join(PROFILES, "gemv_valu_counters.txt")
+PEAK_FILE = os.path.join(PROFILES, "hbm_read_probe_4gib.txt")
 CSRC = os.path.join(ROOT, "block_quantized_decode_qgemv_amd", "csrc")
 KERNEL_SOURCES = {"kernel_source_sha256_16": os.path.join(CSRC, "gemv.hip"),
                   "kernel_core_sha256_16": os.path.join(CSRC, "gemv_core.h"),
                   "kernel_dispatch_sha256_16": os.path.join(CSRC, "gemv_dispatch.h")}
+
+FOUR_FORMATS = [(fmt, n, k, b) for fmt in ("q8_0", "q4_0", "q4_1", "q4_k")
+                for n, k in ((4096, 4096), (14336, 4096)) for b in (1, 8)]
+LOW_BIT = [(fmt, n, k, b) for fmt in ("tern", "bin", "bin8", "q2_k")
+           for n, k in ((4096, 4096), (12288, 4096), (4096, 12288)) for b in (1, 4)]
+# the 8B step's Q4_K shapes at batch 1, fused (qkv 6144, gate/up 28672) and not
+STEP_SHAPES = [("q4_k", n, k, 1) for n, k in ((1024, 4096), (4096, 4096), (6144, 4096), (14336, 4096),
+                                               (28672, 4096), (4096, 14336))]
+VALU_ROWS = FOUR_FORMATS + LOW_BIT
+VALU_LAUNCHES = 3               # launches per row in the VALU counter pass
 
 
 def log(msg):
@@ -50,23 +76,113 @@ def source_hash(path) -> str:
         return hashlib.sha256(fh.read()).hexdigest()[:16]
 
 
-def read_traffic():
-    """HBM bytes per launch from the committed counter summary, or None when the
-    kernel source changed since the counters were taken."""
-    if not os.path.exists(COUNTERS_FILE):
-        return None
+def _summary_fields(path):
     fields = {}
-    with open(COUNTERS_FILE, encoding="utf-8") as fh:
+    if not os.path.exists(path):
+        return None
+    with open(path, encoding="utf-8") as fh:
         for line in fh:
             if ":" in line and not line.startswith("#"):
                 key, val = line.split(":", 1)
                 fields[key.strip()] = val.strip()
-    if any(fields.get(key) != source_hash(path) for key, path in KERNEL_SOURCES.items()):
+    return fields
+
+
+def _sources_match(fields) -> bool:
+    return all(fields.get(key) == source_hash(path) for key, path in KERNEL_SOURCES.items())
+
+
+def read_traffic():
+    """HBM bytes per headline launch from the committed counter summary, or None
+    when the kernel source changed since the counters were taken."""
+    fields = _summary_fields(COUNTERS_FILE)
+    if not fields or not _sources_match(fields):
         return None
     try:
         return float(fields["hbm_bytes_per_launch"])
     except (KeyError, ValueError):
         return None
+
+
+def read_valu():
+    """{(fmt, N, K, B): VALU instructions per launch} from the committed counter
+    summary, or {} when the kernel source changed since it was taken."""
+    fields = _summary_fields(VALU_FILE)
+    if not fields or not _sources_match(fields):
+        return {}
+    out = {}
+    for key, val in fields.items():
+        if key.startswith("row "):
+            fmt, n, k, b = key[4:].split()
+            out[(fmt, int(n), int(k), int(b))] = float(val.split()[0])
+    return out
+
+
+def read_peak():
+    """The 4 GiB streaming read rate from rocprofv3 (FETCH_SIZE over kernel time)."""
+    fields = _summary_fields(PEAK_FILE)
+    try:
+        return float(fields["fetch_GBps"]) if fields else None
+    except (KeyError, ValueError):
+        return None
+
+
+def spread(samples) -> dict:
+    a = np.asarray(samples, dtype=np.float64)
+    return {"median": float(np.median(a)), "p10": float(np.percentile(a, 10)), "p90": float(np.percentile(a, 90))}
+
+
+def replay_times(torch, graph, stream, reps) -> np.ndarray:
+    """Seconds of each of `reps` back-to-back replays of `graph`, from HIP
+    events recorded on the launch stream between replays."""
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+    ev[0].record(stream)
+    for i in range(reps):
+        graph.replay()
+        ev[i + 1].record(stream)
+    ev[-1].synchronize()
+    return np.array([ev[i].elapsed_time(ev[i + 1]) for i in range(reps)]) * 1e-3
+
+
+def capture(torch, stream, launches):
+    """One HIP graph holding `launches` (zero-argument callables issuing work on `stream`)."""
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        for fn in launches:
+            fn()
+    return g
+
+
+def graph_time(torch, stream, launches, reps):
+    """Capture `launches` into one graph, replay it twice untimed, then `reps`
+    times timed; returns the spread of the replay time (seconds)."""
+    g = capture(torch, stream, launches)
+    for _ in range(2):
+        g.replay()
+    torch.cuda.synchronize()
+    return spread(replay_times(torch, g, stream, reps))
+
+
+_PACKED = {}  # (fmt, n, k, seed) -> packed host bytes, shared by the batch sizes of one matrix
+
+
+def packed_matrix(qg, fmt, n, k, seed):
+    import workloads
+
+    key = (fmt, n, k, seed)
+    if key not in _PACKED:
+        if fmt == "tern":
+            packed = qg.qpack_tern(workloads.ternary_codes(n, k, seed, 1),
+                                   workloads.scale_bits_f16((n, k // 128), seed, 2))
+        elif fmt in ("bin", "bin8"):
+            pack = qg.qpack_bin if fmt == "bin" else qg.qpack_bin8
+            packed = pack(workloads.binary_codes(n, k, seed, 1), workloads.scale_bits_f16((n, k // 128), seed, 2))
+        else:
+            packed = qg.qquant(fmt, workloads.student_t_weights(n, k, seed, n), n_threads=16)
+        if len(_PACKED) > 4:
+            _PACKED.clear()
+        _PACKED[key] = packed
+    return _PACKED[key]
 
 
 class Gemv:
@@ -80,14 +196,7 @@ class Gemv:
 
         self.torch = torch
         self.fmt, self.n, self.k, self.b = fmt, n, k, b
-        if fmt == "tern":
-            packed = qg.qpack_tern(workloads.ternary_codes(n, k, seed, 1),
-                                   workloads.scale_bits_f16((n, k // 128), seed, 2))
-        elif fmt in ("bin", "bin8"):
-            pack = qg.qpack_bin if fmt == "bin" else qg.qpack_bin8
-            packed = pack(workloads.binary_codes(n, k, seed, 1), workloads.scale_bits_f16((n, k // 128), seed, 2))
-        else:
-            packed = qg.qquant(fmt, workloads.student_t_weights(n, k, seed, n), n_threads=16)
+        packed = packed_matrix(qg, fmt, n, k, seed)
         self.bytes = packed.size
         copies = max(1, -(-min_bytes // self.bytes))
         # the copies are slices of one allocation, 256-byte aligned
@@ -104,6 +213,9 @@ class Gemv:
         self.fid = qg.FORMATS[fmt]
         self.wp = [t.data_ptr() for t in self.w]
         self.xp, self.yp = self.x.data_ptr(), self.y.data_ptr()
+        self.ws_bytes = qg.qgemv_workspace_size(fmt, n, k, b)
+        self.ws = torch.empty(max(self.ws_bytes, 16), dtype=torch.uint8, device="cuda")
+        self.wsp = self.ws.data_ptr() if self.ws_bytes else None
         # rmsnorm: the same GEMV fed by RMS norm of x (gain gamma, eps 1e-5);
         # "unit": unit gain, the gain folded into the weights (no gamma read)
         self.rmsnorm = rmsnorm
@@ -121,60 +233,29 @@ class Gemv:
             rc = self.lib.qgemv_rmsnorm(self.fid, w, self.xp, self.gp, 1e-5, self.yp, self.n, self.k, self.b,
                                         self.sp)
         else:
-            rc = self.lib.qgemv(self.fid, w, self.xp, self.yp, self.n, self.k, self.b, None, 0, self.sp)
+            rc = self.lib.qgemv(self.fid, w, self.xp, self.yp, self.n, self.k, self.b, self.wsp, self.ws_bytes,
+                                self.sp)
         if rc:
             raise RuntimeError(f"qgemv failed with {rc}")
         self.i += 1
 
     def capture(self) -> int:
         """A graph with one launch per packed copy, in rotation order."""
-        torch = self.torch
         self.i = 0
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g, stream=self.stream):
-            for _ in range(len(self.wp)):
-                self.step()
-        self.graph = g
+        self.graph = capture(self.torch, self.stream, [self.step] * len(self.wp))
         return len(self.wp)
 
     def replay(self, reps):
         for _ in range(reps):
             self.graph.replay()
 
-    def timed_replay(self, reps) -> float:
-        """Average per-launch time (s) over `reps` graph replays, from HIP events
-        recorded on the launch stream."""
-        torch = self.torch
-        a = torch.cuda.Event(enable_timing=True)
-        e = torch.cuda.Event(enable_timing=True)
-        a.record(self.stream)
-        self.replay(reps)
-        e.record(self.stream)
-        e.synchronize()
-        return a.elapsed_time(e) * 1e-3 / (reps * len(self.wp))
+    def launch_times(self, reps) -> np.ndarray:
+        """Per-launch seconds of `reps` graph replays (each replay's time over
+        its launch count)."""
+        return replay_times(self.torch, self.graph, self.stream, reps) / len(self.wp)
 
 
-def graph_time(torch, stream, launches, reps):
-    """Capture `launches` (a list of zero-argument callables issuing work on
-    `stream`) into one HIP graph; return (seconds per replay, graph)."""
-    g = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(g, stream=stream):
-        for fn in launches:
-            fn()
-    for _ in range(2):
-        g.replay()
-    torch.cuda.synchronize()
-    a = torch.cuda.Event(enable_timing=True)
-    e = torch.cuda.Event(enable_timing=True)
-    a.record(stream)
-    for _ in range(reps):
-        g.replay()
-    e.record(stream)
-    e.synchronize()
-    return a.elapsed_time(e) * 1e-3 / reps, g
-
-
-def read_probe(torch, qg, stream, head):
+def read_probe(torch, qg, stream, head, reps=20):
     """Streaming-read rate of the library's probe kernel: over the headline's
     rotating copies (same size, same cold cache) and over one 4 GiB buffer."""
     lib = qg.load()
@@ -184,12 +265,14 @@ def read_probe(torch, qg, stream, head):
     def probe(ptr, nbytes):
         return lambda: lib.qg_hbm_read_probe(ptr, nbytes, sink.data_ptr(), sp)
 
-    t, _ = graph_time(torch, stream, [probe(p, head.bytes) for p in head.wp], 20)
-    same = head.bytes * len(head.wp) / t / 1e9
+    same = graph_time(torch, stream, [probe(p, head.bytes) for p in head.wp], reps)
     big = torch.empty(4 << 30, dtype=torch.uint8, device="cuda")
-    t_big, _ = graph_time(torch, stream, [probe(big.data_ptr(), big.numel())], 10)
-    out = {"same_size_GBps": round(same, 1), "bytes_same_size": head.bytes,
-           "large_4GiB_GBps": round(big.numel() / t_big / 1e9, 1)}
+    large = graph_time(torch, stream, [probe(big.data_ptr(), big.numel())], reps)
+    out = {"same_size_GBps": round(head.bytes * len(head.wp) / same["median"] / 1e9, 1),
+           "bytes_same_size": head.bytes,
+           "large_4GiB_GBps": round(big.numel() / large["median"] / 1e9, 1),
+           "large_4GiB_GBps_p10_p90": [round(big.numel() / large["p90"] / 1e9, 1),
+                                       round(big.numel() / large["p10"] / 1e9, 1)]}
     del big
     torch.cuda.empty_cache()
     return out
@@ -198,19 +281,82 @@ def read_probe(torch, qg, stream, head):
 DENSE_LAYER = (("q", 4096, 4096), ("k", 1024, 4096), ("v", 1024, 4096), ("o", 4096, 4096),
                ("gate", 14336, 4096), ("up", 14336, 4096), ("down", 4096, 14336))
 DENSE_LAYERS = 32
+# one layer of the fused step: (name, N, K); q/k/v and gate/up each one matrix
+FUSED_LAYER = (("qkv", 6144, 4096), ("o", 4096, 4096), ("gateup", 28672, 4096), ("down", 4096, 14336))
 
 
-def dense_step(torch, qg, stream):
-    """The 8B-class decode step: 32 layers x 7 Q4_K GEMVs at batch 1, one HIP
-    graph.  One layer's weights are drawn and quantized; the 32 layers are
-    distinct device copies of it (3.9 GB, far beyond the 256 MB cache, so the
-    content repeat does not help the reads).  Also timed with q/k/v and
-    gate/up each fused into one matrix (128 launches instead of 224)."""
+class StepChain:
+    """The decode step's GEMVs as a dependency chain, as a layer issues them:
+    each projection reads the previous one's output.  q/k/v -> o reads the q
+    part (the attention output has q's shape; attention itself is not part
+    of this path), o -> gate/up, gate/up -> down reads the gate half (standing
+    in for SwiGLU(gate, up), which has its shape), down -> the next layer's
+    q/k/v (or q, k, v unfused).  Every launch writes its own output buffer,
+    so each can be checked after a replay.
+
+    layers: per layer a dict name -> packed device tensor, names from
+    FUSED_LAYER (fused) or DENSE_LAYER (unfused).  gammas (fused only): per
+    layer a [2][4096] device tensor of RMS-norm gains folded into q/k/v and
+    gate/up (qgemv_rmsnorm), or "unit" for gains folded into the weights.
+    """
+
+    def __init__(self, torch, qg, layers, x0, stream, fused=True, gammas=None, eps=1e-5):
+        lib, sp = qg.load(), stream.cuda_stream
+        fid = qg.FORMATS["q4_k"]
+        self.launches, self.records = [], []  # records: (layer, name, n, k, weight tensor, x tensor, y tensor)
+        self.keep = []
+        x = x0
+        shapes = FUSED_LAYER if fused else DENSE_LAYER
+        for li, layer in enumerate(layers):
+            ys = {name: torch.empty((1, n), device="cuda") for name, n, _ in shapes}
+            self.keep.append(ys)
+            for name, n, k in shapes:
+                if name in ("qkv", "q", "k", "v"):
+                    xin = x
+                elif name == "o":
+                    xin = ys["qkv"][:, :4096] if fused else ys["q"]
+                elif name in ("gateup", "gate", "up"):
+                    xin = ys["o"]
+                else:  # down
+                    xin = ys["gateup"][:, :14336] if fused else ys["gate"]
+                w, y = layer[name], ys[name]
+                wsb = qg.qgemv_workspace_size("q4_k", n, k, 1)
+                ws = torch.empty(max(wsb, 16), dtype=torch.uint8, device="cuda")
+                self.keep.append(ws)
+                norm = gammas is not None and name in ("qkv", "gateup")
+                args = (w.data_ptr(), xin.data_ptr(), y.data_ptr(), n, k)
+                if norm:
+                    gp = None if isinstance(gammas, str) else gammas[li][0 if name == "qkv" else 1].data_ptr()
+                    fn = (lambda a=args, gp=gp: lib.qgemv_rmsnorm(fid, a[0], a[1], gp, eps, a[2], a[3], a[4], 1, sp))
+                else:
+                    fn = (lambda a=args, wp=ws.data_ptr() if wsb else None, wsb=wsb:
+                          lib.qgemv(fid, a[0], a[1], a[2], a[3], a[4], 1, wp, wsb, sp))
+                self.launches.append(self._checked(fn, name))
+                self.records.append((li, name, n, k, w, xin, y, norm))
+            x = ys["down"]
+
+    @staticmethod
+    def _checked(fn, name):
+        def call():
+            rc = fn()
+            if rc:
+                raise RuntimeError(f"step launch {name} failed with {rc}")
+        return call
+
+
+def dense_step(torch, qg, stream, variants=("plain", "fused", "norms", "folded"), reps=20, eager=0):
+    """The 8B-class decode step: 32 layers x 7 Q4_K GEMVs at batch 1 as one HIP
+    graph, each GEMV reading the previous one's output (StepChain).  One
+    layer's weights are drawn and quantized; the 32 layers are distinct device
+    copies of it (3.9 GB, far beyond the 256 MB cache, so the content repeat
+    does not help the reads).  Variants: "plain" (224 launches), "fused"
+    (q/k/v and gate/up each one matrix: 128 launches), "norms" (fused, with
+    each layer's two RMS norms folded into q/k/v and gate/up, gain vectors),
+    "folded" (the same with the gains folded into the weights).  eager > 0
+    (profiling): run the fused step that many times without a graph instead
+    of timing."""
     import workloads
 
-    lib = qg.load()
-    fid = qg.FORMATS["q4_k"]
-    sp = stream.cuda_stream
     host = {}
     for j, (name, n, k) in enumerate(DENSE_LAYER):
         host[name] = workloads.student_t_weights_device(n, k, 0, 700 + j).cpu().numpy()
@@ -219,61 +365,52 @@ def dense_step(torch, qg, stream):
              "gateup": qg.qquant("q4_k", np.concatenate([host["gate"], host["up"]]), n_threads=16)}
     del host
     total = sum(p.size for p in packed.values()) * DENSE_LAYERS
-    xs = {4096: workloads.normal_device((1, 4096), 0, 801), 14336: workloads.normal_device((1, 14336), 0, 802)}
-    ys = {n: torch.empty((1, n), device="cuda") for n in (1024, 4096, 6144, 14336, 28672)}
+    x0 = workloads.normal_device((1, 4096), 0, 801)
 
-    def gemv(w, n, k):
-        wp, xp, yp = w.data_ptr(), xs[k].data_ptr(), ys[n].data_ptr()
-        return lambda: lib.qgemv(fid, wp, xp, yp, n, k, 1, None, 0, sp)
-
-    dev = [{name: torch.from_numpy(packed[name]).to("cuda") for name, _, _ in DENSE_LAYER} for _ in range(DENSE_LAYERS)]
-    launches = [gemv(layer[name], n, k) for layer in dev for name, n, k in DENSE_LAYER]
-    t, _ = graph_time(torch, stream, launches, 20)
-    del dev, launches
-    torch.cuda.empty_cache()
+    out = {"layers": DENSE_LAYERS, "bytes": total, "chained": True}
+    if "plain" in variants:
+        dev = [{name: torch.from_numpy(packed[name]).to("cuda") for name, _, _ in DENSE_LAYER}
+               for _ in range(DENSE_LAYERS)]
+        chain = StepChain(torch, qg, dev, x0, stream, fused=False)
+        t = graph_time(torch, stream, chain.launches, reps)
+        out.update({"launches": len(chain.launches), "step_us": round(t["median"] * 1e6, 1),
+                    "step_us_p10_p90": [round(t["p10"] * 1e6, 1), round(t["p90"] * 1e6, 1)],
+                    "tok_s": round(1.0 / t["median"], 1), "GBps": round(total / t["median"] / 1e9, 1)})
+        del dev, chain
+        torch.cuda.empty_cache()
     dev = [{name: torch.from_numpy(p).to("cuda") for name, p in fused.items()} |
            {name: torch.from_numpy(packed[name]).to("cuda") for name in ("o", "down")} for _ in range(DENSE_LAYERS)]
-    launches = []
-    for layer in dev:
-        launches += [gemv(layer["qkv"], 6144, 4096), gemv(layer["o"], 4096, 4096),
-                     gemv(layer["gateup"], 28672, 4096), gemv(layer["down"], 4096, 14336)]
-    t_fused, _ = graph_time(torch, stream, launches, 20)
+    chain = StepChain(torch, qg, dev, x0, stream)
+    if eager:
+        for _ in range(eager):
+            for fn in chain.launches:
+                fn()
+        torch.cuda.synchronize()
+        return {"eager_fused_steps": eager}
+    if "fused" in variants:
+        t = graph_time(torch, stream, chain.launches, reps)
+        out.update({"fused_launches": len(chain.launches), "fused_step_us": round(t["median"] * 1e6, 1),
+                    "fused_step_us_p10_p90": [round(t["p10"] * 1e6, 1), round(t["p90"] * 1e6, 1)],
+                    "fused_tok_s": round(1.0 / t["median"], 1), "fused_GBps": round(total / t["median"] / 1e9, 1)})
     # the same with each layer's two RMS norms folded into the projections
     # they feed (attention norm -> q/k/v, FFN norm -> gate/up)
     gammas = [workloads.normal_device((2, 4096), 0, 900 + j) * 0.25 + 1.0 for j in range(DENSE_LAYERS)]
-
-    def gemv_norm(w, n, k, gamma):
-        wp, xp, yp = w.data_ptr(), xs[k].data_ptr(), ys[n].data_ptr()
-        gp = None if gamma is None else gamma.data_ptr()
-        return lambda: lib.qgemv_rmsnorm(fid, wp, xp, gp, 1e-5, yp, n, k, 1, sp)
-
-    launches = []
-    for layer, gm in zip(dev, gammas):
-        launches += [gemv_norm(layer["qkv"], 6144, 4096, gm[0]), gemv(layer["o"], 4096, 4096),
-                     gemv_norm(layer["gateup"], 28672, 4096, gm[1]), gemv(layer["down"], 4096, 14336)]
-    t_norm, _ = graph_time(torch, stream, launches, 20)
-    # the gains folded into q/k/v and gate/up (same bytes), unit-gain norms at run time
-    launches = []
-    for layer in dev:
-        launches += [gemv_norm(layer["qkv"], 6144, 4096, None), gemv(layer["o"], 4096, 4096),
-                     gemv_norm(layer["gateup"], 28672, 4096, None), gemv(layer["down"], 4096, 14336)]
-    t_fold, _ = graph_time(torch, stream, launches, 20)
-    del dev, launches, gammas
+    for name, g in (("norms", gammas), ("folded", "unit")):
+        if name not in variants:
+            continue
+        chain = StepChain(torch, qg, dev, x0, stream, gammas=g)
+        t = graph_time(torch, stream, chain.launches, reps)
+        key = "fused_with_norms" if name == "norms" else "fused_with_folded_norms"
+        out.update({f"{key}_step_us": round(t["median"] * 1e6, 1), f"{key}_tok_s": round(1.0 / t["median"], 1)})
+    del dev, chain, gammas
     torch.cuda.empty_cache()
-    return {"layers": DENSE_LAYERS, "bytes": total,
-            "launches": DENSE_LAYERS * len(DENSE_LAYER), "step_us": round(t * 1e6, 1),
-            "tok_s": round(1.0 / t, 1), "GBps": round(total / t / 1e9, 1),
-            "fused_launches": DENSE_LAYERS * 4, "fused_step_us": round(t_fused * 1e6, 1),
-            "fused_tok_s": round(1.0 / t_fused, 1), "fused_GBps": round(total / t_fused / 1e9, 1),
-            "fused_with_norms_step_us": round(t_norm * 1e6, 1), "fused_with_norms_tok_s": round(1.0 / t_norm, 1),
-            "fused_with_folded_norms_step_us": round(t_fold * 1e6, 1),
-            "fused_with_folded_norms_tok_s": round(1.0 / t_fold, 1)}
+    return out
 
 
 MOE_E, MOE_H, MOE_I, MOE_TOPK, MOE_POOL, MOE_SETS = 512, 4096, 1024, 4, 8, 32
 
 
-def moe_layer(torch, qg, stream, fmt, t_tokens, norm=False):
+def moe_layer(torch, qg, stream, fmt, t_tokens, norm=False, reps=10, eager=0):
     """The MoE layer (512 experts + 1 shared, hidden 4096, intermediate 1024,
     top-4) at T tokens, every expert resident.  Experts are distinct device
     copies of a pool of MOE_POOL drawn experts (the pool repeats every
@@ -286,7 +423,8 @@ def moe_layer(torch, qg, stream, fmt, t_tokens, norm=False):
     projection (Q8_0 [E][H]) fed by the RMS norm of the block input, then the
     expert layer on the normalised input with the block input as residual;
     MOE_SETS input sets, so every call routes anew.  Its bytes add the
-    router's."""
+    router's.  eager > 0 (profiling): that many passes over the sets without
+    a graph instead of timing."""
     import workloads
 
     lib = qg.load()
@@ -319,6 +457,7 @@ def moe_layer(torch, qg, stream, fmt, t_tokens, norm=False):
         return lambda: lib.moe_expert_ffn(*args)
 
     router_bytes = 0
+    calls = [call(r) for r in range(MOE_SETS)]
     if norm:
         q8 = qg.FORMATS["q8_0"]
         router = torch.from_numpy(qg.qquant("q8_0", workloads.student_t_weights_device(e_, h_, 1, 77).cpu().numpy(),
@@ -341,27 +480,36 @@ def moe_layer(torch, qg, stream, fmt, t_tokens, norm=False):
                     raise RuntimeError(f"MoE block step failed with {rc}")
             return fn
 
-        for r in range(MOE_SETS):
-            call_norm(r)()  # the logits the step's routes come from
+        calls = [call_norm(r) for r in range(MOE_SETS)]
+        for fn in calls:
+            fn()  # the logits the step's routes come from
         torch.cuda.synchronize()
-        t, _ = graph_time(torch, stream, [call_norm(r) for r in range(MOE_SETS)], 10)
-    else:
-        t, _ = graph_time(torch, stream, [call(r) for r in range(MOE_SETS)], 10)
-    t /= MOE_SETS
+    if eager:
+        for _ in range(eager):
+            for fn in calls:
+                fn()
+        torch.cuda.synchronize()
+        del gu, dn, ws
+        torch.cuda.empty_cache()
+        return {"fmt": fmt, "T": t_tokens, "eager_passes": eager}
+    t = graph_time(torch, stream, calls, reps)
     touched = np.mean([len(set(np.argsort(-lg.cpu().numpy(), axis=1, kind="stable")[:, :k_].ravel().tolist())) + 1
                        for lg in logits])
     nbytes = touched * (gu_sz + dn_sz) + router_bytes
+    med = t["median"] / MOE_SETS
     del gu, dn, ws
     torch.cuda.empty_cache()
     return {"fmt": fmt, "T": t_tokens, "norm_block": {False: False, True: "gain vector", "unit": "gain folded"}[norm],
-            "us": round(t * 1e6, 2),
+            "us": round(med * 1e6, 2),
+            "us_p10_p90": [round(t["p10"] / MOE_SETS * 1e6, 2), round(t["p90"] / MOE_SETS * 1e6, 2)],
             "experts_touched": round(float(touched), 2),
-            "bytes": int(nbytes), "GBps": round(float(nbytes) / t / 1e9, 1)}
+            "bytes": int(nbytes), "GBps": round(float(nbytes) / med / 1e9, 1)}
 
 
-def cpu_baseline(seconds=12.0):
-    """The oracle (numpy dequant + float64 matvec) on a bounded sample of the
-    headline workload: whole 14336x4096 Q4_K GEMVs, repeated for ~seconds."""
+def cpu_baseline(seconds=8.0):
+    """The oracle (numpy unpack + dequant + float64 matvec) on a bounded sample
+    of the headline workload: whole 14336x4096 Q4_K GEMVs, repeated for about
+    `seconds` with the BLAS pool at all its threads, then at one thread."""
     import workloads
     from oracle import formats as OF
     from oracle import gemv as OG
@@ -370,44 +518,224 @@ def cpu_baseline(seconds=12.0):
     w = workloads.student_t_weights(n, k, 0, n)
     packed = OF.quantize_packed("q4_k", w)
     x = workloads.normal((1, k), 0, 99)
-    reps = 0
-    t_deq = 0.0
-    t0 = time.perf_counter()
-    while True:
-        t1 = time.perf_counter()
-        w_deq = OF.dequant_packed("q4_k", packed, n, k)
-        t_deq += time.perf_counter() - t1
-        OG.gemv_ref(w_deq, x)
-        reps += 1
-        el = time.perf_counter() - t0
-        if el >= seconds:
-            break
-    threads = 1
+
+    def run(limit):
+        reps, t_deq = 0, 0.0
+        t0 = time.perf_counter()
+        while True:
+            t1 = time.perf_counter()
+            w_deq = OF.dequant_packed("q4_k", packed, n, k)
+            t_deq += time.perf_counter() - t1
+            OG.gemv_ref(w_deq, x)
+            reps += 1
+            el = time.perf_counter() - t0
+            if el >= limit:
+                return reps, el, t_deq
+
+    threads = None
     try:
-        from threadpoolctl import threadpool_info
+        from threadpoolctl import threadpool_info, threadpool_limits
 
         threads = max([1] + [int(p.get("num_threads", 1)) for p in threadpool_info()])
+        reps, el, t_deq = run(seconds)
+        with threadpool_limits(limits=1):
+            reps1, el1, _ = run(seconds)
+    except ImportError:  # pragma: no cover - threadpoolctl ships with scikit-learn here
+        reps, el, t_deq = run(seconds)
+        reps1, el1 = None, None
+    out = {"value": round(packed.size * reps / el / 1e9, 4), "unit": "GB/s", "cores": threads or 1, "kind": "oracle",
+           "sample": f"{reps} full Q4_K 14336x4096 batch-1 GEMVs (unpack + dequant + float64 matvec) in {el:.1f} s "
+                     f"with the BLAS pool at {threads} threads (unpack + dequant, single-threaded numpy, "
+                     f"{100 * t_deq / el:.0f} % of it); host os.cpu_count() = {os.cpu_count()}",
+           "host_cpu_count": os.cpu_count(), "blas_threads": threads,
+           "dequant_share": round(t_deq / el, 3)}
+    if reps1 is not None:
+        out["one_thread_value"] = round(packed.size * reps1 / el1 / 1e9, 4)
+        out["one_thread_sample"] = f"{reps1} of the same GEMVs in {el1:.1f} s with the BLAS pool at 1 thread"
+    return out
+
+
+def environment(torch) -> dict:
+    env = {"torch": torch.__version__, "hip": getattr(torch.version, "hip", None), "python": platform.python_version()}
+    try:
+        with open("/opt/rocm/.info/version", encoding="utf-8") as fh:
+            env["rocm"] = fh.read().strip()
+    except OSError:
+        pass
+    try:
+        with open("/sys/module/amdgpu/version", encoding="utf-8") as fh:
+            env["amdgpu_driver"] = fh.read().strip()
+    except OSError:
+        pass
+    try:
+        props = torch.cuda.get_device_properties(0)
+        env["device"] = props.name
+        env["arch"] = getattr(props, "gcnArchName", None)
+        env["compute_units"] = props.multi_processor_count
     except Exception:
         pass
-    return {"value": round(packed.size * reps / el / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
-            "sample": f"{reps} full Q4_K 14336x4096 batch-1 GEMVs (unpack + dequant + float64 matvec), {el:.1f} s; "
-                      f"unpack + dequant {100 * t_deq / el:.0f} % of it"}
+    try:
+        env["git_rev"] = subprocess.run(["git", "-C", ROOT, "rev-parse", "--short=12", "HEAD"], capture_output=True,
+                                        text=True, check=True, timeout=10).stdout.strip()
+    except Exception:
+        env["git_rev"] = None  # the GPU box gets the tree without .git; the source hashes identify it
+    env.update({key: source_hash(path) for key, path in KERNEL_SOURCES.items()})
+    return env
 
+
+# ------------------------------------------------------------------ rocprofv3 CSVs -> profiles/
+
+def _csv_rows(path):
+    with open(path, newline="", encoding="utf-8") as fh:
+        return list(csv.DictReader(fh))
+
+
+def _counter_per_dispatch(path, name_filter, counter=None):
+    """[(dispatch id, kernel name, grid size, value)] of one counter CSV: the
+    dispatches whose kernel name contains `name_filter`, in dispatch order, the
+    rows of `counter` (every counter when None) summed per dispatch."""
+    rows = {}
+    for r in _csv_rows(path):
+        if name_filter not in r["Kernel_Name"] or (counter and r.get("Counter_Name") != counter):
+            continue
+        did = int(r["Dispatch_Id"])
+        prev = rows.get(did)
+        val = float(r["Counter_Value"])
+        rows[did] = (did, r["Kernel_Name"], int(r.get("Grid_Size", 0) or 0), val + (prev[3] if prev else 0.0))
+    return [rows[d] for d in sorted(rows)]
+
+
+def _copy_kib(path):
+    """Median counter value (KiB) of the 1 GiB device copies of `--profile copy`."""
+    vals = [v for _, _, _, v in _counter_per_dispatch(path, "copyBuffer")] or \
+        [v for _, _, _, v in _counter_per_dispatch(path, "")]
+    return float(np.median(vals))
+
+
+def _header(title, commands):
+    lines = [f"# {title}", "# commands (from the repository root as $REPO):"]
+    lines += [f"#   {c}" for c in commands]
+    lines += [f"{key}: {source_hash(path)}" for key, path in KERNEL_SOURCES.items()]
+    return lines
+
+
+def summarize(kind, paths, commands):
+    """Write the profiles/ summary of `kind` from rocprofv3 CSV `paths`."""
+    if kind == "valu":
+        # paths: counter CSV of `rocprofv3 --pmc SQ_INSTS_VALU SQ_WAVES -- bench.py --profile valu`
+        disp = _counter_per_dispatch(paths[0], "gemv_dpp_kernel", "SQ_INSTS_VALU")
+        waves = {d: v for d, _, _, v in _counter_per_dispatch(paths[0], "gemv_dpp_kernel", "SQ_WAVES")}
+        assert len(disp) == len(VALU_ROWS) * VALU_LAUNCHES, (len(disp), len(VALU_ROWS) * VALU_LAUNCHES)
+        lines = _header("VALU instructions per launch of the register-x GEMV (rocprofv3 SQ_INSTS_VALU)", commands)
+        lines.append(f"# row fmt N K B: VALU instructions per launch (median of {VALU_LAUNCHES}) | lane-ops per weight "
+                     "(64 lanes per instruction over the N*K weights) | waves per launch")
+        for j, (fmt, n, k, b) in enumerate(VALU_ROWS):
+            grp = disp[j * VALU_LAUNCHES:(j + 1) * VALU_LAUNCHES]
+            v = float(np.median([g[3] for g in grp]))
+            wv = float(np.median([waves.get(g[0], 0.0) for g in grp])) if waves else 0.0
+            lines.append(f"row {fmt} {n} {k} {b}: {v:.0f} | {v * 64 / (n * k):.3f} | {wv:.0f}")
+        out = VALU_FILE
+    elif kind == "peak":
+        # paths: kernel-trace CSV and FETCH_SIZE counter CSV of `--profile probe4g`, then the copy calibration CSV
+        tr = [r for r in _csv_rows(paths[0]) if "read_probe_kernel" in r["Kernel_Name"]]
+        dur = [int(r["End_Timestamp"]) - int(r["Start_Timestamp"]) for r in tr]
+        fetch = [v for _, _, _, v in _counter_per_dispatch(paths[1], "read_probe_kernel", "FETCH_SIZE")]
+        copy_fetch = _copy_kib(paths[2])
+        scale = (1 << 30) / 1024 / copy_fetch
+        fb = float(np.median(fetch)) * 1024 * scale
+        lines = _header("HBM streaming-read peak: the library's read probe over one 4 GiB buffer", commands)
+        lines += [f"dispatches_traced: {len(dur)}", f"duration_ns_median: {np.median(dur):.0f}",
+                  f"duration_ns_p10: {np.percentile(dur, 10):.0f}", f"duration_ns_p90: {np.percentile(dur, 90):.0f}",
+                  f"fetch_kib_per_dispatch_median: {np.median(fetch):.1f}",
+                  f"copy_1gib_fetch_kib_median: {copy_fetch:.1f}",
+                  f"fetch_scale: {scale:.4f}", f"fetched_bytes_per_dispatch: {fb:.0f}",
+                  f"buffer_bytes: {4 << 30}",
+                  f"fetch_GBps: {fb / np.median(dur):.1f}",
+                  f"buffer_GBps: {(4 << 30) / np.median(dur):.1f}"]
+        out = PEAK_FILE
+    elif kind in ("moe", "step", "norm"):
+        # paths: FETCH_SIZE CSV, WRITE_SIZE CSV of the same --profile run, then the copy FETCH and WRITE CSVs
+        copy_f, copy_w = _copy_kib(paths[2]), _copy_kib(paths[3])
+        fs, ws = (1 << 30) / 1024 / copy_f, (1 << 30) / 1024 / copy_w
+        per = {}
+        for idx, path in enumerate(paths[:2]):
+            for _, name, grid, v in _counter_per_dispatch(path, "qg::"):
+                short = name.replace("qg::(anonymous namespace)::", "").replace("void ", "").split("(")[0]
+                per.setdefault(f"{short} grid {grid}", ([], []))[idx].append(v)
+        title = {"moe": "MoE layer (512+1 experts, H 4096, I 1024, top-4; Q4_K and Q2_K, T 1 and 8)",
+                 "step": "8B decode step, q/k/v and gate/up fused (128 Q4_K GEMVs per step)",
+                 "norm": "RMS-norm GEMVs and the MoE pre-norm block step"}[kind]
+        lines = _header(f"HBM bytes per dispatch from rocprofv3 FETCH_SIZE / WRITE_SIZE: {title}", commands)
+        lines += [f"copy_1gib_fetch_kib: {copy_f:.1f}", f"copy_1gib_write_kib: {copy_w:.1f}",
+                  f"fetch_scale: {fs:.4f}", f"write_scale: {ws:.4f}",
+                  "# kernel and grid size (work-items): dispatches | fetched MB per dispatch (mean) | "
+                  "written MB per dispatch (mean)"]
+        for name in sorted(per):
+            f_, w_ = per[name]
+            lines.append(f"kernel {name}: {len(f_)} | {np.mean(f_) * 1024 * fs / 1e6:.3f} | "
+                         f"{(np.mean(w_) * 1024 * ws / 1e6) if w_ else float('nan'):.3f}")
+        out = os.path.join(PROFILES, {"moe": "moe_layer_e512_h4096_i1024_counters.txt",
+                                      "step": "dense_8b_step_counters.txt",
+                                      "norm": "q4k_rmsnorm_gemv_and_moe_block_counters.txt"}[kind])
+    elif kind == "step-trace":
+        # paths: kernel-trace CSV of `--profile step-graph` (graph replays of the fused step: 128 GEMVs each)
+        tr = sorted((r for r in _csv_rows(paths[0]) if "gemv_dpp_kernel" in r["Kernel_Name"]),
+                    key=lambda r: int(r["Start_Timestamp"]))
+        st = np.array([int(r["Start_Timestamp"]) for r in tr])
+        en = np.array([int(r["End_Timestamp"]) for r in tr])
+        per_step = 128
+        steps = len(tr) // per_step
+        rows = []
+        for s in range(1, steps):  # the first step pays the first-launch costs
+            a, b = s * per_step, (s + 1) * per_step
+            span = en[b - 1] - st[a]
+            busy = float(np.sum(en[a:b] - st[a:b]))
+            gaps = float(np.sum(np.maximum(st[a + 1:b] - en[a:b - 1], 0)))
+            rows.append((span, busy, gaps))
+        rows = np.array(rows)
+        lines = _header("8B decode step (fused: 128 Q4_K GEMVs per step): kernel time against launch gaps", commands)
+        lines += [f"steps_summarized: {len(rows)}",
+                  f"span_us_median: {np.median(rows[:, 0]) / 1e3:.1f}",
+                  f"kernel_busy_us_median: {np.median(rows[:, 1]) / 1e3:.1f}",
+                  f"gaps_us_median: {np.median(rows[:, 2]) / 1e3:.1f}",
+                  f"gap_per_launch_us: {np.median(rows[:, 2]) / 1e3 / (per_step - 1):.2f}"]
+        out = os.path.join(PROFILES, "dense_8b_step_gaps.txt")
+    else:
+        raise SystemExit(f"unknown summary kind {kind}")
+    with open(out, "w", encoding="utf-8") as fh:
+        fh.write("\n".join(lines) + "\n")
+    log(f"wrote {out}")
+
+
+# ------------------------------------------------------------------------------------------ main
 
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=4000)
-    ap.add_argument("--warmup", type=int, default=200)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--quick", action="store_true", help="headline only, no extra configs")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle cpu_baseline leg")
-    ap.add_argument("--profile", choices=["gemv", "copy", "probe", "moe", "step", "norm"], default=None,
-                    help="run only one part (the headline kernel, a 1 GiB copy, the read probe, the MoE layer, "
-                         "the 8B step, or the RMS-norm GEMVs and MoE block step) for rocprofv3")
+    ap.add_argument("--profile", choices=["gemv", "copy", "probe4g", "valu", "moe", "step", "step-graph", "norm"],
+                    default=None,
+                    help="run only one part for rocprofv3: the headline kernel, a 1 GiB copy, the 4 GiB read "
+                         "probe, every GEMV row for VALU counters, the MoE layer, the 8B step (eager launches, for "
+                         "counters; step-graph: graph replays, for the kernel trace), or the RMS-norm GEMVs and MoE "
+                         "block step")
+    ap.add_argument("--summarize", nargs="+", metavar=("KIND", "CSV"), default=None,
+                    help="write a profiles/ summary from rocprofv3 CSVs (kinds: valu, peak, moe, step, norm, "
+                         "step-trace)")
+    ap.add_argument("--command", action="append", default=[], help="command line recorded in a summary")
     args = ap.parse_args()
+    if args.summarize:
+        summarize(args.summarize[0], args.summarize[1:], args.command)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "
               "(the GEMV is measured on one GPU's share; no collectives are built)", file=sys.stderr)
+        sys.exit(2)
+    if args.steps < 2:
+        print("bench.py: --steps must be at least 2 (the spread needs several replays)", file=sys.stderr)
         sys.exit(2)
 
     import torch
@@ -429,28 +757,48 @@ def main():
         torch.cuda.synchronize()
         log("copied 1 GiB 3 times")
         return
-
+    if args.profile == "probe4g":
+        big = torch.empty(4 << 30, dtype=torch.uint8, device="cuda")
+        sink = torch.zeros(4, dtype=torch.int32, device="cuda")
+        for _ in range(12):
+            qg.qg_hbm_read_probe(big, big.numel(), sink, stream)
+        torch.cuda.synchronize()
+        log("ran 12 read probes over 4 GiB")
+        return
+    if args.profile == "valu":
+        for fmt, n, k, b in VALU_ROWS:
+            g = Gemv(torch, qg, fmt, n, k, b, 0, 1, stream)
+            for _ in range(VALU_LAUNCHES):
+                g.step()
+            torch.cuda.synchronize()
+            log(f"valu pass: {fmt} {n}x{k} B={b}")
+            del g
+            torch.cuda.empty_cache()
+        return
     if args.profile == "moe":
         for fmt in ("q4_k", "q2_k"):
             for t_tokens in (1, 8):
-                log(f"moe {moe_layer(torch, qg, stream, fmt, t_tokens)}")
+                log(f"moe {moe_layer(torch, qg, stream, fmt, t_tokens, eager=2)}")
         return
     if args.profile == "norm":
         for n, k in ((14336, 4096), (4096, 4096)):
             for b in (1, 8):
-                for norm in (False, True, "unit"):
+                for norm in (True, "unit"):
                     g = Gemv(torch, qg, "q4_k", n, k, b, 0, COLD_BYTES, stream, norm)
-                    g.capture()
-                    g.replay(2)
-                    t = g.timed_replay(max(2, 400 // len(g.wp)))
-                    log(f"q4_k {n}x{k} B={b} rmsnorm={norm}: {t * 1e6:.2f} us")
+                    for _ in range(len(g.wp)):
+                        g.step()
+                    torch.cuda.synchronize()
+                    log(f"q4_k {n}x{k} B={b} rmsnorm={norm}: {len(g.wp)} launches")
                     del g
                     torch.cuda.empty_cache()
         for t_tokens in (1, 8):
-            log(f"moe block {moe_layer(torch, qg, stream, 'q4_k', t_tokens, norm=True)}")
+            log(f"moe block {moe_layer(torch, qg, stream, 'q4_k', t_tokens, norm=True, eager=2)}")
         return
     if args.profile == "step":
-        log(f"step {dense_step(torch, qg, stream)}")
+        log(f"step {dense_step(torch, qg, stream, variants=('fused',), eager=6)}")
+        return
+    if args.profile == "step-graph":
+        log(f"step {dense_step(torch, qg, stream, variants=('fused',), reps=6)}")
         return
 
     log("setup: Q4_K 14336x4096 batch 1, rotating copies")
@@ -461,35 +809,26 @@ def main():
         torch.cuda.synchronize()
         log("ran 40 headline GEMVs")
         return
-    if args.profile == "probe":
-        sink = torch.zeros(4, dtype=torch.int32, device="cuda")
-        for p in head.wp:
-            qg.qg_hbm_read_probe(p, head.bytes, sink, stream)
-        torch.cuda.synchronize()
-        log(f"ran {len(head.wp)} read probes")
-        return
 
     per = head.capture()
-    reps_warm = max(1, args.warmup // per)
-    reps = max(1, args.steps // per)
-    steps = reps * per
-    head.replay(reps_warm)
+    head.replay(args.warmup)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    head.replay(reps)
+    step_s = replay_times(torch, head.graph, stream, args.steps)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    value = head.bytes * steps / wall / 1e9
-    log(f"headline: {value:.1f} GB/s over {steps} steps ({reps} graph replays of {per} launches)")
-
-    t_launch = head.timed_replay(reps)
-    achieved = head.bytes / t_launch / 1e9
+    launch = spread(step_s / per)
+    step = spread(step_s)
+    value = head.bytes * per / step["median"] / 1e9
+    achieved = head.bytes / launch["median"] / 1e9
+    log(f"headline: {value:.1f} GB/s (median of {args.steps} steps of {per} launches; "
+        f"p10/p90 per launch {launch['p10'] * 1e6:.3f} / {launch['p90'] * 1e6:.3f} us)")
     # traffic: counter-measured HBM bytes per launch over the same launch time,
     # in the unit of `achieved` (so traffic / achieved = measured / algorithmic bytes)
     hbm_bytes = read_traffic()
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4),
-                "traffic": None if hbm_bytes is None else round(hbm_bytes / t_launch / 1e9, 1)}
+                "traffic": None if hbm_bytes is None else round(hbm_bytes / launch["median"] / 1e9, 1)}
 
     # eager launches (host-issued one by one), for reference
     for _ in range(50):
@@ -501,52 +840,74 @@ def main():
     torch.cuda.synchronize()
     eager_us = (time.perf_counter() - t1) / 500 * 1e6
 
-    extra = {"headline_us_per_launch": round(t_launch * 1e6, 3),
+    probe = read_probe(torch, qg, stream, head)
+    log(f"  read probe {probe}")
+    peak_rocprof = read_peak()
+    measured_peak = probe["large_4GiB_GBps"]
+    extra = {"headline_us_per_launch": round(launch["median"] * 1e6, 3),
+             "headline_us_per_launch_p10": round(launch["p10"] * 1e6, 3),
+             "headline_us_per_launch_p90": round(launch["p90"] * 1e6, 3),
+             "headline_launches_timed": per * args.steps,
+             "headline_wall_GBps": round(head.bytes * per * args.steps / wall / 1e9, 1),
              "headline_eager_us_per_launch": round(eager_us, 3),
              "tok_s_equiv": round(achieved * 1e9 / DENSE_8B_BYTES, 1),
              "headline_algorithmic_bytes": head.bytes,
-             "headline_hbm_bytes_counted": hbm_bytes}
+             "headline_hbm_bytes_counted": hbm_bytes,
+             "hbm_read_probe": probe,
+             "hbm_peak_4GiB_rocprof_GBps": peak_rocprof,
+             "frac_of_measured_peak": round(achieved / measured_peak, 4),
+             "frac_of_measured_peak_rocprof": None if peak_rocprof is None else round(achieved / peak_rocprof, 4),
+             "frac_of_same_size_read": round(achieved / probe["same_size_GBps"], 4),
+             "target_frac_of_measured_peak": 0.8,
+             "target_met": bool(achieved / measured_peak >= 0.8),
+             "environment": environment(torch),
+             "page_context": [
+                 "handbook page decode bound (formula, not a measurement): 9 / 19 / 62 / 157 tok/s for an 8B "
+                 "Q4_K model at 60 / 120 / 400 / 1008 GB/s x 70 %",
+                 "low-bit README page: Q2_K matmul 7.8 -> 13.9 G weights/s and a 0.8B all-Q4_K model at 16.8 tok/s "
+                 "on 4x Cortex-A55",
+                 "Flash-MoE page: Metal dequant matvec saturating at ~418 GiB/s and 4.36 tok/s for a 397B MoE "
+                 "(512 experts, top-4 + shared, hidden 4096) on an M3 Max"]}
     if not args.quick:
-        def measure(fmt, n, k, b, rmsnorm=False):
+        valu = read_valu()
+
+        def measure(fmt, n, k, b, rmsnorm=False, reps=None):
             g = Gemv(torch, qg, fmt, n, k, b, 0, COLD_BYTES, stream, rmsnorm)
             g.capture()
             g.replay(2)
-            t = g.timed_replay(max(2, 400 // len(g.wp)))
+            t = spread(g.launch_times(reps or max(4, 600 // len(g.wp))))
             nbytes = g.bytes
             del g
             torch.cuda.empty_cache()
-            return t, nbytes
+            row = {"fmt": fmt, "N": n, "K": k, "B": b, "us": round(t["median"] * 1e6, 2),
+                   "us_p10_p90": [round(t["p10"] * 1e6, 2), round(t["p90"] * 1e6, 2)],
+                   "GBps": round(nbytes / t["median"] / 1e9, 1), "frac_hbm_peak": round(nbytes / t["median"] / 1e12 / 8, 4),
+                   "Gweights_s": round(n * k * b / t["median"] / 1e9, 1)}
+            if not rmsnorm and (fmt, n, k, b) in valu:
+                row["valu_frac"] = round(valu[(fmt, n, k, b)] * 64 / t["median"] / VALU_PEAK_LANE_OPS, 4)
+                row["valu_lane_ops_per_weight"] = round(valu[(fmt, n, k, b)] * 64 / (n * k), 3)
+            return row
 
-        rows = []
-        for fmt in ("q8_0", "q4_0", "q4_1", "q4_k"):
-            for n, k in ((4096, 4096), (14336, 4096)):
-                for b in (1, 8):
-                    t, nbytes = measure(fmt, n, k, b)
-                    rows.append({"fmt": fmt, "N": n, "K": k, "B": b, "us": round(t * 1e6, 2),
-                                 "GBps": round(nbytes / t / 1e9, 1)})
-                    log(f"  {fmt} {n}x{k} B={b}: {t*1e6:.2f} us, {nbytes/t/1e9:.1f} GB/s")
-        extra["four_formats"] = rows
-        rows = []
-        for fmt in ("tern", "bin", "bin8", "q2_k"):
-            for n, k in ((4096, 4096), (12288, 4096), (4096, 12288)):
-                for b in (1, 4):
-                    t, nbytes = measure(fmt, n, k, b)
-                    rows.append({"fmt": fmt, "N": n, "K": k, "B": b, "us": round(t * 1e6, 2),
-                                 "GBps": round(nbytes / t / 1e9, 1), "Gweights_s": round(n * k * b / t / 1e9, 1)})
-                    log(f"  {fmt} {n}x{k} B={b}: {t*1e6:.2f} us, {nbytes/t/1e9:.1f} GB/s")
-        extra["low_bit"] = rows
+        for key, rows_def in (("four_formats", FOUR_FORMATS), ("low_bit", LOW_BIT), ("step_shapes", STEP_SHAPES)):
+            rows = []
+            for fmt, n, k, b in rows_def:
+                rows.append(measure(fmt, n, k, b))
+                log(f"  {key} {rows[-1]}")
+            extra[key] = rows
         rows = []
         for gain in (True, "unit"):
             for n, k in ((14336, 4096), (4096, 4096)):
                 for b in (1, 8):
-                    t, nbytes = measure("q4_k", n, k, b, rmsnorm=gain)
-                    rows.append({"fmt": "q4_k", "N": n, "K": k, "B": b, "gain": "folded" if gain == "unit" else "vector",
-                                 "us": round(t * 1e6, 2), "GBps": round(nbytes / t / 1e9, 1)})
-                    log(f"  rmsnorm ({rows[-1]['gain']} gain) + q4_k {n}x{k} B={b}: {t*1e6:.2f} us, "
-                        f"{nbytes/t/1e9:.1f} GB/s")
+                    row = measure("q4_k", n, k, b, rmsnorm=gain)
+                    row["gain"] = "folded" if gain == "unit" else "vector"
+                    rows.append(row)
+                    log(f"  rmsnorm {row}")
         extra["rmsnorm_gemv"] = rows
+        extra["valu_counters_current"] = bool(valu)
         log("8B decode step (32 layers x 7 Q4_K GEMVs)")
         extra["dense_8b_step"] = dense_step(torch, qg, stream)
+        extra["dense_8b_step"]["fused_frac_of_measured_peak"] = round(
+            extra["dense_8b_step"]["fused_GBps"] / measured_peak, 4)
         log(f"  {extra['dense_8b_step']}")
         rows = []
         for fmt in ("q4_k", "q2_k"):
@@ -558,26 +919,25 @@ def main():
                 rows.append(moe_layer(torch, qg, stream, "q4_k", t_tokens, norm=norm))
                 log(f"  moe {rows[-1]}")
         extra["moe_layer"] = rows
-    extra["hbm_read_probe"] = read_probe(torch, qg, stream, head)
-    extra["headline_frac_of_read_probe"] = round(achieved / extra["hbm_read_probe"]["same_size_GBps"], 4)
-    log(f"  read probe {extra['hbm_read_probe']}")
 
     line = {
         "metric": "Q4_K batch-1 GEMV effective weight GB/s and % of HBM peak; tok/s-equiv",
         "value": round(value, 1),
         "unit": "GB/s",
         "n_gpus": 1,
-        "steps": steps,
-        "warmup": reps_warm * per,
-        "ms_per_step": round(wall / steps * 1e3, 6),
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(step["median"] * 1e3, 6),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "f32",
         "data": "synthetic",
-        "config": {"workload": "Q4_K GEMV 14336x4096, batch 1, Student-t(5)*0.02 weights, N(0,1) x, "
-                               "cold cache (rotating >= 1 GiB of packed copies), HIP-graph launches",
-                   "format": "q4_k", "N": 14336, "K": 4096, "batch": 1, "parallelism": "none"},
+        "config": {"workload": f"Q4_K GEMV 14336x4096, batch 1, Student-t(5)*0.02 weights, N(0,1) x, cold cache; "
+                               f"one step = one HIP-graph replay of {per} launches over {per} distinct packed copies "
+                               f"({head.bytes * per / 2**30:.2f} GiB)",
+                   "format": "q4_k", "N": 14336, "K": 4096, "batch": 1, "launches_per_step": per,
+                   "parallelism": "none"},
         "roofline": roofline,
         "extra": extra,
     }
