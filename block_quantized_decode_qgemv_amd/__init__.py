@@ -25,7 +25,7 @@ __all__ = [
     "qgemv", "qgemv_q8_0", "qgemv_q4_0", "qgemv_q4_1", "qgemv_q4k", "qgemv_q2k",
     "qgemv_tern", "qgemv_bin", "qgemv_bin8", "qgemv_rmsnorm", "qg_dequant", "qquant", "qquant_device", "qrequant_workspace_size", "qrequant",
     "qpack_tern", "qpack_bin", "qpack_bin8",
-    "moe_expert_ffn_workspace_size", "moe_expert_ffn", "moe_expert_ffn_rmsnorm", "qg_strerror", "qg_last_error",
+    "moe_expert_ffn_workspace_size", "moe_expert_ffn_workspace_layout", "moe_expert_ffn", "moe_expert_ffn_rmsnorm", "qg_strerror", "qg_last_error",
     "qg_version", "EXPORTED_SYMBOLS",
 ]
 
@@ -67,6 +67,8 @@ _SIGNATURES = {
     "qpack_bin": (_i32, [_vp, _vp, _i64, _i64, _vp]),
     "qpack_bin8": (_i32, [_vp, _vp, _i64, _i64, _vp]),
     "moe_expert_ffn_workspace_size": (_sz, [_i32, _i32, _i32, _i32, _i32]),
+    "moe_expert_ffn_workspace_layout": (_i32, [_i32, _i32, _i32, _i32, _i32, ctypes.POINTER(_sz),
+                                               ctypes.POINTER(_sz)]),
     "moe_expert_ffn": (_i32, [_i32, _vp, _vp, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _i32, _u32,
                               _vp, _vp, _sz, _vp]),
     "moe_expert_ffn_rmsnorm": (_i32, [_i32, _vp, _vp, _i32, _i32, _i32, _i32, _vp, _vp, ctypes.c_float, _vp, _vp,
@@ -207,6 +209,15 @@ def qgemv_workspace_size(fmt, n: int, k: int, b: int = 1) -> int:
 
 def moe_expert_ffn_workspace_size(t: int, e: int, h: int, i: int, top_k: int) -> int:
     return load().moe_expert_ffn_workspace_size(t, e, h, i, top_k)
+
+
+def moe_expert_ffn_workspace_layout(t: int, e: int, h: int, i: int, top_k: int) -> tuple[int, int]:
+    """(hsel byte offset, h byte offset) of a finished MoE call's workspace
+    (see moe_expert_ffn_workspace_layout in qgemv.h)."""
+    hs, ho = _sz(0), _sz(0)
+    _check(load().moe_expert_ffn_workspace_layout(t, e, h, i, top_k, ctypes.byref(hs), ctypes.byref(ho)),
+           "moe_expert_ffn_workspace_layout")
+    return hs.value, ho.value
 
 
 def qg_hbm_read_probe(buf, nbytes: int, sink, stream=None) -> None:

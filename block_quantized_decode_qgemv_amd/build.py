@@ -41,7 +41,18 @@ def _run(cmd, verbose):
     subprocess.run(cmd, check=True)
 
 
-def build(verbose: bool = True) -> str:
+def _stale(obj, src) -> bool:
+    """Whether obj is older than src or any header of the library."""
+    if not os.path.exists(obj):
+        return True
+    headers = [os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".h")]
+    headers.append(os.path.join(INCLUDE, "qgemv.h"))
+    return os.path.getmtime(obj) < max(os.path.getmtime(p) for p in [src] + headers)
+
+
+def build(verbose: bool = True, incremental: bool = False) -> str:
+    """Compile every source (or, incremental, only those whose object is older
+    than the source or a header) and link libqgemv.so."""
     os.makedirs(BUILD_DIR, exist_ok=True)
     jobs = []  # (command, object); the sources compile concurrently
     for src in DEVICE_SOURCES:
@@ -50,8 +61,9 @@ def build(verbose: bool = True) -> str:
     for src in HOST_SOURCES:
         obj = os.path.join(BUILD_DIR, src + ".o")
         jobs.append((["g++", *HOST_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj], obj))
-    with ThreadPoolExecutor(max_workers=min(len(jobs), 8)) as pool:
-        for f in [pool.submit(_run, cmd, verbose) for cmd, _ in jobs]:
+    todo = [(cmd, obj) for cmd, obj in jobs if not incremental or _stale(obj, cmd[-3])]
+    with ThreadPoolExecutor(max_workers=max(1, min(len(todo), 8))) as pool:
+        for f in [pool.submit(_run, cmd, verbose) for cmd, _ in todo]:
             f.result()
     tmp = LIB + ".tmp"
     _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *[o for _, o in jobs], "-o", tmp, "-lpthread"],
@@ -61,4 +73,4 @@ def build(verbose: bool = True) -> str:
 
 
 if __name__ == "__main__":
-    build(verbose="-q" not in sys.argv)
+    build(verbose="-q" not in sys.argv, incremental="--incremental" in sys.argv)

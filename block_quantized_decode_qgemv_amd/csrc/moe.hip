@@ -429,17 +429,28 @@ size_t moe_expert_ffn_workspace_size(int T, int E, int H, int I, int top_k) {
     return MoeLayout(T, H, I, top_k).total;
 }
 
+int moe_expert_ffn_workspace_layout(int T, int E, int H, int I, int top_k, size_t* hsel_offset, size_t* h_offset) {
+    clear_error();
+    if (!hsel_offset || !h_offset) return fail(QG_EINVAL, "null offset pointer");
+    if (moe_expert_ffn_workspace_size(T, E, H, I, top_k) == 0)
+        return fail(QG_ERANGE, "T=%d E=%d H=%d I=%d top_k=%d is not a valid layer", T, E, H, I, top_k);
+    const MoeLayout L(T, H, I, top_k);
+    *hsel_offset = L.hsel;
+    *h_offset = L.h;
+    return QG_OK;
+}
+
 }  // extern "C"
 
 namespace {
 
-// Host validation shared by both MoE entry points (QG_OK or the error set).
-int check_moe_args(int fmt, const void* w_gate_up, const void* w_down, int E, int H, int I, int top_k,
-                   const float* x, const float* residual, const float* router_logits,
-                   const float* shared_gate_logit, int T, unsigned flags, float* out, void* workspace,
-                   size_t ws_bytes) {
+// Host validation shared by the MoE entry points (QG_OK or the error set):
+// the layer's shape and its caller buffers, then the workspace.
+int check_moe_layer(int fmt, const void* w_gate_up, const void* w_down, int E, int H, int I, int top_k,
+                    const float* x, const float* residual, const float* router_logits,
+                    const float* shared_gate_logit, int T, unsigned flags, float* out) {
     if (fmt != QG_Q4_K && fmt != QG_Q2_K) return fail(QG_EINVAL, "moe_expert_ffn takes Q4_K or Q2_K experts");
-    if (!w_gate_up || !w_down || !x || !residual || !router_logits || !shared_gate_logit || !out || !workspace)
+    if (!w_gate_up || !w_down || !x || !residual || !router_logits || !shared_gate_logit || !out)
         return fail(QG_EINVAL, "null pointer");
     if (T < 1 || T > kMaxT) return fail(QG_ERANGE, "T=%d must be in [1, %d]", T, kMaxT);
     if (E < 1 || E > kMaxE) return fail(QG_ERANGE, "E=%d must be in [1, %d]", E, kMaxE);
@@ -448,20 +459,40 @@ int check_moe_args(int fmt, const void* w_gate_up, const void* w_down, int E, in
     if (H < 256 || H % 256 || I < 256 || I % 256 || H > (1 << 26) || I > (1 << 26))
         return fail(QG_ESHAPE, "H=%d and I=%d must be multiples of 256 in [256, 2^26]", H, I);
     if (flags & ~QG_MOE_RENORM) return fail(QG_EINVAL, "unknown flags 0x%x", flags);
-    if (!aligned(w_gate_up, 16) || !aligned(w_down, 16) || !aligned(x, 16) || !aligned(workspace, 16))
-        return fail(QG_EALIGN, "weights, x and workspace must be 16-byte aligned");
+    if (!aligned(w_gate_up, 16) || !aligned(w_down, 16) || !aligned(x, 16))
+        return fail(QG_EALIGN, "weights and x must be 16-byte aligned");
     if (!aligned(residual, 4) || !aligned(router_logits, 4) || !aligned(shared_gate_logit, 4) || !aligned(out, 4))
         return fail(QG_EALIGN, "residual, logits and out must be 4-byte aligned");
-    const size_t need = MoeLayout(T, H, I, top_k).total;
-    if (ws_bytes < need) return fail(QG_ERANGE, "workspace of %zu bytes is below the %zu needed", ws_bytes, need);
     const size_t act = (size_t)T * H * 4;
     if (overlap(out, act, x, act) || overlap(out, act, residual, act))
         return fail(QG_EINVAL, "out must not overlap x or residual");
+    return QG_OK;
+}
+
+int check_moe_workspace(int E, int H, int I, int top_k, const float* x, const float* residual,
+                        const float* router_logits, const float* shared_gate_logit, int T, float* out,
+                        void* workspace, size_t ws_bytes) {
+    if (!workspace) return fail(QG_EINVAL, "null workspace");
+    if (!aligned(workspace, 16)) return fail(QG_EALIGN, "the workspace must be 16-byte aligned");
+    const size_t need = MoeLayout(T, H, I, top_k).total;
+    if (ws_bytes < need) return fail(QG_ERANGE, "workspace of %zu bytes is below the %zu needed", ws_bytes, need);
+    const size_t act = (size_t)T * H * 4;
     if (overlap(workspace, need, x, act) || overlap(workspace, need, residual, act) ||
         overlap(workspace, need, out, act) || overlap(workspace, need, router_logits, (size_t)T * E * 4) ||
         overlap(workspace, need, shared_gate_logit, (size_t)T * 4))
         return fail(QG_EINVAL, "workspace must not overlap the inputs or out");
     return QG_OK;
+}
+
+int check_moe_args(int fmt, const void* w_gate_up, const void* w_down, int E, int H, int I, int top_k,
+                   const float* x, const float* residual, const float* router_logits,
+                   const float* shared_gate_logit, int T, unsigned flags, float* out, void* workspace,
+                   size_t ws_bytes) {
+    const int rc = check_moe_layer(fmt, w_gate_up, w_down, E, H, I, top_k, x, residual, router_logits,
+                                   shared_gate_logit, T, flags, out);
+    if (rc) return rc;
+    return check_moe_workspace(E, H, I, top_k, x, residual, router_logits, shared_gate_logit, T, out, workspace,
+                               ws_bytes);
 }
 
 // NORM: 0 plain, 1 RMS norm with a gain vector, 2 RMS norm with unit gain

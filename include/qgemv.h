@@ -276,6 +276,23 @@ int qpack_bin8(const uint8_t* bits, const uint16_t* scale_f16, int64_t N, int64_
  *   float atomics).
  * Errors: QG_EINVAL, QG_ESHAPE, QG_ERANGE, QG_EALIGN, QG_EHIP. */
 size_t moe_expert_ffn_workspace_size(int T, int E, int H, int I, int top_k);
+
+/* Where a finished moe_expert_ffn (or moe_expert_ffn_rmsnorm) call leaves its
+ * intermediate results in the workspace, for stage-wise checks (EPM README,
+ * section "正確性": the SwiGLU intermediate of one implementation fed into the
+ * other's down projection localises a difference).  For the same
+ * (T, E, H, I, top_k), once the call's stream work has completed:
+ *   int32 hsel[T][top_k + 1] at byte *hsel_offset: hsel[t][k] is the h row of
+ *     token t's slot k (slots 0..top_k-1: the routed experts in descending
+ *     weight; slot top_k: the shared expert);
+ *   fp32 h[rows][I] at byte *h_offset: row r holds silu(W_gate x_t) *
+ *     (W_up x_t) of the expert and token that r was assigned to.
+ * hsel_offset and h_offset are HOST pointers receiving the byte offsets.
+ * The contents are scratch: valid only until the workspace is used again.
+ * Returns QG_OK, or QG_ERANGE / QG_EINVAL for arguments that
+ * moe_expert_ffn_workspace_size rejects (it returns 0 for them). */
+int moe_expert_ffn_workspace_layout(int T, int E, int H, int I, int top_k, size_t* hsel_offset, size_t* h_offset);
+
 int moe_expert_ffn(int fmt, const void* w_gate_up, const void* w_down, int E, int H, int I, int top_k,
                    const float* x, const float* residual, const float* router_logits,
                    const float* shared_gate_logit, int T, unsigned flags, float* out,

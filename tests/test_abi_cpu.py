@@ -323,3 +323,15 @@ def test_packers_check_scale_shape(packer, codes):
         fn(codes.reshape(-1), good)
     with pytest.raises(ValueError, match="multiple of 128"):
         fn(np.zeros((3, 200), codes.dtype), good)
+
+
+def test_moe_workspace_layout_offsets():
+    for t, e, h, i, k in ((1, 512, 4096, 1024, 4), (8, 512, 4096, 1024, 4), (3, 16, 512, 256, 2)):
+        size = qg.moe_expert_ffn_workspace_size(t, e, h, i, k)
+        hs, ho = qg.moe_expert_ffn_workspace_layout(t, e, h, i, k)
+        rows = t * k + (t + 1) // 2  # routed (token, slot) pairs plus the shared expert's items, two rows each
+        assert hs % 16 == 0 and ho % 16 == 0
+        assert hs + 4 * t * (k + 1) <= ho
+        assert ho + 4 * 2 * rows * i <= size
+    with pytest.raises(qg.QGError):
+        qg.moe_expert_ffn_workspace_layout(9, 16, 512, 256, 2)

@@ -121,6 +121,57 @@ def test_moe_small(fmt, t, renorm):
     check(out, layer, x, residual, logits, s, top_k, renorm, f"{fmt} T={t} renorm={renorm}")
 
 
+def workspace_stages(ws, t, e, h, i, top_k):
+    """(hsel [T][K+1] int32, h rows as a function of (t, k)) read back from a
+    finished call's workspace at the offsets the library reports."""
+    hs_off, h_off = qg.moe_expert_ffn_workspace_layout(t, e, h, i, top_k)
+    raw = ws.cpu().numpy()
+    hsel = raw[hs_off:hs_off + 4 * t * (top_k + 1)].view(np.int32).reshape(t, top_k + 1).copy()
+    rows = raw[h_off:h_off + (raw.size - h_off) // 4 * 4].view(np.float32)
+    return hsel, (lambda tt, k: rows[hsel[tt, k] * i:(hsel[tt, k] + 1) * i].astype(np.float64))
+
+
+@pytest.mark.parametrize("fmt", KFORMATS)
+@pytest.mark.parametrize("t", [1, 3, 8])
+def test_moe_stagewise_h_then_teacher_forced_down(fmt, t):
+    """Stage-wise check (EPM README, section "正確性"): the SwiGLU intermediate
+    h of every (token, slot) is read from the workspace and checked on its own
+    against the oracle within the gate/up bound; then the GPU's h is fed to the
+    oracle's down projection and combine (teacher forcing), and the GPU's
+    output must match that within the down + combine bound alone."""
+    e, h, i, top_k = 16, 512, 256, 4
+    layer, gu, dn = small_layer(fmt, e, h, i, seed=21)
+    x, residual, logits, s = inputs(t, e, h, seed=300 + t)
+    assert np.all(OM.route_margin(logits, top_k) > 1e-6), "near-tied route; change the seed"
+    ws_bytes = qg.moe_expert_ffn_workspace_size(t, e, h, i, top_k)
+    ws = torch.zeros(ws_bytes, dtype=torch.uint8, device="cuda")
+    out = torch.full((t, h), float("nan"), device="cuda")
+    qg.moe_expert_ffn(fmt, gu, dn, e, h, i, top_k, dev(x), dev(residual), dev(logits), dev(s), t, out, ws,
+                      ws_bytes)
+    torch.cuda.synchronize()
+    out = out.cpu().numpy().astype(np.float64)
+    hsel, h_row = workspace_stages(ws, t, e, h, i, top_k)
+    assert len(set(hsel.ravel().tolist())) == t * (top_k + 1), "every (token, slot) has its own h row"
+    wg, wu, wd = layer.view("gate"), layer.view("up"), layer.view("down")
+    ref = OM.moe_ref(wg, wu, wd, x, residual, logits, s, top_k)
+    for tt in range(t):
+        slots = list(ref["ids"][tt]) + [e]
+        coef = list(ref["weights"][tt]) + [float(ref["sigma"][tt])]
+        out_tf = residual[tt].astype(np.float64).copy()
+        tol = OM.COMBINE_REL * np.abs(residual[tt].astype(np.float64))
+        for k, ex in enumerate(slots):
+            hg = h_row(tt, k)
+            dh = OM.h_tolerance(wg[ex], wu[ex], x[tt:tt + 1])[0]
+            err = np.abs(hg - ref["h"][tt, k])
+            assert np.all(err <= dh), f"h of token {tt} slot {k}: |err|/tol = {np.max(err / dh):.3g}"
+            d64 = np.asarray(wd[ex], np.float32).astype(np.float64)
+            o_tf = d64 @ hg
+            out_tf += coef[k] * o_tf
+            tol += coef[k] * OM.o_tolerance(wd[ex], hg[None], np.zeros((1, i)))[0] + OM.COMBINE_REL * coef[k] * np.abs(o_tf)
+        err = np.abs(out[tt] - out_tf)
+        assert np.all(err <= tol), f"teacher-forced token {tt}: |err|/tol = {np.max(err / tol):.3g}"
+
+
 @pytest.mark.parametrize("fmt", KFORMATS)
 @pytest.mark.parametrize("e,top_k,t", [(4, 4, 5), (9, 1, 8), (12, 8, 7), (1, 1, 3)])
 def test_moe_topk_edges(fmt, e, top_k, t):
