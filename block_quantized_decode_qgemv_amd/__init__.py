@@ -20,15 +20,16 @@ import threading
 import numpy as np
 
 __all__ = [
-    "FORMATS", "QG_MOE_RENORM", "QGError", "QGLibraryMissing", "lib_path", "load",
+    "FORMATS", "QG_MOE_RENORM", "QG_MOE_NOALLOC_SCRATCH_BYTES", "QGError", "QGLibraryMissing", "lib_path", "load",
     "qg_packed_size", "qg_codes_plane_size", "qg_codes_plane_offset", "qg_block_size", "qgemv_workspace_size",
     "qgemv", "qgemv_q8_0", "qgemv_q4_0", "qgemv_q4_1", "qgemv_q4k", "qgemv_q2k",
     "qgemv_tern", "qgemv_bin", "qgemv_bin8", "qgemv_rmsnorm", "qg_dequant", "qquant", "qquant_device", "qrequant_workspace_size", "qrequant",
     "qpack_tern", "qpack_bin", "qpack_bin8",
-    "moe_expert_ffn_workspace_size", "moe_expert_ffn_workspace_layout", "moe_expert_ffn", "moe_expert_ffn_rmsnorm", "qg_strerror", "qg_last_error",
+    "moe_expert_ffn_workspace_size", "moe_expert_ffn_workspace_layout", "moe_expert_ffn", "moe_expert_ffn_noalloc", "moe_expert_ffn_rmsnorm", "qg_strerror", "qg_last_error",
     "qg_version", "EXPORTED_SYMBOLS",
 ]
 
+QG_MOE_NOALLOC_SCRATCH_BYTES = 2 << 20  # the no-allocation MoE entry point's device scratch (qgemv.h)
 FORMATS = {"q8_0": 0, "q4_0": 1, "q4_1": 2, "q4_k": 3, "q2_k": 4, "tern": 5, "bin": 6, "bin8": 7}
 QG_MOE_RENORM = 1
 
@@ -71,6 +72,8 @@ _SIGNATURES = {
                                                ctypes.POINTER(_sz)]),
     "moe_expert_ffn": (_i32, [_i32, _vp, _vp, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _i32, _u32,
                               _vp, _vp, _sz, _vp]),
+    "moe_expert_ffn_noalloc": (_i32, [_i32, _vp, _vp, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _i32, _u32,
+                                      _vp, _vp]),
     "moe_expert_ffn_rmsnorm": (_i32, [_i32, _vp, _vp, _i32, _i32, _i32, _i32, _vp, _vp, ctypes.c_float, _vp, _vp,
                                       _vp, _i32, _u32, _vp, _vp, _sz, _vp]),
     "qg_hbm_read_probe": (_i32, [_vp, _sz, _vp, _vp]),
@@ -398,6 +401,20 @@ def moe_expert_ffn(fmt, w_gate_up, w_down, e: int, h: int, i: int, top_k: int, x
                                _dev(out, f32, "out", act), _ws(workspace, ws_bytes, "workspace"), ws_bytes,
                                _stream(stream))
     _check(rc, "moe_expert_ffn")
+
+
+def moe_expert_ffn_noalloc(fmt, w_gate_up, w_down, e: int, h: int, i: int, top_k: int, x, residual,
+                           router_logits, shared_gate_logit, t: int, out, flags: int = 0, stream=None) -> None:
+    """Routed expert layer with the library's own device scratch as its
+    workspace: no allocation (see moe_expert_ffn_noalloc in qgemv.h)."""
+    f32, u8 = _torch_dtypes()
+    f, gu, dn, act, lg, sl = _moe_sizes(fmt, e, h, i, t)
+    rc = load().moe_expert_ffn_noalloc(f, _dev(w_gate_up, u8, "w_gate_up", gu), _dev(w_down, u8, "w_down", dn),
+                                       e, h, i, top_k, _dev(x, f32, "x", act), _dev(residual, f32, "residual", act),
+                                       _dev(router_logits, f32, "router_logits", lg),
+                                       _dev(shared_gate_logit, f32, "shared_gate_logit", sl), t, flags,
+                                       _dev(out, f32, "out", act), _stream(stream))
+    _check(rc, "moe_expert_ffn_noalloc")
 
 
 def moe_expert_ffn_rmsnorm(fmt, w_gate_up, w_down, e: int, h: int, i: int, top_k: int, x, gamma, eps: float,

@@ -25,9 +25,16 @@
 
 #include <cmath>
 #include <cstdint>
+#include <mutex>
 
 #include "gemv_core.h"
 #include "internal.h"
+
+// Workspace of moe_expert_ffn_noalloc (callers that cannot allocate): a
+// stated maximum, held by every device the library runs on until the
+// process ends.
+constexpr size_t kNoAllocScratchBytes = (size_t)2 << 20;
+static __device__ __align__(256) uint8_t scratch[kNoAllocScratchBytes];
 
 namespace qg {
 namespace {
@@ -414,6 +421,37 @@ hipError_t launch_moe(const uint8_t* wgu, const uint8_t* wdn, int E, int H, int 
     }
 }
 
+// ------------------------------------------- no-allocation workspace
+//
+// moe_expert_ffn_noalloc takes its workspace from the file-scope device array
+// `scratch` (top of this file) instead of a caller buffer.  In host code that
+// name is a host-side stand-in, not device memory: host code uses only the
+// address hipGetSymbolAddress returns for the current device (each device
+// holds its own copy of the array at its own address), resolved once per
+// device.
+constexpr int kMaxDevices = 64;
+std::mutex scratch_mu;
+void* scratch_ptr[kMaxDevices];  // per device; guarded by scratch_mu
+
+// The current device's scratch address, resolving it on the first call on
+// that device; QG_OK or QG_EHIP with the detail recorded.
+int scratch_address(void** out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(QG_EHIP, "hipGetDevice failed: %s", hipGetErrorString(e));
+    if (dev < 0 || dev >= kMaxDevices) return fail(QG_EUNSUPPORTED, "device %d beyond the %d supported", dev, kMaxDevices);
+    std::lock_guard<std::mutex> lock(scratch_mu);
+    if (!scratch_ptr[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p)
+            return fail(QG_EHIP, "hipGetSymbolAddress of the MoE scratch failed: %s", hipGetErrorString(e));
+        scratch_ptr[dev] = p;
+    }
+    *out = scratch_ptr[dev];
+    return QG_OK;
+}
+
 }  // namespace
 }  // namespace qg
 
@@ -527,6 +565,29 @@ int moe_expert_ffn(int fmt, const void* w_gate_up, const void* w_down, int E, in
     if (rc) return rc;
     return moe_call<0>(fmt, w_gate_up, w_down, E, H, I, top_k, x, nullptr, 0.0f, residual, router_logits,
                            shared_gate_logit, T, flags, out, workspace, stream);
+}
+
+int moe_expert_ffn_noalloc(int fmt, const void* w_gate_up, const void* w_down, int E, int H, int I, int top_k,
+                           const float* x, const float* residual, const float* router_logits,
+                           const float* shared_gate_logit, int T, unsigned flags, float* out, void* stream) {
+    clear_error();
+    int rc = check_moe_layer(fmt, w_gate_up, w_down, E, H, I, top_k, x, residual, router_logits, shared_gate_logit,
+                             T, flags, out);
+    if (rc) return rc;
+    const size_t need = MoeLayout(T, H, I, top_k).total;
+    if (need > kNoAllocScratchBytes)
+        return fail(QG_ERANGE, "the layer needs %zu bytes of workspace, above the %zu of the no-allocation scratch",
+                    need, kNoAllocScratchBytes);
+    void* ws = nullptr;
+    rc = scratch_address(&ws);
+    if (rc) return rc;
+    rc = check_moe_workspace(E, H, I, top_k, x, residual, router_logits, shared_gate_logit, T, out, ws,
+                             kNoAllocScratchBytes);
+    if (rc) return rc;
+    // every workspace word a kernel reads is written earlier in the same call
+    // (routing records, h rows), so the scratch needs no clearing
+    return moe_call<0>(fmt, w_gate_up, w_down, E, H, I, top_k, x, nullptr, 0.0f, residual, router_logits,
+                       shared_gate_logit, T, flags, out, ws, stream);
 }
 
 int moe_expert_ffn_rmsnorm(int fmt, const void* w_gate_up, const void* w_down, int E, int H, int I, int top_k,

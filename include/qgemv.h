@@ -298,6 +298,21 @@ int moe_expert_ffn(int fmt, const void* w_gate_up, const void* w_down, int E, in
                    const float* shared_gate_logit, int T, unsigned flags, float* out,
                    void* workspace, size_t ws_bytes, void* stream);
 
+/* The same layer for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * it takes no workspace argument and allocates nothing.  Its workspace is a
+ * library-owned device array of QG_MOE_NOALLOC_SCRATCH_BYTES (2 MiB) per
+ * device, held until the process ends; a layer whose
+ * moe_expert_ffn_workspace_size exceeds that returns QG_ERANGE.  Every call
+ * on one device shares that device's array, so calls that overlap on one
+ * device (concurrent streams, or host threads) race and must be serialised
+ * by the caller.  Every other argument, the result and the errors are those
+ * of moe_expert_ffn (bit-identical output). */
+#define QG_MOE_NOALLOC_SCRATCH_BYTES ((size_t)2 << 20)
+int moe_expert_ffn_noalloc(int fmt, const void* w_gate_up, const void* w_down, int E, int H, int I, int top_k,
+                           const float* x, const float* residual, const float* router_logits,
+                           const float* shared_gate_logit, int T, unsigned flags, float* out, void* stream);
+
 /* The same layer fed through an RMS norm: every expert (routed and shared)
  * sees xhat[t][k] = x[t][k] * gamma[k] / sqrt(mean_k x[t][k]^2 + eps)
  * instead of x, the norm folded into the gate/up GEMVs as in qgemv_rmsnorm

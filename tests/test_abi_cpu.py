@@ -335,3 +335,20 @@ def test_moe_workspace_layout_offsets():
         assert ho + 4 * 2 * rows * i <= size
     with pytest.raises(qg.QGError):
         qg.moe_expert_ffn_workspace_layout(9, 16, 512, 256, 2)
+
+
+@nogpu
+def test_moe_noalloc_validation():
+    lib = qg.load()
+    big = 1 << 24
+
+    def call(fmt=3, e=16, h=512, i=256, k=4, t=2, x=P + big, out=P + 5 * big):
+        return lib.moe_expert_ffn_noalloc(fmt, P, P, e, h, i, k, x, P + 2 * big, P + 3 * big, P + 4 * big, t, 0,
+                                          out, None)
+
+    assert call(fmt=0) == -1
+    assert call(t=9) == -4
+    assert call(h=300) == -2
+    assert call(x=P + 5 * big - 64) == -1      # x overlaps out
+    assert call(i=4096, k=8, t=8) == -4        # the layer's workspace exceeds the scratch
+    assert qg.qg_last_error()
