@@ -9,6 +9,7 @@ the order written, no contraction).  The library lands next to this file.
 from __future__ import annotations
 
 import os
+import re
 import subprocess
 import sys
 from concurrent.futures import ThreadPoolExecutor
@@ -41,13 +42,28 @@ def _run(cmd, verbose):
     subprocess.run(cmd, check=True)
 
 
+def _includes(path, seen=None) -> set:
+    """The library headers `path` includes, directly or through other headers."""
+    seen = set() if seen is None else seen
+    with open(path, encoding="utf-8") as fh:
+        for line in fh:
+            m = re.match(r'\s*#include\s+"([^"]+)"', line)
+            if not m:
+                continue
+            for base in (CSRC, INCLUDE):
+                dep = os.path.join(base, m.group(1))
+                if os.path.exists(dep) and dep not in seen:
+                    seen.add(dep)
+                    _includes(dep, seen)
+                    break
+    return seen
+
+
 def _stale(obj, src) -> bool:
-    """Whether obj is older than src or any header of the library."""
+    """Whether obj is older than src or a header it includes."""
     if not os.path.exists(obj):
         return True
-    headers = [os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".h")]
-    headers.append(os.path.join(INCLUDE, "qgemv.h"))
-    return os.path.getmtime(obj) < max(os.path.getmtime(p) for p in [src] + headers)
+    return os.path.getmtime(obj) < max(os.path.getmtime(p) for p in [src, *_includes(src)])
 
 
 def build(verbose: bool = True, incremental: bool = False) -> str:
