@@ -8,6 +8,14 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 
+# QG_TEST_LIB: run the tests against another build of the library (the
+# sanitized host build of tests/test_sanitize_cpu.py); unset, the in-tree one.
+if os.environ.get("QG_TEST_LIB"):
+    import block_quantized_decode_qgemv_amd as _qg
+
+    _qg.lib_path = lambda: os.environ["QG_TEST_LIB"]
+
+
 def pytest_configure(config):
     config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU and the built HIP library")
     config.addinivalue_line("markers", "slow: long-running CPU test")

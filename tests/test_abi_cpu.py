@@ -199,6 +199,7 @@ def test_binding_rejects_host_tensors():
 def test_library_missing_is_loud(tmp_path, monkeypatch):
     monkeypatch.setattr(qg, "_lib", None)
     monkeypatch.setattr(qg, "_HERE", str(tmp_path))
+    monkeypatch.setattr(qg, "lib_path", lambda: os.path.join(str(tmp_path), "libqgemv.so"))
     with pytest.raises(qg.QGLibraryMissing):
         qg.load()
 
