@@ -60,6 +60,9 @@ FOUR_FORMATS = [(fmt, n, k, b) for fmt in ("q8_0", "q4_0", "q4_1", "q4_k")
                 for n, k in ((4096, 4096), (14336, 4096)) for b in (1, 8)]
 LOW_BIT = [(fmt, n, k, b) for fmt in ("tern", "bin", "bin8", "q2_k")
            for n, k in ((4096, 4096), (12288, 4096), (4096, 12288)) for b in (1, 4)]
+# row-starved shapes at batch 3-8, with the split-K workspace and without
+SPLIT_K = [("q4_k", 1024, 4096, b) for b in (3, 5, 8)] + [(f, 1024, 4096, 8) for f in ("q8_0", "q2_k", "tern")] + \
+    [("q4_k", 2048, 4096, 8), ("q4_k", 1024, 14336, 8)]
 # the 8B step's Q4_K shapes at batch 1, fused (qkv 6144, gate/up 28672) and not
 STEP_SHAPES = [("q4_k", n, k, 1) for n, k in ((1024, 4096), (4096, 4096), (6144, 4096), (14336, 4096),
                                                (28672, 4096), (4096, 14336))]
@@ -191,7 +194,7 @@ class Gemv:
     Launches go straight to the C ABI with precomputed device pointers; timed
     runs replay a HIP graph holding one launch per copy."""
 
-    def __init__(self, torch, qg, fmt, n, k, b, seed, min_bytes, stream, rmsnorm=False):
+    def __init__(self, torch, qg, fmt, n, k, b, seed, min_bytes, stream, rmsnorm=False, use_ws=True):
         import workloads
 
         self.torch = torch
@@ -213,7 +216,7 @@ class Gemv:
         self.fid = qg.FORMATS[fmt]
         self.wp = [t.data_ptr() for t in self.w]
         self.xp, self.yp = self.x.data_ptr(), self.y.data_ptr()
-        self.ws_bytes = qg.qgemv_workspace_size(fmt, n, k, b)
+        self.ws_bytes = qg.qgemv_workspace_size(fmt, n, k, b) if use_ws else 0
         self.ws = torch.empty(max(self.ws_bytes, 16), dtype=torch.uint8, device="cuda")
         self.wsp = self.ws.data_ptr() if self.ws_bytes else None
         # rmsnorm: the same GEMV fed by RMS norm of x (gain gamma, eps 1e-5);
@@ -700,6 +703,45 @@ def summarize(kind, paths, commands):
                   f"gaps_us_median: {np.median(rows[:, 2]) / 1e3:.1f}",
                   f"gap_per_launch_us: {np.median(rows[:, 2]) / 1e3 / (per_step - 1):.2f}"]
         out = os.path.join(PROFILES, "dense_8b_step_gaps.txt")
+    elif kind == "headline":
+        # paths: FETCH_SIZE and WRITE_SIZE CSVs of `--profile gemv`, then the copy FETCH and WRITE CSVs
+        fetch = [v for _, _, _, v in _counter_per_dispatch(paths[0], "gemv_dpp_kernel", "FETCH_SIZE")]
+        write = [v for _, _, _, v in _counter_per_dispatch(paths[1], "gemv_dpp_kernel", "WRITE_SIZE")]
+        copy_f, copy_w = _copy_kib(paths[2]), _copy_kib(paths[3])
+        fs, ws = (1 << 30) / 1024 / copy_f, (1 << 30) / 1024 / copy_w
+        algo = 33_030_144
+        hbm = float(np.mean(fetch)) * 1024 * fs + float(np.mean(write)) * 1024 * ws
+        lines = _header("HBM traffic of the headline kernel (Q4_K GEMV 14336x4096, batch 1) from rocprofv3 counters",
+                        commands)
+        lines += ["# the copy passes calibrate the counters on a 1 GiB device-to-device copy",
+                  f"fetch_kib_per_dispatch: {np.mean(fetch):.1f}  (mean of {len(fetch)} dispatches)",
+                  f"write_kib_per_dispatch: {np.mean(write):.1f}  (mean of {len(write)} dispatches)",
+                  f"copy_1gib_fetch_kib: {copy_f:.1f}", f"copy_1gib_write_kib: {copy_w:.1f}",
+                  f"fetch_scale: {fs:.4f}", f"write_scale: {ws:.4f}",
+                  f"algorithmic_bytes_per_launch: {algo}", f"hbm_bytes_per_launch: {hbm:.0f}",
+                  f"traffic_over_algorithmic: {hbm / algo:.4f}"]
+        out = COUNTERS_FILE
+    elif kind == "headline-trace":
+        # paths: kernel-trace CSV of `--quick --no-cpu` (the headline's timed replays and the read probes)
+        tr = _csv_rows(paths[0])
+        per = {}
+        for r in tr:
+            name = r["Kernel_Name"]
+            per.setdefault(name, []).append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+        total = sum(sum(v) for v in per.values())
+        lines = ["# rocprofv3 kernel trace: Q4_K GEMV 14336x4096, batch 1 (the bench's headline kernel)",
+                 "# commands (from the repository root as $REPO):"] + [f"#   {c}" for c in commands]
+        lines += [f"# {key}: {source_hash(path)}" for key, path in KERNEL_SOURCES.items()]
+        lines += ["# top kernels (durations in microseconds):", "# name | calls | total_us | average_us | percent"]
+        for name, v in sorted(per.items(), key=lambda kv: -sum(kv[1]))[:6]:
+            lines.append(f"{name} | {len(v)} | {sum(v) / 1e3:.1f} | {np.mean(v) / 1e3:.3f} | {100 * sum(v) / total:.2f}")
+        head = max((v for n, v in per.items() if "gemv_dpp_kernel<3, 1," in n), key=len)
+        lines += ["", f"headline kernel dispatches: {len(head)}",
+                  f"headline kernel average_ns: {np.mean(head):.0f}",
+                  f"headline kernel median_ns: {np.median(head):.0f}",
+                  "algorithmic bytes per launch: 33030144",
+                  f"algorithmic GB/s at the average: {33030144 / np.mean(head):.1f}"]
+        out = os.path.join(PROFILES, "q4k_gemv_14336x4096_kernel_trace.txt")
     else:
         raise SystemExit(f"unknown summary kind {kind}")
     with open(out, "w", encoding="utf-8") as fh:
@@ -724,7 +766,7 @@ def main():
                          "block step")
     ap.add_argument("--summarize", nargs="+", metavar=("KIND", "CSV"), default=None,
                     help="write a profiles/ summary from rocprofv3 CSVs (kinds: valu, peak, moe, step, norm, "
-                         "step-trace)")
+                         "step-trace, headline, headline-trace)")
     ap.add_argument("--command", action="append", default=[], help="command line recorded in a summary")
     args = ap.parse_args()
     if args.summarize:
@@ -871,18 +913,20 @@ def main():
     if not args.quick:
         valu = read_valu()
 
-        def measure(fmt, n, k, b, rmsnorm=False, reps=None):
-            g = Gemv(torch, qg, fmt, n, k, b, 0, COLD_BYTES, stream, rmsnorm)
+        def measure(fmt, n, k, b, rmsnorm=False, reps=None, use_ws=True):
+            g = Gemv(torch, qg, fmt, n, k, b, 0, COLD_BYTES, stream, rmsnorm, use_ws)
             g.capture()
             g.replay(2)
             t = spread(g.launch_times(reps or max(4, 600 // len(g.wp))))
-            nbytes = g.bytes
+            nbytes, g_ws = g.bytes, g.ws_bytes
             del g
             torch.cuda.empty_cache()
             row = {"fmt": fmt, "N": n, "K": k, "B": b, "us": round(t["median"] * 1e6, 2),
                    "us_p10_p90": [round(t["p10"] * 1e6, 2), round(t["p90"] * 1e6, 2)],
                    "GBps": round(nbytes / t["median"] / 1e9, 1), "frac_hbm_peak": round(nbytes / t["median"] / 1e12 / 8, 4),
                    "Gweights_s": round(n * k * b / t["median"] / 1e9, 1)}
+            if g_ws:
+                row["split_k_workspace_bytes"] = g_ws
             if not rmsnorm and (fmt, n, k, b) in valu:
                 row["valu_frac"] = round(valu[(fmt, n, k, b)] * 64 / t["median"] / VALU_PEAK_LANE_OPS, 4)
                 row["valu_lane_ops_per_weight"] = round(valu[(fmt, n, k, b)] * 64 / (n * k), 3)
@@ -894,6 +938,13 @@ def main():
                 rows.append(measure(fmt, n, k, b))
                 log(f"  {key} {rows[-1]}")
             extra[key] = rows
+        rows = []
+        for fmt, n, k, b in SPLIT_K:
+            split, single = measure(fmt, n, k, b), measure(fmt, n, k, b, use_ws=False)
+            rows.append({"fmt": fmt, "N": n, "K": k, "B": b, "split_us": split["us"], "single_pass_us": single["us"],
+                         "workspace_bytes": split.get("split_k_workspace_bytes", 0)})
+            log(f"  split-K {rows[-1]}")
+        extra["split_k"] = rows
         rows = []
         for gain in (True, "unit"):
             for n, k in ((14336, 4096), (4096, 4096)):

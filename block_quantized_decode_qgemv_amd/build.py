@@ -38,7 +38,7 @@ SAN_FLAGS = ["-fsanitize=address", "-fsanitize=undefined", "-fno-sanitize-recove
              "-g"]
 ARCH = "gfx950"
 
-DEVICE_SOURCES = ["gemv.hip", "gemv_norm.hip", "gemv_norm_unit.hip", "moe.hip", "quant.hip", "probe.hip"]
+DEVICE_SOURCES = ["gemv.hip", "gemv_splitk.hip", "gemv_norm.hip", "gemv_norm_unit.hip", "moe.hip", "quant.hip", "probe.hip"]
 HOST_SOURCES = ["host.cpp"]
 
 HIP_FLAGS = [

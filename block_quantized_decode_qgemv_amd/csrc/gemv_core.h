@@ -679,12 +679,16 @@ struct GemvDpp {
     // The same on waves [wave0, wave0 + W) of a larger workgroup, with the
     // cross-wave partials in red (W * 16 * B floats of LDS).  Every wave of the
     // workgroup must call it (it synchronizes the whole workgroup once).
-    // NORM, GAMMA: see run_rmsnorm; red_ss holds W * B floats.
+    // NORM, GAMMA: see run_rmsnorm; red_ss holds W * B floats.  [cb, ce):
+    // the code units of each row to sum over (ce < 0: to the row's end), for
+    // a split of K; cb * CPC must be a multiple of 256 columns (whole
+    // super-blocks and 64-column spans).  A split sums only its own columns,
+    // so NORM (which needs every column's square) takes the whole row.
     template <bool NORM = false, bool GAMMA = true, class XRow, class Epi>
     __device__ static void run_group(const uint8_t* __restrict__ codes, const uint8_t* __restrict__ meta,
                                      int N, int K, int g, XRow xrow, int nb, Epi epi, int wave0, float* red,
                                      const float* __restrict__ gamma = nullptr, float eps = 0.0f,
-                                     float* red_ss = nullptr) {
+                                     float* red_ss = nullptr, int cb = 0, int ce = -1) {
         const int tid = threadIdx.x - 64 * wave0, lane = tid & 63, wave = tid >> 6;
         const int r = lane & 15, p = wave * 4 + (lane >> 4);
         const int n_g = min(kRowGroup, N - g * kRowGroup);
@@ -692,6 +696,8 @@ struct GemvDpp {
         const int nb_blocks = K / T::BLOCK;
         const int row_codes = nb_blocks * T::CB, row_meta = nb_blocks * T::MB;
         const int nch = row_codes >> 4;
+        const int c_end = ce < 0 ? nch : ce;  // this call's units: [cb, c_end)
+        const int k_end = c_end * CPC;        // and columns: [cb * CPC, k_end)
         const bool meta_whole = (row_meta & 15) == 0;
         const int ustride = n_g * 16;
         // uniform group bases plus unsigned 32-bit lane offsets (scalar-base loads)
@@ -721,10 +727,10 @@ struct GemvDpp {
             constexpr bool FULL = decltype(full_tag)::value;
             const uint32_t ust = FULL ? kRowGroup * 16 : (uint32_t)ustride;
             const uint32_t rof = FULL ? (uint32_t)r * 16 : ro;
-            for (int c_slice = 0; c_slice < nch; c_slice += SU) {
+            for (int c_slice = cb; c_slice < c_end; c_slice += SU) {
                 const int c0 = c_slice + p * KCS;  // first code unit of this lane's part
                 const int k0 = c0 * CPC;           // its first column
-                const int nvalid = FULL ? KCS : nch - c0;
+                const int nvalid = FULL ? KCS : c_end - c0;
 
                 // (1) x of the part, four columns per lane per span
                 float4 xv[B][NX4];
@@ -732,7 +738,7 @@ struct GemvDpp {
                 if constexpr (NORM && GAMMA) {
 #pragma unroll
                     for (int m = 0; m < NX4; ++m) {
-                        const uint32_t c = (uint32_t)(FULL ? k0 + 64 * m + 4 * r : min(k0 + 64 * m + 4 * r, K - 4));
+                        const uint32_t c = (uint32_t)(FULL ? k0 + 64 * m + 4 * r : min(k0 + 64 * m + 4 * r, k_end - 4));
                         gv[m] = *(const float4*)((const uint8_t*)gamma + c * 4u);
                     }
                 }
@@ -744,7 +750,7 @@ struct GemvDpp {
                         for (int m = 0; m < NX4; ++m) {
                             // columns past K read the row's last float4 instead: they
                             // only meet code units whose contributions are dropped
-                            const uint32_t c = (uint32_t)(FULL ? k0 + 64 * m + 4 * r : min(k0 + 64 * m + 4 * r, K - 4));
+                            const uint32_t c = (uint32_t)(FULL ? k0 + 64 * m + 4 * r : min(k0 + 64 * m + 4 * r, k_end - 4));
                             xv[b][m] = *(const float4*)((const uint8_t*)xb + c * 4u);
                         }
                     }
@@ -759,7 +765,7 @@ struct GemvDpp {
                             // each column once: the lanes of a part tile it, parts are
                             // disjoint, and clamped columns past K are not added
                             const float sq = fmaf(v.w, v.w, fmaf(v.z, v.z, fmaf(v.y, v.y, fmaf(v.x, v.x, ss[b]))));
-                            if (FULL || k0 + 64 * m + 4 * r < K) ss[b] = sq;
+                            if (FULL || k0 + 64 * m + 4 * r < k_end) ss[b] = sq;
                             if constexpr (GAMMA) {
                                 const float4 g4 = gv[m];
                                 xv[b][m] = make_float4(v.x * g4.x, v.y * g4.y, v.z * g4.z, v.w * g4.w);
@@ -772,14 +778,14 @@ struct GemvDpp {
                 uint32_t wd[is_kquant<F>() ? 4 : (MB + 3) / 4];
                 if constexpr (is_kquant<F>()) {
                     const int sbi = c0 / UPS, uo = c0 % UPS;
-                    const uint32_t u = (uint32_t)(FULL ? sbi : min(sbi, nb_blocks - 1));
+                    const uint32_t u = (uint32_t)(FULL ? sbi : min(sbi, (c_end - 1) / UPS));
                     const uint4 v = ld_weights<uint4>(gm + (u * ust + rof));
                     // pairs of the part's first unit moved to the bottom of the field
                     const unsigned __int128 f =
                         ((unsigned __int128)v.z << 64 | (unsigned __int128)v.y << 32 | v.x) >> (12 * SUBS * uo);
                     wd[0] = (uint32_t)f; wd[1] = (uint32_t)(f >> 32); wd[2] = (uint32_t)(f >> 64); wd[3] = v.w;
                 } else {
-                    const int m0 = (FULL ? c0 : min(c0, (nch - 1) / KCS * KCS)) * T::MBU;
+                    const int m0 = (FULL ? c0 : min(c0, (c_end - 1) / KCS * KCS)) * T::MBU;
                     if (meta_whole) {
                         const uint8_t* pm = gm + ((uint32_t)(m0 >> 4) * ust + rof + (m0 & 15));
                         if constexpr (MB >= 16) {
@@ -803,7 +809,7 @@ struct GemvDpp {
                 uint4 q[KCS];
 #pragma unroll
                 for (int i = 0; i < KCS; ++i) {
-                    const uint32_t u = (uint32_t)(FULL ? c0 + i : min(c0 + i, nch - 1));
+                    const uint32_t u = (uint32_t)(FULL ? c0 + i : min(c0 + i, c_end - 1));
                     q[i] = ld_weights<uint4>(gc + (u * ust + rof));
                 }
 
@@ -877,7 +883,7 @@ struct GemvDpp {
             }
         };
         if constexpr (B > 1) {
-            if (n_g == kRowGroup && nch % SU == 0) slices(std::true_type{});
+            if (n_g == kRowGroup && (c_end - cb) % SU == 0) slices(std::true_type{});
             else slices(std::false_type{});
         } else {
             slices(std::false_type{});

@@ -114,7 +114,14 @@ int qg_block_size(int fmt);
 
 /* ------------------------------------------------------------------- GEMV */
 
-/* Device scratch the GEMV needs, in bytes (0 means ws may be NULL). */
+/* Device scratch the GEMV can use, in bytes: S * B * N * 4 when the shape
+ * is split along K (S = 4 or 2 pieces of whole 256-column spans, chosen
+ * when the row groups times S still fit the device's compute units and the
+ * batch is 5 or more, so the launch is VALU-bound on a few compute units --
+ * e.g. 1024 x 4096 at batch 8), else 0.  The split follows the handbook
+ * page's decode bound ("速度上限：带宽 ÷ 权重字节数"): the bytes are the same,
+ * the split only spreads them over more of the chip.  0 also for arguments
+ * qgemv rejects. */
 size_t qgemv_workspace_size(int fmt, int64_t N, int64_t K, int B);
 
 /* Y[b][n] = sum_k W[n][k] * X[b][k] for b < B, n < N, in fp32 with fp32
@@ -127,12 +134,15 @@ size_t qgemv_workspace_size(int fmt, int64_t N, int64_t K, int B);
  *   2^26 (offsets inside a 16-row group are 32-bit);
  *   1 <= B <= 8.
  *   ws  DEVICE scratch of >= qgemv_workspace_size() bytes, 16-byte aligned,
- *       or NULL when that size is 0.
+ *       not overlapping w, x or y: the split-K partial sums (two launches:
+ *       the pieces, then their fixed-order sum).  NULL, or a smaller
+ *       ws_bytes, runs the single-pass kernel instead (same accuracy bound,
+ *       its own summation order).  Its contents are scratch.
  * Accuracy: |y - y_exact| <= 2e-5 * sum_k |W[n][k] X[b][k]| + 1e-7, where
  * y_exact is the exact sum over the decoded weights.  Results are
  * deterministic: the same inputs give the same bits on every call.
- * Errors: QG_EINVAL (null w/x/y, unknown fmt), QG_ESHAPE, QG_ERANGE (B),
- * QG_EALIGN, QG_EHIP. */
+ * Errors: QG_EINVAL (null w/x/y, unknown fmt; a used ws overlapping w, x or
+ * y), QG_ESHAPE, QG_ERANGE (B), QG_EALIGN (also a used ws), QG_EHIP. */
 int qgemv(int fmt, const void* w, const float* x, float* y, int64_t N, int64_t K, int B,
           void* ws, size_t ws_bytes, void* stream);
 

@@ -353,3 +353,30 @@ def test_moe_noalloc_validation():
     assert call(x=P + 5 * big - 64) == -1      # x overlaps out
     assert call(i=4096, k=8, t=8) == -4        # the layer's workspace exceeds the scratch
     assert qg.qg_last_error()
+
+
+def test_gemv_workspace_size():
+    # split K only from batch 5 and for row-starved shapes (groups * S <= compute units)
+    assert qg.qgemv_workspace_size("q4_k", 1024, 4096, 1) == 0
+    assert qg.qgemv_workspace_size("q4_k", 1024, 4096, 3) == 0
+    assert qg.qgemv_workspace_size("q4_k", 4096, 4096, 8) == 0
+    assert qg.qgemv_workspace_size("q4_k", 14336, 4096, 8) == 0
+    for fmt in OF.FORMATS:
+        size = qg.qgemv_workspace_size(fmt, 1024, 4096, 8)
+        assert size in (4 * 8 * 1024 * 4, 2 * 8 * 1024 * 4), size  # 4 splits on a 256-unit chip
+    assert qg.qgemv_workspace_size("q4_k", 1024, 4096 + 256, 8) == 0   # K does not split into 256-column pieces
+    assert qg.qgemv_workspace_size("q4_k", 1024, 128, 8) == 0          # invalid K
+    assert qg.qgemv_workspace_size("q4_k", 1024, 4096, 9) == 0         # invalid B
+
+
+@nogpu
+def test_gemv_splitk_workspace_validation():
+    lib = qg.load()
+    big = 1 << 24
+    n, k, b = 1024, 4096, 8
+    ws = qg.qgemv_workspace_size("q4_k", n, k, b)
+    assert ws > 0
+    # w, x, y and ws apart; ws misaligned / overlapping x: rejected before any launch
+    assert lib.qgemv(3, P, P + big, P + 2 * big, n, k, b, P + 3 * big + 4, ws, None) == -3
+    assert lib.qgemv(3, P, P + big, P + 2 * big, n, k, b, P + big + 64, ws, None) == -1
+    assert qg.qg_last_error()

@@ -5,8 +5,8 @@ UndefinedBehaviorSanitizer: the reference quantizer and packers
 (`python -m block_quantized_decode_qgemv_amd.build --sanitize`) in a child
 process with clang's sanitizer runtime preloaded.  Any heap or stack
 overflow, use after free or undefined behaviour aborts the child.  Skipped
-when that build is absent (it takes minutes, so the CPU suite does not make
-it)."""
+when that build is absent or older than the sources (it takes minutes, so
+the CPU suite does not make it)."""
 import os
 import subprocess
 import sys
@@ -18,7 +18,15 @@ from block_quantized_decode_qgemv_amd import build as B
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 
-@pytest.mark.skipif(not os.path.exists(B.SAN_LIB), reason="sanitized build absent (build.py --sanitize)")
+def _sanitized_build_current() -> bool:
+    if not os.path.exists(B.SAN_LIB):
+        return False
+    srcs = [os.path.join(B.CSRC, f) for f in os.listdir(B.CSRC)] + [os.path.join(B.INCLUDE, "qgemv.h")]
+    return os.path.getmtime(B.SAN_LIB) >= max(os.path.getmtime(p) for p in srcs)
+
+
+@pytest.mark.skipif(not _sanitized_build_current(),
+                    reason="sanitized build absent or older than the sources (build.py --sanitize)")
 def test_host_code_under_asan_ubsan():
     if os.environ.get("QG_TEST_LIB"):
         pytest.skip("already running against another library build")
