@@ -42,6 +42,9 @@ namespace {
 using namespace core;
 
 constexpr int kMaxT = 8, kMaxTopK = 8, kMaxE = 4096;
+// Up to this many experts, a single token's route is computed inside the
+// gate/up workgroups (8 logits per lane) instead of by a routing launch.
+constexpr int kRouteInGateUpMaxE = 512;
 constexpr int kItemInts = 8;  // expert, count, tok[2], kslot[2], wt[2] (as float bits)
 
 // Workspace layout, byte offsets (each region 256-byte aligned).
@@ -131,6 +134,54 @@ __device__ __forceinline__ uint64_t wave_key_max(uint64_t k) {
     return ((uint64_t)hi << 32) | lo;
 }
 
+// One token's route, computed by one wave: softmax statistics, then top_k
+// rounds of a wave argmax (lane owns experts lane + 64 m, values in
+// registers); returns, in lane k < top_k, the k-th expert (my_e) and its
+// routing weight (my_w), and the sigmoid of the shared-gate logit in every
+// lane.
+template <int MPL>  // experts per lane: E <= 64 * MPL
+__device__ __forceinline__ void route_token(const float* __restrict__ l, float sl, int E, int top_k, unsigned flags,
+                                            int lane, int& my_e, float& my_w, float& sig) {
+    float v[MPL];
+#pragma unroll
+    for (int m = 0; m < MPL; ++m) {
+        const int i = lane + 64 * m;
+        const float x = i < E ? l[i] : -INFINITY;
+        v[m] = __builtin_isnan(x) ? -INFINITY : x;  // NaN counts as -inf
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int m = 0; m < MPL; ++m) mx = fmaxf(mx, v[m]);
+    mx = wave_max_dpp(mx);
+    float s = 0.0f;
+#pragma unroll
+    for (int m = 0; m < MPL; ++m)
+        if (lane + 64 * m < E) s += expf(v[m] - mx);
+    s = wave_sum_dpp(s);
+    uint64_t key[MPL];
+#pragma unroll
+    for (int m = 0; m < MPL; ++m) key[m] = lane + 64 * m < E ? logit_key(v[m], lane + 64 * m) : 0;
+    my_e = 0;
+    float my_v = -INFINITY;  // round k's winning logit, kept by lane k
+    for (int k = 0; k < top_k; ++k) {
+        uint64_t best = key[0];
+#pragma unroll
+        for (int m = 1; m < MPL; ++m) best = key_max(best, key[m]);
+        const uint64_t win = wave_key_max(best);
+#pragma unroll
+        for (int m = 0; m < MPL; ++m) key[m] = key[m] == win ? 0 : key[m];  // taken
+        if (lane == k) { my_e = key_index(win); my_v = key_value(win); }
+    }
+    // the weights, off the rounds' dependency chain: lane k turns its logit
+    // into a probability; the renormalising sum adds them in round order
+    const float my_p = expf(my_v - mx) / s;
+    float wsum = 0.0f;
+    if (flags & QG_MOE_RENORM)
+        for (int k = 0; k < top_k; ++k) wsum += rl(my_p, k);
+    my_w = (flags & QG_MOE_RENORM) ? my_p / wsum : my_p;
+    sig = 1.0f / (1.0f + expf(-sl));
+}
+
 template <int MPL>  // experts per lane: E <= 64 * MPL
 __global__ void __launch_bounds__(512)
 moe_route_kernel(const float* __restrict__ logits, const float* __restrict__ shared_logit, int T, int E,
@@ -141,53 +192,16 @@ moe_route_kernel(const float* __restrict__ logits, const float* __restrict__ sha
     __shared__ uint64_t expert_pairs[kMaxE];  // only the chosen experts' entries are touched
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
 
-    // (1) one wave per token: softmax statistics, then top_k rounds of a wave
-    // argmax; lane owns experts lane + 64 m (values in registers) and marks
-    // picked ones in a bit mask
+    // (1) one wave per token
     if (wave < T) {
-        const float* l = logits + (size_t)wave * E;
-        const float sl = shared_logit[wave];  // requested with the router logits
-        float v[MPL];
-#pragma unroll
-        for (int m = 0; m < MPL; ++m) {
-            const int i = lane + 64 * m;
-            const float x = i < E ? l[i] : -INFINITY;
-            v[m] = __builtin_isnan(x) ? -INFINITY : x;  // NaN counts as -inf
-        }
-        float mx = -INFINITY;
-#pragma unroll
-        for (int m = 0; m < MPL; ++m) mx = fmaxf(mx, v[m]);
-        mx = wave_max_dpp(mx);
-        float s = 0.0f;
-#pragma unroll
-        for (int m = 0; m < MPL; ++m)
-            if (lane + 64 * m < E) s += expf(v[m] - mx);
-        s = wave_sum_dpp(s);
-        uint64_t key[MPL];
-#pragma unroll
-        for (int m = 0; m < MPL; ++m) key[m] = lane + 64 * m < E ? logit_key(v[m], lane + 64 * m) : 0;
-        int my_e = 0;
-        float my_v = -INFINITY;  // round k's winning logit, kept by lane k
-        for (int k = 0; k < top_k; ++k) {
-            uint64_t best = key[0];
-#pragma unroll
-            for (int m = 1; m < MPL; ++m) best = key_max(best, key[m]);
-            const uint64_t win = wave_key_max(best);
-#pragma unroll
-            for (int m = 0; m < MPL; ++m) key[m] = key[m] == win ? 0 : key[m];  // taken
-            if (lane == k) { my_e = key_index(win); my_v = key_value(win); }
-        }
-        // the weights, off the rounds' dependency chain: lane k turns its logit
-        // into a probability; the renormalising sum adds them in round order
-        const float my_p = expf(my_v - mx) / s;
-        float wsum = 0.0f;
-        if (flags & QG_MOE_RENORM)
-            for (int k = 0; k < top_k; ++k) wsum += rl(my_p, k);
+        int my_e;
+        float my_w, sg;
+        route_token<MPL>(logits + (size_t)wave * E, shared_logit[wave], E, top_k, flags, lane, my_e, my_w, sg);
         if (lane < top_k) {
             sel_e[wave * top_k + lane] = my_e;
-            sel_w[wave * top_k + lane] = (flags & QG_MOE_RENORM) ? my_p / wsum : my_p;
+            sel_w[wave * top_k + lane] = my_w;
         }
-        if (lane == 0) sig[wave] = 1.0f / (1.0f + expf(-sl));
+        if (lane == 0) sig[wave] = sg;
     }
     __syncthreads();
 
@@ -286,14 +300,58 @@ __device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }
 // rows (rows 2i+1); h[item][b][8g + i] = silu(gate) * up.  NORM 1 or 2: the token
 // rows are RMS-normalised on the way in (gain gamma, eps), as in the
 // normalising GEMV.
-template <int F, int W, int KCS, int NORM>
+//
+// RMPL > 0 (a single token, E <= 64 * RMPL): no routing launch precedes the
+// kernel; the items are the token's top_k experts in order, then the shared
+// expert, and workgroup column j routes the token itself (one wave, the
+// routing launch's own per-token code) to find its expert; workgroup (0, 0)
+// also writes the routing records the down kernel reads (items, hsel), the
+// same records the routing launch writes for one token.
+template <int F, int W, int KCS, int NORM, int RMPL>
 __global__ void __launch_bounds__(W * 64)
 moe_gate_up_kernel(const uint8_t* __restrict__ wgu, size_t expert_bytes, size_t codes_bytes, int H, int I,
                    const float* __restrict__ x, const float* __restrict__ gamma, float eps,
-                   const int* __restrict__ items, float* __restrict__ h) {
+                   int* __restrict__ items, float* __restrict__ h, const float* __restrict__ logits,
+                   const float* __restrict__ shared_logit, int E, int top_k, unsigned flags,
+                   int* __restrict__ hsel) {
     const int j = blockIdx.y;
-    if (j >= items[0]) return;  // uniform: unused item slot
-    const Item it = read_item(items, j);
+    Item it;
+    if constexpr (RMPL > 0) {
+        __shared__ int route_e[kMaxTopK];
+        const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+        it.expert = E;  // slot top_k: the shared expert, no routing needed
+        if (j < top_k) {  // uniform across the workgroup
+            if (wave == 0) {
+                int my_e;
+                float my_w, sg;
+                route_token<RMPL>(logits, shared_logit[0], E, top_k, flags, lane, my_e, my_w, sg);
+                if (lane < top_k) route_e[lane] = my_e;
+                if (blockIdx.x == 0 && j == 0) {
+                    // one token: item k is slot k's expert, then the shared one
+                    if (lane <= top_k) {
+                        int* rec = items + kItemInts * (1 + lane);
+                        rec[0] = lane < top_k ? my_e : E;
+                        rec[1] = 1;
+                        rec[2] = rec[3] = 0;
+                        rec[4] = rec[5] = lane;
+                        rec[6] = __float_as_int(lane < top_k ? my_w : sg);
+                        rec[7] = 0;
+                        hsel[lane] = 2 * lane;
+                    }
+                    if (lane == 0) items[0] = top_k + 1;
+                }
+            }
+            __syncthreads();
+            it.expert = route_e[j];
+        }
+        it.count = 1;
+        it.tok[0] = it.tok[1] = 0;
+        it.kslot[0] = it.kslot[1] = j;
+        it.wt[0] = it.wt[1] = 0.0f;
+    } else {
+        if (j >= items[0]) return;  // uniform: unused item slot
+        it = read_item(items, j);
+    }
     const uint8_t* codes = wgu + (size_t)it.expert * expert_bytes;
     const uint8_t* meta = codes + codes_bytes;
     const int g = blockIdx.x;
@@ -356,13 +414,32 @@ moe_down_kernel(const uint8_t* __restrict__ wdn, size_t expert_bytes, size_t cod
 
 // ------------------------------------------------------------- launchers
 
-template <int F, int W, int KCS, int NORM>
+template <int F, int W, int KCS, int NORM, int RMPL>
 hipError_t launch_gate_up_w(const uint8_t* wgu, int H, int I, const float* x, const float* gamma, float eps,
-                            const int* items, float* h, int max_items, hipStream_t st) {
+                            int* items, float* h, int max_items, const float* logits, const float* slogit, int E,
+                            int top_k, unsigned flags, int* hsel, hipStream_t st) {
     const size_t eb = qg_packed_size(F, 2 * (int64_t)I, H), cb = qg_codes_plane_size(F, 2 * (int64_t)I, H);
-    hipLaunchKernelGGL((moe_gate_up_kernel<F, W, KCS, NORM>), dim3(2 * I / kRowGroup, max_items), dim3(W * 64), 0,
-                       st, wgu, eb, cb, H, I, x, gamma, eps, items, h);
+    hipLaunchKernelGGL((moe_gate_up_kernel<F, W, KCS, NORM, RMPL>), dim3(2 * I / kRowGroup, max_items), dim3(W * 64),
+                       0, st, wgu, eb, cb, H, I, x, gamma, eps, items, h, logits, slogit, E, top_k, flags, hsel);
     return hipGetLastError();
+}
+
+template <int F, int KCS, int NORM, int RMPL>
+hipError_t launch_gate_up(const uint8_t* wgu, int H, int I, const float* x, const float* gamma, float eps, int* items,
+                          float* h, int max_items, const float* logits, const float* slogit, int E, int top_k,
+                          unsigned flags, int* hsel, hipStream_t st) {
+    switch (pick_waves_dpp<F, KCS>(H)) {
+        case 1: return launch_gate_up_w<F, 1, KCS, NORM, RMPL>(wgu, H, I, x, gamma, eps, items, h, max_items, logits,
+                                                               slogit, E, top_k, flags, hsel, st);
+        case 2: return launch_gate_up_w<F, 2, KCS, NORM, RMPL>(wgu, H, I, x, gamma, eps, items, h, max_items, logits,
+                                                               slogit, E, top_k, flags, hsel, st);
+        case 4: return launch_gate_up_w<F, 4, KCS, NORM, RMPL>(wgu, H, I, x, gamma, eps, items, h, max_items, logits,
+                                                               slogit, E, top_k, flags, hsel, st);
+        case 8: return launch_gate_up_w<F, 8, KCS, NORM, RMPL>(wgu, H, I, x, gamma, eps, items, h, max_items, logits,
+                                                               slogit, E, top_k, flags, hsel, st);
+        default: return launch_gate_up_w<F, 16, KCS, NORM, RMPL>(wgu, H, I, x, gamma, eps, items, h, max_items,
+                                                                 logits, slogit, E, top_k, flags, hsel, st);
+    }
 }
 
 template <int F, int WD, int KCS>
@@ -394,20 +471,21 @@ hipError_t launch_moe(const uint8_t* wgu, const uint8_t* wdn, int E, int H, int 
     int* hsel = reinterpret_cast<int*>(ws + L.hsel);
     float* h = reinterpret_cast<float*>(ws + L.h);
     hipError_t e;
-    if (E <= 64) e = launch_route<1>(logits, slogit, T, E, top_k, flags, items, hsel, st);
-    else if (E <= 128) e = launch_route<2>(logits, slogit, T, E, top_k, flags, items, hsel, st);
-    else if (E <= 256) e = launch_route<4>(logits, slogit, T, E, top_k, flags, items, hsel, st);
-    else if (E <= 512) e = launch_route<8>(logits, slogit, T, E, top_k, flags, items, hsel, st);
-    else if (E <= 1024) e = launch_route<16>(logits, slogit, T, E, top_k, flags, items, hsel, st);
-    else if (E <= 2048) e = launch_route<32>(logits, slogit, T, E, top_k, flags, items, hsel, st);
-    else e = launch_route<64>(logits, slogit, T, E, top_k, flags, items, hsel, st);
-    if (e != hipSuccess) return e;
-    switch (pick_waves_dpp<F, KCS>(H)) {
-        case 1: e = launch_gate_up_w<F, 1, KCS, NORM>(wgu, H, I, x, gamma, eps, items, h, L.max_items, st); break;
-        case 2: e = launch_gate_up_w<F, 2, KCS, NORM>(wgu, H, I, x, gamma, eps, items, h, L.max_items, st); break;
-        case 4: e = launch_gate_up_w<F, 4, KCS, NORM>(wgu, H, I, x, gamma, eps, items, h, L.max_items, st); break;
-        case 8: e = launch_gate_up_w<F, 8, KCS, NORM>(wgu, H, I, x, gamma, eps, items, h, L.max_items, st); break;
-        default: e = launch_gate_up_w<F, 16, KCS, NORM>(wgu, H, I, x, gamma, eps, items, h, L.max_items, st); break;
+    if (T == 1 && E <= kRouteInGateUpMaxE) {
+        // one token: the gate/up workgroups route it themselves (no routing launch)
+        e = launch_gate_up<F, KCS, NORM, kRouteInGateUpMaxE / 64>(wgu, H, I, x, gamma, eps, items, h, L.max_items,
+                                                                 logits, slogit, E, top_k, flags, hsel, st);
+    } else {
+        if (E <= 64) e = launch_route<1>(logits, slogit, T, E, top_k, flags, items, hsel, st);
+        else if (E <= 128) e = launch_route<2>(logits, slogit, T, E, top_k, flags, items, hsel, st);
+        else if (E <= 256) e = launch_route<4>(logits, slogit, T, E, top_k, flags, items, hsel, st);
+        else if (E <= 512) e = launch_route<8>(logits, slogit, T, E, top_k, flags, items, hsel, st);
+        else if (E <= 1024) e = launch_route<16>(logits, slogit, T, E, top_k, flags, items, hsel, st);
+        else if (E <= 2048) e = launch_route<32>(logits, slogit, T, E, top_k, flags, items, hsel, st);
+        else e = launch_route<64>(logits, slogit, T, E, top_k, flags, items, hsel, st);
+        if (e != hipSuccess) return e;
+        e = launch_gate_up<F, KCS, NORM, 0>(wgu, H, I, x, gamma, eps, items, h, L.max_items, logits, slogit, E, top_k,
+                                            flags, hsel, st);
     }
     if (e != hipSuccess) return e;
     // down waves per slot: what the row needs, within 16 waves for top_k + 1 slots
