@@ -6,7 +6,8 @@ batch-1 GEMV on a 14336x4096 matrix, cold cache.  The packed matrix exists as
 >= 1 GiB of distinct device copies (33 of 33 MB), so no launch finds its
 weights in the 256 MB last-level cache.  One *step* is one replay of a HIP
 graph that holds one GEMV launch per copy, i.e. one pass of the headline
-GEMV over every copy.  ``--warmup W`` replays are untimed; then exactly
+GEMV over every copy.  After 0.3 s of untimed replays (setup: the GPU
+leaves its idle clock), ``--warmup W`` replays are untimed; then exactly
 ``--steps K`` replays are timed, each bracketed by HIP events on the launch
 stream.  ``ms_per_step`` is the median replay time, ``value`` the packed bytes
 of one step over that median, and ``roofline.achieved`` the same median per
@@ -47,6 +48,7 @@ HBM_PEAK_GBS = 8000.0           # MI355X published HBM3E bandwidth
 VALU_PEAK_LANE_OPS = 256 * 4 * 16 * 2.4e9
 DENSE_8B_BYTES = 3_925_868_544  # Q4_K bytes of the 8B-class step's linear weights
 COLD_BYTES = 1 << 30            # rotate over at least this many bytes of packed copies
+SETTLE_S = 0.3                  # untimed replays before the warm-up steps (clock settle)
 PROFILES = os.path.join(ROOT, "profiles")
 COUNTERS_FILE = os.path.join(PROFILES, "q4k_gemv_14336x4096_counters.txt")
 VALU_FILE = os.path.join(PROFILES, "gemv_valu_counters.txt")
@@ -703,6 +705,27 @@ def summarize(kind, paths, commands):
                   f"gaps_us_median: {np.median(rows[:, 2]) / 1e3:.1f}",
                   f"gap_per_launch_us: {np.median(rows[:, 2]) / 1e3 / (per_step - 1):.2f}"]
         out = os.path.join(PROFILES, "dense_8b_step_gaps.txt")
+    elif kind in ("moe-trace", "norm-trace"):
+        # paths: kernel-trace CSV of `--profile moe` (or `--profile norm`)
+        per = {}
+        for r in _csv_rows(paths[0]):
+            if "qg::" not in r["Kernel_Name"]:
+                continue
+            short = r["Kernel_Name"].replace("qg::(anonymous namespace)::", "").replace("void ", "").split("(")[0]
+            grid = int(r.get("Grid_Size_X", 0) or 0) * int(r.get("Grid_Size_Y", 1) or 1)
+            per.setdefault(f"{short} grid {grid}", []).append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+        title = {"moe-trace": "MoE layer, 512 experts + 1 shared, hidden 4096, intermediate 1024, top-4 "
+                              "(Q4_K then Q2_K, T = 1 then 8; eager passes over 32 routing sets)",
+                 "norm-trace": "RMS-norm GEMVs (Q4_K, 14336x4096 and 4096x4096, batch 1 and 8) and the MoE "
+                               "pre-norm block step"}[kind]
+        lines = _header(f"rocprofv3 kernel trace: {title}", commands)
+        lines.append("# kernel and grid size (work-items): dispatches | median us | p10 us | p90 us")
+        for name in sorted(per):
+            v = np.array(per[name]) / 1e3
+            lines.append(f"kernel {name}: {len(v)} | {np.median(v):.2f} | {np.percentile(v, 10):.2f} | "
+                         f"{np.percentile(v, 90):.2f}")
+        out = os.path.join(PROFILES, {"moe-trace": "moe_layer_e512_h4096_i1024_kernel_trace.txt",
+                                      "norm-trace": "q4k_rmsnorm_gemv_and_moe_block_kernel_trace.txt"}[kind])
     elif kind == "headline":
         # paths: FETCH_SIZE and WRITE_SIZE CSVs of `--profile gemv`, then the copy FETCH and WRITE CSVs
         fetch = [v for _, _, _, v in _counter_per_dispatch(paths[0], "gemv_dpp_kernel", "FETCH_SIZE")]
@@ -766,7 +789,7 @@ def main():
                          "block step")
     ap.add_argument("--summarize", nargs="+", metavar=("KIND", "CSV"), default=None,
                     help="write a profiles/ summary from rocprofv3 CSVs (kinds: valu, peak, moe, step, norm, "
-                         "step-trace, headline, headline-trace)")
+                         "step-trace, headline, headline-trace, moe-trace, norm-trace)")
     ap.add_argument("--command", action="append", default=[], help="command line recorded in a summary")
     args = ap.parse_args()
     if args.summarize:
@@ -853,6 +876,13 @@ def main():
         return
 
     per = head.capture()
+    # setup, not warm-up: replay for SETTLE_S so the GPU leaves its idle clock
+    # before the W warm-up steps (with a handful of steps the timed replays
+    # otherwise catch the clock ramp: median 8.5 against 8.0 us per launch)
+    t_settle = time.perf_counter()
+    while time.perf_counter() - t_settle < SETTLE_S:
+        head.replay(20)
+        torch.cuda.synchronize()
     head.replay(args.warmup)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
