@@ -17,8 +17,9 @@ Also reported: the measured HBM read peak (a 4 GiB streaming read) and the
 headline's fraction of it, a same-size read, every GEMV of the four-format
 comparison (Q8_0/Q4_0/Q4_1/Q4_K x 4096x4096/14336x4096 x batch 1/8), the
 low-bit formats (tern/bin/bin8/Q2_K, batch 1/4) with their fraction of the
-VALU peak where VALU counters were taken, the row-starved shapes of the 8B
-step, the RMS-normalising GEMVs, the 8B decode step and the MoE layer.
+VALU peak where VALU counters were taken, the shapes of the 8B step and one
+larger matrix (57344x4096), the split-K launches against the single pass,
+the RMS-normalising GEMVs, the 8B decode step and the MoE layer.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--quick] [--no-cpu]
     python bench.py --profile {gemv,copy,probe4g,valu,moe,step,norm}   # one part, for rocprofv3
@@ -68,6 +69,8 @@ SPLIT_K = [("q4_k", 1024, 4096, b) for b in (3, 5, 8)] + [(f, 1024, 4096, 8) for
 # the 8B step's Q4_K shapes at batch 1, fused (qkv 6144, gate/up 28672) and not
 STEP_SHAPES = [("q4_k", n, k, 1) for n, k in ((1024, 4096), (4096, 4096), (6144, 4096), (14336, 4096),
                                                (28672, 4096), (4096, 14336))]
+# one larger matrix: how close a single launch gets once its fixed cost is amortized
+LARGE = [("q4_k", 57344, 4096, 1)]
 VALU_ROWS = FOUR_FORMATS + LOW_BIT
 VALU_LAUNCHES = 3               # launches per row in the VALU counter pass
 
@@ -962,12 +965,15 @@ def main():
                 row["valu_lane_ops_per_weight"] = round(valu[(fmt, n, k, b)] * 64 / (n * k), 3)
             return row
 
-        for key, rows_def in (("four_formats", FOUR_FORMATS), ("low_bit", LOW_BIT), ("step_shapes", STEP_SHAPES)):
+        for key, rows_def in (("four_formats", FOUR_FORMATS), ("low_bit", LOW_BIT), ("step_shapes", STEP_SHAPES),
+                              ("large_matrix", LARGE)):
             rows = []
             for fmt, n, k, b in rows_def:
                 rows.append(measure(fmt, n, k, b))
                 log(f"  {key} {rows[-1]}")
             extra[key] = rows
+        for row in extra["large_matrix"]:
+            row["frac_of_measured_peak"] = round(row["GBps"] / measured_peak, 4)
         rows = []
         for fmt, n, k, b in SPLIT_K:
             split, single = measure(fmt, n, k, b), measure(fmt, n, k, b, use_ws=False)
