@@ -23,14 +23,14 @@ __all__ = [
     "FORMATS", "QG_MOE_RENORM", "QG_MOE_NOALLOC_SCRATCH_BYTES", "QGError", "QGLibraryMissing", "lib_path", "load",
     "qg_packed_size", "qg_codes_plane_size", "qg_codes_plane_offset", "qg_block_size", "qgemv_workspace_size",
     "qgemv", "qgemv_q8_0", "qgemv_q4_0", "qgemv_q4_1", "qgemv_q4k", "qgemv_q2k",
-    "qgemv_tern", "qgemv_bin", "qgemv_bin8", "qgemv_rmsnorm", "qg_dequant", "qquant", "qquant_device", "qrequant_workspace_size", "qrequant",
-    "qpack_tern", "qpack_bin", "qpack_bin8",
+    "qgemv_tern", "qgemv_bin", "qgemv_bin8", "qgemv_tern3", "qgemv_rmsnorm", "qg_dequant", "qquant", "qquant_device", "qrequant_workspace_size", "qrequant",
+    "qpack_tern", "qpack_bin", "qpack_bin8", "qpack_tern3",
     "moe_expert_ffn_workspace_size", "moe_expert_ffn_workspace_layout", "moe_expert_ffn", "moe_expert_ffn_noalloc", "moe_expert_ffn_rmsnorm", "qg_strerror", "qg_last_error",
     "qg_version", "EXPORTED_SYMBOLS",
 ]
 
 QG_MOE_NOALLOC_SCRATCH_BYTES = 2 << 20  # the no-allocation MoE entry point's device scratch (qgemv.h)
-FORMATS = {"q8_0": 0, "q4_0": 1, "q4_1": 2, "q4_k": 3, "q2_k": 4, "tern": 5, "bin": 6, "bin8": 7}
+FORMATS = {"q8_0": 0, "q4_0": 1, "q4_1": 2, "q4_k": 3, "q2_k": 4, "tern": 5, "bin": 6, "bin8": 7, "tern3": 8}
 QG_MOE_RENORM = 1
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -58,6 +58,7 @@ _SIGNATURES = {
     "qgemv_tern": (_i32, _GEMV_ARGS),
     "qgemv_bin": (_i32, _GEMV_ARGS),
     "qgemv_bin8": (_i32, _GEMV_ARGS),
+    "qgemv_tern3": (_i32, _GEMV_ARGS),
     "qgemv_rmsnorm": (_i32, [_i32, _vp, _vp, _vp, ctypes.c_float, _vp, _i64, _i64, _i32, _vp]),
     "qg_dequant": (_i32, [_i32, _vp, _vp, _i64, _i64, _vp]),
     "qquant": (_i32, [_i32, _vp, _i64, _i64, _vp, _i32]),
@@ -67,6 +68,7 @@ _SIGNATURES = {
     "qpack_tern": (_i32, [_vp, _vp, _i64, _i64, _vp]),
     "qpack_bin": (_i32, [_vp, _vp, _i64, _i64, _vp]),
     "qpack_bin8": (_i32, [_vp, _vp, _i64, _i64, _vp]),
+    "qpack_tern3": (_i32, [_vp, _vp, _i64, _i64, _vp]),
     "moe_expert_ffn_workspace_size": (_sz, [_i32, _i32, _i32, _i32, _i32]),
     "moe_expert_ffn_workspace_layout": (_i32, [_i32, _i32, _i32, _i32, _i32, ctypes.POINTER(_sz),
                                                ctypes.POINTER(_sz)]),
@@ -275,6 +277,7 @@ qgemv_q2k = _named("qgemv_q2k", "q2_k")
 qgemv_tern = _named("qgemv_tern", "tern")
 qgemv_bin = _named("qgemv_bin", "bin")
 qgemv_bin8 = _named("qgemv_bin8", "bin8")
+qgemv_tern3 = _named("qgemv_tern3", "tern3")
 
 
 def qgemv_rmsnorm(fmt, w, x, gamma, eps: float, y, n: int, k: int, b: int = 1, stream=None) -> None:
@@ -337,18 +340,18 @@ def qquant(fmt, w_host, n_threads: int | None = None) -> np.ndarray:
     return out[:size]
 
 
-def _codes_and_scales(codes, scale_bits, dtype, name):
-    """2-D [N, K] codes and fp16 scale bits of shape [N, K/128], checked so the
-    host packer never reads past either array."""
+def _codes_and_scales(codes, scale_bits, dtype, name, group=128, block=128):
+    """2-D [N, K] codes and fp16 scale bits of shape [N, K/group], checked so
+    the host packer never reads past either array (K a multiple of block)."""
     c = np.ascontiguousarray(codes, dtype=dtype)
     s = np.ascontiguousarray(scale_bits, dtype=np.uint16)
     if c.ndim != 2:
         raise ValueError(f"{name}: codes must be 2-D [N, K], got shape {c.shape}")
     n, k = c.shape
-    if k % 128:
-        raise ValueError(f"{name}: K={k} must be a multiple of 128")
-    if s.shape != (n, k // 128):
-        raise ValueError(f"{name}: scale_bits must have shape {(n, k // 128)}, got {s.shape}")
+    if k % block:
+        raise ValueError(f"{name}: K={k} must be a multiple of {block}")
+    if s.shape != (n, k // group):
+        raise ValueError(f"{name}: scale_bits must have shape {(n, k // group)}, got {s.shape}")
     return c, s, n, k
 
 
@@ -365,6 +368,15 @@ def qpack_bin(bits, scale_bits) -> np.ndarray:
     size = qg_packed_size("bin", n, k)
     out = np.empty(max(size, 1), dtype=np.uint8)
     _check(load().qpack_bin(bb.ctypes.data, s.ctypes.data, n, k, out.ctypes.data), "qpack_bin")
+    return out[:size]
+
+
+def qpack_tern3(codes, scale_bits) -> np.ndarray:
+    """Ternary codes and fp16 scales per 64 weights -> packed tern3 bytes (see qpack_tern3 in qgemv.h)."""
+    t, s, n, k = _codes_and_scales(codes, scale_bits, np.int8, "qpack_tern3", group=64, block=256)
+    size = qg_packed_size("tern3", n, k)
+    out = np.empty(max(size, 1), dtype=np.uint8)
+    _check(load().qpack_tern3(t.ctypes.data, s.ctypes.data, n, k, out.ctypes.data), "qpack_tern3")
     return out[:size]
 
 

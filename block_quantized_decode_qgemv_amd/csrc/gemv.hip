@@ -218,6 +218,7 @@ int splitk_parts(int64_t N, int64_t K, int B) {
 int check_gemv_args(int fmt, const void* w, const float* x, const float* y, int64_t N, int64_t K, int B) {
     int rc = check_matrix(fmt, N, K);
     if (rc) return rc;
+    if (fmt == QG_TERN3) return fail(QG_EUNSUPPORTED, "no TERN3 kernel in this build");
     if (!w || !x || !y) return fail(QG_EINVAL, "null w, x or y");
     if (B < 1 || B > QG_MAX_BATCH) return fail(QG_ERANGE, "B=%d must be in [1, %d]", B, QG_MAX_BATCH);
     // offsets inside a 16-row group are 32-bit
@@ -281,6 +282,7 @@ QG_GEMV_ALIAS(qgemv_q4_1, QG_Q4_1)
 QG_GEMV_ALIAS(qgemv_q4k, QG_Q4_K)
 QG_GEMV_ALIAS(qgemv_q2k, QG_Q2_K)
 QG_GEMV_ALIAS(qgemv_tern, QG_TERN)
+QG_GEMV_ALIAS(qgemv_tern3, QG_TERN3)
 QG_GEMV_ALIAS(qgemv_bin, QG_BIN)
 QG_GEMV_ALIAS(qgemv_bin8, QG_BIN8)
 #undef QG_GEMV_ALIAS
@@ -289,6 +291,7 @@ int qg_dequant(int fmt, const void* w, float* out, int64_t N, int64_t K, void* s
     clear_error();
     int rc = check_matrix(fmt, N, K);
     if (rc) return rc;
+    if (fmt == QG_TERN3) return fail(QG_EUNSUPPORTED, "no TERN3 kernel in this build");
     if (!w || !out) return fail(QG_EINVAL, "null w or out");
     if (!aligned(w, 16)) return fail(QG_EALIGN, "w must be 16-byte aligned");
     if (!aligned(out, 4)) return fail(QG_EALIGN, "out must be 4-byte aligned");

@@ -31,6 +31,7 @@ const FormatInfo kFormats[] = {
     {128, 32, 2},   // TERN
     {128, 16, 2},   // BIN
     {128, 16, 1},   // BIN8 (plus the per-row plane, see qg_packed_size)
+    {256, 48, 12},  // TERN3: four 64-weight scale groups per block
 };
 
 thread_local char g_last_error[512] = "";
@@ -233,7 +234,7 @@ int quant_row(int fmt, const float* w, int64_t K, uint8_t* codes, uint8_t* meta)
 }  // namespace
 
 const FormatInfo* format_info(int fmt) {
-    if (fmt < QG_Q8_0 || fmt > QG_BIN8) return nullptr;
+    if (fmt < QG_Q8_0 || fmt > QG_TERN3) return nullptr;
     return &kFormats[fmt];
 }
 
@@ -313,8 +314,9 @@ const char* qg_version(void) { return "qgemv 0.1 (gfx950)"; }
 
 int qquant(int fmt, const float* w_host, int64_t N, int64_t K, void* out_host, int n_threads) {
     clear_error();
-    if (fmt == QG_TERN || fmt == QG_BIN || fmt == QG_BIN8)
-        return fail(QG_EINVAL, "format %d packs given codes: use qpack_tern / qpack_bin / qpack_bin8", fmt);
+    if (fmt == QG_TERN || fmt == QG_BIN || fmt == QG_BIN8 || fmt == QG_TERN3)
+        return fail(QG_EINVAL, "format %d packs given codes: use qpack_tern / qpack_bin / qpack_bin8 / qpack_tern3",
+                    fmt);
     int rc = check_matrix(fmt, N, K);
     if (rc) return rc;
     if (!w_host || !out_host) return fail(QG_EINVAL, "null pointer");
@@ -387,6 +389,50 @@ int qpack_tern(const int8_t* t, const uint16_t* scale_f16, int64_t N, int64_t K,
                 gc[i * row_codes + k / 4] = byte;
             }
             for (int64_t b = 0; b < K / 128; ++b) put_u16(gm.data() + i * row_meta + 2 * b, scale_f16[(size_t)r * (K / 128) + b]);
+        }
+        interleave_group(gc.data(), n_g, row_codes, codes + (size_t)(16 * g) * row_codes);
+        interleave_group(gm.data(), n_g, row_meta, meta + (size_t)(16 * g) * row_meta);
+    }
+    return QG_OK;
+}
+
+int qpack_tern3(const int8_t* t, const uint16_t* scale_f16, int64_t N, int64_t K, void* out_host) {
+    clear_error();
+    int rc = check_matrix(QG_TERN3, N, K);
+    if (rc) return rc;
+    if (!t || !scale_f16 || !out_host) return fail(QG_EINVAL, "null pointer");
+    const int64_t nb = K / 256;
+    const size_t row_codes = (size_t)nb * 48, row_meta = (size_t)nb * 12;
+    uint8_t* codes = static_cast<uint8_t*>(out_host);
+    uint8_t* meta = codes + (size_t)N * row_codes;
+    std::vector<uint8_t> gc(16 * row_codes), gm(16 * row_meta);
+    for (int64_t g = 0; g < (N + 15) / 16; ++g) {
+        const int n_g = (int)std::min<int64_t>(16, N - 16 * g);
+        for (int i = 0; i < n_g; ++i) {
+            const int64_t r = 16 * g + i;
+            const int8_t* tr = t + (size_t)r * K;
+            for (int64_t k = 0; k < K; ++k)
+                if (tr[k] < -1 || tr[k] > 1)
+                    return fail(QG_EINVAL, "ternary code %d at (%lld, %lld)", tr[k], (long long)r, (long long)k);
+            for (int64_t b = 0; b < nb; ++b) {
+                uint8_t* cb = gc.data() + i * row_codes + 48 * b;
+                uint8_t* mb = gm.data() + i * row_meta + 12 * b;
+                uint32_t field = 0;
+                for (int s = 0; s < 4; ++s) {
+                    const int8_t* ts = tr + 256 * b + 64 * s;  // one 64-weight scale group
+                    // byte 4e + j: the base-3 digits of columns 20e + 4l + j, l = 0..4 (digit l has weight 3^l)
+                    for (int e = 0; e < 3; ++e)
+                        for (int j = 0; j < 4; ++j) {
+                            unsigned v = 0;
+                            for (int l = 4; l >= 0; --l) v = 3 * v + (unsigned)(ts[20 * e + 4 * l + j] + 1);
+                            cb[12 * s + 4 * e + j] = (uint8_t)v;
+                        }
+                    // columns 60..63: 2-bit fields, field byte l at bits 2s
+                    for (int l = 0; l < 4; ++l) field |= (uint32_t)(ts[60 + l] + 1) << (8 * l + 2 * s);
+                    put_u16(mb + 2 * s, scale_f16[(size_t)r * (K / 64) + 4 * b + s]);
+                }
+                for (int l = 0; l < 4; ++l) mb[8 + l] = (uint8_t)(field >> (8 * l));
+            }
         }
         interleave_group(gc.data(), n_g, row_codes, codes + (size_t)(16 * g) * row_codes);
         interleave_group(gm.data(), n_g, row_meta, meta + (size_t)(16 * g) * row_meta);

@@ -250,7 +250,7 @@ hipError_t launch_quant(int fmt, const float* w, int64_t N, int64_t K, uint8_t* 
 }
 
 int check_quant(int fmt, int64_t N, int64_t K, const void* out, const int* status) {
-    if (fmt == QG_TERN || fmt == QG_BIN || fmt == QG_BIN8)
+    if (fmt == QG_TERN || fmt == QG_BIN || fmt == QG_BIN8 || fmt == QG_TERN3)
         return fail(QG_EUNSUPPORTED, "format %d has no quantizer (it packs given codes)", fmt);
     int rc = check_matrix(fmt, N, K);
     if (rc) return rc;

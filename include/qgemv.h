@@ -8,9 +8,10 @@
  * row with the activation vector, y = W x, and every weight is read once per
  * token.  Batch B stacks activation rows: Y[b][n] = sum_k W[n][k] * X[b][k].
  * The block formats are those of the same page, section "GGUF 的量化格式"
- * (Q8_0, Q4_0, Q4_1, Q4_K), plus Q2_K, ternary weights in 2-bit fields and
- * 1-bit sign weights (with fp16 block scales, or 8-bit per-row affine ones)
- * from the low-bit README page's kernel table, and the
+ * (Q8_0, Q4_0, Q4_1, Q4_K), plus Q2_K, ternary weights in 2-bit fields,
+ * ternary weights packed in base 3 at 1.875 bits per weight, and 1-bit sign
+ * weights (with fp16 block scales, or 8-bit per-row affine ones) from the
+ * low-bit README page's kernel table, and the
  * Flash-MoE page's 2-bit experts.  The MoE layer follows the Flash-MoE page,
  * sections "模型架构", "Metal 计算着色器" and "每层流水线".
  *
@@ -49,6 +50,13 @@
  *     TERN    128  32      2       2.125  fp16 scale; 2-bit field = t + 1
  *     BIN     128  16      2       1.125  fp16 scale; bit 1 = +1, 0 = -1
  *     BIN8    128  16      1       1.0625 scale code c; bits as BIN
+ *     TERN3   256  48      12      1.875  4 fp16 scales (one per 64), then a
+ *                                           32-bit field of 2-bit codes
+ *   TERN3 (the low-bit page's lossless base-3 ternary with a scale per 64
+ *   weights, kernel table, ternary Q2_0 row): f = t + 1 as for TERN; for the
+ *   64-weight group s of a block, code byte 12s + 4e + j (e < 3, j < 4) is
+ *   sum_{l<5} f(64s + 20e + 4l + j) * 3^l (<= 242), and f(64s + 60 + l) sits
+ *   at bits 2s..2s+1 of byte l of the meta entry's field (bytes 8..11).
  *   BIN8 adds a third plane: the meta plane is zero-padded to a multiple of
  *   16 bytes and followed by N rows of (base, step), two little-endian fp32;
  *   the block scale is fp32(base + fp32(step * c)) (see qpack_bin8).
@@ -56,7 +64,7 @@
  *   i in byte i>>2 at bits 2*(i&3); bit i in byte i>>3 at bit i&7.  All
  *   multi-byte values are little-endian.  Decoded weights:
  *     Q8_0 q*d; Q4_0 (n-8)*d; Q4_1 n*d+m; Q4_K/Q2_K n*(s_j*d) - t_j*dmin;
- *     TERN (f-1)*scale; BIN, BIN8 (2*bit-1)*scale.
+ *     TERN, TERN3 (f-1)*scale; BIN, BIN8 (2*bit-1)*scale.
  */
 #ifndef QGEMV_H
 #define QGEMV_H
@@ -76,7 +84,8 @@ typedef enum {
     QG_Q2_K = 4,
     QG_TERN = 5,
     QG_BIN = 6,
-    QG_BIN8 = 7
+    QG_BIN8 = 7,
+    QG_TERN3 = 8
 } qg_format;
 
 enum {
@@ -109,7 +118,8 @@ size_t qg_codes_plane_size(int fmt, int64_t N, int64_t K);
  * plane itself starts at offset 0).  0 if invalid. */
 size_t qg_codes_plane_offset(int fmt, int64_t N, int64_t K);
 
-/* Weights per block (32, 256 or 128) or 0 for an unknown format. */
+/* Weights per block (32, 256 or 128; TERN3 256, holding four scale groups
+ * of 64) or 0 for an unknown format. */
 int qg_block_size(int fmt);
 
 /* ------------------------------------------------------------------- GEMV */
@@ -163,6 +173,8 @@ int qgemv_bin(const void* w, const float* x, float* y, int64_t N, int64_t K, int
               void* ws, size_t ws_bytes, void* stream);
 int qgemv_bin8(const void* w, const float* x, float* y, int64_t N, int64_t K, int B,
                void* ws, size_t ws_bytes, void* stream);
+int qgemv_tern3(const void* w, const float* x, float* y, int64_t N, int64_t K, int B,
+                void* ws, size_t ws_bytes, void* stream);
 
 /* ------------------------------------------------- GEMV on normalised x */
 
@@ -206,7 +218,7 @@ int qg_dequant(int fmt, const void* w, float* out, int64_t N, int64_t K, void* s
  * stored values; rounding is half-to-even; a zero scale gives the zero code.
  * Signed zeros in the input are treated as +0.  n_threads <= 0 means 1.
  * Both pointers are HOST memory.  Errors: QG_EINVAL (null, non-finite input,
- * fmt is TERN/BIN/BIN8 -- use qpack_tern/qpack_bin/qpack_bin8), QG_ESHAPE, QG_ERANGE (a
+ * fmt is TERN/BIN/BIN8/TERN3 -- use their qpack_*), QG_ESHAPE, QG_ERANGE (a
  * scale or min overflows fp16; out_host is then unspecified). */
 int qquant(int fmt, const float* w_host, int64_t N, int64_t K, void* out_host, int n_threads);
 
@@ -220,7 +232,8 @@ int qquant(int fmt, const float* w_host, int64_t N, int64_t K, void* out_host, i
  *           with several failures it holds the smallest code.  The blocks
  *           that fail leave their bytes of out unspecified.
  * w, out and status must not overlap (QG_EINVAL).
- * fmt Q8_0, Q4_0, Q4_1, Q4_K or Q2_K (TERN and BIN: QG_EUNSUPPORTED; the
+ * fmt Q8_0, Q4_0, Q4_1, Q4_K or Q2_K (the 1-bit and ternary formats:
+ * QG_EUNSUPPORTED; the
  * pages give no ternarizer or binarizer).  Asynchronous on `stream`; read
  * status after synchronising.  Host errors: QG_EINVAL, QG_ESHAPE, QG_EALIGN,
  * QG_EUNSUPPORTED, QG_EHIP. */
@@ -248,6 +261,12 @@ int qrequant(int src_fmt, const void* src, int dst_fmt, void* dst, int64_t N, in
  * Errors: QG_EINVAL (null pointer, a code out of range), QG_ESHAPE. */
 int qpack_tern(const int8_t* t, const uint16_t* scale_f16, int64_t N, int64_t K, void* out_host);
 int qpack_bin(const uint8_t* bits, const uint16_t* scale_f16, int64_t N, int64_t K, void* out_host);
+
+/* Host packer for QG_TERN3 (layout above): t[N][K] int8 in {-1,0,1} and
+ * scale_f16[N][K/64] fp16 bit patterns (one scale per 64 weights) -> packed
+ * bytes; lossless (qg_dequant gives t * scale exactly).  K a multiple of 256.
+ * Errors: QG_EINVAL (null pointer, a code out of range), QG_ESHAPE. */
+int qpack_tern3(const int8_t* t, const uint16_t* scale_f16, int64_t N, int64_t K, void* out_host);
 
 /* Host packer for QG_BIN8, the 1-bit format whose block scales are 8-bit
  * codes of a per-row affine map (low-bit README page, kernel table, the

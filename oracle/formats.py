@@ -48,6 +48,21 @@ R9  bin8 is the low-bit page's 1-bit format whose block scales are 8-bit
     step = 0).  The (base, step) pairs form a third plane after the meta
     plane, which is zero-padded to a multiple of 16 bytes: N rows of two
     little-endian fp32, row-major, not interleaved.
+R10 tern3 is the low-bit page's lossless 1.875-bit form of ternary weights
+    that keep one scale per 64 weights (kernel table, the ternary Q2_0 row):
+    values t*d with t in {-1, 0, +1} (field f = t + 1, as in tern) and an
+    fp16 d per 64 weights.  The page gives the density, not the bytes.
+    Packing block: 256 weights = four 64-weight scale groups, 48 code bytes
+    and 12 meta bytes (1.875 bits per weight).  Codes: for group s of the
+    block, byte 12s + 4e + j (e < 3, j < 4) holds the base-3 number
+    sum_{l<5} f(64s + 20e + 4l + j) * 3^l (at most 242): five weights per
+    byte.  The last four weights of each group (columns 60..63) sit in a
+    32-bit field at the end of the meta entry: its byte l holds, at bits
+    2s..2s+1, f(64s + 60 + l).  Meta entry: the four fp16 scales in group
+    order (little-endian), then that field.  So a 64-weight group takes 12
+    bytes of base-3 digits plus one byte of 2-bit fields -- the 13 bytes that
+    1.875 bits per weight leave beside the 2-byte scale.  Like tern, these
+    blocks pack given codes and scales exactly (no ternarizer on any page).
 
 Plane layout of one packed [N][K] matrix (reading R8): the codes plane
 followed by the meta plane.  Each plane starts from the row-major byte image
@@ -76,6 +91,9 @@ scale codes.  Q8_0, Q4_0, Q4_1, Q4_K are pinned by the page's printed error
 table (page-literal mode), by the bits/weight closed forms in the listing and
 by round trips of hand-built blocks.  Q2_K, tern and bin are pinned by round
 trips, closed forms and brute force only (their layouts are readings).
+tern3 is pinned by the page's printed density (1.875 bits per weight), by
+hand-worked bytes of single weights in each position class and by exact
+round trips (its byte arrangement is a reading).
 """
 from __future__ import annotations
 
@@ -85,7 +103,7 @@ import numpy as np
 
 F32 = np.float32
 
-FORMATS = ("q8_0", "q4_0", "q4_1", "q4_k", "q2_k", "tern", "bin", "bin8")
+FORMATS = ("q8_0", "q4_0", "q4_1", "q4_k", "q2_k", "tern", "bin", "bin8", "tern3")
 
 
 class QuantInputError(ValueError):
@@ -116,6 +134,7 @@ SPECS = {
     "tern": Spec(128, 32, 2),
     "bin": Spec(128, 16, 2),
     "bin8": Spec(128, 16, 1),
+    "tern3": Spec(256, 48, 12),  # four 64-weight scale groups per block (R10)
 }
 
 # bytes per row of the per-row plane after the meta plane (R9)
@@ -296,6 +315,18 @@ def tern_from_codes(codes, scale_bits) -> dict:
     return {"d": sb.copy(), "f": (codes.astype(np.int16) + 1).astype(np.uint8)}
 
 
+def tern3_from_codes(codes, scale_bits) -> dict:
+    """Ternary codes t in {-1, 0, +1} [N, K] plus fp16 scale bits [N, K/64] (R10)."""
+    codes = np.asarray(codes)
+    n, k = codes.shape
+    if k % 256:
+        raise ValueError("K must be a multiple of 256")
+    if not np.all((codes >= -1) & (codes <= 1)):
+        raise QuantInputError("ternary codes must be -1, 0 or +1")
+    sb = np.asarray(scale_bits, dtype=np.uint16).reshape(n, k // 64)
+    return {"d": sb.copy(), "f": (codes.astype(np.int16) + 1).astype(np.uint8)}
+
+
 def bin_from_codes(bits, scale_bits) -> dict:
     """1-bit codes in {0, 1} [N, K] (1 means +1) plus fp16 scale bits [N, K/128]."""
     bits = np.asarray(bits)
@@ -389,6 +420,9 @@ def dequant(fmt: str, blk: dict) -> np.ndarray:
     if fmt == "tern":
         f = blk["f"]
         return (f.astype(np.int16) - 1).astype(F32) * _per_block(scale_values(blk["d"]), 128, f.shape[1])
+    if fmt == "tern3":
+        f = blk["f"]
+        return (f.astype(F32) - F32(1)) * _per_block(scale_values(blk["d"]), 64, f.shape[1])
     if fmt == "bin":
         bb = blk["b"]
         return (2 * bb.astype(np.int16) - 1).astype(F32) * _per_block(scale_values(blk["d"]), 128, bb.shape[1])
@@ -423,6 +457,41 @@ def _bytes_to_crumbs(by, k):
     for i in range(4):
         out[:, i::4] = (by >> (2 * i)) & 3
     return out
+
+
+def _tern3_bytes(f, d16):
+    """tern3 (R10): fields f [N, K] and scale bits [N, K/64] -> code bytes
+    [N, K/256, 48] and meta bytes [N, K/256, 12]."""
+    n, k = f.shape
+    nb = k // 256
+    g = f.astype(np.uint32).reshape(n, nb, 4, 64)        # [row, block, group s, column]
+    main = g[..., :60].reshape(n, nb, 4, 3, 5, 4)       # [.., s, e, l, j]: column 20e + 4l + j
+    digits = sum(main[..., l, :] * 3 ** l for l in range(5))  # [.., s, e, j]
+    codes = digits.reshape(n, nb, 48).astype(np.uint8)  # byte 12s + 4e + j
+    tail = g[..., 60:]                                  # [.., s, l]: column 60 + l
+    field = sum(tail[:, :, s, :] << (2 * s) for s in range(4))  # [.., l]: byte l, bits 2s
+    scales = _u16_le(d16.reshape(n, nb, 4)).reshape(n, nb, 8)
+    meta = np.concatenate([scales, field.astype(np.uint8)], axis=-1)
+    return codes, meta
+
+
+def _tern3_unbytes(codes, meta, k):
+    """Inverse of ``_tern3_bytes`` for [N, K/256, 48] and [N, K/256, 12] bytes."""
+    n, nb = codes.shape[:2]
+    by = codes.reshape(n, nb, 4, 3, 4).astype(np.uint32)  # [.., s, e, j]
+    main = np.empty((n, nb, 4, 3, 5, 4), dtype=np.uint8)
+    for l in range(5):
+        main[..., l, :] = by % 3
+        by = by // 3
+    if np.any(by):
+        raise ValueError("tern3 code byte above 242")
+    tail = np.empty((n, nb, 4, 4), dtype=np.uint8)      # [.., s, l]
+    for s in range(4):
+        tail[:, :, s, :] = (meta[..., 8:12] >> (2 * s)) & 3
+    if np.any(tail == 3):
+        raise ValueError("tern3 tail field 3")
+    f = np.concatenate([main.reshape(n, nb, 4, 60), tail], axis=-1).reshape(n, k)
+    return f, _le_u16(meta[..., :8].reshape(n, nb, 4, 2)).reshape(n, nb * 4)
 
 
 def _kquant_meta_bytes(blk) -> np.ndarray:
@@ -530,6 +599,8 @@ def pack(fmt: str, blk: dict) -> np.ndarray:
     elif fmt == "tern":
         codes = _crumbs_to_bytes(blk["f"])
         meta = _u16_le(blk["d"])
+    elif fmt == "tern3":
+        codes, meta = _tern3_bytes(blk["f"], blk["d"])
     elif fmt == "bin":
         codes = np.packbits(blk["b"].astype(np.uint8), axis=1, bitorder="little")
         meta = _u16_le(blk["d"])
@@ -572,6 +643,9 @@ def unpack(fmt: str, buf, n: int, k: int) -> dict:
         return {"d": d16, "dmin": dm16, "s": s, "t": t, "n": nn}
     if fmt == "tern":
         return {"d": _le_u16(meta), "f": _bytes_to_crumbs(codes, k)}
+    if fmt == "tern3":
+        f, d16 = _tern3_unbytes(codes.reshape(n, nb, 48), meta, k)
+        return {"d": d16, "f": f}
     if fmt == "bin":
         return {"d": _le_u16(meta), "b": np.unpackbits(codes, axis=1, bitorder="little")[:, :k]}
     if fmt == "bin8":

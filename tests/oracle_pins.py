@@ -158,6 +158,57 @@ def roundtrip_tern_bin(F) -> None:
     np.testing.assert_array_equal(F.dequant("bin", blk), np.where(bits == 1, 1.0, -1.0) * scale)
 
 
+def roundtrip_tern3(F) -> None:
+    """tern3 is lossless: pack -> unpack returns the codes and scales, and the
+    decode is t * d with one scale per 64 weights; every code byte stays
+    within 0..242 and every tail field within 0..2."""
+    n, k = 7, 768
+    codes = workloads.ternary_codes(n, k, seed=10)
+    codes[0] = 1   # all +1: every code byte 242, every tail field 2
+    codes[1] = -1  # all -1: every byte 0
+    sc = workloads.scale_bits_f16((n, k // 64), seed=10, tensor_id=1)
+    blk = F.tern3_from_codes(codes, sc)
+    buf = F.pack("tern3", blk)
+    assert buf.size == n * k * 15 // 64
+    _same(F.unpack("tern3", buf, n, k), blk)
+    scale = np.repeat(sc.view(np.float16).astype(np.float64), 64, axis=1)
+    np.testing.assert_array_equal(F.dequant("tern3", blk), codes * scale)
+    cp = F.codes_plane_size("tern3", n, k)
+    code_rows = F.deinterleave_rows(buf[:cp], n, 3 * 48)
+    meta_rows = F.deinterleave_rows(buf[cp:], n, 3 * 12).reshape(n, 3, 12)
+    assert code_rows.max() <= 242
+    assert np.all(code_rows[0] == 242) and np.all(meta_rows[0, :, 8:] == 0xAA)
+    assert np.all(code_rows[1] == 0) and np.all(meta_rows[1, :, 8:] == 0)
+
+
+def tern3_bytes(F) -> None:
+    """Hand-worked tern3 bytes (reading R10) for one row of 256 weights, all
+    t = -1 (field 0) except:
+      column 0   (group 0, byte 0, digit 0) t = 0  -> byte 0 gets 1
+      column 16  (group 0, byte 0, digit 4) t = +1 -> byte 0 gets 2 * 81, so 163
+      column 117 (group 1, column 53 = 20*2 + 4*3 + 1: byte 12 + 8 + 1 = 21,
+                  digit 3) t = +1 -> byte 21 = 2 * 27 = 54
+      column 63  (group 0, tail column 3: field byte 3, bits 0..1) t = +1
+      column 189 (group 2, tail column 1: field byte 1, bits 4..5) t = 0
+      column 255 (group 3, tail column 3: field byte 3, bits 6..7) t = +1
+    so the field bytes are 00 10 00 82; scales 1.0, 2.0, -0.5 and the
+    smallest fp16 subnormal, little-endian."""
+    t = np.full((1, 256), -1, np.int8)
+    t[0, [0, 189]] = 0
+    t[0, [16, 117, 63, 255]] = 1
+    d16 = np.array([[0x3C00, 0x4000, 0xB800, 0x0001]], np.uint16)
+    buf = F.pack("tern3", F.tern3_from_codes(t, d16))
+    assert buf.size == 60
+    want = np.zeros(48, np.uint8)
+    want[0], want[21] = 163, 54
+    np.testing.assert_array_equal(buf[:48], want)
+    assert list(buf[48:56]) == [0x00, 0x3C, 0x00, 0x40, 0x00, 0xB8, 0x01, 0x00]
+    assert list(buf[56:60]) == [0x00, 0x10, 0x00, 0x82]
+    w = F.dequant("tern3", F.unpack("tern3", buf, 1, 256))
+    assert w[0, 16] == 1.0 and w[0, 117] == 2.0 and w[0, 189] == 0.0 and w[0, 255] == 2.0 ** -24
+    assert w[0, 1] == -1.0 and w[0, 130] == 0.5
+
+
 # ----------------------------------------------------------------------------
 # hand-worked single blocks for the readings R1 and point 3 (Q4_0 ties)
 

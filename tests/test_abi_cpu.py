@@ -75,7 +75,7 @@ P = 0x10000  # fake 16-byte aligned pointer value
     (dict(fmt=0, n=4, k=48, b=1), -2),           # K not a multiple of 32
     (dict(fmt=3, n=4, k=256, b=0), -4),          # B < 1
     (dict(fmt=3, n=4, k=256, b=9), -4),          # B > 8
-    (dict(fmt=8, n=4, k=256, b=1), -1),          # unknown format
+    (dict(fmt=9, n=4, k=256, b=1), -1),          # unknown format
     (dict(fmt=3, n=1 << 31, k=256, b=1), -2),    # N beyond int
     (dict(fmt=-1, n=4, k=256, b=1), -1),
     (dict(fmt=3, n=4, k=256, b=1, w=0), -1),     # null w

@@ -114,6 +114,42 @@ def test_roundtrip_tern_bin():
     P.roundtrip_tern_bin(F)
 
 
+def test_roundtrip_tern3():
+    P.roundtrip_tern3(F)
+
+
+def test_tern3_hand_worked_bytes():
+    P.tern3_bytes(F)
+
+
+def test_tern3_density_matches_page(golden):
+    """tern3 (R10): 48 bytes of base-3 digits (five weights per byte) and 12
+    meta bytes (four fp16 scales, 16 weights in 2-bit fields) per 256 weights
+    give the density the page prints, with its scale group of 64."""
+    printed = {r[0]: float(r[1]) for r in golden("lowbit_ternary_density.txt")}
+    spec = F.SPECS["tern3"]
+    assert spec.bpw == (240 * 8 / 5 + 16 * 2 + 4 * 16) / 256 == printed["bits_per_weight"]
+    assert spec.block // 4 == printed["scale_group"]
+    assert 5 * np.log2(3) <= 8 and 3 ** 5 <= 256  # five base-3 digits fit a byte
+    assert F.packed_size("tern3", 3, 4096) * 8 == 3 * 4096 * 1.875
+
+
+def test_tern3_rejects():
+    with pytest.raises(ValueError):
+        F.tern3_from_codes(np.zeros((1, 128), np.int8), np.zeros((1, 2), np.uint16))
+    with pytest.raises(F.QuantInputError):
+        F.tern3_from_codes(np.full((1, 256), 2, np.int8), np.zeros((1, 4), np.uint16))
+    buf = F.pack("tern3", F.tern3_from_codes(np.zeros((1, 256), np.int8), np.zeros((1, 4), np.uint16)))
+    bad = buf.copy()
+    bad[5] = 243  # not a five-digit base-3 number
+    with pytest.raises(ValueError):
+        F.unpack("tern3", bad, 1, 256)
+    bad = buf.copy()
+    bad[57] = 0x03  # a tail field of 3
+    with pytest.raises(ValueError):
+        F.unpack("tern3", bad, 1, 256)
+
+
 def test_codes_against_stored_scale():
     P.q8_0_codes_against_stored_scale(F)
 

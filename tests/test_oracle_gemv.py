@@ -21,6 +21,8 @@ def test_bruteforce_tiny(fmt, n):
         blk = F.bin_from_codes(workloads.binary_codes(n, k, 1), workloads.scale_bits_f16((n, k // 128), 1))
     elif fmt == "bin8":
         blk = F.bin8_from_codes(workloads.binary_codes(n, k, 1), workloads.scale_bits_f16((n, k // 128), 1))
+    elif fmt == "tern3":
+        blk = F.tern3_from_codes(workloads.ternary_codes(n, k, 1), workloads.scale_bits_f16((n, k // 64), 1))
     else:
         blk = F.quantize(fmt, workloads.student_t_weights(n, k, 1))
     w = F.dequant(fmt, blk)

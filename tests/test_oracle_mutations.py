@@ -70,6 +70,18 @@ FORMAT_MUTANTS = [
     ("bin8 codes floored", [("np.clip(np.rint((d - base[:, None]) / step[:, None]), 0, 255)",
                              "np.clip(np.floor((d - base[:, None]) / step[:, None]), 0, 255)")], "bin8"),
     ("bin8 base from the max", [("base = d.min(axis=1)", "base = d.max(axis=1)")], "bin8"),
+    ("tern3 digits most significant first",
+     [("main[..., l, :] * 3 ** l for l in range(5)", "main[..., l, :] * 3 ** (4 - l) for l in range(5)")], "tern3"),
+    ("tern3 byte holds five consecutive columns",
+     [("main = g[..., :60].reshape(n, nb, 4, 3, 5, 4)", "main = g[..., :60].reshape(n, nb, 4, 3, 4, 5).swapaxes(-1, -2)")],
+     "tern3"),
+    ("tern3 tail field transposed",
+     [("field = sum(tail[:, :, s, :] << (2 * s) for s in range(4))",
+       "field = sum(tail[:, :, :, s] << (2 * s) for s in range(4))")], "tern3"),
+    ("tern3 field offset 0", [("(f.astype(F32) - F32(1))", "f.astype(F32)")], "tern3"),
+    ("tern3 scales after the field",
+     [("meta = np.concatenate([scales, field.astype(np.uint8)], axis=-1)",
+       "meta = np.concatenate([field.astype(np.uint8), scales], axis=-1)")], "tern3"),
 ]
 
 MOE_MUTANTS = [
@@ -112,6 +124,8 @@ def _run_format_pin(kind, mod, page_w, printed):
     elif kind == "bin8":
         P.bin8_affine_exact(mod)
         P.bin8_rounding_bound(mod)
+    elif kind == "tern3":
+        P.tern3_bytes(mod)
     else:
         raise KeyError(kind)
 

@@ -64,6 +64,31 @@ def test_bin8_packer_identical(n, k):
     np.testing.assert_array_equal(qg.qpack_bin8(bits, sc), OF.pack("bin8", OF.bin8_from_codes(bits, sc)))
 
 
+@pytest.mark.parametrize("n,k", [(9, 256), (17, 768), (40, 4096), (3, 256 * 70)])
+def test_tern3_packer_identical(n, k):
+    """The C++ tern3 packer (base-3 bytes, 2-bit tail fields, per-64 scales)
+    against the oracle's, byte for byte: ragged groups, code and meta rows
+    with and without a short unit, rows of all -1 and all +1."""
+    codes = workloads.ternary_codes(n, k, seed=k, tensor_id=3)
+    codes[0] = 1
+    codes[-1] = -1
+    sc = workloads.scale_bits_f16((n, k // 64), seed=k, tensor_id=4)
+    np.testing.assert_array_equal(qg.qpack_tern3(codes, sc), OF.pack("tern3", OF.tern3_from_codes(codes, sc)))
+
+
+def test_tern3_packer_errors():
+    with pytest.raises(qg.QGError) as e:
+        qg.qpack_tern3(np.full((1, 256), -2, np.int8), np.zeros((1, 4), np.uint16))
+    assert e.value.code == -1 and "(0, 0)" in e.value.detail
+    with pytest.raises(qg.QGError) as e:
+        qg.qquant("tern3", np.zeros((1, 256), np.float32))
+    assert e.value.code == -1
+    with pytest.raises(ValueError):
+        qg.qpack_tern3(np.zeros((1, 128), np.int8), np.zeros((1, 2), np.uint16))   # K not a multiple of 256
+    with pytest.raises(ValueError):
+        qg.qpack_tern3(np.zeros((1, 256), np.int8), np.zeros((1, 2), np.uint16))   # scales per 128, not 64
+
+
 def test_quantizer_errors():
     w = np.ones((2, 256), np.float32)
     w[1, 3] = np.inf
