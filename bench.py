@@ -16,7 +16,7 @@ launch; p10 and p90 of the per-launch time come from the same samples.
 Also reported: the measured HBM read peak (a 4 GiB streaming read) and the
 headline's fraction of it, a same-size read, every GEMV of the four-format
 comparison (Q8_0/Q4_0/Q4_1/Q4_K x 4096x4096/14336x4096 x batch 1/8), the
-low-bit formats (tern/bin/bin8/Q2_K, batch 1/4) with their fraction of the
+low-bit formats (tern/bin/bin8/Q2_K/tern3, batch 1/4) with their fraction of the
 VALU peak where VALU counters were taken, the shapes of the 8B step and one
 larger matrix (57344x4096), the split-K launches against the single pass,
 the RMS-normalising GEMVs, the 8B decode step and the MoE layer.
@@ -61,7 +61,7 @@ KERNEL_SOURCES = {"kernel_source_sha256_16": os.path.join(CSRC, "gemv.hip"),
 
 FOUR_FORMATS = [(fmt, n, k, b) for fmt in ("q8_0", "q4_0", "q4_1", "q4_k")
                 for n, k in ((4096, 4096), (14336, 4096)) for b in (1, 8)]
-LOW_BIT = [(fmt, n, k, b) for fmt in ("tern", "bin", "bin8", "q2_k")
+LOW_BIT = [(fmt, n, k, b) for fmt in ("tern", "bin", "bin8", "q2_k", "tern3")
            for n, k in ((4096, 4096), (12288, 4096), (4096, 12288)) for b in (1, 4)]
 # row-starved shapes at batch 3-8, with the split-K workspace and without
 SPLIT_K = [("q4_k", 1024, 4096, b) for b in (3, 5, 8)] + [(f, 1024, 4096, 8) for f in ("q8_0", "q2_k", "tern")] + \
@@ -182,6 +182,9 @@ def packed_matrix(qg, fmt, n, k, seed):
         if fmt == "tern":
             packed = qg.qpack_tern(workloads.ternary_codes(n, k, seed, 1),
                                    workloads.scale_bits_f16((n, k // 128), seed, 2))
+        elif fmt == "tern3":
+            packed = qg.qpack_tern3(workloads.ternary_codes(n, k, seed, 1),
+                                    workloads.scale_bits_f16((n, k // 64), seed, 2))
         elif fmt in ("bin", "bin8"):
             pack = qg.qpack_bin if fmt == "bin" else qg.qpack_bin8
             packed = pack(workloads.binary_codes(n, k, seed, 1), workloads.scale_bits_f16((n, k // 128), seed, 2))

@@ -138,6 +138,40 @@ dequant_kernel(const uint8_t* __restrict__ codes, const uint8_t* __restrict__ me
     }
 }
 
+// tern3: one thread per (row, 64-weight group): its three code dwords, its
+// scale and its block's tail field.
+__global__ void __launch_bounds__(256)
+dequant_tern3_kernel(const uint8_t* __restrict__ codes, const uint8_t* __restrict__ meta,
+                     float* __restrict__ out, int N, int K) {
+    const int ng = K / 64;                        // groups per row
+    const int row_codes = 12 * ng, row_meta = 3 * ng;
+    const int64_t id = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (id >= (int64_t)N * ng) return;
+    const int row = (int)(id / ng), c = (int)(id - (int64_t)row * ng);
+    const int g = row / kRowGroup, r = row - g * kRowGroup;
+    const int n_g = min(kRowGroup, N - g * kRowGroup);
+    const uint8_t* gc = codes + (size_t)g * kRowGroup * row_codes;
+    const uint8_t* gm = meta + (size_t)g * kRowGroup * row_meta;
+    const int blk = c >> 2, s = c & 3;
+    const float d = h2f(meta_u16(gm, n_g, r, 12 * blk + 2 * s, row_meta));
+    const uint32_t field = meta_u16(gm, n_g, r, 12 * blk + 8, row_meta) |
+                           (meta_u16(gm, n_g, r, 12 * blk + 10, row_meta) << 16);
+    float* o = out + (size_t)row * K + (size_t)c * 64;
+#pragma unroll
+    for (int e = 0; e < 3; ++e) {
+        const int off = 12 * c + 4 * e;  // never crosses a 16-byte unit; code rows have no short unit
+        const uint32_t v = *(const uint32_t*)(gc + ((size_t)(off >> 4) * n_g + r) * 16 + (off & 15));
+        float w[20];
+        tern3_digits(v, w);
+#pragma unroll
+        for (int i = 0; i < 20; ++i) o[20 * e + i] = (512.0f * w[i] - 1.0f) * d;  // exact: back to f - 1
+    }
+    float w[4];
+    tern3_tail(field, s, w);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) o[60 + i] = (512.0f * w[i] - 1.0f) * d;
+}
+
 // ---------------------------------------------------------------- launchers
 
 }  // namespace
@@ -191,6 +225,12 @@ hipError_t launch_dequant(int fmt, const uint8_t* codes, const uint8_t* meta, fl
         case QG_Q2_K: return launch_dequant_f<QG_Q2_K>(codes, meta, out, N, K, st);
         case QG_TERN: return launch_dequant_f<QG_TERN>(codes, meta, out, N, K, st);
         case QG_BIN8: return launch_dequant_f<QG_BIN8>(codes, meta, out, N, K, st);
+        case QG_TERN3: {
+            const int64_t n = (int64_t)N * (K / 64);
+            hipLaunchKernelGGL(dequant_tern3_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, codes,
+                               meta, out, N, K);
+            return hipGetLastError();
+        }
         default: return launch_dequant_f<QG_BIN>(codes, meta, out, N, K, st);
     }
 }
@@ -218,7 +258,6 @@ int splitk_parts(int64_t N, int64_t K, int B) {
 int check_gemv_args(int fmt, const void* w, const float* x, const float* y, int64_t N, int64_t K, int B) {
     int rc = check_matrix(fmt, N, K);
     if (rc) return rc;
-    if (fmt == QG_TERN3) return fail(QG_EUNSUPPORTED, "no TERN3 kernel in this build");
     if (!w || !x || !y) return fail(QG_EINVAL, "null w, x or y");
     if (B < 1 || B > QG_MAX_BATCH) return fail(QG_ERANGE, "B=%d must be in [1, %d]", B, QG_MAX_BATCH);
     // offsets inside a 16-row group are 32-bit
@@ -291,7 +330,6 @@ int qg_dequant(int fmt, const void* w, float* out, int64_t N, int64_t K, void* s
     clear_error();
     int rc = check_matrix(fmt, N, K);
     if (rc) return rc;
-    if (fmt == QG_TERN3) return fail(QG_EUNSUPPORTED, "no TERN3 kernel in this build");
     if (!w || !out) return fail(QG_EINVAL, "null w or out");
     if (!aligned(w, 16)) return fail(QG_EALIGN, "w must be 16-byte aligned");
     if (!aligned(out, 4)) return fail(QG_EALIGN, "out must be 4-byte aligned");

@@ -29,6 +29,10 @@ template <> struct Fmt<QG_Q2_K> { static constexpr int CPC = 64,  MBU = 4, GS = 
 template <> struct Fmt<QG_TERN> { static constexpr int CPC = 64,  MBU = 1, GS = 64,  BLOCK = 128, CB = 32,  MB = 2; };
 template <> struct Fmt<QG_BIN>  { static constexpr int CPC = 128, MBU = 2, GS = 128, BLOCK = 128, CB = 16,  MB = 2; };
 template <> struct Fmt<QG_BIN8> { static constexpr int CPC = 128, MBU = 1, GS = 128, BLOCK = 128, CB = 16,  MB = 1; };
+// tern3: a "unit" is one 64-weight scale group (12 code bytes, its scale and
+// its four tail fields); the code bytes of a 256-weight block fill three
+// 16-byte units, which a lane part reads whole (4 groups) or by halves (2)
+template <> struct Fmt<QG_TERN3> { static constexpr int CPC = 64, MBU = 3, GS = 64,  BLOCK = 256, CB = 48,  MB = 12; };
 
 __device__ __forceinline__ float h2f(uint32_t bits16) {
     return (float)__builtin_bit_cast(_Float16, (uint16_t)bits16);
@@ -127,6 +131,35 @@ template <> struct Unit<QG_BIN> {
 };
 
 template <> struct Unit<QG_BIN8> : Unit<QG_BIN> {};
+
+// tern3: the five base-3 digits of each byte of a code dword, digit l of byte
+// j to w[4l + j] (the group's column 20e + 4l + j for code dword e), as
+// e4m3 values n * 2^-9.  Bytes 0, 2 and 1, 3 ride in the two 16-bit halves
+// of a register each (packed 16-bit integer arithmetic), and
+// floor(b / 3) = (171 b) >> 9 exactly for b <= 255.
+typedef unsigned short u16x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ void tern3_digits(uint32_t v, float* w) {
+    u16x2_t lo = __builtin_bit_cast(u16x2_t, v & 0x00FF00FFu);
+    u16x2_t hi = __builtin_bit_cast(u16x2_t, (v >> 8) & 0x00FF00FFu);
+#pragma unroll
+    for (int l = 0; l < 4; ++l) {
+        const u16x2_t ql = (lo * (unsigned short)171) >> (unsigned short)9;
+        const u16x2_t qh = (hi * (unsigned short)171) >> (unsigned short)9;
+        const uint32_t d = __builtin_bit_cast(uint32_t, (u16x2_t)(lo - ql * (unsigned short)3)) |
+                           (__builtin_bit_cast(uint32_t, (u16x2_t)(hi - qh * (unsigned short)3)) << 8);
+        fp8x4(opaque(d), w[4 * l], w[4 * l + 1], w[4 * l + 2], w[4 * l + 3]);
+        lo = ql;
+        hi = qh;
+    }
+    const uint32_t d = __builtin_bit_cast(uint32_t, lo) | (__builtin_bit_cast(uint32_t, hi) << 8);
+    fp8x4(opaque(d), w[16], w[17], w[18], w[19]);
+}
+
+// tern3: the four tail columns (60..63) of group i from its block's field,
+// shifted so that group i sits at bits 2i of each byte
+__device__ __forceinline__ void tern3_tail(uint32_t field, int i, float* w) {
+    fp8x4(opaque((field >> (2 * i)) & 0x03030303u), w[0], w[1], w[2], w[3]);
+}
 
 // Weight bytes are read exactly once per call: stream them past the caches.
 #ifndef QG_WEIGHT_NT
@@ -297,6 +330,16 @@ template <> struct Apply<QG_TERN> {
     // f = t + 1:  w = (f - 1) d  ->  d * (512 P - X); unit i is half of block i/2
     __device__ static void unit(const uint32_t* wd, int i, int, float P, float X, KqState&, float& acc, bool ok) {
         const float v = fmaf(meta_h(wd, i >> 1), fmaf(512.0f, P, -X), acc);
+        acc = ok ? v : acc;
+    }
+};
+
+template <> struct Apply<QG_TERN3> {
+    static constexpr int SUBS = 1;
+    // as tern, with one fp16 scale per 64-weight group: the part's scales are
+    // the consecutive halves of wd
+    __device__ static void unit(const uint32_t* wd, int i, int, float P, float X, KqState&, float& acc, bool ok) {
+        const float v = fmaf(meta_h(wd, i), fmaf(512.0f, P, -X), acc);
         acc = ok ? v : acc;
     }
 };
@@ -602,6 +645,7 @@ template <int F> constexpr bool is_kquant() { return F == QG_Q4_K || F == QG_Q2_
 // batches.
 template <int F> constexpr bool dpp_units_ok(int kcs) {
     using T = Fmt<F>;
+    if (F == QG_TERN3) return kcs == 4 || kcs == 2;  // a whole block, or one half of it
     return (kcs * T::CPC) % 64 == 0 &&
            (is_kquant<F>() ? (T::BLOCK / T::CPC) % kcs == 0      // inside one super-block
                            : (kcs * T::CPC) % T::BLOCK == 0) &&  // whole blocks (aligned meta)
@@ -695,7 +739,7 @@ struct GemvDpp {
         const int rr = min(r, n_g - 1);
         const int nb_blocks = K / T::BLOCK;
         const int row_codes = nb_blocks * T::CB, row_meta = nb_blocks * T::MB;
-        const int nch = row_codes >> 4;
+        const int nch = K / CPC;              // code units of a row (tern3: 64-weight groups)
         const int c_end = ce < 0 ? nch : ce;  // this call's units: [cb, c_end)
         const int k_end = c_end * CPC;        // and columns: [cb * CPC, k_end)
         const bool meta_whole = (row_meta & 15) == 0;
@@ -776,7 +820,42 @@ struct GemvDpp {
                 // (2) meta, then the code units (clamped into the row; units past
                 // its end are dropped by the scale step)
                 uint32_t wd[is_kquant<F>() ? 4 : (MB + 3) / 4];
-                if constexpr (is_kquant<F>()) {
+                uint4 q[F == QG_TERN3 ? 1 : KCS];
+                uint32_t t3[F == QG_TERN3 ? 3 * KCS : 1];  // tern3: the part's code dwords, 3 per group
+                uint32_t t3f = 0;                            // tern3: tail field, group i at bits 2i
+                if constexpr (F == QG_TERN3) {
+                    // a part is a whole block (KCS 4) or one half of it (KCS 2), wholly
+                    // inside the row or wholly past it (then clamped to the last part)
+                    const int ce0 = FULL ? c0 : min(c0, c_end - KCS);
+                    const uint32_t blk = (uint32_t)ce0 >> 2, h = ((uint32_t)ce0 >> 1) & 1u;
+                    const int mo = 12 * (int)blk;  // the block's meta entry in the row's meta bytes
+                    auto meta_dw = [&](int o) -> uint32_t {
+                        if (meta_whole || (o >> 4) < (row_meta >> 4))
+                            return ld_weights<uint32_t>(gm + ((uint32_t)(o >> 4) * ust + rof + (uint32_t)(o & 15)));
+                        uint32_t m1[1];
+                        load_meta<4>(gm, n_g, rr, o, row_meta, m1);
+                        return m1[0];
+                    };
+                    if constexpr (KCS == 4) {
+#pragma unroll
+                        for (int u = 0; u < 3; ++u) {
+                            const uint4 v = ld_weights<uint4>(gc + ((3 * blk + u) * ust + rof));
+                            t3[4 * u] = v.x; t3[4 * u + 1] = v.y; t3[4 * u + 2] = v.z; t3[4 * u + 3] = v.w;
+                        }
+                        wd[0] = meta_dw(mo);
+                        wd[1] = meta_dw(mo + 4);
+                        t3f = meta_dw(mo + 8);
+                    } else {
+                        // half h: code dwords 6h .. 6h+5 of the block, i.e. unit 2h whole
+                        // and the half h of unit 1
+                        const uint4 a = ld_weights<uint4>(gc + ((3 * blk + 2 * h) * ust + rof));
+                        const uint2 b = ld_weights<uint2>(gc + ((3 * blk + 1) * ust + rof + 8 * h));
+                        t3[0] = h ? b.x : a.x; t3[1] = h ? b.y : a.y; t3[2] = h ? a.x : a.z;
+                        t3[3] = h ? a.y : a.w; t3[4] = h ? a.z : b.x; t3[5] = h ? a.w : b.y;
+                        wd[0] = meta_dw(mo + 4 * (int)h);
+                        t3f = meta_dw(mo + 8) >> (4 * h);
+                    }
+                } else if constexpr (is_kquant<F>()) {
                     const int sbi = c0 / UPS, uo = c0 % UPS;
                     const uint32_t u = (uint32_t)(FULL ? sbi : min(sbi, (c_end - 1) / UPS));
                     const uint4 v = ld_weights<uint4>(gm + (u * ust + rof));
@@ -806,11 +885,12 @@ struct GemvDpp {
                     }
                     if constexpr (F == QG_BIN8) wx[0] = wd[0];
                 }
-                uint4 q[KCS];
+                if constexpr (F != QG_TERN3) {
 #pragma unroll
-                for (int i = 0; i < KCS; ++i) {
-                    const uint32_t u = (uint32_t)(FULL ? c0 + i : min(c0 + i, c_end - 1));
-                    q[i] = ld_weights<uint4>(gc + (u * ust + rof));
+                    for (int i = 0; i < KCS; ++i) {
+                        const uint32_t u = (uint32_t)(FULL ? c0 + i : min(c0 + i, c_end - 1));
+                        q[i] = ld_weights<uint4>(gc + (u * ust + rof));
+                    }
                 }
 
                 // (3) column-sum spans of every batch row
@@ -830,6 +910,42 @@ struct GemvDpp {
                 static_for<KCS>([&](auto I) {
                     constexpr int i = decltype(I)::value;
                     const bool ok = i < nvalid;
+                    if constexpr (F == QG_TERN3) {
+                        // group i: three code dwords of 20 columns, then the four tail columns
+                        float ps[B];
+                        if constexpr (B >= 3) {
+                            static_for<3>([&](auto E) {
+                                constexpr int e = decltype(E)::value;
+                                float w[20];
+                                tern3_digits(t3[3 * i + e], w);
+                                fma_cols_batched<i * CPC + 20 * e, 20, NX4, B, e == 0, WIDE>(ps, xv, w);
+                            });
+                            float w[4];
+                            tern3_tail(t3f, i, w);
+                            fma_cols_batched<i * CPC + 60, 4, NX4, B, false, WIDE>(ps, xv, w);
+                        } else {
+                            float pa[B][4];  // started by the first column block's multiplies
+                            static_for<3>([&](auto E) {
+                                constexpr int e = decltype(E)::value;
+                                float w[20];
+                                tern3_digits(t3[3 * i + e], w);
+                                static_for<5>([&](auto G) {
+                                    constexpr int c = 20 * e + 4 * decltype(G)::value;
+#pragma unroll
+                                    for (int b = 0; b < B; ++b)
+                                        fma_cols<i * CPC + c, 4, NX4, c == 0>(pa[b], xv[b], w + (c - 20 * e));
+                                });
+                            });
+                            float w[4];
+                            tern3_tail(t3f, i, w);
+#pragma unroll
+                            for (int b = 0; b < B; ++b) fma_cols<i * CPC + 60, 4, NX4, false>(pa[b], xv[b], w);
+#pragma unroll
+                            for (int b = 0; b < B; ++b) ps[b] = (pa[b][0] + pa[b][1]) + (pa[b][2] + pa[b][3]);
+                        }
+#pragma unroll
+                        for (int b = 0; b < B; ++b) A::unit(wd, i, 0, ps[b], col_sum<i * CPC>(gs[b]), st[b], acc[b], ok);
+                    } else {
                     const uint32_t dw[4] = {q[i].x, q[i].y, q[i].z, q[i].w};
                     static_for<SUBS>([&](auto S) {
                         constexpr int s = decltype(S)::value;
@@ -869,6 +985,7 @@ struct GemvDpp {
                             }
                         }
                     });
+                    }
                     __builtin_amdgcn_sched_barrier(0);
                 });
                 if constexpr (is_kquant<F>()) {
@@ -948,7 +1065,7 @@ constexpr int dpp_max_waves() {
 // slices.
 template <int F, int KCS>
 int pick_waves_dpp(int K, int max_w = 16) {
-    const int nch = K / Fmt<F>::BLOCK * Fmt<F>::CB / 16;
+    const int nch = K / Fmt<F>::CPC;
     int w = 1;
     while (w < max_w && 4 * w * KCS < nch) w *= 2;
     return w;

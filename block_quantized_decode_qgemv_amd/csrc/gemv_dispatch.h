@@ -94,6 +94,7 @@ hipError_t launch_dpp(int fmt, int N, int K, int B, hipStream_t st, Args... args
         case QG_Q2_K: return launch_dpp_f<KS, QG_Q2_K>(N, K, B, st, args...);
         case QG_TERN: return launch_dpp_f<KS, QG_TERN>(N, K, B, st, args...);
         case QG_BIN8: return launch_dpp_f<KS, QG_BIN8>(N, K, B, st, args...);
+        case QG_TERN3: return launch_dpp_f<KS, QG_TERN3>(N, K, B, st, args...);
         default: return launch_dpp_f<KS, QG_BIN>(N, K, B, st, args...);
     }
 }

@@ -71,6 +71,7 @@ int unit_columns(int fmt) {
         case QG_Q2_K: return Fmt<QG_Q2_K>::CPC;
         case QG_TERN: return Fmt<QG_TERN>::CPC;
         case QG_BIN8: return Fmt<QG_BIN8>::CPC;
+        case QG_TERN3: return Fmt<QG_TERN3>::CPC;
         default: return Fmt<QG_BIN>::CPC;
     }
 }

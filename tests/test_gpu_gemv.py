@@ -31,6 +31,9 @@ def make_blocks(fmt, n, k, seed=0, tid=0):
     if fmt == "bin8":
         return OF.bin8_from_codes(workloads.binary_codes(n, k, seed, tid),
                                   workloads.scale_bits_f16((n, k // 128), seed, tid + 1))
+    if fmt == "tern3":
+        return OF.tern3_from_codes(workloads.ternary_codes(n, k, seed, tid),
+                                   workloads.scale_bits_f16((n, k // 64), seed, tid + 1))
     return OF.quantize(fmt, workloads.student_t_weights(n, k, seed, tid))
 
 
@@ -159,6 +162,19 @@ def test_gemv_odd_unit_counts(fmt, k, b):
     assert_parity(y, OF.dequant(fmt, blk), x, f"{fmt} B={b} K={k}")
 
 
+@pytest.mark.parametrize("k", [256, 768, 1280, 2304, 4352])
+@pytest.mark.parametrize("b", [1, 2, 3, 5, 8])
+def test_tern3_odd_block_counts(k, b):
+    """tern3 at K = 256 * odd: rows of whole-block parts (batch 1, 2) and of
+    half-block parts (batch 3 and up) that end inside a slice, and meta rows
+    (12 bytes per block) ending in a short unit."""
+    n = 37
+    blk = make_blocks("tern3", n, k, seed=14, tid=k + b)
+    x = workloads.normal((b, k), 14, k + b)
+    y = run_gemv("tern3", OF.pack("tern3", blk), x, n, k)
+    assert_parity(y, OF.dequant("tern3", blk), x, f"tern3 B={b} K={k}")
+
+
 @pytest.mark.parametrize("fmt", OF.FORMATS)
 def test_gemv_integer_exact(fmt):
     """Power-of-two scales and small-integer activations: every product and
@@ -212,8 +228,8 @@ def full_weights(n, k):
 
 @functools.lru_cache(maxsize=4)
 def full_low_bit_codes(fmt, n, k):
-    gen = workloads.ternary_codes if fmt == "tern" else workloads.binary_codes
-    return gen(n, k, 11, n), workloads.scale_bits_f16((n, k // 128), 11, n + 1)
+    gen = workloads.ternary_codes if fmt in ("tern", "tern3") else workloads.binary_codes
+    return gen(n, k, 11, n), workloads.scale_bits_f16((n, k // (64 if fmt == "tern3" else 128)), 11, n + 1)
 
 
 def sampled_rows(n, salt):
@@ -260,7 +276,7 @@ def test_full_size_sampled_rows(fmt, n, k, b):
 
 
 @pytest.mark.parametrize("n,k", [(12288, 4096), (4096, 12288)])
-@pytest.mark.parametrize("fmt", ["q2_k", "tern", "bin", "bin8"])
+@pytest.mark.parametrize("fmt", ["q2_k", "tern", "bin", "bin8", "tern3"])
 @pytest.mark.parametrize("b", [1, 4, 8])
 def test_full_size_low_bit_sampled_rows(fmt, n, k, b):
     """The low-bit formats at the bench's full sizes: Q2_K from the C++
@@ -281,6 +297,9 @@ def test_full_size_low_bit_sampled_rows(fmt, n, k, b):
         elif fmt == "bin":
             packed = qg.qpack_bin(codes, scales)
             sub = OF.bin_from_codes(codes[rows], scales[rows])
+        elif fmt == "tern3":
+            packed = qg.qpack_tern3(codes, scales)
+            sub = OF.tern3_from_codes(codes[rows], scales[rows])
         else:
             packed = qg.qpack_bin8(codes, scales)
             sub = OF.bin8_from_codes(codes[rows], scales[rows])
@@ -300,7 +319,8 @@ def test_decode_step_shapes_sampled_rows(n, k):
 
 
 ALIASES = {"q8_0": "qgemv_q8_0", "q4_0": "qgemv_q4_0", "q4_1": "qgemv_q4_1", "q4_k": "qgemv_q4k",
-           "q2_k": "qgemv_q2k", "tern": "qgemv_tern", "bin": "qgemv_bin", "bin8": "qgemv_bin8"}
+           "q2_k": "qgemv_q2k", "tern": "qgemv_tern", "bin": "qgemv_bin", "bin8": "qgemv_bin8",
+           "tern3": "qgemv_tern3"}
 
 
 @pytest.mark.parametrize("fmt", OF.FORMATS)

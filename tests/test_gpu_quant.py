@@ -89,7 +89,7 @@ def test_quant_device_reports_errors(fmt):
 
 
 @pytest.mark.parametrize("src,dst", [("q4_k", "q2_k"), ("q8_0", "q4_0"), ("q4_1", "q4_k"), ("tern", "q8_0"),
-                                     ("bin", "q4_1"), ("q2_k", "q4_k")])
+                                     ("bin", "q4_1"), ("q2_k", "q4_k"), ("tern3", "q2_k")])
 def test_requant_bit_exact(src, dst):
     n, k = 45, 1024
     blk = make_blocks(src, n, k, seed=34, tid=n)
