@@ -133,7 +133,7 @@ template <> struct Unit<QG_BIN> {
 template <> struct Unit<QG_BIN8> : Unit<QG_BIN> {};
 
 // tern3: the five base-3 digits of each byte of a code dword, digit l of byte
-// j to w[4l + j] (the group's column 20e + 4l + j for code dword e), as
+// j to w[5j + l] (the group's column 20e + 5j + l for code dword e), as
 // e4m3 values n * 2^-9.  Bytes 0, 2 and 1, 3 ride in the two 16-bit halves
 // of a register each (packed 16-bit integer arithmetic), and
 // floor(b / 3) = (171 b) >> 9 exactly for b <= 255.
@@ -147,12 +147,43 @@ __device__ __forceinline__ void tern3_digits(uint32_t v, float* w) {
         const u16x2_t qh = (hi * (unsigned short)171) >> (unsigned short)9;
         const uint32_t d = __builtin_bit_cast(uint32_t, (u16x2_t)(lo - ql * (unsigned short)3)) |
                            (__builtin_bit_cast(uint32_t, (u16x2_t)(hi - qh * (unsigned short)3)) << 8);
-        fp8x4(opaque(d), w[4 * l], w[4 * l + 1], w[4 * l + 2], w[4 * l + 3]);
+        fp8x4(opaque(d), w[l], w[5 + l], w[10 + l], w[15 + l]);
         lo = ql;
         hi = qh;
     }
     const uint32_t d = __builtin_bit_cast(uint32_t, lo) | (__builtin_bit_cast(uint32_t, hi) << 8);
-    fp8x4(opaque(d), w[16], w[17], w[18], w[19]);
+    fp8x4(opaque(d), w[4], w[9], w[14], w[19]);
+}
+
+// tern3 with a decode table (the GEMV's default): entry b holds the five
+// base-3 digits of b as e4m3 bytes (digits 0..3 in .x, digit 4 in byte 0 of
+// .y), so a code byte costs one LDS read and three conversions instead of
+// the arithmetic above (about 1 against 2 VALU operations per weight; batch
+// 1 measured 14-18 % faster at 12288-14336 x 4096 and 4096 x 12288).  Every
+// byte value has an entry (243..255 never occur in packed data), so no read
+// leaves the table.  QG_TERN3_LUT=0 builds the arithmetic decode instead.
+#ifndef QG_TERN3_LUT
+#define QG_TERN3_LUT 1
+#endif
+constexpr int kTern3Lut = 256;
+__device__ __forceinline__ void tern3_lut_build(uint2* lut, int tid, int nt) {
+    for (int b = tid; b < kTern3Lut; b += nt) {
+        uint32_t x = (uint32_t)b, lo = 0;
+#pragma unroll
+        for (int l = 0; l < 4; ++l) {
+            lo |= (x % 3u) << (8 * l);
+            x /= 3u;
+        }
+        lut[b] = make_uint2(lo, x);
+    }
+}
+__device__ __forceinline__ void tern3_digits_lut(uint32_t v, const uint2* lut, float* w) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const uint2 e = lut[(v >> (8 * j)) & 0xFFu];
+        fp8x4(e.x, w[5 * j], w[5 * j + 1], w[5 * j + 2], w[5 * j + 3]);
+        w[5 * j + 4] = __builtin_amdgcn_cvt_f32_fp8((int)e.y, 0);
+    }
 }
 
 // tern3: the four tail columns (60..63) of group i from its block's field,
@@ -758,6 +789,14 @@ struct GemvDpp {
             wx[1] = __float_as_uint(ab.x);
             wx[2] = __float_as_uint(ab.y);
         }
+        // tern3 decode table (one per workgroup, built before the first slice)
+        [[maybe_unused]] uint2* t3lut = nullptr;
+        if constexpr (F == QG_TERN3 && QG_TERN3_LUT) {
+            __shared__ uint2 lut[kTern3Lut];
+            tern3_lut_build(lut, threadIdx.x, blockDim.x);
+            __syncthreads();
+            t3lut = lut;
+        }
         float acc[B], ss[B];  // row sums; sums of x^2 (NORM)
 #pragma unroll
         for (int b = 0; b < B; ++b) acc[b] = ss[b] = 0.0f;
@@ -917,7 +956,8 @@ struct GemvDpp {
                             static_for<3>([&](auto E) {
                                 constexpr int e = decltype(E)::value;
                                 float w[20];
-                                tern3_digits(t3[3 * i + e], w);
+                                if constexpr (QG_TERN3_LUT) tern3_digits_lut(t3[3 * i + e], t3lut, w);
+                                else tern3_digits(t3[3 * i + e], w);
                                 fma_cols_batched<i * CPC + 20 * e, 20, NX4, B, e == 0, WIDE>(ps, xv, w);
                             });
                             float w[4];
@@ -928,7 +968,8 @@ struct GemvDpp {
                             static_for<3>([&](auto E) {
                                 constexpr int e = decltype(E)::value;
                                 float w[20];
-                                tern3_digits(t3[3 * i + e], w);
+                                if constexpr (QG_TERN3_LUT) tern3_digits_lut(t3[3 * i + e], t3lut, w);
+                                else tern3_digits(t3[3 * i + e], w);
                                 static_for<5>([&](auto G) {
                                     constexpr int c = 20 * e + 4 * decltype(G)::value;
 #pragma unroll

@@ -420,13 +420,12 @@ int qpack_tern3(const int8_t* t, const uint16_t* scale_f16, int64_t N, int64_t K
                 uint32_t field = 0;
                 for (int s = 0; s < 4; ++s) {
                     const int8_t* ts = tr + 256 * b + 64 * s;  // one 64-weight scale group
-                    // byte 4e + j: the base-3 digits of columns 20e + 4l + j, l = 0..4 (digit l has weight 3^l)
-                    for (int e = 0; e < 3; ++e)
-                        for (int j = 0; j < 4; ++j) {
-                            unsigned v = 0;
-                            for (int l = 4; l >= 0; --l) v = 3 * v + (unsigned)(ts[20 * e + 4 * l + j] + 1);
-                            cb[12 * s + 4 * e + j] = (uint8_t)v;
-                        }
+                    // byte m: the base-3 digits of columns 5m .. 5m + 4 (column 5m + l has weight 3^l)
+                    for (int m = 0; m < 12; ++m) {
+                        unsigned v = 0;
+                        for (int l = 4; l >= 0; --l) v = 3 * v + (unsigned)(ts[5 * m + l] + 1);
+                        cb[12 * s + m] = (uint8_t)v;
+                    }
                     // columns 60..63: 2-bit fields, field byte l at bits 2s
                     for (int l = 0; l < 4; ++l) field |= (uint32_t)(ts[60 + l] + 1) << (8 * l + 2 * s);
                     put_u16(mb + 2 * s, scale_f16[(size_t)r * (K / 64) + 4 * b + s]);

@@ -54,8 +54,8 @@
  *                                           32-bit field of 2-bit codes
  *   TERN3 (the low-bit page's lossless base-3 ternary with a scale per 64
  *   weights, kernel table, ternary Q2_0 row): f = t + 1 as for TERN; for the
- *   64-weight group s of a block, code byte 12s + 4e + j (e < 3, j < 4) is
- *   sum_{l<5} f(64s + 20e + 4l + j) * 3^l (<= 242), and f(64s + 60 + l) sits
+ *   64-weight group s of a block, code byte 12s + m (m < 12) is
+ *   sum_{l<5} f(64s + 5m + l) * 3^l (<= 242), and f(64s + 60 + l) sits
  *   at bits 2s..2s+1 of byte l of the meta entry's field (bytes 8..11).
  *   BIN8 adds a third plane: the meta plane is zero-padded to a multiple of
  *   16 bytes and followed by N rows of (base, step), two little-endian fp32;

@@ -54,9 +54,9 @@ R10 tern3 is the low-bit page's lossless 1.875-bit form of ternary weights
     fp16 d per 64 weights.  The page gives the density, not the bytes.
     Packing block: 256 weights = four 64-weight scale groups, 48 code bytes
     and 12 meta bytes (1.875 bits per weight).  Codes: for group s of the
-    block, byte 12s + 4e + j (e < 3, j < 4) holds the base-3 number
-    sum_{l<5} f(64s + 20e + 4l + j) * 3^l (at most 242): five weights per
-    byte.  The last four weights of each group (columns 60..63) sit in a
+    block, byte 12s + m (m < 12) holds the base-3 number
+    sum_{l<5} f(64s + 5m + l) * 3^l (at most 242): five consecutive weights
+    per byte, the first in the least significant digit.  The last four weights of each group (columns 60..63) sit in a
     32-bit field at the end of the meta entry: its byte l holds, at bits
     2s..2s+1, f(64s + 60 + l).  Meta entry: the four fp16 scales in group
     order (little-endian), then that field.  So a 64-weight group takes 12
@@ -465,9 +465,9 @@ def _tern3_bytes(f, d16):
     n, k = f.shape
     nb = k // 256
     g = f.astype(np.uint32).reshape(n, nb, 4, 64)        # [row, block, group s, column]
-    main = g[..., :60].reshape(n, nb, 4, 3, 5, 4)       # [.., s, e, l, j]: column 20e + 4l + j
-    digits = sum(main[..., l, :] * 3 ** l for l in range(5))  # [.., s, e, j]
-    codes = digits.reshape(n, nb, 48).astype(np.uint8)  # byte 12s + 4e + j
+    main = g[..., :60].reshape(n, nb, 4, 12, 5)         # [.., s, m, l]: column 5m + l
+    digits = sum(main[..., l] * 3 ** l for l in range(5))  # [.., s, m]
+    codes = digits.reshape(n, nb, 48).astype(np.uint8)  # byte 12s + m
     tail = g[..., 60:]                                  # [.., s, l]: column 60 + l
     field = sum(tail[:, :, s, :] << (2 * s) for s in range(4))  # [.., l]: byte l, bits 2s
     scales = _u16_le(d16.reshape(n, nb, 4)).reshape(n, nb, 8)
@@ -478,10 +478,10 @@ def _tern3_bytes(f, d16):
 def _tern3_unbytes(codes, meta, k):
     """Inverse of ``_tern3_bytes`` for [N, K/256, 48] and [N, K/256, 12] bytes."""
     n, nb = codes.shape[:2]
-    by = codes.reshape(n, nb, 4, 3, 4).astype(np.uint32)  # [.., s, e, j]
-    main = np.empty((n, nb, 4, 3, 5, 4), dtype=np.uint8)
+    by = codes.reshape(n, nb, 4, 12).astype(np.uint32)  # [.., s, m]
+    main = np.empty((n, nb, 4, 12, 5), dtype=np.uint8)
     for l in range(5):
-        main[..., l, :] = by % 3
+        main[..., l] = by % 3
         by = by // 3
     if np.any(by):
         raise ValueError("tern3 code byte above 242")

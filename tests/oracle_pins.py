@@ -185,9 +185,9 @@ def tern3_bytes(F) -> None:
     """Hand-worked tern3 bytes (reading R10) for one row of 256 weights, all
     t = -1 (field 0) except:
       column 0   (group 0, byte 0, digit 0) t = 0  -> byte 0 gets 1
-      column 16  (group 0, byte 0, digit 4) t = +1 -> byte 0 gets 2 * 81, so 163
-      column 117 (group 1, column 53 = 20*2 + 4*3 + 1: byte 12 + 8 + 1 = 21,
-                  digit 3) t = +1 -> byte 21 = 2 * 27 = 54
+      column 4   (group 0, byte 0, digit 4) t = +1 -> byte 0 gets 2 * 81, so 163
+      column 117 (group 1, column 53 = 5 * 10 + 3: byte 12 + 10 = 22,
+                  digit 3) t = +1 -> byte 22 = 2 * 27 = 54
       column 63  (group 0, tail column 3: field byte 3, bits 0..1) t = +1
       column 189 (group 2, tail column 1: field byte 1, bits 4..5) t = 0
       column 255 (group 3, tail column 3: field byte 3, bits 6..7) t = +1
@@ -195,17 +195,17 @@ def tern3_bytes(F) -> None:
     smallest fp16 subnormal, little-endian."""
     t = np.full((1, 256), -1, np.int8)
     t[0, [0, 189]] = 0
-    t[0, [16, 117, 63, 255]] = 1
+    t[0, [4, 117, 63, 255]] = 1
     d16 = np.array([[0x3C00, 0x4000, 0xB800, 0x0001]], np.uint16)
     buf = F.pack("tern3", F.tern3_from_codes(t, d16))
     assert buf.size == 60
     want = np.zeros(48, np.uint8)
-    want[0], want[21] = 163, 54
+    want[0], want[22] = 163, 54
     np.testing.assert_array_equal(buf[:48], want)
     assert list(buf[48:56]) == [0x00, 0x3C, 0x00, 0x40, 0x00, 0xB8, 0x01, 0x00]
     assert list(buf[56:60]) == [0x00, 0x10, 0x00, 0x82]
     w = F.dequant("tern3", F.unpack("tern3", buf, 1, 256))
-    assert w[0, 16] == 1.0 and w[0, 117] == 2.0 and w[0, 189] == 0.0 and w[0, 255] == 2.0 ** -24
+    assert w[0, 4] == 1.0 and w[0, 117] == 2.0 and w[0, 189] == 0.0 and w[0, 255] == 2.0 ** -24
     assert w[0, 1] == -1.0 and w[0, 130] == 0.5
 
 

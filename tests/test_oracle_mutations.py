@@ -71,10 +71,10 @@ FORMAT_MUTANTS = [
                              "np.clip(np.floor((d - base[:, None]) / step[:, None]), 0, 255)")], "bin8"),
     ("bin8 base from the max", [("base = d.min(axis=1)", "base = d.max(axis=1)")], "bin8"),
     ("tern3 digits most significant first",
-     [("main[..., l, :] * 3 ** l for l in range(5)", "main[..., l, :] * 3 ** (4 - l) for l in range(5)")], "tern3"),
-    ("tern3 byte holds five consecutive columns",
-     [("main = g[..., :60].reshape(n, nb, 4, 3, 5, 4)", "main = g[..., :60].reshape(n, nb, 4, 3, 4, 5).swapaxes(-1, -2)")],
-     "tern3"),
+     [("main[..., l] * 3 ** l for l in range(5)", "main[..., l] * 3 ** (4 - l) for l in range(5)")], "tern3"),
+    ("tern3 digits of a byte four columns apart",
+     [("main = g[..., :60].reshape(n, nb, 4, 12, 5)",
+       "main = g[..., :60].reshape(n, nb, 4, 3, 5, 4).swapaxes(-1, -2).reshape(n, nb, 4, 12, 5)")], "tern3"),
     ("tern3 tail field transposed",
      [("field = sum(tail[:, :, s, :] << (2 * s) for s in range(4))",
        "field = sum(tail[:, :, :, s] << (2 * s) for s in range(4))")], "tern3"),
