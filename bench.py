@@ -655,6 +655,7 @@ def summarize(kind, paths, commands):
         scale = (1 << 30) / 1024 / copy_fetch
         fb = float(np.median(fetch)) * 1024 * scale
         lines = _header("HBM streaming-read peak: the library's read probe over one 4 GiB buffer", commands)
+        lines.append(f"probe_source_sha256_16: {source_hash(os.path.join(CSRC, 'probe.hip'))}")
         lines += [f"dispatches_traced: {len(dur)}", f"duration_ns_median: {np.median(dur):.0f}",
                   f"duration_ns_p10: {np.percentile(dur, 10):.0f}", f"duration_ns_p90: {np.percentile(dur, 90):.0f}",
                   f"fetch_kib_per_dispatch_median: {np.median(fetch):.1f}",
