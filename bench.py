@@ -589,7 +589,7 @@ def environment(torch) -> dict:
         env["git_rev"] = subprocess.run(["git", "-C", ROOT, "rev-parse", "--short=12", "HEAD"], capture_output=True,
                                         text=True, check=True, timeout=10).stdout.strip()
     except Exception:
-        env["git_rev"] = None  # the GPU machine gets the tree without .git; the source hashes identify it
+        env["git_rev"] = None  # a copy of the tree without .git; the source hashes identify the kernels
     env.update({key: source_hash(path) for key, path in KERNEL_SOURCES.items()})
     return env
 
