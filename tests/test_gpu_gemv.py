@@ -338,7 +338,7 @@ def test_per_format_entry_points_match_qgemv(fmt):
 
 
 @pytest.mark.parametrize("fmt,n,k,b", [("q4_k", 57344, 4096, 1), ("q8_0", 64, 65536, 2), ("q4_k", 48, 131072, 3),
-                                       ("bin8", 40, 65536, 8)])
+                                       ("bin8", 40, 65536, 8), ("tern3", 40, 65536, 8), ("tern3", 24, 131072, 1)])
 def test_large_shapes(fmt, n, k, b):
     """Far beyond the bench's shapes: 57344 rows (3584 row groups, several
     rounds of workgroups per compute unit) and K up to 131072 (many K slices
@@ -349,6 +349,11 @@ def test_large_shapes(fmt, n, k, b):
         packed = qg.qpack_bin8(bits, sc)
         rows = np.arange(n)
         sub = OF.bin8_from_codes(bits, sc)
+    elif fmt == "tern3":
+        codes, sc = workloads.ternary_codes(n, k, 37, 1), workloads.scale_bits_f16((n, k // 64), 37, 2)
+        packed = qg.qpack_tern3(codes, sc)
+        rows = np.arange(n)
+        sub = OF.tern3_from_codes(codes, sc)
     else:
         w = workloads.student_t_weights(n, k, 37, n)
         packed = qg.qquant(fmt, w, n_threads=16)

@@ -8,15 +8,16 @@ import block_quantized_decode_qgemv_amd as qg
 import workloads
 from oracle import formats as OF
 from oracle import gemv as OG
+from tests.test_gpu_gemv import make_blocks
 
 pytestmark = pytest.mark.gpu
 torch = pytest.importorskip("torch")
 
 
-@pytest.mark.parametrize("fmt", ["q4_k", "q8_0", "q2_k"])
+@pytest.mark.parametrize("fmt", ["q4_k", "q8_0", "q2_k", "tern3"])
 def test_graph_replays_match_eager(fmt):
     n, k, copies = 515, 4096, 3
-    blks = [OF.quantize(fmt, workloads.student_t_weights(n, k, 4, c)) for c in range(copies)]
+    blks = [make_blocks(fmt, n, k, seed=4, tid=c) for c in range(copies)]
     w = [torch.from_numpy(OF.pack(fmt, b)).cuda() for b in blks]
     x = torch.from_numpy(workloads.normal((1, k), 4, 9)).cuda()
     ys = [torch.empty((1, n), device="cuda") for _ in range(copies)]
