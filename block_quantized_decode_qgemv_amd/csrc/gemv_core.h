@@ -753,7 +753,8 @@ struct GemvDpp {
 
     // The same on waves [wave0, wave0 + W) of a larger workgroup, with the
     // cross-wave partials in red (W * 16 * B floats of LDS).  Every wave of the
-    // workgroup must call it (it synchronizes the whole workgroup once).
+    // workgroup must call it (it synchronizes the whole workgroup once; tern3
+    // twice, the first time after the workgroup has built its decode table).
     // NORM, GAMMA: see run_rmsnorm; red_ss holds W * B floats.  [cb, ce):
     // the code units of each row to sum over (ce < 0: to the row's end), for
     // a split of K; cb * CPC must be a multiple of 256 columns (whole

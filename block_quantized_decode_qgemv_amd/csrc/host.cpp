@@ -231,6 +231,15 @@ int quant_row(int fmt, const float* w, int64_t K, uint8_t* codes, uint8_t* meta)
     }
 }
 
+// Codes are validated before anything is written (the packers' error
+// contract): the index of the first value of v[0 .. n) outside [lo, hi], or -1.
+template <typename T>
+int64_t first_out_of_range(const T* v, int64_t n, int lo, int hi) {
+    for (int64_t i = 0; i < n; ++i)
+        if ((int)v[i] < lo || (int)v[i] > hi) return i;
+    return -1;
+}
+
 }  // namespace
 
 const FormatInfo* format_info(int fmt) {
@@ -370,6 +379,8 @@ int qpack_tern(const int8_t* t, const uint16_t* scale_f16, int64_t N, int64_t K,
     int rc = check_matrix(QG_TERN, N, K);
     if (rc) return rc;
     if (!t || !scale_f16 || !out_host) return fail(QG_EINVAL, "null pointer");
+    if (const int64_t i = first_out_of_range(t, N * K, -1, 1); i >= 0)
+        return fail(QG_EINVAL, "ternary code %d at (%lld, %lld)", t[i], (long long)(i / K), (long long)(i % K));
     const size_t row_codes = (size_t)K / 4, row_meta = (size_t)(K / 128) * 2;
     uint8_t* codes = static_cast<uint8_t*>(out_host);
     uint8_t* meta = codes + (size_t)N * row_codes;
@@ -381,9 +392,7 @@ int qpack_tern(const int8_t* t, const uint16_t* scale_f16, int64_t N, int64_t K,
             for (int64_t k = 0; k < K; k += 4) {
                 uint8_t byte = 0;
                 for (int j = 0; j < 4; ++j) {
-                    const int v = t[(size_t)r * K + k + j];
-                    if (v < -1 || v > 1)
-                        return fail(QG_EINVAL, "ternary code %d at (%lld, %lld)", v, (long long)r, (long long)(k + j));
+                    const int v = t[(size_t)r * K + k + j];  // validated above
                     byte |= (uint8_t)((v + 1) << (2 * j));
                 }
                 gc[i * row_codes + k / 4] = byte;
@@ -401,6 +410,8 @@ int qpack_tern3(const int8_t* t, const uint16_t* scale_f16, int64_t N, int64_t K
     int rc = check_matrix(QG_TERN3, N, K);
     if (rc) return rc;
     if (!t || !scale_f16 || !out_host) return fail(QG_EINVAL, "null pointer");
+    if (const int64_t i = first_out_of_range(t, N * K, -1, 1); i >= 0)
+        return fail(QG_EINVAL, "ternary code %d at (%lld, %lld)", t[i], (long long)(i / K), (long long)(i % K));
     const int64_t nb = K / 256;
     const size_t row_codes = (size_t)nb * 48, row_meta = (size_t)nb * 12;
     uint8_t* codes = static_cast<uint8_t*>(out_host);
@@ -411,9 +422,6 @@ int qpack_tern3(const int8_t* t, const uint16_t* scale_f16, int64_t N, int64_t K
         for (int i = 0; i < n_g; ++i) {
             const int64_t r = 16 * g + i;
             const int8_t* tr = t + (size_t)r * K;
-            for (int64_t k = 0; k < K; ++k)
-                if (tr[k] < -1 || tr[k] > 1)
-                    return fail(QG_EINVAL, "ternary code %d at (%lld, %lld)", tr[k], (long long)r, (long long)k);
             for (int64_t b = 0; b < nb; ++b) {
                 uint8_t* cb = gc.data() + i * row_codes + 48 * b;
                 uint8_t* mb = gm.data() + i * row_meta + 12 * b;
@@ -444,6 +452,8 @@ int qpack_bin(const uint8_t* bits, const uint16_t* scale_f16, int64_t N, int64_t
     int rc = check_matrix(QG_BIN, N, K);
     if (rc) return rc;
     if (!bits || !scale_f16 || !out_host) return fail(QG_EINVAL, "null pointer");
+    if (const int64_t i = first_out_of_range(bits, N * K, 0, 1); i >= 0)
+        return fail(QG_EINVAL, "1-bit code %u at (%lld, %lld)", bits[i], (long long)(i / K), (long long)(i % K));
     const size_t row_codes = (size_t)K / 8, row_meta = (size_t)(K / 128) * 2;
     uint8_t* codes = static_cast<uint8_t*>(out_host);
     uint8_t* meta = codes + (size_t)N * row_codes;
@@ -455,9 +465,7 @@ int qpack_bin(const uint8_t* bits, const uint16_t* scale_f16, int64_t N, int64_t
             for (int64_t k = 0; k < K; k += 8) {
                 uint8_t byte = 0;
                 for (int j = 0; j < 8; ++j) {
-                    const unsigned v = bits[(size_t)r * K + k + j];
-                    if (v > 1)
-                        return fail(QG_EINVAL, "1-bit code %u at (%lld, %lld)", v, (long long)r, (long long)(k + j));
+                    const unsigned v = bits[(size_t)r * K + k + j];  // validated above
                     byte |= (uint8_t)(v << j);
                 }
                 gc[i * row_codes + k / 8] = byte;
@@ -475,6 +483,11 @@ int qpack_bin8(const uint8_t* bits, const uint16_t* scale_f16, int64_t N, int64_
     int rc = check_matrix(QG_BIN8, N, K);
     if (rc) return rc;
     if (!bits || !scale_f16 || !out_host) return fail(QG_EINVAL, "null pointer");
+    if (const int64_t i = first_out_of_range(bits, N * K, 0, 1); i >= 0)
+        return fail(QG_EINVAL, "1-bit code %u at (%lld, %lld)", bits[i], (long long)(i / K), (long long)(i % K));
+    for (int64_t i = 0; i < N * (K / 128); ++i)
+        if (!std::isfinite(f16_to_f32(scale_f16[i])))
+            return fail(QG_EINVAL, "non-finite scale in row %lld", (long long)(i / (K / 128)));
     const int64_t nb = K / 128;
     const size_t row_codes = (size_t)K / 8, row_meta = (size_t)nb;
     uint8_t* codes = static_cast<uint8_t*>(out_host);
@@ -491,9 +504,7 @@ int qpack_bin8(const uint8_t* bits, const uint16_t* scale_f16, int64_t N, int64_
             for (int64_t k = 0; k < K; k += 8) {
                 uint8_t byte = 0;
                 for (int j = 0; j < 8; ++j) {
-                    const unsigned v = bits[(size_t)r * K + k + j];
-                    if (v > 1)
-                        return fail(QG_EINVAL, "1-bit code %u at (%lld, %lld)", v, (long long)r, (long long)(k + j));
+                    const unsigned v = bits[(size_t)r * K + k + j];  // validated above
                     byte |= (uint8_t)(v << j);
                 }
                 gc[i * row_codes + k / 8] = byte;
@@ -501,8 +512,7 @@ int qpack_bin8(const uint8_t* bits, const uint16_t* scale_f16, int64_t N, int64_
             // the row's block scales as 8-bit codes of base + step * c
             float lo = 0.0f, hi = 0.0f;
             for (int64_t b = 0; b < nb; ++b) {
-                d[b] = f16_to_f32(scale_f16[(size_t)r * nb + b]);
-                if (!std::isfinite(d[b])) return fail(QG_EINVAL, "non-finite scale in row %lld", (long long)r);
+                d[b] = f16_to_f32(scale_f16[(size_t)r * nb + b]);  // finite: validated above
                 if (b == 0 || d[b] < lo) lo = d[b];
                 if (b == 0 || d[b] > hi) hi = d[b];
             }

@@ -219,7 +219,8 @@ int qg_dequant(int fmt, const void* w, float* out, int64_t N, int64_t K, void* s
  * Signed zeros in the input are treated as +0.  n_threads <= 0 means 1.
  * Both pointers are HOST memory.  Errors: QG_EINVAL (null, non-finite input,
  * fmt is TERN/BIN/BIN8/TERN3 -- use their qpack_*), QG_ESHAPE, QG_ERANGE (a
- * scale or min overflows fp16; out_host is then unspecified). */
+ * scale or min overflows fp16).  After QG_EINVAL for a non-finite weight or
+ * QG_ERANGE, out_host is unspecified (rows are quantized as they are read). */
 int qquant(int fmt, const float* w_host, int64_t N, int64_t K, void* out_host, int n_threads);
 
 /* Device quantizer: the same quantizers as qquant (byte-identical output),
@@ -258,7 +259,8 @@ int qrequant(int src_fmt, const void* src, int dst_fmt, void* dst, int64_t N, in
 /* Host packers for the trained low-bit formats (the pages give no
  * ternarizer/binarizer): t[N][K] int8 in {-1,0,1} or bits[N][K] uint8 in
  * {0,1}, plus scale_f16[N][K/128] fp16 bit patterns -> packed bytes.
- * Errors: QG_EINVAL (null pointer, a code out of range), QG_ESHAPE. */
+ * Errors: QG_EINVAL (null pointer, a code out of range), QG_ESHAPE; every
+ * code is checked before any byte of out_host is written. */
 int qpack_tern(const int8_t* t, const uint16_t* scale_f16, int64_t N, int64_t K, void* out_host);
 int qpack_bin(const uint8_t* bits, const uint16_t* scale_f16, int64_t N, int64_t K, void* out_host);
 
