@@ -96,59 +96,61 @@ __device__ __forceinline__ float wave_sum_dpp(float v) {
     return (rl(v, 0) + rl(v, 16)) + (rl(v, 32) + rl(v, 48));
 }
 
-// (value, index) keys in a total order as one 64-bit integer: an
-// order-preserving image of the logit's bits above the complemented index, so
-// a larger value wins and, between equal values, the lower index (-0 is first
-// turned into +0, which compares equal to it).  Key 0 is below every expert,
-// -inf logits included, so a round's pick is always a valid expert.
-__device__ __forceinline__ uint64_t logit_key(float v, int i) {
-    const uint32_t b = __float_as_uint(v + 0.0f);
-    const uint32_t ord = (b & 0x80000000u) ? ~b : (b | 0x80000000u);
-    return ((uint64_t)ord << 32) | (uint32_t)~i;
-}
-__device__ __forceinline__ float key_value(uint64_t k) {
-    const uint32_t ord = (uint32_t)(k >> 32);
-    return __uint_as_float((ord & 0x80000000u) ? (ord & 0x7FFFFFFFu) : ~ord);
-}
-__device__ __forceinline__ int key_index(uint64_t k) { return (int)~(uint32_t)k; }
-
-__device__ __forceinline__ uint64_t key_max(uint64_t a, uint64_t b) { return a > b ? a : b; }
-
-template <int CTRL, int ROW_MASK = 0xF>
-__device__ __forceinline__ uint64_t dpp_key(uint64_t k) {
-    const int lo = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)k, CTRL, ROW_MASK, 0xF, false);
-    const int hi = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)(k >> 32), CTRL, ROW_MASK, 0xF, false);
-    return ((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo;
+// One token's logits in a wave's registers: lane owns experts lane + 64 m.
+// A NaN logit counts as -inf; experts past E hold NaN, which the selection
+// below never picks.
+template <int MPL>
+__device__ __forceinline__ void load_logits(const float* __restrict__ l, int E, int lane, float (&v)[MPL]) {
+#pragma unroll
+    for (int m = 0; m < MPL; ++m) {
+        const int i = lane + 64 * m;
+        const float x = i < E ? l[i] : 0.0f;
+        v[m] = i < E ? (__builtin_isnan(x) ? -INFINITY : x) : __builtin_nanf("");
+    }
 }
 
-// the wave's largest key, in every lane
-__device__ __forceinline__ uint64_t wave_key_max(uint64_t k) {
-    k = key_max(k, dpp_key<0xB1>(k));        // quad_perm [1,0,3,2]
-    k = key_max(k, dpp_key<0x4E>(k));        // quad_perm [2,3,0,1]
-    k = key_max(k, dpp_key<0x141>(k));       // row_half_mirror
-    k = key_max(k, dpp_key<0x140>(k));       // row_mirror: every lane of a row holds its max
-    k = key_max(k, dpp_key<0x142, 0xA>(k));  // row_bcast:15 into rows 1, 3
-    k = key_max(k, dpp_key<0x143, 0xC>(k));  // row_bcast:31 into rows 2, 3: lane 63 holds the max
-    const uint32_t lo = __builtin_amdgcn_readlane((int)(uint32_t)k, 63);
-    const uint32_t hi = __builtin_amdgcn_readlane((int)(uint32_t)(k >> 32), 63);
-    return ((uint64_t)hi << 32) | lo;
+// The first `rounds` rounds of the top-K selection: round k takes the largest
+// remaining logit (a wave maximum; NaN, for experts past E and experts
+// already taken, is passed over by fmaxf and equals nothing) and, between
+// equal logits (-0 equal to +0), the lowest expert index -- the lowest m
+// whose ballot is non-empty, then that ballot's lowest lane.  Lane k keeps
+// round k's expert (my_e) and logit (my_v).  rounds <= E.
+template <int MPL>
+__device__ __forceinline__ void top_rounds(float (&v)[MPL], int rounds, int lane, int& my_e, float& my_v) {
+    my_e = 0;
+    my_v = -INFINITY;
+    for (int k = 0; k < rounds; ++k) {
+        float lm = v[0];
+#pragma unroll
+        for (int m = 1; m < MPL; ++m) lm = fmaxf(lm, v[m]);
+        const float wm = wave_max_dpp(lm);  // the same in every lane
+        int win = -1;
+#pragma unroll
+        for (int m = 0; m < MPL; ++m) {
+            const uint64_t bal = __ballot(v[m] == wm);  // uniform
+            if (bal) {
+                win = (int)__builtin_ctzll(bal) + 64 * m;
+                break;
+            }
+        }
+#pragma unroll
+        for (int m = 0; m < MPL; ++m) v[m] = lane + 64 * m == win ? __builtin_nanf("") : v[m];  // taken
+        if (lane == k) {
+            my_e = win < 0 ? 0 : win;
+            my_v = wm;
+        }
+    }
 }
 
 // One token's route, computed by one wave: softmax statistics, then top_k
-// rounds of a wave argmax (lane owns experts lane + 64 m, values in
-// registers); returns, in lane k < top_k, the k-th expert (my_e) and its
-// routing weight (my_w), and the sigmoid of the shared-gate logit in every
-// lane.
+// rounds of a wave argmax; returns, in lane k < top_k, the k-th expert
+// (my_e) and its routing weight (my_w), and the sigmoid of the shared-gate
+// logit in every lane.
 template <int MPL>  // experts per lane: E <= 64 * MPL
 __device__ __forceinline__ void route_token(const float* __restrict__ l, float sl, int E, int top_k, unsigned flags,
                                             int lane, int& my_e, float& my_w, float& sig) {
     float v[MPL];
-#pragma unroll
-    for (int m = 0; m < MPL; ++m) {
-        const int i = lane + 64 * m;
-        const float x = i < E ? l[i] : -INFINITY;
-        v[m] = __builtin_isnan(x) ? -INFINITY : x;  // NaN counts as -inf
-    }
+    load_logits<MPL>(l, E, lane, v);
     float mx = -INFINITY;
 #pragma unroll
     for (int m = 0; m < MPL; ++m) mx = fmaxf(mx, v[m]);
@@ -158,20 +160,8 @@ __device__ __forceinline__ void route_token(const float* __restrict__ l, float s
     for (int m = 0; m < MPL; ++m)
         if (lane + 64 * m < E) s += expf(v[m] - mx);
     s = wave_sum_dpp(s);
-    uint64_t key[MPL];
-#pragma unroll
-    for (int m = 0; m < MPL; ++m) key[m] = lane + 64 * m < E ? logit_key(v[m], lane + 64 * m) : 0;
-    my_e = 0;
-    float my_v = -INFINITY;  // round k's winning logit, kept by lane k
-    for (int k = 0; k < top_k; ++k) {
-        uint64_t best = key[0];
-#pragma unroll
-        for (int m = 1; m < MPL; ++m) best = key_max(best, key[m]);
-        const uint64_t win = wave_key_max(best);
-#pragma unroll
-        for (int m = 0; m < MPL; ++m) key[m] = key[m] == win ? 0 : key[m];  // taken
-        if (lane == k) { my_e = key_index(win); my_v = key_value(win); }
-    }
+    float my_v;
+    top_rounds<MPL>(v, top_k, lane, my_e, my_v);
     // the weights, off the rounds' dependency chain: lane k turns its logit
     // into a probability; the renormalising sum adds them in round order
     const float my_p = expf(my_v - mx) / s;
@@ -324,7 +314,14 @@ moe_gate_up_kernel(const uint8_t* __restrict__ wgu, size_t expert_bytes, size_t 
             if (wave == 0) {
                 int my_e;
                 float my_w, sg;
-                route_token<RMPL>(logits, shared_logit[0], E, top_k, flags, lane, my_e, my_w, sg);
+                if (blockIdx.x == 0 && j == 0) {
+                    route_token<RMPL>(logits, shared_logit[0], E, top_k, flags, lane, my_e, my_w, sg);
+                } else {
+                    // only slot j's expert is needed here: rounds 0 .. j, no weights
+                    float v[RMPL], my_v;
+                    load_logits<RMPL>(logits, E, lane, v);
+                    top_rounds<RMPL>(v, j + 1, lane, my_e, my_v);
+                }
                 if (lane < top_k) route_e[lane] = my_e;
                 if (blockIdx.x == 0 && j == 0) {
                     // one token: item k is slot k's expert, then the shared one
