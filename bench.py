@@ -623,10 +623,12 @@ def _copy_kib(path):
     return float(np.median(vals))
 
 
-def _header(title, commands):
+def _header(title, commands, moe=False):
     lines = [f"# {title}", "# commands (from the repository root as $REPO):"]
     lines += [f"#   {c}" for c in commands]
     lines += [f"{key}: {source_hash(path)}" for key, path in KERNEL_SOURCES.items()]
+    if moe:  # the expert-layer kernels live in their own source
+        lines.append(f"moe_source_sha256_16: {source_hash(os.path.join(CSRC, 'moe.hip'))}")
     return lines
 
 
@@ -677,7 +679,8 @@ def summarize(kind, paths, commands):
         title = {"moe": "MoE layer (512+1 experts, H 4096, I 1024, top-4; Q4_K and Q2_K, T 1 and 8)",
                  "step": "8B decode step, q/k/v and gate/up fused (128 Q4_K GEMVs per step)",
                  "norm": "RMS-norm GEMVs and the MoE pre-norm block step"}[kind]
-        lines = _header(f"HBM bytes per dispatch from rocprofv3 FETCH_SIZE / WRITE_SIZE: {title}", commands)
+        lines = _header(f"HBM bytes per dispatch from rocprofv3 FETCH_SIZE / WRITE_SIZE: {title}", commands,
+                        moe=kind in ("moe", "norm"))
         lines += [f"copy_1gib_fetch_kib: {copy_f:.1f}", f"copy_1gib_write_kib: {copy_w:.1f}",
                   f"fetch_scale: {fs:.4f}", f"write_scale: {ws:.4f}",
                   "# kernel and grid size (work-items): dispatches | fetched MB per dispatch (mean) | "
@@ -725,7 +728,7 @@ def summarize(kind, paths, commands):
                               "(Q4_K then Q2_K, T = 1 then 8; eager passes over 32 routing sets)",
                  "norm-trace": "RMS-norm GEMVs (Q4_K, 14336x4096 and 4096x4096, batch 1 and 8) and the MoE "
                                "pre-norm block step"}[kind]
-        lines = _header(f"rocprofv3 kernel trace: {title}", commands)
+        lines = _header(f"rocprofv3 kernel trace: {title}", commands, moe=True)
         lines.append("# kernel and grid size (work-items): dispatches | median us | p10 us | p90 us")
         for name in sorted(per):
             v = np.array(per[name]) / 1e3
