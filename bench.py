@@ -566,6 +566,91 @@ def cpu_baseline(seconds=8.0):
     return out
 
 
+def oracle_per_config(reps: int = 3) -> list:
+    """The oracle on the host for each benchmark configuration: unpack +
+    dequant and the float64 matvec timed apart (median of `reps` after one
+    warm-up call each), at the BLAS pool's default threads.  One row per case:
+    packed bytes, dequant ms, matvec ms per batch, and the packed GB/s and
+    weights/s of dequant + one batch-1 matvec.  Weights are drawn once per
+    shape and shared across formats.  The 8B step is one layer's seven GEMVs
+    (q, k, v, o, gate, up, down) timed here and multiplied by 32; the MoE layer
+    is one drawn expert's dequant and forward pass, counted per touched expert
+    (dequant) and per (token, slot) (forward), as the oracle layer runs them."""
+    import workloads
+    from oracle import formats as OF
+    from oracle import gemv as OG
+    from oracle import moe as OM
+
+    def med(fn):
+        fn()
+        ts = []
+        for _ in range(reps):
+            t0 = time.perf_counter()
+            fn()
+            ts.append(time.perf_counter() - t0)
+        return float(np.median(ts))
+
+    rows = []
+
+    def gemv_case(config, fmt, packed, n, k, batches, x):
+        deq = OF.dequant_packed(fmt, packed, n, k)
+        t_deq = med(lambda: OF.dequant_packed(fmt, packed, n, k))
+        dots = {b: med(lambda b=b: OG.gemv_ref(deq, x[:b, :k])) for b in batches}
+        t1 = t_deq + dots[batches[0]]
+        rows.append({"config": config, "fmt": fmt, "N": n, "K": k, "packed_bytes": int(packed.size),
+                     "dequant_ms": round(t_deq * 1e3, 2),
+                     "matvec_ms": {f"B={b}": round(v * 1e3, 2) for b, v in dots.items()},
+                     "GBps": round(packed.size / t1 / 1e9, 4), "Gweights_s": round(n * k / t1 / 1e9, 4)})
+        return t1
+
+    x = workloads.normal((8, 14336), 0, 99)
+    # 1: the small Q4_K case
+    w = workloads.student_t_weights(1024, 1024, 0, 1)
+    gemv_case("1", "q4_k", OF.quantize_packed("q4_k", w), 1024, 1024, (1,), x)
+    # 2: four formats at two shapes, B = 1 and 8; the Q4_K matrices also serve the 8B layer
+    q4k = {}
+    for n, k in ((4096, 4096), (14336, 4096)):
+        w = workloads.student_t_weights(n, k, 0, n)
+        for fmt in ("q8_0", "q4_0", "q4_1", "q4_k"):
+            packed = OF.quantize_packed(fmt, w)
+            t1 = gemv_case("2", fmt, packed, n, k, (1, 8), x)
+            if fmt == "q4_k":
+                q4k[(n, k)] = t1
+        if n == 4096:
+            kv = OF.quantize_packed("q4_k", w[:1024])
+    # 3: one 8B layer, x32
+    wdn = workloads.student_t_weights(4096, 14336, 0, 7)
+    t_down = gemv_case("3", "q4_k", OF.quantize_packed("q4_k", wdn), 4096, 14336, (1,), x)
+    t_kv = gemv_case("3", "q4_k", kv, 1024, 4096, (1,), x)
+    layer = 2 * q4k[(4096, 4096)] + 2 * t_kv + 2 * q4k[(14336, 4096)] + t_down
+    rows.append({"config": "3", "case": "8B decode step, one layer's 7 GEMVs x 32", "step_ms": round(32 * layer * 1e3, 1),
+                 "tok_s": round(1 / (32 * layer), 3), "GBps": round(3925868544 / (32 * layer) / 1e9, 4)})
+    # 4: MoE expert (gate, up 1024x4096; down 4096x1024), T = 1 and 8 (top-4 + shared)
+    wg = workloads.student_t_weights(1024, 4096, 0, 41)
+    wu = workloads.student_t_weights(1024, 4096, 0, 42)
+    wd = workloads.student_t_weights(4096, 1024, 0, 43)
+    for fmt in ("q4_k", "q2_k"):
+        pk = [OF.quantize_packed(fmt, m) for m in (wg, wu, wd)]
+        shapes = ((1024, 4096), (1024, 4096), (4096, 1024))
+        t_deq = med(lambda: [OF.dequant_packed(fmt, p, n, k) for p, (n, k) in zip(pk, shapes)])
+        d = [OF.dequant_packed(fmt, p, n, k) for p, (n, k) in zip(pk, shapes)]
+        t_fwd = med(lambda: OM.expert_forward(d[0], d[1], d[2], x[:1, :4096]))
+        ebytes = sum(int(p.size) for p in pk)
+        for t, touched in ((1, 5), (8, 32.2)):
+            total = touched * t_deq + t * 5 * t_fwd
+            rows.append({"config": "4", "fmt": fmt, "T": t, "experts_touched": touched,
+                         "expert_dequant_ms": round(t_deq * 1e3, 2), "expert_forward_ms": round(t_fwd * 1e3, 3),
+                         "layer_ms": round(total * 1e3, 1), "GBps": round(touched * ebytes / total / 1e9, 4)})
+    # 5: tern and bin at three shapes, B = 1 and 4
+    for n, k in ((4096, 4096), (12288, 4096), (4096, 12288)):
+        sb = workloads.scale_bits_f16((n, k // 128), 0, 5)
+        t_codes = workloads.ternary_codes(n, k, 0, 3)
+        b_codes = workloads.binary_codes(n, k, 0, 4)
+        gemv_case("5", "tern", OF.pack("tern", OF.tern_from_codes(t_codes, sb)), n, k, (1, 4), x)
+        gemv_case("5", "bin", OF.pack("bin", OF.bin_from_codes(b_codes, sb)), n, k, (1, 4), x)
+    return rows
+
+
 def environment(torch) -> dict:
     env = {"torch": torch.__version__, "hip": getattr(torch.version, "hip", None), "python": platform.python_version()}
     try:
@@ -1038,6 +1123,9 @@ def main():
     if not args.no_cpu:
         log("cpu baseline (oracle)")
         line["cpu_baseline"] = cpu_baseline()
+        t0 = time.perf_counter()
+        line["cpu_baseline"]["per_config"] = oracle_per_config()
+        log(f"oracle per config: {time.perf_counter() - t0:.0f} s")
     print(json.dumps(line), flush=True)
 
 
