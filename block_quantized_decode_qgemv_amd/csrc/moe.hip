@@ -45,10 +45,15 @@ constexpr int kMaxT = 8, kMaxTopK = 8, kMaxE = 4096;
 // Up to this many experts, a single token's route is computed inside the
 // gate/up workgroups (8 logits per lane) instead of by a routing launch.
 constexpr int kRouteInGateUpMaxE = 512;
-// Tokens one down workgroup takes in turn.  At T = 8, 4 per workgroup beat 1
-// (Q4_K 67.6 -> 64.9 us, Q2_K 53.3 -> 50.6 us for the layer, same box);
-// 8 per workgroup matched 4 for Q4_K and lost 13% for Q2_K.
-constexpr int kDownTokensPerGroup = 4;
+// Down workgroups per 16-row group (each takes its share of the T tokens in
+// turn).  Measured for the layer at T = 2..8 against every power of two of
+// tokens per workgroup, same machine: Q4_K is fastest with 4 tokens per
+// workgroup (T = 8: 65.3 us against 67.8 with one token per workgroup), Q2_K
+// with two workgroups whatever T (T = 4: 31.0 against 33.7 with one).
+template <int F>
+int down_token_groups(int T) {
+    return F == QG_Q2_K ? (T < 2 ? T : 2) : (T + 3) / 4;
+}
 constexpr int kItemInts = 8;  // expert, count, tok[2], kslot[2], wt[2] (as float bits)
 
 // Workspace layout, byte offsets (each region 256-byte aligned).
@@ -453,7 +458,7 @@ template <int F, int WD, int KCS>
 hipError_t launch_down_w(const uint8_t* wdn, int H, int I, int top_k, int T, const int* items, const int* hsel,
                          const float* h, const float* residual, float* out, hipStream_t st) {
     const size_t eb = qg_packed_size(F, H, I), cb = qg_codes_plane_size(F, H, I);
-    const int ty = (T + kDownTokensPerGroup - 1) / kDownTokensPerGroup;
+    const int ty = down_token_groups<F>(T);
     hipLaunchKernelGGL((moe_down_kernel<F, WD, KCS>), dim3(H / kRowGroup, ty), dim3((top_k + 1) * WD * 64), 0, st,
                        wdn, eb, cb, H, I, T, top_k, items, hsel, h, residual, out);
     return hipGetLastError();
