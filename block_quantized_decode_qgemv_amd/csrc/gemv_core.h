@@ -680,7 +680,8 @@ template <int F> constexpr bool dpp_units_ok(int kcs) {
     return (kcs * T::CPC) % 64 == 0 &&
            (is_kquant<F>() ? (T::BLOCK / T::CPC) % kcs == 0      // inside one super-block
                            : (kcs * T::CPC) % T::BLOCK == 0) &&  // whole blocks (aligned meta)
-           (kcs * T::MBU >= 2 || T::MB == 1);                    // at least one fp16 of meta, or whole 1-byte entries
+           (kcs * T::MBU >= 2 || T::MB == 1) &&                  // at least one fp16 of meta, or whole 1-byte entries
+           (is_kquant<F>() || kcs * T::MBU <= 16);               // the part's meta in one 16-byte load
 }
 template <int F, int B> constexpr int dpp_lane_units() {
     int best = 0;
@@ -717,6 +718,7 @@ struct GemvDpp {
     static constexpr int DPS = 4 / SUBS;          // code dwords per sub-group
     static constexpr int UPS = is_kquant<F>() ? T::BLOCK / CPC : 1;  // units per super-block
     static_assert(NXC % 64 == 0, "a part covers whole 64-column spans");
+    static_assert(dpp_units_ok<F>(KCS), "lane part width");
     static_assert(!is_kquant<F>() || UPS % KCS == 0, "a K-quant part stays in one super-block");
     static_assert(B * NX4 * 4 <= 64, "x registers per lane");
 
