@@ -10,13 +10,15 @@
 //      top-K experts (ties to the lower index) and weights, and
 //      sigmoid(shared-gate logit); then it groups the (token, k) pairs into
 //      work items -- one expert with at most 2 tokens, in order of first
-//      appearance -- and appends the shared expert as ceil(T/2) items;
+//      appearance -- and appends the shared expert as ceil(T/2) items (a
+//      single token needs no routing launch: the gate/up workgroups route it);
 //   2. gate/up: one grouped GEMV over the items (x rows gathered by token);
 //      gate and up rows are interleaved (row 2i = gate i, row 2i+1 = up i), so
 //      each 16-row group holds 8 (gate, up) pairs and the epilogue writes
 //      h = silu(gate) * up directly (fused SwiGLU);
-//   3. down + combine: one workgroup per (16 output rows, token) runs the
-//      down projection of each of the token's K + 1 slots in its own wave
+//   3. down + combine: for each 16 output rows, one or a few workgroups that
+//      share the tokens; for each of its tokens in turn a workgroup runs the
+//      down projection of the token's K + 1 slots, each in its own wave
 //      group, scales it by the slot's routing weight (sigmoid gate for the
 //      shared expert), and writes out = residual + the K routed sums + the
 //      shared sum, in that fixed order (deterministic; no float atomics and
@@ -303,7 +305,8 @@ __device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }
 // RMPL > 0 (a single token, E <= 64 * RMPL): no routing launch precedes the
 // kernel; the items are the token's top_k experts in order, then the shared
 // expert, and workgroup column j routes the token itself (one wave, the
-// routing launch's own per-token code) to find its expert; workgroup (0, 0)
+// routing launch's per-token rounds, only those up to slot j) to find its
+// expert; workgroup (0, 0)
 // also writes the routing records the down kernel reads (items, hsel), the
 // same records the routing launch writes for one token.
 template <int F, int W, int KCS, int NORM, int RMPL>
