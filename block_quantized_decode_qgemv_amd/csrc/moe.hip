@@ -17,9 +17,9 @@
 //      each 16-row group holds 8 (gate, up) pairs and the epilogue writes
 //      h = silu(gate) * up directly (fused SwiGLU);
 //   3. down + combine: for each 16 output rows, one or a few workgroups that
-//      share the tokens; for each of its tokens in turn a workgroup runs the
-//      down projection of the token's K + 1 slots, each in its own wave
-//      group, scales it by the slot's routing weight (sigmoid gate for the
+//      share the tokens; for each of its tokens (or token pairs) in turn a
+//      workgroup runs the down projection of the token's K + 1 slots, each in
+//      its own wave group, scales it by the slot's routing weight (sigmoid gate for the
 //      shared expert), and writes out = residual + the K routed sums + the
 //      shared sum, in that fixed order (deterministic; no float atomics and
 //      no partial results leaving the workgroup).
@@ -386,24 +386,28 @@ moe_gate_up_kernel(const uint8_t* __restrict__ wgu, size_t expert_bytes, size_t 
 }
 
 // down + combine: one workgroup per 16-row group g and token t, or per g and a
-// run of tokens taken in turn (t = blockIdx.y, blockIdx.y + gridDim.y, ...,
-// the two LDS arrays reused after a barrier).  Its waves form
-// top_k + 1 groups of WD waves; group s runs the down projection of the
-// token's slot s (the K routed experts, then the shared one) on its h row and
-// scales it by the slot's weight; then out = residual + the slot sums in slot
-// order.  A token pair sharing an item reads that expert's down rows twice,
-// but no partial leaves the workgroup.
-template <int F, int WD, int KCS>
+// run of tokens taken TP at a time (t0 = TP * blockIdx.y, then TP * gridDim.y
+// further, the LDS arrays reused after a barrier).  Its waves form TP x
+// (top_k + 1) groups of WD waves; group (u, s) runs the down projection of
+// token t0 + u's slot s (the K routed experts, then the shared one) on its h
+// row and scales it by the slot's weight; then out = residual + the slot sums
+// in slot order, per token.  A token pair sharing an item reads that expert's
+// down rows twice, but no partial leaves the workgroup.
+template <int F, int WD, int KCS, int TP>
 __global__ void __launch_bounds__(1024)
 moe_down_kernel(const uint8_t* __restrict__ wdn, size_t expert_bytes, size_t codes_bytes, int H, int I, int T,
                 int top_k, const int* __restrict__ items, const int* __restrict__ hsel,
                 const float* __restrict__ h, const float* __restrict__ residual, float* __restrict__ out) {
-    __shared__ float red[kMaxTopK + 1][WD * kRowGroup];
-    __shared__ float slot_sum[kMaxTopK + 1][kRowGroup];
+    __shared__ float red[TP][kMaxTopK + 1][WD * kRowGroup];
+    __shared__ float slot_sum[TP][kMaxTopK + 1][kRowGroup];
     const int g = blockIdx.x;
-    const int s = threadIdx.x / (64 * WD);  // slot group, uniform per wave
-    // tokens blockIdx.y, blockIdx.y + gridDim.y, ... (uniform loop)
-    for (int t = blockIdx.y; t < T; t += gridDim.y) {
+    const int grp = threadIdx.x / (64 * WD);  // wave group, uniform per wave
+    const int tp = TP == 1 ? 0 : grp / (top_k + 1), s = grp - tp * (top_k + 1);
+    // TP tokens at a time: t0 = TP * blockIdx.y, then TP * gridDim.y further (uniform loop)
+    for (int t0 = TP * blockIdx.y; t0 < T; t0 += TP * gridDim.y) {
+        // a group past the last token repeats token T - 1 and its sums go
+        // unused (every group must run: the GEMV synchronizes the workgroup)
+        const int t = TP == 1 ? t0 : min(t0 + tp, T - 1);
         const int hs = hsel[t * (top_k + 1) + s];
         const int* it = items + kItemInts * (1 + (hs >> 1));
         const float wt = __int_as_float(it[6 + (hs & 1)]);
@@ -413,17 +417,20 @@ moe_down_kernel(const uint8_t* __restrict__ wdn, size_t expert_bytes, size_t cod
         GemvDpp<F, 1, WD, KCS>::run_group(
             codes, meta, H, I, g, [&](int) { return xr; }, 1,
             [&](auto sum, int, int tid) {
-                if (tid < kRowGroup) slot_sum[s][tid] = wt * sum(tid);
+                if (tid < kRowGroup) slot_sum[tp][s][tid] = wt * sum(tid);
             },
-            s * WD, &red[s][0]);
+            grp * WD, &red[tp][s][0]);
         __syncthreads();
-        if (threadIdx.x < kRowGroup) {
-            const size_t o = (size_t)t * H + (size_t)kRowGroup * g + threadIdx.x;
-            float v = residual[o];
-            for (int k = 0; k <= top_k; ++k) v += slot_sum[k][threadIdx.x];
-            out[o] = v;
+        if (threadIdx.x < TP * kRowGroup) {
+            const int u = TP == 1 ? 0 : threadIdx.x / kRowGroup, r = threadIdx.x - u * kRowGroup;
+            if (TP == 1 || t0 + u < T) {
+                const size_t o = (size_t)(t0 + u) * H + (size_t)kRowGroup * g + r;
+                float v = residual[o];
+                for (int k = 0; k <= top_k; ++k) v += slot_sum[u][k][r];
+                out[o] = v;
+            }
         }
-        __syncthreads();  // red and slot_sum are reused by the next token
+        __syncthreads();  // red and slot_sum are reused by the next tokens
     }
 }
 
@@ -457,13 +464,13 @@ hipError_t launch_gate_up(const uint8_t* wgu, int H, int I, const float* x, cons
     }
 }
 
-template <int F, int WD, int KCS>
+template <int F, int WD, int KCS, int TP = 1>
 hipError_t launch_down_w(const uint8_t* wdn, int H, int I, int top_k, int T, const int* items, const int* hsel,
-                         const float* h, const float* residual, float* out, hipStream_t st) {
+                         const float* h, const float* residual, float* out, hipStream_t st, int ty = 0) {
     const size_t eb = qg_packed_size(F, H, I), cb = qg_codes_plane_size(F, H, I);
-    const int ty = down_token_groups<F>(T);
-    hipLaunchKernelGGL((moe_down_kernel<F, WD, KCS>), dim3(H / kRowGroup, ty), dim3((top_k + 1) * WD * 64), 0, st,
-                       wdn, eb, cb, H, I, T, top_k, items, hsel, h, residual, out);
+    if (ty <= 0) ty = down_token_groups<F>(T);
+    hipLaunchKernelGGL((moe_down_kernel<F, WD, KCS, TP>), dim3(H / kRowGroup, ty), dim3(TP * (top_k + 1) * WD * 64), 0,
+                       st, wdn, eb, cb, H, I, T, top_k, items, hsel, h, residual, out);
     return hipGetLastError();
 }
 
@@ -504,6 +511,17 @@ hipError_t launch_moe(const uint8_t* wgu, const uint8_t* wdn, int E, int H, int 
                                             flags, hsel, st);
     }
     if (e != hipSuccess) return e;
+    // down, even T: two tokens at a time, each slot's row in one wave of
+    // double-width lane parts (Q4_K at I = 1024: 10 waves of 9 KB each instead
+    // of 10 of 4.6 KB); one workgroup per row group takes the token pairs in
+    // turn.  T = 2 / 4 / 6 / 8 layer: 23.2 / 36.9 / 49.1 / 60.5 us against
+    // 24.4 / 39.2 / 52.4 / 64.7 (same machine); odd T would leave a group
+    // idle (T = 3: 32.2 against 31.3 us), so it keeps one token at a time.
+    constexpr int KW = 2 * KCS;
+    if constexpr (KW <= 8 && dpp_units_ok<F>(KW)) {
+        if (T >= 2 && T % 2 == 0 && 2 * (top_k + 1) <= 16 && pick_waves_dpp<F, KW>(I) == 1)
+            return launch_down_w<F, 1, KW, 2>(wdn, H, I, top_k, T, items, hsel, h, residual, out, st, 1);
+    }
     // down: where a slot would get one wave, half-width lane parts give it
     // two (Q2_K, I = 1024: single-token layer 12.4 -> 11.9 us, T = 8 equal)
     if constexpr (KCS >= 2 && dpp_units_ok<F>(KCS / 2)) {
