@@ -110,7 +110,7 @@ def small_layer(fmt, e, h, i, seed):
 
 
 @pytest.mark.parametrize("fmt", KFORMATS)
-@pytest.mark.parametrize("t", [1, 2, 3, 8])
+@pytest.mark.parametrize("t", [1, 2, 3, 4, 5, 6, 7, 8])
 @pytest.mark.parametrize("renorm", [False, True])
 def test_moe_small(fmt, t, renorm):
     e, h, i, top_k = 16, 512, 256, 4
@@ -394,7 +394,7 @@ class PooledExperts:
 
 
 @pytest.mark.parametrize("fmt", KFORMATS)
-@pytest.mark.parametrize("t", [1, 8])
+@pytest.mark.parametrize("t", [1, 4, 8])
 def test_moe_full_layer(fmt, t):
     e, h, i, top_k = FULL_E, FULL_H, FULL_I, FULL_K
     x, residual, logits, s = inputs(t, e, h, seed=600 + t)
