@@ -516,16 +516,25 @@ hipError_t launch_moe(const uint8_t* wgu, const uint8_t* wdn, int E, int H, int 
                                             flags, hsel, st);
     }
     if (e != hipSuccess) return e;
-    // down, even T: two tokens at a time, each slot's row in one wave of
-    // double-width lane parts (Q4_K at I = 1024: 10 waves of 9 KB each instead
-    // of 10 of 4.6 KB); one workgroup per row group takes the token pairs in
-    // turn.  T = 2 / 4 / 6 / 8 layer: 23.2 / 36.9 / 49.1 / 60.5 us against
-    // 24.4 / 39.2 / 52.4 / 64.7 (same machine); odd T would leave a group
-    // idle (T = 3: 32.2 against 31.3 us), so it keeps one token at a time.
+    // down from two tokens up: two or three tokens at a time, each slot's row
+    // in one wave of double-width lane parts (Q4_K at I = 1024: 9 KB in flight
+    // per wave instead of 4.6 KB), the tokens' slot groups side by side in one
+    // workgroup per row group, which takes them in turn.  Three at a time
+    // where that takes fewer rounds than two (a last round may hold an idle
+    // group), two where the rounds tie.  Two against one at T = 2 / 4 / 6 / 8:
+    // layer 23.2 / 36.9 / 49.1 / 60.5 us against 24.4 / 39.2 / 52.4 / 64.7;
+    // three against the choice before it at T = 3 / 5 / 6 / 7 / 8: 27.4 /
+    // 40.7 / 44.0 / 53.3 / 56.6 us against 30.1 / 43.5 / 46.1 / 55.7 / 57.2,
+    // and 37.2 against 34.4 us at T = 4 (same-machine A/B runs).  Odd T
+    // without room for three slot groups keeps one token at a time.
     constexpr int KW = 2 * KCS;
     if constexpr (KW <= 8 && dpp_units_ok<F>(KW)) {
-        if (T >= 2 && T % 2 == 0 && 2 * (top_k + 1) <= 16 && pick_waves_dpp<F, KW>(I) == 1)
-            return launch_down_w<F, 1, KW, 2>(wdn, H, I, top_k, T, items, hsel, h, residual, out, st, 1);
+        if (T >= 2 && pick_waves_dpp<F, KW>(I) == 1) {
+            if (T >= 3 && 3 * (top_k + 1) <= 16 && (T + 2) / 3 < (T + 1) / 2)
+                return launch_down_w<F, 1, KW, 3>(wdn, H, I, top_k, T, items, hsel, h, residual, out, st, 1);
+            if (T % 2 == 0 && 2 * (top_k + 1) <= 16)
+                return launch_down_w<F, 1, KW, 2>(wdn, H, I, top_k, T, items, hsel, h, residual, out, st, 1);
+        }
     }
     // down: where a slot would get one wave, half-width lane parts give it
     // two (Q2_K, I = 1024: single-token layer 12.4 -> 11.9 us, T = 8 equal)
