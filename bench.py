@@ -31,6 +31,7 @@ from __future__ import annotations
 
 import argparse
 import csv
+import glob
 import hashlib
 import json
 import os
@@ -676,6 +677,16 @@ def environment(torch) -> dict:
     except Exception:
         env["git_rev"] = None  # a copy of the tree without .git; the source hashes identify the kernels
     env.update({key: source_hash(path) for key, path in KERNEL_SOURCES.items()})
+    env["moe_source_sha256_16"] = source_hash(os.path.join(CSRC, "moe.hip"))
+    # every library source and the header, in name order: identifies the build
+    # where the tree travels without its history
+    digest = hashlib.sha256()
+    for path in sorted(glob.glob(os.path.join(CSRC, "*"))) + [os.path.join(ROOT, "include", "qgemv.h")]:
+        if os.path.isfile(path):
+            digest.update(os.path.basename(path).encode() + b"\0")
+            with open(path, "rb") as fh:
+                digest.update(fh.read())
+    env["library_sources_sha256_16"] = digest.hexdigest()[:16]
     return env
 
 
