@@ -17,12 +17,12 @@
 //      each 16-row group holds 8 (gate, up) pairs and the epilogue writes
 //      h = silu(gate) * up directly (fused SwiGLU);
 //   3. down + combine: for each 16 output rows, one or a few workgroups that
-//      share the tokens; for each of its tokens (or token pairs) in turn a
-//      workgroup runs the down projection of the token's K + 1 slots, each in
-//      its own wave group, scales it by the slot's routing weight (sigmoid gate for the
-//      shared expert), and writes out = residual + the K routed sums + the
-//      shared sum, in that fixed order (deterministic; no float atomics and
-//      no partial results leaving the workgroup).
+//      share the tokens; for each of its tokens in turn (or two or three at
+//      once) a workgroup runs the down projection of the token's K + 1 slots,
+//      each in its own wave group, scales it by the slot's routing weight
+//      (sigmoid gate for the shared expert), and writes out = residual + the
+//      K routed sums + the shared sum, in that fixed order (deterministic; no
+//      float atomics and no partial results leaving the workgroup).
 #include <hip/hip_runtime.h>
 
 #include <cmath>
