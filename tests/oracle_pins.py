@@ -209,6 +209,33 @@ def tern3_bytes(F) -> None:
     assert w[0, 1] == -1.0 and w[0, 130] == 0.5
 
 
+def q2k_bytes_and_values(F) -> None:
+    """Hand-worked Q2_K block (readings R4, R6): d = 1.0, dmin = 0.5, scale
+    codes s_j = j + 1 and min codes t_j = 2j for the eight 32-weight
+    sub-blocks; every weight code 0 except column 1 (code 1), column 6
+    (code 3) and column 255 (code 2).  Code bytes: field i in byte i >> 2 at
+    bits 2 (i & 3), so byte 0 = 1 << 2, byte 1 = 3 << 4, byte 63 = 2 << 6.
+    Values d s_j q - dmin t_j: column 1 -> 1, column 6 -> 3, column 255 ->
+    8 * 2 - 0.5 * 14 = 9, column 32 (sub-block 1, code 0) -> -1."""
+    n = np.zeros((1, 256), np.uint8)
+    n[0, 1], n[0, 6], n[0, 255] = 1, 3, 2
+    blk = {"d": np.array([[0x3C00]], np.uint16), "dmin": np.array([[0x3800]], np.uint16),
+           "s": np.arange(1, 9, dtype=np.uint8).reshape(1, 1, 8),
+           "t": (2 * np.arange(8)).astype(np.uint8).reshape(1, 1, 8), "n": n}
+    buf = F.pack("q2_k", blk)
+    cp = F.codes_plane_size("q2_k", 1, 256)
+    assert cp == 64 and buf.size == 80
+    want = np.zeros(64, np.uint8)
+    want[0], want[1], want[63] = 0x04, 0x30, 0x80
+    np.testing.assert_array_equal(buf[:64], want)
+    assert list(buf[76:80]) == [0x00, 0x3C, 0x00, 0x38]
+    field = int.from_bytes(bytes(buf[64:76]), "little")
+    assert [(field >> (12 * j)) & 0x3F for j in range(8)] == list(range(1, 9))
+    assert [(field >> (12 * j + 6)) & 0x3F for j in range(8)] == [2 * j for j in range(8)]
+    w = F.dequant_packed("q2_k", buf, 1, 256)
+    assert w[0, 1] == 1.0 and w[0, 6] == 3.0 and w[0, 255] == 9.0 and w[0, 32] == -1.0 and w[0, 0] == 0.0
+
+
 # ----------------------------------------------------------------------------
 # hand-worked single blocks for the readings R1 and point 3 (Q4_0 ties)
 

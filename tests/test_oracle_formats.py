@@ -122,6 +122,10 @@ def test_tern3_hand_worked_bytes():
     P.tern3_bytes(F)
 
 
+def test_q2k_hand_worked_bytes_and_values():
+    P.q2k_bytes_and_values(F)
+
+
 def test_tern3_density_matches_page(golden):
     """tern3 (R10): 48 bytes of base-3 digits (five weights per byte) and 12
     meta bytes (four fp16 scales, 16 weights in 2-bit fields) per 256 weights
