@@ -410,8 +410,10 @@ moe_down_kernel(const uint8_t* __restrict__ wdn, size_t expert_bytes, size_t cod
     const int tp = TP == 1 ? 0 : grp / (top_k + 1), s = grp - tp * (top_k + 1);
     // TP tokens at a time: t0 = TP * blockIdx.y, then TP * gridDim.y further (uniform loop)
     for (int t0 = TP * blockIdx.y; t0 < T; t0 += TP * gridDim.y) {
-        // a group past the last token repeats token T - 1 and its sums go
-        // unused (every group must run: the GEMV synchronizes the workgroup)
+        // a group past the last token runs the GEMV over an empty column range
+        // (no loads; every group must run it: it synchronizes the workgroup),
+        // its sums unused
+        const bool live = TP == 1 || t0 + tp < T;
         const int t = TP == 1 ? t0 : min(t0 + tp, T - 1);
         const int hs = hsel[t * (top_k + 1) + s];
         const int* it = items + kItemInts * (1 + (hs >> 1));
@@ -424,7 +426,7 @@ moe_down_kernel(const uint8_t* __restrict__ wdn, size_t expert_bytes, size_t cod
             [&](auto sum, int, int tid) {
                 if (tid < kRowGroup) slot_sum[tp][s][tid] = wt * sum(tid);
             },
-            grp * WD, &red[tp][s][0]);
+            grp * WD, &red[tp][s][0], nullptr, 0.0f, nullptr, 0, live ? -1 : 0);
         __syncthreads();
         if (threadIdx.x < TP * kRowGroup) {
             const int u = TP == 1 ? 0 : threadIdx.x / kRowGroup, r = threadIdx.x - u * kRowGroup;
