@@ -524,7 +524,7 @@ hipError_t launch_moe(const uint8_t* wgu, const uint8_t* wdn, int E, int H, int 
     }
     if (e != hipSuccess) return e;
     // down from two tokens up: two or three tokens at a time, each slot's row
-    // in one wave of double-width lane parts (Q4_K at I = 1024: 9 KB in flight
+    // in one wave of the widest lane parts (Q4_K at I = 1024: 9 KB in flight
     // per wave instead of 4.6 KB), the tokens' slot groups side by side in one
     // workgroup per row group, which takes them in turn.  Three at a time
     // where that takes fewer rounds than two (a last round may hold an idle
@@ -534,7 +534,10 @@ hipError_t launch_moe(const uint8_t* wgu, const uint8_t* wdn, int E, int H, int 
     // 40.7 / 44.0 / 53.3 / 56.6 us against 30.1 / 43.5 / 46.1 / 55.7 / 57.2,
     // and 37.2 against 34.4 us at T = 4 (same-machine A/B runs).  Odd T
     // without room for three slot groups keeps one token at a time.
-    constexpr int KW = 2 * KCS;
+    // (the gate/up's width: Q4_K twice the usual, Q2_K the usual; for Q2_K
+    // at T = 3 / 6 / 8: 24.8 / 39.7 / 50.2 us against 25.4 / 41.7 / 52.4 one
+    // token at a time, T = 2, 4, 5, 7 within 1 %)
+    constexpr int KW = KGU;
     if constexpr (KW <= 8 && dpp_units_ok<F>(KW)) {
         if (T >= 2 && pick_waves_dpp<F, KW>(I) == 1) {
             if (T >= 3 && 3 * (top_k + 1) <= 16 && (T + 2) / 3 < (T + 1) / 2)
