@@ -47,11 +47,13 @@ constexpr int kMaxT = 8, kMaxTopK = 8, kMaxE = 4096;
 // Up to this many experts, a single token's route is computed inside the
 // gate/up workgroups (8 logits per lane) instead of by a routing launch.
 constexpr int kRouteInGateUpMaxE = 512;
-// Down workgroups per 16-row group (each takes its share of the T tokens in
-// turn).  Measured for the layer at T = 2..8 against every power of two of
-// tokens per workgroup, same machine: Q4_K is fastest with 4 tokens per
-// workgroup (T = 8: 65.3 us against 67.8 with one token per workgroup), Q2_K
-// with two workgroups whatever T (T = 4: 31.0 against 33.7 with one).
+// Down workgroups per 16-row group when the down takes one token at a time
+// (a single token, or odd T where three slot groups do not fit a workgroup);
+// each takes its share of the T tokens in turn.  Measured for the layer at
+// T = 2..8 against every power of two of tokens per workgroup, same machine:
+// Q4_K is fastest with 4 tokens per workgroup (T = 8: 65.3 us against 67.8
+// with one token per workgroup), Q2_K with two workgroups whatever T (T = 4:
+// 31.0 against 33.7 with one).
 template <int F>
 int down_token_groups(int T) {
     return F == QG_Q2_K ? (T < 2 ? T : 2) : (T + 3) / 4;
